@@ -1,0 +1,171 @@
+"""ctypes binding of libw4a4.so (include/w4a4.h): argument marshalling only.
+
+Every step of the hot path runs in the library's HIP kernels.  PyTorch supplies
+device memory (tensor data pointers) and the current stream.  There is no
+fallback: if the library is missing or a call fails, this raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libw4a4.so")
+
+DTYPE_F32 = 0
+DTYPE_F16 = 1
+
+
+class W4A4Error(RuntimeError):
+    """A libw4a4 call returned a status other than W4A4_OK."""
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise W4A4Error(f"{LIB_PATH} is not built; run `python -m hadamard_rotated_w4a4_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, SZ, ST = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+        sigs = {
+            "w4a4_status_string": ([ST], ctypes.c_char_p),
+            "w4a4_last_hip_error": ([], ctypes.c_char_p),
+            "w4a4_q4_0_bytes": ([I64, I64], SZ),
+            "w4a4_quantize_q4_0_h32": ([P, I64, I64, I64, P, P], ST),
+            "w4a4_packed_weight_bytes": ([I64, I64], SZ),
+            "w4a4_repack_q4_0_h32": ([P, P, I64, I64, P], ST),
+            "w4a4_rotate_quantize_act": ([P, ST, I64, I64, I64, P, P, P], ST),
+            "w4a4_gemm": ([P, P, P, P, I64, I64, I64, I64, P], ST),
+            "w4a4_gemm_id_workspace_bytes": ([I64, I64, I64], SZ),
+            "w4a4_gemm_id": ([P, I64, P, P, I64, P, I64, I64, P, I64, I64, P, SZ, P], ST),
+        }
+        for name, (args, res) in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().w4a4_status_string(status).decode()
+        detail = lib().w4a4_last_hip_error().decode()
+        raise W4A4Error(f"{what}: {msg}" + (f" ({detail})" if detail else ""))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise W4A4Error("tensors must live on the GPU")
+
+
+# --------------------------------------------------------------------------
+# sizes
+# --------------------------------------------------------------------------
+
+def q4_0_bytes(n: int, k: int) -> int:
+    return int(lib().w4a4_q4_0_bytes(n, k))
+
+
+def packed_weight_bytes(n: int, k: int) -> int:
+    return int(lib().w4a4_packed_weight_bytes(n, k))
+
+
+def gemm_id_workspace_bytes(n_expert: int, n_tokens: int, top_k: int) -> int:
+    return int(lib().w4a4_gemm_id_workspace_bytes(n_expert, n_tokens, top_k))
+
+
+# --------------------------------------------------------------------------
+# entry points
+# --------------------------------------------------------------------------
+
+def quantize_q4_0_h32(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 [n, k] (row stride w.stride(0)) -> rotated Q4_0 bytes uint8 [n, k/32, 18]."""
+    _require_cuda(w, out)
+    assert w.dtype == torch.float32 and w.dim() == 2 and w.stride(1) == 1
+    n, k = w.shape
+    if out is None:
+        out = torch.empty((n, k // 32, 18), dtype=torch.uint8, device=w.device)
+    _check(lib().w4a4_quantize_q4_0_h32(_ptr(w), n, k, w.stride(0), _ptr(out), _stream(w.device)),
+           "w4a4_quantize_q4_0_h32")
+    return out
+
+
+def repack_q4_0_h32(q4: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rotated Q4_0 bytes -> packed weight buffer (uint8, private layout)."""
+    _require_cuda(q4, out)
+    if out is None:
+        out = torch.empty(packed_weight_bytes(n, k), dtype=torch.uint8, device=q4.device)
+    _check(lib().w4a4_repack_q4_0_h32(_ptr(q4), _ptr(out), n, k, _stream(q4.device)),
+           "w4a4_repack_q4_0_h32")
+    return out
+
+
+def rotate_quantize_act(x: torch.Tensor, k: int | None = None, codes: torch.Tensor | None = None,
+                        scales: torch.Tensor | None = None):
+    """x fp16/fp32 [m, >=k] (row stride x.stride(0)) -> (codes uint8 [m, k/2], scales fp32 [m, k/32])."""
+    _require_cuda(x, codes, scales)
+    assert x.dim() == 2 and x.stride(1) == 1
+    dt = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16}.get(x.dtype)
+    if dt is None:
+        raise W4A4Error(f"unsupported activation dtype {x.dtype}")
+    m = x.shape[0]
+    k = x.shape[1] if k is None else k
+    if codes is None:
+        codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    _check(lib().w4a4_rotate_quantize_act(_ptr(x), dt, m, k, x.stride(0), _ptr(codes), _ptr(scales),
+                                          _stream(x.device)), "w4a4_rotate_quantize_act")
+    return codes, scales
+
+
+def gemm(packed: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: int, k: int,
+         y: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A4 product: fp32 [m, n] (row stride y.stride(0))."""
+    _require_cuda(packed, codes, scales, y)
+    m = codes.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=codes.device)
+    assert y.stride(1) == 1
+    _check(lib().w4a4_gemm(_ptr(packed), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, y.stride(0),
+                           _stream(codes.device)), "w4a4_gemm")
+    return y
+
+
+def gemm_id(packed: torch.Tensor, n_expert: int, codes: torch.Tensor, scales: torch.Tensor,
+            act_rows_per_token: int, ids: torch.Tensor, n: int, k: int, y: torch.Tensor | None = None,
+            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """MUL_MAT_ID: fp32 [n_tokens, top_k, n]."""
+    _require_cuda(packed, codes, scales, ids, y, workspace)
+    assert ids.dtype == torch.int32 and ids.dim() == 2
+    n_tokens, top_k = ids.shape
+    if y is None:
+        y = torch.empty((n_tokens, top_k, n), dtype=torch.float32, device=ids.device)
+    need = gemm_id_workspace_bytes(n_expert, n_tokens, top_k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ids.device)
+    _check(lib().w4a4_gemm_id(_ptr(packed), n_expert, _ptr(codes), _ptr(scales), act_rows_per_token,
+                              _ptr(ids.contiguous()), n_tokens, top_k, _ptr(y), n, k, _ptr(workspace),
+                              workspace.numel(), _stream(ids.device)), "w4a4_gemm_id")
+    return y
+
+
+def prepare_weights(w: torch.Tensor) -> torch.Tensor:
+    """Offline step on the GPU: fp32 [n, k] -> rotated Q4_0 -> packed buffer."""
+    n, k = w.shape
+    return repack_q4_0_h32(quantize_q4_0_h32(w), n, k)

@@ -1,0 +1,96 @@
+// Offline weight preparation and the one-time repack.
+//
+// 1bit-MONSTER engine docs, "The lean option: ROCmFP4, ROCmI4 and Hadamard
+// Q4_0", section "Hadamard-rotated Q4_0: W4A4 prompt processing": the weights
+// are rotated once by the 32-point Walsh-Hadamard transform per 32-element
+// block along K and quantised to plain Q4_0; the W4A4 kernel reads the Q4_0
+// codes bit for bit, using that q ^ 8 read as a signed nibble is q - 8.
+#pragma once
+
+#include "common.h"
+
+namespace w4a4 {
+
+// fp64(1/sqrt(32)) correctly rounded (= fp64(sqrt(2)) / 8).
+__device__ constexpr double kInvSqrt32d = 0.17677669529663688110021109052621763;
+
+// One thread per 32-element block: rotate in fp64, round to fp32, quantise to Q4_0.
+__global__ __launch_bounds__(256) void quantize_q4_0_h32_kernel(const float *__restrict__ w,
+                                                                 int64_t n, int64_t k, int64_t ldw,
+                                                                 uint8_t *__restrict__ q4) {
+    const int64_t nb = k / QK;
+    const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blk >= n * nb) return;
+    const int64_t row = blk / nb, b = blk % nb;
+    const float *src = w + row * ldw + b * QK;
+
+    float x[QK];
+#pragma unroll
+    for (int j = 0; j < QK; j++) x[j] = src[j];
+
+    float r[QK];
+    float amax = 0.0f, mx = 0.0f;
+#pragma unroll
+    for (int t = 0; t < QK; t++) {
+        double u = 0.0;
+#pragma unroll
+        for (int j = 0; j < QK; j++) {
+            // H[t][j] = (-1)^popcount(t & j); adding +-x_j is exact per term
+            const bool neg = __builtin_popcount((unsigned)(t & j)) & 1;
+            u = __dadd_rn(u, neg ? -(double)x[j] : (double)x[j]);
+        }
+        r[t] = (float)__dmul_rn(u, kInvSqrt32d);
+        const float a = fabsf(r[t]);
+        if (a > amax) { amax = a; mx = r[t]; }
+    }
+    const float d = __fdiv_rn(mx, -8.0f);
+    const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
+    const __half dh = __float2half_rn(opaque(d));  // keeps the sign of a zero scale
+    uint8_t *dst = q4 + blk * 18;
+    const uint16_t dbits = __half_as_ushort(dh);
+    dst[0] = (uint8_t)(dbits & 0xff);
+    dst[1] = (uint8_t)(dbits >> 8);
+#pragma unroll
+    for (int j = 0; j < QK / 2; j++) {
+        int q0 = (int)__fadd_rn(__fmul_rn(r[j], id), 8.5f);
+        int q1 = (int)__fadd_rn(__fmul_rn(r[j + 16], id), 8.5f);
+        q0 = q0 > 15 ? 15 : q0;
+        q1 = q1 > 15 ? 15 : q1;
+        dst[2 + j] = (uint8_t)(q0 | (q1 << 4));
+    }
+}
+
+// One thread per (tile, block, lane): 8 code bytes (XOR 0x88) and, for lanes
+// 0..31, the column's fp16 scale.
+__global__ __launch_bounds__(256) void repack_kernel(const uint8_t *__restrict__ q4, int64_t n,
+                                                     int64_t k, uint8_t *__restrict__ packed) {
+    const int64_t nb = k / QK;
+    const int64_t tiles = padded_n(n) / TILE_N;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= tiles * nb * 64) return;
+    const int lane = (int)(gid & 63);
+    const int64_t tb = gid >> 6;  // tile * nb + b
+    const int64_t tile = tb / nb, b = tb % nb;
+    const int c = lane & 31, g = lane >> 5;
+    const int64_t col = tile * TILE_N + c;
+
+    uint32_t w0 = 0, w1 = 0;
+    uint16_t dbits = 0;
+    if (col < n) {
+        const uint8_t *blk = q4 + (col * nb + b) * 18;
+        const uint8_t *qs = blk + 2 + 8 * g;
+        w0 = (uint32_t)qs[0] | ((uint32_t)qs[1] << 8) | ((uint32_t)qs[2] << 16) | ((uint32_t)qs[3] << 24);
+        w1 = (uint32_t)qs[4] | ((uint32_t)qs[5] << 8) | ((uint32_t)qs[6] << 16) | ((uint32_t)qs[7] << 24);
+        w0 ^= 0x88888888u;
+        w1 ^= 0x88888888u;
+        dbits = (uint16_t)(blk[0] | (blk[1] << 8));
+    }
+    uint2 *codes = reinterpret_cast<uint2 *>(packed);
+    codes[tb * 64 + lane] = make_uint2(w0, w1);
+    if (g == 0) {
+        uint16_t *scales = reinterpret_cast<uint16_t *>(packed + packed_code_bytes(n, k));
+        scales[tb * TILE_SCALE_HALFS + c] = dbits;
+    }
+}
+
+}  // namespace w4a4

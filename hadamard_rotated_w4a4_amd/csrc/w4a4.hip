@@ -1,0 +1,230 @@
+// libw4a4.so: host side of the C ABI declared in include/w4a4.h.
+//
+// Every entry point validates its arguments on the host, then enqueues its
+// kernels on the caller's stream and returns; nothing here allocates, frees
+// or synchronises.
+#include "w4a4.h"
+
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+#include "k_gemm.h"
+#include "k_prep.h"
+#include "k_rotq.h"
+
+using namespace w4a4;
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+w4a4_status hip_status(const char *what) {
+    const hipError_t err = hipGetLastError();
+    if (err == hipSuccess) return W4A4_OK;
+    std::snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s", what, hipGetErrorString(err));
+    return W4A4_ERR_HIP;
+}
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+inline unsigned blocks_for(int64_t work, int per) { return (unsigned)((work + per - 1) / per); }
+
+// Dense large-M tiles: 4 waves in 2 x 2, each 64 x 64, 128 x 128 per workgroup.
+using DenseCfg = TileCfg<2, 2, 2, 2, 4>;
+// Grouped expert tiles: 32 rows (experts are small), 4 waves across 256 columns.
+using GroupedCfg = TileCfg<1, 4, 1, 2, 4>;
+
+// Row bounds that keep every grid.y within the hardware's 65535.
+constexpr int64_t kMaxGridY = 65535;
+constexpr int64_t kMaxRows = kMaxGridY * 128;
+
+w4a4_status check_gemm_common(const void *packed_w, const uint8_t *codes, const float *scales,
+                              const float *y, int64_t n, int64_t k) {
+    if (n < 0 || k < 0) return W4A4_ERR_INVALID_VALUE;
+    if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
+    if (!packed_w || !codes || !scales || !y) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(packed_w, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(y, 4))
+        return W4A4_ERR_MISALIGNED;
+    return W4A4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *w4a4_status_string(w4a4_status s) {
+    switch (s) {
+    case W4A4_OK: return "W4A4_OK";
+    case W4A4_ERR_INVALID_VALUE: return "W4A4_ERR_INVALID_VALUE";
+    case W4A4_ERR_K_NOT_MULTIPLE_OF_32: return "W4A4_ERR_K_NOT_MULTIPLE_OF_32";
+    case W4A4_ERR_MISALIGNED: return "W4A4_ERR_MISALIGNED";
+    case W4A4_ERR_UNSUPPORTED_DTYPE: return "W4A4_ERR_UNSUPPORTED_DTYPE";
+    case W4A4_ERR_WORKSPACE_TOO_SMALL: return "W4A4_ERR_WORKSPACE_TOO_SMALL";
+    case W4A4_ERR_HIP: return "W4A4_ERR_HIP";
+    }
+    return "W4A4_ERR_UNKNOWN";
+}
+
+const char *w4a4_last_hip_error(void) { return g_last_hip_error; }
+
+size_t w4a4_q4_0_bytes(int64_t n, int64_t k) {
+    if (n < 0 || k < 0 || k % QK) return 0;
+    return (size_t)(n * (k / QK) * 18);
+}
+
+size_t w4a4_packed_weight_bytes(int64_t n, int64_t k) {
+    if (n < 0 || k < 0 || k % QK) return 0;
+    return (size_t)packed_total_bytes(n, k);
+}
+
+w4a4_status w4a4_quantize_q4_0_h32(const float *w, int64_t n, int64_t k, int64_t ldw, void *q4_0,
+                                   void *stream) {
+    if (n < 0 || k < 0 || ldw < k) return W4A4_ERR_INVALID_VALUE;
+    if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
+    if (n == 0 || k == 0) return W4A4_OK;
+    if (!w || !q4_0) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(w, 4)) return W4A4_ERR_MISALIGNED;
+    const int64_t blocks = n * (k / QK);
+    quantize_q4_0_h32_kernel<<<blocks_for(blocks, 256), 256, 0, as_stream(stream)>>>(
+        w, n, k, ldw, static_cast<uint8_t *>(q4_0));
+    return hip_status("quantize_q4_0_h32_kernel");
+}
+
+w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int64_t k, void *stream) {
+    if (n < 0 || k < 0) return W4A4_ERR_INVALID_VALUE;
+    if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
+    if (n == 0 || k == 0) return W4A4_OK;
+    if (!q4_0 || !packed) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(packed, 16)) return W4A4_ERR_MISALIGNED;
+    const int64_t threads = padded_n(n) / TILE_N * (k / QK) * 64;
+    repack_kernel<<<blocks_for(threads, 256), 256, 0, as_stream(stream)>>>(
+        static_cast<const uint8_t *>(q4_0), n, k, static_cast<uint8_t *>(packed));
+    return hip_status("repack_kernel");
+}
+
+w4a4_status w4a4_rotate_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                                     uint8_t *codes, float *scales, void *stream) {
+    if (dt != W4A4_DTYPE_F32 && dt != W4A4_DTYPE_F16) return W4A4_ERR_UNSUPPORTED_DTYPE;
+    if (m < 0 || k < 0 || ldx < k || m > kMaxRows) return W4A4_ERR_INVALID_VALUE;
+    if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
+    if (m == 0 || k == 0) return W4A4_OK;
+    if (!x || !codes || !scales) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(x, dt == W4A4_DTYPE_F32 ? 4 : 2) || !aligned(codes, 16) || !aligned(scales, 4))
+        return W4A4_ERR_MISALIGNED;
+    const int64_t blocks = m * (k / QK);
+    const unsigned grid = blocks_for(blocks, 256 / QK);
+    if (dt == W4A4_DTYPE_F32)
+        rotate_quantize_kernel<float><<<grid, 256, 0, as_stream(stream)>>>(
+            static_cast<const float *>(x), m, k, ldx, codes, scales);
+    else
+        rotate_quantize_kernel<__half><<<grid, 256, 0, as_stream(stream)>>>(
+            static_cast<const __half *>(x), m, k, ldx, codes, scales);
+    return hip_status("rotate_quantize_kernel");
+}
+
+w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *scales, float *y,
+                      int64_t m, int64_t n, int64_t k, int64_t ldy, void *stream) {
+    if (m < 0 || m > kMaxRows || ldy < n) return W4A4_ERR_INVALID_VALUE;
+    if (m == 0 || n == 0) {
+        if (n < 0 || k < 0) return W4A4_ERR_INVALID_VALUE;
+        return k % QK ? W4A4_ERR_K_NOT_MULTIPLE_OF_32 : W4A4_OK;
+    }
+    const w4a4_status st = check_gemm_common(packed_w, codes, scales, y, n, k);
+    if (st != W4A4_OK) return st;
+    hipStream_t s = as_stream(stream);
+    if (k == 0) {  // empty sum
+        zero_rows_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(y, m, n, ldy);
+        return hip_status("zero_rows_kernel");
+    }
+    GemmArgs a{};
+    a.codes = codes;
+    a.scales = scales;
+    a.packed = static_cast<const uint8_t *>(packed_w);
+    a.y = y;
+    a.ldy = ldy;
+    a.m = m;
+    a.n = n;
+    a.k = k;
+    const int64_t tiles_n = padded_n(n) / TILE_N;
+    if (m <= SMALL_M_MAX) {
+        if (tiles_n >= 256)
+            gemm_small_m_kernel<8><<<(unsigned)tiles_n, 64 * 8, 0, s>>>(a);
+        else
+            gemm_small_m_kernel<16><<<(unsigned)tiles_n, 64 * 16, 0, s>>>(a);
+        return hip_status("gemm_small_m_kernel");
+    }
+    const dim3 grid((unsigned)blocks_for(n, DenseCfg::BN), (unsigned)blocks_for(m, DenseCfg::BM));
+    gemm_tiled_kernel<DenseCfg, false><<<grid, DenseCfg::NT, 0, s>>>(a);
+    return hip_status("gemm_tiled_kernel");
+}
+
+size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t top_k) {
+    if (n_expert < 0 || n_tokens < 0 || top_k < 0) return 0;
+    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+    return (size_t)(2 * up((n_expert + 1) * 4) + up(n_tokens * top_k * 4));
+}
+
+w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *codes, const float *scales,
+                         int64_t act_rows_per_token, const int32_t *ids, int64_t n_tokens, int64_t top_k,
+                         float *y, int64_t n, int64_t k, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    if (n_tokens < 0 || top_k < 0 || n_expert < 0 || n < 0 || k < 0) return W4A4_ERR_INVALID_VALUE;
+    if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
+    if (n_tokens == 0 || top_k == 0 || n == 0) return W4A4_OK;
+    if (n_expert < 1 || n_expert > ROUTE_MAX_EXPERTS) return W4A4_ERR_INVALID_VALUE;
+    if (act_rows_per_token != 1 && act_rows_per_token != top_k) return W4A4_ERR_INVALID_VALUE;
+    if (n_tokens * top_k > kMaxGridY * GroupedCfg::BM - n_expert * GroupedCfg::BM)
+        return W4A4_ERR_INVALID_VALUE;
+    if (!ids || !workspace) return W4A4_ERR_INVALID_VALUE;
+    if (k > 0) {
+        const w4a4_status st = check_gemm_common(packed_w, codes, scales, y, n, k);
+        if (st != W4A4_OK) return st;
+    } else if (!y) {
+        return W4A4_ERR_INVALID_VALUE;
+    }
+    if (!aligned(ids, 4) || !aligned(workspace, 256) || !aligned(y, 4)) return W4A4_ERR_MISALIGNED;
+    if (workspace_bytes < w4a4_gemm_id_workspace_bytes(n_expert, n_tokens, top_k))
+        return W4A4_ERR_WORKSPACE_TOO_SMALL;
+
+    hipStream_t s = as_stream(stream);
+    const int64_t n_rows = n_tokens * top_k;
+    if (k == 0) {  // empty sums: every row is zero
+        zero_rows_kernel<<<blocks_for(n_rows * n, 256), 256, 0, s>>>(y, n_rows, n, n);
+        return hip_status("zero_rows_kernel");
+    }
+    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    int32_t *offsets = reinterpret_cast<int32_t *>(ws);
+    int32_t *tile_prefix = reinterpret_cast<int32_t *>(ws + up((n_expert + 1) * 4));
+    int32_t *perm = reinterpret_cast<int32_t *>(ws + 2 * up((n_expert + 1) * 4));
+
+    route_kernel<<<1, ROUTE_THREADS, 0, s>>>(ids, (int)n_rows, (int)n_expert, GroupedCfg::BM, offsets,
+                                             tile_prefix, perm, y, n);
+    w4a4_status st = hip_status("route_kernel");
+    if (st != W4A4_OK) return st;
+
+    GemmArgs a{};
+    a.codes = codes;
+    a.scales = scales;
+    a.packed = static_cast<const uint8_t *>(packed_w);
+    a.expert_bytes = packed_total_bytes(n, k);
+    a.y = y;
+    a.ldy = n;
+    a.m = n_rows;
+    a.n = n;
+    a.k = k;
+    a.perm = perm;
+    a.offsets = offsets;
+    a.tile_prefix = tile_prefix;
+    a.n_expert = (int)n_expert;
+    a.top_k = (int)top_k;
+    a.act_rows_per_token = (int)act_rows_per_token;
+    // every expert adds at most one partial tile to the full ones
+    const int64_t max_tiles = blocks_for(n_rows, GroupedCfg::BM) + n_expert;
+    const dim3 grid((unsigned)blocks_for(n, GroupedCfg::BN), (unsigned)max_tiles);
+    gemm_tiled_kernel<GroupedCfg, true><<<grid, GroupedCfg::NT, 0, s>>>(a);
+    return hip_status("gemm_tiled_kernel<grouped>");
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+/*
+ * w4a4.h -- C ABI of libw4a4.so: the Hadamard-rotated W4A4 Q4_0 matmul on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (1bit-MONSTER engine docs, page "The lean option: ROCmFP4,
+ * ROCmI4 and Hadamard Q4_0", section "Hadamard-rotated Q4_0: W4A4 prompt
+ * processing"): weights are plain Q4_0 (blocks of 32, one fp16 scale, a code q
+ * stands for q - 8), rotated once by a normalised 32-point Walsh-Hadamard
+ * transform per 32-element block along K.  At run time every activation row is
+ * rotated by the same transform per block and rounded to 4 bits; the 4-bit
+ * activation codes are multiplied with the 4-bit weight codes in integer
+ * arithmetic and each block's integer dot is scaled into an fp32 accumulator.
+ * Section "MoE: W4A4 on the experts" of the same page: the expert matmuls
+ * (MUL_MAT_ID) take the same path.
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers unless stated otherwise.  The caller owns
+ *     every buffer; the library keeps no per-call state, never allocates,
+ *     frees or synchronises, and never writes its inputs.
+ *   - `stream` is a hipStream_t (NULL for the null stream).  Work is enqueued
+ *     on it and returns immediately; results are ready when the stream is.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     failed check returns its status and touches no device memory.  m == 0
+ *     (or n == 0, n_tokens == 0) returns W4A4_OK without a launch.
+ *   - A failed launch returns W4A4_ERR_HIP (detail: w4a4_last_hip_error()).
+ *     Faults during execution surface at the caller's next synchronisation.
+ *   - No C++ exception crosses this interface.
+ *   - K must be a multiple of 32 (one Q4_0 block).  Any m, n >= 1 works.
+ */
+#ifndef W4A4_H
+#define W4A4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A4_OK = 0,
+    W4A4_ERR_INVALID_VALUE = 1,        /* null pointer with work to do, negative size, bad stride or enum */
+    W4A4_ERR_K_NOT_MULTIPLE_OF_32 = 2, /* k % 32 != 0 */
+    W4A4_ERR_MISALIGNED = 3,           /* a pointer below its required alignment */
+    W4A4_ERR_UNSUPPORTED_DTYPE = 4,    /* activation dtype not in w4a4_dtype */
+    W4A4_ERR_WORKSPACE_TOO_SMALL = 5,  /* workspace_bytes below w4a4_gemm_id_workspace_bytes() */
+    W4A4_ERR_HIP = 6                   /* a HIP runtime call failed */
+} w4a4_status;
+
+typedef enum { W4A4_DTYPE_F32 = 0, W4A4_DTYPE_F16 = 1 } w4a4_dtype;
+
+/* Human-readable name of a status.  Host only; never NULL. */
+const char *w4a4_status_string(w4a4_status s);
+
+/* Detail of the last W4A4_ERR_HIP on the calling thread ("" if none).  Host only. */
+const char *w4a4_last_hip_error(void);
+
+/* Bytes of a Q4_0 matrix [n][k/32] x 18-byte blocks.  Host only, pure. */
+size_t w4a4_q4_0_bytes(int64_t n, int64_t k);
+
+/*
+ * Offline weight preparation (the step the page's tools/hadamard_q4_0.py does
+ * on a model file): rotate each 32-block of each row of an fp32 weight matrix
+ * by H/sqrt(32) and quantise the result to Q4_0.
+ *   w     fp32 [n][ldw], ldw >= k (elements); 4-byte aligned.
+ *   q4_0  out, [n][k/32] blocks of 18 bytes: fp16 scale d (little endian)
+ *         then 16 bytes, byte j = code of element j (low nibble) | code of
+ *         element j+16 (high nibble) << 4; codes 0..15 stand for q - 8.
+ * Arithmetic: per element, the sum over j of +-w_j in fp64 in ascending j,
+ * times fp64(1/sqrt(32)), rounded to fp32; then d = mx / -8 with mx the
+ * element of largest magnitude (first on ties), q = min(15, trunc(w/d' +
+ * 8.5)) with w/d' formed as w * (1/d) in fp32, d stored as fp16 (nearest even).
+ */
+w4a4_status w4a4_quantize_q4_0_h32(const float *w, int64_t n, int64_t k, int64_t ldw,
+                                   void *q4_0, void *stream);
+
+/* Bytes of the packed weight buffer w4a4_repack_q4_0_h32 writes.  Host only, pure. */
+size_t w4a4_packed_weight_bytes(int64_t n, int64_t k);
+
+/*
+ * One-time, lossless re-layout of H32-rotated Q4_0 weights for the GEMMs.
+ *   q4_0    [n][k/32] x 18 B, as above (any alignment).  The `_h32` in the
+ *           name is the caller's assertion that the weights were rotated:
+ *           unrotated weights give silently wrong products.
+ *   packed  out, w4a4_packed_weight_bytes(n, k) bytes, 256-byte aligned.  Its
+ *           layout is private to this library.  Each code is stored as q ^ 8,
+ *           which read as a signed nibble is exactly q - 8 (the page's
+ *           identity), so the weights stay exact.
+ */
+w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int64_t k,
+                                 void *stream);
+
+/*
+ * Rotate and quantise activations, one 32-element block at a time:
+ * unnormalised fast Walsh-Hadamard butterflies in fp32 (stages 1, 2, 4, 8,
+ * 16), amax = max |v|, d = amax / 7, codes = clamp(round-half-away(v *
+ * (1/d)), -7, 7), stored scale s = d * fp32(1/sqrt(32)).  A block with d below
+ * FLT_MIN stores zero codes and s = 0.
+ *   x       [m][ldx] fp32 or fp16 (dt), ldx >= k; 4-byte (fp32) or 2-byte
+ *           (fp16) aligned.  Non-finite values are outside the contract.
+ *   codes   out, [m][k/2] bytes, 16-byte aligned: byte 16b + j holds the
+ *           code of element 32b + j in its low nibble and of element
+ *           32b + j + 16 in its high nibble, two's complement.
+ *   scales  out, [m][k/32] fp32, 4-byte aligned.
+ */
+w4a4_status w4a4_rotate_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k,
+                                     int64_t ldx, uint8_t *codes, float *scales, void *stream);
+
+/*
+ * Dense W4A4 product: y[i][j] = sum_b d_w[j][b] * s[i][b] * S[i][j][b], where
+ * S = sum_t (q_w - 8) * q_a is the exact integer dot of block b (int8 matrix
+ * cores), accumulated in fp32 (block order ascending within a thread).
+ *   packed_w  from w4a4_repack_q4_0_h32(n, k).
+ *   codes, scales  from w4a4_rotate_quantize_act (m rows).
+ *   y         out, [m][ldy] fp32, ldy >= n, 4-byte aligned.
+ * m <= 16 takes a weight-streaming kernel; larger m a tiled MFMA kernel.
+ */
+w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *scales, float *y,
+                      int64_t m, int64_t n, int64_t k, int64_t ldy, void *stream);
+
+/* Workspace bytes w4a4_gemm_id needs.  Host only, pure. */
+size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t top_k);
+
+/*
+ * MUL_MAT_ID: expert-routed W4A4 product (section "MoE: W4A4 on the experts").
+ *   packed_w  n_expert consecutive packed buffers of w4a4_packed_weight_bytes(n, k).
+ *   codes, scales  activation rows: n_tokens of them when act_rows_per_token
+ *             == 1 (every slot of token t reads row t), n_tokens * top_k when
+ *             act_rows_per_token == top_k (slot j of token t reads row
+ *             t * top_k + j).
+ *   ids       [n_tokens][top_k] int32 expert indices.  An id outside
+ *             [0, n_expert) yields a zero output row (defined behaviour).
+ *   y         out, [n_tokens][top_k][n] fp32.
+ *   workspace device scratch of w4a4_gemm_id_workspace_bytes() bytes,
+ *             256-byte aligned; contents on entry are ignored.
+ * Supports n_expert <= 8192.
+ */
+w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *codes,
+                         const float *scales, int64_t act_rows_per_token, const int32_t *ids,
+                         int64_t n_tokens, int64_t top_k, float *y, int64_t n, int64_t k,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A4_H */

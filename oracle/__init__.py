@@ -52,11 +52,11 @@ def _load():
         lib.oracle_half_to_float.restype = ctypes.c_float
         lib.oracle_float_to_half.argtypes = [ctypes.c_float]
         lib.oracle_float_to_half.restype = ctypes.c_uint16
-        lib.oracle_rotate_weights.argtypes = [P, I64, I64, P]
-        lib.oracle_q4_0_quantize.argtypes = [P, I64, I64, P]
+        lib.oracle_rotate_weights.argtypes = [P, I64, I64, P, ctypes.c_int]
+        lib.oracle_q4_0_quantize.argtypes = [P, I64, I64, P, ctypes.c_int]
         lib.oracle_q4_0_dequantize.argtypes = [P, I64, I64, P]
         lib.oracle_fwht32_f32.argtypes = [P]
-        lib.oracle_rotate_quantize_act.argtypes = [P, ctypes.c_int, I64, I64, I64, P, P]
+        lib.oracle_rotate_quantize_act.argtypes = [P, ctypes.c_int, I64, I64, I64, P, P, ctypes.c_int]
         lib.oracle_block_sums.argtypes = [P, P, I64, I64, I64, P]
         lib.oracle_gemm.argtypes = [P, P, P, I64, I64, I64, P, I64, ctypes.c_int]
         lib.oracle_gemm_id.argtypes = [P, I64, P, P, I64, P, I64, I64, I64, I64, P, ctypes.c_int]
@@ -99,23 +99,23 @@ def float_to_half(x) -> int:
     return int(_load().oracle_float_to_half(float(np.float32(x))))
 
 
-def rotate_weights(w: np.ndarray) -> np.ndarray:
+def rotate_weights(w: np.ndarray, threads: int | None = None) -> np.ndarray:
     """fp32 [n, k] -> fp32 [n, k], each 32-block multiplied by H/sqrt(32) (fp64 sum)."""
     w = np.ascontiguousarray(w, np.float32)
     n, k = w.shape
     assert k % QK == 0
     out = np.empty_like(w)
-    _load().oracle_rotate_weights(_ptr(w), n, k, _ptr(out))
+    _load().oracle_rotate_weights(_ptr(w), n, k, _ptr(out), threads or default_threads())
     return out
 
 
-def q4_0_quantize(wr: np.ndarray) -> np.ndarray:
+def q4_0_quantize(wr: np.ndarray, threads: int | None = None) -> np.ndarray:
     """fp32 [n, k] -> Q4_0 bytes [n, k/32, 18]."""
     wr = np.ascontiguousarray(wr, np.float32)
     n, k = wr.shape
     assert k % QK == 0
     out = np.empty((n, k // QK, 18), np.uint8)
-    _load().oracle_q4_0_quantize(_ptr(wr), n, k, _ptr(out))
+    _load().oracle_q4_0_quantize(_ptr(wr), n, k, _ptr(out), threads or default_threads())
     return out
 
 
@@ -127,9 +127,9 @@ def q4_0_dequantize(q4: np.ndarray, k: int) -> np.ndarray:
     return out
 
 
-def prepare_weights(w: np.ndarray) -> np.ndarray:
+def prepare_weights(w: np.ndarray, threads: int | None = None) -> np.ndarray:
     """Offline step: rotate fp32 weights per 32-block, then Q4_0-quantise."""
-    return q4_0_quantize(rotate_weights(w))
+    return q4_0_quantize(rotate_weights(w, threads), threads)
 
 
 def fwht32_f32(v: np.ndarray) -> np.ndarray:
@@ -138,7 +138,7 @@ def fwht32_f32(v: np.ndarray) -> np.ndarray:
     return v
 
 
-def rotate_quantize_act(x: np.ndarray, k: int | None = None):
+def rotate_quantize_act(x: np.ndarray, k: int | None = None, threads: int | None = None):
     """x fp32 or fp16 [m, ldx] -> (codes uint8 [m, k/2], scales fp32 [m, k/32])."""
     assert x.dtype in (np.float32, np.float16)
     x = np.ascontiguousarray(x)
@@ -148,7 +148,8 @@ def rotate_quantize_act(x: np.ndarray, k: int | None = None):
     codes = np.empty((m, k // 2), np.uint8)
     scales = np.empty((m, k // QK), np.float32)
     dtype = 0 if x.dtype == np.float32 else 1
-    _load().oracle_rotate_quantize_act(_ptr(x), dtype, m, k, ldx, _ptr(codes), _ptr(scales))
+    _load().oracle_rotate_quantize_act(_ptr(x), dtype, m, k, ldx, _ptr(codes), _ptr(scales),
+                                       threads or default_threads())
     return codes, scales
 
 

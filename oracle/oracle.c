@@ -62,6 +62,44 @@
 
 #define QK 32
 
+/* Run fn(ctx, r0, r1) over [0, n) split into contiguous row ranges, one per
+ * thread.  Rows are independent, so the split changes no arithmetic. */
+typedef void (*row_range_fn)(void *ctx, int64_t r0, int64_t r1);
+typedef struct {
+    row_range_fn fn;
+    void *ctx;
+    int64_t r0, r1;
+} row_range_job;
+
+static void *row_range_worker(void *p)
+{
+    row_range_job *j = (row_range_job *)p;
+    j->fn(j->ctx, j->r0, j->r1);
+    return NULL;
+}
+
+static void parallel_rows(int64_t n, int nthreads, row_range_fn fn, void *ctx)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > n)
+        nthreads = (int)(n > 0 ? n : 1);
+    if (nthreads == 1) {
+        fn(ctx, 0, n);
+        return;
+    }
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    row_range_job *jobs = (row_range_job *)calloc((size_t)nthreads, sizeof(row_range_job));
+    for (int t = 0; t < nthreads; t++) {
+        jobs[t] = (row_range_job){fn, ctx, n * t / nthreads, n * (t + 1) / nthreads};
+        pthread_create(&th[t], NULL, row_range_worker, &jobs[t]);
+    }
+    for (int t = 0; t < nthreads; t++)
+        pthread_join(th[t], NULL);
+    free(th);
+    free(jobs);
+}
+
 /* ------------------------------------------------------------------ */
 /* Hadamard matrix (R1)                                                */
 /* ------------------------------------------------------------------ */
@@ -143,15 +181,22 @@ uint16_t oracle_float_to_half(float f)
 /* ------------------------------------------------------------------ */
 
 /* wr[r][32b + t] = fp32( (sum_j H[t][j] * w[r][32b + j]) * c64 ), sum in fp64. */
-void oracle_rotate_weights(const float *w, int64_t n, int64_t k, float *wr)
+typedef struct {
+    const float *w;
+    int64_t k;
+    float *wr;
+} rotate_ctx;
+
+static void rotate_rows(void *p, int64_t r0, int64_t r1)
 {
+    rotate_ctx *c = (rotate_ctx *)p;
     int32_t H[QK * QK];
     oracle_h32(H);
     const double c64 = oracle_c64();
-    for (int64_t r = 0; r < n; r++) {
-        for (int64_t b = 0; b < k / QK; b++) {
-            const float *src = w + r * k + b * QK;
-            float *dst = wr + r * k + b * QK;
+    for (int64_t r = r0; r < r1; r++) {
+        for (int64_t b = 0; b < c->k / QK; b++) {
+            const float *src = c->w + r * c->k + b * QK;
+            float *dst = c->wr + r * c->k + b * QK;
             for (int t = 0; t < QK; t++) {
                 double u = 0.0;
                 for (int j = 0; j < QK; j++)
@@ -162,10 +207,26 @@ void oracle_rotate_weights(const float *w, int64_t n, int64_t k, float *wr)
     }
 }
 
-/* Q4_0-quantise rows of fp32 values (R3).  q4 gets n * (k/32) blocks of 18 B. */
-void oracle_q4_0_quantize(const float *wr, int64_t n, int64_t k, uint8_t *q4)
+void oracle_rotate_weights(const float *w, int64_t n, int64_t k, float *wr, int nthreads)
 {
-    for (int64_t r = 0; r < n; r++) {
+    rotate_ctx c = {w, k, wr};
+    parallel_rows(n, nthreads, rotate_rows, &c);
+}
+
+/* Q4_0-quantise rows of fp32 values (R3).  q4 gets n * (k/32) blocks of 18 B. */
+typedef struct {
+    const float *wr;
+    int64_t k;
+    uint8_t *q4;
+} q4_ctx;
+
+static void q4_rows(void *p, int64_t r0, int64_t r1)
+{
+    q4_ctx *c = (q4_ctx *)p;
+    const float *wr = c->wr;
+    const int64_t k = c->k;
+    uint8_t *q4 = c->q4;
+    for (int64_t r = r0; r < r1; r++) {
         for (int64_t b = 0; b < k / QK; b++) {
             const float *x = wr + r * k + b * QK;
             uint8_t *blk = q4 + (r * (k / QK) + b) * 18;
@@ -192,6 +253,12 @@ void oracle_q4_0_quantize(const float *wr, int64_t n, int64_t k, uint8_t *q4)
             }
         }
     }
+}
+
+void oracle_q4_0_quantize(const float *wr, int64_t n, int64_t k, uint8_t *q4, int nthreads)
+{
+    q4_ctx c = {wr, k, q4};
+    parallel_rows(n, nthreads, q4_rows, &c);
 }
 
 /* Code t (0..15) of a Q4_0 block, and its value d * (q - 8). */
@@ -269,30 +336,45 @@ static float quantize_block(const float *v, int8_t *q)
     return d * oracle_c32();
 }
 
+typedef struct {
+    const void *x;
+    int dtype;
+    int64_t k, ldx;
+    uint8_t *codes;
+    float *scales;
+} act_ctx;
+
+static void act_rows(void *p, int64_t r0, int64_t r1)
+{
+    act_ctx *c = (act_ctx *)p;
+    const int64_t k = c->k, nb = k / QK;
+    for (int64_t r = r0; r < r1; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            float v[QK];
+            for (int t = 0; t < QK; t++) {
+                int64_t idx = r * c->ldx + b * QK + t;
+                v[t] = c->dtype == 0 ? ((const float *)c->x)[idx]
+                                     : oracle_half_to_float(((const uint16_t *)c->x)[idx]);
+            }
+            oracle_fwht32_f32(v);
+            int8_t q[QK];
+            c->scales[r * nb + b] = quantize_block(v, q);
+            uint8_t *dst = c->codes + r * (k / 2) + b * 16;
+            for (int j = 0; j < 16; j++)
+                dst[j] = (uint8_t)(((uint8_t)q[j] & 0x0f) | (((uint8_t)q[j + 16] & 0x0f) << 4));
+        }
+    }
+}
+
 /*
  * x: [m][ldx] elements, fp32 (dtype 0) or fp16 bits (dtype 1).
  * codes: [m][k/2] bytes, scales: [m][k/32].
  */
 void oracle_rotate_quantize_act(const void *x, int dtype, int64_t m, int64_t k, int64_t ldx,
-                                uint8_t *codes, float *scales)
+                                uint8_t *codes, float *scales, int nthreads)
 {
-    const int64_t nb = k / QK;
-    for (int64_t r = 0; r < m; r++) {
-        for (int64_t b = 0; b < nb; b++) {
-            float v[QK];
-            for (int t = 0; t < QK; t++) {
-                int64_t idx = r * ldx + b * QK + t;
-                v[t] = dtype == 0 ? ((const float *)x)[idx]
-                                  : oracle_half_to_float(((const uint16_t *)x)[idx]);
-            }
-            oracle_fwht32_f32(v);
-            int8_t q[QK];
-            scales[r * nb + b] = quantize_block(v, q);
-            uint8_t *dst = codes + r * (k / 2) + b * 16;
-            for (int j = 0; j < 16; j++)
-                dst[j] = (uint8_t)(((uint8_t)q[j] & 0x0f) | (((uint8_t)q[j + 16] & 0x0f) << 4));
-        }
-    }
+    act_ctx c = {x, dtype, k, ldx, codes, scales};
+    parallel_rows(m, nthreads, act_rows, &c);
 }
 
 /* Signed int4 code t (-8..7) of an activation block. */

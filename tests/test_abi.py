@@ -1,0 +1,126 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+symbol include/w4a4.h declares, and rejects bad arguments on the host before
+anything is launched (fake device pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a4.h")
+
+OK, INVALID, KMUL, MISALIGNED, DTYPE, WS, HIP = range(7)
+
+
+@pytest.fixture(scope="module")
+def L():
+    from hadamard_rotated_w4a4_amd import _lib
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code, name in enumerate(["W4A4_OK", "W4A4_ERR_INVALID_VALUE", "W4A4_ERR_K_NOT_MULTIPLE_OF_32",
+                                 "W4A4_ERR_MISALIGNED", "W4A4_ERR_UNSUPPORTED_DTYPE",
+                                 "W4A4_ERR_WORKSPACE_TOO_SMALL", "W4A4_ERR_HIP"]):
+        assert L.w4a4_status_string(code).decode() == name
+    assert L.w4a4_last_hip_error().decode() == ""
+
+
+def test_size_queries(L):
+    assert L.w4a4_q4_0_bytes(17408, 5120) == 17408 * 160 * 18
+    # packed = 32-column tiles x blocks x (512 code bytes + 32 fp16 scales)
+    assert L.w4a4_packed_weight_bytes(17408, 5120) == 17408 * 160 * 18
+    assert L.w4a4_packed_weight_bytes(33, 64) == 64 * 2 * 18  # n padded to 64
+    assert L.w4a4_packed_weight_bytes(10, 33) == 0
+    assert L.w4a4_gemm_id_workspace_bytes(128, 1024, 8) == 2 * 768 + 32768
+    assert L.w4a4_gemm_id_workspace_bytes(-1, 1, 1) == 0
+
+
+A = 0x10000000          # fake, aligned device addresses: never dereferenced
+ODD = 0x10000001
+
+
+def P(x):
+    return ctypes.c_void_p(x)
+
+
+def test_gemm_validation(L):
+    g = L.w4a4_gemm
+    assert g(P(A), P(A), P(A), P(A), 64, 64, 33, 64, None) == KMUL
+    assert g(P(A), P(A), P(A), P(A), -1, 64, 64, 64, None) == INVALID
+    assert g(P(A), P(A), P(A), P(A), 8, -1, 64, 64, None) == INVALID
+    assert g(P(A), P(A), P(A), P(A), 8, 64, 64, 63, None) == INVALID  # ldy < n
+    assert g(None, P(A), P(A), P(A), 8, 64, 64, 64, None) == INVALID
+    assert g(P(A), None, P(A), P(A), 8, 64, 64, 64, None) == INVALID
+    assert g(P(A), P(A), None, P(A), 8, 64, 64, 64, None) == INVALID
+    assert g(P(A), P(A), P(A), None, 8, 64, 64, 64, None) == INVALID
+    assert g(P(A), P(A + 8), P(A), P(A), 8, 64, 64, 64, None) == MISALIGNED  # codes need 16 B
+    assert g(P(A + 8), P(A), P(A), P(A), 8, 64, 64, 64, None) == MISALIGNED  # packed needs 16 B
+    assert g(P(A), P(A), P(ODD), P(A), 8, 64, 64, 64, None) == MISALIGNED
+    assert g(P(A), P(A), P(A), P(A + 2), 8, 64, 64, 64, None) == MISALIGNED
+    # nothing to do: no launch, no pointer needed
+    assert g(None, None, None, None, 0, 64, 64, 64, None) == OK
+    assert g(None, None, None, None, 8, 0, 64, 0, None) == OK
+
+
+def test_rotate_quantize_validation(L):
+    f = L.w4a4_rotate_quantize_act
+    assert f(P(A), 2, 4, 64, 64, P(A), P(A), None) == DTYPE
+    assert f(P(A), 1, 4, 48, 64, P(A), P(A), None) == KMUL
+    assert f(P(A), 1, 4, 64, 32, P(A), P(A), None) == INVALID  # ldx < k
+    assert f(P(A), 1, -4, 64, 64, P(A), P(A), None) == INVALID
+    assert f(None, 1, 4, 64, 64, P(A), P(A), None) == INVALID
+    assert f(P(ODD), 1, 4, 64, 64, P(A), P(A), None) == MISALIGNED
+    assert f(P(A + 2), 0, 4, 64, 64, P(A), P(A), None) == MISALIGNED  # fp32 needs 4 B
+    assert f(P(A), 1, 4, 64, 64, P(A + 4), P(A), None) == MISALIGNED
+    assert f(None, 1, 0, 64, 64, None, None, None) == OK
+
+
+def test_prep_validation(L):
+    q = L.w4a4_quantize_q4_0_h32
+    assert q(P(A), 4, 40, 40, P(A), None) == KMUL
+    assert q(P(A), 4, 64, 32, P(A), None) == INVALID
+    assert q(P(ODD), 4, 64, 64, P(A), None) == MISALIGNED
+    assert q(None, 0, 64, 64, None, None) == OK
+    r = L.w4a4_repack_q4_0_h32
+    assert r(P(A), P(A), 4, 40, None) == KMUL
+    assert r(P(A), P(A + 8), 4, 64, None) == MISALIGNED
+    assert r(None, P(A), 4, 64, None) == INVALID
+    assert r(None, None, 0, 64, None) == OK
+
+
+def test_gemm_id_validation(L):
+    f = L.w4a4_gemm_id
+    ws = L.w4a4_gemm_id_workspace_bytes(4, 8, 2)
+    args = dict(packed=P(A), E=4, codes=P(A), scales=P(A), arpt=1, ids=P(A), T=8, top_k=2,
+                y=P(A), n=64, k=64, ws=P(A), wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["packed"], a["E"], a["codes"], a["scales"], a["arpt"], a["ids"], a["T"], a["top_k"],
+                 a["y"], a["n"], a["k"], a["ws"], a["wsb"], None)
+
+    assert call(k=40) == KMUL
+    assert call(arpt=3) == INVALID
+    assert call(E=0) == INVALID
+    assert call(E=9000) == INVALID
+    assert call(ids=None) == INVALID
+    assert call(ws=None) == INVALID
+    assert call(wsb=ws - 1) == WS
+    assert call(ws=P(A + 16)) == MISALIGNED
+    assert call(ids=P(A + 2)) == MISALIGNED
+    assert call(T=0, packed=None, codes=None, scales=None, ids=None, y=None, ws=None) == OK

@@ -1,0 +1,369 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: bit-exact for the Q4_0 bytes, activation codes and scales, and for the
+integer block sums (checked through the public ABI with unit and one-hot block
+scales, where every fp32 partial sum is an exact integer); fp32 outputs within
+max|err| <= 2e-3 * max|ref| per row.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from hadamard_rotated_w4a4_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from hadamard_rotated_w4a4_amd import _lib
+    _lib.lib()
+    return _lib
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def assert_rows_close(y, ref, what=""):
+    err = np.abs(y.astype(np.float64) - ref.astype(np.float64)).max(axis=-1)
+    bound = TOL * np.abs(ref.astype(np.float64)).max(axis=-1)
+    bad = np.nonzero(err > bound)
+    assert bad[0].size == 0, (f"{what}: {bad[0].size} rows outside tolerance; worst err "
+                              f"{err.max():.3e} vs bound {bound[np.argmax(err - bound)]:.3e}")
+
+
+def with_unit_scales(q4):
+    """Same codes, every weight scale fp16 1.0."""
+    q = q4.copy()
+    q[..., 0:2] = np.frombuffer(np.float16(1.0).tobytes(), np.uint8)
+    return q
+
+
+def with_one_hot_scales(q4, b0):
+    q = q4.copy()
+    q[..., 0:2] = 0
+    q[..., b0, 0:2] = np.frombuffer(np.float16(1.0).tobytes(), np.uint8)
+    return q
+
+
+# --------------------------------------------------------------------------
+# offline weight preparation: rotated Q4_0 bytes, bit-exact
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k,pad", [(256, 256, 0), (33, 96, 0), (7, 32, 5), (1, 288, 32)])
+def test_quantize_q4_0_h32_bit_exact(ops, n, k, pad):
+    say(f"quantize_q4_0_h32 n={n} k={k} pad={pad}")
+    w = synth.weights(n, k + pad, np.random.default_rng(n * 1000 + k))
+    q4 = host(ops.quantize_q4_0_h32(dev(w)[:, :k]))
+    assert np.array_equal(q4, oracle.prepare_weights(np.ascontiguousarray(w[:, :k])))
+
+
+def test_quantize_q4_0_h32_ffn_up_full(ops):
+    d = synth.ffn_up(m=1)
+    say(f"quantize_q4_0_h32 full {d.n}x{d.k}")
+    q4 = host(ops.quantize_q4_0_h32(dev(d.w)))
+    assert np.array_equal(q4, oracle.prepare_weights(d.w))
+
+
+def test_quantize_special_blocks(ops):
+    w = np.zeros((6, 64), np.float32)
+    w[1, :32] = 0.5            # constant block -> one nonzero rotated value
+    w[2, 3] = -7.0             # one-hot
+    w[3, :] = 1e-30            # tiny
+    w[4, :] = np.linspace(-1, 1, 64)
+    w[5, 32:] = 3e4
+    say("quantize_q4_0_h32 special blocks")
+    assert np.array_equal(host(ops.quantize_q4_0_h32(dev(w))), oracle.prepare_weights(w))
+
+
+# --------------------------------------------------------------------------
+# activation rotate + quantise: codes and scales bit-exact
+# --------------------------------------------------------------------------
+
+def test_rotate_quantize_tiny_fp32(ops):
+    d = synth.tiny()
+    say("rotate_quantize tiny fp32")
+    c, s = ops.rotate_quantize_act(dev(d.x))
+    rc, rs = oracle.rotate_quantize_act(d.x)
+    assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs)
+
+
+def test_rotate_quantize_ffn_up_fp16(ops):
+    d = synth.ffn_up()
+    say("rotate_quantize 512x5120 fp16")
+    c, s = ops.rotate_quantize_act(dev(d.x))
+    rc, rs = oracle.rotate_quantize_act(d.x)
+    assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs)
+
+
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+def test_rotate_quantize_strided_and_ragged(ops, dtype):
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((7, 160)) * 3).astype(dtype)
+    say(f"rotate_quantize strided {dtype.__name__}")
+    c, s = ops.rotate_quantize_act(dev(x), k=96)
+    rc, rs = oracle.rotate_quantize_act(x, k=96)
+    assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs)
+
+
+def test_rotate_quantize_edge_blocks(ops):
+    rng = np.random.default_rng(22)
+    x = np.zeros((8, 128), np.float32)
+    x[1] = 1e-44                                     # subnormal: zero block
+    x[2, :32] = 0.37                                 # constant block
+    x[3, 5] = -20.0                                  # one-hot outlier
+    x[4] = rng.standard_normal(128) * 1e-30
+    x[5] = rng.standard_normal(128) * 1e30
+    v = np.zeros(32); v[:8] = [7, 2.5, -2.5, 0.5, -0.5, 3.5, -1.25, 6.5]  # exact ties
+    import scipy.linalg
+    x[6, :32] = (scipy.linalg.hadamard(32) @ v / 32).astype(np.float32)
+    x[7] = rng.integers(-3, 4, 128).astype(np.float32) * 0.25  # many ties after scaling
+    say("rotate_quantize edge blocks")
+    c, s = ops.rotate_quantize_act(dev(x))
+    rc, rs = oracle.rotate_quantize_act(x)
+    assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs)
+
+
+def test_rotate_quantize_many_random_blocks(ops):
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal((256, 4096)) * rng.uniform(0.01, 100, (256, 1))).astype(np.float16)
+    x[:, rng.choice(4096, 41, replace=False)] *= np.float16(20)
+    say("rotate_quantize 1M elements fp16")
+    c, s = ops.rotate_quantize_act(dev(x))
+    rc, rs = oracle.rotate_quantize_act(x)
+    assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs)
+
+
+# --------------------------------------------------------------------------
+# GEMM: integer block sums exact (fed the oracle's codes), fp32 within tolerance
+# --------------------------------------------------------------------------
+
+SHAPES = [(64, 256, 256), (1, 32, 32), (5, 33, 96), (16, 100, 288), (17, 64, 64),
+          (33, 257, 160), (130, 96, 320), (300, 200, 128), (16, 1024, 5120)]
+
+
+def _problem(m, n, k, seed):
+    rng = np.random.default_rng(seed)
+    w = synth.weights(n, k, rng)
+    x = synth.activations(m, k, rng, max(1, k // 100))
+    return w, x
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_gemm_integer_unit_scales(ops, m, n, k):
+    w, x = _problem(m, n, k, m + n + k)
+    q4 = with_unit_scales(oracle.prepare_weights(w))
+    rc, _ = oracle.rotate_quantize_act(x)
+    ones = np.ones((m, k // 32), np.float32)
+    say(f"gemm integer unit scales m={m} n={n} k={k}")
+    packed = ops.repack_q4_0_h32(dev(q4), n, k)
+    y = host(ops.gemm(packed, dev(rc), dev(ones), n, k))
+    ref = oracle.gemm(q4, rc, ones, k)  # = sum_b S, an exact integer
+    assert np.array_equal(y, ref)
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 256, 256), (16, 100, 288), (130, 96, 320)])
+def test_gemm_integer_one_hot_block(ops, m, n, k):
+    w, x = _problem(m, n, k, 7 * m + n)
+    q4 = oracle.prepare_weights(w)
+    rc, _ = oracle.rotate_quantize_act(x)
+    ones = np.ones((m, k // 32), np.float32)
+    S = oracle.block_sums(q4, rc, k)
+    for b0 in range(k // 32):
+        say(f"gemm one-hot block {b0} m={m} n={n} k={k}")
+        q = with_one_hot_scales(q4, b0)
+        y = host(ops.gemm(ops.repack_q4_0_h32(dev(q), n, k), dev(rc), dev(ones), n, k))
+        assert np.array_equal(y, S[:, :, b0].astype(np.float32))
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_gemm_end_to_end(ops, m, n, k):
+    w, x = _problem(m, n, k, 3 * m + n + k)
+    say(f"gemm end-to-end m={m} n={n} k={k}")
+    packed = ops.prepare_weights(dev(w))
+    c, s = ops.rotate_quantize_act(dev(x))
+    y = host(ops.gemm(packed, c, s, n, k))
+    q4 = oracle.prepare_weights(w)
+    rc, rs = oracle.rotate_quantize_act(x)
+    assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs)
+    assert_rows_close(y, oracle.gemm(q4, rc, rs, k), f"m={m} n={n} k={k}")
+
+
+def test_gemm_output_stride_and_determinism(ops):
+    m, n, k = 40, 70, 128
+    w, x = _problem(m, n, k, 5)
+    packed = ops.prepare_weights(dev(w))
+    c, s = ops.rotate_quantize_act(dev(x))
+    say("gemm ldy > n, twice")
+    ybig = torch.full((m, 100), 7.0, device="cuda")
+    ops.gemm(packed, c, s, n, k, y=ybig[:, :n])
+    y1 = host(ybig)
+    assert np.all(y1[:, n:] == 7.0)  # columns past n untouched
+    y2 = host(ops.gemm(packed, c, s, n, k))
+    assert np.array_equal(y1[:, :n], y2)
+
+
+def test_gemm_degenerate(ops):
+    say("gemm m=0 and k=0")
+    packed = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    codes = torch.zeros((0, 16), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((0, 1), dtype=torch.float32, device="cuda")
+    y = ops.gemm(packed, codes, scales, 8, 32)
+    assert y.shape == (0, 8)
+    codes = torch.zeros((3, 1), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((3, 1), dtype=torch.float32, device="cuda")
+    y = torch.full((3, 8), 5.0, device="cuda")
+    ops.gemm(packed, codes, scales, 8, 0, y=y)
+    assert not host(y).any()
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times
+# --------------------------------------------------------------------------
+
+def test_ffn_up_full_size_sampled_rows(ops):
+    d = synth.ffn_up()
+    say(f"{d.name}: full GEMM, sampled rows vs oracle")
+    packed = ops.prepare_weights(dev(d.w))
+    c, s = ops.rotate_quantize_act(dev(d.x))
+    y = host(ops.gemm(packed, c, s, d.n, d.k))
+    rc, rs = oracle.rotate_quantize_act(d.x)
+    assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs)
+    q4 = oracle.prepare_weights(d.w)
+    rows = np.array([0, 1, 127, 128, 255, 300, 383, 511])
+    ref = oracle.gemm(q4, rc[rows], rs[rows], d.k)
+    assert_rows_close(y[rows], ref, d.name)
+    # integer sums of the same rows, fed the oracle's codes with unit scales
+    q1 = with_unit_scales(q4)
+    ones = np.ones_like(rs)
+    yi = host(ops.gemm(ops.repack_q4_0_h32(dev(q1), d.n, d.k), dev(rc), dev(ones), d.n, d.k))
+    assert np.array_equal(yi[rows], oracle.gemm(q1, rc[rows], ones[rows], d.k))
+
+
+@pytest.mark.parametrize("name,k,n", synth.DENSE_PROJECTIONS)
+def test_verify_block_m16_projection(ops, name, k, n):
+    """16-token verify batch, each projection of the dense layer, all outputs."""
+    w = synth.weights(n, k, synth.rng_for(0, 4, k + n))
+    x = synth.activations(16, k, synth.rng_for(0, 4, 7 * k + n), synth.outlier_count(k))
+    say(f"m=16 projection {name} {k}->{n}")
+    packed = ops.prepare_weights(dev(w))
+    c, s = ops.rotate_quantize_act(dev(x))
+    y = host(ops.gemm(packed, c, s, n, k))
+    q4 = oracle.prepare_weights(w)
+    rc, rs = oracle.rotate_quantize_act(x)
+    assert_rows_close(y, oracle.gemm(q4, rc, rs, k), name)
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 8, 15, 16])
+def test_small_m_ragged_rows(ops, m):
+    k, n = 1024, 300
+    w, x = _problem(m, n, k, 100 + m)
+    say(f"small-m m={m}")
+    packed = ops.prepare_weights(dev(w))
+    c, s = ops.rotate_quantize_act(dev(x))
+    y = host(ops.gemm(packed, c, s, n, k))
+    assert_rows_close(y, oracle.gemm(oracle.prepare_weights(w), *oracle.rotate_quantize_act(x), k))
+
+
+def test_last_microbatch_302_rows(ops):
+    k, n = 6144, 5120  # the output projection
+    w = synth.weights(n, k, synth.rng_for(0, 3, 3))
+    x = synth.layer_inputs(302, microbatch=3)["attn_out"]
+    say("m=302 o-proj 6144->5120, sampled rows")
+    packed = ops.prepare_weights(dev(w))
+    c, s = ops.rotate_quantize_act(dev(x))
+    y = host(ops.gemm(packed, c, s, n, k))
+    rows = np.array([0, 31, 32, 150, 255, 256, 290, 301])
+    rc, rs = oracle.rotate_quantize_act(x)
+    assert_rows_close(y[rows], oracle.gemm(oracle.prepare_weights(w), rc[rows], rs[rows], k))
+
+
+# --------------------------------------------------------------------------
+# MUL_MAT_ID
+# --------------------------------------------------------------------------
+
+def _moe_small(seed, E=6, T=11, top_k=3, n=70, k=96, bad_ids=True):
+    rng = np.random.default_rng(seed)
+    we = [synth.weights(n, k, rng) for _ in range(E)]
+    ids = np.stack([rng.choice(E, top_k, replace=False) for _ in range(T)]).astype(np.int32)
+    if bad_ids:
+        ids[2, 1] = E + 1
+        ids[5, 0] = -3
+    return we, ids, rng
+
+
+@pytest.mark.parametrize("rows_per_token", [1, 3])
+def test_gemm_id_small_end_to_end(ops, rows_per_token):
+    E, T, top_k, n, k = 6, 11, 3, 70, 96
+    we, ids, rng = _moe_small(1 + rows_per_token)
+    x = synth.activations(T * rows_per_token, k, rng, 2)
+    say(f"gemm_id small rows_per_token={rows_per_token}")
+    packed = torch.cat([ops.prepare_weights(dev(w)) for w in we])
+    c, s = ops.rotate_quantize_act(dev(x))
+    y = host(ops.gemm_id(packed, E, c, s, rows_per_token, dev(ids), n, k))
+    q4e = np.stack([oracle.prepare_weights(w) for w in we])
+    rc, rs = oracle.rotate_quantize_act(x)
+    ref = oracle.gemm_id(q4e, rc, rs, rows_per_token, ids, n, k)
+    assert not y[2, 1].any() and not y[5, 0].any()
+    assert_rows_close(y.reshape(-1, n), ref.reshape(-1, n), "gemm_id")
+
+
+def test_gemm_id_integer_unit_scales(ops):
+    E, T, top_k, n, k = 6, 11, 3, 70, 96
+    we, ids, rng = _moe_small(9)
+    x = synth.activations(T, k, rng, 2)
+    q4e = np.stack([with_unit_scales(oracle.prepare_weights(w)) for w in we])
+    rc, _ = oracle.rotate_quantize_act(x)
+    ones = np.ones((T, k // 32), np.float32)
+    say("gemm_id integer unit scales")
+    packed = torch.cat([ops.repack_q4_0_h32(dev(q), n, k) for q in q4e])
+    y = host(ops.gemm_id(packed, E, dev(rc), dev(ones), 1, dev(ids), n, k))
+    assert np.array_equal(y, oracle.gemm_id(q4e, rc, ones, 1, ids, n, k))
+
+
+def test_gemm_id_single_expert_equals_gemm(ops):
+    m, n, k = 50, 64, 128
+    w, x = _problem(m, n, k, 77)
+    say("gemm_id E=1 top_k=1 == gemm")
+    packed = ops.prepare_weights(dev(w))
+    c, s = ops.rotate_quantize_act(dev(x))
+    ids = torch.zeros((m, 1), dtype=torch.int32, device="cuda")
+    y1 = host(ops.gemm_id(packed, 1, c, s, 1, ids, n, k))[:, 0, :]
+    y0 = host(ops.gemm(packed, c, s, n, k))
+    assert np.array_equal(y0, y1)
+
+
+@pytest.mark.parametrize("which", ["gate", "down"])
+def test_gemm_id_moe_full_size_sampled(ops, which):
+    mo = synth.moe()
+    T, top_k, E = mo.ids.shape[0], mo.ids.shape[1], mo.w_gate.shape[0]
+    if which == "gate":
+        w, x, rpt, n, k = mo.w_gate, mo.x, 1, synth.MOE_D_FF, synth.MOE_D_MODEL
+    else:
+        w, x, rpt, n, k = mo.w_down, mo.h, top_k, synth.MOE_D_MODEL, synth.MOE_D_FF
+    say(f"gemm_id MoE {which}: {E} experts, {T} tokens, top-{top_k}, {k}->{n}")
+    packed = torch.cat([ops.prepare_weights(dev(w[e])) for e in range(E)])
+    c, s = ops.rotate_quantize_act(dev(x))
+    y = host(ops.gemm_id(packed, E, c, s, rpt, dev(mo.ids), n, k))
+    toks = np.array([0, 1, 100, 511, 777, 1023])
+    q4e = np.stack([oracle.prepare_weights(w[e]) for e in range(E)])
+    rc, rs = oracle.rotate_quantize_act(x)
+    if rpt == 1:
+        ref = oracle.gemm_id(q4e, rc[toks], rs[toks], 1, mo.ids[toks], n, k)
+    else:
+        rows = (toks[:, None] * top_k + np.arange(top_k)[None]).reshape(-1)
+        ref = oracle.gemm_id(q4e, rc[rows], rs[rows], top_k, mo.ids[toks], n, k)
+    assert_rows_close(y[toks].reshape(-1, n), ref.reshape(-1, n), f"moe {which}")
