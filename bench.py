@@ -1,0 +1,407 @@
+"""Benchmark of the W4A4 Q4_0-H32 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+
+A step is one pass of the whole hot path over one batch: rotate + quantise the
+activations of the 27B-class FFN up projection (M=512 tokens, K=5120, fp16)
+and run the W4A4 GEMM against its H32-rotated Q4_0 weights (N=17408).  The
+offline weight preparation (rotation, Q4_0, repack) happens before timing.
+Weights rotate through copies totalling > 1 GB so the 256 MB last-level cache
+cannot hold them across steps.
+
+Prints ONE JSON line (stdout).  Besides the contract's fields it carries:
+  roofline      the GEMM kernel's achieved int8 TOP/s (2*M*N*K per launch over
+                its mean duration, HIP events on its stream) against the
+                5.0 POP/s dense int8 MFMA peak; HBM traffic from rocprofv3
+                counters recorded in profiles/ (null if the kernel source has
+                changed since they were taken);
+  cpu_baseline  the CPU oracle (test infrastructure) timed on a bounded sample
+                of the same workload on the host cores;
+  extras        the 16-token verify set (GB/s vs 8 TB/s), the MoE layer
+                (MUL_MAT_ID) and the dense layer set over a 1,838-token prompt.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+COLD_BYTES = 1 << 30         # weight copies rotated per step exceed this
+PROFILE_JSON = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "hadamard_rotated_w4a4_amd", "csrc", f)
+                  for f in ("common.h", "k_gemm.h", "k_rotq.h", "k_prep.h", "w4a4.hip")]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def q4_bytes(n, k):
+    return n * (k // 32) * 18
+
+
+def gemm_bytes(m, n, k):
+    """Algorithmic HBM bytes of one GEMM: Q4_0 weights, int4 codes, fp32 scales, fp32 out."""
+    return q4_bytes(n, k) + m * k // 2 + m * (k // 32) * 4 + m * n * 4
+
+
+class Timer:
+    """Pairs of HIP events on the current stream (where the library launches)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        self.a = self.torch.cuda.Event(enable_timing=True)
+        self.b = self.torch.cuda.Event(enable_timing=True)
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.pairs.append((self.a, self.b))
+
+    def mean_ms(self, skip=0):
+        ts = [a.elapsed_time(b) for a, b in self.pairs[skip:]]
+        return float(np.mean(ts)) if ts else float("nan")
+
+
+def weight_copies(torch, packed, total_bytes=COLD_BYTES):
+    n = max(2, -(-total_bytes // packed.numel()))
+    return [packed] + [packed.clone() for _ in range(n - 1)]
+
+
+# --------------------------------------------------------------------------
+# the measured step: FFN up projection, M=512
+# --------------------------------------------------------------------------
+
+def run_main(torch, ops, synth, steps, warmup):
+    d = synth.ffn_up()
+    m, n, k = d.m, d.n, d.k
+    dev = torch.device("cuda:0")
+    w = torch.from_numpy(d.w).to(dev)
+    packed = ops.prepare_weights(w)
+    del w
+    copies = weight_copies(torch, packed)
+    x = torch.from_numpy(d.x).to(dev)
+    codes = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((m, k // 32), dtype=torch.float32, device=dev)
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    t_rq, t_gemm = Timer(torch), Timer(torch)
+
+    def step(i, timed):
+        if timed:
+            with t_rq:
+                ops.rotate_quantize_act(x, codes=codes, scales=scales)
+            with t_gemm:
+                ops.gemm(copies[i % len(copies)], codes, scales, n, k, y=y)
+        else:
+            ops.rotate_quantize_act(x, codes=codes, scales=scales)
+            ops.gemm(copies[i % len(copies)], codes, scales, n, k, y=y)
+
+    for i in range(warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    # wall-clock pass: exactly `steps` steps between two synchronisations
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, False)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    # event pass: per-kernel durations on the launch stream
+    for i in range(steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    rq_ms, gemm_ms = t_rq.mean_ms(), t_gemm.mean_ms()
+    ops_per = 2.0 * m * n * k
+    return dict(workload=d.name, m=m, n=n, k=k, wall_ms=wall_ms, rq_ms=rq_ms, gemm_ms=gemm_ms,
+                gemm_tops=ops_per / (gemm_ms * 1e-3) / 1e12, gemm_ops=ops_per,
+                gemm_bytes=gemm_bytes(m, n, k), weight_copies=len(copies))
+
+
+# --------------------------------------------------------------------------
+# extras
+# --------------------------------------------------------------------------
+
+def graph_time_us(torch, fn, reps=10, inner=1):
+    """Capture `fn` (which enqueues `inner` identical units of work) in a HIP
+    graph, replay it, and return the mean time of one unit in microseconds.
+    Graph replay removes the Python launch overhead between kernels."""
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * inner)
+
+
+def run_verify16(torch, ops, synth):
+    """16-token verify block through the seven dense projections (M<=16 path)."""
+    dev = torch.device("cuda:0")
+    ws = synth.layer_weights(workload=4)
+    xs = synth.layer_inputs(16, workload=4)
+    packed = {name: ops.prepare_weights(torch.from_numpy(ws[name]).to(dev)) for name, _, _ in synth.DENSE_PROJECTIONS}
+    del ws
+    layer_bytes = sum(p.numel() for p in packed.values())
+    nsets = max(2, -(-COLD_BYTES // layer_bytes))
+    sets = [packed] + [{k_: v.clone() for k_, v in packed.items()} for _ in range(nsets - 1)]
+    inputs = {name: torch.from_numpy(a).to(dev) for name, a in xs.items()}
+    q = {inp: ops.rotate_quantize_act(xin) for inp, xin in inputs.items()}
+    ys = {name: torch.empty((16, n), dtype=torch.float32, device=dev) for name, _, n in synth.DENSE_PROJECTIONS}
+    out = {"rows": 16, "weight_sets": nsets, "timing": "HIP graph replay, weights rotated over the sets"}
+    tot_us, tot_bytes = 0.0, 0
+    for name, k, n in synth.DENSE_PROJECTIONS:
+        c, sc = q[synth.DENSE_INPUT_OF[name]]
+
+        def one(name=name, k=k, n=n, c=c, sc=sc):
+            for i in range(2 * nsets):
+                ops.gemm(sets[i % nsets][name], c, sc, n, k, y=ys[name])
+        us = graph_time_us(torch, one, inner=2 * nsets)
+        b = gemm_bytes(16, n, k)
+        tot_us += us
+        tot_bytes += b
+        out[name] = {"k": k, "n": n, "us": round(us, 2), "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
+
+    def step():
+        for i in range(nsets):
+            qq = {inp: ops.rotate_quantize_act(xin) for inp, xin in inputs.items()}
+            for name, k, n in synth.DENSE_PROJECTIONS:
+                c, sc = qq[synth.DENSE_INPUT_OF[name]]
+                ops.gemm(sets[i][name], c, sc, n, k, y=ys[name])
+    step_us = graph_time_us(torch, step, inner=nsets)
+    out["gemm_us_total"] = round(tot_us, 2)
+    out["gemm_GB/s"] = round(tot_bytes / (tot_us * 1e-6) / 1e9, 1)
+    out["hbm_frac"] = round(tot_bytes / (tot_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+    out["step_us"] = round(step_us, 2)
+    out["tokens/s"] = round(16 / (step_us * 1e-6), 1)
+    return out
+
+
+def run_moe(torch, ops, synth):
+    """MoE layer: gate, up (one activation row per token) and down (one per slot)."""
+    dev = torch.device("cuda:0")
+    mo = synth.moe()
+    E, T, top_k = mo.w_gate.shape[0], mo.ids.shape[0], mo.ids.shape[1]
+    dm, dff = synth.MOE_D_MODEL, synth.MOE_D_FF
+    pg = torch.cat([ops.prepare_weights(torch.from_numpy(mo.w_gate[e]).to(dev)) for e in range(E)])
+    pu = torch.cat([ops.prepare_weights(torch.from_numpy(mo.w_up[e]).to(dev)) for e in range(E)])
+    pd = torch.cat([ops.prepare_weights(torch.from_numpy(mo.w_down[e]).to(dev)) for e in range(E)])
+    ids = torch.from_numpy(mo.ids).to(dev)
+    x = torch.from_numpy(mo.x).to(dev)
+    h = torch.from_numpy(mo.h).to(dev)
+    counts = np.bincount(mo.ids.reshape(-1), minlength=E)
+    ws = torch.empty(ops.gemm_id_workspace_bytes(E, T, top_k), dtype=torch.uint8, device=dev)
+    yg = torch.empty((T, top_k, dff), dtype=torch.float32, device=dev)
+    yu = torch.empty_like(yg)
+    yd = torch.empty((T, top_k, dm), dtype=torch.float32, device=dev)
+    cx, sx = ops.rotate_quantize_act(x)
+    ch, sh = ops.rotate_quantize_act(h)
+    g = graph_time_us(torch, lambda: ops.gemm_id(pg, E, cx, sx, 1, ids, dff, dm, y=yg, workspace=ws))
+    u = graph_time_us(torch, lambda: ops.gemm_id(pu, E, cx, sx, 1, ids, dff, dm, y=yu, workspace=ws))
+    dd = graph_time_us(torch, lambda: ops.gemm_id(pd, E, ch, sh, top_k, ids, dm, dff, y=yd, workspace=ws))
+    qx = graph_time_us(torch, lambda: ops.rotate_quantize_act(x, codes=cx, scales=sx))
+    qh = graph_time_us(torch, lambda: ops.rotate_quantize_act(h, codes=ch, scales=sh))
+
+    def step():
+        ops.rotate_quantize_act(x, codes=cx, scales=sx)
+        ops.rotate_quantize_act(h, codes=ch, scales=sh)
+        ops.gemm_id(pg, E, cx, sx, 1, ids, dff, dm, y=yg, workspace=ws)
+        ops.gemm_id(pu, E, cx, sx, 1, ids, dff, dm, y=yu, workspace=ws)
+        ops.gemm_id(pd, E, ch, sh, top_k, ids, dm, dff, y=yd, workspace=ws)
+    step_us = graph_time_us(torch, step)
+    rows = T * top_k
+    used = int((counts > 0).sum())
+    b_gate = used * q4_bytes(dff, dm) + T * dm // 2 + T * dm // 8 + rows * dff * 4
+    b_down = used * q4_bytes(dm, dff) + rows * dff // 2 + rows * dff // 8 + rows * dm * 4
+    tot_ops = 2 * (2.0 * rows * dff * dm) + 2.0 * rows * dm * dff
+    tot_bytes = 2 * b_gate + b_down
+    gemm_us = g + u + dd
+    return {"experts": E, "tokens": T, "top_k": top_k, "count_min": int(counts.min()),
+            "count_median": float(np.median(counts)), "count_max": int(counts.max()),
+            "timing": "HIP graph replay (weights resident in the last-level cache across replays)",
+            "gate_us": round(g, 2), "up_us": round(u, 2), "down_us": round(dd, 2),
+            "quant_us": round(qx + qh, 2), "step_us": round(step_us, 2),
+            "tokens/s": round(T / (step_us * 1e-6), 1),
+            "gemm_TOP/s": round(tot_ops / (gemm_us * 1e-6) / 1e12, 1),
+            "mfma_frac": round(tot_ops / (gemm_us * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4),
+            "gemm_GB/s": round(tot_bytes / (gemm_us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(tot_bytes / (gemm_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def run_layer_prompt(torch, ops, synth):
+    """Dense layer's seven projections over a 1,838-token prompt (512+512+512+302)."""
+    dev = torch.device("cuda:0")
+    ws = synth.layer_weights(workload=3)
+    packed = {name: ops.prepare_weights(torch.from_numpy(ws[name]).to(dev)) for name, _, _ in synth.DENSE_PROJECTIONS}
+    del ws
+    mbs = []
+    for i, mrows in enumerate(synth.PROMPT_MICROBATCHES):
+        xs = synth.layer_inputs(mrows, workload=3, microbatch=i)
+        mbs.append({k_: torch.from_numpy(v).to(dev) for k_, v in xs.items()})
+    ys = [{name: torch.empty((mb["attn_in"].shape[0], n), dtype=torch.float32, device=dev)
+           for name, _, n in synth.DENSE_PROJECTIONS} for mb in mbs]
+
+    def layer():
+        for mb, yb in zip(mbs, ys):
+            q = {inp: ops.rotate_quantize_act(xin) for inp, xin in mb.items()}
+            for name, k, n in synth.DENSE_PROJECTIONS:
+                c, s = q[synth.DENSE_INPUT_OF[name]]
+                ops.gemm(packed[name], c, s, n, k, y=yb[name])
+    us = graph_time_us(torch, layer, reps=5)
+    tokens = sum(synth.PROMPT_MICROBATCHES)
+    ops_tot = sum(2.0 * tokens * n * k for _, k, n in synth.DENSE_PROJECTIONS)
+    return {"tokens": tokens, "microbatches": list(synth.PROMPT_MICROBATCHES), "layer_ms": round(us * 1e-3, 4),
+            "timing": "HIP graph replay of the four micro-batches",
+            "tokens/s": round(tokens / (us * 1e-6), 1),
+            "TOP/s": round(ops_tot / (us * 1e-6) / 1e12, 1),
+            "mfma_frac": round(ops_tot / (us * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4)}
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# --------------------------------------------------------------------------
+
+def cpu_baseline(synth, target_s=12.0):
+    import oracle  # test infrastructure, timed here as a baseline only
+    d = synth.ffn_up()
+    threads = oracle.default_threads()
+    q4 = oracle.prepare_weights(d.w)  # offline step, not timed
+    rows = 4
+    while True:
+        t0 = time.perf_counter()
+        c, s = oracle.rotate_quantize_act(d.x[:rows], threads=threads)
+        oracle.gemm(q4, c, s, d.k, threads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or rows >= d.m:
+            break
+        rows = min(d.m, max(rows * 2, int(rows * target_s / max(dt, 1e-3) * 1.05)))
+    return {"value": round(rows / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"rotate-quantise + GEMM of the first {rows} of {d.m} token rows of {d.name} "
+                      f"(all N={d.n} outputs per row), {dt:.1f} s wall, fp64 sums, {threads} threads",
+            "ops/s": round(2.0 * rows * d.n * d.k / dt, 1)}
+
+
+def counters_for(kernel: str):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if still current."""
+    if not os.path.exists(PROFILE_JSON):
+        return None
+    rec = json.load(open(PROFILE_JSON))
+    if rec.get("source_hash") != source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="first run 5 plain device copies of this many MiB (scales rocprofv3 byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the GEMM shards over N with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from hadamard_rotated_w4a4_amd import _lib as ops
+    from hadamard_rotated_w4a4_amd import synth
+
+    ops.lib()
+    log(f"[bench] device: {torch.cuda.get_device_name(0)}")
+    if args.calibrate_copy_mb:
+        src = torch.empty(args.calibrate_copy_mb << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration: 5 copies of {args.calibrate_copy_mb} MiB")
+        del src, dst
+    log("[bench] main: ffn_up M=512 K=5120 N=17408")
+    r = run_main(torch, ops, synth, args.steps, args.warmup)
+    log(f"[bench] main: {r['wall_ms']:.4f} ms/step, rotq {r['rq_ms'] * 1e3:.1f} us, gemm {r['gemm_ms'] * 1e3:.1f} us, "
+        f"{r['gemm_tops']:.1f} TOP/s")
+    value = r["m"] / (r["wall_ms"] * 1e-3)
+    traffic = counters_for("gemm_tiled_kernel")
+    roofline = {"bound": "mfma", "achieved": round(r["gemm_tops"], 2), "peak": PEAK_INT8_TOPS,
+                "unit": "TOP/s", "frac": round(r["gemm_tops"] / PEAK_INT8_TOPS, 4), "traffic": traffic,
+                "kernel": "gemm_tiled_kernel (int8 MFMA 32x32x32, per-block fp32 epilogue)",
+                "ops_per_launch": r["gemm_ops"], "algorithmic_bytes_per_launch": r["gemm_bytes"],
+                "mean_launch_us": round(r["gemm_ms"] * 1e3, 3)}
+    extras = {}
+    if not args.no_extras:
+        log("[bench] extra: 16-token verify block, seven projections")
+        extras["verify_m16"] = run_verify16(torch, ops, synth)
+        log(f"[bench] verify_m16: {extras['verify_m16']['gemm_GB/s']} GB/s")
+        log("[bench] extra: MoE MUL_MAT_ID layer")
+        extras["moe"] = run_moe(torch, ops, synth)
+        log(f"[bench] moe: {extras['moe']['step_us']} us/step")
+        log("[bench] extra: dense layer set over a 1,838-token prompt")
+        extras["layer_prompt_1838"] = run_layer_prompt(torch, ops, synth)
+        log(f"[bench] layer: {extras['layer_prompt_1838']['layer_ms']} ms")
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle, bounded sample)")
+        cpu = cpu_baseline(synth)
+        log(f"[bench] cpu: {cpu['value']} tokens/s on {cpu['cores']} threads")
+    out = {
+        "metric": "W4A4 Q4_0-H32 GEMM tokens/s & int8 TOPS at M=512 (% MFMA peak); GB/s at M=16",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["wall_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": r["workload"], "m": r["m"], "k": r["k"], "n": r["n"],
+                   "activations": "fp16 N(0,1), 1% channels x20", "weights": "N(0,0.02) H32-rotated Q4_0",
+                   "step": "rotate_quantize_act + gemm", "weight_copies": r["weight_copies"]},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "gemm_us": round(r["gemm_ms"] * 1e3, 3),
+        "rotate_quantize_us": round(r["rq_ms"] * 1e3, 3),
+        "extras": extras,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

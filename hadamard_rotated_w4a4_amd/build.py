@@ -29,6 +29,8 @@ FLAGS = [
     # no silent multiply-add fusion: the quantisers' codes depend on every
     # rounding step; the GEMM epilogue asks for its fused multiply-adds by name
     "-ffp-contract=off",
+    # matrix-core results straight into VGPRs: no accvgpr reads in the epilogue
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]

@@ -9,6 +9,9 @@ namespace w4a4 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int QK = 32;               // Q4_0 block length along K
 constexpr int TILE_N = 32;           // columns per packed weight tile (one MFMA N)
@@ -46,6 +49,53 @@ __device__ __forceinline__ v4i unpack_nibbles_x16(uint32_t lo_word, uint32_t hi_
 __device__ __forceinline__ v16i mfma_i8_32x32x32(v4i a, v4i b) {
     v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zero, 0, 0, 0);
+}
+
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(uint4 a, uint4 b) {
+    v16f zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), zero, 0, 0, 0);
+}
+
+// 32x32x8 bf16 MFMA: 4 bf16 per lane, lane groups l/32 hold K 0..3 and 4..7.
+__device__ __forceinline__ v16f mfma_bf16_32x32x8(uint2 a, uint2 b) {
+    v16f zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(v4s, a), __builtin_bit_cast(v4s, b),
+                                                   zero, 0, 0, 0);
+}
+
+// 32x32x2 fp32 MFMA: one fp32 per lane, lane groups l/32 hold K 0 and 1.
+__device__ __forceinline__ v16f mfma_f32_32x32x2(float a, float b) {
+    v16f zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, zero, 0, 0, 0);
+}
+
+// Exact splits of fp32 scales into bf16 parts, so that a bf16 MFMA can form
+// the outer product s[m] * d[n] of a block's scales with exact partial
+// products (8 x 8 significant bits) summed in fp32.
+//   s (24 significant bits) = s1 + s2 + s3, each part 8 bits: masking the low
+//   16 bits of an fp32 keeps its top 8 significant bits; the remainder of that
+//   subtraction is exact.
+//   d (an fp16 scale: 11 significant bits) = d1 + d2.
+// Operand K slots 0..7: A = {s1, s1, s2, s2, s3, s3, 0, 0}, B = {d1, d2, d1,
+// d2, d1, d2, 0, 0}; their dot is (s1 + s2 + s3)(d1 + d2).  As a 32x32x8 MFMA
+// operand, lane group 0 takes slots 0..3 (the low 8 bytes) and group 1 slots
+// 4..7 (the high 8 bytes).
+__device__ __forceinline__ uint4 split_scale_a(float s) {
+    const uint32_t h1 = __float_as_uint(s) & 0xFFFF0000u;
+    const float r1 = __fsub_rn(s, __uint_as_float(h1));
+    const uint32_t h2 = __float_as_uint(r1) & 0xFFFF0000u;
+    const float r2 = __fsub_rn(r1, __uint_as_float(h2));
+    const uint32_t h3 = __float_as_uint(r2) & 0xFFFF0000u;
+    return make_uint4(h1 | (h1 >> 16), h2 | (h2 >> 16), h3 | (h3 >> 16), 0u);
+}
+
+__device__ __forceinline__ uint4 split_scale_b(float d) {
+    const uint32_t h1 = __float_as_uint(d) & 0xFFFF0000u;
+    const float r1 = __fsub_rn(d, __uint_as_float(h1));
+    const uint32_t h2 = __float_as_uint(r1) & 0xFFFF0000u;
+    const uint32_t pair = h2 | (h1 >> 16);
+    return make_uint4(pair, pair, pair, 0u);
 }
 
 // Materialise a value in a register so that the compiler cannot fuse the

@@ -36,26 +36,40 @@ struct GemmArgs {
 // Tiled kernel: WAVES_M x WAVES_N waves, each owning TM x TN 32x32 MFMA tiles;
 // BKB Q4_0 blocks staged in LDS per step.
 // -------------------------------------------------------------------------
-template <int WAVES_M, int WAVES_N, int TM, int TN, int BKB>
+// How the per-block scale product s[m] * d_w[n] of a 32x32 tile is formed on
+// the matrix cores: a 32x32x8 bf16 MFMA over exact bf16 splits of the scales,
+// or a 32x32x2 fp32 MFMA over the scales themselves (one fp32 rounding).
+enum ScaleMfma { kScaleBf16 = 0, kScaleF32 = 1 };
+
+template <int WAVES_M, int WAVES_N, int TM, int TN, int BKB, int SCALE = kScaleBf16>
 struct TileCfg {
     static constexpr int BM = WAVES_M * TM * 32;
     static constexpr int BN = WAVES_N * TN * 32;
     static constexpr int NT = 64 * WAVES_M * WAVES_N;
     static constexpr int NTILES = BN / 32;
     static constexpr int kBKB = BKB;
-    static constexpr int kWM = WAVES_M, kWN = WAVES_N, kTM = TM, kTN = TN;
+    static constexpr int kWM = WAVES_M, kWN = WAVES_N, kTM = TM, kTN = TN, kScale = SCALE;
 };
 
 template <class C, bool GROUPED>
 __global__ __launch_bounds__(C::NT) void gemm_tiled_kernel(GemmArgs a) {
-    constexpr int BM = C::BM, BKB = C::kBKB, NTILES = C::NTILES;
+    constexpr int BM = C::BM, BN = C::BN, BKB = C::kBKB, NTILES = C::NTILES;
     constexpr int TM = C::kTM, TN = C::kTN, NT = C::NT;
-    __shared__ uint4 sA[BKB][BM];               // packed activation codes
-    __shared__ uint2 sB[BKB][NTILES][64];       // packed weight codes, MFMA lane order
-    __shared__ __attribute__((aligned(16))) float sSa[BKB][BM];  // activation scales
-    __shared__ float sDw[BKB][NTILES * 32];     // weight scales / 256
-    __shared__ int sArow[BM];                   // activation row of each tile row, -1 if none
-    __shared__ int sOrow[BM];                   // output row
+    // Operands are unpacked once per workgroup while staging: each row (A) or
+    // column (B) of a block becomes 2 x 16 int8 (one MFMA lane's operand per
+    // lane group).  Rows are padded by 16 bytes so that the staging writes of
+    // neighbouring lanes (different blocks, same row) fall in different banks.
+    constexpr int AP = BM + 1;
+    __shared__ uint4 sA[BKB][AP][2];              // int8 activation operands
+    __shared__ uint4 sB[BKB][NTILES][64];         // int8 weight operands, MFMA lane order
+    // operands of the scale-product MFMA, 16 bytes per row / column and block:
+    // bf16 splits (lane group g reads half g), or {scale, 0, ...} as fp32
+    // (lane group 0 reads the scale, group 1 the zero)
+    constexpr bool SCALE_F32 = C::kScale == kScaleF32;
+    __shared__ uint4 sAP[BKB][AP];
+    __shared__ uint4 sBP[BKB][BN];
+    __shared__ int sArow[BM];  // activation row of each tile row, -1 if none
+    __shared__ int sOrow[BM];  // output row
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::kWN, wn = wave % C::kWN;
@@ -100,6 +114,94 @@ __global__ __launch_bounds__(C::NT) void gemm_tiled_kernel(GemmArgs a) {
     const uint16_t *wscales = reinterpret_cast<const uint16_t *>(wbase + packed_code_bytes(a.n, k));
     __syncthreads();
 
+    // ---- per-thread staging slots, fixed across K steps ----
+    // A: (row, block) pairs; B: 16-byte pieces of (tile, block) codes and
+    // single fp16 scales.  Each slot keeps a source pointer that advances by
+    // BKB blocks per step, the block it stages, and whether its row/tile exists.
+    constexpr int A_WORK = BM * BKB, B_WORK = NTILES * BKB * 32;
+    constexpr int A_SLOTS = (A_WORK + NT - 1) / NT, B_SLOTS = (B_WORK + NT - 1) / NT;
+    const uint8_t *a_src[A_SLOTS];
+    const float *s_src[A_SLOTS];
+    int a_bb[A_SLOTS];
+    bool a_ok[A_SLOTS];
+#pragma unroll
+    for (int p = 0; p < A_SLOTS; p++) {
+        const int i = tid + p * NT;
+        const int r = i / BKB, bb = i % BKB;
+        const int ar = i < A_WORK ? sArow[r] : -1;
+        a_ok[p] = ar >= 0;
+        a_bb[p] = bb;
+        a_src[p] = a.codes + (int64_t)(ar >= 0 ? ar : 0) * (k / 2) + bb * 16;
+        s_src[p] = a.scales + (int64_t)(ar >= 0 ? ar : 0) * nb + bb;
+    }
+    const uint4 *b_src[B_SLOTS];
+    const uint16_t *d_src[B_SLOTS];
+    int b_bb[B_SLOTS];
+    bool b_ok[B_SLOTS];
+#pragma unroll
+    for (int p = 0; p < B_SLOTS; p++) {
+        const int i = tid + p * NT;
+        const int t = i / (BKB * 32), rem = i % (BKB * 32), bb = rem / 32, q = rem % 32;
+        const int64_t tile = tile0 + t;
+        b_ok[p] = i < B_WORK && tile < tiles_n;
+        b_bb[p] = bb;
+        const int64_t tb = (b_ok[p] ? tile : 0) * nb + bb;
+        b_src[p] = reinterpret_cast<const uint4 *>(wcodes + tb * TILE_CODE_BYTES) + q;
+        d_src[p] = wscales + tb * TILE_SCALE_HALFS + q;
+    }
+    uint4 a_reg[A_SLOTS], b_reg[B_SLOTS];
+    float s_reg[A_SLOTS];
+    uint16_t d_reg[B_SLOTS];
+
+    auto load_stage = [&](int64_t kb0) {
+#pragma unroll
+        for (int p = 0; p < A_SLOTS; p++) {
+            a_reg[p] = make_uint4(0, 0, 0, 0);
+            s_reg[p] = 0.0f;
+            if (a_ok[p] && kb0 + a_bb[p] < nb) {
+                a_reg[p] = *reinterpret_cast<const uint4 *>(a_src[p] + kb0 * 16);
+                s_reg[p] = s_src[p][kb0];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < B_SLOTS; p++) {
+            b_reg[p] = make_uint4(0, 0, 0, 0);
+            d_reg[p] = 0;
+            if (b_ok[p] && kb0 + b_bb[p] < nb) {
+                b_reg[p] = b_src[p][kb0 * (TILE_CODE_BYTES / 16)];
+                d_reg[p] = d_src[p][kb0 * TILE_SCALE_HALFS];
+            }
+        }
+    };
+    auto store_stage = [&]() {
+#pragma unroll
+        for (int p = 0; p < A_SLOTS; p++) {
+            const int i = tid + p * NT;
+            if (i < A_WORK) {
+                const int r = i / BKB, bb = i % BKB;
+                const uint4 q = a_reg[p];
+                const v4i lo = unpack_nibbles_x16(q.x, q.y), hi = unpack_nibbles_x16(q.z, q.w);
+                sA[bb][r][0] = make_uint4(lo.x, lo.y, lo.z, lo.w);
+                sA[bb][r][1] = make_uint4(hi.x, hi.y, hi.z, hi.w);
+                sAP[bb][r] = SCALE_F32 ? make_uint4(__float_as_uint(s_reg[p]), 0, 0, 0) : split_scale_a(s_reg[p]);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < B_SLOTS; p++) {
+            const int i = tid + p * NT;
+            if (i < B_WORK) {
+                const int t = i / (BKB * 32), rem = i % (BKB * 32), bb = rem / 32, q = rem % 32;
+                const uint4 w = b_reg[p];  // the packed operands of lanes 2q and 2q + 1
+                const v4i l0 = unpack_nibbles_x16(w.x, w.y), l1 = unpack_nibbles_x16(w.z, w.w);
+                sB[bb][t][2 * q] = make_uint4(l0.x, l0.y, l0.z, l0.w);
+                sB[bb][t][2 * q + 1] = make_uint4(l1.x, l1.y, l1.z, l1.w);
+                // / 256 (exact) undoes the 16 x 16 scaling of the unpacked operands
+                const float dsc = __half2float(__ushort_as_half(d_reg[p])) * (1.0f / 256.0f);
+                sBP[bb][t * 32 + q] = SCALE_F32 ? make_uint4(__float_as_uint(dsc), 0, 0, 0) : split_scale_b(dsc);
+            }
+        }
+    };
+
     float acc[TM][TN][16];
 #pragma unroll
     for (int i = 0; i < TM; i++)
@@ -109,70 +211,48 @@ __global__ __launch_bounds__(C::NT) void gemm_tiled_kernel(GemmArgs a) {
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
     const int wrow0 = wm * TM * 32;  // first tile row of this wave
+    load_stage(0);
     for (int64_t kb0 = 0; kb0 < nb; kb0 += BKB) {
-        // ---- stage BKB blocks into LDS ----
-        for (int i = tid; i < BM * BKB; i += NT) {
-            const int r = i / BKB, bb = i % BKB;
-            const int ar = sArow[r];
-            uint4 v = make_uint4(0, 0, 0, 0);
-            float s = 0.0f;
-            if (ar >= 0 && kb0 + bb < nb) {
-                v = *reinterpret_cast<const uint4 *>(a.codes + (int64_t)ar * (k / 2) + (kb0 + bb) * 16);
-                s = a.scales[(int64_t)ar * nb + kb0 + bb];
-            }
-            sA[bb][r] = v;
-            sSa[bb][r] = s;
-        }
-        for (int i = tid; i < NTILES * BKB * 32; i += NT) {
-            const int t = i / (BKB * 32), rem = i % (BKB * 32), bb = rem / 32, q = rem % 32;
-            const int64_t tile = tile0 + t;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (tile < tiles_n && kb0 + bb < nb)
-                v = reinterpret_cast<const uint4 *>(wcodes + (tile * nb + kb0 + bb) * TILE_CODE_BYTES)[q];
-            reinterpret_cast<uint4 *>(&sB[bb][t][0])[q] = v;
-        }
-        for (int i = tid; i < NTILES * BKB * 32; i += NT) {
-            const int t = i / (BKB * 32), rem = i % (BKB * 32), bb = rem / 32, cc = rem % 32;
-            const int64_t tile = tile0 + t;
-            float d = 0.0f;
-            if (tile < tiles_n && kb0 + bb < nb)
-                d = __half2float(__ushort_as_half(wscales[(tile * nb + kb0 + bb) * TILE_SCALE_HALFS + cc]));
-            sDw[bb][t * 32 + cc] = d * (1.0f / 256.0f);  // exact: undoes the 16 x 16 operand scaling
-        }
+        store_stage();
         __syncthreads();
+        if (kb0 + BKB < nb) load_stage(kb0 + BKB);  // in flight during the compute below
 
-        // ---- compute ----
+        // ---- compute: per 32x32 tile and block, S on int8 MFMA, s*d_w on a float MFMA ----
 #pragma unroll
         for (int bb = 0; bb < BKB; bb++) {
             v4i af[TM], bf[TN];
+            uint2 ap[TM], bp[TN];
 #pragma unroll
             for (int i = 0; i < TM; i++) {
-                const uint2 p = reinterpret_cast<const uint2 *>(&sA[bb][wrow0 + i * 32 + c])[g];
-                af[i] = unpack_nibbles_x16(p.x, p.y);
+                af[i] = __builtin_bit_cast(v4i, sA[bb][wrow0 + i * 32 + c][g]);
+                if constexpr (SCALE_F32)
+                    ap[i].x = reinterpret_cast<const uint32_t *>(&sAP[bb][wrow0 + i * 32 + c])[g];
+                else
+                    ap[i] = reinterpret_cast<const uint2 *>(&sAP[bb][wrow0 + i * 32 + c])[g];
             }
 #pragma unroll
             for (int j = 0; j < TN; j++) {
-                const uint2 p = sB[bb][wn * TN + j][lane];
-                bf[j] = unpack_nibbles_x16(p.x, p.y);
+                bf[j] = __builtin_bit_cast(v4i, sB[bb][wn * TN + j][lane]);
+                if constexpr (SCALE_F32)
+                    bp[j].x = reinterpret_cast<const uint32_t *>(&sBP[bb][(wn * TN + j) * 32 + c])[g];
+                else
+                    bp[j] = reinterpret_cast<const uint2 *>(&sBP[bb][(wn * TN + j) * 32 + c])[g];
             }
-            float dw[TN];
-#pragma unroll
-            for (int j = 0; j < TN; j++) dw[j] = sDw[bb][(wn * TN + j) * 32 + c];
+            // Empty tile rows carry zero codes and zero scales, so they add 0;
+            // no branch here keeps each block's MFMAs and epilogue in one
+            // basic block for the scheduler.
 #pragma unroll
             for (int i = 0; i < TM; i++) {
-                if (wrow0 + i * 32 >= valid_rows) continue;  // uniform: tile rows all empty
-                float sa[16];
-#pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const float4 s4 = *reinterpret_cast<const float4 *>(&sSa[bb][wrow0 + i * 32 + 8 * q + 4 * g]);
-                    sa[4 * q + 0] = s4.x; sa[4 * q + 1] = s4.y; sa[4 * q + 2] = s4.z; sa[4 * q + 3] = s4.w;
-                }
 #pragma unroll
                 for (int j = 0; j < TN; j++) {
                     const v16i S = mfma_i8_32x32x32(af[i], bf[j]);
+                    v16f P;
+                    if constexpr (SCALE_F32)
+                        P = mfma_f32_32x32x2(__uint_as_float(ap[i].x), __uint_as_float(bp[j].x));
+                    else
+                        P = mfma_bf16_32x32x8(ap[i], bp[j]);
 #pragma unroll
-                    for (int v = 0; v < 16; v++)
-                        acc[i][j][v] = fmaf((float)S[v], sa[v] * dw[j], acc[i][j][v]);
+                    for (int v = 0; v < 16; v++) acc[i][j][v] = fmaf((float)S[v], P[v], acc[i][j][v]);
                 }
             }
         }
@@ -197,71 +277,142 @@ __global__ __launch_bounds__(C::NT) void gemm_tiled_kernel(GemmArgs a) {
 }
 
 // -------------------------------------------------------------------------
-// Small-M kernel (m <= 16): weight streaming.  One workgroup per 32-column
-// tile; its W waves take interleaved K blocks, each weight byte is read from
-// HBM exactly once, the activation scales are staged in LDS per chunk, and
-// the waves' partial sums are reduced in LDS before one store.
+// Small-M kernel (m <= 16): weight streaming, one pass over HBM.
+//
+// A workgroup owns one 32-column tile; its waves split K into contiguous runs
+// of `bpw` blocks, so every weight byte is read once.  Each wave streams its
+// run in stages of SMALL_STAGE blocks through a ring of NS stage buffers of
+// its own in LDS: every byte a stage needs (weight codes and scales,
+// activation codes and scales) arrives by direct global-to-LDS loads, so data
+// in flight costs no registers, and NS - 1 stages are in flight while one is
+// computed.  The loads are issued from inline assembly with the wave's own
+// vmcnt accounting (5 loads per stage, retired in order; the loop issues no
+// other vector-memory operation), because the compiler cannot see that a
+// stage being read is not the one being loaded and would wait for all loads.
+// Past the end of the run the ring keeps loading the last block (L2 hits), so
+// the count of loads in flight is the same at every step.
+//
+// Per block: the int8 MFMA gives S (tile rows 16..31 are unused), an fp32
+// 32x32x2 MFMA the scale products s[m] * d_w[n] (the weight-scale operand is
+// zero in lane group 1, so the other operand's group-1 lanes may hold any
+// finite value), and the VALU does one convert and one fused multiply-add per
+// output.  Rows >= m reuse row m - 1 and blocks past the run get a zero
+// weight scale: nothing diverges and those outputs are never stored or are
+// exactly zero.  The waves' partial sums meet in LDS for one store.
 // -------------------------------------------------------------------------
 constexpr int SMALL_M_MAX = 16;
-constexpr int SMALL_CHUNK = 256;  // blocks of activation scales staged per pass
+constexpr int SMALL_STAGE = 4;          // blocks per stage
+constexpr int SMALL_MAX_WAVES = 8;
+constexpr int SMALL_MAX_NS = 8;          // deepest ring instantiated
+// per stage, in LDS: weight codes [4][512 B], weight scales [4][32] fp16,
+// activation codes [4][16 rows][16 B], activation scales [4][16 rows] fp32
+constexpr int SMALL_W_OFF = 0, SMALL_D_OFF = 2048, SMALL_A_OFF = 2304, SMALL_S_OFF = 3328;
+constexpr int SMALL_STAGE_BYTES = 3584;
+constexpr int SMALL_LOADS_PER_STAGE = 5;
 
-template <int W>
-__global__ __launch_bounds__(64 * W) void gemm_small_m_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) float sSa[SMALL_CHUNK][SMALL_M_MAX];
-    __shared__ float sRed[W][8][64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// One global-to-LDS load: lane l's `size` bytes at `g` land at LDS byte
+// address lds + l * size (lds is wave-uniform, passed through M0).
+__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+template <int NS>
+__global__ __launch_bounds__(64 * SMALL_MAX_WAVES) void gemm_small_m_kernel(GemmArgs a, int bpw) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [waves][NS][stage]
+    const int tid = threadIdx.x, lane = tid & 63, waves = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
     const int g = lane >> 5, c = lane & 31;
     const int64_t k = a.k, nb = k / QK;
     const int64_t tile = blockIdx.x;
     const int m = (int)a.m;
-    const uint2 *wcodes = reinterpret_cast<const uint2 *>(a.packed) + tile * nb * 64;
-    const uint16_t *wscales =
-        reinterpret_cast<const uint16_t *>(a.packed + packed_code_bytes(a.n, k)) + tile * nb * TILE_SCALE_HALFS;
-    const bool arow_ok = c < m;
-    const uint8_t *arow = a.codes + (int64_t)(arow_ok ? c : 0) * (k / 2) + 8 * g;
+    const int64_t b0 = min((int64_t)wave * bpw, nb), b1 = min(b0 + bpw, nb);
+    uint8_t *ring = smem + wave * NS * SMALL_STAGE_BYTES;
+    const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+
+    // per-lane global sources of the stage loads (see the layout above)
+    const uint8_t *wsrc = a.packed + tile * nb * TILE_CODE_BYTES + (lane & 31) * 16;      // + blk * 512
+    const uint8_t *dsrc = a.packed + packed_code_bytes(a.n, k) + tile * nb * 64 + (lane & 15) * 4;
+    const int arow = min(lane & 15, m - 1);
+    const uint8_t *asrc = a.codes + (int64_t)arow * (k / 2);                               // + blk * 16
+    const float *ssrc = a.scales + (int64_t)arow * nb;                                     // + blk
+
+    auto issue = [&](int64_t b, int slot) {  // loads of blocks b .. b + 3 (clamped to the run)
+        const uint32_t st = ring_lds + slot * SMALL_STAGE_BYTES;
+        const int64_t last = b1 - 1;
+        const int64_t bw0 = min(b + (lane >> 5), last), bw1 = min(b + 2 + (lane >> 5), last);
+        const int64_t bq = min(b + (lane >> 4), last);
+        lds_dma16(wsrc + bw0 * TILE_CODE_BYTES, st + SMALL_W_OFF);
+        lds_dma16(wsrc + bw1 * TILE_CODE_BYTES, st + SMALL_W_OFF + 1024);
+        lds_dma4(dsrc + bq * 64, st + SMALL_D_OFF);
+        lds_dma16(asrc + bq * 16, st + SMALL_A_OFF);
+        lds_dma4(ssrc + bq, st + SMALL_S_OFF);
+    };
 
     float acc[8];
 #pragma unroll
     for (int v = 0; v < 8; v++) acc[v] = 0.0f;
 
-    for (int64_t cb = 0; cb < nb; cb += SMALL_CHUNK) {
-        const int chunk = (int)min((int64_t)SMALL_CHUNK, nb - cb);
-        for (int i = tid; i < chunk * SMALL_M_MAX; i += 64 * W) {
-            const int bb = i / SMALL_M_MAX, r = i % SMALL_M_MAX;
-            sSa[bb][r] = r < m ? a.scales[(int64_t)r * nb + cb + bb] : 0.0f;
+    const int row = min(c, m - 1);  // this lane's activation row in the MFMA
+    auto compute = [&](int64_t b, int slot) {
+        const uint8_t *st = ring + slot * SMALL_STAGE_BYTES;
+#pragma unroll
+        for (int u = 0; u < SMALL_STAGE; u++) {
+            const uint2 w = *reinterpret_cast<const uint2 *>(st + SMALL_W_OFF + u * 512 + lane * 8);
+            const uint32_t d = *reinterpret_cast<const uint16_t *>(st + SMALL_D_OFF + u * 64 + c * 2);
+            const uint2 av = *reinterpret_cast<const uint2 *>(st + SMALL_A_OFF + (u * 16 + row) * 16 + g * 8);
+            const float sc = *reinterpret_cast<const float *>(st + SMALL_S_OFF + (u * 16 + row) * 4);
+            const v16i S = mfma_i8_32x32x32(unpack_nibbles_x16(av.x, av.y), unpack_nibbles_x16(w.x, w.y));
+            // lane group 1 and blocks past the run contribute a zero weight scale
+            const uint32_t keep = (b + u < b1) ? (uint32_t)(g - 1) & 0xFFFFu : 0u;  // 0xFFFF for g == 0
+            // / 256 (exact) undoes the 16 x 16 scaling of the unpacked operands
+            const float dw = __half2float(__ushort_as_half((uint16_t)(d & keep))) * (1.0f / 256.0f);
+            const v16f P = mfma_f32_32x32x2(sc, dw);
+#pragma unroll
+            for (int v = 0; v < 8; v++) acc[v] = fmaf((float)S[v], P[v], acc[v]);
         }
-        __syncthreads();
-        for (int bb = wave; bb < chunk; bb += W) {
-            const int64_t b = cb + bb;
-            const uint2 wp = wcodes[b * 64 + lane];
-            const float dw = __half2float(__ushort_as_half(wscales[b * TILE_SCALE_HALFS + c])) * (1.0f / 256.0f);
-            uint2 ap = make_uint2(0, 0);
-            if (arow_ok) ap = *reinterpret_cast<const uint2 *>(arow + b * 16);
-            const v16i S = mfma_i8_32x32x32(unpack_nibbles_x16(ap.x, ap.y), unpack_nibbles_x16(wp.x, wp.y));
-            const float4 s0 = *reinterpret_cast<const float4 *>(&sSa[bb][4 * g]);
-            const float4 s1 = *reinterpret_cast<const float4 *>(&sSa[bb][8 + 4 * g]);
-            acc[0] = fmaf((float)S[0], s0.x * dw, acc[0]);
-            acc[1] = fmaf((float)S[1], s0.y * dw, acc[1]);
-            acc[2] = fmaf((float)S[2], s0.z * dw, acc[2]);
-            acc[3] = fmaf((float)S[3], s0.w * dw, acc[3]);
-            acc[4] = fmaf((float)S[4], s1.x * dw, acc[4]);
-            acc[5] = fmaf((float)S[5], s1.y * dw, acc[5]);
-            acc[6] = fmaf((float)S[6], s1.z * dw, acc[6]);
-            acc[7] = fmaf((float)S[7], s1.w * dw, acc[7]);
+    };
+
+    if (b0 < b1) {
+#pragma unroll
+        for (int s = 0; s < NS - 1; s++) issue(b0 + s * SMALL_STAGE, s);
+        int slot = 0;
+        for (int64_t b = b0; b < b1; b += SMALL_STAGE) {
+            int ahead = slot + NS - 1;
+            if (ahead >= NS) ahead -= NS;
+            issue(b + (NS - 1) * SMALL_STAGE, ahead);              // keep NS - 1 stages in flight
+            wait_vmcnt<SMALL_LOADS_PER_STAGE * (NS - 1)>();        // this stage has landed
+            compute(b, slot);
+            // the next issue overwrites the slot computed NS - 1 stages from now;
+            // this slot is refilled only after its reads have returned
+            if (++slot == NS) slot = 0;
         }
-        __syncthreads();
+        wait_vmcnt<0>();  // no load may still write the LDS reused below
     }
-#pragma unroll
-    for (int v = 0; v < 8; v++) sRed[wave][v][lane] = acc[v];
+
+    // cross-wave reduction, reusing the front of this wave's ring
     __syncthreads();
-    for (int i = tid; i < 8 * 64; i += 64 * W) {
-        const int v = i / 64, l = i % 64;
-        float s = 0.0f;
+    float *red = reinterpret_cast<float *>(ring);
 #pragma unroll
-        for (int w = 0; w < W; w++) s += sRed[w][v][l];
+    for (int v = 0; v < 8; v++) red[v * 64 + lane] = acc[v];
+    __syncthreads();
+    for (int i = tid; i < 8 * 64; i += blockDim.x) {
+        const int v = i / 64, l = i % 64;
+        float sum = 0.0f;
+        for (int w = 0; w < waves; w++) sum += reinterpret_cast<const float *>(smem + w * NS * SMALL_STAGE_BYTES)[i];
         const int r = mfma32_row(v, l);
         const int64_t col = tile * 32 + (l & 31);
-        if (r < m && col < a.n) a.y[(int64_t)r * a.ldy + col] = s;
+        if (r < m && col < a.n) a.y[(int64_t)r * a.ldy + col] = sum;
     }
 }
 

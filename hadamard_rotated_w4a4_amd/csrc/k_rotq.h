@@ -7,12 +7,12 @@
 // coarse scale on the rest.  The same per-block rotation was applied to the
 // weights offline, so the product is unchanged in exact arithmetic.
 //
-// Lane mapping: 32 lanes per block, one element per lane, two blocks per
-// wave64.  The butterflies exchange across lanes (xor 1, 2, 4, 8, 16 never
-// leaves the 32-lane half), the amax is a 5-step xor max, and each lane
-// quantises its own element.  The fp32 operation sequence is fixed: IEEE add
-// and subtract per stage in the order h = 1, 2, 4, 8, 16, correctly rounded
-// division and reciprocal, multiply without contraction, round half away.
+// Mapping: one thread per 32-element block, the whole transform in registers
+// (the pass is a single read of the activations and is bound by memory and
+// launch latency, not arithmetic).  The fp32 operation sequence is fixed:
+// IEEE add and subtract per stage in the order h = 1, 2, 4, 8, 16, correctly
+// rounded division and reciprocal, multiply without contraction, round half
+// away from zero.
 #pragma once
 
 #include "common.h"
@@ -27,54 +27,89 @@ __device__ __forceinline__ float round_half_away(float x) {
     return frac >= 0.5f ? __fadd_rn(t, x < 0.0f ? -1.0f : 1.0f) : t;
 }
 
-template <typename T>
-__device__ __forceinline__ float load_act(const T *p);
-template <>
-__device__ __forceinline__ float load_act<float>(const float *p) { return *p; }
-template <>
-__device__ __forceinline__ float load_act<__half>(const __half *p) { return __half2float(*p); }
+// Load the 32 elements of one block as fp32 (exact from fp16).
+__device__ __forceinline__ void load_block(const float *__restrict__ p, float v[QK]) {
+    const float4 *q = reinterpret_cast<const float4 *>(p);
+#pragma unroll
+    for (int i = 0; i < QK / 4; i++) {
+        const float4 f = q[i];
+        v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+}
+__device__ __forceinline__ void load_block(const __half *__restrict__ p, float v[QK]) {
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+    for (int i = 0; i < QK / 8; i++) {
+        const uint4 u = q[i];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            v[8 * i + 2 * j] = __half2float(__ushort_as_half((uint16_t)(w[j] & 0xffff)));
+            v[8 * i + 2 * j + 1] = __half2float(__ushort_as_half((uint16_t)(w[j] >> 16)));
+        }
+    }
+}
 
-template <typename T>
+// One thread per 32-element block, all in registers: unnormalised FWHT,
+// amax, scale, codes, packing.  Loads are 16-byte vectors when the row stride
+// and base keep every block 16-byte aligned (checked on the host); the
+// element-wise variant below covers any other stride.
+template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void rotate_quantize_kernel(const T *__restrict__ x, int64_t m,
                                                               int64_t k, int64_t ldx,
                                                               uint8_t *__restrict__ codes,
                                                               float *__restrict__ scales) {
     const int64_t nb = k / QK;
-    const int64_t gblk = (int64_t)blockIdx.x * (blockDim.x / QK) + (threadIdx.x / QK);
-    if (gblk >= m * nb) return;  // uniform across the 32 lanes of one block
-    const int t = threadIdx.x & (QK - 1);
-    const int64_t row = gblk / nb, b = gblk % nb;
+    const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blk >= m * nb) return;
+    const int64_t row = blk / nb, b = blk % nb;
+    const T *src = x + row * ldx + b * QK;
 
-    float v = load_act<T>(x + row * ldx + b * QK + t);
-
-    // unnormalised FWHT: (a, b) -> (a + b, a - b) for the pair (i, i + h)
+    float v[QK];
+    if constexpr (VEC) {
+        load_block(src, v);
+    } else {
 #pragma unroll
-    for (int h = 1; h < QK; h <<= 1) {
-        const float p = __shfl_xor(v, h, QK);
-        v = (t & h) ? __fsub_rn(p, v) : __fadd_rn(v, p);
+        for (int t = 0; t < QK; t++) {
+            if constexpr (sizeof(T) == 4) v[t] = src[t];
+            else v[t] = __half2float(src[t]);
+        }
     }
 
-    float amax = fabsf(v);
+    // (a, b) -> (a + b, a - b) for the pair (i, i + h), h = 1, 2, 4, 8, 16
 #pragma unroll
-    for (int h = 1; h < QK; h <<= 1) amax = fmaxf(amax, __shfl_xor(amax, h, QK));
+    for (int h = 1; h < QK; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < QK; i++) {
+            if (i & h) continue;
+            const float a0 = v[i], a1 = v[i + h];
+            v[i] = __fadd_rn(a0, a1);
+            v[i + h] = __fsub_rn(a0, a1);
+        }
+    }
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int t = 0; t < QK; t++) amax = fmaxf(amax, fabsf(v[t]));
 
     const float d = __fdiv_rn(amax, 7.0f);
-    int q = 0;
+    uint32_t packed[4] = {0u, 0u, 0u, 0u};
     float s = 0.0f;
     if (d >= 1.17549435e-38f) {  // FLT_MIN: zero and subnormal scales give a zero block
         const float id = __fdiv_rn(1.0f, d);
-        float r = round_half_away(__fmul_rn(v, id));
-        r = fminf(7.0f, fmaxf(-7.0f, r));
-        q = (int)r;
+#pragma unroll
+        for (int j = 0; j < QK / 2; j++) {
+            const float r0 = fminf(7.0f, fmaxf(-7.0f, round_half_away(__fmul_rn(v[j], id))));
+            const float r1 = fminf(7.0f, fmaxf(-7.0f, round_half_away(__fmul_rn(v[j + 16], id))));
+            const uint32_t byte = ((uint32_t)(int)r0 & 0xFu) | (((uint32_t)(int)r1 & 0xFu) << 4);
+            packed[j >> 2] |= byte << (8 * (j & 3));
+        }
         s = __fmul_rn(d, kInvSqrt32f);
     }
-
-    // byte j (j < 16) = code j (low nibble) | code j + 16 (high nibble)
-    const int hi = __shfl_down(q, 16, QK);
-    if (t < 16) {
-        codes[row * (k / 2) + b * 16 + t] = (uint8_t)((q & 0xF) | ((hi & 0xF) << 4));
-    }
-    if (t == 0) scales[row * nb + b] = s;
+    // byte j of the block: code j (low nibble) | code j + 16 (high nibble)
+    *reinterpret_cast<uint4 *>(codes + row * (k / 2) + b * 16) =
+        make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    scales[row * nb + b] = s;
 }
 
 }  // namespace w4a4

@@ -5,6 +5,8 @@
 // or synchronises.
 #include "w4a4.h"
 
+#include <algorithm>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 
@@ -30,8 +32,8 @@ inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 inline unsigned blocks_for(int64_t work, int per) { return (unsigned)((work + per - 1) / per); }
 
-// Dense large-M tiles: 4 waves in 2 x 2, each 64 x 64, 128 x 128 per workgroup.
-using DenseCfg = TileCfg<2, 2, 2, 2, 4>;
+// Dense large-M tiles: 8 waves in 2 x 4, each 32 x 32, 64 x 128 per workgroup.
+using DenseCfg = TileCfg<2, 4, 1, 1, 4>;
 // Grouped expert tiles: 32 rows (experts are small), 4 waves across 256 columns.
 using GroupedCfg = TileCfg<1, 4, 1, 2, 4>;
 
@@ -113,13 +115,19 @@ w4a4_status w4a4_rotate_quantize_act(const void *x, w4a4_dtype dt, int64_t m, in
     if (!aligned(x, dt == W4A4_DTYPE_F32 ? 4 : 2) || !aligned(codes, 16) || !aligned(scales, 4))
         return W4A4_ERR_MISALIGNED;
     const int64_t blocks = m * (k / QK);
-    const unsigned grid = blocks_for(blocks, 256 / QK);
-    if (dt == W4A4_DTYPE_F32)
-        rotate_quantize_kernel<float><<<grid, 256, 0, as_stream(stream)>>>(
-            static_cast<const float *>(x), m, k, ldx, codes, scales);
-    else
-        rotate_quantize_kernel<__half><<<grid, 256, 0, as_stream(stream)>>>(
-            static_cast<const __half *>(x), m, k, ldx, codes, scales);
+    const unsigned grid = blocks_for(blocks, 256);
+    const size_t esz = dt == W4A4_DTYPE_F32 ? 4 : 2;
+    const bool vec = aligned(x, 16) && (ldx * esz) % 16 == 0;  // every block 16-byte aligned
+    hipStream_t s = as_stream(stream);
+    if (dt == W4A4_DTYPE_F32) {
+        const float *xf = static_cast<const float *>(x);
+        if (vec) rotate_quantize_kernel<float, true><<<grid, 256, 0, s>>>(xf, m, k, ldx, codes, scales);
+        else rotate_quantize_kernel<float, false><<<grid, 256, 0, s>>>(xf, m, k, ldx, codes, scales);
+    } else {
+        const __half *xh = static_cast<const __half *>(x);
+        if (vec) rotate_quantize_kernel<__half, true><<<grid, 256, 0, s>>>(xh, m, k, ldx, codes, scales);
+        else rotate_quantize_kernel<__half, false><<<grid, 256, 0, s>>>(xh, m, k, ldx, codes, scales);
+    }
     return hip_status("rotate_quantize_kernel");
 }
 
@@ -148,10 +156,32 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
     a.k = k;
     const int64_t tiles_n = padded_n(n) / TILE_N;
     if (m <= SMALL_M_MAX) {
-        if (tiles_n >= 256)
-            gemm_small_m_kernel<8><<<(unsigned)tiles_n, 64 * 8, 0, s>>>(a);
-        else
-            gemm_small_m_kernel<16><<<(unsigned)tiles_n, 64 * 16, 0, s>>>(a);
+        // One workgroup per 32-column tile, all resident in one round.  Most
+        // waves per tile first (runs of >= 4 stages, <= 6 waves per SIMD):
+        // one wave's compute is a serial MFMA chain, so spreading K wins.
+        // Then the ring depth the LDS left per workgroup allows, within 64 KB:
+        // measured on MI355X, rings deeper than that were slower, not faster.
+        const int64_t nb = k / QK;
+        const int64_t stages = (nb + SMALL_STAGE - 1) / SMALL_STAGE;
+        const int64_t wgs_per_cu = (tiles_n + 255) / 256;
+        int64_t w = std::min<int64_t>(SMALL_MAX_WAVES, std::max<int64_t>(1, stages / 4));
+        while (w > 1 && w * wgs_per_cu > 24) w--;
+        const int64_t lds_budget = std::min<int64_t>(64 * 1024, 160 * 1024 / wgs_per_cu);
+        while (w > 1 && w * 2 * SMALL_STAGE_BYTES > lds_budget) w--;
+        const int64_t ns = std::max<int64_t>(2, std::min<int64_t>(SMALL_MAX_NS, lds_budget / (w * SMALL_STAGE_BYTES)));
+        const int64_t bpw = (stages + w - 1) / w * SMALL_STAGE;
+        const int waves = (int)((nb + bpw - 1) / bpw);
+        const size_t lds = (size_t)waves * ns * SMALL_STAGE_BYTES;
+        const dim3 grid((unsigned)tiles_n), block(64 * waves);
+        switch (ns) {
+        case 2: gemm_small_m_kernel<2><<<grid, block, lds, s>>>(a, (int)bpw); break;
+        case 3: gemm_small_m_kernel<3><<<grid, block, lds, s>>>(a, (int)bpw); break;
+        case 4: gemm_small_m_kernel<4><<<grid, block, lds, s>>>(a, (int)bpw); break;
+        case 5: gemm_small_m_kernel<5><<<grid, block, lds, s>>>(a, (int)bpw); break;
+        case 6: gemm_small_m_kernel<6><<<grid, block, lds, s>>>(a, (int)bpw); break;
+        case 7: gemm_small_m_kernel<7><<<grid, block, lds, s>>>(a, (int)bpw); break;
+        default: gemm_small_m_kernel<8><<<grid, block, lds, s>>>(a, (int)bpw); break;
+        }
         return hip_status("gemm_small_m_kernel");
     }
     const dim3 grid((unsigned)blocks_for(n, DenseCfg::BN), (unsigned)blocks_for(m, DenseCfg::BM));
