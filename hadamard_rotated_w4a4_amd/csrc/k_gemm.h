@@ -76,12 +76,30 @@ __global__ __launch_bounds__(C::NT) void gemm_tiled_kernel(GemmArgs a) {
     const int g = lane >> 5, c = lane & 31;
     const int64_t k = a.k, nb = k / QK;
     const int64_t tiles_n = padded_n(a.n) / TILE_N;
-    const int64_t tile0 = (int64_t)blockIdx.x * NTILES;
+
+    // Dense launches use a 1-D grid in an XCD-aware order.  Workgroups are
+    // dealt to the 8 XCDs round-robin, so ids x, x + 8, x + 16, ... share an
+    // XCD and its L2: the row tiles of one weight column tile are given ids
+    // x + 8y, i.e. the same XCD and close in dispatch time, and the weights
+    // they share are read from HBM about once.
+    int64_t bx, by;
+    if constexpr (GROUPED) {
+        bx = blockIdx.x;
+        by = blockIdx.y;
+    } else {
+        constexpr int64_t XCDS = 8;
+        const int64_t nx = (a.n + C::BN - 1) / C::BN, ny = (a.m + BM - 1) / BM;
+        const int64_t id = blockIdx.x, group = id / (XCDS * ny), in = id % (XCDS * ny);
+        const int64_t width = min(XCDS, nx - group * XCDS);  // columns in this group (last may be short)
+        bx = group * XCDS + in % width;
+        by = in / width;
+    }
+    const int64_t tile0 = bx * NTILES;
 
     int valid_rows;
     const uint8_t *wbase = a.packed;
     if constexpr (GROUPED) {
-        const int ty = blockIdx.y;
+        const int ty = (int)by;
         if (ty >= a.tile_prefix[a.n_expert]) return;  // uniform: whole workgroup exits
         int lo = 0, hi = a.n_expert;                  // largest e with tile_prefix[e] <= ty
         while (hi - lo > 1) {
@@ -103,7 +121,7 @@ __global__ __launch_bounds__(C::NT) void gemm_tiled_kernel(GemmArgs a) {
         }
         wbase = a.packed + (int64_t)e * a.expert_bytes;
     } else {
-        const int64_t row0 = (int64_t)blockIdx.y * BM;
+        const int64_t row0 = by * BM;
         valid_rows = (int)min((int64_t)BM, a.m - row0);
         for (int r = tid; r < BM; r += NT) {
             sArow[r] = r < valid_rows ? (int)(row0 + r) : -1;

@@ -39,7 +39,7 @@ using GroupedCfg = TileCfg<1, 4, 1, 2, 4>;
 
 // Row bounds that keep every grid.y within the hardware's 65535.
 constexpr int64_t kMaxGridY = 65535;
-constexpr int64_t kMaxRows = kMaxGridY * 128;
+constexpr int64_t kMaxRows = kMaxGridY * 128;  // also bounds the 1-D dense grid (< 2^31 workgroups)
 
 w4a4_status check_gemm_common(const void *packed_w, const uint8_t *codes, const float *scales,
                               const float *y, int64_t n, int64_t k) {
@@ -184,8 +184,8 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
         }
         return hip_status("gemm_small_m_kernel");
     }
-    const dim3 grid((unsigned)blocks_for(n, DenseCfg::BN), (unsigned)blocks_for(m, DenseCfg::BM));
-    gemm_tiled_kernel<DenseCfg, false><<<grid, DenseCfg::NT, 0, s>>>(a);
+    const int64_t wgs = (int64_t)blocks_for(n, DenseCfg::BN) * blocks_for(m, DenseCfg::BM);
+    gemm_tiled_kernel<DenseCfg, false><<<(unsigned)wgs, DenseCfg::NT, 0, s>>>(a);
     return hip_status("gemm_tiled_kernel");
 }
 
