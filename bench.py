@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 COLD_BYTES = 1 << 30         # weight copies rotated per step exceed this
 PROFILE_JSON = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "hadamard_rotated_w4a4_amd", "csrc", f)
-                  for f in ("common.h", "k_gemm.h", "k_rotq.h", "k_prep.h", "w4a4.hip")]
+                  for f in ("common.h", "k_gemm.h", "k_dense.h", "k_rotq.h", "k_prep.h", "w4a4.hip")]
 
 
 def log(msg):
@@ -105,6 +105,7 @@ def run_main(torch, ops, synth, steps, warmup):
     codes = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
     scales = torch.empty((m, k // 32), dtype=torch.float32, device=dev)
     y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, ops.gemm_workspace_bytes(m, n, k)), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     t_rq, t_gemm = Timer(torch), Timer(torch)
@@ -114,10 +115,10 @@ def run_main(torch, ops, synth, steps, warmup):
             with t_rq:
                 ops.rotate_quantize_act(x, codes=codes, scales=scales)
             with t_gemm:
-                ops.gemm(copies[i % len(copies)], codes, scales, n, k, y=y)
+                ops.gemm(copies[i % len(copies)], codes, scales, n, k, y=y, workspace=ws)
         else:
             ops.rotate_quantize_act(x, codes=codes, scales=scales)
-            ops.gemm(copies[i % len(copies)], codes, scales, n, k, y=y)
+            ops.gemm(copies[i % len(copies)], codes, scales, n, k, y=y, workspace=ws)
 
     for i in range(warmup):
         step(i, False)
@@ -269,13 +270,15 @@ def run_layer_prompt(torch, ops, synth):
         mbs.append({k_: torch.from_numpy(v).to(dev) for k_, v in xs.items()})
     ys = [{name: torch.empty((mb["attn_in"].shape[0], n), dtype=torch.float32, device=dev)
            for name, _, n in synth.DENSE_PROJECTIONS} for mb in mbs]
+    ws = torch.empty(max(ops.gemm_workspace_bytes(512, n, k) for _, k, n in synth.DENSE_PROJECTIONS),
+                     dtype=torch.uint8, device=dev)
 
     def layer():
         for mb, yb in zip(mbs, ys):
             q = {inp: ops.rotate_quantize_act(xin) for inp, xin in mb.items()}
             for name, k, n in synth.DENSE_PROJECTIONS:
                 c, s = q[synth.DENSE_INPUT_OF[name]]
-                ops.gemm(packed[name], c, s, n, k, y=yb[name])
+                ops.gemm(packed[name], c, s, n, k, y=yb[name], workspace=ws)
     us = graph_time_us(torch, layer, reps=5)
     tokens = sum(synth.PROMPT_MICROBATCHES)
     ops_tot = sum(2.0 * tokens * n * k for _, k, n in synth.DENSE_PROJECTIONS)

@@ -40,7 +40,8 @@ def lib() -> ctypes.CDLL:
             "w4a4_packed_weight_bytes": ([I64, I64], SZ),
             "w4a4_repack_q4_0_h32": ([P, P, I64, I64, P], ST),
             "w4a4_rotate_quantize_act": ([P, ST, I64, I64, I64, P, P, P], ST),
-            "w4a4_gemm": ([P, P, P, P, I64, I64, I64, I64, P], ST),
+            "w4a4_gemm_workspace_bytes": ([I64, I64, I64], SZ),
+            "w4a4_gemm": ([P, P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_id_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_gemm_id": ([P, I64, P, P, I64, P, I64, I64, P, I64, I64, P, SZ, P], ST),
         }
@@ -83,6 +84,10 @@ def q4_0_bytes(n: int, k: int) -> int:
 
 def packed_weight_bytes(n: int, k: int) -> int:
     return int(lib().w4a4_packed_weight_bytes(n, k))
+
+
+def gemm_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(lib().w4a4_gemm_workspace_bytes(m, n, k))
 
 
 def gemm_id_workspace_bytes(n_expert: int, n_tokens: int, top_k: int) -> int:
@@ -135,14 +140,19 @@ def rotate_quantize_act(x: torch.Tensor, k: int | None = None, codes: torch.Tens
 
 
 def gemm(packed: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: int, k: int,
-         y: torch.Tensor | None = None) -> torch.Tensor:
-    """W4A4 product: fp32 [m, n] (row stride y.stride(0))."""
-    _require_cuda(packed, codes, scales, y)
+         y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A4 product: fp32 [m, n] (row stride y.stride(0)).  The workspace is
+    allocated here unless given (uint8, at least gemm_workspace_bytes)."""
+    _require_cuda(packed, codes, scales, y, workspace)
     m = codes.shape[0]
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=codes.device)
     assert y.stride(1) == 1
+    need = gemm_workspace_bytes(m, n, k)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=codes.device)
     _check(lib().w4a4_gemm(_ptr(packed), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, y.stride(0),
+                           _ptr(workspace), 0 if workspace is None else workspace.numel(),
                            _stream(codes.device)), "w4a4_gemm")
     return y
 

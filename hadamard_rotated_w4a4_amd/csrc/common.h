@@ -27,8 +27,41 @@ __host__ __device__ inline int64_t padded_n(int64_t n) { return (n + TILE_N - 1)
 __host__ __device__ inline int64_t packed_code_bytes(int64_t n, int64_t k) {
     return padded_n(n) / TILE_N * (k / QK) * TILE_CODE_BYTES;
 }
+// Matrix-core operand section (read by the m > 16 GEMMs), after the codes
+// and scales above, 256-byte aligned: [Np/32][nbp][1 KB] with nbp = nb rounded
+// up to MX_BLOCK_PAD.  One 1 KB record per (32-column tile, block):
+//   bytes [0, 768)     fp6 E2M3 operand, [p = 0..2][column c][8 bytes]: the
+//                      six dwords of column c's 32 codes (element t at bits
+//                      6t..6t+5 of the 192-bit value; dwords 2p, 2p + 1 at p);
+//   bytes [768, 896)   per column, the bf16 pair (d1, d2) with d1 + d2 =
+//                      32 * d exactly (d the column's fp16 Q4_0 scale);
+//   bytes [896, 1024)  zero.
+// The activation operand built by the GEMM's pre-pass has the same record
+// shape per (32-row tile, block), with a bf16 triple per row at 768.
+constexpr int MX_REC = 1024;            // bytes per (tile, block) record
+constexpr int MX_CODE_BYTES = 768;      // fp6 codes of 32 rows / columns
+constexpr int MX_BLOCK_PAD = 8;         // records per tile are padded to a multiple of this
+__host__ __device__ inline int64_t mx_blocks(int64_t k) { return (k / QK + MX_BLOCK_PAD - 1) / MX_BLOCK_PAD * MX_BLOCK_PAD; }
+__host__ __device__ inline int64_t mx_section_offset(int64_t n, int64_t k) {
+    return (padded_n(n) / TILE_N * (k / QK) * (TILE_CODE_BYTES + 2 * TILE_SCALE_HALFS) + 255) / 256 * 256;
+}
 __host__ __device__ inline int64_t packed_total_bytes(int64_t n, int64_t k) {
-    return padded_n(n) / TILE_N * (k / QK) * (TILE_CODE_BYTES + 2 * TILE_SCALE_HALFS);
+    return mx_section_offset(n, k) + padded_n(n) / TILE_N * mx_blocks(k) * MX_REC;
+}
+
+// FP6 E2M3 code of the integer q in [-8, 8], read by the MFMA as q / 8: the
+// five magnitude bits of E2M3 are linear in the value for magnitudes below
+// 2 (subnormals m / 8, then 1 + m / 8), so |q| itself is the magnitude field.
+__host__ __device__ inline uint32_t fp6_e2m3_of(int q) { return (q < 0 ? 0x20u : 0u) | (uint32_t)(q < 0 ? -q : q); }
+
+// Pack 32 six-bit fields (element t at bits 6t..6t+5) into six dwords.
+__host__ __device__ inline void pack_fp6x32(const uint32_t f[32], uint32_t w[6]) {
+    for (int i = 0; i < 6; i++) w[i] = 0;
+    for (int t = 0; t < 32; t++) {
+        const int bit = 6 * t, dw = bit >> 5, off = bit & 31;
+        w[dw] |= f[t] << off;
+        if (off > 26) w[dw + 1] |= f[t] >> (32 - off);
+    }
 }
 
 // Eight packed bytes (16 signed nibbles) -> sixteen int8 lanes of an MFMA

@@ -1,0 +1,252 @@
+// Dense W4A4 GEMM for m > 16 on the gfx950 matrix cores.
+//
+// 1bit-MONSTER engine docs, "The lean option: ROCmFP4, ROCmI4 and Hadamard
+// Q4_0", section "Hadamard-rotated Q4_0: W4A4 prompt processing": int4
+// weights times int4 rotated activations on the matrix units, each block's
+// integer dot scaled into fp32.
+//
+// The integer dot of one Q4_0 block for a 32x32 output tile is one
+// v_mfma_scale_f32_32x32x64_f8f6f4 with FP6 E2M3 operands: every code q in
+// [-8, 7] is exactly q / 8 in E2M3, each product is exact and every partial
+// sum is a multiple of 1/64 far below 2^24, so the fp32 result is the integer
+// dot S exactly (scaled by 2/64).  Both K halves of the instruction carry the
+// same block (lanes l and l + 32 read the same bytes), hence the factor 2.
+// The MFMA hands back fp32, so the epilogue needs no int -> float convert.
+//
+// Per 32x32 tile and block the exact epilogue is one fp32 multiply-add per
+// output, y += (s[m] * d_w[n]) * S.  The scale product P = s (x) d_w is an
+// outer product formed by a bf16 MFMA over exact splits of the scales
+// (s = s1 + s2 + s3, 32 d_w = d1 + d2, all six partial products exact in
+// fp32).  So a tile and block cost two MFMAs and 16 vector multiply-adds per
+// lane; on gfx950 vector and matrix instructions of one SIMD overlap only
+// partly, and this kernel keeps every other vector instruction out of the
+// loop: operands arrive in the MFMA's register layout (weights repacked
+// offline, activations by a pre-pass), by direct global-to-LDS loads.
+//
+// Workgroup: 4 waves (2 x 2), each owning 2 x 2 tiles of 32x32: a 128 x 128
+// output tile.  K is walked in stages of BKB blocks through a ring of NS LDS
+// stage buffers; NS - 1 stages are in flight while one is computed.
+#pragma once
+
+#include "common.h"
+#include "k_gemm.h"
+
+namespace w4a4 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// Activation pre-pass: int4 codes [m][k/2] + fp32 scales [m][k/32] -> operand
+// records [ceil(m/32)][nbp][1 KB] (same shape as the weight records):
+//   [0, 768)    fp6 E2M3 codes, [p][row r][8 bytes] as for the weights;
+//   [768, 1024) per row the bf16 split {s1, s2, s3, 0} of the scale, read by
+//               both lane groups of the scale-product MFMA.
+// One thread per (row, padded block); padding rows and blocks are zero.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void act_operand_kernel(const uint8_t *__restrict__ codes,
+                                                          const float *__restrict__ scales, int64_t m,
+                                                          int64_t k, uint8_t *__restrict__ ws) {
+    const int64_t nb = k / QK, nbp = mx_blocks(k);
+    const int64_t rows = (m + 31) / 32 * 32;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= rows * nbp) return;
+    // consecutive threads: consecutive rows of one block (coalesced record writes)
+    const int64_t b = gid / rows, row = gid % rows;
+    uint32_t w[6] = {0, 0, 0, 0, 0, 0};
+    uint2 sop = make_uint2(0, 0);
+    if (row < m && b < nb) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(codes + row * (k / 2) + b * 16);
+        const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+        uint32_t f[32];
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            const uint32_t byte = (qw[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+            f[j] = fp6_e2m3_of(((int)(byte << 28)) >> 28);       // low nibble, two's complement
+            f[j + 16] = fp6_e2m3_of(((int)(byte << 24)) >> 28);  // high nibble
+        }
+        pack_fp6x32(f, w);
+        // exact bf16 split s = s1 + s2 + s3 (truncations; each remainder is exact)
+        const float s = scales[row * nb + b];
+        const uint32_t h1 = __float_as_uint(s) & 0xFFFF0000u;
+        const float r1 = __fsub_rn(s, __uint_as_float(h1));
+        const uint32_t h2 = __float_as_uint(r1) & 0xFFFF0000u;
+        const float r2 = __fsub_rn(r1, __uint_as_float(h2));
+        const uint32_t h3 = __float_as_uint(r2) & 0xFFFF0000u;
+        sop = make_uint2((h1 >> 16) | h2, h3 >> 16);
+    }
+    uint8_t *rec = ws + ((row / 32) * nbp + b) * MX_REC;
+    const int r = (int)(row % 32);
+#pragma unroll
+    for (int p = 0; p < 3; p++) reinterpret_cast<uint2 *>(rec)[p * 32 + r] = make_uint2(w[2 * p], w[2 * p + 1]);
+    reinterpret_cast<uint2 *>(rec + MX_CODE_BYTES)[r] = sop;
+}
+
+// ---------------------------------------------------------------------------
+// The GEMM.
+// ---------------------------------------------------------------------------
+struct MxArgs {
+    const uint8_t *act;     // activation records [rtiles][nbp][1 KB]
+    const uint8_t *wrec;    // weight records [tiles_n][nbp][1 KB]
+    float *y;
+    int64_t ldy, m, n, k;
+};
+
+template <int BKB_, int NS_>
+struct MxCfg {
+    static constexpr int BKB = BKB_, NS = NS_;
+    static constexpr int TM = 2, TN = 2, WM = 2, WN = 2, NT = 256;
+    static constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+    static constexpr int RT = BM / 32, CT = BN / 32;
+    static constexpr int STAGE_BYTES = (RT + CT) * BKB * MX_REC;
+    static constexpr int DMA_PER_STAGE = (RT + CT) * BKB;  // 1 KB each
+    static constexpr int DMA_PER_WAVE = DMA_PER_STAGE / 4;
+    static_assert(DMA_PER_STAGE % 4 == 0, "loads split evenly over the 4 waves");
+    static_assert(MX_BLOCK_PAD % BKB == 0, "stages tile the padded block range");
+};
+
+// One global-to-LDS load of 16 bytes per lane: lane l's bytes at `g` land at
+// LDS byte address lds + 16 l (lds is wave-uniform, passed through M0).
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_mx_kernel(MxArgs a) {
+    constexpr int BKB = C::BKB, NS = C::NS, TM = C::TM, TN = C::TN, RT = C::RT;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int g = lane >> 5, c = lane & 31;
+    const int64_t nbp = mx_blocks(a.k);
+    const int64_t rtiles = (a.m + 31) / 32, ctiles = padded_n(a.n) / TILE_N;
+
+    // XCD-aware 1-D grid: workgroups are dealt to the 8 XCDs round-robin, so
+    // ids x, x + 8, x + 16, ... share an XCD and its L2; the row tiles of one
+    // weight column tile get ids x + 8y and read those weights from HBM ~once.
+    constexpr int64_t XCDS = 8;
+    const int64_t nx = (a.n + C::BN - 1) / C::BN, ny = (a.m + C::BM - 1) / C::BM;
+    const int64_t id = blockIdx.x, group = id / (XCDS * ny), in = id % (XCDS * ny);
+    const int64_t width = min(XCDS, nx - group * XCDS);
+    const int64_t bx = group * XCDS + in % width, by = in / width;
+    const int64_t rt0 = by * RT, ct0 = bx * C::CT;
+
+    // ---- this wave's loads: DMA_PER_WAVE records of 1 KB per stage ----
+    // load i = wave * DMA_PER_WAVE + d covers tile i / BKB (row tiles first,
+    // then column tiles), block i % BKB of the stage.  Tiles past the matrix
+    // edge are clamped to the last one (their outputs are never stored).
+    const uint8_t *src[C::DMA_PER_WAVE];
+    uint32_t dst[C::DMA_PER_WAVE];
+    const uint32_t smem_base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)smem;
+#pragma unroll
+    for (int d = 0; d < C::DMA_PER_WAVE; d++) {
+        const int i = wave * C::DMA_PER_WAVE + d, t = i / BKB, bb = i % BKB;
+        const uint8_t *base = t < RT ? a.act + min(rt0 + t, rtiles - 1) * nbp * MX_REC
+                                     : a.wrec + min(ct0 + t - RT, ctiles - 1) * nbp * MX_REC;
+        src[d] = base + bb * MX_REC + lane * 16;
+        dst[d] = (uint32_t)((t * BKB + bb) * MX_REC);
+    }
+    const int nstages = (int)(nbp / BKB);
+    auto issue = [&](int stage, int slot) {
+        // past the last stage the ring keeps reloading the last one (its
+        // slot is never computed): the count of loads in flight stays fixed
+        const int64_t kb0 = (int64_t)min(stage, nstages - 1) * BKB;
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(smem_base + slot * C::STAGE_BYTES);
+#pragma unroll
+        for (int d = 0; d < C::DMA_PER_WAVE; d++) dma16(src[d] + kb0 * MX_REC, lds + dst[d]);
+    };
+
+    // scale-product operand of the weights: lane group g reads {d_g, d_g, d_g, 0}
+    const uint32_t sel0 = g ? 0x03020302u : 0x01000100u, sel1 = g ? 0x0C0C0302u : 0x0C0C0100u;
+
+    v16f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
+
+#pragma unroll
+    for (int s = 0; s < NS - 1; s++) issue(s, s);
+
+    for (int s = 0; s < nstages; s++) {
+        // this wave's loads of stage s have landed (NS - 2 later stages may
+        // still be in flight); the barrier makes every wave's visible and
+        // guarantees stage s - 1's slot is no longer read
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 2)) : "memory");
+        __syncthreads();
+        issue(s + NS - 1, (s + NS - 1) % NS);
+        const uint8_t *st = smem + (s % NS) * C::STAGE_BYTES;
+
+        v8i af[2][TM], bf[2][TN];
+        uint2 ap[2][TM], bp[2][TN];
+        auto load_frags = [&](int bb, int buf) {
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+                const uint8_t *rec = st + ((wm * TM + i) * BKB + bb) * MX_REC;
+                const uint2 w0 = reinterpret_cast<const uint2 *>(rec)[c];
+                const uint2 w1 = reinterpret_cast<const uint2 *>(rec)[32 + c];
+                const uint2 w2 = reinterpret_cast<const uint2 *>(rec)[64 + c];
+                af[buf][i] = (v8i){(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y, (int)w2.x, (int)w2.y, 0, 0};
+                ap[buf][i] = reinterpret_cast<const uint2 *>(rec + MX_CODE_BYTES)[c];
+            }
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const uint8_t *rec = st + ((RT + wn * TN + j) * BKB + bb) * MX_REC;
+                const uint2 w0 = reinterpret_cast<const uint2 *>(rec)[c];
+                const uint2 w1 = reinterpret_cast<const uint2 *>(rec)[32 + c];
+                const uint2 w2 = reinterpret_cast<const uint2 *>(rec)[64 + c];
+                bf[buf][j] = (v8i){(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y, (int)w2.x, (int)w2.y, 0, 0};
+                const uint32_t sw = reinterpret_cast<const uint32_t *>(rec + MX_CODE_BYTES)[c];
+                bp[buf][j] = make_uint2(__builtin_amdgcn_perm(sw, sw, sel0), __builtin_amdgcn_perm(sw, sw, sel1));
+            }
+        };
+
+        // Software pipeline over the stage's BKB * TM * TN tile steps: the two
+        // MFMAs of step t + 1 are issued before the multiply-adds of step t,
+        // and the operands of block bb + 1 are read while block bb computes.
+        // The scheduling barriers keep that order (loads and scalar work may
+        // cross them).
+        constexpr int STEPS = BKB * TM * TN, PER = TM * TN;
+        v16f S[2], P[2];
+        load_frags(0, 0);
+        S[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][0], bf[0][0], v16f{}, 2, 2, 0, 0, 0, 0);
+        P[0] = mfma_bf16_32x32x8(ap[0][0], bp[0][0]);
+#pragma unroll
+        for (int t = 0; t < STEPS; t++) {
+            const int i = (t / TN) % TM, j = t % TN;
+            if (t % PER == 0 && t / PER + 1 < BKB) load_frags(t / PER + 1, (t / PER + 1) & 1);
+            if (t + 1 < STEPS) {
+                const int t1 = t + 1, b1 = (t1 / PER) & 1, i1 = (t1 / TN) % TM, j1 = t1 % TN;
+                S[t1 & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[b1][i1], bf[b1][j1], v16f{}, 2, 2,
+                                                                            0, 0, 0, 0);
+                P[t1 & 1] = mfma_bf16_32x32x8(ap[b1][i1], bp[b1][j1]);
+            }
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[i][j][v] = fmaf(S[t & 1][v], P[t & 1][v], acc[i][j][v]);
+            asm volatile("" : "+v"(acc[i][j]));  // materialised here, not sunk past the loop's end
+            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still be writing LDS at exit
+
+    // ---- store ----
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+        const int64_t rbase = (rt0 + wm * TM + i) * 32;
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int64_t col = (ct0 + wn * TN + j) * 32 + c;
+            if (col >= a.n) continue;
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int64_t r = rbase + mfma32_row(v, lane);
+                if (r < a.m) a.y[r * a.ldy + col] = acc[i][j][v];
+            }
+        }
+    }
+}
+
+}  // namespace w4a4

@@ -93,4 +93,39 @@ __global__ __launch_bounds__(256) void repack_kernel(const uint8_t *__restrict__
     }
 }
 
+// Matrix-core operand records (see common.h), one thread per (tile, padded
+// block, column).  Padding columns and blocks get zero codes and zero scales.
+__global__ __launch_bounds__(256) void repack_mx_kernel(const uint8_t *__restrict__ q4, int64_t n,
+                                                        int64_t k, uint8_t *__restrict__ packed) {
+    const int64_t nb = k / QK, nbp = mx_blocks(k);
+    const int64_t tiles = padded_n(n) / TILE_N;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= tiles * nbp * 32) return;
+    const int c = (int)(gid & 31);
+    const int64_t tb = gid >> 5;  // tile * nbp + b
+    const int64_t tile = tb / nbp, b = tb % nbp;
+    const int64_t col = tile * TILE_N + c;
+    uint32_t w[6] = {0, 0, 0, 0, 0, 0};
+    uint32_t sw = 0;
+    if (col < n && b < nb) {
+        const uint8_t *blk = q4 + (col * nb + b) * 18;
+        uint32_t f[32];
+        for (int j = 0; j < 16; j++) {
+            f[j] = fp6_e2m3_of((int)(blk[2 + j] & 0xF) - 8);
+            f[j + 16] = fp6_e2m3_of((int)(blk[2 + j] >> 4) - 8);
+        }
+        pack_fp6x32(f, w);
+        // 32 * d: the MFMA reads codes as q / 8 and sums both K halves (x 2)
+        const float d = __half2float(__ushort_as_half((uint16_t)(blk[0] | (blk[1] << 8)))) * 32.0f;
+        const uint32_t h1 = __float_as_uint(d) & 0xFFFF0000u;
+        const float r1 = __fsub_rn(d, __uint_as_float(h1));  // exact: at most 3 significant bits remain
+        sw = (h1 >> 16) | (__float_as_uint(r1) & 0xFFFF0000u);
+    }
+    uint8_t *rec = packed + mx_section_offset(n, k) + tb * MX_REC;
+    for (int p = 0; p < 3; p++)
+        reinterpret_cast<uint2 *>(rec)[p * 32 + c] = make_uint2(w[2 * p], w[2 * p + 1]);
+    reinterpret_cast<uint32_t *>(rec + MX_CODE_BYTES)[c] = sw;
+    reinterpret_cast<uint32_t *>(rec + MX_CODE_BYTES + 128)[c] = 0u;
+}
+
 }  // namespace w4a4

@@ -11,6 +11,7 @@
 #include <cstring>
 
 #include "common.h"
+#include "k_dense.h"
 #include "k_gemm.h"
 #include "k_prep.h"
 #include "k_rotq.h"
@@ -32,8 +33,8 @@ inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 inline unsigned blocks_for(int64_t work, int per) { return (unsigned)((work + per - 1) / per); }
 
-// Dense large-M tiles: 8 waves in 2 x 4, each 32 x 32, 64 x 128 per workgroup.
-using DenseCfg = TileCfg<2, 4, 1, 1, 4>;
+// Dense m > 16: 128 x 128 workgroup tiles, stages of 2 blocks, a ring of 4 stages.
+using DenseMx = MxCfg<2, 4>;
 // Grouped expert tiles: 32 rows (experts are small), 4 waves across 256 columns.
 using GroupedCfg = TileCfg<1, 4, 1, 2, 4>;
 
@@ -102,7 +103,12 @@ w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int6
     const int64_t threads = padded_n(n) / TILE_N * (k / QK) * 64;
     repack_kernel<<<blocks_for(threads, 256), 256, 0, as_stream(stream)>>>(
         static_cast<const uint8_t *>(q4_0), n, k, static_cast<uint8_t *>(packed));
-    return hip_status("repack_kernel");
+    const w4a4_status st = hip_status("repack_kernel");
+    if (st != W4A4_OK) return st;
+    const int64_t mx_threads = padded_n(n) / TILE_N * mx_blocks(k) * 32;
+    repack_mx_kernel<<<blocks_for(mx_threads, 256), 256, 0, as_stream(stream)>>>(
+        static_cast<const uint8_t *>(q4_0), n, k, static_cast<uint8_t *>(packed));
+    return hip_status("repack_mx_kernel");
 }
 
 w4a4_status w4a4_rotate_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
@@ -131,8 +137,15 @@ w4a4_status w4a4_rotate_quantize_act(const void *x, w4a4_dtype dt, int64_t m, in
     return hip_status("rotate_quantize_kernel");
 }
 
+size_t w4a4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+    if (m < 0 || n < 0 || k < 0 || k % QK) return 0;
+    if (m <= SMALL_M_MAX || n == 0 || k == 0) return 0;
+    return (size_t)((m + 31) / 32 * mx_blocks(k) * MX_REC);
+}
+
 w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *scales, float *y,
-                      int64_t m, int64_t n, int64_t k, int64_t ldy, void *stream) {
+                      int64_t m, int64_t n, int64_t k, int64_t ldy, void *workspace, size_t workspace_bytes,
+                      void *stream) {
     if (m < 0 || m > kMaxRows || ldy < n) return W4A4_ERR_INVALID_VALUE;
     if (m == 0 || n == 0) {
         if (n < 0 || k < 0) return W4A4_ERR_INVALID_VALUE;
@@ -145,17 +158,17 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
         zero_rows_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(y, m, n, ldy);
         return hip_status("zero_rows_kernel");
     }
-    GemmArgs a{};
-    a.codes = codes;
-    a.scales = scales;
-    a.packed = static_cast<const uint8_t *>(packed_w);
-    a.y = y;
-    a.ldy = ldy;
-    a.m = m;
-    a.n = n;
-    a.k = k;
-    const int64_t tiles_n = padded_n(n) / TILE_N;
     if (m <= SMALL_M_MAX) {
+        GemmArgs a{};
+        a.codes = codes;
+        a.scales = scales;
+        a.packed = static_cast<const uint8_t *>(packed_w);
+        a.y = y;
+        a.ldy = ldy;
+        a.m = m;
+        a.n = n;
+        a.k = k;
+        const int64_t tiles_n = padded_n(n) / TILE_N;
         // One workgroup per 32-column tile, all resident in one round.  Most
         // waves per tile first (runs of >= 4 stages, <= 6 waves per SIMD):
         // one wave's compute is a serial MFMA chain, so spreading K wins.
@@ -184,9 +197,25 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
         }
         return hip_status("gemm_small_m_kernel");
     }
-    const int64_t wgs = (int64_t)blocks_for(n, DenseCfg::BN) * blocks_for(m, DenseCfg::BM);
-    gemm_tiled_kernel<DenseCfg, false><<<(unsigned)wgs, DenseCfg::NT, 0, s>>>(a);
-    return hip_status("gemm_tiled_kernel");
+    if (!workspace) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(workspace, 256)) return W4A4_ERR_MISALIGNED;
+    if (workspace_bytes < w4a4_gemm_workspace_bytes(m, n, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const int64_t pre_threads = (m + 31) / 32 * 32 * mx_blocks(k);
+    act_operand_kernel<<<blocks_for(pre_threads, 256), 256, 0, s>>>(codes, scales, m, k, ws);
+    const w4a4_status pst = hip_status("act_operand_kernel");
+    if (pst != W4A4_OK) return pst;
+    MxArgs a{};
+    a.act = ws;
+    a.wrec = static_cast<const uint8_t *>(packed_w) + mx_section_offset(n, k);
+    a.y = y;
+    a.ldy = ldy;
+    a.m = m;
+    a.n = n;
+    a.k = k;
+    const int64_t wgs = (int64_t)blocks_for(n, DenseMx::BN) * blocks_for(m, DenseMx::BM);
+    gemm_mx_kernel<DenseMx><<<(unsigned)wgs, DenseMx::NT, 0, s>>>(a);
+    return hip_status("gemm_mx_kernel");
 }
 
 size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t top_k) {

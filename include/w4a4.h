@@ -83,9 +83,12 @@ size_t w4a4_packed_weight_bytes(int64_t n, int64_t k);
  *           name is the caller's assertion that the weights were rotated:
  *           unrotated weights give silently wrong products.
  *   packed  out, w4a4_packed_weight_bytes(n, k) bytes, 256-byte aligned.  Its
- *           layout is private to this library.  Each code is stored as q ^ 8,
- *           which read as a signed nibble is exactly q - 8 (the page's
- *           identity), so the weights stay exact.
+ *           layout is private to this library.  It holds the weights twice,
+ *           losslessly: 4-bit codes stored as q ^ 8 (read as a signed nibble
+ *           that is exactly q - 8, the page's identity) with the fp16 scales,
+ *           streamed by the m <= 16 kernel; and the matrix-core operand of the
+ *           m > 16 kernels (each q - 8 as an FP6 E2M3 code, the scale as an
+ *           exact bf16 pair), 8 bits per weight.
  */
 w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int64_t k,
                                  void *stream);
@@ -106,17 +109,27 @@ w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int6
 w4a4_status w4a4_rotate_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k,
                                      int64_t ldx, uint8_t *codes, float *scales, void *stream);
 
+/* Workspace bytes w4a4_gemm needs for these sizes (0 when m <= 16 or an
+ * argument is invalid).  Host only, pure. */
+size_t w4a4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
 /*
  * Dense W4A4 product: y[i][j] = sum_b d_w[j][b] * s[i][b] * S[i][j][b], where
- * S = sum_t (q_w - 8) * q_a is the exact integer dot of block b (int8 matrix
- * cores), accumulated in fp32 (block order ascending within a thread).
- *   packed_w  from w4a4_repack_q4_0_h32(n, k).
+ * S = sum_t (q_w - 8) * q_a is the exact integer dot of block b, accumulated
+ * in fp32 (block order ascending within a thread).
+ *   packed_w  from w4a4_repack_q4_0_h32(n, k), 16-byte aligned.
  *   codes, scales  from w4a4_rotate_quantize_act (m rows).
  *   y         out, [m][ldy] fp32, ldy >= n, 4-byte aligned.
- * m <= 16 takes a weight-streaming kernel; larger m a tiled MFMA kernel.
+ *   workspace device scratch of w4a4_gemm_workspace_bytes(m, n, k) bytes,
+ *             256-byte aligned (may be NULL when that is 0); contents on entry
+ *             are ignored.  Calls that share a workspace must not overlap.
+ * m <= 16 takes a weight-streaming kernel on the 4-bit codes.  Larger m first
+ * re-lays the activation codes and scales into the matrix-core operand format
+ * in the workspace, then runs the tiled matrix-core kernel.
  */
 w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *scales, float *y,
-                      int64_t m, int64_t n, int64_t k, int64_t ldy, void *stream);
+                      int64_t m, int64_t n, int64_t k, int64_t ldy, void *workspace,
+                      size_t workspace_bytes, void *stream);
 
 /* Workspace bytes w4a4_gemm_id needs.  Host only, pure. */
 size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t top_k);

@@ -42,9 +42,10 @@ def test_status_strings(L):
 
 def test_size_queries(L):
     assert L.w4a4_q4_0_bytes(17408, 5120) == 17408 * 160 * 18
-    # packed = 32-column tiles x blocks x (512 code bytes + 32 fp16 scales)
-    assert L.w4a4_packed_weight_bytes(17408, 5120) == 17408 * 160 * 18
-    assert L.w4a4_packed_weight_bytes(33, 64) == 64 * 2 * 18  # n padded to 64
+    # packed = 32-column tiles x blocks x (512 code bytes + 32 fp16 scales),
+    # rounded up to 256 bytes, then 32-column tiles x blocks padded to 8 x 1 KB
+    assert L.w4a4_packed_weight_bytes(17408, 5120) == 17408 * 160 * 18 + 544 * 160 * 1024
+    assert L.w4a4_packed_weight_bytes(33, 64) == 2 * 2 * 576 + 2 * 8 * 1024  # n padded to 64
     assert L.w4a4_packed_weight_bytes(10, 33) == 0
     assert L.w4a4_gemm_id_workspace_bytes(128, 1024, 8) == 2 * 768 + 32768
     assert L.w4a4_gemm_id_workspace_bytes(-1, 1, 1) == 0
@@ -60,21 +61,29 @@ def P(x):
 
 def test_gemm_validation(L):
     g = L.w4a4_gemm
-    assert g(P(A), P(A), P(A), P(A), 64, 64, 33, 64, None) == KMUL
-    assert g(P(A), P(A), P(A), P(A), -1, 64, 64, 64, None) == INVALID
-    assert g(P(A), P(A), P(A), P(A), 8, -1, 64, 64, None) == INVALID
-    assert g(P(A), P(A), P(A), P(A), 8, 64, 64, 63, None) == INVALID  # ldy < n
-    assert g(None, P(A), P(A), P(A), 8, 64, 64, 64, None) == INVALID
-    assert g(P(A), None, P(A), P(A), 8, 64, 64, 64, None) == INVALID
-    assert g(P(A), P(A), None, P(A), 8, 64, 64, 64, None) == INVALID
-    assert g(P(A), P(A), P(A), None, 8, 64, 64, 64, None) == INVALID
-    assert g(P(A), P(A + 8), P(A), P(A), 8, 64, 64, 64, None) == MISALIGNED  # codes need 16 B
-    assert g(P(A + 8), P(A), P(A), P(A), 8, 64, 64, 64, None) == MISALIGNED  # packed needs 16 B
-    assert g(P(A), P(A), P(ODD), P(A), 8, 64, 64, 64, None) == MISALIGNED
-    assert g(P(A), P(A), P(A), P(A + 2), 8, 64, 64, 64, None) == MISALIGNED
+    assert g(P(A), P(A), P(A), P(A), 64, 64, 33, 64, None, 0, None) == KMUL
+    assert g(P(A), P(A), P(A), P(A), -1, 64, 64, 64, None, 0, None) == INVALID
+    assert g(P(A), P(A), P(A), P(A), 8, -1, 64, 64, None, 0, None) == INVALID
+    assert g(P(A), P(A), P(A), P(A), 8, 64, 64, 63, None, 0, None) == INVALID  # ldy < n
+    assert g(None, P(A), P(A), P(A), 8, 64, 64, 64, None, 0, None) == INVALID
+    assert g(P(A), None, P(A), P(A), 8, 64, 64, 64, None, 0, None) == INVALID
+    assert g(P(A), P(A), None, P(A), 8, 64, 64, 64, None, 0, None) == INVALID
+    assert g(P(A), P(A), P(A), None, 8, 64, 64, 64, None, 0, None) == INVALID
+    assert g(P(A), P(A + 8), P(A), P(A), 8, 64, 64, 64, None, 0, None) == MISALIGNED  # codes need 16 B
+    assert g(P(A + 8), P(A), P(A), P(A), 8, 64, 64, 64, None, 0, None) == MISALIGNED  # packed needs 16 B
+    assert g(P(A), P(A), P(ODD), P(A), 8, 64, 64, 64, None, 0, None) == MISALIGNED
+    assert g(P(A), P(A), P(A), P(A + 2), 8, 64, 64, 64, None, 0, None) == MISALIGNED
     # nothing to do: no launch, no pointer needed
-    assert g(None, None, None, None, 0, 64, 64, 64, None) == OK
-    assert g(None, None, None, None, 8, 0, 64, 0, None) == OK
+    assert g(None, None, None, None, 0, 64, 64, 64, None, 0, None) == OK
+    assert g(None, None, None, None, 8, 0, 64, 0, None, 0, None) == OK
+    # m > 16 needs the workspace the size query names, 256-byte aligned
+    need = L.w4a4_gemm_workspace_bytes(64, 64, 64)
+    assert need == 2 * 8 * 1024  # 32-row tiles x blocks padded to 8 x 1 KB records
+    assert L.w4a4_gemm_workspace_bytes(16, 64, 64) == 0
+    assert L.w4a4_gemm_workspace_bytes(17, 64, 33) == 0
+    assert g(P(A), P(A), P(A), P(A), 64, 64, 64, 64, None, need, None) == INVALID
+    assert g(P(A), P(A), P(A), P(A), 64, 64, 64, 64, P(A + 16), need, None) == MISALIGNED
+    assert g(P(A), P(A), P(A), P(A), 64, 64, 64, 64, P(A), need - 1, None) == WS
 
 
 def test_rotate_quantize_validation(L):
