@@ -29,12 +29,17 @@ __host__ __device__ inline int64_t packed_code_bytes(int64_t n, int64_t k) {
 }
 // Matrix-core operand section (read by the m > 16 GEMMs), after the codes
 // and scales above, 256-byte aligned: [Np/32][nbp][1 KB] with nbp = nb rounded
-// up to MX_BLOCK_PAD.  One 1 KB record per (32-column tile, block):
-//   bytes [0, 768)     fp6 E2M3 operand, [p = 0..2][column c][8 bytes]: the
-//                      six dwords of column c's 32 codes (element t at bits
-//                      6t..6t+5 of the 192-bit value; dwords 2p, 2p + 1 at p);
+// up to MX_BLOCK_PAD.  One 1 KB record per (32-column tile, block), laid out
+// as the MFMA's lanes want it.  Lane l = 32 g + c stands for column c and K
+// half g; it carries codes 16 g .. 16 g + 15 of the column's block as FP6
+// E2M3 (code t at bits 6 (t - 16 g) of a 96-bit value; the lane's other 96
+// operand bits are zero), so the two K halves of one 32x32x64 MFMA together
+// hold the 32 codes once:
+//   bytes [0, 512)     dwords 0..1 of lane l at 8 l;
+//   bytes [512, 768)   dword 2 of lane l at 512 + 4 l (both planes are read
+//                      conflict-free by a wave);
 //   bytes [768, 896)   per column, the bf16 pair (d1, d2) with d1 + d2 =
-//                      32 * d exactly (d the column's fp16 Q4_0 scale);
+//                      64 * d exactly (d the column's fp16 Q4_0 scale);
 //   bytes [896, 1024)  zero.
 // The activation operand built by the GEMM's pre-pass has the same record
 // shape per (32-row tile, block), with a bf16 triple per row at 768.
@@ -54,14 +59,20 @@ __host__ __device__ inline int64_t packed_total_bytes(int64_t n, int64_t k) {
 // 2 (subnormals m / 8, then 1 + m / 8), so |q| itself is the magnitude field.
 __host__ __device__ inline uint32_t fp6_e2m3_of(int q) { return (q < 0 ? 0x20u : 0u) | (uint32_t)(q < 0 ? -q : q); }
 
-// Pack 32 six-bit fields (element t at bits 6t..6t+5) into six dwords.
-__host__ __device__ inline void pack_fp6x32(const uint32_t f[32], uint32_t w[6]) {
-    for (int i = 0; i < 6; i++) w[i] = 0;
-    for (int t = 0; t < 32; t++) {
-        const int bit = 6 * t, dw = bit >> 5, off = bit & 31;
-        w[dw] |= f[t] << off;
-        if (off > 26) w[dw + 1] |= f[t] >> (32 - off);
+// Pack 16 six-bit fields (element j at bits 6j..6j+5) into three dwords.
+__host__ __device__ inline void pack_fp6x16(const uint32_t f[16], uint32_t w[3]) {
+    w[0] = w[1] = w[2] = 0;
+    for (int j = 0; j < 16; j++) {
+        const int bit = 6 * j, dw = bit >> 5, off = bit & 31;
+        w[dw] |= f[j] << off;
+        if (off > 26) w[dw + 1] |= f[j] >> (32 - off);
     }
+}
+
+// Write one lane's three operand dwords into a record (layout above).
+__host__ __device__ inline void put_mx_lane(uint8_t *rec, int lane, const uint32_t w[3]) {
+    reinterpret_cast<uint2 *>(rec)[lane] = make_uint2(w[0], w[1]);
+    reinterpret_cast<uint32_t *>(rec + 512)[lane] = w[2];
 }
 
 // Eight packed bytes (16 signed nibbles) -> sixteen int8 lanes of an MFMA

@@ -9,14 +9,15 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4 with FP6 E2M3 operands: every code q in
 // [-8, 7] is exactly q / 8 in E2M3, each product is exact and every partial
 // sum is a multiple of 1/64 far below 2^24, so the fp32 result is the integer
-// dot S exactly (scaled by 2/64).  Both K halves of the instruction carry the
-// same block (lanes l and l + 32 read the same bytes), hence the factor 2.
-// The MFMA hands back fp32, so the epilogue needs no int -> float convert.
+// dot S exactly (scaled by 1/64).  Each K half of the instruction carries 16
+// of the block's 32 codes (padded with zeros), so a lane reads 12 bytes of
+// operand per block.  The MFMA hands back fp32, so the epilogue needs no
+// int -> float convert.
 //
 // Per 32x32 tile and block the exact epilogue is one fp32 multiply-add per
 // output, y += (s[m] * d_w[n]) * S.  The scale product P = s (x) d_w is an
 // outer product formed by a bf16 MFMA over exact splits of the scales
-// (s = s1 + s2 + s3, 32 d_w = d1 + d2, all six partial products exact in
+// (s = s1 + s2 + s3, 64 d_w = d1 + d2, all six partial products exact in
 // fp32).  So a tile and block cost two MFMAs and 16 vector multiply-adds per
 // lane; on gfx950 vector and matrix instructions of one SIMD overlap only
 // partly, and this kernel keeps every other vector instruction out of the
@@ -38,7 +39,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 // ---------------------------------------------------------------------------
 // Activation pre-pass: int4 codes [m][k/2] + fp32 scales [m][k/32] -> operand
 // records [ceil(m/32)][nbp][1 KB] (same shape as the weight records):
-//   [0, 768)    fp6 E2M3 codes, [p][row r][8 bytes] as for the weights;
+//   [0, 768)    fp6 E2M3 codes of row r, laid out as for the weights;
 //   [768, 1024) per row the bf16 split {s1, s2, s3, 0} of the scale, read by
 //               both lane groups of the scale-product MFMA.
 // One thread per (row, padded block); padding rows and blocks are zero.
@@ -52,19 +53,20 @@ __global__ __launch_bounds__(256) void act_operand_kernel(const uint8_t *__restr
     if (gid >= rows * nbp) return;
     // consecutive threads: consecutive rows of one block (coalesced record writes)
     const int64_t b = gid / rows, row = gid % rows;
-    uint32_t w[6] = {0, 0, 0, 0, 0, 0};
+    uint32_t lo[3] = {0, 0, 0}, hi[3] = {0, 0, 0};
     uint2 sop = make_uint2(0, 0);
     if (row < m && b < nb) {
         const uint4 q = *reinterpret_cast<const uint4 *>(codes + row * (k / 2) + b * 16);
         const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
-        uint32_t f[32];
+        uint32_t f0[16], f1[16];
 #pragma unroll
         for (int j = 0; j < 16; j++) {
             const uint32_t byte = (qw[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-            f[j] = fp6_e2m3_of(((int)(byte << 28)) >> 28);       // low nibble, two's complement
-            f[j + 16] = fp6_e2m3_of(((int)(byte << 24)) >> 28);  // high nibble
+            f0[j] = fp6_e2m3_of(((int)(byte << 28)) >> 28);  // code j: low nibble, two's complement
+            f1[j] = fp6_e2m3_of(((int)(byte << 24)) >> 28);  // code j + 16: high nibble
         }
-        pack_fp6x32(f, w);
+        pack_fp6x16(f0, lo);
+        pack_fp6x16(f1, hi);
         // exact bf16 split s = s1 + s2 + s3 (truncations; each remainder is exact)
         const float s = scales[row * nb + b];
         const uint32_t h1 = __float_as_uint(s) & 0xFFFF0000u;
@@ -76,8 +78,8 @@ __global__ __launch_bounds__(256) void act_operand_kernel(const uint8_t *__restr
     }
     uint8_t *rec = ws + ((row / 32) * nbp + b) * MX_REC;
     const int r = (int)(row % 32);
-#pragma unroll
-    for (int p = 0; p < 3; p++) reinterpret_cast<uint2 *>(rec)[p * 32 + r] = make_uint2(w[2 * p], w[2 * p + 1]);
+    put_mx_lane(rec, r, lo);
+    put_mx_lane(rec, 32 + r, hi);
     reinterpret_cast<uint2 *>(rec + MX_CODE_BYTES)[r] = sop;
 }
 
@@ -103,6 +105,17 @@ struct MxCfg {
     static_assert(DMA_PER_STAGE % 4 == 0, "loads split evenly over the 4 waves");
     static_assert(MX_BLOCK_PAD % BKB == 0, "stages tile the padded block range");
 };
+
+// LDS reads of one fragment.  They are volatile so that the compiler never
+// merges reads of two different fragments into one instruction (that would
+// scatter a fragment over non-adjacent registers and cost moves and early
+// waits); immediate offsets still fold.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <class T>
+__device__ __forceinline__ T lds_read(const uint8_t *p) {
+    return *reinterpret_cast<const volatile __attribute__((address_space(3))) T *>(
+        (const __attribute__((address_space(3))) uint8_t *)p);
+}
 
 // One global-to-LDS load of 16 bytes per lane: lane l's bytes at `g` land at
 // LDS byte address lds + 16 l (lds is wave-uniform, passed through M0).
@@ -168,64 +181,87 @@ __global__ __launch_bounds__(C::NT) void gemm_mx_kernel(MxArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
+    // ---- one software pipeline over all blocks ----
+    // Step t of a stage = (block t / PER, tile t % PER).  The two MFMAs of
+    // step t + 1 are issued around the first half of step t's multiply-adds;
+    // the operands of the next block are read while the current one computes
+    // (the weights' scale word is expanded only where it is used, so nothing
+    // waits for those reads early).  The wait + barrier that publishes stage
+    // s + 1 sits at the start of stage s's last block, so the pipeline never
+    // drains at a stage boundary.
+    static_assert(BKB % 2 == 0, "operand buffers alternate per block");
+    static_assert(NS >= 3, "one stage in flight besides the two in use");
+    constexpr int STEPS = BKB * TM * TN, PER = TM * TN;
+    v8i af[2][TM] = {}, bf[2][TN] = {};  // operand dwords 3..7 are zero
+    uint2 ap[2][TM];
+    uint32_t bw[2][TN];
+    auto load_frags = [&](const uint8_t *st, int bb, int buf) {
 #pragma unroll
-    for (int s = 0; s < NS - 1; s++) issue(s, s);
+        for (int i = 0; i < TM; i++) {
+            const uint8_t *rec = st + ((wm * TM + i) * BKB + bb) * MX_REC;
+            const u32x2 f01 = lds_read<u32x2>(rec + 8 * lane);
+            const uint32_t f2 = lds_read<uint32_t>(rec + 512 + 4 * lane);
+            af[buf][i][0] = (int)f01.x;  // elements 3..7 stay zero
+            af[buf][i][1] = (int)f01.y;
+            af[buf][i][2] = (int)f2;
+            const u32x2 sp = lds_read<u32x2>(rec + MX_CODE_BYTES + 8 * c);
+            ap[buf][i] = make_uint2(sp.x, sp.y);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const uint8_t *rec = st + ((RT + wn * TN + j) * BKB + bb) * MX_REC;
+            const u32x2 f01 = lds_read<u32x2>(rec + 8 * lane);
+            const uint32_t f2 = lds_read<uint32_t>(rec + 512 + 4 * lane);
+            bf[buf][j][0] = (int)f01.x;
+            bf[buf][j][1] = (int)f01.y;
+            bf[buf][j][2] = (int)f2;
+            bw[buf][j] = lds_read<uint32_t>(rec + MX_CODE_BYTES + 4 * c);
+        }
+    };
+    auto mfma_s = [&](int buf, int i, int j) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[buf][i], bf[buf][j], v16f{}, 2, 2, 0, 0, 0, 0);
+    };
+    auto mfma_p = [&](int buf, int i, int j) {
+        const uint32_t w = bw[buf][j];
+        return mfma_bf16_32x32x8(ap[buf][i], make_uint2(__builtin_amdgcn_perm(w, w, sel0), __builtin_amdgcn_perm(w, w, sel1)));
+    };
+
+#pragma unroll
+    for (int x = 0; x < NS - 1; x++) issue(x, x);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 2)) : "memory");
+    __syncthreads();
+    v16f S[2], P[2];
+    load_frags(smem, 0, 0);
+    S[0] = mfma_s(0, 0, 0);
+    P[0] = mfma_p(0, 0, 0);
 
     for (int s = 0; s < nstages; s++) {
-        // this wave's loads of stage s have landed (NS - 2 later stages may
-        // still be in flight); the barrier makes every wave's visible and
-        // guarantees stage s - 1's slot is no longer read
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 2)) : "memory");
-        __syncthreads();
-        issue(s + NS - 1, (s + NS - 1) % NS);
         const uint8_t *st = smem + (s % NS) * C::STAGE_BYTES;
-
-        v8i af[2][TM], bf[2][TN];
-        uint2 ap[2][TM], bp[2][TN];
-        auto load_frags = [&](int bb, int buf) {
-#pragma unroll
-            for (int i = 0; i < TM; i++) {
-                const uint8_t *rec = st + ((wm * TM + i) * BKB + bb) * MX_REC;
-                const uint2 w0 = reinterpret_cast<const uint2 *>(rec)[c];
-                const uint2 w1 = reinterpret_cast<const uint2 *>(rec)[32 + c];
-                const uint2 w2 = reinterpret_cast<const uint2 *>(rec)[64 + c];
-                af[buf][i] = (v8i){(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y, (int)w2.x, (int)w2.y, 0, 0};
-                ap[buf][i] = reinterpret_cast<const uint2 *>(rec + MX_CODE_BYTES)[c];
-            }
-#pragma unroll
-            for (int j = 0; j < TN; j++) {
-                const uint8_t *rec = st + ((RT + wn * TN + j) * BKB + bb) * MX_REC;
-                const uint2 w0 = reinterpret_cast<const uint2 *>(rec)[c];
-                const uint2 w1 = reinterpret_cast<const uint2 *>(rec)[32 + c];
-                const uint2 w2 = reinterpret_cast<const uint2 *>(rec)[64 + c];
-                bf[buf][j] = (v8i){(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y, (int)w2.x, (int)w2.y, 0, 0};
-                const uint32_t sw = reinterpret_cast<const uint32_t *>(rec + MX_CODE_BYTES)[c];
-                bp[buf][j] = make_uint2(__builtin_amdgcn_perm(sw, sw, sel0), __builtin_amdgcn_perm(sw, sw, sel1));
-            }
-        };
-
-        // Software pipeline over the stage's BKB * TM * TN tile steps: the two
-        // MFMAs of step t + 1 are issued before the multiply-adds of step t,
-        // and the operands of block bb + 1 are read while block bb computes.
-        // The scheduling barriers keep that order (loads and scalar work may
-        // cross them).
-        constexpr int STEPS = BKB * TM * TN, PER = TM * TN;
-        v16f S[2], P[2];
-        load_frags(0, 0);
-        S[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][0], bf[0][0], v16f{}, 2, 2, 0, 0, 0, 0);
-        P[0] = mfma_bf16_32x32x8(ap[0][0], bp[0][0]);
 #pragma unroll
         for (int t = 0; t < STEPS; t++) {
-            const int i = (t / TN) % TM, j = t % TN;
-            if (t % PER == 0 && t / PER + 1 < BKB) load_frags(t / PER + 1, (t / PER + 1) & 1);
-            if (t + 1 < STEPS) {
-                const int t1 = t + 1, b1 = (t1 / PER) & 1, i1 = (t1 / TN) % TM, j1 = t1 % TN;
-                S[t1 & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[b1][i1], bf[b1][j1], v16f{}, 2, 2,
-                                                                            0, 0, 0, 0);
-                P[t1 & 1] = mfma_bf16_32x32x8(ap[b1][i1], bp[b1][j1]);
+            const int bb = t / PER, i = (t / TN) % TM, j = t % TN;
+            if (t % PER == 0) {
+                if (bb + 1 < BKB) {
+                    load_frags(st, bb + 1, (bb + 1) & 1);
+                } else {
+                    // stage s + 1 has landed for this wave; after the barrier
+                    // for every wave, and stage s - 1's slot is no longer read.
+                    // (After the last stage this reads a reloaded stage; the
+                    // MFMAs it feeds are never consumed.)
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 3)) : "memory");
+                    __syncthreads();
+                    issue(s + NS - 1, (s + NS - 1) % NS);
+                    load_frags(smem + ((s + 1) % NS) * C::STAGE_BYTES, 0, 0);
+                }
             }
+            const int t1 = (t + 1) % STEPS, b1 = (t1 / PER) & 1, i1 = (t1 / TN) % TM, j1 = t1 % TN;
+            S[(t + 1) & 1] = mfma_s(b1, i1, j1);
 #pragma unroll
-            for (int v = 0; v < 16; v++) acc[i][j][v] = fmaf(S[t & 1][v], P[t & 1][v], acc[i][j][v]);
+            for (int v = 0; v < 8; v++) acc[i][j][v] = fmaf(S[t & 1][v], P[t & 1][v], acc[i][j][v]);
+            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
+            P[(t + 1) & 1] = mfma_p(b1, i1, j1);
+#pragma unroll
+            for (int v = 8; v < 16; v++) acc[i][j][v] = fmaf(S[t & 1][v], P[t & 1][v], acc[i][j][v]);
             asm volatile("" : "+v"(acc[i][j]));  // materialised here, not sunk past the loop's end
             __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
         }
