@@ -40,7 +40,11 @@ def lib() -> ctypes.CDLL:
             "w4a4_packed_weight_bytes": ([I64, I64], SZ),
             "w4a4_repack_q4_0_h32": ([P, P, I64, I64, P], ST),
             "w4a4_rotate_quantize_act": ([P, ST, I64, I64, I64, P, P, P], ST),
+            "w4a4_rotate_quantize_prepare": ([P, ST, I64, I64, I64, P, P, P, SZ, P], ST),
             "w4a4_gemm_workspace_bytes": ([I64, I64, I64], SZ),
+            "w4a4_act_operand_bytes": ([I64, I64], SZ),
+            "w4a4_gemm_prepare_act": ([P, P, I64, I64, P, SZ, P], ST),
+            "w4a4_gemm_prepared": ([P, P, P, I64, I64, I64, I64, P], ST),
             "w4a4_gemm": ([P, P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_id_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_gemm_id": ([P, I64, P, P, I64, P, I64, I64, P, I64, I64, P, SZ, P], ST),
@@ -88,6 +92,10 @@ def packed_weight_bytes(n: int, k: int) -> int:
 
 def gemm_workspace_bytes(m: int, n: int, k: int) -> int:
     return int(lib().w4a4_gemm_workspace_bytes(m, n, k))
+
+
+def act_operand_bytes(m: int, k: int) -> int:
+    return int(lib().w4a4_act_operand_bytes(m, k))
 
 
 def gemm_id_workspace_bytes(n_expert: int, n_tokens: int, top_k: int) -> int:
@@ -139,6 +147,25 @@ def rotate_quantize_act(x: torch.Tensor, k: int | None = None, codes: torch.Tens
     return codes, scales
 
 
+def rotate_quantize_prepare(x: torch.Tensor, act: torch.Tensor, k: int | None = None,
+                            codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """rotate_quantize_act that also writes the matrix-core operand into `act`."""
+    _require_cuda(x, act, codes, scales)
+    assert x.dim() == 2 and x.stride(1) == 1
+    dt = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16}.get(x.dtype)
+    if dt is None:
+        raise W4A4Error(f"unsupported activation dtype {x.dtype}")
+    m = x.shape[0]
+    k = x.shape[1] if k is None else k
+    if codes is None:
+        codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    _check(lib().w4a4_rotate_quantize_prepare(_ptr(x), dt, m, k, x.stride(0), _ptr(codes), _ptr(scales), _ptr(act),
+                                              act.numel(), _stream(x.device)), "w4a4_rotate_quantize_prepare")
+    return codes, scales
+
+
 def gemm(packed: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: int, k: int,
          y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """W4A4 product: fp32 [m, n] (row stride y.stride(0)).  The workspace is
@@ -154,6 +181,30 @@ def gemm(packed: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: int
     _check(lib().w4a4_gemm(_ptr(packed), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, y.stride(0),
                            _ptr(workspace), 0 if workspace is None else workspace.numel(),
                            _stream(codes.device)), "w4a4_gemm")
+    return y
+
+
+def prepare_act(codes: torch.Tensor, scales: torch.Tensor, k: int,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """Activation codes + scales -> prepared matrix-core operand (uint8, private layout)."""
+    _require_cuda(codes, scales, out)
+    m = codes.shape[0]
+    if out is None:
+        out = torch.empty(max(1, act_operand_bytes(m, k)), dtype=torch.uint8, device=codes.device)
+    _check(lib().w4a4_gemm_prepare_act(_ptr(codes), _ptr(scales), m, k, _ptr(out), out.numel(),
+                                       _stream(codes.device)), "w4a4_gemm_prepare_act")
+    return out
+
+
+def gemm_prepared(packed: torch.Tensor, act: torch.Tensor, m: int, n: int, k: int,
+                  y: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A4 product on a prepared activation: fp32 [m, n] (row stride y.stride(0))."""
+    _require_cuda(packed, act, y)
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=act.device)
+    assert y.stride(1) == 1
+    _check(lib().w4a4_gemm_prepared(_ptr(packed), _ptr(act), _ptr(y), m, n, k, y.stride(0),
+                                    _stream(act.device)), "w4a4_gemm_prepared")
     return y
 
 

@@ -24,9 +24,9 @@
 // loop: operands arrive in the MFMA's register layout (weights repacked
 // offline, activations by a pre-pass), by direct global-to-LDS loads.
 //
-// Workgroup: 4 waves (2 x 2), each owning 2 x 2 tiles of 32x32: a 128 x 128
-// output tile.  K is walked in stages of BKB blocks through a ring of NS LDS
-// stage buffers; NS - 1 stages are in flight while one is computed.
+// Workgroup: 4 waves (2 x 2), each owning TM x TN tiles of 32x32 (a 128 x 128
+// output tile for 2 x 2).  K is walked in stages of BKB blocks through a ring
+// of NS LDS stage buffers; NS - 1 stages are in flight while one is computed.
 #pragma once
 
 #include "common.h"
@@ -93,10 +93,10 @@ struct MxArgs {
     int64_t ldy, m, n, k;
 };
 
-template <int BKB_, int NS_>
+template <int BKB_, int NS_, int TM_, int TN_>
 struct MxCfg {
     static constexpr int BKB = BKB_, NS = NS_;
-    static constexpr int TM = 2, TN = 2, WM = 2, WN = 2, NT = 256;
+    static constexpr int TM = TM_, TN = TN_, WM = 2, WN = 2, NT = 256;
     static constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     static constexpr int RT = BM / 32, CT = BN / 32;
     static constexpr int STAGE_BYTES = (RT + CT) * BKB * MX_REC;

@@ -7,11 +7,18 @@
 // coarse scale on the rest.  The same per-block rotation was applied to the
 // weights offline, so the product is unchanged in exact arithmetic.
 //
-// Mapping: one thread per 32-element block, the whole transform in registers
-// (the pass is a single read of the activations and is bound by memory and
-// launch latency, not arithmetic).  The fp32 operation sequence is fixed:
-// IEEE add and subtract per stage in the order h = 1, 2, 4, 8, 16, correctly
-// rounded division and reciprocal, multiply without contraction, round half
+// Mapping: eight lanes per 32-element block, four consecutive elements per
+// lane (one 8-byte fp16 load; a wave reads 8 rows x 64 contiguous bytes).  The
+// butterflies of distance 1 and 2 are in-lane, those of distance 4, 8 and 16
+// exchange values with lane L ^ 1, L ^ 2, L ^ 4 of the block's eight; the
+// absmax is a three-step exchange too.  A workgroup of 256 threads covers 32
+// rows of one block, so it can also write that block's matrix-core operand
+// record (see common.h) in one coalesced kilobyte.
+//
+// The fp32 operation sequence is fixed and the same as a serial evaluation:
+// in stage h = 1, 2, 4, 8, 16 each pair (i, i + h) with i & h == 0 becomes
+// (v_i + v_{i+h}, v_i - v_{i+h}) with IEEE add and subtract; correctly
+// rounded division and reciprocal; multiply without contraction; round half
 // away from zero.
 #pragma once
 
@@ -27,89 +34,124 @@ __device__ __forceinline__ float round_half_away(float x) {
     return frac >= 0.5f ? __fadd_rn(t, x < 0.0f ? -1.0f : 1.0f) : t;
 }
 
-// Load the 32 elements of one block as fp32 (exact from fp16).
-__device__ __forceinline__ void load_block(const float *__restrict__ p, float v[QK]) {
-    const float4 *q = reinterpret_cast<const float4 *>(p);
-#pragma unroll
-    for (int i = 0; i < QK / 4; i++) {
-        const float4 f = q[i];
-        v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
-    }
-}
-__device__ __forceinline__ void load_block(const __half *__restrict__ p, float v[QK]) {
-    const uint4 *q = reinterpret_cast<const uint4 *>(p);
-#pragma unroll
-    for (int i = 0; i < QK / 8; i++) {
-        const uint4 u = q[i];
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            v[8 * i + 2 * j] = __half2float(__ushort_as_half((uint16_t)(w[j] & 0xffff)));
-            v[8 * i + 2 * j + 1] = __half2float(__ushort_as_half((uint16_t)(w[j] >> 16)));
-        }
-    }
-}
+// value of lane (self ^ mask) within the 8-lane group of a block
+__device__ __forceinline__ float xchg(float v, int mask) { return __shfl_xor(v, mask, 8); }
+__device__ __forceinline__ uint32_t xchg(uint32_t v, int mask) { return (uint32_t)__shfl_xor((int)v, mask, 8); }
 
-// One thread per 32-element block, all in registers: unnormalised FWHT,
-// amax, scale, codes, packing.  Loads are 16-byte vectors when the row stride
-// and base keep every block 16-byte aligned (checked on the host); the
-// element-wise variant below covers any other stride.
-template <typename T, bool VEC>
-__global__ __launch_bounds__(256) void rotate_quantize_kernel(const T *__restrict__ x, int64_t m,
-                                                              int64_t k, int64_t ldx,
-                                                              uint8_t *__restrict__ codes,
-                                                              float *__restrict__ scales) {
-    const int64_t nb = k / QK;
-    const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (blk >= m * nb) return;
-    const int64_t row = blk / nb, b = blk % nb;
-    const T *src = x + row * ldx + b * QK;
-
-    float v[QK];
-    if constexpr (VEC) {
-        load_block(src, v);
+// Four consecutive elements as fp32 (exact from fp16).
+__device__ __forceinline__ void load4(const float *p, bool vec, float v[4]) {
+    if (vec) {
+        const float4 f = *reinterpret_cast<const float4 *>(p);
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
     } else {
+        for (int i = 0; i < 4; i++) v[i] = p[i];
+    }
+}
+__device__ __forceinline__ void load4(const __half *p, bool vec, float v[4]) {
+    if (vec) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(p);
+        v[0] = __half2float(__ushort_as_half((uint16_t)(u.x & 0xffff)));
+        v[1] = __half2float(__ushort_as_half((uint16_t)(u.x >> 16)));
+        v[2] = __half2float(__ushort_as_half((uint16_t)(u.y & 0xffff)));
+        v[3] = __half2float(__ushort_as_half((uint16_t)(u.y >> 16)));
+    } else {
+        for (int i = 0; i < 4; i++) v[i] = __half2float(p[i]);
+    }
+}
+
+// One workgroup = 32 rows (row tile blockIdx.y) x one 32-element block
+// (blockIdx.x); thread t: row r = t / 8 of the tile, lane L = t % 8 of the
+// block, elements 4L .. 4L + 3.  `vec`: every 4-element group is aligned for
+// one vector load (checked on the host).  With `act` set, also writes the
+// block's operand record for the matrix-core GEMM (blockIdx.x runs over the
+// padded block count then; padding rows and blocks get zero records).
+template <typename T>
+__global__ __launch_bounds__(256) void rotate_quantize_kernel(const T *__restrict__ x, int64_t m, int64_t k,
+                                                              int64_t ldx, bool vec, uint8_t *__restrict__ codes,
+                                                              float *__restrict__ scales,
+                                                              uint8_t *__restrict__ act) {
+    const int64_t nb = k / QK;
+    const int tid = threadIdx.x, L = tid & 7, r = tid >> 3;
+    const int64_t b = blockIdx.x, row = (int64_t)blockIdx.y * 32 + r;
+    const bool live = row < m && b < nb;  // uniform per 8-lane group
+
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (live) load4(x + row * ldx + b * QK + 4 * L, vec, v);
+
+    // distance 1 and 2: inside the lane
+    {
+        const float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+        v[0] = __fadd_rn(a0, a1); v[1] = __fsub_rn(a0, a1);
+        v[2] = __fadd_rn(a2, a3); v[3] = __fsub_rn(a2, a3);
+    }
+    {
+        const float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+        v[0] = __fadd_rn(a0, a2); v[2] = __fsub_rn(a0, a2);
+        v[1] = __fadd_rn(a1, a3); v[3] = __fsub_rn(a1, a3);
+    }
+    // distance 4, 8, 16: partner lane L ^ 1, L ^ 2, L ^ 4 holds the other element
 #pragma unroll
-        for (int t = 0; t < QK; t++) {
-            if constexpr (sizeof(T) == 4) v[t] = src[t];
-            else v[t] = __half2float(src[t]);
+    for (int mask = 1; mask < 8; mask <<= 1) {
+        const bool upper = (L & mask) != 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float p = xchg(v[i], mask);
+            v[i] = upper ? __fsub_rn(p, v[i]) : __fadd_rn(v[i], p);  // (lower - upper) / (lower + upper)
         }
     }
 
-    // (a, b) -> (a + b, a - b) for the pair (i, i + h), h = 1, 2, 4, 8, 16
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 #pragma unroll
-    for (int h = 1; h < QK; h <<= 1) {
-#pragma unroll
-        for (int i = 0; i < QK; i++) {
-            if (i & h) continue;
-            const float a0 = v[i], a1 = v[i + h];
-            v[i] = __fadd_rn(a0, a1);
-            v[i + h] = __fsub_rn(a0, a1);
-        }
-    }
-
-    float amax = 0.0f;
-#pragma unroll
-    for (int t = 0; t < QK; t++) amax = fmaxf(amax, fabsf(v[t]));
+    for (int mask = 1; mask < 8; mask <<= 1) amax = fmaxf(amax, xchg(amax, mask));
 
     const float d = __fdiv_rn(amax, 7.0f);
-    uint32_t packed[4] = {0u, 0u, 0u, 0u};
-    float s = 0.0f;
-    if (d >= 1.17549435e-38f) {  // FLT_MIN: zero and subnormal scales give a zero block
-        const float id = __fdiv_rn(1.0f, d);
+    const bool nonzero = d >= 1.17549435e-38f;  // FLT_MIN: zero and subnormal scales give a zero block
+    const float id = nonzero ? __fdiv_rn(1.0f, d) : 0.0f;
+    const float s = nonzero ? __fmul_rn(d, kInvSqrt32f) : 0.0f;
+    int q[4];
 #pragma unroll
-        for (int j = 0; j < QK / 2; j++) {
-            const float r0 = fminf(7.0f, fmaxf(-7.0f, round_half_away(__fmul_rn(v[j], id))));
-            const float r1 = fminf(7.0f, fmaxf(-7.0f, round_half_away(__fmul_rn(v[j + 16], id))));
-            const uint32_t byte = ((uint32_t)(int)r0 & 0xFu) | (((uint32_t)(int)r1 & 0xFu) << 4);
-            packed[j >> 2] |= byte << (8 * (j & 3));
+    for (int i = 0; i < 4; i++)
+        q[i] = nonzero ? (int)fminf(7.0f, fmaxf(-7.0f, round_half_away(__fmul_rn(v[i], id)))) : 0;
+
+    // public codes: byte j = code j | code j + 16 << 4; lane L < 4 writes bytes 4L .. 4L + 3
+    const uint32_t mine = (q[0] & 0xF) | (q[1] & 0xF) << 4 | (q[2] & 0xF) << 8 | (q[3] & 0xF) << 12;
+    const uint32_t high = xchg(mine, 4);  // codes 16 + 4L .. of lane L + 4
+    if (live && b < nb && codes) {
+        if (L < 4) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < 4; i++) word |= (((mine >> (4 * i)) & 0xF) | ((high >> (4 * i)) & 0xF) << 4) << (8 * i);
+            reinterpret_cast<uint32_t *>(codes + row * (k / 2) + b * 16)[L] = word;
         }
-        s = __fmul_rn(d, kInvSqrt32f);
+        if (L == 0) scales[row * nb + b] = s;
     }
-    // byte j of the block: code j (low nibble) | code j + 16 (high nibble)
-    *reinterpret_cast<uint4 *>(codes + row * (k / 2) + b * 16) =
-        make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    scales[row * nb + b] = s;
+
+    if (act) {
+        // operand record of (row tile, block): lane (g, r) holds codes 16 g ..
+        // 16 g + 15 as fp6 fields; this thread's four codes are 24 bits at
+        // bit 24 (L % 4) of group g = L / 4's 96-bit value
+        uint32_t f24 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) f24 |= fp6_e2m3_of(live ? q[i] : 0) << (6 * i);
+        const uint32_t x1 = xchg(f24, 1), x2 = xchg(f24, 2), x3 = xchg(f24, 3);  // from L + 1, L + 2, L + 3
+        uint8_t *rec = act + ((int64_t)blockIdx.y * mx_blocks(k) + b) * MX_REC;
+        if ((L & 3) == 0) {
+            const int lane = (L >> 2) * 32 + r;
+            const uint32_t w0 = f24 | x1 << 24, w1 = x1 >> 8 | x2 << 16, w2 = x2 >> 16 | x3 << 8;
+            reinterpret_cast<uint2 *>(rec)[lane] = make_uint2(w0, w1);
+            reinterpret_cast<uint32_t *>(rec + 512)[lane] = w2;
+        }
+        if (L == 0) {
+            // exact bf16 split s = s1 + s2 + s3 (truncations; each remainder is exact)
+            const float sl = live ? s : 0.0f;
+            const uint32_t h1 = __float_as_uint(sl) & 0xFFFF0000u;
+            const float r1 = __fsub_rn(sl, __uint_as_float(h1));
+            const uint32_t h2 = __float_as_uint(r1) & 0xFFFF0000u;
+            const float r2 = __fsub_rn(r1, __uint_as_float(h2));
+            const uint32_t h3 = __float_as_uint(r2) & 0xFFFF0000u;
+            reinterpret_cast<uint2 *>(rec + MX_CODE_BYTES)[r] = make_uint2((h1 >> 16) | h2, h3 >> 16);
+        }
+    }
 }
 
 }  // namespace w4a4

@@ -33,8 +33,64 @@ inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 inline unsigned blocks_for(int64_t work, int per) { return (unsigned)((work + per - 1) / per); }
 
-// Dense m > 16: 128 x 128 workgroup tiles, stages of 2 blocks, a ring of 4 stages.
-using DenseMx = MxCfg<2, 4>;
+// Dense m > 16: stages of 2 blocks, a ring of 4 stages; workgroup tiles of
+// 128 x 128, 128 x 64 or 64 x 128, chosen per problem (see launch_mx).
+using Mx128x128 = MxCfg<2, 4, 2, 2>;
+using Mx128x64 = MxCfg<2, 4, 2, 1>;
+using Mx64x128 = MxCfg<2, 4, 1, 2>;
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+template <class C>
+int mx_occupancy() {  // resident workgroups per CU (registers and LDS decide)
+    static const int occ = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_mx_kernel<C>, C::NT, 0) != hipSuccess || n < 1)
+            n = 1;
+        return n;
+    }();
+    return occ;
+}
+
+// Modelled time of one tile shape: rounds of resident workgroups times the
+// padded work per tile (the smaller tiles reuse operands less: ~8% slower per
+// output on MI355X); ties go to the shape that pads less.
+struct MxCost {
+    double time, padded;
+    bool operator<=(const MxCost &o) const { return time < o.time || (time == o.time && padded <= o.padded); }
+};
+template <class C>
+MxCost mx_cost(int64_t m, int64_t n) {
+    const int64_t tm = (m + C::BM - 1) / C::BM, tn = (n + C::BN - 1) / C::BN, tiles = tm * tn;
+    const int64_t slots = (int64_t)device_cus() * mx_occupancy<C>();
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    return {(double)rounds * C::BM * C::BN * (C::TM * C::TN == 4 ? 1.0 : 1.08), (double)(tm * C::BM) * (tn * C::BN)};
+}
+
+template <class C>
+void launch_mx_cfg(const MxArgs &a, hipStream_t s) {
+    const int64_t wgs = (a.n + C::BN - 1) / C::BN * ((a.m + C::BM - 1) / C::BM);
+    gemm_mx_kernel<C><<<(unsigned)wgs, C::NT, 0, s>>>(a);
+}
+
+void launch_mx(const MxArgs &a, hipStream_t s) {
+    const MxCost c0 = mx_cost<Mx128x128>(a.m, a.n), c1 = mx_cost<Mx128x64>(a.m, a.n),
+                 c2 = mx_cost<Mx64x128>(a.m, a.n);
+    if (c0 <= c1 && c0 <= c2) launch_mx_cfg<Mx128x128>(a, s);
+    else if (c1 <= c2) launch_mx_cfg<Mx128x64>(a, s);
+    else launch_mx_cfg<Mx64x128>(a, s);
+}
 // Grouped expert tiles: 32 rows (experts are small), 4 waves across 256 columns.
 using GroupedCfg = TileCfg<1, 4, 1, 2, 4>;
 
@@ -111,8 +167,9 @@ w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int6
     return hip_status("repack_mx_kernel");
 }
 
-w4a4_status w4a4_rotate_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
-                                     uint8_t *codes, float *scales, void *stream) {
+namespace {
+w4a4_status rotate_quantize(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx, uint8_t *codes,
+                            float *scales, void *act, size_t act_bytes, void *stream) {
     if (dt != W4A4_DTYPE_F32 && dt != W4A4_DTYPE_F16) return W4A4_ERR_UNSUPPORTED_DTYPE;
     if (m < 0 || k < 0 || ldx < k || m > kMaxRows) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
@@ -120,27 +177,42 @@ w4a4_status w4a4_rotate_quantize_act(const void *x, w4a4_dtype dt, int64_t m, in
     if (!x || !codes || !scales) return W4A4_ERR_INVALID_VALUE;
     if (!aligned(x, dt == W4A4_DTYPE_F32 ? 4 : 2) || !aligned(codes, 16) || !aligned(scales, 4))
         return W4A4_ERR_MISALIGNED;
-    const int64_t blocks = m * (k / QK);
-    const unsigned grid = blocks_for(blocks, 256);
-    const size_t esz = dt == W4A4_DTYPE_F32 ? 4 : 2;
-    const bool vec = aligned(x, 16) && (ldx * esz) % 16 == 0;  // every block 16-byte aligned
-    hipStream_t s = as_stream(stream);
-    if (dt == W4A4_DTYPE_F32) {
-        const float *xf = static_cast<const float *>(x);
-        if (vec) rotate_quantize_kernel<float, true><<<grid, 256, 0, s>>>(xf, m, k, ldx, codes, scales);
-        else rotate_quantize_kernel<float, false><<<grid, 256, 0, s>>>(xf, m, k, ldx, codes, scales);
-    } else {
-        const __half *xh = static_cast<const __half *>(x);
-        if (vec) rotate_quantize_kernel<__half, true><<<grid, 256, 0, s>>>(xh, m, k, ldx, codes, scales);
-        else rotate_quantize_kernel<__half, false><<<grid, 256, 0, s>>>(xh, m, k, ldx, codes, scales);
+    if (act) {
+        if (!aligned(act, 256)) return W4A4_ERR_MISALIGNED;
+        if (act_bytes < w4a4_act_operand_bytes(m, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
     }
+    const size_t esz = dt == W4A4_DTYPE_F32 ? 4 : 2;
+    // every 4-element group aligned for one vector load (8 bytes fp16, 16 bytes fp32)
+    const bool vec = aligned(x, 4 * esz) && (ldx % 4) == 0;
+    const dim3 grid((unsigned)(act ? mx_blocks(k) : k / QK), (unsigned)((m + 31) / 32));
+    hipStream_t s = as_stream(stream);
+    uint8_t *a = static_cast<uint8_t *>(act);
+    if (dt == W4A4_DTYPE_F32)
+        rotate_quantize_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(x), m, k, ldx, vec, codes,
+                                                          scales, a);
+    else
+        rotate_quantize_kernel<__half><<<grid, 256, 0, s>>>(static_cast<const __half *>(x), m, k, ldx, vec, codes,
+                                                           scales, a);
     return hip_status("rotate_quantize_kernel");
+}
+}  // namespace
+
+w4a4_status w4a4_rotate_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                                     uint8_t *codes, float *scales, void *stream) {
+    return rotate_quantize(x, dt, m, k, ldx, codes, scales, nullptr, 0, stream);
+}
+
+w4a4_status w4a4_rotate_quantize_prepare(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                                         uint8_t *codes, float *scales, void *act, size_t act_bytes,
+                                         void *stream) {
+    if (!act && m > 0 && k > 0) return W4A4_ERR_INVALID_VALUE;
+    return rotate_quantize(x, dt, m, k, ldx, codes, scales, act, act_bytes, stream);
 }
 
 size_t w4a4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
     if (m < 0 || n < 0 || k < 0 || k % QK) return 0;
     if (m <= SMALL_M_MAX || n == 0 || k == 0) return 0;
-    return (size_t)((m + 31) / 32 * mx_blocks(k) * MX_REC);
+    return w4a4_act_operand_bytes(m, k);
 }
 
 w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *scales, float *y,
@@ -197,24 +269,53 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
         }
         return hip_status("gemm_small_m_kernel");
     }
-    if (!workspace) return W4A4_ERR_INVALID_VALUE;
-    if (!aligned(workspace, 256)) return W4A4_ERR_MISALIGNED;
-    if (workspace_bytes < w4a4_gemm_workspace_bytes(m, n, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    const int64_t pre_threads = (m + 31) / 32 * 32 * mx_blocks(k);
-    act_operand_kernel<<<blocks_for(pre_threads, 256), 256, 0, s>>>(codes, scales, m, k, ws);
-    const w4a4_status pst = hip_status("act_operand_kernel");
+    const w4a4_status pst = w4a4_gemm_prepare_act(codes, scales, m, k, workspace, workspace_bytes, stream);
     if (pst != W4A4_OK) return pst;
+    return w4a4_gemm_prepared(packed_w, workspace, y, m, n, k, ldy, stream);
+}
+
+size_t w4a4_act_operand_bytes(int64_t m, int64_t k) {
+    if (m < 0 || k < 0 || k % QK) return 0;
+    return (size_t)((m + 31) / 32 * mx_blocks(k) * MX_REC);
+}
+
+w4a4_status w4a4_gemm_prepare_act(const uint8_t *codes, const float *scales, int64_t m, int64_t k,
+                                  void *act, size_t act_bytes, void *stream) {
+    if (m < 0 || k < 0 || m > kMaxRows) return W4A4_ERR_INVALID_VALUE;
+    if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
+    if (m == 0 || k == 0) return W4A4_OK;
+    if (!codes || !scales || !act) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(act, 256)) return W4A4_ERR_MISALIGNED;
+    if (act_bytes < w4a4_act_operand_bytes(m, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
+    const int64_t threads = (m + 31) / 32 * 32 * mx_blocks(k);
+    act_operand_kernel<<<blocks_for(threads, 256), 256, 0, as_stream(stream)>>>(codes, scales, m, k,
+                                                                               static_cast<uint8_t *>(act));
+    return hip_status("act_operand_kernel");
+}
+
+w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, int64_t m, int64_t n,
+                               int64_t k, int64_t ldy, void *stream) {
+    if (m < 0 || n < 0 || k < 0 || m > kMaxRows || ldy < n) return W4A4_ERR_INVALID_VALUE;
+    if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
+    if (m == 0 || n == 0) return W4A4_OK;
+    if (!y) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(y, 4)) return W4A4_ERR_MISALIGNED;
+    hipStream_t s = as_stream(stream);
+    if (k == 0) {  // empty sum
+        zero_rows_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(y, m, n, ldy);
+        return hip_status("zero_rows_kernel");
+    }
+    if (!packed_w || !act) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(packed_w, 16) || !aligned(act, 256)) return W4A4_ERR_MISALIGNED;
     MxArgs a{};
-    a.act = ws;
+    a.act = static_cast<const uint8_t *>(act);
     a.wrec = static_cast<const uint8_t *>(packed_w) + mx_section_offset(n, k);
     a.y = y;
     a.ldy = ldy;
     a.m = m;
     a.n = n;
     a.k = k;
-    const int64_t wgs = (int64_t)blocks_for(n, DenseMx::BN) * blocks_for(m, DenseMx::BM);
-    gemm_mx_kernel<DenseMx><<<(unsigned)wgs, DenseMx::NT, 0, s>>>(a);
+    launch_mx(a, s);
     return hip_status("gemm_mx_kernel");
 }
 

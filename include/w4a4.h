@@ -113,6 +113,20 @@ w4a4_status w4a4_rotate_quantize_act(const void *x, w4a4_dtype dt, int64_t m, in
  * argument is invalid).  Host only, pure. */
 size_t w4a4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
+/* Bytes of the matrix-core operand of m activation rows of width k (0 for
+ * invalid sizes).  Host only, pure. */
+size_t w4a4_act_operand_bytes(int64_t m, int64_t k);
+
+/*
+ * w4a4_rotate_quantize_act, and in the same pass the matrix-core operand of
+ * the rows (what w4a4_gemm_prepare_act would make of codes and scales):
+ *   act   out, w4a4_act_operand_bytes(m, k) bytes, 256-byte aligned, for
+ *         w4a4_gemm_prepared.  Other arguments as w4a4_rotate_quantize_act.
+ */
+w4a4_status w4a4_rotate_quantize_prepare(const void *x, w4a4_dtype dt, int64_t m, int64_t k,
+                                         int64_t ldx, uint8_t *codes, float *scales, void *act,
+                                         size_t act_bytes, void *stream);
+
 /*
  * Dense W4A4 product: y[i][j] = sum_b d_w[j][b] * s[i][b] * S[i][j][b], where
  * S = sum_t (q_w - 8) * q_a is the exact integer dot of block b, accumulated
@@ -130,6 +144,25 @@ size_t w4a4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *scales, float *y,
                       int64_t m, int64_t n, int64_t k, int64_t ldy, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/*
+ * The two steps of w4a4_gemm for m > 16, callable on their own (one prepared
+ * activation can feed several products that read the same rows, e.g. the
+ * query, key and value projections).
+ *
+ * w4a4_gemm_prepare_act: re-lays activation codes and scales from
+ * w4a4_rotate_quantize_act into the matrix-core operand format (every code
+ * as an FP6 E2M3 value, exactly q / 8; every scale as an exact bf16 triple).
+ *   act   out, w4a4_act_operand_bytes(m, k) bytes, 256-byte aligned; private
+ *         layout.
+ *
+ * w4a4_gemm_prepared: the product of packed_w with a prepared activation, as
+ * w4a4_gemm (any m >= 1; y [m][ldy] fp32).
+ */
+w4a4_status w4a4_gemm_prepare_act(const uint8_t *codes, const float *scales, int64_t m, int64_t k,
+                                  void *act, size_t act_bytes, void *stream);
+w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, int64_t m, int64_t n,
+                               int64_t k, int64_t ldy, void *stream);
 
 /* Workspace bytes w4a4_gemm_id needs.  Host only, pure. */
 size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t top_k);

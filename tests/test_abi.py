@@ -86,6 +86,41 @@ def test_gemm_validation(L):
     assert g(P(A), P(A), P(A), P(A), 64, 64, 64, 64, P(A), need - 1, None) == WS
 
 
+def test_prepared_gemm_validation(L):
+    pb = L.w4a4_act_operand_bytes(64, 64)
+    assert pb == 2 * 8 * 1024
+    assert L.w4a4_act_operand_bytes(64, 33) == 0
+    prep = L.w4a4_gemm_prepare_act
+    assert prep(P(A), P(A), 64, 33, P(A), pb, None) == KMUL
+    assert prep(P(A), P(A), -1, 64, P(A), pb, None) == INVALID
+    assert prep(None, P(A), 64, 64, P(A), pb, None) == INVALID
+    assert prep(P(A), P(A), 64, 64, None, pb, None) == INVALID
+    assert prep(P(A + 8), P(A), 64, 64, P(A), pb, None) == MISALIGNED
+    assert prep(P(A), P(A), 64, 64, P(A + 16), pb, None) == MISALIGNED
+    assert prep(P(A), P(A), 64, 64, P(A), pb - 1, None) == WS
+    assert prep(None, None, 0, 64, None, 0, None) == OK
+    run = L.w4a4_gemm_prepared
+    assert run(P(A), P(A), P(A), 64, 64, 33, 64, None) == KMUL
+    assert run(P(A), P(A), P(A), 64, 64, 64, 63, None) == INVALID  # ldy < n
+    assert run(None, P(A), P(A), 64, 64, 64, 64, None) == INVALID
+    assert run(P(A), None, P(A), 64, 64, 64, 64, None) == INVALID
+    assert run(P(A), P(A), None, 64, 64, 64, 64, None) == INVALID
+    assert run(P(A), P(A + 16), P(A), 64, 64, 64, 64, None) == MISALIGNED
+    assert run(P(A + 8), P(A), P(A), 64, 64, 64, 64, None) == MISALIGNED
+    assert run(None, None, None, 0, 64, 64, 64, None) == OK
+
+
+def test_rotate_quantize_prepare_validation(L):
+    f = L.w4a4_rotate_quantize_prepare
+    pb = L.w4a4_act_operand_bytes(8, 64)
+    assert f(P(A), 1, 8, 64, 64, P(A), P(A), None, pb, None) == INVALID  # act required
+    assert f(P(A), 1, 8, 64, 64, P(A), P(A), P(A + 16), pb, None) == MISALIGNED
+    assert f(P(A), 1, 8, 64, 64, P(A), P(A), P(A), pb - 1, None) == WS
+    assert f(P(A), 7, 8, 64, 64, P(A), P(A), P(A), pb, None) == DTYPE
+    assert f(P(A), 1, 8, 48, 64, P(A), P(A), P(A), pb, None) == KMUL
+    assert f(None, 1, 0, 64, 64, None, None, None, 0, None) == OK
+
+
 def test_rotate_quantize_validation(L):
     f = L.w4a4_rotate_quantize_act
     assert f(P(A), 2, 4, 64, 64, P(A), P(A), None) == DTYPE

@@ -147,6 +147,21 @@ def test_rotate_quantize_many_random_blocks(ops):
     assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs)
 
 
+@pytest.mark.parametrize("m,k,dtype", [(512, 5120, np.float16), (45, 288, np.float32), (33, 96, np.float16)])
+def test_rotate_quantize_prepare_operand(ops, m, k, dtype):
+    """The fused pass: codes and scales as the oracle's, and an operand equal
+    byte for byte to the one prepare_act builds from the oracle's codes."""
+    rng = np.random.default_rng(m + k)
+    x = synth.activations(m, k, rng, max(1, k // 100), dtype=dtype)
+    say(f"rotate_quantize_prepare m={m} k={k} {dtype.__name__}")
+    act = torch.empty(ops.act_operand_bytes(m, k), dtype=torch.uint8, device="cuda")
+    c, s = ops.rotate_quantize_prepare(dev(x), act)
+    rc, rs = oracle.rotate_quantize_act(x)
+    assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs)
+    ref = ops.prepare_act(dev(rc), dev(rs), k)
+    assert np.array_equal(host(act), host(ref))
+
+
 # --------------------------------------------------------------------------
 # GEMM: integer block sums exact (fed the oracle's codes), fp32 within tolerance
 # --------------------------------------------------------------------------
@@ -200,6 +215,36 @@ def test_gemm_end_to_end(ops, m, n, k):
     rc, rs = oracle.rotate_quantize_act(x)
     assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs)
     assert_rows_close(y, oracle.gemm(q4, rc, rs, k), f"m={m} n={n} k={k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(512, 17408, 256), (512, 16384, 256), (64, 4096, 160), (100, 600, 96)])
+def test_gemm_tile_shapes_integer(ops, m, n, k):
+    """Shapes that pick each workgroup tile (128x128, 128x64, 64x128): integer sums exact."""
+    w, x = _problem(m, n, k, m + 3 * n)
+    q4 = with_unit_scales(oracle.prepare_weights(w))
+    rc, _ = oracle.rotate_quantize_act(x)
+    ones = np.ones((m, k // 32), np.float32)
+    say(f"gemm tile shapes, integer unit scales m={m} n={n} k={k}")
+    y = host(ops.gemm(ops.repack_q4_0_h32(dev(q4), n, k), dev(rc), dev(ones), n, k))
+    rows = np.unique(np.linspace(0, m - 1, 9).astype(int))
+    assert np.array_equal(y[rows], oracle.gemm(q4, rc[rows], ones[rows], k))
+
+
+def test_gemm_prepared_matches_gemm(ops):
+    """One prepared activation feeding two products equals the one-call path bit for bit."""
+    m, k = 200, 320
+    rng = np.random.default_rng(31)
+    x = synth.activations(m, k, rng, 3)
+    w1, w2 = synth.weights(96, k, rng), synth.weights(160, k, rng)
+    say("gemm_prepared vs gemm")
+    c, s = ops.rotate_quantize_act(dev(x))
+    p1, p2 = ops.prepare_weights(dev(w1)), ops.prepare_weights(dev(w2))
+    act = ops.prepare_act(c, s, k)
+    y1, y2 = host(ops.gemm_prepared(p1, act, m, 96, k)), host(ops.gemm_prepared(p2, act, m, 160, k))
+    assert np.array_equal(y1, host(ops.gemm(p1, c, s, 96, k)))
+    assert np.array_equal(y2, host(ops.gemm(p2, c, s, 160, k)))
+    q4 = oracle.prepare_weights(w2)
+    assert_rows_close(y2, oracle.gemm(q4, *oracle.rotate_quantize_act(x), k), "prepared")
 
 
 def test_gemm_output_stride_and_determinism(ops):
