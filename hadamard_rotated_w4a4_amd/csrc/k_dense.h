@@ -123,6 +123,18 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
 }
 
+// Workgroup tile of index id in an XCD-aware order.  Workgroups are dealt to
+// the 8 XCDs round-robin, so ids x, x + 8, x + 16, ... share an XCD and its
+// L2; the row tiles of one weight column tile get ids x + 8y and read those
+// weights from HBM about once.  nx, ny: column and row tiles of the matrix.
+__device__ __forceinline__ void mx_tile_of(int64_t id, int64_t nx, int64_t ny, int64_t &bx, int64_t &by) {
+    constexpr int64_t XCDS = 8;
+    const int64_t group = id / (XCDS * ny), in = id % (XCDS * ny);
+    const int64_t width = min(XCDS, nx - group * XCDS);
+    bx = group * XCDS + in % width;
+    by = in / width;
+}
+
 template <class C>
 __global__ __launch_bounds__(C::NT) void gemm_mx_kernel(MxArgs a) {
     constexpr int BKB = C::BKB, NS = C::NS, TM = C::TM, TN = C::TN, RT = C::RT;
@@ -135,14 +147,8 @@ __global__ __launch_bounds__(C::NT) void gemm_mx_kernel(MxArgs a) {
     const int64_t nbp = mx_blocks(a.k);
     const int64_t rtiles = (a.m + 31) / 32, ctiles = padded_n(a.n) / TILE_N;
 
-    // XCD-aware 1-D grid: workgroups are dealt to the 8 XCDs round-robin, so
-    // ids x, x + 8, x + 16, ... share an XCD and its L2; the row tiles of one
-    // weight column tile get ids x + 8y and read those weights from HBM ~once.
-    constexpr int64_t XCDS = 8;
-    const int64_t nx = (a.n + C::BN - 1) / C::BN, ny = (a.m + C::BM - 1) / C::BM;
-    const int64_t id = blockIdx.x, group = id / (XCDS * ny), in = id % (XCDS * ny);
-    const int64_t width = min(XCDS, nx - group * XCDS);
-    const int64_t bx = group * XCDS + in % width, by = in / width;
+    int64_t bx, by;
+    mx_tile_of(blockIdx.x, (a.n + C::BN - 1) / C::BN, (a.m + C::BM - 1) / C::BM, bx, by);
     const int64_t rt0 = by * RT, ct0 = bx * C::CT;
 
     // ---- this wave's loads: DMA_PER_WAVE records of 1 KB per stage ----
@@ -282,6 +288,121 @@ __global__ __launch_bounds__(C::NT) void gemm_mx_kernel(MxArgs a) {
                 if (r < a.m) a.y[r * a.ldy + col] = acc[i][j][v];
             }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Leftover tiles.  When the workgroup tiles of a problem do not fill whole
+// rounds of the GPU, the main kernel takes the whole rounds and this kernel
+// the rest: each workgroup computes one 32x32 piece of a leftover tile, its 4
+// waves each over a quarter of K, and the quarters meet in LDS.  A wave
+// streams its own operand records through its own LDS ring (no barrier until
+// the reduction), two MFMAs and 16 multiply-adds per block as above.
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_>
+struct MxPieceCfg {
+    static constexpr int BM = BM_, BN = BN_;                 // tile shape of the main kernel
+    static constexpr int PIECES = (BM / 32) * (BN / 32);     // 32x32 pieces per leftover tile
+    static constexpr int BKB = 2, NS = 4, NT = 256;          // per wave: NS stages of BKB blocks
+    static constexpr int WAVE_RING = NS * BKB * 2 * MX_REC;  // A and B record per block
+};
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_mx_piece_kernel(MxArgs a, int64_t first_tile) {
+    constexpr int BKB = C::BKB, NS = C::NS;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::WAVE_RING];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, c = lane & 31;
+    const int64_t nbp = mx_blocks(a.k);
+    const int64_t rtiles = (a.m + 31) / 32, ctiles = padded_n(a.n) / TILE_N;
+
+    int64_t bx, by;
+    mx_tile_of(first_tile + blockIdx.x / C::PIECES, (a.n + C::BN - 1) / C::BN, (a.m + C::BM - 1) / C::BM, bx, by);
+    const int sub = blockIdx.x % C::PIECES;
+    const int64_t rt = by * (C::BM / 32) + sub / (C::BN / 32), ct = bx * (C::BN / 32) + sub % (C::BN / 32);
+    // pieces past the matrix edge compute on clamped tiles and store nothing
+    const uint8_t *arec = a.act + min(rt, rtiles - 1) * nbp * MX_REC;
+    const uint8_t *brec = a.wrec + min(ct, ctiles - 1) * nbp * MX_REC;
+
+    // this wave's quarter of the blocks, in whole stages
+    const int64_t nstages_all = nbp / BKB;
+    const int64_t s_begin = nstages_all * wave / 4, s_end = nstages_all * (wave + 1) / 4;
+    const int nst = (int)(s_end - s_begin);
+    uint8_t *ring = smem + wave * C::WAVE_RING;
+    const uint32_t ring_lds =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)ring);
+    auto issue = [&](int stage, int slot) {
+        // past the last stage the ring reloads the last one (never computed)
+        const int64_t kb0 = (s_begin + min(stage, max(nst - 1, 0))) * BKB;
+        const uint32_t lds = ring_lds + slot * BKB * 2 * MX_REC;
+#pragma unroll
+        for (int bb = 0; bb < BKB; bb++) {
+            dma16(arec + (kb0 + bb) * MX_REC + lane * 16, lds + (2 * bb) * MX_REC);
+            dma16(brec + (kb0 + bb) * MX_REC + lane * 16, lds + (2 * bb + 1) * MX_REC);
+        }
+    };
+    const uint32_t sel0 = g ? 0x03020302u : 0x01000100u, sel1 = g ? 0x0C0C0302u : 0x0C0C0100u;
+
+    v16f acc;
+#pragma unroll
+    for (int v = 0; v < 16; v++) acc[v] = 0.0f;
+    // Pipeline: the two MFMAs of block bb + 1 are issued before the
+    // multiply-adds of block bb (one tile per wave leaves nothing else to
+    // cover the MFMA latency).
+    auto mfmas = [&](const uint8_t *st, int bb, v16f &S, v16f &P) {
+        const uint8_t *ra = st + (2 * bb) * MX_REC, *rb = st + (2 * bb + 1) * MX_REC;
+        v8i af = {}, bf = {};  // operand dwords 3..7 are zero
+        const u32x2 a01 = lds_read<u32x2>(ra + 8 * lane), b01 = lds_read<u32x2>(rb + 8 * lane);
+        af[0] = (int)a01.x; af[1] = (int)a01.y; af[2] = (int)lds_read<uint32_t>(ra + 512 + 4 * lane);
+        bf[0] = (int)b01.x; bf[1] = (int)b01.y; bf[2] = (int)lds_read<uint32_t>(rb + 512 + 4 * lane);
+        const u32x2 sp = lds_read<u32x2>(ra + MX_CODE_BYTES + 8 * c);
+        const uint32_t w = lds_read<uint32_t>(rb + MX_CODE_BYTES + 4 * c);
+        S = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, v16f{}, 2, 2, 0, 0, 0, 0);
+        P = mfma_bf16_32x32x8(make_uint2(sp.x, sp.y),
+                              make_uint2(__builtin_amdgcn_perm(w, w, sel0), __builtin_amdgcn_perm(w, w, sel1)));
+    };
+    if (nst > 0) {
+#pragma unroll
+        for (int x = 0; x < NS - 1; x++) issue(x, x);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * BKB * (NS - 2)) : "memory");  // stage 0 has landed
+        v16f S[2], P[2];
+        mfmas(ring, 0, S[0], P[0]);
+        for (int s = 0; s < nst; s++) {
+            const uint8_t *st = ring + (s % NS) * BKB * 2 * MX_REC;
+#pragma unroll
+            for (int bb = 0; bb < BKB; bb++) {
+                if (bb + 1 < BKB) {
+                    mfmas(st, bb + 1, S[(bb + 1) & 1], P[(bb + 1) & 1]);
+                } else {
+                    // next stage: refill the slot computed last, wait for stage s + 1
+                    // (after the last stage this reads a reloaded stage; unused)
+                    issue(s + NS - 1, (s + NS - 1) % NS);
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * BKB * (NS - 2)) : "memory");
+                    mfmas(ring + ((s + 1) % NS) * BKB * 2 * MX_REC, 0, S[(bb + 1) & 1], P[(bb + 1) & 1]);
+                }
+#pragma unroll
+                for (int v = 0; v < 16; v++) acc[v] = fmaf(S[bb & 1][v], P[bb & 1][v], acc[v]);
+                asm volatile("" : "+v"(acc));
+                __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still be writing the ring
+    }
+
+    // the quarters meet in LDS (the rings are free now) in ascending K order
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int v = 0; v < 16; v++) red[(wave * 16 + v) * 64 + lane] = acc[v];
+    __syncthreads();
+    for (int i = tid; i < 16 * 64; i += C::NT) {
+        const int v = i / 64, l = i % 64;
+        const float sum = ((red[(0 * 16 + v) * 64 + l] + red[(1 * 16 + v) * 64 + l]) + red[(2 * 16 + v) * 64 + l]) +
+                          red[(3 * 16 + v) * 64 + l];
+        const int64_t r = rt * 32 + mfma32_row(v, l), col = ct * 32 + (l & 31);
+        if (rt < rtiles && r < a.m && col < a.n) a.y[r * a.ldy + col] = sum;
     }
 }
 

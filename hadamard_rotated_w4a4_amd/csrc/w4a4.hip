@@ -63,33 +63,60 @@ int mx_occupancy() {  // resident workgroups per CU (registers and LDS decide)
     return occ;
 }
 
-// Modelled time of one tile shape: rounds of resident workgroups times the
-// padded work per tile (the smaller tiles reuse operands less: ~8% slower per
-// output on MI355X); ties go to the shape that pads less.
-struct MxCost {
+template <class P>
+int piece_occupancy() {
+    static const int occ = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_mx_piece_kernel<P>, P::NT, 0) != hipSuccess || n < 1)
+            n = 1;
+        return n;
+    }();
+    return occ;
+}
+
+// Launch plan of one tile shape.  Whole rounds of resident workgroups go to
+// the main kernel; the leftover tiles either form one more (partial) round or,
+// when that is cheaper, go to the piece kernel (a piece is 1/PIECES of a tile
+// at about 1.6x the cost per output: no operand reuse across waves).  The
+// modelled time counts rounds x padded work per tile (the smaller tiles reuse
+// operands less: ~15% slower per output on MI355X); ties go to the shape that
+// pads less.
+struct MxPlan {
+    int64_t main_wgs, piece_wgs, first_piece_tile;
     double time, padded;
-    bool operator<=(const MxCost &o) const { return time < o.time || (time == o.time && padded <= o.padded); }
+    bool operator<=(const MxPlan &o) const { return time < o.time || (time == o.time && padded <= o.padded); }
 };
 template <class C>
-MxCost mx_cost(int64_t m, int64_t n) {
+MxPlan mx_plan(int64_t m, int64_t n) {
+    using P = MxPieceCfg<C::BM, C::BN>;
     const int64_t tm = (m + C::BM - 1) / C::BM, tn = (n + C::BN - 1) / C::BN, tiles = tm * tn;
     const int64_t slots = (int64_t)device_cus() * mx_occupancy<C>();
-    const int64_t rounds = (tiles + slots - 1) / slots;
-    return {(double)rounds * C::BM * C::BN * (C::TM * C::TN == 4 ? 1.0 : 1.08), (double)(tm * C::BM) * (tn * C::BN)};
+    const int64_t whole = tiles / slots * slots, left = tiles - whole;
+    const int64_t pslots = (int64_t)device_cus() * piece_occupancy<P>();
+    const double prounds = (double)((left * P::PIECES + pslots - 1) / pslots) * 1.6 / P::PIECES;
+    const bool pieces = left > 0 && prounds < 1.0;
+    const double rounds = (double)(whole / slots) + (left == 0 ? 0.0 : pieces ? prounds : 1.0);
+    MxPlan p;
+    p.main_wgs = pieces ? whole : tiles;
+    p.piece_wgs = pieces ? left * P::PIECES : 0;
+    p.first_piece_tile = whole;
+    p.time = rounds * C::BM * C::BN * (C::TM * C::TN == 4 ? 1.0 : 1.15);
+    p.padded = (double)(tm * C::BM) * (tn * C::BN);
+    return p;
 }
 
 template <class C>
-void launch_mx_cfg(const MxArgs &a, hipStream_t s) {
-    const int64_t wgs = (a.n + C::BN - 1) / C::BN * ((a.m + C::BM - 1) / C::BM);
-    gemm_mx_kernel<C><<<(unsigned)wgs, C::NT, 0, s>>>(a);
+void launch_mx_cfg(const MxArgs &a, const MxPlan &p, hipStream_t s) {
+    if (p.main_wgs > 0) gemm_mx_kernel<C><<<(unsigned)p.main_wgs, C::NT, 0, s>>>(a);
+    if (p.piece_wgs > 0)
+        gemm_mx_piece_kernel<MxPieceCfg<C::BM, C::BN>><<<(unsigned)p.piece_wgs, C::NT, 0, s>>>(a, p.first_piece_tile);
 }
 
 void launch_mx(const MxArgs &a, hipStream_t s) {
-    const MxCost c0 = mx_cost<Mx128x128>(a.m, a.n), c1 = mx_cost<Mx128x64>(a.m, a.n),
-                 c2 = mx_cost<Mx64x128>(a.m, a.n);
-    if (c0 <= c1 && c0 <= c2) launch_mx_cfg<Mx128x128>(a, s);
-    else if (c1 <= c2) launch_mx_cfg<Mx128x64>(a, s);
-    else launch_mx_cfg<Mx64x128>(a, s);
+    const MxPlan p0 = mx_plan<Mx128x128>(a.m, a.n), p1 = mx_plan<Mx128x64>(a.m, a.n), p2 = mx_plan<Mx64x128>(a.m, a.n);
+    if (p0 <= p1 && p0 <= p2) launch_mx_cfg<Mx128x128>(a, p0, s);
+    else if (p1 <= p2) launch_mx_cfg<Mx128x64>(a, p1, s);
+    else launch_mx_cfg<Mx64x128>(a, p2, s);
 }
 // Grouped expert tiles: 32 rows (experts are small), 4 waves across 256 columns.
 using GroupedCfg = TileCfg<1, 4, 1, 2, 4>;

@@ -380,6 +380,9 @@ def test_gemm_id_integer_unit_scales(ops):
 
 
 def test_gemm_id_single_expert_equals_gemm(ops):
+    """E = 1, top_k = 1 is the dense product: both paths meet the oracle's bar
+    and give the same exact integer sums with unit scales (their fp32
+    accumulation orders differ, so real scales are compared by tolerance)."""
     m, n, k = 50, 64, 128
     w, x = _problem(m, n, k, 77)
     say("gemm_id E=1 top_k=1 == gemm")
@@ -388,7 +391,16 @@ def test_gemm_id_single_expert_equals_gemm(ops):
     ids = torch.zeros((m, 1), dtype=torch.int32, device="cuda")
     y1 = host(ops.gemm_id(packed, 1, c, s, 1, ids, n, k))[:, 0, :]
     y0 = host(ops.gemm(packed, c, s, n, k))
-    assert np.array_equal(y0, y1)
+    ref = oracle.gemm(oracle.prepare_weights(w), *oracle.rotate_quantize_act(x), k)
+    assert_rows_close(y0, ref, "gemm")
+    assert_rows_close(y1, ref, "gemm_id")
+    q1 = with_unit_scales(oracle.prepare_weights(w))
+    rc, _ = oracle.rotate_quantize_act(x)
+    ones = dev(np.ones((m, k // 32), np.float32))
+    p1 = ops.repack_q4_0_h32(dev(q1), n, k)
+    yi0 = host(ops.gemm(p1, dev(rc), ones, n, k))
+    yi1 = host(ops.gemm_id(p1, 1, dev(rc), ones, 1, ids, n, k))[:, 0, :]
+    assert np.array_equal(yi0, yi1)
 
 
 @pytest.mark.parametrize("which", ["gate", "down"])
