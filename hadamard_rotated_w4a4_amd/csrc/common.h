@@ -8,6 +8,7 @@
 namespace w4a4 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -50,8 +51,39 @@ __host__ __device__ inline int64_t mx_blocks(int64_t k) { return (k / QK + MX_BL
 __host__ __device__ inline int64_t mx_section_offset(int64_t n, int64_t k) {
     return (padded_n(n) / TILE_N * (k / QK) * (TILE_CODE_BYTES + 2 * TILE_SCALE_HALFS) + 255) / 256 * 256;
 }
+// Streaming section (read by the m <= 16 GEMM), 256-byte aligned after the
+// matrix-core section: [Np/32][nq][2304 B] with nq = ceil(nb / 4), one record
+// per (32-column tile, 4 consecutive blocks).  Per column and block the 32
+// signed codes (q ^ 8) form four "K8 words", one per K-group g of 8 codes:
+// byte i of word g holds code 8 g + i in its low nibble and code 8 g + 4 + i
+// in its high nibble.  Lane l = 16 g + c (c < 16) of a 16x16x32 int8 MFMA
+// wants word g of columns c and 16 + c:
+//   bytes [0, 1024)     lane l's 16 B at 16 l: blocks 0 and 1 of the record,
+//                       each as (word of column c, word of column 16 + c);
+//   bytes [1024, 2048)  the same for blocks 2 and 3;
+//   bytes [2048, 2304)  16 B at 2048 + 16 c: for blocks 0..3 the fp16 pair
+//                       (d of column c, d of column 16 + c).
+// Blocks past nb and padding columns hold zero codes and zero scales.  A wave
+// reads a record with three 16-byte loads per lane, the first two contiguous.
+constexpr int SQ_BLOCKS = 4;            // blocks per streaming record
+constexpr int SQ_REC = 2304;            // bytes per (tile, 4 blocks) record
+constexpr int SQ_SCALE_OFF = 2048;
+__host__ __device__ inline int64_t sq_quads(int64_t k) { return (k / QK + SQ_BLOCKS - 1) / SQ_BLOCKS; }
+__host__ __device__ inline int64_t sq_section_offset(int64_t n, int64_t k) {
+    return (mx_section_offset(n, k) + padded_n(n) / TILE_N * mx_blocks(k) * MX_REC + 255) / 256 * 256;
+}
 __host__ __device__ inline int64_t packed_total_bytes(int64_t n, int64_t k) {
-    return mx_section_offset(n, k) + padded_n(n) / TILE_N * mx_blocks(k) * MX_REC;
+    return sq_section_offset(n, k) + padded_n(n) / TILE_N * sq_quads(k) * SQ_REC;
+}
+// The four K8 words of one block from its 16 Q4_0 code bytes (u.x = bytes
+// 0..3, ...; byte j holds code j low and code j + 16 high).
+__host__ __device__ inline uint4 k8_words(uint4 u) {
+    uint4 w;
+    w.x = (u.x & 0x0F0F0F0Fu) | (u.y & 0x0F0F0F0Fu) << 4;         // codes 0..7
+    w.y = (u.z & 0x0F0F0F0Fu) | (u.w & 0x0F0F0F0Fu) << 4;         // codes 8..15
+    w.z = (u.x >> 4 & 0x0F0F0F0Fu) | (u.y & 0xF0F0F0F0u);         // codes 16..23
+    w.w = (u.z >> 4 & 0x0F0F0F0Fu) | (u.w & 0xF0F0F0F0u);         // codes 24..31
+    return w;
 }
 
 // FP6 E2M3 code of the integer q in [-8, 8], read by the MFMA as q / 8: the

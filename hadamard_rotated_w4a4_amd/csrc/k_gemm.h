@@ -295,146 +295,6 @@ __global__ __launch_bounds__(C::NT) void gemm_tiled_kernel(GemmArgs a) {
 }
 
 // -------------------------------------------------------------------------
-// Small-M kernel (m <= 16): weight streaming, one pass over HBM.
-//
-// A workgroup owns one 32-column tile; its waves split K into contiguous runs
-// of `bpw` blocks, so every weight byte is read once.  Each wave streams its
-// run in stages of SMALL_STAGE blocks through a ring of NS stage buffers of
-// its own in LDS: every byte a stage needs (weight codes and scales,
-// activation codes and scales) arrives by direct global-to-LDS loads, so data
-// in flight costs no registers, and NS - 1 stages are in flight while one is
-// computed.  The loads are issued from inline assembly with the wave's own
-// vmcnt accounting (5 loads per stage, retired in order; the loop issues no
-// other vector-memory operation), because the compiler cannot see that a
-// stage being read is not the one being loaded and would wait for all loads.
-// Past the end of the run the ring keeps loading the last block (L2 hits), so
-// the count of loads in flight is the same at every step.
-//
-// Per block: the int8 MFMA gives S (tile rows 16..31 are unused), an fp32
-// 32x32x2 MFMA the scale products s[m] * d_w[n] (the weight-scale operand is
-// zero in lane group 1, so the other operand's group-1 lanes may hold any
-// finite value), and the VALU does one convert and one fused multiply-add per
-// output.  Rows >= m reuse row m - 1 and blocks past the run get a zero
-// weight scale: nothing diverges and those outputs are never stored or are
-// exactly zero.  The waves' partial sums meet in LDS for one store.
-// -------------------------------------------------------------------------
-constexpr int SMALL_M_MAX = 16;
-constexpr int SMALL_STAGE = 4;          // blocks per stage
-constexpr int SMALL_MAX_WAVES = 8;
-constexpr int SMALL_MAX_NS = 8;          // deepest ring instantiated
-// per stage, in LDS: weight codes [4][512 B], weight scales [4][32] fp16,
-// activation codes [4][16 rows][16 B], activation scales [4][16 rows] fp32
-constexpr int SMALL_W_OFF = 0, SMALL_D_OFF = 2048, SMALL_A_OFF = 2304, SMALL_S_OFF = 3328;
-constexpr int SMALL_STAGE_BYTES = 3584;
-constexpr int SMALL_LOADS_PER_STAGE = 5;
-
-// One global-to-LDS load: lane l's `size` bytes at `g` land at LDS byte
-// address lds + l * size (lds is wave-uniform, passed through M0).
-__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
-}
-__device__ __forceinline__ void lds_dma4(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-template <int NS>
-__global__ __launch_bounds__(64 * SMALL_MAX_WAVES) void gemm_small_m_kernel(GemmArgs a, int bpw) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [waves][NS][stage]
-    const int tid = threadIdx.x, lane = tid & 63, waves = blockDim.x >> 6;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
-    const int g = lane >> 5, c = lane & 31;
-    const int64_t k = a.k, nb = k / QK;
-    const int64_t tile = blockIdx.x;
-    const int m = (int)a.m;
-    const int64_t b0 = min((int64_t)wave * bpw, nb), b1 = min(b0 + bpw, nb);
-    uint8_t *ring = smem + wave * NS * SMALL_STAGE_BYTES;
-    const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
-
-    // per-lane global sources of the stage loads (see the layout above)
-    const uint8_t *wsrc = a.packed + tile * nb * TILE_CODE_BYTES + (lane & 31) * 16;      // + blk * 512
-    const uint8_t *dsrc = a.packed + packed_code_bytes(a.n, k) + tile * nb * 64 + (lane & 15) * 4;
-    const int arow = min(lane & 15, m - 1);
-    const uint8_t *asrc = a.codes + (int64_t)arow * (k / 2);                               // + blk * 16
-    const float *ssrc = a.scales + (int64_t)arow * nb;                                     // + blk
-
-    auto issue = [&](int64_t b, int slot) {  // loads of blocks b .. b + 3 (clamped to the run)
-        const uint32_t st = ring_lds + slot * SMALL_STAGE_BYTES;
-        const int64_t last = b1 - 1;
-        const int64_t bw0 = min(b + (lane >> 5), last), bw1 = min(b + 2 + (lane >> 5), last);
-        const int64_t bq = min(b + (lane >> 4), last);
-        lds_dma16(wsrc + bw0 * TILE_CODE_BYTES, st + SMALL_W_OFF);
-        lds_dma16(wsrc + bw1 * TILE_CODE_BYTES, st + SMALL_W_OFF + 1024);
-        lds_dma4(dsrc + bq * 64, st + SMALL_D_OFF);
-        lds_dma16(asrc + bq * 16, st + SMALL_A_OFF);
-        lds_dma4(ssrc + bq, st + SMALL_S_OFF);
-    };
-
-    float acc[8];
-#pragma unroll
-    for (int v = 0; v < 8; v++) acc[v] = 0.0f;
-
-    const int row = min(c, m - 1);  // this lane's activation row in the MFMA
-    auto compute = [&](int64_t b, int slot) {
-        const uint8_t *st = ring + slot * SMALL_STAGE_BYTES;
-#pragma unroll
-        for (int u = 0; u < SMALL_STAGE; u++) {
-            const uint2 w = *reinterpret_cast<const uint2 *>(st + SMALL_W_OFF + u * 512 + lane * 8);
-            const uint32_t d = *reinterpret_cast<const uint16_t *>(st + SMALL_D_OFF + u * 64 + c * 2);
-            const uint2 av = *reinterpret_cast<const uint2 *>(st + SMALL_A_OFF + (u * 16 + row) * 16 + g * 8);
-            const float sc = *reinterpret_cast<const float *>(st + SMALL_S_OFF + (u * 16 + row) * 4);
-            const v16i S = mfma_i8_32x32x32(unpack_nibbles_x16(av.x, av.y), unpack_nibbles_x16(w.x, w.y));
-            // lane group 1 and blocks past the run contribute a zero weight scale
-            const uint32_t keep = (b + u < b1) ? (uint32_t)(g - 1) & 0xFFFFu : 0u;  // 0xFFFF for g == 0
-            // / 256 (exact) undoes the 16 x 16 scaling of the unpacked operands
-            const float dw = __half2float(__ushort_as_half((uint16_t)(d & keep))) * (1.0f / 256.0f);
-            const v16f P = mfma_f32_32x32x2(sc, dw);
-#pragma unroll
-            for (int v = 0; v < 8; v++) acc[v] = fmaf((float)S[v], P[v], acc[v]);
-        }
-    };
-
-    if (b0 < b1) {
-#pragma unroll
-        for (int s = 0; s < NS - 1; s++) issue(b0 + s * SMALL_STAGE, s);
-        int slot = 0;
-        for (int64_t b = b0; b < b1; b += SMALL_STAGE) {
-            int ahead = slot + NS - 1;
-            if (ahead >= NS) ahead -= NS;
-            issue(b + (NS - 1) * SMALL_STAGE, ahead);              // keep NS - 1 stages in flight
-            wait_vmcnt<SMALL_LOADS_PER_STAGE * (NS - 1)>();        // this stage has landed
-            compute(b, slot);
-            // the next issue overwrites the slot computed NS - 1 stages from now;
-            // this slot is refilled only after its reads have returned
-            if (++slot == NS) slot = 0;
-        }
-        wait_vmcnt<0>();  // no load may still write the LDS reused below
-    }
-
-    // cross-wave reduction, reusing the front of this wave's ring
-    __syncthreads();
-    float *red = reinterpret_cast<float *>(ring);
-#pragma unroll
-    for (int v = 0; v < 8; v++) red[v * 64 + lane] = acc[v];
-    __syncthreads();
-    for (int i = tid; i < 8 * 64; i += blockDim.x) {
-        const int v = i / 64, l = i % 64;
-        float sum = 0.0f;
-        for (int w = 0; w < waves; w++) sum += reinterpret_cast<const float *>(smem + w * NS * SMALL_STAGE_BYTES)[i];
-        const int r = mfma32_row(v, l);
-        const int64_t col = tile * 32 + (l & 31);
-        if (r < m && col < a.n) a.y[(int64_t)r * a.ldy + col] = sum;
-    }
-}
-
-// -------------------------------------------------------------------------
 // MUL_MAT_ID routing: one workgroup groups the (token, slot) rows by expert
 // and counts each expert's row tiles; rows with an invalid id are zeroed.
 // -------------------------------------------------------------------------

@@ -129,4 +129,35 @@ __global__ __launch_bounds__(256) void repack_mx_kernel(const uint8_t *__restric
     reinterpret_cast<uint32_t *>(rec + MX_CODE_BYTES + 128)[c] = 0u;
 }
 
+// Streaming records (see common.h), one thread per (tile, padded block,
+// column).
+__global__ __launch_bounds__(256) void repack_sq_kernel(const uint8_t *__restrict__ q4, int64_t n,
+                                                        int64_t k, uint8_t *__restrict__ packed) {
+    const int64_t nb = k / QK, nq = sq_quads(k);
+    const int64_t tiles = padded_n(n) / TILE_N;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= tiles * nq * SQ_BLOCKS * 32) return;
+    const int c = (int)(gid & 31);
+    const int64_t tb = gid >> 5;  // tile * 4 nq + padded block
+    const int64_t tile = tb / (nq * SQ_BLOCKS), b = tb % (nq * SQ_BLOCKS);
+    const int64_t col = tile * TILE_N + c;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    uint16_t dbits = 0;
+    if (col < n && b < nb) {
+        const uint8_t *blk = q4 + (col * nb + b) * 18;
+        uint32_t u[4];
+        for (int i = 0; i < 4; i++)
+            u[i] = ((uint32_t)blk[2 + 4 * i] | (uint32_t)blk[3 + 4 * i] << 8 | (uint32_t)blk[4 + 4 * i] << 16 |
+                    (uint32_t)blk[5 + 4 * i] << 24) ^ 0x88888888u;  // q ^ 8: signed nibble q - 8
+        w = k8_words(make_uint4(u[0], u[1], u[2], u[3]));
+        dbits = (uint16_t)(blk[0] | (blk[1] << 8));
+    }
+    uint8_t *rec = packed + sq_section_offset(n, k) + (tile * nq + b / SQ_BLOCKS) * SQ_REC;
+    const int j = (int)(b % SQ_BLOCKS), c16 = c & 15, half = c >> 4;
+    const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+    for (int g = 0; g < 4; g++)
+        reinterpret_cast<uint32_t *>(rec + (j >> 1) * 1024 + (16 * g + c16) * 16 + (j & 1) * 8)[half] = words[g];
+    reinterpret_cast<uint16_t *>(rec + SQ_SCALE_OFF + c16 * 16 + j * 4)[half] = dbits;
+}
+
 }  // namespace w4a4

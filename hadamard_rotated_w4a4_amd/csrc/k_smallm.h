@@ -1,0 +1,244 @@
+// W4A4 GEMM for m <= 16 (a speculative-verify-sized batch): HBM-bound, every
+// weight byte is read from HBM once per call.
+//
+// 1bit-MONSTER engine docs, "The lean option: ROCmFP4, ROCmI4 and Hadamard
+// Q4_0", section "Hadamard-rotated Q4_0: W4A4 prompt processing": the same
+// int4 x int4 block dots and per-block scaling as the large-m path; only the
+// way the weights are streamed differs.
+//
+// Work split: a workgroup owns one 32-column weight tile and a contiguous
+// range of K (split z of the tile's streaming records, 4 blocks each; narrow
+// projections split K so that every CU gets workgroups).  At the start it
+// stages the range's activations in LDS: per block, the 16 rows' codes as K8
+// words (the weights' order, see common.h) and the rows' fp32 scales.  Its
+// waves then take the range's records round-robin and stream them straight
+// into registers through a ring SM_DEPTH records deep (a wave's weight bytes
+// are its own, so they need no LDS).  Per block and wave: two 16x16x32 int8
+// MFMAs (columns c and 16 + c of the tile, all 16 rows), then per output a
+// convert, the scale product s * d and a fused multiply-add.  Codes enter the
+// MFMA as 16 x (signed nibble), so the integer sum is 256 S, and d is scaled
+// by 2^-8 (exact) to match.  The waves' sums meet in LDS; the workgroup
+// stores its 16 x 32 outputs, or its partial sums when K is split (a second
+// kernel adds the splits in ascending order).
+//
+// Measured on MI355X (7 dense projections of a 27B-class layer, 16 rows):
+// 8 waves per workgroup and a 2-record ring beat 4 waves or deeper rings;
+// sharing one staged activation range across 2 or 4 tiles per workgroup was
+// slower (fewer workgroups, more K splits).
+#pragma once
+
+#include "common.h"
+
+namespace w4a4 {
+
+constexpr int SMALL_M_MAX = 16;
+constexpr int SM_WAVES = 8;             // waves per workgroup
+constexpr int SM_DEPTH = 2;             // streaming records in flight per wave
+constexpr int SM_MAX_RANGE = 40;        // records per workgroup (activations staged: 1280 B each)
+constexpr int SM_ITEM_TARGET = 512;     // workgroups wanted (two per CU on a 256-CU part)
+constexpr int SM_ACT_REC_BYTES = SQ_BLOCKS * (64 * 4 + 16 * 4);  // K8 words + scales of 16 rows
+
+struct SmallArgs {
+    const uint8_t *codes;   // activation codes [m][k/2]
+    const float *scales;    // activation scales [m][k/32]
+    const uint8_t *sq;      // streaming section of the packed weights
+    float *y;               // [m][ldy] (splits == 1) ...
+    float *partial;         // ... or [splits][m][n] partial sums
+    int64_t ldy, m, n, k;
+    int64_t range;          // records per split
+};
+
+// Launch plan of an m <= 16 product: the K splits.  A workgroup's staged
+// activation range must fit its LDS share, and narrow projections split
+// further so that about SM_ITEM_TARGET workgroups run.  Pure function of the
+// sizes (the workspace size depends on it).
+struct SmallPlan {
+    int64_t tiles, splits, range;
+};
+__host__ __device__ inline SmallPlan small_m_plan(int64_t n, int64_t k) {
+    const int64_t tiles = padded_n(n) / TILE_N, nq = sq_quads(k);
+    int64_t splits = (nq + SM_MAX_RANGE - 1) / SM_MAX_RANGE;
+    const int64_t want = (SM_ITEM_TARGET + tiles - 1) / tiles;
+    if (want > splits) splits = want < nq ? want : nq;
+    const int64_t range = (nq + splits - 1) / splits;
+    return SmallPlan{tiles, (nq + range - 1) / range, range};
+}
+__host__ __device__ inline int64_t small_m_splits(int64_t n, int64_t k) { return small_m_plan(n, k).splits; }
+
+__device__ __forceinline__ long widen_k8(uint32_t w) {  // 8 signed nibbles -> 8 x int8 (x 16), K order
+    const uint32_t lo = (w << 4) & 0xF0F0F0F0u, hi = w & 0xF0F0F0F0u;
+    return (long)((uint64_t)hi << 32 | lo);
+}
+
+__device__ __forceinline__ v4i mfma_i8_16x16x32(long a, long b) {
+    return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, v4i{0, 0, 0, 0}, 0, 0, 0);
+}
+
+template <int WAVES, int DEPTH>
+__global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
+    const int64_t k = a.k, nb = k / QK, nq = sq_quads(k);
+    const int64_t tiles = padded_n(a.n) / TILE_N;
+    const int64_t tile = blockIdx.x, z = blockIdx.y;
+    const int m = (int)a.m;
+    const int64_t q_lo = z * a.range;
+    const int nr = (int)min(nq - q_lo, a.range);  // records of this split (>= 1)
+
+    // this wave's records: local index wave, wave + WAVES, ...
+    const int cnt = nr > wave ? (nr - wave + WAVES - 1) / WAVES : 0;
+    // Buffer loads over this split's records: the record offset is scalar and
+    // the lane offset a fixed register, so no address arithmetic touches the
+    // registers that loads are still filling (the hardware also range-checks
+    // every load against the split's bytes).
+    const __amdgpu_buffer_rsrc_t wbuf = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(a.sq + (tile * nq + q_lo) * SQ_REC), 0, nr * SQ_REC, 0x00020000);
+    const int lo16 = lane * 16, d16 = SQ_SCALE_OFF + (lane & 15) * 16;
+    struct Rec {
+        v4u c0, c1, d;
+    };
+    // Every wave issues the same loads whatever its count (slots past it
+    // reload the split's last record, a cache hit), so the number of loads in
+    // flight is the same on every path into the main loop and its waits stay
+    // exact.
+    auto load = [&](int i, Rec &R) {
+        const int off = __builtin_amdgcn_readfirstlane(min(wave + WAVES * i, nr - 1) * SQ_REC);
+        R.c0 = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lo16, off, 0);
+        __builtin_amdgcn_sched_barrier(0);  // one issue order everywhere (c0, c1, d)
+        R.c1 = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lo16 + 1024, off, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        R.d = __builtin_amdgcn_raw_buffer_load_b128(wbuf, d16, off, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Staging of the range's activations in LDS: K8 words [block][g][row],
+    // then scales [block][row].  Every thread issues all of its loads at once
+    // (at most FILL, addresses clamped into the matrix, out-of-range items
+    // zeroed afterwards), then the ring's first records, and only then waits
+    // and writes LDS: one cache latency, overlapped with the weights'.
+    constexpr int FILL = SM_MAX_RANGE * SQ_BLOCKS * 16 / (64 * WAVES);
+    static_assert(FILL * 64 * WAVES == SM_MAX_RANGE * SQ_BLOCKS * 16, "whole staging rounds");
+    const int items = nr * SQ_BLOCKS * 16;
+    uint4 fu[FILL];
+    float fs[FILL];
+#pragma unroll
+    for (int t = 0; t < FILL; t++) {
+        const int i = min(tid + t * 64 * WAVES, items - 1);
+        const int r = min(i & 15, m - 1);
+        const int64_t b = min(q_lo * SQ_BLOCKS + (i >> 4), nb - 1);
+        fu[t] = *reinterpret_cast<const uint4 *>(a.codes + (int64_t)r * (k / 2) + b * 16);
+        fs[t] = a.scales[(int64_t)r * nb + b];
+    }
+    Rec ring[DEPTH];
+#pragma unroll
+    for (int j = 0; j < DEPTH - 1; j++) load(j, ring[j]);
+    uint32_t *act = reinterpret_cast<uint32_t *>(smem);
+    float *asc = reinterpret_cast<float *>(smem + nr * SQ_BLOCKS * 256);
+#pragma unroll
+    for (int t = 0; t < FILL; t++) {
+        const int i = tid + t * 64 * WAVES, bl = i >> 4, r = i & 15;
+        // rows past m and blocks past nb are zero
+        const bool live = r < m && q_lo * SQ_BLOCKS + bl < nb;
+        const uint4 w = k8_words(live ? fu[t] : make_uint4(0, 0, 0, 0));
+        if (i < items) {
+            act[bl * 64 + 0 * 16 + r] = w.x;
+            act[bl * 64 + 1 * 16 + r] = w.y;
+            act[bl * 64 + 2 * 16 + r] = w.z;
+            act[bl * 64 + 3 * 16 + r] = w.w;
+            asc[bl * 16 + r] = live ? fs[t] : 0.0f;
+        }
+    }
+    __syncthreads();
+
+    float acc[8];
+#pragma unroll
+    for (int v = 0; v < 8; v++) acc[v] = 0.0f;
+    // One block: two MFMAs (columns c and 16 + c of the tile, all 16 rows),
+    // then per output the scale product and a fused multiply-add.
+    auto block = [&](int bl, uint32_t w0, uint32_t w1, uint32_t dpair) {
+        const long av = widen_k8(act[bl * 64 + lane]);  // row lane % 16, K-group lane / 16
+        const v4i S0 = mfma_i8_16x16x32(av, widen_k8(w0));
+        const v4i S1 = mfma_i8_16x16x32(av, widen_k8(w1));
+        const float4 s4 = *reinterpret_cast<const float4 *>(asc + bl * 16 + 4 * (lane >> 4));
+        const float d0 = __half2float(__ushort_as_half((uint16_t)(dpair & 0xFFFF))) * (1.0f / 256.0f);
+        const float d1 = __half2float(__ushort_as_half((uint16_t)(dpair >> 16))) * (1.0f / 256.0f);
+        const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            acc[i] = fmaf((float)S0[i], __fmul_rn(sv[i], d0), acc[i]);
+            acc[4 + i] = fmaf((float)S1[i], __fmul_rn(sv[i], d1), acc[4 + i]);
+        }
+    };
+    auto compute = [&](int i, const Rec &R) {
+        const int bl = (wave + WAVES * i) * SQ_BLOCKS;
+        block(bl + 0, R.c0[0], R.c0[1], R.d[0]);
+        block(bl + 1, R.c0[2], R.c0[3], R.d[1]);
+        block(bl + 2, R.c1[0], R.c1[1], R.d[2]);
+        block(bl + 3, R.c1[2], R.c1[3], R.d[3]);
+    };
+
+    // Ring of DEPTH records: record i + DEPTH - 1 is loaded before record i
+    // is computed.  The loop is unrolled DEPTH times so that every ring index
+    // is static; the scheduling barriers keep the loads ahead of the compute
+    // (the scheduler would otherwise sink them to their first use).
+    for (int i = 0; i < cnt; i += DEPTH) {
+#pragma unroll
+        for (int j = 0; j < DEPTH; j++) {
+            load(i + j + DEPTH - 1, ring[(j + DEPTH - 1) % DEPTH]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(i + j, ring[j]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i + j + 1 >= cnt) break;
+        }
+    }
+
+    // the waves' sums meet in LDS (ascending wave order), then one store
+    __syncthreads();  // every wave is done with the staged activations
+    float *red = reinterpret_cast<float *>(smem);  // [wave][8][64]
+#pragma unroll
+    for (int v = 0; v < 8; v++) red[(wave * 8 + v) * 64 + lane] = acc[v];
+    __syncthreads();
+    for (int i = tid; i < 512; i += 64 * WAVES) {
+        const int v = i >> 6, l = i & 63;
+        float sum = red[i];
+#pragma unroll
+        for (int w = 1; w < WAVES; w++) sum += red[w * 512 + i];
+        const int r = 4 * (l >> 4) + (v & 3);
+        const int64_t col = tile * TILE_N + (v >> 2) * 16 + (l & 15);
+        if (r < m && col < a.n) {
+            if (a.partial) a.partial[(z * a.m + r) * a.n + col] = sum;
+            else a.y[(int64_t)r * a.ldy + col] = sum;
+        }
+    }
+}
+
+// LDS bytes of one workgroup: the staged activations, or the cross-wave
+// reduction if that is larger.
+__host__ inline size_t small_m_lds_bytes(const SmallPlan &p) {
+    const size_t stage = (size_t)p.range * SM_ACT_REC_BYTES, red = (size_t)SM_WAVES * 8 * 64 * 4;
+    return stage > red ? stage : red;
+}
+
+// y = sum over the K splits of the partial sums, in ascending split order.
+// The loads of eight splits are issued together (clamped past the last
+// split, which then adds nothing), so the latency is paid once per eight.
+__global__ __launch_bounds__(256) void small_m_reduce_kernel(const float *__restrict__ partial, int64_t splits,
+                                                             int64_t m, int64_t n, float *__restrict__ y,
+                                                             int64_t ldy) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= m * n) return;
+    const int64_t mn = m * n;
+    float sum = 0.0f;
+    for (int64_t z0 = 0; z0 < splits; z0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = partial[min(z0 + j, splits - 1) * mn + i];
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            if (z0 + j < splits) sum = (z0 + j == 0) ? v[j] : sum + v[j];
+    }
+    y[(i / n) * ldy + i % n] = sum;
+}
+
+}  // namespace w4a4

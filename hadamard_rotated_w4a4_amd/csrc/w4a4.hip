@@ -15,6 +15,7 @@
 #include "k_gemm.h"
 #include "k_prep.h"
 #include "k_rotq.h"
+#include "k_smallm.h"
 
 using namespace w4a4;
 
@@ -191,7 +192,12 @@ w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int6
     const int64_t mx_threads = padded_n(n) / TILE_N * mx_blocks(k) * 32;
     repack_mx_kernel<<<blocks_for(mx_threads, 256), 256, 0, as_stream(stream)>>>(
         static_cast<const uint8_t *>(q4_0), n, k, static_cast<uint8_t *>(packed));
-    return hip_status("repack_mx_kernel");
+    const w4a4_status st2 = hip_status("repack_mx_kernel");
+    if (st2 != W4A4_OK) return st2;
+    const int64_t sq_threads = padded_n(n) / TILE_N * sq_quads(k) * SQ_BLOCKS * 32;
+    repack_sq_kernel<<<blocks_for(sq_threads, 256), 256, 0, as_stream(stream)>>>(
+        static_cast<const uint8_t *>(q4_0), n, k, static_cast<uint8_t *>(packed));
+    return hip_status("repack_sq_kernel");
 }
 
 namespace {
@@ -238,7 +244,11 @@ w4a4_status w4a4_rotate_quantize_prepare(const void *x, w4a4_dtype dt, int64_t m
 
 size_t w4a4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
     if (m < 0 || n < 0 || k < 0 || k % QK) return 0;
-    if (m <= SMALL_M_MAX || n == 0 || k == 0) return 0;
+    if (n == 0 || k == 0 || m == 0) return 0;
+    if (m <= SMALL_M_MAX) {  // partial sums of the K splits
+        const int64_t splits = small_m_splits(n, k);
+        return splits > 1 ? (size_t)((splits * m * n * 4 + 255) / 256 * 256) : 0;
+    }
     return w4a4_act_operand_bytes(m, k);
 }
 
@@ -258,43 +268,30 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
         return hip_status("zero_rows_kernel");
     }
     if (m <= SMALL_M_MAX) {
-        GemmArgs a{};
+        const int64_t splits = small_m_splits(n, k);
+        if (splits > 1) {
+            if (!workspace) return W4A4_ERR_INVALID_VALUE;
+            if (!aligned(workspace, 256)) return W4A4_ERR_MISALIGNED;
+            if (workspace_bytes < w4a4_gemm_workspace_bytes(m, n, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
+        }
+        SmallArgs a{};
         a.codes = codes;
         a.scales = scales;
-        a.packed = static_cast<const uint8_t *>(packed_w);
+        a.sq = static_cast<const uint8_t *>(packed_w) + sq_section_offset(n, k);
         a.y = y;
+        a.partial = splits > 1 ? static_cast<float *>(workspace) : nullptr;
         a.ldy = ldy;
         a.m = m;
         a.n = n;
         a.k = k;
-        const int64_t tiles_n = padded_n(n) / TILE_N;
-        // One workgroup per 32-column tile, all resident in one round.  Most
-        // waves per tile first (runs of >= 4 stages, <= 6 waves per SIMD):
-        // one wave's compute is a serial MFMA chain, so spreading K wins.
-        // Then the ring depth the LDS left per workgroup allows, within 64 KB:
-        // measured on MI355X, rings deeper than that were slower, not faster.
-        const int64_t nb = k / QK;
-        const int64_t stages = (nb + SMALL_STAGE - 1) / SMALL_STAGE;
-        const int64_t wgs_per_cu = (tiles_n + 255) / 256;
-        int64_t w = std::min<int64_t>(SMALL_MAX_WAVES, std::max<int64_t>(1, stages / 4));
-        while (w > 1 && w * wgs_per_cu > 24) w--;
-        const int64_t lds_budget = std::min<int64_t>(64 * 1024, 160 * 1024 / wgs_per_cu);
-        while (w > 1 && w * 2 * SMALL_STAGE_BYTES > lds_budget) w--;
-        const int64_t ns = std::max<int64_t>(2, std::min<int64_t>(SMALL_MAX_NS, lds_budget / (w * SMALL_STAGE_BYTES)));
-        const int64_t bpw = (stages + w - 1) / w * SMALL_STAGE;
-        const int waves = (int)((nb + bpw - 1) / bpw);
-        const size_t lds = (size_t)waves * ns * SMALL_STAGE_BYTES;
-        const dim3 grid((unsigned)tiles_n), block(64 * waves);
-        switch (ns) {
-        case 2: gemm_small_m_kernel<2><<<grid, block, lds, s>>>(a, (int)bpw); break;
-        case 3: gemm_small_m_kernel<3><<<grid, block, lds, s>>>(a, (int)bpw); break;
-        case 4: gemm_small_m_kernel<4><<<grid, block, lds, s>>>(a, (int)bpw); break;
-        case 5: gemm_small_m_kernel<5><<<grid, block, lds, s>>>(a, (int)bpw); break;
-        case 6: gemm_small_m_kernel<6><<<grid, block, lds, s>>>(a, (int)bpw); break;
-        case 7: gemm_small_m_kernel<7><<<grid, block, lds, s>>>(a, (int)bpw); break;
-        default: gemm_small_m_kernel<8><<<grid, block, lds, s>>>(a, (int)bpw); break;
-        }
-        return hip_status("gemm_small_m_kernel");
+        const SmallPlan plan = small_m_plan(n, k);
+        a.range = plan.range;
+        gemm_small_m_kernel<SM_WAVES, SM_DEPTH><<<dim3((unsigned)plan.tiles, (unsigned)plan.splits), 64 * SM_WAVES,
+                                                   small_m_lds_bytes(plan), s>>>(a);
+        const w4a4_status st2 = hip_status("gemm_small_m_kernel");
+        if (st2 != W4A4_OK || splits == 1) return st2;
+        small_m_reduce_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(a.partial, splits, m, n, y, ldy);
+        return hip_status("small_m_reduce_kernel");
     }
     const w4a4_status pst = w4a4_gemm_prepare_act(codes, scales, m, k, workspace, workspace_bytes, stream);
     if (pst != W4A4_OK) return pst;

@@ -83,12 +83,15 @@ size_t w4a4_packed_weight_bytes(int64_t n, int64_t k);
  *           name is the caller's assertion that the weights were rotated:
  *           unrotated weights give silently wrong products.
  *   packed  out, w4a4_packed_weight_bytes(n, k) bytes, 256-byte aligned.  Its
- *           layout is private to this library.  It holds the weights twice,
- *           losslessly: 4-bit codes stored as q ^ 8 (read as a signed nibble
- *           that is exactly q - 8, the page's identity) with the fp16 scales,
- *           streamed by the m <= 16 kernel; and the matrix-core operand of the
- *           m > 16 kernels (each q - 8 as an FP6 E2M3 code, the scale as an
- *           exact bf16 pair), 8 bits per weight.
+ *           layout is private to this library.  It holds the weights three
+ *           times, losslessly, once per consumer: 4-bit codes stored as
+ *           q ^ 8 (read as a signed nibble that is exactly q - 8, the page's
+ *           identity) with the fp16 scales, in the tile order of the grouped
+ *           expert kernel; the matrix-core operand of the m > 16 kernels
+ *           (each q - 8 as an FP6 E2M3 code, the scale as an exact bf16
+ *           pair), 8 bits per weight; and the same 4-bit codes and fp16
+ *           scales in 2304-byte records of 32 columns x 4 blocks, streamed
+ *           by the m <= 16 kernel.
  */
 w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int64_t k,
                                  void *stream);
@@ -109,8 +112,8 @@ w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int6
 w4a4_status w4a4_rotate_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k,
                                      int64_t ldx, uint8_t *codes, float *scales, void *stream);
 
-/* Workspace bytes w4a4_gemm needs for these sizes (0 when m <= 16 or an
- * argument is invalid).  Host only, pure. */
+/* Workspace bytes w4a4_gemm needs for these sizes (0 when none is needed or
+ * an argument is invalid).  Host only, pure. */
 size_t w4a4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 /* Bytes of the matrix-core operand of m activation rows of width k (0 for
@@ -137,9 +140,12 @@ w4a4_status w4a4_rotate_quantize_prepare(const void *x, w4a4_dtype dt, int64_t m
  *   workspace device scratch of w4a4_gemm_workspace_bytes(m, n, k) bytes,
  *             256-byte aligned (may be NULL when that is 0); contents on entry
  *             are ignored.  Calls that share a workspace must not overlap.
- * m <= 16 takes a weight-streaming kernel on the 4-bit codes.  Larger m first
- * re-lays the activation codes and scales into the matrix-core operand format
- * in the workspace, then runs the tiled matrix-core kernel.
+ * m <= 16 takes a weight-streaming kernel on the 4-bit records (products
+ * with few 32-column tiles or long K split K over workgroups; the workspace
+ * then holds their partial sums, added in ascending split order by a second
+ * kernel).  Larger m first re-lays the activation codes and
+ * scales into the matrix-core operand format in the workspace, then runs the
+ * tiled matrix-core kernel.
  */
 w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *scales, float *y,
                       int64_t m, int64_t n, int64_t k, int64_t ldy, void *workspace,

@@ -44,8 +44,8 @@ def test_size_queries(L):
     assert L.w4a4_q4_0_bytes(17408, 5120) == 17408 * 160 * 18
     # packed = 32-column tiles x blocks x (512 code bytes + 32 fp16 scales),
     # rounded up to 256 bytes, then 32-column tiles x blocks padded to 8 x 1 KB
-    assert L.w4a4_packed_weight_bytes(17408, 5120) == 17408 * 160 * 18 + 544 * 160 * 1024
-    assert L.w4a4_packed_weight_bytes(33, 64) == 2 * 2 * 576 + 2 * 8 * 1024  # n padded to 64
+    assert L.w4a4_packed_weight_bytes(17408, 5120) == 17408 * 160 * 18 + 544 * 160 * 1024 + 544 * 40 * 2304
+    assert L.w4a4_packed_weight_bytes(33, 64) == 2 * 2 * 576 + 2 * 8 * 1024 + 2 * 1 * 2304  # n padded to 64
     assert L.w4a4_packed_weight_bytes(10, 33) == 0
     assert L.w4a4_gemm_id_workspace_bytes(128, 1024, 8) == 2 * 768 + 32768
     assert L.w4a4_gemm_id_workspace_bytes(-1, 1, 1) == 0
