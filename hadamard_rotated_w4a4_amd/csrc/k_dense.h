@@ -135,10 +135,10 @@ __device__ __forceinline__ void mx_tile_of(int64_t id, int64_t nx, int64_t ny, i
     by = in / width;
 }
 
+// One whole tile (workgroup index id) of the main kernel.
 template <class C>
-__global__ __launch_bounds__(C::NT) void gemm_mx_kernel(MxArgs a) {
+__device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *smem) {
     constexpr int BKB = C::BKB, NS = C::NS, TM = C::TM, TN = C::TN, RT = C::RT;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mx_kernel(MxArgs a) {
     const int64_t rtiles = (a.m + 31) / 32, ctiles = padded_n(a.n) / TILE_N;
 
     int64_t bx, by;
-    mx_tile_of(blockIdx.x, (a.n + C::BN - 1) / C::BN, (a.m + C::BM - 1) / C::BM, bx, by);
+    mx_tile_of(id, (a.n + C::BN - 1) / C::BN, (a.m + C::BM - 1) / C::BM, bx, by);
     const int64_t rt0 = by * RT, ct0 = bx * C::CT;
 
     // ---- this wave's loads: DMA_PER_WAVE records of 1 KB per stage ----
@@ -293,8 +293,8 @@ __global__ __launch_bounds__(C::NT) void gemm_mx_kernel(MxArgs a) {
 
 // ---------------------------------------------------------------------------
 // Leftover tiles.  When the workgroup tiles of a problem do not fill whole
-// rounds of the GPU, the main kernel takes the whole rounds and this kernel
-// the rest: each workgroup computes one 32x32 piece of a leftover tile, its 4
+// rounds of the GPU, whole tiles take the whole rounds and pieces the rest:
+// each such workgroup computes one 32x32 piece of a leftover tile, its 4
 // waves each over a quarter of K, and the quarters meet in LDS.  A wave
 // streams its own operand records through its own LDS ring (no barrier until
 // the reduction), two MFMAs and 16 multiply-adds per block as above.
@@ -308,9 +308,8 @@ struct MxPieceCfg {
 };
 
 template <class C>
-__global__ __launch_bounds__(C::NT) void gemm_mx_piece_kernel(MxArgs a, int64_t first_tile) {
+__device__ __forceinline__ void mx_piece(const MxArgs &a, int64_t first_tile, int64_t id, uint8_t *smem) {
     constexpr int BKB = C::BKB, NS = C::NS;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::WAVE_RING];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -319,8 +318,8 @@ __global__ __launch_bounds__(C::NT) void gemm_mx_piece_kernel(MxArgs a, int64_t 
     const int64_t rtiles = (a.m + 31) / 32, ctiles = padded_n(a.n) / TILE_N;
 
     int64_t bx, by;
-    mx_tile_of(first_tile + blockIdx.x / C::PIECES, (a.n + C::BN - 1) / C::BN, (a.m + C::BM - 1) / C::BM, bx, by);
-    const int sub = blockIdx.x % C::PIECES;
+    mx_tile_of(first_tile + id / C::PIECES, (a.n + C::BN - 1) / C::BN, (a.m + C::BM - 1) / C::BM, bx, by);
+    const int sub = (int)(id % C::PIECES);
     const int64_t rt = by * (C::BM / 32) + sub / (C::BN / 32), ct = bx * (C::BN / 32) + sub % (C::BN / 32);
     // pieces past the matrix edge compute on clamped tiles and store nothing
     const uint8_t *arec = a.act + min(rt, rtiles - 1) * nbp * MX_REC;
@@ -404,6 +403,20 @@ __global__ __launch_bounds__(C::NT) void gemm_mx_piece_kernel(MxArgs a, int64_t 
         const int64_t r = rt * 32 + mfma32_row(v, l), col = ct * 32 + (l & 31);
         if (rt < rtiles && r < a.m && col < a.n) a.y[r * a.ldy + col] = sum;
     }
+}
+
+// One launch for a whole product: workgroups below main_wgs take whole tiles
+// (in the XCD-aware order), the rest take the pieces of the leftover tiles.
+// Workgroups are dispatched in index order, so the pieces fill the CUs that
+// the last whole tiles leave idle, without a second launch and its gap.
+template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_mx_kernel(MxArgs a, int64_t main_wgs, int64_t first_piece_tile) {
+    using P = MxPieceCfg<C::BM, C::BN>;
+    static_assert(P::NT == C::NT, "one workgroup size for both kinds");
+    constexpr int MAIN_LDS = C::NS * C::STAGE_BYTES, PIECE_LDS = 4 * P::WAVE_RING;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[MAIN_LDS > PIECE_LDS ? MAIN_LDS : PIECE_LDS];
+    if ((int64_t)blockIdx.x < main_wgs) mx_tile<C>(a, blockIdx.x, smem);  // uniform per workgroup
+    else mx_piece<P>(a, first_piece_tile, blockIdx.x - main_wgs, smem);
 }
 
 }  // namespace w4a4

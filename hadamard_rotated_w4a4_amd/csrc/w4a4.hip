@@ -64,20 +64,9 @@ int mx_occupancy() {  // resident workgroups per CU (registers and LDS decide)
     return occ;
 }
 
-template <class P>
-int piece_occupancy() {
-    static const int occ = [] {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_mx_piece_kernel<P>, P::NT, 0) != hipSuccess || n < 1)
-            n = 1;
-        return n;
-    }();
-    return occ;
-}
-
-// Launch plan of one tile shape.  Whole rounds of resident workgroups go to
-// the main kernel; the leftover tiles either form one more (partial) round or,
-// when that is cheaper, go to the piece kernel (a piece is 1/PIECES of a tile
+// Launch plan of one tile shape.  Whole rounds of resident workgroups take
+// whole tiles; the leftover tiles either form one more (partial) round or,
+// when that is cheaper, are split into pieces (a piece is 1/PIECES of a tile
 // at about 1.6x the cost per output: no operand reuse across waves).  The
 // modelled time counts rounds x padded work per tile (the smaller tiles reuse
 // operands less: ~15% slower per output on MI355X); ties go to the shape that
@@ -93,8 +82,7 @@ MxPlan mx_plan(int64_t m, int64_t n) {
     const int64_t tm = (m + C::BM - 1) / C::BM, tn = (n + C::BN - 1) / C::BN, tiles = tm * tn;
     const int64_t slots = (int64_t)device_cus() * mx_occupancy<C>();
     const int64_t whole = tiles / slots * slots, left = tiles - whole;
-    const int64_t pslots = (int64_t)device_cus() * piece_occupancy<P>();
-    const double prounds = (double)((left * P::PIECES + pslots - 1) / pslots) * 1.6 / P::PIECES;
+    const double prounds = (double)((left * P::PIECES + slots - 1) / slots) * 1.6 / P::PIECES;
     const bool pieces = left > 0 && prounds < 1.0;
     const double rounds = (double)(whole / slots) + (left == 0 ? 0.0 : pieces ? prounds : 1.0);
     MxPlan p;
@@ -108,9 +96,7 @@ MxPlan mx_plan(int64_t m, int64_t n) {
 
 template <class C>
 void launch_mx_cfg(const MxArgs &a, const MxPlan &p, hipStream_t s) {
-    if (p.main_wgs > 0) gemm_mx_kernel<C><<<(unsigned)p.main_wgs, C::NT, 0, s>>>(a);
-    if (p.piece_wgs > 0)
-        gemm_mx_piece_kernel<MxPieceCfg<C::BM, C::BN>><<<(unsigned)p.piece_wgs, C::NT, 0, s>>>(a, p.first_piece_tile);
+    gemm_mx_kernel<C><<<(unsigned)(p.main_wgs + p.piece_wgs), C::NT, 0, s>>>(a, p.main_wgs, p.first_piece_tile);
 }
 
 void launch_mx(const MxArgs &a, hipStream_t s) {
