@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 COLD_BYTES = 1 << 30         # weight copies rotated per step exceed this
 PROFILE_JSON = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "hadamard_rotated_w4a4_amd", "csrc", f)
-                  for f in ("common.h", "k_gemm.h", "k_dense.h", "k_smallm.h", "k_rotq.h", "k_prep.h", "w4a4.hip")]
+                  for f in ("common.h", "k_route.h", "k_dense.h", "k_smallm.h", "k_rotq.h", "k_prep.h", "w4a4.hip")]
 
 
 def log(msg):
@@ -211,7 +211,8 @@ def run_moe(torch, ops, synth):
     x = torch.from_numpy(mo.x).to(dev)
     h = torch.from_numpy(mo.h).to(dev)
     counts = np.bincount(mo.ids.reshape(-1), minlength=E)
-    ws = torch.empty(ops.gemm_id_workspace_bytes(E, T, top_k), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(ops.gemm_id_workspace_bytes(E, T, top_k, dm), ops.gemm_id_workspace_bytes(E, T, top_k, dff)),
+                     dtype=torch.uint8, device=dev)
     yg = torch.empty((T, top_k, dff), dtype=torch.float32, device=dev)
     yu = torch.empty_like(yg)
     yd = torch.empty((T, top_k, dm), dtype=torch.float32, device=dev)

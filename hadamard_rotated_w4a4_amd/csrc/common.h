@@ -9,33 +9,23 @@ namespace w4a4 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int QK = 32;               // Q4_0 block length along K
 constexpr int TILE_N = 32;           // columns per packed weight tile (one MFMA N)
-constexpr int TILE_CODE_BYTES = 512; // packed codes of one (tile, block): 32 cols x 16 B
-constexpr int TILE_SCALE_HALFS = 32; // fp16 scales of one (tile, block)
 
-// Packed weight layout (written by the repack kernel, read by the GEMMs):
-//   codes  [Np/32][nb][64 lanes][8 B]; lane l = 32g + c holds bytes 8g..8g+7
-//          of column c's Q4_0 block, each byte XOR 0x88 (signed nibbles).
-//   scales [Np/32][nb][32] fp16, directly after the codes.
-// Np = n rounded up to 32; padded columns hold zero codes and zero scales.
-__host__ __device__ inline int64_t padded_n(int64_t n) { return (n + TILE_N - 1) / TILE_N * TILE_N; }
-__host__ __device__ inline int64_t packed_code_bytes(int64_t n, int64_t k) {
-    return padded_n(n) / TILE_N * (k / QK) * TILE_CODE_BYTES;
-}
-// Matrix-core operand section (read by the m > 16 GEMMs), after the codes
-// and scales above, 256-byte aligned: [Np/32][nbp][1 KB] with nbp = nb rounded
-// up to MX_BLOCK_PAD.  One 1 KB record per (32-column tile, block), laid out
-// as the MFMA's lanes want it.  Lane l = 32 g + c stands for column c and K
-// half g; it carries codes 16 g .. 16 g + 15 of the column's block as FP6
-// E2M3 (code t at bits 6 (t - 16 g) of a 96-bit value; the lane's other 96
-// operand bits are zero), so the two K halves of one 32x32x64 MFMA together
-// hold the 32 codes once:
+// Packed weight layout (written by the repack kernels, read by the GEMMs).
+// Np = n rounded up to 32; padding columns hold zero codes and zero scales.
+// Two sections hold the same weights losslessly, one per reader.
+//
+// Matrix-core section (the m > 16 kernels), at offset 0: [Np/32][nbp][1 KB]
+// with nbp = nb rounded up to MX_BLOCK_PAD.  One 1 KB record per (32-column
+// tile, block), laid out as the MFMA's lanes want it.  Lane l = 32 g + c
+// stands for column c and K half g; it carries codes 16 g .. 16 g + 15 of the
+// column's block (each q - 8) as FP6 E2M3 (code t at bits 6 (t - 16 g) of a
+// 96-bit value; the lane's other 96 operand bits are zero), so the two K
+// halves of one 32x32x64 MFMA together hold the 32 codes once:
 //   bytes [0, 512)     dwords 0..1 of lane l at 8 l;
 //   bytes [512, 768)   dword 2 of lane l at 512 + 4 l (both planes are read
 //                      conflict-free by a wave);
@@ -44,15 +34,13 @@ __host__ __device__ inline int64_t packed_code_bytes(int64_t n, int64_t k) {
 //   bytes [896, 1024)  zero.
 // The activation operand built by the GEMM's pre-pass has the same record
 // shape per (32-row tile, block), with a bf16 triple per row at 768.
+__host__ __device__ inline int64_t padded_n(int64_t n) { return (n + TILE_N - 1) / TILE_N * TILE_N; }
 constexpr int MX_REC = 1024;            // bytes per (tile, block) record
 constexpr int MX_CODE_BYTES = 768;      // fp6 codes of 32 rows / columns
 constexpr int MX_BLOCK_PAD = 8;         // records per tile are padded to a multiple of this
 __host__ __device__ inline int64_t mx_blocks(int64_t k) { return (k / QK + MX_BLOCK_PAD - 1) / MX_BLOCK_PAD * MX_BLOCK_PAD; }
-__host__ __device__ inline int64_t mx_section_offset(int64_t n, int64_t k) {
-    return (padded_n(n) / TILE_N * (k / QK) * (TILE_CODE_BYTES + 2 * TILE_SCALE_HALFS) + 255) / 256 * 256;
-}
-// Streaming section (read by the m <= 16 GEMM), 256-byte aligned after the
-// matrix-core section: [Np/32][nq][2304 B] with nq = ceil(nb / 4), one record
+// Streaming section (the m <= 16 kernel), directly after the matrix-core
+// section (a multiple of 1 KB): [Np/32][nq][2304 B] with nq = ceil(nb / 4), one record
 // per (32-column tile, 4 consecutive blocks).  Per column and block the 32
 // signed codes (q ^ 8) form four "K8 words", one per K-group g of 8 codes:
 // byte i of word g holds code 8 g + i in its low nibble and code 8 g + 4 + i
@@ -70,7 +58,7 @@ constexpr int SQ_REC = 2304;            // bytes per (tile, 4 blocks) record
 constexpr int SQ_SCALE_OFF = 2048;
 __host__ __device__ inline int64_t sq_quads(int64_t k) { return (k / QK + SQ_BLOCKS - 1) / SQ_BLOCKS; }
 __host__ __device__ inline int64_t sq_section_offset(int64_t n, int64_t k) {
-    return (mx_section_offset(n, k) + padded_n(n) / TILE_N * mx_blocks(k) * MX_REC + 255) / 256 * 256;
+    return padded_n(n) / TILE_N * mx_blocks(k) * MX_REC;
 }
 __host__ __device__ inline int64_t packed_total_bytes(int64_t n, int64_t k) {
     return sq_section_offset(n, k) + padded_n(n) / TILE_N * sq_quads(k) * SQ_REC;
@@ -107,71 +95,11 @@ __host__ __device__ inline void put_mx_lane(uint8_t *rec, int lane, const uint32
     reinterpret_cast<uint32_t *>(rec + 512)[lane] = w[2];
 }
 
-// Eight packed bytes (16 signed nibbles) -> sixteen int8 lanes of an MFMA
-// operand, each holding 16 * nibble: masking the high nibble keeps it in
-// place (two's complement survives), shifting the low nibble up by 4 does the
-// same for it.  Products therefore carry a factor 256, which the epilogue
-// folds into the weight scale.  A and B go through the same permutation, so
-// the dot over the 32 K positions is unchanged.
-__device__ __forceinline__ v4i unpack_nibbles_x16(uint32_t lo_word, uint32_t hi_word) {
-    v4i r;
-    r.x = (int)((lo_word << 4) & 0xF0F0F0F0u);
-    r.y = (int)((hi_word << 4) & 0xF0F0F0F0u);
-    r.z = (int)(lo_word & 0xF0F0F0F0u);
-    r.w = (int)(hi_word & 0xF0F0F0F0u);
-    return r;
-}
-
-__device__ __forceinline__ v16i mfma_i8_32x32x32(v4i a, v4i b) {
-    v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zero, 0, 0, 0);
-}
-
-__device__ __forceinline__ v16f mfma_bf16_32x32x16(uint4 a, uint4 b) {
-    v16f zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                  __builtin_bit_cast(bf16x8, b), zero, 0, 0, 0);
-}
-
 // 32x32x8 bf16 MFMA: 4 bf16 per lane, lane groups l/32 hold K 0..3 and 4..7.
 __device__ __forceinline__ v16f mfma_bf16_32x32x8(uint2 a, uint2 b) {
     v16f zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(v4s, a), __builtin_bit_cast(v4s, b),
                                                    zero, 0, 0, 0);
-}
-
-// 32x32x2 fp32 MFMA: one fp32 per lane, lane groups l/32 hold K 0 and 1.
-__device__ __forceinline__ v16f mfma_f32_32x32x2(float a, float b) {
-    v16f zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, zero, 0, 0, 0);
-}
-
-// Exact splits of fp32 scales into bf16 parts, so that a bf16 MFMA can form
-// the outer product s[m] * d[n] of a block's scales with exact partial
-// products (8 x 8 significant bits) summed in fp32.
-//   s (24 significant bits) = s1 + s2 + s3, each part 8 bits: masking the low
-//   16 bits of an fp32 keeps its top 8 significant bits; the remainder of that
-//   subtraction is exact.
-//   d (an fp16 scale: 11 significant bits) = d1 + d2.
-// Operand K slots 0..7: A = {s1, s1, s2, s2, s3, s3, 0, 0}, B = {d1, d2, d1,
-// d2, d1, d2, 0, 0}; their dot is (s1 + s2 + s3)(d1 + d2).  As a 32x32x8 MFMA
-// operand, lane group 0 takes slots 0..3 (the low 8 bytes) and group 1 slots
-// 4..7 (the high 8 bytes).
-__device__ __forceinline__ uint4 split_scale_a(float s) {
-    const uint32_t h1 = __float_as_uint(s) & 0xFFFF0000u;
-    const float r1 = __fsub_rn(s, __uint_as_float(h1));
-    const uint32_t h2 = __float_as_uint(r1) & 0xFFFF0000u;
-    const float r2 = __fsub_rn(r1, __uint_as_float(h2));
-    const uint32_t h3 = __float_as_uint(r2) & 0xFFFF0000u;
-    return make_uint4(h1 | (h1 >> 16), h2 | (h2 >> 16), h3 | (h3 >> 16), 0u);
-}
-
-__device__ __forceinline__ uint4 split_scale_b(float d) {
-    const uint32_t h1 = __float_as_uint(d) & 0xFFFF0000u;
-    const float r1 = __fsub_rn(d, __uint_as_float(h1));
-    const uint32_t h2 = __float_as_uint(r1) & 0xFFFF0000u;
-    const uint32_t pair = h2 | (h1 >> 16);
-    return make_uint4(pair, pair, pair, 0u);
 }
 
 // Materialise a value in a register so that the compiler cannot fuse the

@@ -30,7 +30,7 @@
 #pragma once
 
 #include "common.h"
-#include "k_gemm.h"
+#include "k_route.h"
 
 namespace w4a4 {
 
@@ -44,18 +44,17 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 //               both lane groups of the scale-product MFMA.
 // One thread per (row, padded block); padding rows and blocks are zero.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void act_operand_kernel(const uint8_t *__restrict__ codes,
-                                                          const float *__restrict__ scales, int64_t m,
-                                                          int64_t k, uint8_t *__restrict__ ws) {
-    const int64_t nb = k / QK, nbp = mx_blocks(k);
-    const int64_t rows = (m + 31) / 32 * 32;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= rows * nbp) return;
-    // consecutive threads: consecutive rows of one block (coalesced record writes)
-    const int64_t b = gid / rows, row = gid % rows;
+// Row r (of 32) of record `rec`: block b of activation row `src` (codes and
+// scales as the rotate-quantiser writes them), or zeros for src < 0 and for
+// padding blocks.
+__device__ __forceinline__ void write_act_record(const uint8_t *__restrict__ codes,
+                                                 const float *__restrict__ scales, int64_t src, int64_t k,
+                                                 int64_t b, uint8_t *rec, int r) {
+    const int64_t nb = k / QK;
     uint32_t lo[3] = {0, 0, 0}, hi[3] = {0, 0, 0};
     uint2 sop = make_uint2(0, 0);
-    if (row < m && b < nb) {
+    if (src >= 0 && b < nb) {
+        const int64_t row = src;
         const uint4 q = *reinterpret_cast<const uint4 *>(codes + row * (k / 2) + b * 16);
         const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
         uint32_t f0[16], f1[16];
@@ -76,11 +75,69 @@ __global__ __launch_bounds__(256) void act_operand_kernel(const uint8_t *__restr
         const uint32_t h3 = __float_as_uint(r2) & 0xFFFF0000u;
         sop = make_uint2((h1 >> 16) | h2, h3 >> 16);
     }
-    uint8_t *rec = ws + ((row / 32) * nbp + b) * MX_REC;
-    const int r = (int)(row % 32);
     put_mx_lane(rec, r, lo);
     put_mx_lane(rec, 32 + r, hi);
     reinterpret_cast<uint2 *>(rec + MX_CODE_BYTES)[r] = sop;
+}
+
+__global__ __launch_bounds__(256) void act_operand_kernel(const uint8_t *__restrict__ codes,
+                                                          const float *__restrict__ scales, int64_t m,
+                                                          int64_t k, uint8_t *__restrict__ ws) {
+    const int64_t nbp = mx_blocks(k);
+    const int64_t rows = (m + 31) / 32 * 32;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= rows * nbp) return;
+    // consecutive threads: consecutive rows of one block (coalesced record writes)
+    const int64_t b = gid / rows, row = gid % rows;
+    write_act_record(codes, scales, row < m ? row : -1, k, b, ws + ((row / 32) * nbp + b) * MX_REC,
+                     (int)(row % 32));
+}
+
+// Expert routing shared by the grouped pre-pass and the grouped GEMM: rows
+// are grouped by expert (perm), each expert's rows padded to whole tiles of
+// GROUP_ROWS; tile_prefix[e] counts the tiles of experts before e.
+constexpr int GROUP_ROWS = 64;
+struct Routing {
+    const int32_t *perm;         // [n_rows] (token, slot) row ids, grouped by expert
+    const int32_t *offsets;      // [E + 1] start of each expert's rows in perm
+    const int32_t *tile_prefix;  // [E + 1]
+    int n_expert;
+};
+// Expert of row tile t < tile_prefix[E]: the largest e with tile_prefix[e] <= t.
+__device__ __forceinline__ int expert_of_tile(const Routing &g, int64_t t) {
+    int lo = 0, hi = g.n_expert;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (g.tile_prefix[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// Grouped pre-pass: operand records of the routed rows, expert by expert, in
+// tiles of GROUP_ROWS rows.  Workgroup (tile t, blocks 4 y .. 4 y + 3), one
+// thread per (row, block): the tile's expert is found once per workgroup (a
+// wave-uniform search).  Activation row of routed row i = t * top_k + j: t
+// (one row per token) or i (one row per slot).  Rows past an expert's count
+// are zero; tiles past the last expert's are not written (nor read).
+constexpr int GROUPED_PREP_BLOCKS = 4;
+__global__ __launch_bounds__(GROUP_ROWS * GROUPED_PREP_BLOCKS) void act_operand_grouped_kernel(
+    const uint8_t *__restrict__ codes, const float *__restrict__ scales, int64_t k, Routing g, int top_k,
+    int per_slot, uint8_t *__restrict__ ws) {
+    const int64_t nbp = mx_blocks(k);
+    const int64_t t = blockIdx.x;
+    if (t >= g.tile_prefix[g.n_expert]) return;  // uniform
+    const int e = expert_of_tile(g, t);
+    const int r = threadIdx.x % GROUP_ROWS;
+    const int64_t b = (int64_t)blockIdx.y * GROUPED_PREP_BLOCKS + threadIdx.x / GROUP_ROWS;
+    if (b >= nbp) return;
+    const int64_t local = (t - g.tile_prefix[e]) * GROUP_ROWS + r;
+    int64_t src = -1;
+    if (local < g.offsets[e + 1] - g.offsets[e]) {
+        const int64_t i = g.perm[g.offsets[e] + local];
+        src = per_slot ? i : i / top_k;
+    }
+    const int64_t p = t * GROUP_ROWS + r;  // row of the padded order
+    write_act_record(codes, scales, src, k, b, ws + ((p / 32) * nbp + b) * MX_REC, (int)(p % 32));
 }
 
 // ---------------------------------------------------------------------------
@@ -88,9 +145,13 @@ __global__ __launch_bounds__(256) void act_operand_kernel(const uint8_t *__restr
 // ---------------------------------------------------------------------------
 struct MxArgs {
     const uint8_t *act;     // activation records [rtiles][nbp][1 KB]
-    const uint8_t *wrec;    // weight records [tiles_n][nbp][1 KB]
+    const uint8_t *wrec;    // weight records [tiles_n][nbp][1 KB] (grouped: expert 0's)
     float *y;
     int64_t ldy, m, n, k;
+    // grouped (expert) products only: routing, and the bytes between two
+    // experts' packed weights
+    Routing g;
+    int64_t expert_bytes;
 };
 
 template <int BKB_, int NS_, int TM_, int TN_>
@@ -135,8 +196,10 @@ __device__ __forceinline__ void mx_tile_of(int64_t id, int64_t nx, int64_t ny, i
     by = in / width;
 }
 
-// One whole tile (workgroup index id) of the main kernel.
-template <class C>
+// One whole tile (workgroup index id) of the main kernel.  GROUPED: the row
+// tiles are the experts' routed rows (GROUP_ROWS per tile, see the grouped
+// pre-pass), each tile multiplies its expert's weights and scatters its rows.
+template <class C, bool GROUPED = false>
 __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *smem) {
     constexpr int BKB = C::BKB, NS = C::NS, TM = C::TM, TN = C::TN, RT = C::RT;
 
@@ -148,7 +211,29 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
     const int64_t rtiles = (a.m + 31) / 32, ctiles = padded_n(a.n) / TILE_N;
 
     int64_t bx, by;
-    mx_tile_of(id, (a.n + C::BN - 1) / C::BN, (a.m + C::BM - 1) / C::BM, bx, by);
+    const uint8_t *wrec = a.wrec;
+    int64_t row_lo = 0, row_cnt = a.m;  // rows of this tile's matrix (grouped: of its expert)
+    const int32_t *perm = nullptr;
+    if constexpr (!GROUPED) {
+        mx_tile_of(id, (a.n + C::BN - 1) / C::BN, (a.m + C::BM - 1) / C::BM, bx, by);
+    } else {
+        // The routed tiles, expert by expert, as (row tile, column tile)
+        // items; each XCD takes a contiguous eighth of the item list (ids x,
+        // x + 8, ... run on XCD x), so an expert's row tiles share one L2 and
+        // read its weights from HBM about once.
+        static_assert(C::BM == GROUP_ROWS, "grouped tiles are the routing's tiles");
+        const int64_t nx = (a.n + C::BN - 1) / C::BN;
+        const int64_t items = (int64_t)a.g.tile_prefix[a.g.n_expert] * nx, per_xcd = (items + 7) / 8;
+        const int64_t j = id / 8, item = (id % 8) * per_xcd + j;
+        if (j >= per_xcd || item >= items) return;  // uniform: no item for this workgroup
+        by = item / nx;
+        bx = item % nx;
+        const int e = expert_of_tile(a.g, by);
+        wrec += e * a.expert_bytes;
+        row_lo = (by - a.g.tile_prefix[e]) * GROUP_ROWS;
+        row_cnt = a.g.offsets[e + 1] - a.g.offsets[e];
+        perm = a.g.perm + a.g.offsets[e];
+    }
     const int64_t rt0 = by * RT, ct0 = bx * C::CT;
 
     // ---- this wave's loads: DMA_PER_WAVE records of 1 KB per stage ----
@@ -162,7 +247,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
     for (int d = 0; d < C::DMA_PER_WAVE; d++) {
         const int i = wave * C::DMA_PER_WAVE + d, t = i / BKB, bb = i % BKB;
         const uint8_t *base = t < RT ? a.act + min(rt0 + t, rtiles - 1) * nbp * MX_REC
-                                     : a.wrec + min(ct0 + t - RT, ctiles - 1) * nbp * MX_REC;
+                                     : wrec + min(ct0 + t - RT, ctiles - 1) * nbp * MX_REC;
         src[d] = base + bb * MX_REC + lane * 16;
         dst[d] = (uint32_t)((t * BKB + bb) * MX_REC);
     }
@@ -277,7 +362,8 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
     // ---- store ----
 #pragma unroll
     for (int i = 0; i < TM; i++) {
-        const int64_t rbase = (rt0 + wm * TM + i) * 32;
+        // row of this tile's matrix; grouped: of the expert's routed rows
+        const int64_t rbase = GROUPED ? row_lo + (wm * TM + i) * 32 : (rt0 + wm * TM + i) * 32;
 #pragma unroll
         for (int j = 0; j < TN; j++) {
             const int64_t col = (ct0 + wn * TN + j) * 32 + c;
@@ -285,7 +371,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int64_t r = rbase + mfma32_row(v, lane);
-                if (r < a.m) a.y[r * a.ldy + col] = acc[i][j][v];
+                if (r < row_cnt) a.y[(GROUPED ? (int64_t)perm[r] : r) * a.ldy + col] = acc[i][j][v];
             }
         }
     }
@@ -417,6 +503,14 @@ __global__ __launch_bounds__(C::NT) void gemm_mx_kernel(MxArgs a, int64_t main_w
     __shared__ __attribute__((aligned(1024))) uint8_t smem[MAIN_LDS > PIECE_LDS ? MAIN_LDS : PIECE_LDS];
     if ((int64_t)blockIdx.x < main_wgs) mx_tile<C>(a, blockIdx.x, smem);  // uniform per workgroup
     else mx_piece<P>(a, first_piece_tile, blockIdx.x - main_wgs, smem);
+}
+
+// Grouped (MUL_MAT_ID) product: one whole tile per workgroup; a.m is the
+// routing's bound on padded rows (tiles past the last expert's exit).
+template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_mx_grouped_kernel(MxArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE_BYTES];
+    mx_tile<C, true>(a, blockIdx.x, smem);
 }
 
 }  // namespace w4a4

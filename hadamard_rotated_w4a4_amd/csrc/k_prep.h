@@ -60,39 +60,6 @@ __global__ __launch_bounds__(256) void quantize_q4_0_h32_kernel(const float *__r
     }
 }
 
-// One thread per (tile, block, lane): 8 code bytes (XOR 0x88) and, for lanes
-// 0..31, the column's fp16 scale.
-__global__ __launch_bounds__(256) void repack_kernel(const uint8_t *__restrict__ q4, int64_t n,
-                                                     int64_t k, uint8_t *__restrict__ packed) {
-    const int64_t nb = k / QK;
-    const int64_t tiles = padded_n(n) / TILE_N;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= tiles * nb * 64) return;
-    const int lane = (int)(gid & 63);
-    const int64_t tb = gid >> 6;  // tile * nb + b
-    const int64_t tile = tb / nb, b = tb % nb;
-    const int c = lane & 31, g = lane >> 5;
-    const int64_t col = tile * TILE_N + c;
-
-    uint32_t w0 = 0, w1 = 0;
-    uint16_t dbits = 0;
-    if (col < n) {
-        const uint8_t *blk = q4 + (col * nb + b) * 18;
-        const uint8_t *qs = blk + 2 + 8 * g;
-        w0 = (uint32_t)qs[0] | ((uint32_t)qs[1] << 8) | ((uint32_t)qs[2] << 16) | ((uint32_t)qs[3] << 24);
-        w1 = (uint32_t)qs[4] | ((uint32_t)qs[5] << 8) | ((uint32_t)qs[6] << 16) | ((uint32_t)qs[7] << 24);
-        w0 ^= 0x88888888u;
-        w1 ^= 0x88888888u;
-        dbits = (uint16_t)(blk[0] | (blk[1] << 8));
-    }
-    uint2 *codes = reinterpret_cast<uint2 *>(packed);
-    codes[tb * 64 + lane] = make_uint2(w0, w1);
-    if (g == 0) {
-        uint16_t *scales = reinterpret_cast<uint16_t *>(packed + packed_code_bytes(n, k));
-        scales[tb * TILE_SCALE_HALFS + c] = dbits;
-    }
-}
-
 // Matrix-core operand records (see common.h), one thread per (tile, padded
 // block, column).  Padding columns and blocks get zero codes and zero scales.
 __global__ __launch_bounds__(256) void repack_mx_kernel(const uint8_t *__restrict__ q4, int64_t n,
@@ -122,7 +89,7 @@ __global__ __launch_bounds__(256) void repack_mx_kernel(const uint8_t *__restric
         const float r1 = __fsub_rn(d, __uint_as_float(h1));  // exact: at most 3 significant bits remain
         sw = (h1 >> 16) | (__float_as_uint(r1) & 0xFFFF0000u);
     }
-    uint8_t *rec = packed + mx_section_offset(n, k) + tb * MX_REC;
+    uint8_t *rec = packed + tb * MX_REC;
     put_mx_lane(rec, c, lo);
     put_mx_lane(rec, 32 + c, hi);
     reinterpret_cast<uint32_t *>(rec + MX_CODE_BYTES)[c] = sw;

@@ -12,9 +12,9 @@
 
 #include "common.h"
 #include "k_dense.h"
-#include "k_gemm.h"
 #include "k_prep.h"
 #include "k_rotq.h"
+#include "k_route.h"
 #include "k_smallm.h"
 
 using namespace w4a4;
@@ -105,8 +105,6 @@ void launch_mx(const MxArgs &a, hipStream_t s) {
     else if (p1 <= p2) launch_mx_cfg<Mx128x64>(a, p1, s);
     else launch_mx_cfg<Mx64x128>(a, p2, s);
 }
-// Grouped expert tiles: 32 rows (experts are small), 4 waves across 256 columns.
-using GroupedCfg = TileCfg<1, 4, 1, 2, 4>;
 
 // Row bounds that keep every grid.y within the hardware's 65535.
 constexpr int64_t kMaxGridY = 65535;
@@ -170,11 +168,6 @@ w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int6
     if (n == 0 || k == 0) return W4A4_OK;
     if (!q4_0 || !packed) return W4A4_ERR_INVALID_VALUE;
     if (!aligned(packed, 16)) return W4A4_ERR_MISALIGNED;
-    const int64_t threads = padded_n(n) / TILE_N * (k / QK) * 64;
-    repack_kernel<<<blocks_for(threads, 256), 256, 0, as_stream(stream)>>>(
-        static_cast<const uint8_t *>(q4_0), n, k, static_cast<uint8_t *>(packed));
-    const w4a4_status st = hip_status("repack_kernel");
-    if (st != W4A4_OK) return st;
     const int64_t mx_threads = padded_n(n) / TILE_N * mx_blocks(k) * 32;
     repack_mx_kernel<<<blocks_for(mx_threads, 256), 256, 0, as_stream(stream)>>>(
         static_cast<const uint8_t *>(q4_0), n, k, static_cast<uint8_t *>(packed));
@@ -319,7 +312,7 @@ w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, 
     if (!aligned(packed_w, 16) || !aligned(act, 256)) return W4A4_ERR_MISALIGNED;
     MxArgs a{};
     a.act = static_cast<const uint8_t *>(act);
-    a.wrec = static_cast<const uint8_t *>(packed_w) + mx_section_offset(n, k);
+    a.wrec = static_cast<const uint8_t *>(packed_w);  // the matrix-core section
     a.y = y;
     a.ldy = ldy;
     a.m = m;
@@ -329,10 +322,19 @@ w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, 
     return hip_status("gemm_mx_kernel");
 }
 
-size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t top_k) {
-    if (n_expert < 0 || n_tokens < 0 || top_k < 0) return 0;
-    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
-    return (size_t)(2 * up((n_expert + 1) * 4) + up(n_tokens * top_k * 4));
+namespace {
+// Routing bound: every expert adds at most one partial tile to the full ones.
+int64_t grouped_row_tiles(int64_t n_expert, int64_t n_rows) {
+    return (n_rows + GROUP_ROWS - 1) / GROUP_ROWS + n_expert;
+}
+size_t up256(int64_t b) { return (size_t)((b + 255) / 256 * 256); }
+}  // namespace
+
+size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t top_k, int64_t k) {
+    if (n_expert < 0 || n_tokens < 0 || top_k < 0 || k < 0 || k % QK) return 0;
+    const int64_t n_rows = n_tokens * top_k;
+    const int64_t act = grouped_row_tiles(n_expert, n_rows) * (GROUP_ROWS / 32) * mx_blocks(k) * MX_REC;
+    return 2 * up256((n_expert + 1) * 4) + up256(n_rows * 4) + (size_t)act;
 }
 
 w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *codes, const float *scales,
@@ -344,8 +346,11 @@ w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *
     if (n_tokens == 0 || top_k == 0 || n == 0) return W4A4_OK;
     if (n_expert < 1 || n_expert > ROUTE_MAX_EXPERTS) return W4A4_ERR_INVALID_VALUE;
     if (act_rows_per_token != 1 && act_rows_per_token != top_k) return W4A4_ERR_INVALID_VALUE;
-    if (n_tokens * top_k > kMaxGridY * GroupedCfg::BM - n_expert * GroupedCfg::BM)
-        return W4A4_ERR_INVALID_VALUE;
+    const int64_t n_rows = n_tokens * top_k;
+    using C = Mx64x128;
+    const int64_t row_tiles = grouped_row_tiles(n_expert, n_rows);
+    const int64_t col_tiles = (n + C::BN - 1) / C::BN;
+    if (n_rows > INT32_MAX || row_tiles * col_tiles + 8 > INT32_MAX) return W4A4_ERR_INVALID_VALUE;
     if (!ids || !workspace) return W4A4_ERR_INVALID_VALUE;
     if (k > 0) {
         const w4a4_status st = check_gemm_common(packed_w, codes, scales, y, n, k);
@@ -354,47 +359,47 @@ w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *
         return W4A4_ERR_INVALID_VALUE;
     }
     if (!aligned(ids, 4) || !aligned(workspace, 256) || !aligned(y, 4)) return W4A4_ERR_MISALIGNED;
-    if (workspace_bytes < w4a4_gemm_id_workspace_bytes(n_expert, n_tokens, top_k))
+    if (workspace_bytes < w4a4_gemm_id_workspace_bytes(n_expert, n_tokens, top_k, k))
         return W4A4_ERR_WORKSPACE_TOO_SMALL;
 
     hipStream_t s = as_stream(stream);
-    const int64_t n_rows = n_tokens * top_k;
     if (k == 0) {  // empty sums: every row is zero
         zero_rows_kernel<<<blocks_for(n_rows * n, 256), 256, 0, s>>>(y, n_rows, n, n);
         return hip_status("zero_rows_kernel");
     }
-    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     int32_t *offsets = reinterpret_cast<int32_t *>(ws);
-    int32_t *tile_prefix = reinterpret_cast<int32_t *>(ws + up((n_expert + 1) * 4));
-    int32_t *perm = reinterpret_cast<int32_t *>(ws + 2 * up((n_expert + 1) * 4));
+    int32_t *tile_prefix = reinterpret_cast<int32_t *>(ws + up256((n_expert + 1) * 4));
+    int32_t *perm = reinterpret_cast<int32_t *>(ws + 2 * up256((n_expert + 1) * 4));
+    uint8_t *act = ws + 2 * up256((n_expert + 1) * 4) + up256(n_rows * 4);
 
-    route_kernel<<<1, ROUTE_THREADS, 0, s>>>(ids, (int)n_rows, (int)n_expert, GroupedCfg::BM, offsets,
-                                             tile_prefix, perm, y, n);
+    route_kernel<<<1, ROUTE_THREADS, 0, s>>>(ids, (int)n_rows, (int)n_expert, GROUP_ROWS, offsets, tile_prefix,
+                                             perm, y, n);
     w4a4_status st = hip_status("route_kernel");
     if (st != W4A4_OK) return st;
 
-    GemmArgs a{};
-    a.codes = codes;
-    a.scales = scales;
-    a.packed = static_cast<const uint8_t *>(packed_w);
-    a.expert_bytes = packed_total_bytes(n, k);
+    const Routing g{perm, offsets, tile_prefix, (int)n_expert};
+    const int64_t rows = row_tiles * GROUP_ROWS;
+    const dim3 pgrid((unsigned)row_tiles,
+                     (unsigned)((mx_blocks(k) + GROUPED_PREP_BLOCKS - 1) / GROUPED_PREP_BLOCKS));
+    act_operand_grouped_kernel<<<pgrid, GROUP_ROWS * GROUPED_PREP_BLOCKS, 0, s>>>(
+        codes, scales, k, g, (int)top_k, act_rows_per_token != 1 ? 1 : 0, act);
+    st = hip_status("act_operand_grouped_kernel");
+    if (st != W4A4_OK) return st;
+
+    MxArgs a{};
+    a.act = act;
+    a.wrec = static_cast<const uint8_t *>(packed_w);  // the matrix-core section
     a.y = y;
     a.ldy = n;
-    a.m = n_rows;
+    a.m = rows;
     a.n = n;
     a.k = k;
-    a.perm = perm;
-    a.offsets = offsets;
-    a.tile_prefix = tile_prefix;
-    a.n_expert = (int)n_expert;
-    a.top_k = (int)top_k;
-    a.act_rows_per_token = (int)act_rows_per_token;
-    // every expert adds at most one partial tile to the full ones
-    const int64_t max_tiles = blocks_for(n_rows, GroupedCfg::BM) + n_expert;
-    const dim3 grid((unsigned)blocks_for(n, GroupedCfg::BN), (unsigned)max_tiles);
-    gemm_tiled_kernel<GroupedCfg, true><<<grid, GroupedCfg::NT, 0, s>>>(a);
-    return hip_status("gemm_tiled_kernel<grouped>");
+    a.g = g;
+    a.expert_bytes = packed_total_bytes(n, k);
+    // a bound on the items (row tiles x column tiles), rounded up to whole XCD rows
+    gemm_mx_grouped_kernel<C><<<(unsigned)((row_tiles * col_tiles + 7) / 8 * 8), C::NT, 0, s>>>(a);
+    return hip_status("gemm_mx_grouped_kernel");
 }
 
 }  // extern "C"
