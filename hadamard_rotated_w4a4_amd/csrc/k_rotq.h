@@ -8,12 +8,14 @@
 // weights offline, so the product is unchanged in exact arithmetic.
 //
 // Mapping: eight lanes per 32-element block, four consecutive elements per
-// lane (one 8-byte fp16 load; a wave reads 8 rows x 64 contiguous bytes).  The
-// butterflies of distance 1 and 2 are in-lane, those of distance 4, 8 and 16
-// exchange values with lane L ^ 1, L ^ 2, L ^ 4 of the block's eight; the
-// absmax is a three-step exchange too.  A workgroup of 256 threads covers 32
-// rows of one block, so it can also write that block's matrix-core operand
-// record (see common.h) in one coalesced kilobyte.
+// lane (one 8-byte fp16 load).  The butterflies of distance 1 and 2 are
+// in-lane, those of distance 4, 8 and 16 exchange values with lane L ^ 1,
+// L ^ 2, L ^ 4 of the block's eight; the absmax is a three-step exchange too.
+// A workgroup of 512 threads covers 32 rows of two neighbouring blocks: each
+// row's two blocks are one 128-byte line of fp16 input, read by one
+// workgroup (with one block per workgroup, neighbouring workgroups land on
+// different XCDs and both fetch the line), and each half writes its block's
+// matrix-core operand record (see common.h) in one coalesced kilobyte.
 //
 // The fp32 operation sequence is fixed and the same as a serial evaluation:
 // in stage h = 1, 2, 4, 8, 16 each pair (i, i + h) with i & h == 0 becomes
@@ -59,20 +61,23 @@ __device__ __forceinline__ void load4(const __half *p, bool vec, float v[4]) {
     }
 }
 
-// One workgroup = 32 rows (row tile blockIdx.y) x one 32-element block
-// (blockIdx.x); thread t: row r = t / 8 of the tile, lane L = t % 8 of the
-// block, elements 4L .. 4L + 3.  `vec`: every 4-element group is aligned for
-// one vector load (checked on the host).  With `act` set, also writes the
-// block's operand record for the matrix-core GEMM (blockIdx.x runs over the
-// padded block count then; padding rows and blocks get zero records).
+// One workgroup = 32 rows (row tile blockIdx.y) x two 32-element blocks
+// (2 blockIdx.x and 2 blockIdx.x + 1); thread t: block half t / 256, row
+// r = (t / 8) % 32 of the tile, lane L = t % 8 of the block, elements
+// 4L .. 4L + 3.  `vec`: every 4-element group is aligned for one vector load
+// (checked on the host).  With `act` set, also writes the block's operand
+// record for the matrix-core GEMM (the blocks then run over the padded block
+// count, an even number; padding rows and blocks get zero records).
+constexpr int RQ_BLOCKS = 2;  // blocks per workgroup
 template <typename T>
-__global__ __launch_bounds__(256) void rotate_quantize_kernel(const T *__restrict__ x, int64_t m, int64_t k,
-                                                              int64_t ldx, bool vec, uint8_t *__restrict__ codes,
-                                                              float *__restrict__ scales,
-                                                              uint8_t *__restrict__ act) {
+__global__ __launch_bounds__(256 * RQ_BLOCKS) void rotate_quantize_kernel(const T *__restrict__ x, int64_t m,
+                                                                          int64_t k, int64_t ldx, bool vec,
+                                                                          uint8_t *__restrict__ codes,
+                                                                          float *__restrict__ scales,
+                                                                          uint8_t *__restrict__ act) {
     const int64_t nb = k / QK;
-    const int tid = threadIdx.x, L = tid & 7, r = tid >> 3;
-    const int64_t b = blockIdx.x, row = (int64_t)blockIdx.y * 32 + r;
+    const int tid = threadIdx.x, L = tid & 7, r = (tid >> 3) & 31;
+    const int64_t b = (int64_t)blockIdx.x * RQ_BLOCKS + (tid >> 8), row = (int64_t)blockIdx.y * 32 + r;
     const bool live = row < m && b < nb;  // uniform per 8-lane group
 
     float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const T *__restric
         if (L == 0) scales[row * nb + b] = s;
     }
 
-    if (act) {
+    if (act && b < mx_blocks(k)) {
         // operand record of (row tile, block): lane (g, r) holds codes 16 g ..
         // 16 g + 15 as fp6 fields; this thread's four codes are 24 bits at
         // bit 24 (L % 4) of group g = L / 4's 96-bit value

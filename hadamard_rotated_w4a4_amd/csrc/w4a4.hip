@@ -196,14 +196,15 @@ w4a4_status rotate_quantize(const void *x, w4a4_dtype dt, int64_t m, int64_t k, 
     const size_t esz = dt == W4A4_DTYPE_F32 ? 4 : 2;
     // every 4-element group aligned for one vector load (8 bytes fp16, 16 bytes fp32)
     const bool vec = aligned(x, 4 * esz) && (ldx % 4) == 0;
-    const dim3 grid((unsigned)(act ? mx_blocks(k) : k / QK), (unsigned)((m + 31) / 32));
+    const int64_t blocks = act ? mx_blocks(k) : k / QK;
+    const dim3 grid((unsigned)((blocks + RQ_BLOCKS - 1) / RQ_BLOCKS), (unsigned)((m + 31) / 32));
     hipStream_t s = as_stream(stream);
     uint8_t *a = static_cast<uint8_t *>(act);
     if (dt == W4A4_DTYPE_F32)
-        rotate_quantize_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(x), m, k, ldx, vec, codes,
+        rotate_quantize_kernel<float><<<grid, 256 * RQ_BLOCKS, 0, s>>>(static_cast<const float *>(x), m, k, ldx, vec, codes,
                                                           scales, a);
     else
-        rotate_quantize_kernel<__half><<<grid, 256, 0, s>>>(static_cast<const __half *>(x), m, k, ldx, vec, codes,
+        rotate_quantize_kernel<__half><<<grid, 256 * RQ_BLOCKS, 0, s>>>(static_cast<const __half *>(x), m, k, ldx, vec, codes,
                                                            scales, a);
     return hip_status("rotate_quantize_kernel");
 }
