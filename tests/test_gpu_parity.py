@@ -323,6 +323,29 @@ def test_small_m_ragged_rows(ops, m):
     assert_rows_close(y, oracle.gemm(oracle.prepare_weights(w), *oracle.rotate_quantize_act(x), k))
 
 
+def test_small_m_split_k_shared_workspace(ops):
+    """K-split small-m products on one workspace sized for the largest shape,
+    shapes interleaved and repeated: every call equals a call on a fresh
+    workspace bit for bit (the partial sums are added in a fixed order)."""
+    import torch
+    shapes = [(16, 1024, 5120), (7, 160, 2048), (16, 96, 17408), (3, 1024, 5120)]  # (m, n, k), all split
+    need = max(ops.gemm_workspace_bytes(m, n, k) for m, n, k in shapes)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda:0")  # stale contents are ignored
+    probs = []
+    for i, (m, n, k) in enumerate(shapes):
+        w, x = _problem(m, n, k, 300 + i)
+        packed = ops.prepare_weights(dev(w))
+        c, s = ops.rotate_quantize_act(dev(x))
+        fresh = host(ops.gemm(packed, c, s, n, k))
+        assert_rows_close(fresh, oracle.gemm(oracle.prepare_weights(w), *oracle.rotate_quantize_act(x), k))
+        probs.append((packed, c, s, n, k, fresh))
+    for rep in range(2):
+        for packed, c, s, n, k, fresh in probs:
+            say(f"shared workspace rep {rep} m={c.shape[0]} n={n} k={k}")
+            y = host(ops.gemm(packed, c, s, n, k, workspace=ws))
+            assert np.array_equal(y, fresh)
+
+
 def test_last_microbatch_302_rows(ops):
     k, n = 6144, 5120  # the output projection
     w = synth.weights(n, k, synth.rng_for(0, 3, 3))
