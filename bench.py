@@ -211,8 +211,7 @@ def run_moe(torch, ops, synth):
     x = torch.from_numpy(mo.x).to(dev)
     h = torch.from_numpy(mo.h).to(dev)
     counts = np.bincount(mo.ids.reshape(-1), minlength=E)
-    ws = torch.empty(max(ops.gemm_id_workspace_bytes(E, T, top_k, dm), ops.gemm_id_workspace_bytes(E, T, top_k, dff)),
-                     dtype=torch.uint8, device=dev)
+    ws = torch.empty(ops.gemm_id_workspace_bytes(E, T, top_k), dtype=torch.uint8, device=dev)
     yg = torch.empty((T, top_k, dff), dtype=torch.float32, device=dev)
     yu = torch.empty_like(yg)
     yd = torch.empty((T, top_k, dm), dtype=torch.float32, device=dev)

@@ -46,7 +46,7 @@ def lib() -> ctypes.CDLL:
             "w4a4_gemm_prepare_act": ([P, P, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_prepared": ([P, P, P, I64, I64, I64, I64, P], ST),
             "w4a4_gemm": ([P, P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
-            "w4a4_gemm_id_workspace_bytes": ([I64, I64, I64, I64], SZ),
+            "w4a4_gemm_id_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_gemm_id": ([P, I64, P, P, I64, P, I64, I64, P, I64, I64, P, SZ, P], ST),
         }
         for name, (args, res) in sigs.items():
@@ -98,8 +98,8 @@ def act_operand_bytes(m: int, k: int) -> int:
     return int(lib().w4a4_act_operand_bytes(m, k))
 
 
-def gemm_id_workspace_bytes(n_expert: int, n_tokens: int, top_k: int, k: int) -> int:
-    return int(lib().w4a4_gemm_id_workspace_bytes(n_expert, n_tokens, top_k, k))
+def gemm_id_workspace_bytes(n_expert: int, n_tokens: int, top_k: int) -> int:
+    return int(lib().w4a4_gemm_id_workspace_bytes(n_expert, n_tokens, top_k))
 
 
 # --------------------------------------------------------------------------
@@ -217,7 +217,7 @@ def gemm_id(packed: torch.Tensor, n_expert: int, codes: torch.Tensor, scales: to
     n_tokens, top_k = ids.shape
     if y is None:
         y = torch.empty((n_tokens, top_k, n), dtype=torch.float32, device=ids.device)
-    need = gemm_id_workspace_bytes(n_expert, n_tokens, top_k, k)
+    need = gemm_id_workspace_bytes(n_expert, n_tokens, top_k)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ids.device)
     _check(lib().w4a4_gemm_id(_ptr(packed), n_expert, _ptr(codes), _ptr(scales), act_rows_per_token,

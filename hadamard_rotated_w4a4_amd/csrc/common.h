@@ -102,6 +102,17 @@ __device__ __forceinline__ v16f mfma_bf16_32x32x8(uint2 a, uint2 b) {
                                                    zero, 0, 0, 0);
 }
 
+// A K8 word (8 signed nibbles, see the streaming section) as 8 int8 MFMA
+// operand bytes, each 16 x the nibble, in K order: 3 bit operations.
+__device__ __forceinline__ long widen_k8(uint32_t w) {  // 8 signed nibbles -> 8 x int8 (x 16), K order
+    const uint32_t lo = (w << 4) & 0xF0F0F0F0u, hi = w & 0xF0F0F0F0u;
+    return (long)((uint64_t)hi << 32 | lo);
+}
+
+__device__ __forceinline__ v4i mfma_i8_16x16x32(long a, long b) {
+    return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, v4i{0, 0, 0, 0}, 0, 0, 0);
+}
+
 // Materialise a value in a register so that the compiler cannot fuse the
 // operation producing it with the one consuming it (e.g. a multiply folded
 // into a mixed-precision conversion as fma(x, c, +0), which loses -0.0).

@@ -93,65 +93,14 @@ __global__ __launch_bounds__(256) void act_operand_kernel(const uint8_t *__restr
                      (int)(row % 32));
 }
 
-// Expert routing shared by the grouped pre-pass and the grouped GEMM: rows
-// are grouped by expert (perm), each expert's rows padded to whole tiles of
-// GROUP_ROWS; tile_prefix[e] counts the tiles of experts before e.
-constexpr int GROUP_ROWS = 64;
-struct Routing {
-    const int32_t *perm;         // [n_rows] (token, slot) row ids, grouped by expert
-    const int32_t *offsets;      // [E + 1] start of each expert's rows in perm
-    const int32_t *tile_prefix;  // [E + 1]
-    int n_expert;
-};
-// Expert of row tile t < tile_prefix[E]: the largest e with tile_prefix[e] <= t.
-__device__ __forceinline__ int expert_of_tile(const Routing &g, int64_t t) {
-    int lo = 0, hi = g.n_expert;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (g.tile_prefix[mid] <= t) lo = mid; else hi = mid;
-    }
-    return lo;
-}
-
-// Grouped pre-pass: operand records of the routed rows, expert by expert, in
-// tiles of GROUP_ROWS rows.  Workgroup (tile t, blocks 4 y .. 4 y + 3), one
-// thread per (row, block): the tile's expert is found once per workgroup (a
-// wave-uniform search).  Activation row of routed row i = t * top_k + j: t
-// (one row per token) or i (one row per slot).  Rows past an expert's count
-// are zero; tiles past the last expert's are not written (nor read).
-constexpr int GROUPED_PREP_BLOCKS = 4;
-__global__ __launch_bounds__(GROUP_ROWS * GROUPED_PREP_BLOCKS) void act_operand_grouped_kernel(
-    const uint8_t *__restrict__ codes, const float *__restrict__ scales, int64_t k, Routing g, int top_k,
-    int per_slot, uint8_t *__restrict__ ws) {
-    const int64_t nbp = mx_blocks(k);
-    const int64_t t = blockIdx.x;
-    if (t >= g.tile_prefix[g.n_expert]) return;  // uniform
-    const int e = expert_of_tile(g, t);
-    const int r = threadIdx.x % GROUP_ROWS;
-    const int64_t b = (int64_t)blockIdx.y * GROUPED_PREP_BLOCKS + threadIdx.x / GROUP_ROWS;
-    if (b >= nbp) return;
-    const int64_t local = (t - g.tile_prefix[e]) * GROUP_ROWS + r;
-    int64_t src = -1;
-    if (local < g.offsets[e + 1] - g.offsets[e]) {
-        const int64_t i = g.perm[g.offsets[e] + local];
-        src = per_slot ? i : i / top_k;
-    }
-    const int64_t p = t * GROUP_ROWS + r;  // row of the padded order
-    write_act_record(codes, scales, src, k, b, ws + ((p / 32) * nbp + b) * MX_REC, (int)(p % 32));
-}
-
 // ---------------------------------------------------------------------------
 // The GEMM.
 // ---------------------------------------------------------------------------
 struct MxArgs {
     const uint8_t *act;     // activation records [rtiles][nbp][1 KB]
-    const uint8_t *wrec;    // weight records [tiles_n][nbp][1 KB] (grouped: expert 0's)
+    const uint8_t *wrec;    // weight records [tiles_n][nbp][1 KB]
     float *y;
     int64_t ldy, m, n, k;
-    // grouped (expert) products only: routing, and the bytes between two
-    // experts' packed weights
-    Routing g;
-    int64_t expert_bytes;
 };
 
 template <int BKB_, int NS_, int TM_, int TN_>
@@ -196,10 +145,8 @@ __device__ __forceinline__ void mx_tile_of(int64_t id, int64_t nx, int64_t ny, i
     by = in / width;
 }
 
-// One whole tile (workgroup index id) of the main kernel.  GROUPED: the row
-// tiles are the experts' routed rows (GROUP_ROWS per tile, see the grouped
-// pre-pass), each tile multiplies its expert's weights and scatters its rows.
-template <class C, bool GROUPED = false>
+// One whole tile (workgroup index id) of the main kernel.
+template <class C>
 __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *smem) {
     constexpr int BKB = C::BKB, NS = C::NS, TM = C::TM, TN = C::TN, RT = C::RT;
 
@@ -211,29 +158,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
     const int64_t rtiles = (a.m + 31) / 32, ctiles = padded_n(a.n) / TILE_N;
 
     int64_t bx, by;
-    const uint8_t *wrec = a.wrec;
-    int64_t row_lo = 0, row_cnt = a.m;  // rows of this tile's matrix (grouped: of its expert)
-    const int32_t *perm = nullptr;
-    if constexpr (!GROUPED) {
-        mx_tile_of(id, (a.n + C::BN - 1) / C::BN, (a.m + C::BM - 1) / C::BM, bx, by);
-    } else {
-        // The routed tiles, expert by expert, as (row tile, column tile)
-        // items; each XCD takes a contiguous eighth of the item list (ids x,
-        // x + 8, ... run on XCD x), so an expert's row tiles share one L2 and
-        // read its weights from HBM about once.
-        static_assert(C::BM == GROUP_ROWS, "grouped tiles are the routing's tiles");
-        const int64_t nx = (a.n + C::BN - 1) / C::BN;
-        const int64_t items = (int64_t)a.g.tile_prefix[a.g.n_expert] * nx, per_xcd = (items + 7) / 8;
-        const int64_t j = id / 8, item = (id % 8) * per_xcd + j;
-        if (j >= per_xcd || item >= items) return;  // uniform: no item for this workgroup
-        by = item / nx;
-        bx = item % nx;
-        const int e = expert_of_tile(a.g, by);
-        wrec += e * a.expert_bytes;
-        row_lo = (by - a.g.tile_prefix[e]) * GROUP_ROWS;
-        row_cnt = a.g.offsets[e + 1] - a.g.offsets[e];
-        perm = a.g.perm + a.g.offsets[e];
-    }
+    mx_tile_of(id, (a.n + C::BN - 1) / C::BN, (a.m + C::BM - 1) / C::BM, bx, by);
     const int64_t rt0 = by * RT, ct0 = bx * C::CT;
 
     // ---- this wave's loads: DMA_PER_WAVE records of 1 KB per stage ----
@@ -247,7 +172,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
     for (int d = 0; d < C::DMA_PER_WAVE; d++) {
         const int i = wave * C::DMA_PER_WAVE + d, t = i / BKB, bb = i % BKB;
         const uint8_t *base = t < RT ? a.act + min(rt0 + t, rtiles - 1) * nbp * MX_REC
-                                     : wrec + min(ct0 + t - RT, ctiles - 1) * nbp * MX_REC;
+                                     : a.wrec + min(ct0 + t - RT, ctiles - 1) * nbp * MX_REC;
         src[d] = base + bb * MX_REC + lane * 16;
         dst[d] = (uint32_t)((t * BKB + bb) * MX_REC);
     }
@@ -362,8 +287,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
     // ---- store ----
 #pragma unroll
     for (int i = 0; i < TM; i++) {
-        // row of this tile's matrix; grouped: of the expert's routed rows
-        const int64_t rbase = GROUPED ? row_lo + (wm * TM + i) * 32 : (rt0 + wm * TM + i) * 32;
+        const int64_t rbase = (rt0 + wm * TM + i) * 32;
 #pragma unroll
         for (int j = 0; j < TN; j++) {
             const int64_t col = (ct0 + wn * TN + j) * 32 + c;
@@ -371,7 +295,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int64_t r = rbase + mfma32_row(v, lane);
-                if (r < row_cnt) a.y[(GROUPED ? (int64_t)perm[r] : r) * a.ldy + col] = acc[i][j][v];
+                if (r < a.m) a.y[r * a.ldy + col] = acc[i][j][v];
             }
         }
     }
@@ -503,14 +427,6 @@ __global__ __launch_bounds__(C::NT) void gemm_mx_kernel(MxArgs a, int64_t main_w
     __shared__ __attribute__((aligned(1024))) uint8_t smem[MAIN_LDS > PIECE_LDS ? MAIN_LDS : PIECE_LDS];
     if ((int64_t)blockIdx.x < main_wgs) mx_tile<C>(a, blockIdx.x, smem);  // uniform per workgroup
     else mx_piece<P>(a, first_piece_tile, blockIdx.x - main_wgs, smem);
-}
-
-// Grouped (MUL_MAT_ID) product: one whole tile per workgroup; a.m is the
-// routing's bound on padded rows (tiles past the last expert's exit).
-template <class C>
-__global__ __launch_bounds__(C::NT) void gemm_mx_grouped_kernel(MxArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE_BYTES];
-    mx_tile<C, true>(a, blockIdx.x, smem);
 }
 
 }  // namespace w4a4

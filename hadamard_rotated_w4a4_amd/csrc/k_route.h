@@ -10,6 +10,25 @@
 
 namespace w4a4 {
 
+// Expert routing as the grouped kernels read it: rows grouped by expert
+// (perm), each expert's rows padded to whole tiles of the kernel's row count;
+// tile_prefix[e] counts the tiles of experts before e.
+struct Routing {
+    const int32_t *perm;         // [n_rows] (token, slot) row ids, grouped by expert
+    const int32_t *offsets;      // [E + 1] start of each expert's rows in perm
+    const int32_t *tile_prefix;  // [E + 1]
+    int n_expert;
+};
+// Expert of row tile t < tile_prefix[E]: the largest e with tile_prefix[e] <= t.
+__device__ __forceinline__ int expert_of_tile(const Routing &g, int64_t t) {
+    int lo = 0, hi = g.n_expert;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (g.tile_prefix[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
 // -------------------------------------------------------------------------
 // MUL_MAT_ID routing: one workgroup groups the (token, slot) rows by expert
 // and counts each expert's row tiles; rows with an invalid id are zeroed.

@@ -65,15 +65,6 @@ __host__ __device__ inline SmallPlan small_m_plan(int64_t n, int64_t k) {
 }
 __host__ __device__ inline int64_t small_m_splits(int64_t n, int64_t k) { return small_m_plan(n, k).splits; }
 
-__device__ __forceinline__ long widen_k8(uint32_t w) {  // 8 signed nibbles -> 8 x int8 (x 16), K order
-    const uint32_t lo = (w << 4) & 0xF0F0F0F0u, hi = w & 0xF0F0F0F0u;
-    return (long)((uint64_t)hi << 32 | lo);
-}
-
-__device__ __forceinline__ v4i mfma_i8_16x16x32(long a, long b) {
-    return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, v4i{0, 0, 0, 0}, 0, 0, 0);
-}
-
 template <int WAVES, int DEPTH>
 __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];

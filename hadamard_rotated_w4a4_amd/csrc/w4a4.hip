@@ -12,6 +12,7 @@
 
 #include "common.h"
 #include "k_dense.h"
+#include "k_grouped.h"
 #include "k_prep.h"
 #include "k_rotq.h"
 #include "k_route.h"
@@ -325,17 +326,15 @@ w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, 
 
 namespace {
 // Routing bound: every expert adds at most one partial tile to the full ones.
-int64_t grouped_row_tiles(int64_t n_expert, int64_t n_rows) {
-    return (n_rows + GROUP_ROWS - 1) / GROUP_ROWS + n_expert;
+int64_t grouped_row_tiles(int64_t n_expert, int64_t n_rows, int64_t tile_rows) {
+    return (n_rows + tile_rows - 1) / tile_rows + n_expert;
 }
 size_t up256(int64_t b) { return (size_t)((b + 255) / 256 * 256); }
 }  // namespace
 
-size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t top_k, int64_t k) {
-    if (n_expert < 0 || n_tokens < 0 || top_k < 0 || k < 0 || k % QK) return 0;
-    const int64_t n_rows = n_tokens * top_k;
-    const int64_t act = grouped_row_tiles(n_expert, n_rows) * (GROUP_ROWS / 32) * mx_blocks(k) * MX_REC;
-    return 2 * up256((n_expert + 1) * 4) + up256(n_rows * 4) + (size_t)act;
+size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t top_k) {
+    if (n_expert < 0 || n_tokens < 0 || top_k < 0) return 0;
+    return 2 * up256((n_expert + 1) * 4) + up256(n_tokens * top_k * 4);
 }
 
 w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *codes, const float *scales,
@@ -348,10 +347,9 @@ w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *
     if (n_expert < 1 || n_expert > ROUTE_MAX_EXPERTS) return W4A4_ERR_INVALID_VALUE;
     if (act_rows_per_token != 1 && act_rows_per_token != top_k) return W4A4_ERR_INVALID_VALUE;
     const int64_t n_rows = n_tokens * top_k;
-    using C = Mx64x128;
-    const int64_t row_tiles = grouped_row_tiles(n_expert, n_rows);
-    const int64_t col_tiles = (n + C::BN - 1) / C::BN;
-    if (n_rows > INT32_MAX || row_tiles * col_tiles + 8 > INT32_MAX) return W4A4_ERR_INVALID_VALUE;
+    const int64_t row_tiles = grouped_row_tiles(n_expert, n_rows, GS_ROWS);
+    const int64_t col_chunks = (padded_n(n) / TILE_N + GS_WAVES - 1) / GS_WAVES;
+    if (n_rows > INT32_MAX || row_tiles * col_chunks + 8 > INT32_MAX) return W4A4_ERR_INVALID_VALUE;
     if (!ids || !workspace) return W4A4_ERR_INVALID_VALUE;
     if (k > 0) {
         const w4a4_status st = check_gemm_common(packed_w, codes, scales, y, n, k);
@@ -360,7 +358,7 @@ w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *
         return W4A4_ERR_INVALID_VALUE;
     }
     if (!aligned(ids, 4) || !aligned(workspace, 256) || !aligned(y, 4)) return W4A4_ERR_MISALIGNED;
-    if (workspace_bytes < w4a4_gemm_id_workspace_bytes(n_expert, n_tokens, top_k, k))
+    if (workspace_bytes < w4a4_gemm_id_workspace_bytes(n_expert, n_tokens, top_k))
         return W4A4_ERR_WORKSPACE_TOO_SMALL;
 
     hipStream_t s = as_stream(stream);
@@ -372,35 +370,27 @@ w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *
     int32_t *offsets = reinterpret_cast<int32_t *>(ws);
     int32_t *tile_prefix = reinterpret_cast<int32_t *>(ws + up256((n_expert + 1) * 4));
     int32_t *perm = reinterpret_cast<int32_t *>(ws + 2 * up256((n_expert + 1) * 4));
-    uint8_t *act = ws + 2 * up256((n_expert + 1) * 4) + up256(n_rows * 4);
 
-    route_kernel<<<1, ROUTE_THREADS, 0, s>>>(ids, (int)n_rows, (int)n_expert, GROUP_ROWS, offsets, tile_prefix,
-                                             perm, y, n);
+    route_kernel<<<1, ROUTE_THREADS, 0, s>>>(ids, (int)n_rows, (int)n_expert, GS_ROWS, offsets, tile_prefix, perm,
+                                             y, n);
     w4a4_status st = hip_status("route_kernel");
     if (st != W4A4_OK) return st;
 
-    const Routing g{perm, offsets, tile_prefix, (int)n_expert};
-    const int64_t rows = row_tiles * GROUP_ROWS;
-    const dim3 pgrid((unsigned)row_tiles,
-                     (unsigned)((mx_blocks(k) + GROUPED_PREP_BLOCKS - 1) / GROUPED_PREP_BLOCKS));
-    act_operand_grouped_kernel<<<pgrid, GROUP_ROWS * GROUPED_PREP_BLOCKS, 0, s>>>(
-        codes, scales, k, g, (int)top_k, act_rows_per_token != 1 ? 1 : 0, act);
-    st = hip_status("act_operand_grouped_kernel");
-    if (st != W4A4_OK) return st;
-
-    MxArgs a{};
-    a.act = act;
-    a.wrec = static_cast<const uint8_t *>(packed_w);  // the matrix-core section
+    GsArgs a{};
+    a.codes = codes;
+    a.scales = scales;
+    a.packed = static_cast<const uint8_t *>(packed_w);
+    a.expert_bytes = packed_total_bytes(n, k);
     a.y = y;
-    a.ldy = n;
-    a.m = rows;
     a.n = n;
     a.k = k;
-    a.g = g;
-    a.expert_bytes = packed_total_bytes(n, k);
-    // a bound on the items (row tiles x column tiles), rounded up to whole XCD rows
-    gemm_mx_grouped_kernel<C><<<(unsigned)((row_tiles * col_tiles + 7) / 8 * 8), C::NT, 0, s>>>(a);
-    return hip_status("gemm_mx_grouped_kernel");
+    a.g = Routing{perm, offsets, tile_prefix, (int)n_expert};
+    a.top_k = (int)top_k;
+    a.per_slot = act_rows_per_token != 1 ? 1 : 0;
+    a.col_chunks = col_chunks;
+    // a bound on the items (row tiles x column chunks), rounded up to whole XCD rows
+    gemm_grouped_stream_kernel<<<(unsigned)((row_tiles * col_chunks + 7) / 8 * 8), 64 * GS_WAVES, 0, s>>>(a);
+    return hip_status("gemm_grouped_stream_kernel");
 }
 
 }  // extern "C"

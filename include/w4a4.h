@@ -171,7 +171,7 @@ w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, 
                                int64_t k, int64_t ldy, void *stream);
 
 /* Workspace bytes w4a4_gemm_id needs (0 for invalid sizes).  Host only, pure. */
-size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t top_k, int64_t k);
+size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t top_k);
 
 /*
  * MUL_MAT_ID: expert-routed W4A4 product (section "MoE: W4A4 on the experts").
@@ -184,14 +184,15 @@ size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t 
  *             [0, n_expert) yields a zero output row (defined behaviour).
  *   y         out, [n_tokens][top_k][n] fp32.
  *   workspace device scratch of w4a4_gemm_id_workspace_bytes(n_expert,
- *             n_tokens, top_k, k) bytes, 256-byte aligned; contents on entry
- *             are ignored.  Calls that share a workspace must not overlap.
- * One launch groups the (token, slot) rows by expert (tiles of 64 rows per
- * expert), a second lays the routed activation rows out as matrix-core
- * operands in the workspace, a third runs the tiled matrix-core product, each
- * tile against its expert's weights, and scatters the rows to y.  Each output
- * element depends only on its own row and column: the result does not depend
- * on how rows are grouped.  Supports n_expert <= 8192.
+ *             n_tokens, top_k) bytes, 256-byte aligned (the routing: expert
+ *             offsets, tile counts, row permutation); contents on entry are
+ *             ignored.  Calls that share a workspace must not overlap.
+ * One launch groups the (token, slot) rows by expert (tiles of 32 rows per
+ * expert); a second streams each expert's 4-bit weight records once per row
+ * tile against the tile's activation rows (read through the permutation)
+ * and scatters the rows to y.  Each output element depends only on its own
+ * row and column: the result does not depend on how rows are grouped.
+ * Supports n_expert <= 8192.
  */
 w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *codes,
                          const float *scales, int64_t act_rows_per_token, const int32_t *ids,

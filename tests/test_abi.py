@@ -47,11 +47,9 @@ def test_size_queries(L):
     assert L.w4a4_packed_weight_bytes(17408, 5120) == 544 * 160 * 1024 + 544 * 40 * 2304
     assert L.w4a4_packed_weight_bytes(33, 64) == 2 * 8 * 1024 + 2 * 1 * 2304  # n padded to 64
     assert L.w4a4_packed_weight_bytes(10, 33) == 0
-    # offsets and tile counts (129 int32 each, 256-byte rounded), perm (8192
-    # int32), operand records of (8192 / 64 + 128) tiles of 64 rows x 64 blocks
-    assert L.w4a4_gemm_id_workspace_bytes(128, 1024, 8, 2048) == 2 * 768 + 32768 + 256 * 2 * 64 * 1024
-    assert L.w4a4_gemm_id_workspace_bytes(-1, 1, 1, 32) == 0
-    assert L.w4a4_gemm_id_workspace_bytes(1, 1, 1, 40) == 0
+    # offsets and tile counts (129 int32 each, 256-byte rounded), perm (8192 int32)
+    assert L.w4a4_gemm_id_workspace_bytes(128, 1024, 8) == 2 * 768 + 32768
+    assert L.w4a4_gemm_id_workspace_bytes(-1, 1, 1) == 0
 
 
 A = 0x10000000          # fake, aligned device addresses: never dereferenced
@@ -152,7 +150,7 @@ def test_prep_validation(L):
 
 def test_gemm_id_validation(L):
     f = L.w4a4_gemm_id
-    ws = L.w4a4_gemm_id_workspace_bytes(4, 8, 2, 64)
+    ws = L.w4a4_gemm_id_workspace_bytes(4, 8, 2)
     args = dict(packed=P(A), E=4, codes=P(A), scales=P(A), arpt=1, ids=P(A), T=8, top_k=2,
                 y=P(A), n=64, k=64, ws=P(A), wsb=ws)
 
