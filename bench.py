@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 COLD_BYTES = 1 << 30         # weight copies rotated per step exceed this
 PROFILE_JSON = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "hadamard_rotated_w4a4_amd", "csrc", f)
-                  for f in ("common.h", "k_route.h", "k_dense.h", "k_smallm.h", "k_rotq.h", "k_prep.h", "w4a4.hip")]
+                  for f in ("common.h", "k_route.h", "k_dense.h", "k_smallm.h", "k_grouped.h", "k_rotq.h", "k_prep.h", "w4a4.hip")]
 
 
 def log(msg):

@@ -426,6 +426,29 @@ def test_gemm_id_single_expert_equals_gemm(ops):
     assert np.array_equal(yi0, yi1)
 
 
+@pytest.mark.parametrize("rows_per_token", [1, 2])
+def test_gemm_id_long_k_ragged_tiles(ops, rows_per_token):
+    """K over two staging chunks with a ragged last record (nb = 69), n over
+    two column chunks with a ragged last tile (n = 300), an expert with
+    several row tiles, one with none, and invalid ids."""
+    E, T, top_k, n, k = 5, 40, 2, 300, 2208
+    rng = np.random.default_rng(2208 + rows_per_token)
+    we = [synth.weights(n, k, rng) for _ in range(E)]
+    ids = np.where(rng.random((T, top_k)) < 0.7, 0, rng.integers(1, 4, (T, top_k))).astype(np.int32)
+    ids[:, 1] = np.where(ids[:, 0] == ids[:, 1], (ids[:, 1] + 1) % 4, ids[:, 1])  # distinct per token; expert 4 unused
+    ids[3, 0] = E
+    x = synth.activations(T * rows_per_token, k, rng, synth.outlier_count(k))
+    say(f"gemm_id long k rows_per_token={rows_per_token}: counts {np.bincount(ids[ids < E], minlength=E)}")
+    packed = torch.cat([ops.prepare_weights(dev(w)) for w in we])
+    c, s = ops.rotate_quantize_act(dev(x))
+    y = host(ops.gemm_id(packed, E, c, s, rows_per_token, dev(ids), n, k))
+    q4e = np.stack([oracle.prepare_weights(w) for w in we])
+    rc, rs = oracle.rotate_quantize_act(x)
+    ref = oracle.gemm_id(q4e, rc, rs, rows_per_token, ids, n, k)
+    assert not y[3, 0].any()
+    assert_rows_close(y.reshape(-1, n), ref.reshape(-1, n), "gemm_id long k")
+
+
 @pytest.mark.parametrize("which", ["gate", "down"])
 def test_gemm_id_moe_full_size_sampled(ops, which):
     mo = synth.moe()
