@@ -60,6 +60,9 @@ def _load():
         lib.oracle_block_sums.argtypes = [P, P, I64, I64, I64, P]
         lib.oracle_gemm.argtypes = [P, P, P, I64, I64, I64, P, I64, ctypes.c_int]
         lib.oracle_gemm_id.argtypes = [P, I64, P, P, I64, P, I64, I64, I64, I64, P, ctypes.c_int]
+        lib.oracle_rotate_quantize_act8.argtypes = [P, ctypes.c_int, I64, I64, I64, P, P, ctypes.c_int]
+        lib.oracle_block_sums_a8.argtypes = [P, P, I64, I64, I64, P]
+        lib.oracle_gemm_a8.argtypes = [P, P, P, I64, I64, I64, P, I64, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -189,5 +192,47 @@ def gemm_id(q4_experts: np.ndarray, codes: np.ndarray, scales: np.ndarray,
     y = np.empty((n_tokens, top_k, n), np.float32)
     _load().oracle_gemm_id(_ptr(q4_experts), n_expert, _ptr(codes), _ptr(scales),
                            act_rows_per_token, _ptr(ids), n_tokens, top_k, n, k, _ptr(y),
+                           threads or default_threads())
+    return y
+
+
+# --------------------------------------------------------------------------
+# W4A8-H32 (reading R8 in oracle.c): int8 activation codes, same rotation
+# --------------------------------------------------------------------------
+
+def rotate_quantize_act8(x: np.ndarray, k: int | None = None, threads: int | None = None):
+    """x fp32 or fp16 [m, ldx] -> (codes int8 [m, k], scales fp32 [m, k/32])."""
+    assert x.dtype in (np.float32, np.float16)
+    x = np.ascontiguousarray(x)
+    m, ldx = x.shape
+    k = ldx if k is None else k
+    assert k % QK == 0 and k <= ldx
+    codes = np.empty((m, k), np.int8)
+    scales = np.empty((m, k // QK), np.float32)
+    dtype = 0 if x.dtype == np.float32 else 1
+    _load().oracle_rotate_quantize_act8(_ptr(x), dtype, m, k, ldx, _ptr(codes), _ptr(scales),
+                                        threads or default_threads())
+    return codes, scales
+
+
+def block_sums_a8(q4: np.ndarray, codes: np.ndarray, k: int) -> np.ndarray:
+    """int32 [m, n, k/32]: exact per-block dots of int8 codes with Q4_0 codes."""
+    q4 = np.ascontiguousarray(q4, np.uint8)
+    codes = np.ascontiguousarray(codes, np.int8)
+    m, n = codes.shape[0], q4.shape[0]
+    S = np.empty((m, n, k // QK), np.int32)
+    _load().oracle_block_sums_a8(_ptr(q4), _ptr(codes), m, n, k, _ptr(S))
+    return S
+
+
+def gemm_a8(q4: np.ndarray, codes: np.ndarray, scales: np.ndarray, k: int,
+            threads: int | None = None) -> np.ndarray:
+    """fp32 [m, n] = sum_b dw*s*S with int8 codes, each term and the sum in fp64."""
+    q4 = np.ascontiguousarray(q4, np.uint8)
+    codes = np.ascontiguousarray(codes, np.int8)
+    scales = np.ascontiguousarray(scales, np.float32)
+    m, n = codes.shape[0], q4.shape[0]
+    y = np.empty((m, n), np.float32)
+    _load().oracle_gemm_a8(_ptr(q4), _ptr(codes), _ptr(scales), m, n, k, _ptr(y), n,
                            threads or default_threads())
     return y

@@ -44,6 +44,13 @@
  *   R7  MUL_MAT_ID: output row (t, j) uses expert ids[t][j] and activation
  *       row t (one activation row per token) or t*top_k + j (one per slot);
  *       an id outside [0, n_expert) gives a row of zeros.
+ *   R8  W4A8-H32, the page's exact int8 path for a rotated file (section
+ *       "Hadamard-rotated Q4_0: W4A4 prompt processing": the rotated file
+ *       can run on the exact int8 path instead of W4A4): the activations are
+ *       rotated as in R4 and rounded to 8 bits per block, d = amax/127,
+ *       id = 1/d, q = clamp(round_half_away(v*id), -127, 127), s = d * c32,
+ *       zero blocks as in R5; the output is R6 with these codes.  Codes are
+ *       stored one signed byte per element, [m][k].
  *
  * Byte layouts:
  *   Q4_0 block (18 bytes): fp16 d (little endian), then 16 bytes; byte j holds
@@ -313,14 +320,16 @@ static float round_half_away(float x)
     return t;
 }
 
-/* Quantise one rotated block: codes q[32] in [-7, 7], returns the stored scale. */
-static float quantize_block(const float *v, int8_t *q)
+/* Quantise one rotated block to codes q[32] in [-qmax, qmax] (qmax = 7 for
+ * R5, 127 for R8); returns the stored scale. */
+static float quantize_block(const float *v, int8_t *q, int qmax)
 {
     float amax = 0.0f;
     for (int t = 0; t < QK; t++)
         if (fabsf(v[t]) > amax)
             amax = fabsf(v[t]);
-    float d = amax / 7.0f;
+    const float fq = (float)qmax;
+    float d = amax / fq;
     if (!(d >= FLT_MIN)) {
         for (int t = 0; t < QK; t++)
             q[t] = 0;
@@ -329,11 +338,20 @@ static float quantize_block(const float *v, int8_t *q)
     float id = 1.0f / d;
     for (int t = 0; t < QK; t++) {
         float r = round_half_away(v[t] * id);
-        if (r > 7.0f) r = 7.0f;
-        if (r < -7.0f) r = -7.0f;
+        if (r > fq) r = fq;
+        if (r < -fq) r = -fq;
         q[t] = (int8_t)r;
     }
     return d * oracle_c32();
+}
+
+/* Block b of row r of x, as fp32. */
+static void load_block(const void *x, int dtype, int64_t ldx, int64_t r, int64_t b, float *v)
+{
+    for (int t = 0; t < QK; t++) {
+        int64_t idx = r * ldx + b * QK + t;
+        v[t] = dtype == 0 ? ((const float *)x)[idx] : oracle_half_to_float(((const uint16_t *)x)[idx]);
+    }
 }
 
 typedef struct {
@@ -351,14 +369,10 @@ static void act_rows(void *p, int64_t r0, int64_t r1)
     for (int64_t r = r0; r < r1; r++) {
         for (int64_t b = 0; b < nb; b++) {
             float v[QK];
-            for (int t = 0; t < QK; t++) {
-                int64_t idx = r * c->ldx + b * QK + t;
-                v[t] = c->dtype == 0 ? ((const float *)c->x)[idx]
-                                     : oracle_half_to_float(((const uint16_t *)c->x)[idx]);
-            }
+            load_block(c->x, c->dtype, c->ldx, r, b, v);
             oracle_fwht32_f32(v);
             int8_t q[QK];
-            c->scales[r * nb + b] = quantize_block(v, q);
+            c->scales[r * nb + b] = quantize_block(v, q, 7);
             uint8_t *dst = c->codes + r * (k / 2) + b * 16;
             for (int j = 0; j < 16; j++)
                 dst[j] = (uint8_t)(((uint8_t)q[j] & 0x0f) | (((uint8_t)q[j + 16] & 0x0f) << 4));
@@ -375,6 +389,27 @@ void oracle_rotate_quantize_act(const void *x, int dtype, int64_t m, int64_t k, 
 {
     act_ctx c = {x, dtype, k, ldx, codes, scales};
     parallel_rows(m, nthreads, act_rows, &c);
+}
+
+static void act8_rows(void *p, int64_t r0, int64_t r1)
+{
+    act_ctx *c = (act_ctx *)p;
+    const int64_t k = c->k, nb = k / QK;
+    for (int64_t r = r0; r < r1; r++)
+        for (int64_t b = 0; b < nb; b++) {
+            float v[QK];
+            load_block(c->x, c->dtype, c->ldx, r, b, v);
+            oracle_fwht32_f32(v);
+            c->scales[r * nb + b] = quantize_block(v, (int8_t *)(c->codes + r * k + b * QK), 127);
+        }
+}
+
+/* R8: codes [m][k] signed bytes, scales [m][k/32]. */
+void oracle_rotate_quantize_act8(const void *x, int dtype, int64_t m, int64_t k, int64_t ldx,
+                                 int8_t *codes, float *scales, int nthreads)
+{
+    act_ctx c = {x, dtype, k, ldx, (uint8_t *)codes, scales};
+    parallel_rows(m, nthreads, act8_rows, &c);
 }
 
 /* Signed int4 code t (-8..7) of an activation block. */
@@ -402,6 +437,23 @@ void oracle_block_sums(const uint8_t *q4, const uint8_t *codes, int64_t m, int64
                 int32_t s = 0;
                 for (int t = 0; t < QK; t++)
                     s += (q4_code(wb, t) - 8) * act_code(ab, t);
+                S[(i * n + j) * nb + b] = s;
+            }
+}
+
+/* R8 block dots: S[(i*n + j)*nb + b] = sum_t (qw - 8) * qa with int8 codes. */
+void oracle_block_sums_a8(const uint8_t *q4, const int8_t *codes, int64_t m, int64_t n, int64_t k,
+                          int32_t *S)
+{
+    const int64_t nb = k / QK;
+    for (int64_t i = 0; i < m; i++)
+        for (int64_t j = 0; j < n; j++)
+            for (int64_t b = 0; b < nb; b++) {
+                const uint8_t *wb = q4 + (j * nb + b) * 18;
+                const int8_t *ab = codes + i * k + b * QK;
+                int32_t s = 0;
+                for (int t = 0; t < QK; t++)
+                    s += (q4_code(wb, t) - 8) * ab[t];
                 S[(i * n + j) * nb + b] = s;
             }
 }
@@ -461,6 +513,42 @@ void oracle_gemm(const uint8_t *q4, const uint8_t *codes, const float *scales, i
         pthread_join(th[t], NULL);
     free(th);
     free(jobs);
+}
+
+/* R8 output: as oracle_gemm with int8 codes [m][k]. */
+typedef struct {
+    const uint8_t *q4;
+    const int8_t *codes;
+    const float *scales;
+    int64_t n, k;
+    float *y;
+    int64_t ldy;
+} gemm8_ctx;
+
+static void gemm8_rows(void *p, int64_t r0, int64_t r1)
+{
+    gemm8_ctx *g = (gemm8_ctx *)p;
+    const int64_t nb = g->k / QK;
+    for (int64_t i = r0; i < r1; i++)
+        for (int64_t j = 0; j < g->n; j++) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < nb; b++) {
+                const uint8_t *wb = g->q4 + (j * nb + b) * 18;
+                const int8_t *ab = g->codes + i * g->k + b * QK;
+                int32_t s = 0;
+                for (int t = 0; t < QK; t++)
+                    s += (q4_code(wb, t) - 8) * ab[t];
+                acc += (double)q4_scale(wb) * (double)g->scales[i * nb + b] * (double)s;
+            }
+            g->y[i * g->ldy + j] = (float)acc;
+        }
+}
+
+void oracle_gemm_a8(const uint8_t *q4, const int8_t *codes, const float *scales, int64_t m,
+                    int64_t n, int64_t k, float *y, int64_t ldy, int nthreads)
+{
+    gemm8_ctx c = {q4, codes, scales, n, k, y, ldy};
+    parallel_rows(m, nthreads, gemm8_rows, &c);
 }
 
 /* ------------------------------------------------------------------ */

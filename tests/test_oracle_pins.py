@@ -397,6 +397,110 @@ def test_rotation_lowers_w4a4_error_on_outliers():
 
 
 # --------------------------------------------------------------------------
+# W4A8-H32 (reading R8): int8 activation codes, the same rotation
+# --------------------------------------------------------------------------
+
+def test_quantiser8_special_blocks():
+    c32 = np.float32(oracle.c32())
+    for scale in (0.0, 1e-44):
+        codes, s = oracle.rotate_quantize_act8(np.full((1, 32), scale, np.float32))
+        assert not codes.any() and s[0, 0] == 0.0
+    # constant block: H x = (32a, 0, ..., 0) -> codes (127 sign a, 0, ...)
+    for a in (0.37, -2.5, 300.0):
+        codes, s = oracle.rotate_quantize_act8(np.full((1, 32), a, np.float32))
+        assert list(codes[0]) == [127 * int(np.sign(a))] + [0] * 31
+        d = np.float32(np.float32(32 * np.float32(abs(a))) / np.float32(127))
+        assert s[0, 0] == np.float32(d * c32)
+    # one-hot: every rotated value is +-a, so every code is +-127
+    for j in (0, 17):
+        x = np.zeros((1, 32), np.float32)
+        x[0, j] = -4.0
+        codes, s = oracle.rotate_quantize_act8(x)
+        assert np.array_equal(codes[0].astype(int), -127 * H_SCIPY[:, j])
+
+
+def test_quantiser8_closed_form_recovers_codes():
+    """x = H(sigma*c)/32, c in [-127, 127] with 127 in every block, sigma a
+    power of two: the quantiser returns c and sigma*c32."""
+    rng = np.random.default_rng(19)
+    m, k = 6, 256
+    c = rng.integers(-127, 128, (m, k // 32, 32))
+    for r in range(m):
+        for b in range(k // 32):
+            c[r, b, rng.integers(0, 32)] = rng.choice([-127, 127])
+    sig = 2.0 ** rng.integers(-8, -2, (m, k // 32))
+    x = (np.einsum("ij,rbj->rbi", H_SCIPY, c) * (sig[..., None] / 32)).reshape(m, k).astype(np.float32)
+    codes, s = oracle.rotate_quantize_act8(x)
+    assert np.array_equal(codes.astype(int).reshape(m, k // 32, 32), c)
+    assert np.array_equal(s, (sig.astype(np.float32) * np.float32(oracle.c32())).astype(np.float32))
+
+
+def test_quantiser8_ties_away_and_nearest():
+    v = np.zeros(32)
+    v[:6] = [127, 2.5, -2.5, 0.5, -100.5, 3.25]  # amax 127: d = 1, ties round away from zero
+    x = (H_SCIPY @ v / 32).astype(np.float32)[None]
+    codes, _ = oracle.rotate_quantize_act8(x)
+    assert list(codes[0, :6]) == [127, 3, -3, 1, -101, 3]
+    d = synth.ffn_up(m=2)
+    x = d.x[:, :512]
+    codes, s = oracle.rotate_quantize_act8(x)
+    c32 = float(np.float32(oracle.c32()))
+    v = x.astype(np.float64).reshape(2, 16, 32) @ H_SCIPY.T
+    dd = s.astype(np.float64) / c32
+    assert np.abs(v / dd[..., None] - codes.reshape(2, 16, 32)).max() <= 0.5 + 1e-4
+    assert (np.abs(codes.reshape(2, 16, 32)).max(axis=2) == 127).all()
+
+
+def test_block_sums8_brute_force_and_extremes():
+    rng = np.random.default_rng(20)
+    w = synth.weights(3, 64, rng)
+    x = rng.standard_normal((2, 64)).astype(np.float32) * 3
+    q4 = oracle.prepare_weights(w)
+    codes, _ = oracle.rotate_quantize_act8(x)
+    S = oracle.block_sums_a8(q4, codes, 64)
+    for i in range(2):
+        for j in range(3):
+            for b in range(2):
+                _, qw = decode_q4_block(q4[j, b])
+                assert S[i, j, b] == sum((qw[t] - 8) * int(codes[i, 32 * b + t]) for t in range(32))
+    blk_w = np.zeros((1, 1, 18), np.uint8)  # codes 0 -> -8
+    act = np.full((1, 32), -127, np.int8)
+    assert oracle.block_sums_a8(blk_w, act, 32)[0, 0, 0] == 32 * 8 * 127
+
+
+def test_gemm8_brute_force_tiny():
+    rng = np.random.default_rng(21)
+    w = synth.weights(4, 96, rng)
+    x = rng.standard_normal((3, 96)).astype(np.float32)
+    q4 = oracle.prepare_weights(w)
+    codes, s = oracle.rotate_quantize_act8(x)
+    y = oracle.gemm_a8(q4, codes, s, 96, threads=2)
+    for i in range(3):
+        for j in range(4):
+            acc = 0.0
+            for b in range(3):
+                d, qw = decode_q4_block(q4[j, b])
+                S = sum((qw[t] - 8) * int(codes[i, 32 * b + t]) for t in range(32))
+                acc += d * float(s[i, b]) * S
+            assert y[i, j] == np.float32(acc)
+
+
+def test_w4a8_error_far_below_w4a4():
+    """Both against the fp64 product of the dequantised rotated weights with the
+    exactly rotated activations: 8-bit codes leave ~16x less activation noise."""
+    d = synth.tiny()
+    q4 = oracle.prepare_weights(d.w)
+    wdeq = oracle.q4_0_dequantize(q4, d.k).astype(np.float64)
+    hx = (d.x.astype(np.float64).reshape(64, 8, 32) @ H_SCIPY.T / np.sqrt(32.0)).reshape(64, 256)
+    ref = hx @ wdeq.T
+    c4, s4 = oracle.rotate_quantize_act(d.x)
+    c8, s8 = oracle.rotate_quantize_act8(d.x)
+    e4 = np.abs(oracle.gemm(q4, c4, s4, d.k) - ref).mean()
+    e8 = np.abs(oracle.gemm_a8(q4, c8, s8, d.k) - ref).mean()
+    assert e8 < e4 / 8
+
+
+# --------------------------------------------------------------------------
 # MUL_MAT_ID
 # --------------------------------------------------------------------------
 
