@@ -47,6 +47,9 @@ def lib() -> ctypes.CDLL:
             "w4a4_gemm_prepared": ([P, P, P, I64, I64, I64, I64, P], ST),
             "w4a4_gemm": ([P, P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_id_workspace_bytes": ([I64, I64, I64], SZ),
+            "w4a4_rotate_quantize_act8": ([P, ST, I64, I64, I64, P, P, P], ST),
+            "w4a4_gemm_a8_workspace_bytes": ([I64, I64, I64], SZ),
+            "w4a4_gemm_a8": ([P, P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_id": ([P, I64, P, P, I64, P, I64, I64, P, I64, I64, P, SZ, P], ST),
         }
         for name, (args, res) in sigs.items():
@@ -223,6 +226,42 @@ def gemm_id(packed: torch.Tensor, n_expert: int, codes: torch.Tensor, scales: to
     _check(lib().w4a4_gemm_id(_ptr(packed), n_expert, _ptr(codes), _ptr(scales), act_rows_per_token,
                               _ptr(ids.contiguous()), n_tokens, top_k, _ptr(y), n, k, _ptr(workspace),
                               workspace.numel(), _stream(ids.device)), "w4a4_gemm_id")
+    return y
+
+
+def rotate_quantize_act8(x: torch.Tensor, k: int | None = None, codes: torch.Tensor | None = None,
+                         scales: torch.Tensor | None = None):
+    """W4A8-H32 activations: x fp16/fp32 [m, >=k] -> (codes int8 [m, k], scales fp32 [m, k/32])."""
+    _require_cuda(x, codes, scales)
+    assert x.dim() == 2 and x.stride(1) == 1
+    dt = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16}.get(x.dtype)
+    if dt is None:
+        raise W4A4Error(f"unsupported activation dtype {x.dtype}")
+    m = x.shape[0]
+    k = x.shape[1] if k is None else k
+    if codes is None:
+        codes = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    _check(lib().w4a4_rotate_quantize_act8(_ptr(x), dt, m, k, x.stride(0), _ptr(codes), _ptr(scales),
+                                           _stream(x.device)), "w4a4_rotate_quantize_act8")
+    return codes, scales
+
+
+def gemm_a8(packed: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: int, k: int,
+            y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A8-H32 product: fp32 [m, n] (row stride y.stride(0))."""
+    _require_cuda(packed, codes, scales, y, workspace)
+    m = codes.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=codes.device)
+    assert y.stride(1) == 1
+    need = int(lib().w4a4_gemm_a8_workspace_bytes(m, n, k))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=codes.device)
+    _check(lib().w4a4_gemm_a8(_ptr(packed), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, y.stride(0),
+                              _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                              _stream(codes.device)), "w4a4_gemm_a8")
     return y
 
 

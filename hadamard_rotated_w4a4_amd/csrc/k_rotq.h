@@ -68,13 +68,18 @@ __device__ __forceinline__ void load4(const __half *p, bool vec, float v[4]) {
 // (checked on the host).  With `act` set, also writes the block's operand
 // record for the matrix-core GEMM (the blocks then run over the padded block
 // count, an even number; padding rows and blocks get zero records).
+//
+// QMAX = 7: int4 codes (W4A4).  QMAX = 127: int8 codes for the exact int8
+// path on a rotated file (W4A8), one signed byte per element in `codes`
+// ([m][k]), same rotation, d = amax / 127; no operand record.
 constexpr int RQ_BLOCKS = 2;  // blocks per workgroup
-template <typename T>
+template <typename T, int QMAX = 7>
 __global__ __launch_bounds__(256 * RQ_BLOCKS) void rotate_quantize_kernel(const T *__restrict__ x, int64_t m,
                                                                           int64_t k, int64_t ldx, bool vec,
                                                                           uint8_t *__restrict__ codes,
                                                                           float *__restrict__ scales,
                                                                           uint8_t *__restrict__ act) {
+    static_assert(QMAX == 7 || QMAX == 127, "int4 or int8 codes");
     const int64_t nb = k / QK;
     const int tid = threadIdx.x, L = tid & 7, r = (tid >> 3) & 31;
     const int64_t b = (int64_t)blockIdx.x * RQ_BLOCKS + (tid >> 8), row = (int64_t)blockIdx.y * 32 + r;
@@ -109,14 +114,24 @@ __global__ __launch_bounds__(256 * RQ_BLOCKS) void rotate_quantize_kernel(const 
 #pragma unroll
     for (int mask = 1; mask < 8; mask <<= 1) amax = fmaxf(amax, xchg(amax, mask));
 
-    const float d = __fdiv_rn(amax, 7.0f);
+    const float d = __fdiv_rn(amax, (float)QMAX);
     const bool nonzero = d >= 1.17549435e-38f;  // FLT_MIN: zero and subnormal scales give a zero block
     const float id = nonzero ? __fdiv_rn(1.0f, d) : 0.0f;
     const float s = nonzero ? __fmul_rn(d, kInvSqrt32f) : 0.0f;
     int q[4];
 #pragma unroll
     for (int i = 0; i < 4; i++)
-        q[i] = nonzero ? (int)fminf(7.0f, fmaxf(-7.0f, round_half_away(__fmul_rn(v[i], id)))) : 0;
+        q[i] = nonzero ? (int)fminf((float)QMAX, fmaxf(-(float)QMAX, round_half_away(__fmul_rn(v[i], id)))) : 0;
+
+    if constexpr (QMAX == 127) {  // int8 codes: lane L writes elements 4L .. 4L + 3
+        if (live) {
+            const uint32_t word = (uint32_t)(q[0] & 0xFF) | (uint32_t)(q[1] & 0xFF) << 8 |
+                                  (uint32_t)(q[2] & 0xFF) << 16 | (uint32_t)(q[3] & 0xFF) << 24;
+            reinterpret_cast<uint32_t *>(codes + row * k + b * QK)[L] = word;
+            if (L == 0) scales[row * nb + b] = s;
+        }
+        return;
+    }
 
     // public codes: byte j = code j | code j + 16 << 4; lane L < 4 writes bytes 4L .. 4L + 3
     const uint32_t mine = (q[0] & 0xF) | (q[1] & 0xF) << 4 | (q[2] & 0xF) << 8 | (q[3] & 0xF) << 12;

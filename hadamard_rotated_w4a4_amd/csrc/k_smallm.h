@@ -35,11 +35,13 @@ constexpr int SMALL_M_MAX = 16;
 constexpr int SM_WAVES = 8;             // waves per workgroup
 constexpr int SM_DEPTH = 2;             // streaming records in flight per wave
 constexpr int SM_MAX_RANGE = 40;        // records per workgroup (activations staged: 1280 B each)
+constexpr int SM_MAX_RANGE_A8 = 16;     // the same for int8 activations (2304 B each)
 constexpr int SM_ITEM_TARGET = 512;     // workgroups wanted (two per CU on a 256-CU part)
-constexpr int SM_ACT_REC_BYTES = SQ_BLOCKS * (64 * 4 + 16 * 4);  // K8 words + scales of 16 rows
+constexpr int SM_ACT_REC_BYTES = SQ_BLOCKS * (64 * 4 + 16 * 4);    // K8 words + scales of 16 rows
+constexpr int SM_ACT8_REC_BYTES = SQ_BLOCKS * (64 * 8 + 16 * 4);   // int8 codes + scales of 16 rows
 
 struct SmallArgs {
-    const uint8_t *codes;   // activation codes [m][k/2]
+    const uint8_t *codes;   // activation codes [m][k/2] (int8 activations: [m][k])
     const float *scales;    // activation scales [m][k/32]
     const uint8_t *sq;      // streaming section of the packed weights
     float *y;               // [m][ldy] (splits == 1) ...
@@ -55,17 +57,23 @@ struct SmallArgs {
 struct SmallPlan {
     int64_t tiles, splits, range;
 };
-__host__ __device__ inline SmallPlan small_m_plan(int64_t n, int64_t k) {
+__host__ __device__ inline SmallPlan small_m_plan(int64_t n, int64_t k, bool a8 = false) {
     const int64_t tiles = padded_n(n) / TILE_N, nq = sq_quads(k);
-    int64_t splits = (nq + SM_MAX_RANGE - 1) / SM_MAX_RANGE;
+    const int64_t max_range = a8 ? SM_MAX_RANGE_A8 : SM_MAX_RANGE;
+    int64_t splits = (nq + max_range - 1) / max_range;
     const int64_t want = (SM_ITEM_TARGET + tiles - 1) / tiles;
     if (want > splits) splits = want < nq ? want : nq;
     const int64_t range = (nq + splits - 1) / splits;
     return SmallPlan{tiles, (nq + range - 1) / range, range};
 }
-__host__ __device__ inline int64_t small_m_splits(int64_t n, int64_t k) { return small_m_plan(n, k).splits; }
+__host__ __device__ inline int64_t small_m_splits(int64_t n, int64_t k, bool a8 = false) {
+    return small_m_plan(n, k, a8).splits;
+}
 
-template <int WAVES, int DEPTH>
+// A8: int8 activation codes (the exact int8 path on a rotated file): staged
+// as 8-byte K-group entries and fed to the MFMA as they are; the weights still
+// enter as 16 x nibble, so d is scaled by 2^-4.
+template <int WAVES, int DEPTH, bool A8 = false>
 __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -108,35 +116,49 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
     // (at most FILL, addresses clamped into the matrix, out-of-range items
     // zeroed afterwards), then the ring's first records, and only then waits
     // and writes LDS: one cache latency, overlapped with the weights'.
-    constexpr int FILL = SM_MAX_RANGE * SQ_BLOCKS * 16 / (64 * WAVES);
-    static_assert(FILL * 64 * WAVES == SM_MAX_RANGE * SQ_BLOCKS * 16, "whole staging rounds");
+    constexpr int MAX_RANGE = A8 ? SM_MAX_RANGE_A8 : SM_MAX_RANGE;
+    constexpr int FILL = (MAX_RANGE * SQ_BLOCKS * 16 + 64 * WAVES - 1) / (64 * WAVES);
+    constexpr int ROW_BYTES = A8 ? QK : QK / 2;  // activation code bytes per (row, block)
     const int items = nr * SQ_BLOCKS * 16;
-    uint4 fu[FILL];
+    uint4 fu[FILL][A8 ? 2 : 1];
     float fs[FILL];
 #pragma unroll
     for (int t = 0; t < FILL; t++) {
         const int i = min(tid + t * 64 * WAVES, items - 1);
         const int r = min(i & 15, m - 1);
         const int64_t b = min(q_lo * SQ_BLOCKS + (i >> 4), nb - 1);
-        fu[t] = *reinterpret_cast<const uint4 *>(a.codes + (int64_t)r * (k / 2) + b * 16);
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.codes + (int64_t)r * (k / 32 * ROW_BYTES) + b * ROW_BYTES);
+#pragma unroll
+        for (int h = 0; h < (A8 ? 2 : 1); h++) fu[t][h] = src[h];
         fs[t] = a.scales[(int64_t)r * nb + b];
     }
     Rec ring[DEPTH];
 #pragma unroll
     for (int j = 0; j < DEPTH - 1; j++) load(j, ring[j]);
+    // A4: K8 words [block][g][row] (4 B each); A8: 8 codes [block][g][row] (8 B each)
     uint32_t *act = reinterpret_cast<uint32_t *>(smem);
-    float *asc = reinterpret_cast<float *>(smem + nr * SQ_BLOCKS * 256);
+    uint2 *act8 = reinterpret_cast<uint2 *>(smem);
+    float *asc = reinterpret_cast<float *>(smem + nr * SQ_BLOCKS * 64 * (A8 ? 8 : 4));
 #pragma unroll
     for (int t = 0; t < FILL; t++) {
         const int i = tid + t * 64 * WAVES, bl = i >> 4, r = i & 15;
         // rows past m and blocks past nb are zero
         const bool live = r < m && q_lo * SQ_BLOCKS + bl < nb;
-        const uint4 w = k8_words(live ? fu[t] : make_uint4(0, 0, 0, 0));
         if (i < items) {
-            act[bl * 64 + 0 * 16 + r] = w.x;
-            act[bl * 64 + 1 * 16 + r] = w.y;
-            act[bl * 64 + 2 * 16 + r] = w.z;
-            act[bl * 64 + 3 * 16 + r] = w.w;
+            if constexpr (A8) {
+                const uint4 u0 = live ? fu[t][0] : make_uint4(0, 0, 0, 0);
+                const uint4 u1 = live ? fu[t][1] : make_uint4(0, 0, 0, 0);
+                act8[bl * 64 + 0 * 16 + r] = make_uint2(u0.x, u0.y);  // codes 0..7
+                act8[bl * 64 + 1 * 16 + r] = make_uint2(u0.z, u0.w);  // codes 8..15
+                act8[bl * 64 + 2 * 16 + r] = make_uint2(u1.x, u1.y);
+                act8[bl * 64 + 3 * 16 + r] = make_uint2(u1.z, u1.w);
+            } else {
+                const uint4 w = k8_words(live ? fu[t][0] : make_uint4(0, 0, 0, 0));
+                act[bl * 64 + 0 * 16 + r] = w.x;
+                act[bl * 64 + 1 * 16 + r] = w.y;
+                act[bl * 64 + 2 * 16 + r] = w.z;
+                act[bl * 64 + 3 * 16 + r] = w.w;
+            }
             asc[bl * 16 + r] = live ? fs[t] : 0.0f;
         }
     }
@@ -147,13 +169,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
     for (int v = 0; v < 8; v++) acc[v] = 0.0f;
     // One block: two MFMAs (columns c and 16 + c of the tile, all 16 rows),
     // then per output the scale product and a fused multiply-add.
+    constexpr float UNSCALE = A8 ? 1.0f / 16.0f : 1.0f / 256.0f;  // the operands' 16 x factors
     auto block = [&](int bl, uint32_t w0, uint32_t w1, uint32_t dpair) {
-        const long av = widen_k8(act[bl * 64 + lane]);  // row lane % 16, K-group lane / 16
+        long av;  // row lane % 16, K-group lane / 16
+        if constexpr (A8) {
+            const uint2 u = act8[bl * 64 + lane];
+            av = (long)((uint64_t)u.y << 32 | u.x);
+        } else {
+            av = widen_k8(act[bl * 64 + lane]);
+        }
         const v4i S0 = mfma_i8_16x16x32(av, widen_k8(w0));
         const v4i S1 = mfma_i8_16x16x32(av, widen_k8(w1));
         const float4 s4 = *reinterpret_cast<const float4 *>(asc + bl * 16 + 4 * (lane >> 4));
-        const float d0 = __half2float(__ushort_as_half((uint16_t)(dpair & 0xFFFF))) * (1.0f / 256.0f);
-        const float d1 = __half2float(__ushort_as_half((uint16_t)(dpair >> 16))) * (1.0f / 256.0f);
+        const float d0 = __half2float(__ushort_as_half((uint16_t)(dpair & 0xFFFF))) * UNSCALE;
+        const float d1 = __half2float(__ushort_as_half((uint16_t)(dpair >> 16))) * UNSCALE;
         const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -206,8 +235,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
 
 // LDS bytes of one workgroup: the staged activations, or the cross-wave
 // reduction if that is larger.
-__host__ inline size_t small_m_lds_bytes(const SmallPlan &p) {
-    const size_t stage = (size_t)p.range * SM_ACT_REC_BYTES, red = (size_t)SM_WAVES * 8 * 64 * 4;
+__host__ inline size_t small_m_lds_bytes(const SmallPlan &p, bool a8 = false) {
+    const size_t stage = (size_t)p.range * (a8 ? SM_ACT8_REC_BYTES : SM_ACT_REC_BYTES),
+                 red = (size_t)SM_WAVES * 8 * 64 * 4;
     return stage > red ? stage : red;
 }
 

@@ -181,8 +181,9 @@ w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int6
 }
 
 namespace {
-w4a4_status rotate_quantize(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx, uint8_t *codes,
-                            float *scales, void *act, size_t act_bytes, void *stream) {
+// a8: int8 codes ([m][k] bytes) instead of int4 ([m][k/2])
+w4a4_status rotate_quantize(bool a8, const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                            uint8_t *codes, float *scales, void *act, size_t act_bytes, void *stream) {
     if (dt != W4A4_DTYPE_F32 && dt != W4A4_DTYPE_F16) return W4A4_ERR_UNSUPPORTED_DTYPE;
     if (m < 0 || k < 0 || ldx < k || m > kMaxRows) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
@@ -201,26 +202,32 @@ w4a4_status rotate_quantize(const void *x, w4a4_dtype dt, int64_t m, int64_t k, 
     const dim3 grid((unsigned)((blocks + RQ_BLOCKS - 1) / RQ_BLOCKS), (unsigned)((m + 31) / 32));
     hipStream_t s = as_stream(stream);
     uint8_t *a = static_cast<uint8_t *>(act);
-    if (dt == W4A4_DTYPE_F32)
-        rotate_quantize_kernel<float><<<grid, 256 * RQ_BLOCKS, 0, s>>>(static_cast<const float *>(x), m, k, ldx, vec, codes,
-                                                          scales, a);
-    else
-        rotate_quantize_kernel<__half><<<grid, 256 * RQ_BLOCKS, 0, s>>>(static_cast<const __half *>(x), m, k, ldx, vec, codes,
-                                                           scales, a);
+    const float *xf = static_cast<const float *>(x);
+    const __half *xh = static_cast<const __half *>(x);
+    const unsigned nt = 256 * RQ_BLOCKS;
+    if (dt == W4A4_DTYPE_F32 && a8) rotate_quantize_kernel<float, 127><<<grid, nt, 0, s>>>(xf, m, k, ldx, vec, codes, scales, a);
+    else if (dt == W4A4_DTYPE_F32) rotate_quantize_kernel<float, 7><<<grid, nt, 0, s>>>(xf, m, k, ldx, vec, codes, scales, a);
+    else if (a8) rotate_quantize_kernel<__half, 127><<<grid, nt, 0, s>>>(xh, m, k, ldx, vec, codes, scales, a);
+    else rotate_quantize_kernel<__half, 7><<<grid, nt, 0, s>>>(xh, m, k, ldx, vec, codes, scales, a);
     return hip_status("rotate_quantize_kernel");
 }
 }  // namespace
 
 w4a4_status w4a4_rotate_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
                                      uint8_t *codes, float *scales, void *stream) {
-    return rotate_quantize(x, dt, m, k, ldx, codes, scales, nullptr, 0, stream);
+    return rotate_quantize(false, x, dt, m, k, ldx, codes, scales, nullptr, 0, stream);
+}
+
+w4a4_status w4a4_rotate_quantize_act8(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                                      int8_t *codes, float *scales, void *stream) {
+    return rotate_quantize(true, x, dt, m, k, ldx, reinterpret_cast<uint8_t *>(codes), scales, nullptr, 0, stream);
 }
 
 w4a4_status w4a4_rotate_quantize_prepare(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
                                          uint8_t *codes, float *scales, void *act, size_t act_bytes,
                                          void *stream) {
     if (!act && m > 0 && k > 0) return W4A4_ERR_INVALID_VALUE;
-    return rotate_quantize(x, dt, m, k, ldx, codes, scales, act, act_bytes, stream);
+    return rotate_quantize(false, x, dt, m, k, ldx, codes, scales, act, act_bytes, stream);
 }
 
 size_t w4a4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
@@ -277,6 +284,74 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
     const w4a4_status pst = w4a4_gemm_prepare_act(codes, scales, m, k, workspace, workspace_bytes, stream);
     if (pst != W4A4_OK) return pst;
     return w4a4_gemm_prepared(packed_w, workspace, y, m, n, k, ldy, stream);
+}
+
+size_t w4a4_gemm_a8_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+    if (m < 0 || n < 0 || k < 0 || k % QK) return 0;
+    if (n == 0 || k == 0 || m == 0 || m > SMALL_M_MAX) return 0;
+    const int64_t splits = small_m_splits(n, k, true);  // partial sums of the K splits
+    return splits > 1 ? (size_t)((splits * m * n * 4 + 255) / 256 * 256) : 0;
+}
+
+w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float *scales, float *y, int64_t m,
+                         int64_t n, int64_t k, int64_t ldy, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    if (m < 0 || m > kMaxRows || ldy < n) return W4A4_ERR_INVALID_VALUE;
+    if (m == 0 || n == 0) {
+        if (n < 0 || k < 0) return W4A4_ERR_INVALID_VALUE;
+        return k % QK ? W4A4_ERR_K_NOT_MULTIPLE_OF_32 : W4A4_OK;
+    }
+    const uint8_t *c8 = reinterpret_cast<const uint8_t *>(codes);
+    const w4a4_status st = check_gemm_common(packed_w, c8, scales, y, n, k);
+    if (st != W4A4_OK) return st;
+    hipStream_t s = as_stream(stream);
+    if (k == 0) {  // empty sum
+        zero_rows_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(y, m, n, ldy);
+        return hip_status("zero_rows_kernel");
+    }
+    if (m <= SMALL_M_MAX) {
+        const SmallPlan plan = small_m_plan(n, k, true);
+        if (plan.splits > 1) {
+            if (!workspace) return W4A4_ERR_INVALID_VALUE;
+            if (!aligned(workspace, 256)) return W4A4_ERR_MISALIGNED;
+            if (workspace_bytes < w4a4_gemm_a8_workspace_bytes(m, n, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
+        }
+        SmallArgs a{};
+        a.codes = c8;
+        a.scales = scales;
+        a.sq = static_cast<const uint8_t *>(packed_w) + sq_section_offset(n, k);
+        a.y = y;
+        a.partial = plan.splits > 1 ? static_cast<float *>(workspace) : nullptr;
+        a.ldy = ldy;
+        a.m = m;
+        a.n = n;
+        a.k = k;
+        a.range = plan.range;
+        gemm_small_m_kernel<SM_WAVES, SM_DEPTH, true>
+            <<<dim3((unsigned)plan.tiles, (unsigned)plan.splits), 64 * SM_WAVES, small_m_lds_bytes(plan, true), s>>>(a);
+        const w4a4_status st2 = hip_status("gemm_small_m_kernel<a8>");
+        if (st2 != W4A4_OK || plan.splits == 1) return st2;
+        small_m_reduce_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(a.partial, plan.splits, m, n, y, ldy);
+        return hip_status("small_m_reduce_kernel");
+    }
+    // m > 16: the streaming kernel, all rows as one group
+    const int64_t col_chunks = (padded_n(n) / TILE_N + GS_WAVES - 1) / GS_WAVES;
+    const int64_t items = (m + GS_ROWS - 1) / GS_ROWS * col_chunks;
+    if (items + 8 > INT32_MAX) return W4A4_ERR_INVALID_VALUE;
+    GsArgs a{};
+    a.codes = c8;
+    a.scales = scales;
+    a.packed = static_cast<const uint8_t *>(packed_w);
+    a.y = y;
+    a.ldy = ldy;
+    a.n = n;
+    a.k = k;
+    a.dense_rows = m;
+    a.top_k = 1;
+    a.per_slot = 1;
+    a.col_chunks = col_chunks;
+    gemm_grouped_stream_kernel<true><<<(unsigned)((items + 7) / 8 * 8), 64 * GS_WAVES, 0, s>>>(a);
+    return hip_status("gemm_grouped_stream_kernel<a8>");
 }
 
 size_t w4a4_act_operand_bytes(int64_t m, int64_t k) {
@@ -382,14 +457,16 @@ w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *
     a.packed = static_cast<const uint8_t *>(packed_w);
     a.expert_bytes = packed_total_bytes(n, k);
     a.y = y;
+    a.ldy = n;
     a.n = n;
     a.k = k;
+    a.dense_rows = -1;
     a.g = Routing{perm, offsets, tile_prefix, (int)n_expert};
     a.top_k = (int)top_k;
     a.per_slot = act_rows_per_token != 1 ? 1 : 0;
     a.col_chunks = col_chunks;
     // a bound on the items (row tiles x column chunks), rounded up to whole XCD rows
-    gemm_grouped_stream_kernel<<<(unsigned)((row_tiles * col_chunks + 7) / 8 * 8), 64 * GS_WAVES, 0, s>>>(a);
+    gemm_grouped_stream_kernel<false><<<(unsigned)((row_tiles * col_chunks + 7) / 8 * 8), 64 * GS_WAVES, 0, s>>>(a);
     return hip_status("gemm_grouped_stream_kernel");
 }
 

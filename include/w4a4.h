@@ -170,6 +170,31 @@ w4a4_status w4a4_gemm_prepare_act(const uint8_t *codes, const float *scales, int
 w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, int64_t m, int64_t n,
                                int64_t k, int64_t ldy, void *stream);
 
+/*
+ * W4A8-H32: the exact int8 path for a rotated file (section "Hadamard-rotated
+ * Q4_0: W4A4 prompt processing" names it as the alternative to W4A4 for the
+ * same file).  The activations get the same rotation and are rounded to 8
+ * bits per block instead of 4; the weights are the same packed buffer.
+ *
+ * w4a4_rotate_quantize_act8: as w4a4_rotate_quantize_act, but d = amax / 127
+ * and codes clamp(round-half-away(v * (1/d)), -127, 127).
+ *   codes   out, [m][k] int8 (one signed byte per element, element order),
+ *           16-byte aligned.
+ *   scales  out, [m][k/32] fp32, s = d * fp32(1/sqrt(32)).
+ *
+ * w4a4_gemm_a8: y = sum_b d_w * s * S with S the exact integer dot of the
+ * Q4_0 codes (q - 8) with the int8 codes.  Arguments as w4a4_gemm, with the
+ * workspace of w4a4_gemm_a8_workspace_bytes (non-zero only for m <= 16 when
+ * K is split; may be NULL when 0).  m <= 16 streams the weights as w4a4_gemm
+ * does; larger m runs the streaming kernel over 32-row groups.
+ */
+w4a4_status w4a4_rotate_quantize_act8(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                                      int8_t *codes, float *scales, void *stream);
+size_t w4a4_gemm_a8_workspace_bytes(int64_t m, int64_t n, int64_t k);
+w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float *scales, float *y,
+                         int64_t m, int64_t n, int64_t k, int64_t ldy, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 /* Workspace bytes w4a4_gemm_id needs (0 for invalid sizes).  Host only, pure. */
 size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t top_k);
 

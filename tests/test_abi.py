@@ -87,6 +87,27 @@ def test_gemm_validation(L):
     assert g(P(A), P(A), P(A), P(A), 64, 64, 64, 64, P(A), need - 1, None) == WS
 
 
+def test_a8_validation(L):
+    q = L.w4a4_rotate_quantize_act8
+    assert q(P(A), 0, 4, 40, 64, P(A), P(A), None) == KMUL
+    assert q(P(A), 5, 4, 64, 64, P(A), P(A), None) == DTYPE
+    assert q(P(A), 0, 4, 64, 32, P(A), P(A), None) == INVALID  # ldx < k
+    assert q(P(A), 0, 4, 64, 64, P(A + 8), P(A), None) == MISALIGNED
+    assert q(None, 0, 0, 64, 64, None, None, None) == OK
+    g = L.w4a4_gemm_a8
+    assert g(P(A), P(A), P(A), P(A), 8, 64, 40, 64, None, 0, None) == KMUL
+    assert g(P(A), P(A + 8), P(A), P(A), 8, 64, 64, 64, None, 0, None) == MISALIGNED
+    assert g(P(A), P(A), P(A), P(A), 8, 64, 64, 32, None, 0, None) == INVALID  # ldy < n
+    assert g(None, None, None, None, 0, 64, 64, 64, None, 0, None) == OK
+    # m <= 16 with K split needs the partial-sum workspace; m > 16 needs none
+    need = L.w4a4_gemm_a8_workspace_bytes(16, 1024, 5120)
+    assert need > 0 and need % 256 == 0
+    assert L.w4a4_gemm_a8_workspace_bytes(64, 1024, 5120) == 0
+    assert L.w4a4_gemm_a8_workspace_bytes(16, 64, 33) == 0
+    assert g(P(A), P(A), P(A), P(A), 16, 1024, 5120, 1024, None, 0, None) == INVALID
+    assert g(P(A), P(A), P(A), P(A), 16, 1024, 5120, 1024, P(A), need - 1, None) == WS
+
+
 def test_prepared_gemm_validation(L):
     pb = L.w4a4_act_operand_bytes(64, 64)
     assert pb == 2 * 8 * 1024
