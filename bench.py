@@ -249,6 +249,47 @@ def run_moe(torch, ops, synth):
             "hbm_frac": round(tot_bytes / (gemm_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+def run_w4a8(torch, ops, synth):
+    """W4A8-H32 (int8 activation codes on the rotated file): the FFN-up step at
+    M=512 and the gate projection of the 16-token verify block."""
+    dev = torch.device("cuda:0")
+    d = synth.ffn_up()
+    packed = ops.prepare_weights(torch.from_numpy(d.w).to(dev))
+    copies = weight_copies(torch, packed)
+    x = torch.from_numpy(d.x).to(dev)
+    codes = torch.empty((d.m, d.k), dtype=torch.int8, device=dev)
+    scales = torch.empty((d.m, d.k // 32), dtype=torch.float32, device=dev)
+    y = torch.empty((d.m, d.n), dtype=torch.float32, device=dev)
+
+    def step(i):
+        ops.rotate_quantize_act8(x, codes=codes, scales=scales)
+        ops.gemm_a8(copies[i % len(copies)], codes, scales, d.n, d.k, y=y)
+    for i in range(3):
+        step(i)
+    step_us = events_ms(torch, step, 10) * 1e3
+    gemm_us = events_ms(torch, lambda i: ops.gemm_a8(copies[i % len(copies)], codes, scales, d.n, d.k, y=y), 10) * 1e3
+    ops_per = 2.0 * d.m * d.n * d.k
+    # verify block: m=16, gate 5120 -> 17408
+    x16 = x[:16].contiguous()
+    c16, s16 = ops.rotate_quantize_act8(x16)
+    y16 = torch.empty((16, d.n), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, ops.lib().w4a4_gemm_a8_workspace_bytes(16, d.n, d.k)), dtype=torch.uint8, device=dev)
+    nsets = len(copies)
+
+    def one():
+        for i in range(2 * nsets):
+            ops.gemm_a8(copies[i % nsets], c16, s16, d.n, d.k, y=y16, workspace=ws)
+    us16 = graph_time_us(torch, one, inner=2 * nsets)
+    b16 = gemm_bytes(16, d.n, d.k) + 16 * d.k // 2  # int8 codes: twice the int4 bytes
+    return {"ffn_up_m512": {"step_us": round(step_us, 2), "gemm_us": round(gemm_us, 2),
+                            "tokens/s": round(d.m / (step_us * 1e-6), 1),
+                            "TOP/s": round(ops_per / (gemm_us * 1e-6) / 1e12, 1),
+                            "frac_of_int8_peak": round(ops_per / (gemm_us * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4)},
+            "gate_m16": {"us": round(us16, 2), "GB/s": round(b16 / (us16 * 1e-6) / 1e9, 1),
+                         "hbm_frac": round(b16 / (us16 * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+            "timing": "events over back-to-back calls (M=512); HIP graph replay (m=16)"}
+
+
 def run_layer_prompt(torch, ops, synth):
     """Dense layer's seven projections over a 1,838-token prompt (512+512+512+302)."""
     dev = torch.device("cuda:0")
@@ -384,6 +425,9 @@ def main():
         log("[bench] extra: MoE MUL_MAT_ID layer")
         extras["moe"] = run_moe(torch, ops, synth)
         log(f"[bench] moe: {extras['moe']['step_us']} us/step")
+        log("[bench] extra: W4A8-H32 (int8 activations)")
+        extras["w4a8"] = run_w4a8(torch, ops, synth)
+        log(f"[bench] w4a8: {extras['w4a8']['ffn_up_m512']}")
         log("[bench] extra: dense layer set over a 1,838-token prompt")
         extras["layer_prompt_1838"] = run_layer_prompt(torch, ops, synth)
         log(f"[bench] layer: {extras['layer_prompt_1838']['layer_ms']} ms")
