@@ -14,7 +14,7 @@
 // a 2-deep register ring.  Per block and wave: 4 int8 16x16x32 MFMAs (two
 // 16-row halves x columns c and 16 + c), then per output the scale product
 // and a fused multiply-add (codes enter as 16 x nibble, so d is scaled by
-// 2^-8).  K longer than GS_KCHUNK blocks is staged in chunks.  Each
+// 2^-8).  Long K is staged in chunks (gs_kchunk blocks).  Each
 // workgroup scatters its rows to y.  Each XCD takes a contiguous share of
 // the expert-ordered items, so an expert's row tiles share one L2 and read
 // its weights from HBM about once.

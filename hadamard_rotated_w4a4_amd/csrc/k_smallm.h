@@ -79,7 +79,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
     const int64_t k = a.k, nb = k / QK, nq = sq_quads(k);
-    const int64_t tiles = padded_n(a.n) / TILE_N;
     const int64_t tile = blockIdx.x, z = blockIdx.y;
     const int m = (int)a.m;
     const int64_t q_lo = z * a.range;
