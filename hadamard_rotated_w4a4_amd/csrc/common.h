@@ -21,17 +21,17 @@ constexpr int TILE_N = 32;           // columns per packed weight tile (one MFMA
 //
 // Matrix-core section (the m > 16 kernels), at offset 0: [Np/32][nbp][1 KB]
 // with nbp = nb rounded up to MX_BLOCK_PAD.  One 1 KB record per (32-column
-// tile, block), laid out as the MFMA's lanes want it.  Lane l = 32 g + c
-// stands for column c and K half g; it carries codes 16 g .. 16 g + 15 of the
-// column's block (each q - 8) as FP6 E2M3 (code t at bits 6 (t - 16 g) of a
-// 96-bit value; the lane's other 96 operand bits are zero), so the two K
-// halves of one 32x32x64 MFMA together hold the 32 codes once:
-//   bytes [0, 512)     dwords 0..1 of lane l at 8 l;
-//   bytes [512, 768)   dword 2 of lane l at 512 + 4 l (both planes are read
-//                      conflict-free by a wave);
-//   bytes [768, 896)   per column, the bf16 pair (d1, d2) with d1 + d2 =
-//                      64 * d exactly (d the column's fp16 Q4_0 scale);
-//   bytes [896, 1024)  zero.
+// tile, block).  Column c's 32 codes (each q - 8) form one 192-bit MFMA lane
+// operand of FP6 E2M3 fields, code t at bits 6t..6t+5; its six dwords lie in
+// three planes so that 32 lanes read each plane conflict-free:
+//   bytes [0, 768)     dwords 2p, 2p + 1 of column c at 256 p + 8 c (p < 3);
+//   bytes [768, 1024)  4 B at 768 + 4 (32 g + c) (g = 0, 1): the bf16 part d_g
+//                      of 64 * d = d_0 + d_1 (exact; d the column's fp16 Q4_0
+//                      scale) in both halves, so that lane 32 g + c of the
+//                      scale-product MFMA reads its operand as one dword.
+// A 32x32x64 MFMA lane l takes its operand from the record of block b + l/32
+// (lanes 32..63 the next block), so one operand register set carries two
+// blocks; per-lane MX scales select one of them per MFMA.
 // The activation operand built by the GEMM's pre-pass has the same record
 // shape per (32-row tile, block), with a bf16 triple per row at 768.
 __host__ __device__ inline int64_t padded_n(int64_t n) { return (n + TILE_N - 1) / TILE_N * TILE_N; }
@@ -79,20 +79,19 @@ __host__ __device__ inline uint4 k8_words(uint4 u) {
 // 2 (subnormals m / 8, then 1 + m / 8), so |q| itself is the magnitude field.
 __host__ __device__ inline uint32_t fp6_e2m3_of(int q) { return (q < 0 ? 0x20u : 0u) | (uint32_t)(q < 0 ? -q : q); }
 
-// Pack 16 six-bit fields (element j at bits 6j..6j+5) into three dwords.
-__host__ __device__ inline void pack_fp6x16(const uint32_t f[16], uint32_t w[3]) {
-    w[0] = w[1] = w[2] = 0;
-    for (int j = 0; j < 16; j++) {
+// Pack 32 six-bit fields (element j at bits 6j..6j+5) into six dwords.
+__host__ __device__ inline void pack_fp6x32(const uint32_t f[32], uint32_t w[6]) {
+    for (int i = 0; i < 6; i++) w[i] = 0;
+    for (int j = 0; j < 32; j++) {
         const int bit = 6 * j, dw = bit >> 5, off = bit & 31;
         w[dw] |= f[j] << off;
         if (off > 26) w[dw + 1] |= f[j] >> (32 - off);
     }
 }
 
-// Write one lane's three operand dwords into a record (layout above).
-__host__ __device__ inline void put_mx_lane(uint8_t *rec, int lane, const uint32_t w[3]) {
-    reinterpret_cast<uint2 *>(rec)[lane] = make_uint2(w[0], w[1]);
-    reinterpret_cast<uint32_t *>(rec + 512)[lane] = w[2];
+// Write the operand of row / column r (six dwords) into a record (layout above).
+__host__ __device__ inline void put_mx_row(uint8_t *rec, int r, const uint32_t w[6]) {
+    for (int p = 0; p < 3; p++) reinterpret_cast<uint2 *>(rec + 256 * p)[r] = make_uint2(w[2 * p], w[2 * p + 1]);
 }
 
 // 32x32x8 bf16 MFMA: 4 bf16 per lane, lane groups l/32 hold K 0..3 and 4..7.

@@ -9,16 +9,20 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4 with FP6 E2M3 operands: every code q in
 // [-8, 7] is exactly q / 8 in E2M3, each product is exact and every partial
 // sum is a multiple of 1/64 far below 2^24, so the fp32 result is the integer
-// dot S exactly (scaled by 1/64).  Each K half of the instruction carries 16
-// of the block's 32 codes (padded with zeros), so a lane reads 12 bytes of
-// operand per block.  The MFMA hands back fp32, so the epilogue needs no
-// int -> float convert.
+// dot S exactly (scaled by 1/64).  A lane's 32 K values are one whole block
+// (lanes 32..63 the next block), so one operand register set carries two
+// blocks and no zero padding; the MFMA's per-lane E8M0 scales select one
+// block: 1 (byte 127) on its lanes, 2^-127 (byte 0) on the other half, for
+// A and B alike, so the other block's products are scaled by 2^-254 and round
+// away exactly (at most 32 * 2^-254, below half the least fp32 step).  The
+// MFMA hands back fp32, so the epilogue needs no int -> float convert.
 //
 // Per 32x32 tile and block the exact epilogue is one fp32 multiply-add per
 // output, y += (s[m] * d_w[n]) * S.  The scale product P = s (x) d_w is an
 // outer product formed by a bf16 MFMA over exact splits of the scales
-// (s = s1 + s2 + s3, 64 d_w = d1 + d2, all six partial products exact in
-// fp32).  So a tile and block cost two MFMAs and 16 vector multiply-adds per
+// (s = s1 + s2 + s3 on the K slots of each lane group, 64 d_w = d_0 + d_1
+// with lane group g holding d_g in all its slots; all six partial products
+// are exact in fp32).  So a tile and block cost two MFMAs and 16 vector multiply-adds per
 // lane; on gfx950 vector and matrix instructions of one SIMD overlap only
 // partly, and this kernel keeps every other vector instruction out of the
 // loop: operands arrive in the MFMA's register layout (weights repacked
@@ -35,6 +39,34 @@
 namespace w4a4 {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v6i __attribute__((ext_vector_type(6)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// An FP6 operand (six dwords) as the v8i the builtin takes; the last two
+// elements are left undefined (the instruction reads six registers for FP6).
+__device__ __forceinline__ v8i fp6_operand(u32x2 a, u32x2 b, u32x2 c) {
+    const v6i v = {(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y};
+    return __builtin_shufflevector(v, v, 0, 1, 2, 3, 4, 5, -1, -1);
+}
+
+// The register pair {w, w}.  The copy is a byte permute with an identity
+// selector the compiler cannot see through (`id_sel` = 0x03020100 from an
+// opaque move), so it stays next to its use; a plain copy is coalesced into
+// the LDS read of w and makes the wave wait for that read right there.
+__device__ __forceinline__ uint2 dup_at_use(uint32_t w, uint32_t id_sel) {
+    return make_uint2(w, __builtin_amdgcn_perm(w, w, id_sel));
+}
+__device__ __forceinline__ uint32_t opaque_identity_selector() {
+    uint32_t v;
+    asm("v_mov_b32 %0, 0x03020100" : "=v"(v));
+    return v;
+}
+
+// S / 64 of the block on the lanes whose E8M0 scale byte `sel` is 127 (the
+// other half of the lanes gets 0: see the file comment).
+__device__ __forceinline__ v16f mfma_block(v8i a, v8i b, int sel) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, v16f{}, 2, 2, 0, sel, 0, sel);
+}
 
 // ---------------------------------------------------------------------------
 // Activation pre-pass: int4 codes [m][k/2] + fp32 scales [m][k/32] -> operand
@@ -51,21 +83,20 @@ __device__ __forceinline__ void write_act_record(const uint8_t *__restrict__ cod
                                                  const float *__restrict__ scales, int64_t src, int64_t k,
                                                  int64_t b, uint8_t *rec, int r) {
     const int64_t nb = k / QK;
-    uint32_t lo[3] = {0, 0, 0}, hi[3] = {0, 0, 0};
+    uint32_t w[6] = {0, 0, 0, 0, 0, 0};
     uint2 sop = make_uint2(0, 0);
     if (src >= 0 && b < nb) {
         const int64_t row = src;
         const uint4 q = *reinterpret_cast<const uint4 *>(codes + row * (k / 2) + b * 16);
         const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
-        uint32_t f0[16], f1[16];
+        uint32_t f[32];
 #pragma unroll
         for (int j = 0; j < 16; j++) {
             const uint32_t byte = (qw[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-            f0[j] = fp6_e2m3_of(((int)(byte << 28)) >> 28);  // code j: low nibble, two's complement
-            f1[j] = fp6_e2m3_of(((int)(byte << 24)) >> 28);  // code j + 16: high nibble
+            f[j] = fp6_e2m3_of(((int)(byte << 28)) >> 28);       // code j: low nibble, two's complement
+            f[j + 16] = fp6_e2m3_of(((int)(byte << 24)) >> 28);  // code j + 16: high nibble
         }
-        pack_fp6x16(f0, lo);
-        pack_fp6x16(f1, hi);
+        pack_fp6x32(f, w);
         // exact bf16 split s = s1 + s2 + s3 (truncations; each remainder is exact)
         const float s = scales[row * nb + b];
         const uint32_t h1 = __float_as_uint(s) & 0xFFFF0000u;
@@ -75,8 +106,7 @@ __device__ __forceinline__ void write_act_record(const uint8_t *__restrict__ cod
         const uint32_t h3 = __float_as_uint(r2) & 0xFFFF0000u;
         sop = make_uint2((h1 >> 16) | h2, h3 >> 16);
     }
-    put_mx_lane(rec, r, lo);
-    put_mx_lane(rec, 32 + r, hi);
+    put_mx_row(rec, r, w);
     reinterpret_cast<uint2 *>(rec + MX_CODE_BYTES)[r] = sop;
 }
 
@@ -120,17 +150,27 @@ struct MxCfg {
 // merges reads of two different fragments into one instruction (that would
 // scatter a fragment over non-adjacent registers and cost moves and early
 // waits); immediate offsets still fold.
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 template <class T>
 __device__ __forceinline__ T lds_read(const uint8_t *p) {
     return *reinterpret_cast<const volatile __attribute__((address_space(3))) T *>(
         (const __attribute__((address_space(3))) uint8_t *)p);
 }
 
-// One global-to-LDS load of 16 bytes per lane: lane l's bytes at `g` land at
-// LDS byte address lds + 16 l (lds is wave-uniform, passed through M0).
-__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+// One global-to-LDS load of 16 bytes per lane: lane l's bytes at sbase +
+// voff land at LDS byte address lds + 16 l (lds is wave-uniform, passed
+// through M0).  The base is wave-uniform (SGPRs) and voff a per-lane 32-bit
+// byte offset, so no 64-bit vector address arithmetic is needed per load.
+__device__ __forceinline__ void dma16s(const uint8_t *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds) : "memory");
+}
+
+// A wave-uniform pointer, placed in SGPRs.  (The builtin returns a signed
+// int: each half is widened through uint32_t, never sign-extended.)
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint8_t *)(uintptr_t)((uint64_t)hi << 32 | (uint64_t)lo);
 }
 
 // Workgroup tile of index id in an XCD-aware order.  Workgroups are dealt to
@@ -173,21 +213,23 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
         const int i = wave * C::DMA_PER_WAVE + d, t = i / BKB, bb = i % BKB;
         const uint8_t *base = t < RT ? a.act + min(rt0 + t, rtiles - 1) * nbp * MX_REC
                                      : a.wrec + min(ct0 + t - RT, ctiles - 1) * nbp * MX_REC;
-        src[d] = base + bb * MX_REC + lane * 16;
+        src[d] = uniform_ptr(base + bb * MX_REC);
         dst[d] = (uint32_t)((t * BKB + bb) * MX_REC);
     }
+    const uint32_t voff = lane * 16;
     const int nstages = (int)(nbp / BKB);
-    auto issue = [&](int stage, int slot) {
-        // past the last stage the ring keeps reloading the last one (its
-        // slot is never computed): the count of loads in flight stays fixed
+    // Load d of stage `stage` into ring slot `slot`.  Past the last stage
+    // the ring keeps reloading the last one (its slot is never computed): the
+    // count of loads in flight stays fixed.
+    auto issue_one = [&](int stage, int slot, int d) {
         const int64_t kb0 = (int64_t)min(stage, nstages - 1) * BKB;
         const uint32_t lds = __builtin_amdgcn_readfirstlane(smem_base + slot * C::STAGE_BYTES);
-#pragma unroll
-        for (int d = 0; d < C::DMA_PER_WAVE; d++) dma16(src[d] + kb0 * MX_REC, lds + dst[d]);
+        dma16s(src[d] + kb0 * MX_REC, voff, lds + dst[d]);
     };
-
-    // scale-product operand of the weights: lane group g reads {d_g, d_g, d_g, 0}
-    const uint32_t sel0 = g ? 0x03020302u : 0x01000100u, sel1 = g ? 0x0C0C0302u : 0x0C0C0100u;
+    auto issue = [&](int stage, int slot) {
+#pragma unroll
+        for (int d = 0; d < C::DMA_PER_WAVE; d++) issue_one(stage, slot, d);
+    };
 
     v16f acc[TM][TN];
 #pragma unroll
@@ -198,48 +240,55 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
     // ---- one software pipeline over all blocks ----
-    // Step t of a stage = (block t / PER, tile t % PER).  The two MFMAs of
-    // step t + 1 are issued around the first half of step t's multiply-adds;
-    // the operands of the next block are read while the current one computes
-    // (the weights' scale word is expanded only where it is used, so nothing
-    // waits for those reads early).  The wait + barrier that publishes stage
-    // s + 1 sits at the start of stage s's last block, so the pipeline never
-    // drains at a stage boundary.
-    static_assert(BKB % 2 == 0, "operand buffers alternate per block");
+    // A stage is two blocks; one operand register set per row / column tile
+    // carries both (lanes 0..31 block 0, lanes 32..63 block 1).  Step t of a
+    // stage = (block t / PER, tile t % PER); the two MFMAs of step t + 1 are
+    // issued around the halves of step t's multiply-adds.  At step BAR of
+    // stage s the wait + barrier publish stage s + 1 and the slot of stage
+    // s - 1 (read during stage s - 2) is refilled; stage s + 1's operands are
+    // then read into the other register set one tile per step, in the order
+    // of first use, so that no burst of LDS reads stalls the wave and every
+    // read has several steps to land.  The pipeline never drains at a stage
+    // boundary.
+    static_assert(BKB == 2, "one operand register set carries a stage's two blocks");
     static_assert(NS >= 3, "one stage in flight besides the two in use");
     constexpr int STEPS = BKB * TM * TN, PER = TM * TN;
-    v8i af[2][TM] = {}, bf[2][TN] = {};  // operand dwords 3..7 are zero
-    uint2 ap[2][TM];
-    uint32_t bw[2][TN];
-    auto load_frags = [&](const uint8_t *st, int bb, int buf) {
+    constexpr int BAR = STEPS - (TM + TN) < 2 ? STEPS - (TM + TN) : 2;  // step of the barrier
+    static_assert(BAR >= 0, "a stage's steps cover its operand reads");
+    static_assert(BAR + C::DMA_PER_WAVE <= STEPS, "a stage's steps cover its loads");
+    v8i af[2][TM], bf[2][TN];
+    uint2 ap[2][BKB][TM];
+    uint32_t bw[2][BKB][TN];
+    const int sel[BKB] = {g ? 0 : 127, g ? 127 : 0};  // E8M0 lane masks of blocks 0 and 1
+    const uint32_t id_sel = opaque_identity_selector();
+    // Operand reads of one row tile (i) or column tile (j) of a stage.
+    auto load_a = [&](const uint8_t *st, int buf, int i) {
+        const uint8_t *rec = st + (wm * TM + i) * BKB * MX_REC, *p = rec + g * MX_REC + 8 * c;
+        af[buf][i] = fp6_operand(lds_read<u32x2>(p), lds_read<u32x2>(p + 256), lds_read<u32x2>(p + 512));
 #pragma unroll
-        for (int i = 0; i < TM; i++) {
-            const uint8_t *rec = st + ((wm * TM + i) * BKB + bb) * MX_REC;
-            const u32x2 f01 = lds_read<u32x2>(rec + 8 * lane);
-            const uint32_t f2 = lds_read<uint32_t>(rec + 512 + 4 * lane);
-            af[buf][i][0] = (int)f01.x;  // elements 3..7 stay zero
-            af[buf][i][1] = (int)f01.y;
-            af[buf][i][2] = (int)f2;
-            const u32x2 sp = lds_read<u32x2>(rec + MX_CODE_BYTES + 8 * c);
-            ap[buf][i] = make_uint2(sp.x, sp.y);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; j++) {
-            const uint8_t *rec = st + ((RT + wn * TN + j) * BKB + bb) * MX_REC;
-            const u32x2 f01 = lds_read<u32x2>(rec + 8 * lane);
-            const uint32_t f2 = lds_read<uint32_t>(rec + 512 + 4 * lane);
-            bf[buf][j][0] = (int)f01.x;
-            bf[buf][j][1] = (int)f01.y;
-            bf[buf][j][2] = (int)f2;
-            bw[buf][j] = lds_read<uint32_t>(rec + MX_CODE_BYTES + 4 * c);
+        for (int bb = 0; bb < BKB; bb++) {
+            const u32x2 sp = lds_read<u32x2>(rec + bb * MX_REC + MX_CODE_BYTES + 8 * c);
+            ap[buf][bb][i] = make_uint2(sp.x, sp.y);
         }
     };
-    auto mfma_s = [&](int buf, int i, int j) {
-        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[buf][i], bf[buf][j], v16f{}, 2, 2, 0, 0, 0, 0);
+    auto load_b = [&](const uint8_t *st, int buf, int j) {
+        const uint8_t *rec = st + (RT + wn * TN + j) * BKB * MX_REC, *p = rec + g * MX_REC + 8 * c;
+        bf[buf][j] = fp6_operand(lds_read<u32x2>(p), lds_read<u32x2>(p + 256), lds_read<u32x2>(p + 512));
+#pragma unroll
+        for (int bb = 0; bb < BKB; bb++) bw[buf][bb][j] = lds_read<uint32_t>(rec + bb * MX_REC + MX_CODE_BYTES + 4 * lane);
     };
-    auto mfma_p = [&](int buf, int i, int j) {
-        const uint32_t w = bw[buf][j];
-        return mfma_bf16_32x32x8(ap[buf][i], make_uint2(__builtin_amdgcn_perm(w, w, sel0), __builtin_amdgcn_perm(w, w, sel1)));
+    // Part p of a stage's operands, in the order the stage's steps first use
+    // them (steps run j fastest): A 0, B 0, the other B tiles, the other A tiles.
+    constexpr int PARTS = TM + TN;
+    auto load_part = [&](const uint8_t *st, int buf, int p) {
+        if (p == 0) load_a(st, buf, 0);
+        else if (p <= TN) load_b(st, buf, p - 1);
+        else load_a(st, buf, p - TN);
+    };
+    auto mfma_s = [&](int buf, int bb, int i, int j) { return mfma_block(af[buf][i], bf[buf][j], sel[bb]); };
+    auto mfma_p = [&](int buf, int bb, int i, int j) {
+        // lane group g: K slots {s1, s2, s3, 0} against {d_g, d_g, d_g, d_g}
+        return mfma_bf16_32x32x8(ap[buf][bb][i], dup_at_use(bw[buf][bb][j], id_sel));
     };
 
 #pragma unroll
@@ -247,39 +296,45 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 2)) : "memory");
     __syncthreads();
     v16f S[2], P[2];
-    load_frags(smem, 0, 0);
-    S[0] = mfma_s(0, 0, 0);
-    P[0] = mfma_p(0, 0, 0);
-
-    for (int s = 0; s < nstages; s++) {
-        const uint8_t *st = smem + (s % NS) * C::STAGE_BYTES;
 #pragma unroll
-        for (int t = 0; t < STEPS; t++) {
-            const int bb = t / PER, i = (t / TN) % TM, j = t % TN;
-            if (t % PER == 0) {
-                if (bb + 1 < BKB) {
-                    load_frags(st, bb + 1, (bb + 1) & 1);
-                } else {
+    for (int p = 0; p < PARTS; p++) load_part(smem, 0, p);
+    S[0] = mfma_s(0, 0, 0, 0);
+    P[0] = mfma_p(0, 0, 0, 0);
+
+    // stages in pairs, so that the operand register set of each is fixed at
+    // compile time (the stage count is a multiple of MX_BLOCK_PAD / BKB)
+    static_assert((MX_BLOCK_PAD / BKB) % 2 == 0, "even stage count");
+    for (int s0 = 0; s0 < nstages; s0 += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int s = s0 + u;
+#pragma unroll
+            for (int t = 0; t < STEPS; t++) {
+                const int i = (t / TN) % TM, j = t % TN;
+                if (t == BAR) {
                     // stage s + 1 has landed for this wave; after the barrier
-                    // for every wave, and stage s - 1's slot is no longer read.
-                    // (After the last stage this reads a reloaded stage; the
-                    // MFMAs it feeds are never consumed.)
+                    // for every wave, and stage s - 1's slot is free.  (After
+                    // the last stage the reads below see a reloaded stage; the
+                    // MFMAs they feed are never consumed.)
                     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 3)) : "memory");
                     __syncthreads();
-                    issue(s + NS - 1, (s + NS - 1) % NS);
-                    load_frags(smem + ((s + 1) % NS) * C::STAGE_BYTES, 0, 0);
                 }
+                // refill stage s - 1's slot, one load per step (a burst of them
+                // stalls the issue while every wave of the CU does the same)
+                if (t >= BAR && t - BAR < C::DMA_PER_WAVE) issue_one(s + NS - 1, (s + NS - 1) % NS, t - BAR);
+                if (t >= BAR && t - BAR < PARTS) load_part(smem + ((s + 1) % NS) * C::STAGE_BYTES, u ^ 1, t - BAR);
+                const int t1 = (t + 1) % STEPS, buf1 = t1 == 0 ? u ^ 1 : u;
+                const int b1 = t1 / PER, i1 = (t1 / TN) % TM, j1 = t1 % TN;
+                S[(t + 1) & 1] = mfma_s(buf1, b1, i1, j1);
+#pragma unroll
+                for (int v = 0; v < 8; v++) acc[i][j][v] = fmaf(S[t & 1][v], P[t & 1][v], acc[i][j][v]);
+                __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);  // scalar and global-to-LDS ops may move; LDS reads stay in their step
+                P[(t + 1) & 1] = mfma_p(buf1, b1, i1, j1);
+#pragma unroll
+                for (int v = 8; v < 16; v++) acc[i][j][v] = fmaf(S[t & 1][v], P[t & 1][v], acc[i][j][v]);
+                asm volatile("" : "+v"(acc[i][j]));  // materialised here, not sunk past the loop's end
+                __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);  // scalar and global-to-LDS ops may move; LDS reads stay in their step
             }
-            const int t1 = (t + 1) % STEPS, b1 = (t1 / PER) & 1, i1 = (t1 / TN) % TM, j1 = t1 % TN;
-            S[(t + 1) & 1] = mfma_s(b1, i1, j1);
-#pragma unroll
-            for (int v = 0; v < 8; v++) acc[i][j][v] = fmaf(S[t & 1][v], P[t & 1][v], acc[i][j][v]);
-            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
-            P[(t + 1) & 1] = mfma_p(b1, i1, j1);
-#pragma unroll
-            for (int v = 8; v < 16; v++) acc[i][j][v] = fmaf(S[t & 1][v], P[t & 1][v], acc[i][j][v]);
-            asm volatile("" : "+v"(acc[i][j]));  // materialised here, not sunk past the loop's end
-            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still be writing LDS at exit
@@ -314,7 +369,7 @@ struct MxPieceCfg {
     static constexpr int BM = BM_, BN = BN_;                 // tile shape of the main kernel
     static constexpr int PIECES = (BM / 32) * (BN / 32);     // 32x32 pieces per leftover tile
     static constexpr int BKB = 2, NS = 4, NT = 256;          // per wave: NS stages of BKB blocks
-    static constexpr int WAVE_RING = NS * BKB * 2 * MX_REC;  // A and B record per block
+    static constexpr int WAVE_RING = NS * BKB * 2 * MX_REC;  // per stage: A records of its blocks, then B's
 };
 
 template <class C>
@@ -332,8 +387,8 @@ __device__ __forceinline__ void mx_piece(const MxArgs &a, int64_t first_tile, in
     const int sub = (int)(id % C::PIECES);
     const int64_t rt = by * (C::BM / 32) + sub / (C::BN / 32), ct = bx * (C::BN / 32) + sub % (C::BN / 32);
     // pieces past the matrix edge compute on clamped tiles and store nothing
-    const uint8_t *arec = a.act + min(rt, rtiles - 1) * nbp * MX_REC;
-    const uint8_t *brec = a.wrec + min(ct, ctiles - 1) * nbp * MX_REC;
+    const uint8_t *arec = uniform_ptr(a.act + min(rt, rtiles - 1) * nbp * MX_REC);
+    const uint8_t *brec = uniform_ptr(a.wrec + min(ct, ctiles - 1) * nbp * MX_REC);
 
     // this wave's quarter of the blocks, in whole stages
     const int64_t nstages_all = nbp / BKB;
@@ -342,60 +397,70 @@ __device__ __forceinline__ void mx_piece(const MxArgs &a, int64_t first_tile, in
     uint8_t *ring = smem + wave * C::WAVE_RING;
     const uint32_t ring_lds =
         __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)ring);
+    const uint32_t voff = lane * 16;
     auto issue = [&](int stage, int slot) {
         // past the last stage the ring reloads the last one (never computed)
         const int64_t kb0 = (s_begin + min(stage, max(nst - 1, 0))) * BKB;
         const uint32_t lds = ring_lds + slot * BKB * 2 * MX_REC;
 #pragma unroll
         for (int bb = 0; bb < BKB; bb++) {
-            dma16(arec + (kb0 + bb) * MX_REC + lane * 16, lds + (2 * bb) * MX_REC);
-            dma16(brec + (kb0 + bb) * MX_REC + lane * 16, lds + (2 * bb + 1) * MX_REC);
+            dma16s(arec + (kb0 + bb) * MX_REC, voff, lds + bb * MX_REC);
+            dma16s(brec + (kb0 + bb) * MX_REC, voff, lds + (BKB + bb) * MX_REC);
         }
     };
-    const uint32_t sel0 = g ? 0x03020302u : 0x01000100u, sel1 = g ? 0x0C0C0302u : 0x0C0C0100u;
+    const int sel[BKB] = {g ? 0 : 127, g ? 127 : 0};  // E8M0 lane masks of blocks 0 and 1
+    const uint32_t id_sel = opaque_identity_selector();
+    static_assert(BKB == 2, "one operand register set carries a stage's two blocks");
 
     v16f acc;
 #pragma unroll
     for (int v = 0; v < 16; v++) acc[v] = 0.0f;
-    // Pipeline: the two MFMAs of block bb + 1 are issued before the
-    // multiply-adds of block bb (one tile per wave leaves nothing else to
-    // cover the MFMA latency).
-    auto mfmas = [&](const uint8_t *st, int bb, v16f &S, v16f &P) {
-        const uint8_t *ra = st + (2 * bb) * MX_REC, *rb = st + (2 * bb + 1) * MX_REC;
-        v8i af = {}, bf = {};  // operand dwords 3..7 are zero
-        const u32x2 a01 = lds_read<u32x2>(ra + 8 * lane), b01 = lds_read<u32x2>(rb + 8 * lane);
-        af[0] = (int)a01.x; af[1] = (int)a01.y; af[2] = (int)lds_read<uint32_t>(ra + 512 + 4 * lane);
-        bf[0] = (int)b01.x; bf[1] = (int)b01.y; bf[2] = (int)lds_read<uint32_t>(rb + 512 + 4 * lane);
-        const u32x2 sp = lds_read<u32x2>(ra + MX_CODE_BYTES + 8 * c);
-        const uint32_t w = lds_read<uint32_t>(rb + MX_CODE_BYTES + 4 * c);
-        S = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, v16f{}, 2, 2, 0, 0, 0, 0);
-        P = mfma_bf16_32x32x8(make_uint2(sp.x, sp.y),
-                              make_uint2(__builtin_amdgcn_perm(w, w, sel0), __builtin_amdgcn_perm(w, w, sel1)));
+    // The operands of a stage (both blocks) are read at once; the two MFMAs
+    // of the next block are issued before the multiply-adds of the current
+    // one (one tile per wave leaves nothing else to cover their latency).
+    v8i af, bf;
+    uint2 ap[BKB];
+    uint32_t bw[BKB];
+    auto load = [&](const uint8_t *st) {
+        const uint8_t *pa = st + g * MX_REC + 8 * c, *pb = st + (BKB + g) * MX_REC + 8 * c;
+        af = fp6_operand(lds_read<u32x2>(pa), lds_read<u32x2>(pa + 256), lds_read<u32x2>(pa + 512));
+        bf = fp6_operand(lds_read<u32x2>(pb), lds_read<u32x2>(pb + 256), lds_read<u32x2>(pb + 512));
+#pragma unroll
+        for (int bb = 0; bb < BKB; bb++) {
+            const u32x2 sp = lds_read<u32x2>(st + bb * MX_REC + MX_CODE_BYTES + 8 * c);
+            ap[bb] = make_uint2(sp.x, sp.y);
+            bw[bb] = lds_read<uint32_t>(st + (BKB + bb) * MX_REC + MX_CODE_BYTES + 4 * lane);
+        }
+    };
+    auto mfmas = [&](int bb, v16f &S, v16f &P) {
+        S = mfma_block(af, bf, sel[bb]);
+        P = mfma_bf16_32x32x8(ap[bb], dup_at_use(bw[bb], id_sel));
     };
     if (nst > 0) {
 #pragma unroll
         for (int x = 0; x < NS - 1; x++) issue(x, x);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * BKB * (NS - 2)) : "memory");  // stage 0 has landed
         v16f S[2], P[2];
-        mfmas(ring, 0, S[0], P[0]);
+        load(ring);
+        mfmas(0, S[0], P[0]);
         for (int s = 0; s < nst; s++) {
-            const uint8_t *st = ring + (s % NS) * BKB * 2 * MX_REC;
+            // block 1 of stage s
+            mfmas(1, S[1], P[1]);
 #pragma unroll
-            for (int bb = 0; bb < BKB; bb++) {
-                if (bb + 1 < BKB) {
-                    mfmas(st, bb + 1, S[(bb + 1) & 1], P[(bb + 1) & 1]);
-                } else {
-                    // next stage: refill the slot computed last, wait for stage s + 1
-                    // (after the last stage this reads a reloaded stage; unused)
-                    issue(s + NS - 1, (s + NS - 1) % NS);
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * BKB * (NS - 2)) : "memory");
-                    mfmas(ring + ((s + 1) % NS) * BKB * 2 * MX_REC, 0, S[(bb + 1) & 1], P[(bb + 1) & 1]);
-                }
+            for (int v = 0; v < 16; v++) acc[v] = fmaf(S[0][v], P[0][v], acc[v]);
+            asm volatile("" : "+v"(acc));
+            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
+            // next stage: refill the slot computed last, wait for stage s + 1
+            // and read its operands (after the last stage this reads a
+            // reloaded stage; unused)
+            issue(s + NS - 1, (s + NS - 1) % NS);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * BKB * (NS - 2)) : "memory");
+            load(ring + ((s + 1) % NS) * BKB * 2 * MX_REC);
+            mfmas(0, S[0], P[0]);
 #pragma unroll
-                for (int v = 0; v < 16; v++) acc[v] = fmaf(S[bb & 1][v], P[bb & 1][v], acc[v]);
-                asm volatile("" : "+v"(acc));
-                __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
-            }
+            for (int v = 0; v < 16; v++) acc[v] = fmaf(S[1][v], P[1][v], acc[v]);
+            asm volatile("" : "+v"(acc));
+            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still be writing the ring
     }

@@ -72,28 +72,28 @@ __global__ __launch_bounds__(256) void repack_mx_kernel(const uint8_t *__restric
     const int64_t tb = gid >> 5;  // tile * nbp + b
     const int64_t tile = tb / nbp, b = tb % nbp;
     const int64_t col = tile * TILE_N + c;
-    uint32_t lo[3] = {0, 0, 0}, hi[3] = {0, 0, 0};
-    uint32_t sw = 0;
+    uint32_t w[6] = {0, 0, 0, 0, 0, 0};
+    uint32_t sw0 = 0, sw1 = 0;
     if (col < n && b < nb) {
         const uint8_t *blk = q4 + (col * nb + b) * 18;
-        uint32_t f0[16], f1[16];
+        uint32_t f[32];
         for (int j = 0; j < 16; j++) {
-            f0[j] = fp6_e2m3_of((int)(blk[2 + j] & 0xF) - 8);   // code j
-            f1[j] = fp6_e2m3_of((int)(blk[2 + j] >> 4) - 8);    // code j + 16
+            f[j] = fp6_e2m3_of((int)(blk[2 + j] & 0xF) - 8);        // code j
+            f[j + 16] = fp6_e2m3_of((int)(blk[2 + j] >> 4) - 8);    // code j + 16
         }
-        pack_fp6x16(f0, lo);
-        pack_fp6x16(f1, hi);
+        pack_fp6x32(f, w);
         // 64 * d: the MFMA reads codes as q / 8
         const float d = __half2float(__ushort_as_half((uint16_t)(blk[0] | (blk[1] << 8)))) * 64.0f;
         const uint32_t h1 = __float_as_uint(d) & 0xFFFF0000u;
         const float r1 = __fsub_rn(d, __uint_as_float(h1));  // exact: at most 3 significant bits remain
-        sw = (h1 >> 16) | (__float_as_uint(r1) & 0xFFFF0000u);
+        const uint32_t h2 = __float_as_uint(r1) & 0xFFFF0000u;
+        sw0 = h1 | (h1 >> 16);
+        sw1 = h2 | (h2 >> 16);
     }
     uint8_t *rec = packed + tb * MX_REC;
-    put_mx_lane(rec, c, lo);
-    put_mx_lane(rec, 32 + c, hi);
-    reinterpret_cast<uint32_t *>(rec + MX_CODE_BYTES)[c] = sw;
-    reinterpret_cast<uint32_t *>(rec + MX_CODE_BYTES + 128)[c] = 0u;
+    put_mx_row(rec, c, w);
+    reinterpret_cast<uint32_t *>(rec + MX_CODE_BYTES)[c] = sw0;
+    reinterpret_cast<uint32_t *>(rec + MX_CODE_BYTES)[32 + c] = sw1;
 }
 
 // Streaming records (see common.h), one thread per (tile, padded block,

@@ -147,20 +147,18 @@ __global__ __launch_bounds__(256 * RQ_BLOCKS) void rotate_quantize_kernel(const 
     }
 
     if (act && b < mx_blocks(k)) {
-        // operand record of (row tile, block): lane (g, r) holds codes 16 g ..
-        // 16 g + 15 as fp6 fields; this thread's four codes are 24 bits at
-        // bit 24 (L % 4) of group g = L / 4's 96-bit value
+        // operand record of (row tile, block): row r's 32 codes are one 192-bit
+        // string of fp6 fields; this thread's four codes are its 24 bits at
+        // bit 24 L.  Lanes 0, 3 and 6 write the planes (bits 64 p .. 64 p + 63).
         uint32_t f24 = 0;
 #pragma unroll
         for (int i = 0; i < 4; i++) f24 |= fp6_e2m3_of(live ? q[i] : 0) << (6 * i);
-        const uint32_t x1 = xchg(f24, 1), x2 = xchg(f24, 2), x3 = xchg(f24, 3);  // from L + 1, L + 2, L + 3
+        const uint32_t n1 = (uint32_t)__shfl_down((int)f24, 1, 8), n2 = (uint32_t)__shfl_down((int)f24, 2, 8);
+        const uint32_t p1 = (uint32_t)__shfl_up((int)f24, 1, 8);  // lanes L + 1, L + 2, L - 1
         uint8_t *rec = act + ((int64_t)blockIdx.y * mx_blocks(k) + b) * MX_REC;
-        if ((L & 3) == 0) {
-            const int lane = (L >> 2) * 32 + r;
-            const uint32_t w0 = f24 | x1 << 24, w1 = x1 >> 8 | x2 << 16, w2 = x2 >> 16 | x3 << 8;
-            reinterpret_cast<uint2 *>(rec)[lane] = make_uint2(w0, w1);
-            reinterpret_cast<uint32_t *>(rec + 512)[lane] = w2;
-        }
+        if (L == 0) reinterpret_cast<uint2 *>(rec)[r] = make_uint2(f24 | n1 << 24, n1 >> 8 | n2 << 16);
+        if (L == 3) reinterpret_cast<uint2 *>(rec + 256)[r] = make_uint2(p1 >> 16 | f24 << 8, n1 | n2 << 24);
+        if (L == 6) reinterpret_cast<uint2 *>(rec + 512)[r] = make_uint2(p1 >> 8 | f24 << 16, f24 >> 16 | n1 << 8);
         if (L == 0) {
             // exact bf16 split s = s1 + s2 + s3 (truncations; each remainder is exact)
             const float sl = live ? s : 0.0f;
