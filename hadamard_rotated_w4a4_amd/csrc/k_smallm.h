@@ -8,23 +8,23 @@
 //
 // Work split: a workgroup owns one 32-column weight tile and a contiguous
 // range of K (split z of the tile's streaming records, 4 blocks each; narrow
-// projections split K so that every CU gets workgroups).  At the start it
-// stages the range's activations in LDS: per block, the 16 rows' codes as K8
-// words (the weights' order, see common.h) and the rows' fp32 scales.  Its
-// waves then take the range's records round-robin and stream them straight
-// into registers through a ring SM_DEPTH records deep (a wave's weight bytes
-// are its own, so they need no LDS).  Per block and wave: two 16x16x32 int8
-// MFMAs (columns c and 16 + c of the tile, all 16 rows), then per output a
-// convert, the scale product s * d and a fused multiply-add.  Codes enter the
-// MFMA as 16 x (signed nibble), so the integer sum is 256 S, and d is scaled
-// by 2^-8 (exact) to match.  The waves' sums meet in LDS; the workgroup
-// stores its 16 x 32 outputs, or its partial sums when K is split (a second
-// kernel adds the splits in ascending order).
+// projections split K so that every CU gets workgroups).  Its waves take the
+// range's records round-robin and stream them straight into registers
+// through a ring SM_DEPTH records deep, each record together with its 16
+// rows' activation codes and scales (one 16-byte and one 4-byte load per
+// lane).  A record's activations are needed by its wave alone: the wave
+// moves them through its own LDS slot into the MFMA's lane order just before
+// computing the record, so no workgroup-wide staging phase or barrier
+// precedes the stream.  Per block and wave: two 16x16x32 int8 MFMAs (columns
+// c and 16 + c of the tile, all 16 rows), then per output a convert, the
+// scale product s * d and a fused multiply-add.  Codes enter the MFMA as
+// 16 x (signed nibble), so the integer sum is 256 S, and d is scaled by 2^-8
+// (exact) to match.  The waves' sums meet in LDS; the workgroup stores its
+// 16 x 32 outputs, or its partial sums when K is split (a second kernel adds
+// the splits in ascending order).
 //
 // Measured on MI355X (7 dense projections of a 27B-class layer, 16 rows):
-// 8 waves per workgroup and a 2-record ring beat 4 waves or deeper rings;
-// sharing one staged activation range across 2 or 4 tiles per workgroup was
-// slower (fewer workgroups, more K splits).
+// 8 waves per workgroup and a 2-record ring beat 4 waves or deeper rings.
 #pragma once
 
 #include "common.h"
@@ -34,11 +34,7 @@ namespace w4a4 {
 constexpr int SMALL_M_MAX = 16;
 constexpr int SM_WAVES = 8;             // waves per workgroup
 constexpr int SM_DEPTH = 2;             // streaming records in flight per wave
-constexpr int SM_MAX_RANGE = 40;        // records per workgroup (activations staged: 1280 B each)
-constexpr int SM_MAX_RANGE_A8 = 16;     // the same for int8 activations (2304 B each)
 constexpr int SM_ITEM_TARGET = 512;     // workgroups wanted (two per CU on a 256-CU part)
-constexpr int SM_ACT_REC_BYTES = SQ_BLOCKS * (64 * 4 + 16 * 4);    // K8 words + scales of 16 rows
-constexpr int SM_ACT8_REC_BYTES = SQ_BLOCKS * (64 * 8 + 16 * 4);   // int8 codes + scales of 16 rows
 
 struct SmallArgs {
     const uint8_t *codes;   // activation codes [m][k/2] (int8 activations: [m][k])
@@ -50,19 +46,17 @@ struct SmallArgs {
     int64_t range;          // records per split
 };
 
-// Launch plan of an m <= 16 product: the K splits.  A workgroup's staged
-// activation range must fit its LDS share, and narrow projections split
-// further so that about SM_ITEM_TARGET workgroups run.  Pure function of the
-// sizes (the workspace size depends on it).
+// Launch plan of an m <= 16 product: the K splits.  Narrow projections split
+// K so that about SM_ITEM_TARGET workgroups run.  Pure function of the sizes
+// (the workspace size depends on it).
 struct SmallPlan {
     int64_t tiles, splits, range;
 };
 __host__ __device__ inline SmallPlan small_m_plan(int64_t n, int64_t k, bool a8 = false) {
+    (void)a8;
     const int64_t tiles = padded_n(n) / TILE_N, nq = sq_quads(k);
-    const int64_t max_range = a8 ? SM_MAX_RANGE_A8 : SM_MAX_RANGE;
-    int64_t splits = (nq + max_range - 1) / max_range;
     const int64_t want = (SM_ITEM_TARGET + tiles - 1) / tiles;
-    if (want > splits) splits = want < nq ? want : nq;
+    const int64_t splits = want < nq ? want : nq;
     const int64_t range = (nq + splits - 1) / splits;
     return SmallPlan{tiles, (nq + range - 1) / range, range};
 }
@@ -86,82 +80,77 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
 
     // this wave's records: local index wave, wave + WAVES, ...
     const int cnt = nr > wave ? (nr - wave + WAVES - 1) / WAVES : 0;
-    // Buffer loads over this split's records: the record offset is scalar and
-    // the lane offset a fixed register, so no address arithmetic touches the
-    // registers that loads are still filling (the hardware also range-checks
-    // every load against the split's bytes).
+    // Buffer loads: record offsets are scalar or fixed per lane, so no
+    // address arithmetic touches the registers that loads are still filling;
+    // the hardware range-checks every load (bytes past a buffer read zero).
+    constexpr int CFG = 0x00020000;
     const __amdgpu_buffer_rsrc_t wbuf = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(a.sq + (tile * nq + q_lo) * SQ_REC), 0, nr * SQ_REC, 0x00020000);
+        const_cast<uint8_t *>(a.sq + (tile * nq + q_lo) * SQ_REC), 0, nr * SQ_REC, CFG);
+    constexpr int ROW_BYTES = A8 ? QK : QK / 2;  // activation code bytes per (row, block)
+    const __amdgpu_buffer_rsrc_t cbuf = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(a.codes), 0, (int)(m * nb * ROW_BYTES), CFG);
+    const __amdgpu_buffer_rsrc_t sbuf = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a.scales), 0, (int)(m * nb * 4), CFG);
     const int lo16 = lane * 16, d16 = SQ_SCALE_OFF + (lane & 15) * 16;
+    // A record's activations are loaded by its own wave, lane (row r = l % 16,
+    // block l / 16 of the record) taking that row's code bytes of the block
+    // and its scale; the range check zeroes rows past m and the bytes past the
+    // matrix (the weights of blocks past nb are zero, so what those lanes read
+    // inside the matrix adds nothing).  The record position is part of the
+    // lane offset because the range check does not cover the scalar offset.
+    const int ar = lane & 15, ab = lane >> 4;
     struct Rec {
         v4u c0, c1, d;
+        uint4 ac[A8 ? 2 : 1];
+        float as;
     };
     // Every wave issues the same loads whatever its count (slots past it
     // reload the split's last record, a cache hit), so the number of loads in
     // flight is the same on every path into the main loop and its waits stay
     // exact.
     auto load = [&](int i, Rec &R) {
-        const int off = __builtin_amdgcn_readfirstlane(min(wave + WAVES * i, nr - 1) * SQ_REC);
+        const int li = min(wave + WAVES * i, nr - 1);
+        const int off = __builtin_amdgcn_readfirstlane(li * SQ_REC);
+        const int blk = (int)(q_lo + li) * SQ_BLOCKS + ab;  // block of this lane's activations
         R.c0 = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lo16, off, 0);
-        __builtin_amdgcn_sched_barrier(0);  // one issue order everywhere (c0, c1, d)
+        __builtin_amdgcn_sched_barrier(0);  // one issue order everywhere
         R.c1 = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lo16 + 1024, off, 0);
         __builtin_amdgcn_sched_barrier(0);
         R.d = __builtin_amdgcn_raw_buffer_load_b128(wbuf, d16, off, 0);
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int h = 0; h < (A8 ? 2 : 1); h++) {
+            const v4u u = __builtin_amdgcn_raw_buffer_load_b128(cbuf, (ar * (int)nb + blk) * ROW_BYTES + 16 * h, 0, 0);
+            R.ac[h] = make_uint4(u[0], u[1], u[2], u[3]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        R.as = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, (ar * (int)nb + blk) * 4, 0, 0));
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Staging of the range's activations in LDS: K8 words [block][g][row],
-    // then scales [block][row].  Every thread issues all of its loads at once
-    // (at most FILL, addresses clamped into the matrix, out-of-range items
-    // zeroed afterwards), then the ring's first records, and only then waits
-    // and writes LDS: one cache latency, overlapped with the weights'.
-    constexpr int MAX_RANGE = A8 ? SM_MAX_RANGE_A8 : SM_MAX_RANGE;
-    constexpr int FILL = (MAX_RANGE * SQ_BLOCKS * 16 + 64 * WAVES - 1) / (64 * WAVES);
-    constexpr int ROW_BYTES = A8 ? QK : QK / 2;  // activation code bytes per (row, block)
-    const int items = nr * SQ_BLOCKS * 16;
-    uint4 fu[FILL][A8 ? 2 : 1];
-    float fs[FILL];
-#pragma unroll
-    for (int t = 0; t < FILL; t++) {
-        const int i = min(tid + t * 64 * WAVES, items - 1);
-        const int r = min(i & 15, m - 1);
-        const int64_t b = min(q_lo * SQ_BLOCKS + (i >> 4), nb - 1);
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.codes + (int64_t)r * (k / 32 * ROW_BYTES) + b * ROW_BYTES);
-#pragma unroll
-        for (int h = 0; h < (A8 ? 2 : 1); h++) fu[t][h] = src[h];
-        fs[t] = a.scales[(int64_t)r * nb + b];
-    }
-    Rec ring[DEPTH];
-#pragma unroll
-    for (int j = 0; j < DEPTH - 1; j++) load(j, ring[j]);
-    // A4: K8 words [block][g][row] (4 B each); A8: 8 codes [block][g][row] (8 B each)
-    uint32_t *act = reinterpret_cast<uint32_t *>(smem);
-    uint2 *act8 = reinterpret_cast<uint2 *>(smem);
-    float *asc = reinterpret_cast<float *>(smem + nr * SQ_BLOCKS * 64 * (A8 ? 8 : 4));
-#pragma unroll
-    for (int t = 0; t < FILL; t++) {
-        const int i = tid + t * 64 * WAVES, bl = i >> 4, r = i & 15;
-        // rows past m and blocks past nb are zero
-        const bool live = r < m && q_lo * SQ_BLOCKS + bl < nb;
-        if (i < items) {
-            if constexpr (A8) {
-                const uint4 u0 = live ? fu[t][0] : make_uint4(0, 0, 0, 0);
-                const uint4 u1 = live ? fu[t][1] : make_uint4(0, 0, 0, 0);
-                act8[bl * 64 + 0 * 16 + r] = make_uint2(u0.x, u0.y);  // codes 0..7
-                act8[bl * 64 + 1 * 16 + r] = make_uint2(u0.z, u0.w);  // codes 8..15
-                act8[bl * 64 + 2 * 16 + r] = make_uint2(u1.x, u1.y);
-                act8[bl * 64 + 3 * 16 + r] = make_uint2(u1.z, u1.w);
-            } else {
-                const uint4 w = k8_words(live ? fu[t][0] : make_uint4(0, 0, 0, 0));
-                act[bl * 64 + 0 * 16 + r] = w.x;
-                act[bl * 64 + 1 * 16 + r] = w.y;
-                act[bl * 64 + 2 * 16 + r] = w.z;
-                act[bl * 64 + 3 * 16 + r] = w.w;
-            }
-            asc[bl * 16 + r] = live ? fs[t] : 0.0f;
+    // This wave's LDS slot for one record's activations, in the MFMA's lane
+    // order: A4 K8 words [block][g][row] (4 B), A8 8 codes [block][g][row]
+    // (8 B), then the scales [block][row].
+    constexpr int SLOT = SQ_BLOCKS * 64 * (A8 ? 8 : 4) + SQ_BLOCKS * 16 * 4;
+    uint8_t *slot = smem + wave * SLOT;
+    uint32_t *act = reinterpret_cast<uint32_t *>(slot);
+    uint2 *act8 = reinterpret_cast<uint2 *>(slot);
+    float *asc = reinterpret_cast<float *>(slot + SQ_BLOCKS * 64 * (A8 ? 8 : 4));
+    auto put = [&](const Rec &R) {
+        if constexpr (A8) {
+            act8[ab * 64 + 0 * 16 + ar] = make_uint2(R.ac[0].x, R.ac[0].y);  // codes 0..7
+            act8[ab * 64 + 1 * 16 + ar] = make_uint2(R.ac[0].z, R.ac[0].w);  // codes 8..15
+            act8[ab * 64 + 2 * 16 + ar] = make_uint2(R.ac[1].x, R.ac[1].y);
+            act8[ab * 64 + 3 * 16 + ar] = make_uint2(R.ac[1].z, R.ac[1].w);
+        } else {
+            const uint4 w = k8_words(R.ac[0]);
+            act[ab * 64 + 0 * 16 + ar] = w.x;
+            act[ab * 64 + 1 * 16 + ar] = w.y;
+            act[ab * 64 + 2 * 16 + ar] = w.z;
+            act[ab * 64 + 3 * 16 + ar] = w.w;
         }
-    }
-    __syncthreads();
+        asc[ab * 16 + ar] = R.as;
+    };
 
     float acc[8];
 #pragma unroll
@@ -189,31 +178,34 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
             acc[4 + i] = fmaf((float)S1[i], __fmul_rn(sv[i], d1), acc[4 + i]);
         }
     };
-    auto compute = [&](int i, const Rec &R) {
-        const int bl = (wave + WAVES * i) * SQ_BLOCKS;
-        block(bl + 0, R.c0[0], R.c0[1], R.d[0]);
-        block(bl + 1, R.c0[2], R.c0[3], R.d[1]);
-        block(bl + 2, R.c1[0], R.c1[1], R.d[2]);
-        block(bl + 3, R.c1[2], R.c1[3], R.d[3]);
+    auto compute = [&](const Rec &R) {
+        put(R);  // the same wave reads the slot next: LDS operations of a wave stay in order
+        block(0, R.c0[0], R.c0[1], R.d[0]);
+        block(1, R.c0[2], R.c0[3], R.d[1]);
+        block(2, R.c1[0], R.c1[1], R.d[2]);
+        block(3, R.c1[2], R.c1[3], R.d[3]);
     };
 
     // Ring of DEPTH records: record i + DEPTH - 1 is loaded before record i
     // is computed.  The loop is unrolled DEPTH times so that every ring index
     // is static; the scheduling barriers keep the loads ahead of the compute
     // (the scheduler would otherwise sink them to their first use).
+    Rec ring[DEPTH];
+#pragma unroll
+    for (int j = 0; j < DEPTH - 1; j++) load(j, ring[j]);
     for (int i = 0; i < cnt; i += DEPTH) {
 #pragma unroll
         for (int j = 0; j < DEPTH; j++) {
             load(i + j + DEPTH - 1, ring[(j + DEPTH - 1) % DEPTH]);
             __builtin_amdgcn_sched_barrier(0);
-            compute(i + j, ring[j]);
+            compute(ring[j]);
             __builtin_amdgcn_sched_barrier(0);
             if (i + j + 1 >= cnt) break;
         }
     }
 
     // the waves' sums meet in LDS (ascending wave order), then one store
-    __syncthreads();  // every wave is done with the staged activations
+    __syncthreads();  // every wave is done with its activation slot
     float *red = reinterpret_cast<float *>(smem);  // [wave][8][64]
 #pragma unroll
     for (int v = 0; v < 8; v++) red[(wave * 8 + v) * 64 + lane] = acc[v];
@@ -232,12 +224,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
     }
 }
 
-// LDS bytes of one workgroup: the staged activations, or the cross-wave
+// LDS bytes of one workgroup: the waves' activation slots, or the cross-wave
 // reduction if that is larger.
 __host__ inline size_t small_m_lds_bytes(const SmallPlan &p, bool a8 = false) {
-    const size_t stage = (size_t)p.range * (a8 ? SM_ACT8_REC_BYTES : SM_ACT_REC_BYTES),
+    (void)p;
+    const size_t slots = (size_t)SM_WAVES * SQ_BLOCKS * (64 * (a8 ? 8 : 4) + 16 * 4),
                  red = (size_t)SM_WAVES * 8 * 64 * 4;
-    return stage > red ? stage : red;
+    return slots > red ? slots : red;
 }
 
 // y = sum over the K splits of the partial sums, in ascending split order.
