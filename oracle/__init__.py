@@ -63,6 +63,7 @@ def _load():
         lib.oracle_rotate_quantize_act8.argtypes = [P, ctypes.c_int, I64, I64, I64, P, P, ctypes.c_int]
         lib.oracle_block_sums_a8.argtypes = [P, P, I64, I64, I64, P]
         lib.oracle_gemm_a8.argtypes = [P, P, P, I64, I64, I64, P, I64, ctypes.c_int]
+        lib.oracle_quantize_act_plain.argtypes = [P, ctypes.c_int, I64, I64, I64, P, P, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -154,6 +155,27 @@ def rotate_quantize_act(x: np.ndarray, k: int | None = None, threads: int | None
     _load().oracle_rotate_quantize_act(_ptr(x), dtype, m, k, ldx, _ptr(codes), _ptr(scales),
                                        threads or default_threads())
     return codes, scales
+
+
+def quantize_act_plain(x: np.ndarray, k: int | None = None, threads: int | None = None):
+    """R9 (unrotated ablation): x fp32 or fp16 [m, ldx] -> (codes uint8 [m, k/2],
+    scales fp32 [m, k/32]), per-block symmetric int4 without the rotation."""
+    assert x.dtype in (np.float32, np.float16)
+    x = np.ascontiguousarray(x)
+    m, ldx = x.shape
+    k = ldx if k is None else k
+    assert k % QK == 0 and k <= ldx
+    codes = np.empty((m, k // 2), np.uint8)
+    scales = np.empty((m, k // QK), np.float32)
+    dtype = 0 if x.dtype == np.float32 else 1
+    _load().oracle_quantize_act_plain(_ptr(x), dtype, m, k, ldx, _ptr(codes), _ptr(scales),
+                                      threads or default_threads())
+    return codes, scales
+
+
+def prepare_weights_plain(w: np.ndarray, threads: int | None = None) -> np.ndarray:
+    """R9 (unrotated ablation): plain Q4_0 of the unrotated weights."""
+    return q4_0_quantize(w, threads)
 
 
 def block_sums(q4: np.ndarray, codes: np.ndarray, k: int) -> np.ndarray:

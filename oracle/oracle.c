@@ -51,6 +51,13 @@
  *       id = 1/d, q = clamp(round_half_away(v*id), -127, 127), s = d * c32,
  *       zero blocks as in R5; the output is R6 with these codes.  Codes are
  *       stored one signed byte per element, [m][k].
+ *   R9  Unrotated W4A4, the ablation of section "MoE: W4A4 on the experts"
+ *       (the same W4A4 without the rotation costs about twice the accuracy):
+ *       the weights are plain Q4_0 of the unrotated weights (R3 applied to w
+ *       itself), the activations are quantised per block as in R5 but with
+ *       no rotation and no normalisation: v = x, d = amax/7, id = 1/d,
+ *       q = clamp(round_half_away(v*id), -7, 7), s = d, zero blocks as in
+ *       R5; the output is R6 with these codes and scales.
  *
  * Byte layouts:
  *   Q4_0 block (18 bytes): fp16 d (little endian), then 16 bytes; byte j holds
@@ -389,6 +396,54 @@ void oracle_rotate_quantize_act(const void *x, int dtype, int64_t m, int64_t k, 
 {
     act_ctx c = {x, dtype, k, ldx, codes, scales};
     parallel_rows(m, nthreads, act_rows, &c);
+}
+
+/* R9: one unrotated block to codes q[32] in [-7, 7]; returns s = d. */
+static float quantize_block_plain(const float *v, int8_t *q)
+{
+    float amax = 0.0f;
+    for (int t = 0; t < QK; t++)
+        if (fabsf(v[t]) > amax)
+            amax = fabsf(v[t]);
+    float d = amax / 7.0f;
+    if (!(d >= FLT_MIN)) {
+        for (int t = 0; t < QK; t++)
+            q[t] = 0;
+        return 0.0f;
+    }
+    float id = 1.0f / d;
+    for (int t = 0; t < QK; t++) {
+        float r = round_half_away(v[t] * id);
+        if (r > 7.0f) r = 7.0f;
+        if (r < -7.0f) r = -7.0f;
+        q[t] = (int8_t)r;
+    }
+    return d;
+}
+
+static void act_plain_rows(void *p, int64_t r0, int64_t r1)
+{
+    act_ctx *c = (act_ctx *)p;
+    const int64_t k = c->k, nb = k / QK;
+    for (int64_t r = r0; r < r1; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            float v[QK];
+            load_block(c->x, c->dtype, c->ldx, r, b, v);
+            int8_t q[QK];
+            c->scales[r * nb + b] = quantize_block_plain(v, q);
+            uint8_t *dst = c->codes + r * (k / 2) + b * 16;
+            for (int j = 0; j < 16; j++)
+                dst[j] = (uint8_t)(((uint8_t)q[j] & 0x0f) | (((uint8_t)q[j + 16] & 0x0f) << 4));
+        }
+    }
+}
+
+/* R9 activations: as oracle_rotate_quantize_act without the rotation. */
+void oracle_quantize_act_plain(const void *x, int dtype, int64_t m, int64_t k, int64_t ldx,
+                               uint8_t *codes, float *scales, int nthreads)
+{
+    act_ctx c = {x, dtype, k, ldx, codes, scales};
+    parallel_rows(m, nthreads, act_plain_rows, &c);
 }
 
 static void act8_rows(void *p, int64_t r0, int64_t r1)

@@ -551,3 +551,67 @@ def test_tiny_workload_golden_digests():
     got = {"q4_0": q4, "codes": codes, "scales": s, "y": y}
     for key, arr in got.items():
         assert hashlib.sha256(arr.tobytes()).hexdigest() == ref[key + "_sha256"], key
+
+
+# --------------------------------------------------------------------------
+# Unrotated W4A4 ablation (reading R9): no rotation on either side
+# --------------------------------------------------------------------------
+
+def test_plain_quantiser_special_blocks():
+    """Closed forms: zero and subnormal blocks give zeros; a constant block a
+    gives all codes 7 sign(a) with s = fl(|a| / 7); a one-hot block a e_j gives
+    7 sign(a) at j only (no rotation spreads it)."""
+    for scale in (0.0, 1e-44):
+        codes, s = oracle.quantize_act_plain(np.full((1, 32), scale, np.float32))
+        assert not codes.any() and s[0, 0] == 0.0
+    for a in (0.37, -2.5, 1e-3, 300.0):
+        codes, s = oracle.quantize_act_plain(np.full((1, 32), a, np.float32))
+        assert decode_act_codes(codes[0], 32) == [7 * int(np.sign(a))] * 32
+        assert s[0, 0] == np.float32(np.float32(abs(a)) / np.float32(7))
+    for j in (0, 5, 16, 31):
+        for a in (20.0, -3.25):
+            x = np.zeros((1, 32), np.float32)
+            x[0, j] = a
+            codes, s = oracle.quantize_act_plain(x)
+            q = [0] * 32
+            q[j] = 7 * int(np.sign(a))
+            assert decode_act_codes(codes[0], 32) == q
+            assert s[0, 0] == np.float32(np.float32(abs(a)) / np.float32(7))
+
+
+def test_plain_quantiser_power_of_two_invariance():
+    """Scaling a block by 2^e leaves its codes and scales its scale by 2^e
+    exactly (every step is a correctly rounded fp32 operation)."""
+    rng = np.random.default_rng(41)
+    x = synth.activations(6, 256, rng, 3)
+    c0, s0 = oracle.quantize_act_plain(x)
+    for e in (-5, 3, 12):
+        c1, s1 = oracle.quantize_act_plain((x * np.float32(2.0 ** e)).astype(np.float32))
+        assert np.array_equal(c0, c1)
+        assert np.array_equal(s1, (s0 * np.float32(2.0 ** e)).astype(np.float32))
+
+
+def test_plain_quantiser_is_the_rotated_rule_before_the_rotation():
+    """The rotated quantiser (R5, pinned above) is this one applied to the
+    FWHT of each block, with the scale times c32: codes equal, and
+    s_R5 = fl(s_plain * c32)."""
+    rng = np.random.default_rng(43)
+    x = synth.activations(8, 256, rng, 3)
+    c_rot, s_rot = oracle.rotate_quantize_act(x)
+    xh = np.stack([oracle.fwht32_f32(blk) for blk in x.reshape(-1, 32)]).reshape(x.shape).astype(np.float32)
+    c_pl, s_pl = oracle.quantize_act_plain(xh)
+    assert np.array_equal(c_rot, c_pl)
+    assert np.array_equal(s_rot, (s_pl * np.float32(oracle.c32())).astype(np.float32))
+
+
+def test_ablation_without_rotation_costs_more():
+    """Direction of the ablation (section "MoE: W4A4 on the experts"): on
+    outlier data, plain Q4_0 weights with unrotated int4 activations land
+    further from the exact fp64 product than the rotated pair does."""
+    d = synth.tiny()
+    ref = d.x.astype(np.float64) @ d.w.astype(np.float64).T
+    y_rot = oracle.gemm(oracle.prepare_weights(d.w), *oracle.rotate_quantize_act(d.x), d.k)
+    y_plain = oracle.gemm(oracle.prepare_weights_plain(d.w), *oracle.quantize_act_plain(d.x), d.k)
+    err_rot = np.abs(y_rot - ref).mean()
+    err_plain = np.abs(y_plain - ref).mean()
+    assert err_plain > 1.3 * err_rot
