@@ -290,6 +290,35 @@ def run_w4a8(torch, ops, synth):
             "timing": "events over back-to-back calls (M=512); HIP graph replay (m=16)"}
 
 
+def run_ablation(torch, ops, synth):
+    """Unrotated W4A4 ablation (section "MoE: W4A4 on the experts": without
+    the rotation W4A4 costs about twice the accuracy): the FFN-up workload
+    through both pipelines, errors against the exact fp64 product of the
+    unquantised operands on sampled rows, and the unrotated quantiser's time."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    d = synth.ffn_up()
+    w = torch.from_numpy(d.w).to(dev)
+    x = torch.from_numpy(d.x).to(dev)
+    y_rot = ops.gemm(ops.prepare_weights(w), *ops.rotate_quantize_act(x), d.n, d.k)
+    y_plain = ops.gemm(ops.prepare_weights_plain(w), *ops.quantize_act(x), d.n, d.k)
+    rows = np.arange(0, d.m, d.m // 16)
+    torch.cuda.synchronize()
+    exact = d.x[rows].astype(np.float64) @ d.w.astype(np.float64).T
+    out = {"workload": d.name, "rows_sampled": len(rows)}
+    for name, y in (("rotated", y_rot), ("unrotated", y_plain)):
+        e = y.cpu().numpy()[rows].astype(np.float64) - exact
+        out[name] = {"mean_abs_err": float(np.abs(e).mean()),
+                     "rel_rms_err": float(np.sqrt((e ** 2).mean() / (exact ** 2).mean()))}
+    out["err_ratio_unrotated_over_rotated"] = round(out["unrotated"]["mean_abs_err"] / out["rotated"]["mean_abs_err"], 3)
+    codes = torch.empty((d.m, d.k // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((d.m, d.k // 32), dtype=torch.float32, device=dev)
+    q_rot = events_ms(torch, lambda i: ops.rotate_quantize_act(x, codes=codes, scales=scales), 20) * 1e3
+    q_plain = events_ms(torch, lambda i: ops.quantize_act(x, codes=codes, scales=scales), 20) * 1e3
+    out["quantise_us"] = {"rotated": round(q_rot, 2), "unrotated": round(q_plain, 2)}
+    return out
+
+
 def run_layer_prompt(torch, ops, synth):
     """Dense layer's seven projections over a 1,838-token prompt (512+512+512+302)."""
     dev = torch.device("cuda:0")
@@ -428,6 +457,8 @@ def main():
         log("[bench] extra: W4A8-H32 (int8 activations)")
         extras["w4a8"] = run_w4a8(torch, ops, synth)
         log(f"[bench] w4a8: {extras['w4a8']['ffn_up_m512']}")
+        extras["ablation_unrotated"] = run_ablation(torch, ops, synth)
+        log(f"[bench] ablation: error ratio {extras['ablation_unrotated']['err_ratio_unrotated_over_rotated']}")
         log("[bench] extra: dense layer set over a 1,838-token prompt")
         extras["layer_prompt_1838"] = run_layer_prompt(torch, ops, synth)
         log(f"[bench] layer: {extras['layer_prompt_1838']['layer_ms']} ms")

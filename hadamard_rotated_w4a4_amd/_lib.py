@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
             "w4a4_gemm": ([P, P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_id_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_rotate_quantize_act8": ([P, ST, I64, I64, I64, P, P, P], ST),
+            "w4a4_quantize_q4_0": ([P, I64, I64, I64, P, P], ST),
+            "w4a4_quantize_act": ([P, ST, I64, I64, I64, P, P, P], ST),
             "w4a4_gemm_a8_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_gemm_a8": ([P, P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_id": ([P, I64, P, P, I64, P, I64, I64, P, I64, I64, P, SZ, P], ST),
@@ -269,3 +271,43 @@ def prepare_weights(w: torch.Tensor) -> torch.Tensor:
     """Offline step on the GPU: fp32 [n, k] -> rotated Q4_0 -> packed buffer."""
     n, k = w.shape
     return repack_q4_0_h32(quantize_q4_0_h32(w), n, k)
+
+
+# --------------------------------------------------------------------------
+# Unrotated W4A4 ablation: the same GEMM entry points, nothing rotated
+# --------------------------------------------------------------------------
+
+def quantize_q4_0(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 [n, k] (row stride w.stride(0)) -> plain (unrotated) Q4_0 bytes uint8 [n, k/32, 18]."""
+    _require_cuda(w, out)
+    assert w.dtype == torch.float32 and w.dim() == 2 and w.stride(1) == 1
+    n, k = w.shape
+    if out is None:
+        out = torch.empty((n, k // 32, 18), dtype=torch.uint8, device=w.device)
+    _check(lib().w4a4_quantize_q4_0(_ptr(w), n, k, w.stride(0), _ptr(out), _stream(w.device)), "w4a4_quantize_q4_0")
+    return out
+
+
+def quantize_act(x: torch.Tensor, k: int | None = None, codes: torch.Tensor | None = None,
+                 scales: torch.Tensor | None = None):
+    """x fp16/fp32 [m, >=k] -> unrotated int4 (codes uint8 [m, k/2], scales fp32 [m, k/32])."""
+    _require_cuda(x, codes, scales)
+    assert x.dim() == 2 and x.stride(1) == 1
+    dt = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16}.get(x.dtype)
+    if dt is None:
+        raise W4A4Error(f"unsupported activation dtype {x.dtype}")
+    m = x.shape[0]
+    k = x.shape[1] if k is None else k
+    if codes is None:
+        codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    _check(lib().w4a4_quantize_act(_ptr(x), dt, m, k, x.stride(0), _ptr(codes), _ptr(scales), _stream(x.device)),
+           "w4a4_quantize_act")
+    return codes, scales
+
+
+def prepare_weights_plain(w: torch.Tensor) -> torch.Tensor:
+    """fp32 [n, k] -> plain (unrotated) Q4_0 -> packed buffer (the ablation's weights)."""
+    n, k = w.shape
+    return repack_q4_0_h32(quantize_q4_0(w), n, k)

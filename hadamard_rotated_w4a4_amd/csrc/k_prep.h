@@ -14,7 +14,10 @@ namespace w4a4 {
 // fp64(1/sqrt(32)) correctly rounded (= fp64(sqrt(2)) / 8).
 __device__ constexpr double kInvSqrt32d = 0.17677669529663688110021109052621763;
 
-// One thread per 32-element block: rotate in fp64, round to fp32, quantise to Q4_0.
+// One thread per 32-element block: rotate in fp64, round to fp32, quantise to
+// Q4_0.  ROTATE = false: plain Q4_0 of the unrotated block (the weights of the
+// unrotated W4A4 ablation, section "MoE: W4A4 on the experts").
+template <bool ROTATE = true>
 __global__ __launch_bounds__(256) void quantize_q4_0_h32_kernel(const float *__restrict__ w,
                                                                  int64_t n, int64_t k, int64_t ldw,
                                                                  uint8_t *__restrict__ q4) {
@@ -32,14 +35,18 @@ __global__ __launch_bounds__(256) void quantize_q4_0_h32_kernel(const float *__r
     float amax = 0.0f, mx = 0.0f;
 #pragma unroll
     for (int t = 0; t < QK; t++) {
-        double u = 0.0;
+        if constexpr (ROTATE) {
+            double u = 0.0;
 #pragma unroll
-        for (int j = 0; j < QK; j++) {
-            // H[t][j] = (-1)^popcount(t & j); adding +-x_j is exact per term
-            const bool neg = __builtin_popcount((unsigned)(t & j)) & 1;
-            u = __dadd_rn(u, neg ? -(double)x[j] : (double)x[j]);
+            for (int j = 0; j < QK; j++) {
+                // H[t][j] = (-1)^popcount(t & j); adding +-x_j is exact per term
+                const bool neg = __builtin_popcount((unsigned)(t & j)) & 1;
+                u = __dadd_rn(u, neg ? -(double)x[j] : (double)x[j]);
+            }
+            r[t] = (float)__dmul_rn(u, kInvSqrt32d);
+        } else {
+            r[t] = x[t];
         }
-        r[t] = (float)__dmul_rn(u, kInvSqrt32d);
         const float a = fabsf(r[t]);
         if (a > amax) { amax = a; mx = r[t]; }
     }

@@ -72,8 +72,11 @@ __device__ __forceinline__ void load4(const __half *p, bool vec, float v[4]) {
 // QMAX = 7: int4 codes (W4A4).  QMAX = 127: int8 codes for the exact int8
 // path on a rotated file (W4A8), one signed byte per element in `codes`
 // ([m][k]), same rotation, d = amax / 127; no operand record.
+// ROTATE = false: the unrotated W4A4 ablation (section "MoE: W4A4 on the
+// experts"): no butterflies, and the stored scale is d itself (there is no
+// normalisation to fold in).
 constexpr int RQ_BLOCKS = 2;  // blocks per workgroup
-template <typename T, int QMAX = 7>
+template <typename T, int QMAX = 7, bool ROTATE = true>
 __global__ __launch_bounds__(256 * RQ_BLOCKS) void rotate_quantize_kernel(const T *__restrict__ x, int64_t m,
                                                                           int64_t k, int64_t ldx, bool vec,
                                                                           uint8_t *__restrict__ codes,
@@ -88,25 +91,27 @@ __global__ __launch_bounds__(256 * RQ_BLOCKS) void rotate_quantize_kernel(const 
     float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (live) load4(x + row * ldx + b * QK + 4 * L, vec, v);
 
-    // distance 1 and 2: inside the lane
-    {
-        const float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
-        v[0] = __fadd_rn(a0, a1); v[1] = __fsub_rn(a0, a1);
-        v[2] = __fadd_rn(a2, a3); v[3] = __fsub_rn(a2, a3);
-    }
-    {
-        const float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
-        v[0] = __fadd_rn(a0, a2); v[2] = __fsub_rn(a0, a2);
-        v[1] = __fadd_rn(a1, a3); v[3] = __fsub_rn(a1, a3);
-    }
-    // distance 4, 8, 16: partner lane L ^ 1, L ^ 2, L ^ 4 holds the other element
+    if constexpr (ROTATE) {
+        // distance 1 and 2: inside the lane
+        {
+            const float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+            v[0] = __fadd_rn(a0, a1); v[1] = __fsub_rn(a0, a1);
+            v[2] = __fadd_rn(a2, a3); v[3] = __fsub_rn(a2, a3);
+        }
+        {
+            const float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+            v[0] = __fadd_rn(a0, a2); v[2] = __fsub_rn(a0, a2);
+            v[1] = __fadd_rn(a1, a3); v[3] = __fsub_rn(a1, a3);
+        }
+        // distance 4, 8, 16: partner lane L ^ 1, L ^ 2, L ^ 4 holds the other element
 #pragma unroll
-    for (int mask = 1; mask < 8; mask <<= 1) {
-        const bool upper = (L & mask) != 0;
+        for (int mask = 1; mask < 8; mask <<= 1) {
+            const bool upper = (L & mask) != 0;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float p = xchg(v[i], mask);
-            v[i] = upper ? __fsub_rn(p, v[i]) : __fadd_rn(v[i], p);  // (lower - upper) / (lower + upper)
+            for (int i = 0; i < 4; i++) {
+                const float p = xchg(v[i], mask);
+                v[i] = upper ? __fsub_rn(p, v[i]) : __fadd_rn(v[i], p);  // (lower - upper) / (lower + upper)
+            }
         }
     }
 
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(256 * RQ_BLOCKS) void rotate_quantize_kernel(const 
     const float d = __fdiv_rn(amax, (float)QMAX);
     const bool nonzero = d >= 1.17549435e-38f;  // FLT_MIN: zero and subnormal scales give a zero block
     const float id = nonzero ? __fdiv_rn(1.0f, d) : 0.0f;
-    const float s = nonzero ? __fmul_rn(d, kInvSqrt32f) : 0.0f;
+    const float s = !nonzero ? 0.0f : ROTATE ? __fmul_rn(d, kInvSqrt32f) : d;
     int q[4];
 #pragma unroll
     for (int i = 0; i < 4; i++)

@@ -150,17 +150,28 @@ size_t w4a4_packed_weight_bytes(int64_t n, int64_t k) {
     return (size_t)packed_total_bytes(n, k);
 }
 
-w4a4_status w4a4_quantize_q4_0_h32(const float *w, int64_t n, int64_t k, int64_t ldw, void *q4_0,
-                                   void *stream) {
+namespace {
+w4a4_status quantize_q4_0(bool rotate, const float *w, int64_t n, int64_t k, int64_t ldw, void *q4_0, void *stream) {
     if (n < 0 || k < 0 || ldw < k) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
     if (n == 0 || k == 0) return W4A4_OK;
     if (!w || !q4_0) return W4A4_ERR_INVALID_VALUE;
     if (!aligned(w, 4)) return W4A4_ERR_MISALIGNED;
     const int64_t blocks = n * (k / QK);
-    quantize_q4_0_h32_kernel<<<blocks_for(blocks, 256), 256, 0, as_stream(stream)>>>(
-        w, n, k, ldw, static_cast<uint8_t *>(q4_0));
+    uint8_t *q = static_cast<uint8_t *>(q4_0);
+    if (rotate) quantize_q4_0_h32_kernel<true><<<blocks_for(blocks, 256), 256, 0, as_stream(stream)>>>(w, n, k, ldw, q);
+    else quantize_q4_0_h32_kernel<false><<<blocks_for(blocks, 256), 256, 0, as_stream(stream)>>>(w, n, k, ldw, q);
     return hip_status("quantize_q4_0_h32_kernel");
+}
+}  // namespace
+
+w4a4_status w4a4_quantize_q4_0_h32(const float *w, int64_t n, int64_t k, int64_t ldw, void *q4_0,
+                                   void *stream) {
+    return quantize_q4_0(true, w, n, k, ldw, q4_0, stream);
+}
+
+w4a4_status w4a4_quantize_q4_0(const float *w, int64_t n, int64_t k, int64_t ldw, void *q4_0, void *stream) {
+    return quantize_q4_0(false, w, n, k, ldw, q4_0, stream);
 }
 
 w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int64_t k, void *stream) {
@@ -181,9 +192,11 @@ w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int6
 }
 
 namespace {
-// a8: int8 codes ([m][k] bytes) instead of int4 ([m][k/2])
+// a8: int8 codes ([m][k] bytes) instead of int4 ([m][k/2]); rotate = false:
+// no rotation (the unrotated ablation; int4 only)
 w4a4_status rotate_quantize(bool a8, const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
-                            uint8_t *codes, float *scales, void *act, size_t act_bytes, void *stream) {
+                            uint8_t *codes, float *scales, void *act, size_t act_bytes, void *stream,
+                            bool rotate = true) {
     if (dt != W4A4_DTYPE_F32 && dt != W4A4_DTYPE_F16) return W4A4_ERR_UNSUPPORTED_DTYPE;
     if (m < 0 || k < 0 || ldx < k || m > kMaxRows) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
@@ -205,7 +218,9 @@ w4a4_status rotate_quantize(bool a8, const void *x, w4a4_dtype dt, int64_t m, in
     const float *xf = static_cast<const float *>(x);
     const __half *xh = static_cast<const __half *>(x);
     const unsigned nt = 256 * RQ_BLOCKS;
-    if (dt == W4A4_DTYPE_F32 && a8) rotate_quantize_kernel<float, 127><<<grid, nt, 0, s>>>(xf, m, k, ldx, vec, codes, scales, a);
+    if (!rotate && dt == W4A4_DTYPE_F32) rotate_quantize_kernel<float, 7, false><<<grid, nt, 0, s>>>(xf, m, k, ldx, vec, codes, scales, a);
+    else if (!rotate) rotate_quantize_kernel<__half, 7, false><<<grid, nt, 0, s>>>(xh, m, k, ldx, vec, codes, scales, a);
+    else if (dt == W4A4_DTYPE_F32 && a8) rotate_quantize_kernel<float, 127><<<grid, nt, 0, s>>>(xf, m, k, ldx, vec, codes, scales, a);
     else if (dt == W4A4_DTYPE_F32) rotate_quantize_kernel<float, 7><<<grid, nt, 0, s>>>(xf, m, k, ldx, vec, codes, scales, a);
     else if (a8) rotate_quantize_kernel<__half, 127><<<grid, nt, 0, s>>>(xh, m, k, ldx, vec, codes, scales, a);
     else rotate_quantize_kernel<__half, 7><<<grid, nt, 0, s>>>(xh, m, k, ldx, vec, codes, scales, a);
@@ -216,6 +231,11 @@ w4a4_status rotate_quantize(bool a8, const void *x, w4a4_dtype dt, int64_t m, in
 w4a4_status w4a4_rotate_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
                                      uint8_t *codes, float *scales, void *stream) {
     return rotate_quantize(false, x, dt, m, k, ldx, codes, scales, nullptr, 0, stream);
+}
+
+w4a4_status w4a4_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx, uint8_t *codes,
+                              float *scales, void *stream) {
+    return rotate_quantize(false, x, dt, m, k, ldx, codes, scales, nullptr, 0, stream, false);
 }
 
 w4a4_status w4a4_rotate_quantize_act8(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,

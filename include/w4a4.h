@@ -195,6 +195,28 @@ w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float 
                          int64_t m, int64_t n, int64_t k, int64_t ldy, void *workspace,
                          size_t workspace_bytes, void *stream);
 
+/*
+ * Unrotated W4A4, the ablation of section "MoE: W4A4 on the experts" (the
+ * same W4A4 without the rotation costs about twice the accuracy).  Both
+ * sides skip the rotation; the GEMM entry points are the same, fed with
+ * weights packed from w4a4_quantize_q4_0 and codes from w4a4_quantize_act.
+ * (Pairing these with rotated weights, or rotated activations with these
+ * weights, computes garbage: the rotation identity needs both sides.)
+ *
+ * w4a4_quantize_q4_0: plain Q4_0 of the unrotated weights; arguments and
+ * arithmetic as w4a4_quantize_q4_0_h32 without the rotation step (the
+ * quantiser sees the fp32 weights themselves).
+ *
+ * w4a4_quantize_act: per-block symmetric int4 without the rotation;
+ * arguments and errors as w4a4_rotate_quantize_act.  Per block: d = amax / 7,
+ * codes clamp(round-half-away(x * (1/d)), -7, 7), s = d (there is no
+ * normalisation to fold in); a block with d below FLT_MIN gets zero codes
+ * and s = 0.
+ */
+w4a4_status w4a4_quantize_q4_0(const float *w, int64_t n, int64_t k, int64_t ldw, void *q4_0, void *stream);
+w4a4_status w4a4_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx, uint8_t *codes,
+                              float *scales, void *stream);
+
 /* Workspace bytes w4a4_gemm_id needs (0 for invalid sizes).  Host only, pure. */
 size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t top_k);
 

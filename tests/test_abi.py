@@ -156,6 +156,21 @@ def test_rotate_quantize_validation(L):
     assert f(None, 1, 0, 64, 64, None, None, None) == OK
 
 
+def test_ablation_validation(L):
+    q = L.w4a4_quantize_act
+    assert q(P(A), 2, 4, 64, 64, P(A), P(A), None) == DTYPE
+    assert q(P(A), 1, 4, 48, 64, P(A), P(A), None) == KMUL
+    assert q(P(A), 1, 4, 64, 32, P(A), P(A), None) == INVALID  # ldx < k
+    assert q(P(ODD), 1, 4, 64, 64, P(A), P(A), None) == MISALIGNED
+    assert q(P(A), 1, 4, 64, 64, P(A + 4), P(A), None) == MISALIGNED
+    assert q(None, 1, 0, 64, 64, None, None, None) == OK
+    w = L.w4a4_quantize_q4_0
+    assert w(P(A), 4, 40, 40, P(A), None) == KMUL
+    assert w(P(A), 4, 64, 32, P(A), None) == INVALID
+    assert w(P(ODD), 4, 64, 64, P(A), None) == MISALIGNED
+    assert w(None, 0, 64, 64, None, None) == OK
+
+
 def test_prep_validation(L):
     q = L.w4a4_quantize_q4_0_h32
     assert q(P(A), 4, 40, 40, P(A), None) == KMUL
