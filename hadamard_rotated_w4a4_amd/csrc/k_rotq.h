@@ -7,15 +7,13 @@
 // coarse scale on the rest.  The same per-block rotation was applied to the
 // weights offline, so the product is unchanged in exact arithmetic.
 //
-// Mapping: eight lanes per 32-element block, four consecutive elements per
-// lane (one 8-byte fp16 load).  The butterflies of distance 1 and 2 are
-// in-lane, those of distance 4, 8 and 16 exchange values with lane L ^ 1,
-// L ^ 2, L ^ 4 of the block's eight; the absmax is a three-step exchange too.
-// A workgroup of 512 threads covers 32 rows of two neighbouring blocks: each
-// row's two blocks are one 128-byte line of fp16 input, read by one
-// workgroup (with one block per workgroup, neighbouring workgroups land on
-// different XCDs and both fetch the line), and each half writes its block's
-// matrix-core operand record (see common.h) in one coalesced kilobyte.
+// Mapping: four lanes per (row, 32-element block), lane L holding elements
+// 8L .. 8L + 7: butterfly stages 1, 2 and 4 run inside the lane, stages 8 and
+// 16 exchange values with lane L ^ 1 and L ^ 2 through DPP quad permutes (no
+// LDS traffic); the absmax is two more permutes, and each lane then derives
+// the block's scale itself.  A wave covers 16 rows of one block, so the
+// block's matrix-core operand record (see common.h) is written as coalesced
+// 128-byte runs per plane.
 //
 // The fp32 operation sequence is fixed and the same as a serial evaluation:
 // in stage h = 1, 2, 4, 8, 16 each pair (i, i + h) with i & h == 0 becomes
@@ -36,38 +34,59 @@ __device__ __forceinline__ float round_half_away(float x) {
     return frac >= 0.5f ? __fadd_rn(t, x < 0.0f ? -1.0f : 1.0f) : t;
 }
 
-// value of lane (self ^ mask) within the 8-lane group of a block
-__device__ __forceinline__ float xchg(float v, int mask) { return __shfl_xor(v, mask, 8); }
-__device__ __forceinline__ uint32_t xchg(uint32_t v, int mask) { return (uint32_t)__shfl_xor((int)v, mask, 8); }
 
-// Four consecutive elements as fp32 (exact from fp16).
-__device__ __forceinline__ void load4(const float *p, bool vec, float v[4]) {
-    if (vec) {
-        const float4 f = *reinterpret_cast<const float4 *>(p);
-        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+// Eight consecutive elements as fp32 (exact from fp16).  mode 2: 16-byte
+// aligned groups; mode 1: 4-element groups aligned (8 bytes fp16, 16 bytes
+// fp32); mode 0: one element at a time.
+__device__ __forceinline__ void load8(const float *p, int mode, float v[8]) {
+    if (mode > 0) {
+        const float4 f0 = reinterpret_cast<const float4 *>(p)[0], f1 = reinterpret_cast<const float4 *>(p)[1];
+        v[0] = f0.x; v[1] = f0.y; v[2] = f0.z; v[3] = f0.w;
+        v[4] = f1.x; v[5] = f1.y; v[6] = f1.z; v[7] = f1.w;
     } else {
-        for (int i = 0; i < 4; i++) v[i] = p[i];
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = p[j];
     }
 }
-__device__ __forceinline__ void load4(const __half *p, bool vec, float v[4]) {
-    if (vec) {
-        const uint2 u = *reinterpret_cast<const uint2 *>(p);
-        v[0] = __half2float(__ushort_as_half((uint16_t)(u.x & 0xffff)));
-        v[1] = __half2float(__ushort_as_half((uint16_t)(u.x >> 16)));
-        v[2] = __half2float(__ushort_as_half((uint16_t)(u.y & 0xffff)));
-        v[3] = __half2float(__ushort_as_half((uint16_t)(u.y >> 16)));
+__device__ __forceinline__ void halves_to_float(uint32_t u, float &lo, float &hi) {
+    lo = __half2float(__ushort_as_half((uint16_t)(u & 0xffff)));
+    hi = __half2float(__ushort_as_half((uint16_t)(u >> 16)));
+}
+__device__ __forceinline__ void load8(const __half *p, int mode, float v[8]) {
+    if (mode == 2) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(p);
+        halves_to_float(u.x, v[0], v[1]); halves_to_float(u.y, v[2], v[3]);
+        halves_to_float(u.z, v[4], v[5]); halves_to_float(u.w, v[6], v[7]);
+    } else if (mode == 1) {
+        const uint2 u0 = reinterpret_cast<const uint2 *>(p)[0], u1 = reinterpret_cast<const uint2 *>(p)[1];
+        halves_to_float(u0.x, v[0], v[1]); halves_to_float(u0.y, v[2], v[3]);
+        halves_to_float(u1.x, v[4], v[5]); halves_to_float(u1.y, v[6], v[7]);
     } else {
-        for (int i = 0; i < 4; i++) v[i] = __half2float(p[i]);
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = __half2float(p[j]);
     }
 }
 
-// One workgroup = 32 rows (row tile blockIdx.y) x two 32-element blocks
-// (2 blockIdx.x and 2 blockIdx.x + 1); thread t: block half t / 256, row
-// r = (t / 8) % 32 of the tile, lane L = t % 8 of the block, elements
-// 4L .. 4L + 3.  `vec`: every 4-element group is aligned for one vector load
-// (checked on the host).  With `act` set, also writes the block's operand
-// record for the matrix-core GEMM (the blocks then run over the padded block
-// count, an even number; padding rows and blocks get zero records).
+// Value of lane (self ^ 1), (self ^ 2) or (self + 1, clamped) within a quad of
+// lanes: DPP quad permutes.
+constexpr int QP_XOR1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int QP_XOR2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+constexpr int QP_NEXT = 0xF9;  // quad_perm [1, 2, 3, 3]
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float quad_f32(float v) {
+    return __uint_as_float(quad_u32<CTRL>(__float_as_uint(v)));
+}
+
+// One workgroup = 32 rows (row tile blockIdx.y) x 2 neighbouring blocks
+// (2 blockIdx.x and 2 blockIdx.x + 1), four lanes per (row, block): wave w
+// takes block w / 2 and rows 16 (w % 2) .. + 15, lane 4 i + L row i, elements
+// 8L .. 8L + 7.  With `act` set, also writes the blocks' operand records for
+// the matrix-core GEMM (the blocks then run over the padded block count;
+// padding rows and blocks get zero records).
 //
 // QMAX = 7: int4 codes (W4A4).  QMAX = 127: int8 codes for the exact int8
 // path on a rotated file (W4A8), one signed byte per element in `codes`
@@ -77,98 +96,117 @@ __device__ __forceinline__ void load4(const __half *p, bool vec, float v[4]) {
 // normalisation to fold in).
 constexpr int RQ_BLOCKS = 2;  // blocks per workgroup
 template <typename T, int QMAX = 7, bool ROTATE = true>
-__global__ __launch_bounds__(256 * RQ_BLOCKS) void rotate_quantize_kernel(const T *__restrict__ x, int64_t m,
-                                                                          int64_t k, int64_t ldx, bool vec,
+__global__ __launch_bounds__(128 * RQ_BLOCKS) void rotate_quantize_kernel(const T *__restrict__ x, int64_t m,
+                                                                          int64_t k, int64_t ldx, int mode,
                                                                           uint8_t *__restrict__ codes,
                                                                           float *__restrict__ scales,
                                                                           uint8_t *__restrict__ act) {
     static_assert(QMAX == 7 || QMAX == 127, "int4 or int8 codes");
     const int64_t nb = k / QK;
-    const int tid = threadIdx.x, L = tid & 7, r = (tid >> 3) & 31;
-    const int64_t b = (int64_t)blockIdx.x * RQ_BLOCKS + (tid >> 8), row = (int64_t)blockIdx.y * 32 + r;
-    const bool live = row < m && b < nb;  // uniform per 8-lane group
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, L = lane & 3;
+    const int r = (wave & 1) * 16 + (lane >> 2);  // row within the tile
+    const int64_t b = (int64_t)blockIdx.x * RQ_BLOCKS + (wave >> 1), row = (int64_t)blockIdx.y * 32 + r;
+    const bool live = row < m && b < nb;  // uniform per quad
 
-    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (live) load4(x + row * ldx + b * QK + 4 * L, vec, v);
+    float v[8];
+    if (live) {
+        load8(x + row * ldx + b * QK + 8 * L, mode, v);
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; t++) v[t] = 0.0f;
+    }
 
     if constexpr (ROTATE) {
-        // distance 1 and 2: inside the lane
-        {
-            const float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
-            v[0] = __fadd_rn(a0, a1); v[1] = __fsub_rn(a0, a1);
-            v[2] = __fadd_rn(a2, a3); v[3] = __fsub_rn(a2, a3);
-        }
-        {
-            const float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
-            v[0] = __fadd_rn(a0, a2); v[2] = __fsub_rn(a0, a2);
-            v[1] = __fadd_rn(a1, a3); v[3] = __fsub_rn(a1, a3);
-        }
-        // distance 4, 8, 16: partner lane L ^ 1, L ^ 2, L ^ 4 holds the other element
+        // stage h: each pair (i, i + h) with i & h == 0 becomes (v_i + v_{i+h}, v_i - v_{i+h})
 #pragma unroll
-        for (int mask = 1; mask < 8; mask <<= 1) {
-            const bool upper = (L & mask) != 0;
+        for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const float p = xchg(v[i], mask);
+            for (int i = 0; i < 8; i++) {
+                if (i & h) continue;
+                const float a0 = v[i], a1 = v[i + h];
+                v[i] = __fadd_rn(a0, a1);
+                v[i + h] = __fsub_rn(a0, a1);
+            }
+        }
+        // stages 8 and 16: the partner element sits in lane L ^ 1, L ^ 2
+        {
+            const bool upper = L & 1;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const float p = quad_f32<QP_XOR1>(v[i]);
                 v[i] = upper ? __fsub_rn(p, v[i]) : __fadd_rn(v[i], p);  // (lower - upper) / (lower + upper)
+            }
+        }
+        {
+            const bool upper = L & 2;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const float p = quad_f32<QP_XOR2>(v[i]);
+                v[i] = upper ? __fsub_rn(p, v[i]) : __fadd_rn(v[i], p);
             }
         }
     }
 
-    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    float amax = 0.0f;
 #pragma unroll
-    for (int mask = 1; mask < 8; mask <<= 1) amax = fmaxf(amax, xchg(amax, mask));
+    for (int t = 0; t < 8; t++) amax = fmaxf(amax, fabsf(v[t]));
+    amax = fmaxf(amax, quad_f32<QP_XOR1>(amax));
+    amax = fmaxf(amax, quad_f32<QP_XOR2>(amax));
 
     const float d = __fdiv_rn(amax, (float)QMAX);
     const bool nonzero = d >= 1.17549435e-38f;  // FLT_MIN: zero and subnormal scales give a zero block
     const float id = nonzero ? __fdiv_rn(1.0f, d) : 0.0f;
     const float s = !nonzero ? 0.0f : ROTATE ? __fmul_rn(d, kInvSqrt32f) : d;
-    int q[4];
+    int q[8];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-        q[i] = nonzero ? (int)fminf((float)QMAX, fmaxf(-(float)QMAX, round_half_away(__fmul_rn(v[i], id)))) : 0;
+    for (int t = 0; t < 8; t++)
+        q[t] = nonzero ? (int)fminf((float)QMAX, fmaxf(-(float)QMAX, round_half_away(__fmul_rn(v[t], id)))) : 0;
 
-    if constexpr (QMAX == 127) {  // int8 codes: lane L writes elements 4L .. 4L + 3
+    if constexpr (QMAX == 127) {  // int8 codes: lane L writes elements 8L .. 8L + 7
         if (live) {
-            const uint32_t word = (uint32_t)(q[0] & 0xFF) | (uint32_t)(q[1] & 0xFF) << 8 |
-                                  (uint32_t)(q[2] & 0xFF) << 16 | (uint32_t)(q[3] & 0xFF) << 24;
-            reinterpret_cast<uint32_t *>(codes + row * k + b * QK)[L] = word;
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                w0 |= (uint32_t)(q[i] & 0xFF) << (8 * i);
+                w1 |= (uint32_t)(q[4 + i] & 0xFF) << (8 * i);
+            }
+            *reinterpret_cast<uint2 *>(codes + row * k + b * QK + 8 * L) = make_uint2(w0, w1);
             if (L == 0) scales[row * nb + b] = s;
         }
         return;
     }
 
-    // public codes: byte j = code j | code j + 16 << 4; lane L < 4 writes bytes 4L .. 4L + 3
-    const uint32_t mine = (q[0] & 0xF) | (q[1] & 0xF) << 4 | (q[2] & 0xF) << 8 | (q[3] & 0xF) << 12;
-    const uint32_t high = xchg(mine, 4);  // codes 16 + 4L .. of lane L + 4
-    if (live && b < nb && codes) {
-        if (L < 4) {
-            uint32_t word = 0;
+    // public codes: byte j = code j | code j + 16 << 4; lane L < 2 writes bytes
+    // 8L .. 8L + 7 from its codes and those of lane L + 2
+    uint32_t nib0 = 0, nib1 = 0;  // this lane's 8 codes, one nibble each, in byte positions
 #pragma unroll
-            for (int i = 0; i < 4; i++) word |= (((mine >> (4 * i)) & 0xF) | ((high >> (4 * i)) & 0xF) << 4) << (8 * i);
-            reinterpret_cast<uint32_t *>(codes + row * (k / 2) + b * 16)[L] = word;
-        }
+    for (int i = 0; i < 4; i++) {
+        nib0 |= (uint32_t)(q[i] & 0xF) << (8 * i);
+        nib1 |= (uint32_t)(q[4 + i] & 0xF) << (8 * i);
+    }
+    const uint32_t hi0 = quad_u32<QP_XOR2>(nib0), hi1 = quad_u32<QP_XOR2>(nib1);
+    if (live && codes && L < 2) {
+        *reinterpret_cast<uint2 *>(codes + row * (k / 2) + b * 16 + 8 * L) = make_uint2(nib0 | hi0 << 4, nib1 | hi1 << 4);
         if (L == 0) scales[row * nb + b] = s;
     }
 
     if (act && b < mx_blocks(k)) {
-        // operand record of (row tile, block): row r's 32 codes are one 192-bit
-        // string of fp6 fields; this thread's four codes are its 24 bits at
-        // bit 24 L.  Lanes 0, 3 and 6 write the planes (bits 64 p .. 64 p + 63).
-        uint32_t f24 = 0;
+        // operand record of (row tile, block): row r's 32 codes as one 192-bit
+        // string of fp6 fields; this lane's 8 codes are 48 bits at bit 48 L,
+        // lanes 0, 1, 2 write planes 0, 1, 2 (bits 64 p .. 64 p + 63)
+        uint64_t mine = 0;
 #pragma unroll
-        for (int i = 0; i < 4; i++) f24 |= fp6_e2m3_of(live ? q[i] : 0) << (6 * i);
-        const uint32_t n1 = (uint32_t)__shfl_down((int)f24, 1, 8), n2 = (uint32_t)__shfl_down((int)f24, 2, 8);
-        const uint32_t p1 = (uint32_t)__shfl_up((int)f24, 1, 8);  // lanes L + 1, L + 2, L - 1
+        for (int t = 0; t < 8; t++) mine |= (uint64_t)fp6_e2m3_of(q[t]) << (6 * t);
+        const uint64_t next = (uint64_t)quad_u32<QP_NEXT>((uint32_t)mine) |
+                              (uint64_t)quad_u32<QP_NEXT>((uint32_t)(mine >> 32)) << 32;
         uint8_t *rec = act + ((int64_t)blockIdx.y * mx_blocks(k) + b) * MX_REC;
-        if (L == 0) reinterpret_cast<uint2 *>(rec)[r] = make_uint2(f24 | n1 << 24, n1 >> 8 | n2 << 16);
-        if (L == 3) reinterpret_cast<uint2 *>(rec + 256)[r] = make_uint2(p1 >> 16 | f24 << 8, n1 | n2 << 24);
-        if (L == 6) reinterpret_cast<uint2 *>(rec + 512)[r] = make_uint2(p1 >> 8 | f24 << 16, f24 >> 16 | n1 << 8);
-        if (L == 0) {
+        if (L < 3) {
+            const uint64_t plane = L == 0 ? (mine | next << 48) : L == 1 ? (mine >> 16 | next << 32) : (mine >> 32 | next << 16);
+            reinterpret_cast<uint2 *>(rec + 256 * L)[r] = make_uint2((uint32_t)plane, (uint32_t)(plane >> 32));
+        } else {
             // exact bf16 split s = s1 + s2 + s3 (truncations; each remainder is exact)
-            const float sl = live ? s : 0.0f;
-            const uint32_t h1 = __float_as_uint(sl) & 0xFFFF0000u;
-            const float r1 = __fsub_rn(sl, __uint_as_float(h1));
+            const uint32_t h1 = __float_as_uint(s) & 0xFFFF0000u;
+            const float r1 = __fsub_rn(s, __uint_as_float(h1));
             const uint32_t h2 = __float_as_uint(r1) & 0xFFFF0000u;
             const float r2 = __fsub_rn(r1, __uint_as_float(h2));
             const uint32_t h3 = __float_as_uint(r2) & 0xFFFF0000u;

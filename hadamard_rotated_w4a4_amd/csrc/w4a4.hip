@@ -209,15 +209,16 @@ w4a4_status rotate_quantize(bool a8, const void *x, w4a4_dtype dt, int64_t m, in
         if (act_bytes < w4a4_act_operand_bytes(m, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
     }
     const size_t esz = dt == W4A4_DTYPE_F32 ? 4 : 2;
-    // every 4-element group aligned for one vector load (8 bytes fp16, 16 bytes fp32)
-    const bool vec = aligned(x, 4 * esz) && (ldx % 4) == 0;
+    // vector loads of a block: 16-byte (every block start 16-byte aligned),
+    // 4-element (every 4-element group aligned), or none
+    const int vec = aligned(x, 16) && (ldx * esz) % 16 == 0 ? 2 : aligned(x, 4 * esz) && (ldx % 4) == 0 ? 1 : 0;
     const int64_t blocks = act ? mx_blocks(k) : k / QK;
     const dim3 grid((unsigned)((blocks + RQ_BLOCKS - 1) / RQ_BLOCKS), (unsigned)((m + 31) / 32));
     hipStream_t s = as_stream(stream);
     uint8_t *a = static_cast<uint8_t *>(act);
     const float *xf = static_cast<const float *>(x);
     const __half *xh = static_cast<const __half *>(x);
-    const unsigned nt = 256 * RQ_BLOCKS;
+    const unsigned nt = 128 * RQ_BLOCKS;
     if (!rotate && dt == W4A4_DTYPE_F32) rotate_quantize_kernel<float, 7, false><<<grid, nt, 0, s>>>(xf, m, k, ldx, vec, codes, scales, a);
     else if (!rotate) rotate_quantize_kernel<__half, 7, false><<<grid, nt, 0, s>>>(xh, m, k, ldx, vec, codes, scales, a);
     else if (dt == W4A4_DTYPE_F32 && a8) rotate_quantize_kernel<float, 127><<<grid, nt, 0, s>>>(xf, m, k, ldx, vec, codes, scales, a);
