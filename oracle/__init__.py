@@ -64,6 +64,9 @@ def _load():
         lib.oracle_block_sums_a8.argtypes = [P, P, I64, I64, I64, P]
         lib.oracle_gemm_a8.argtypes = [P, P, P, I64, I64, I64, P, I64, ctypes.c_int]
         lib.oracle_quantize_act_plain.argtypes = [P, ctypes.c_int, I64, I64, I64, P, P, ctypes.c_int]
+        lib.oracle_rotate_act16.argtypes = [P, ctypes.c_int, I64, I64, I64, P, ctypes.c_int]
+        lib.oracle_dequantize_w16.argtypes = [P, I64, I64, P]
+        lib.oracle_gemm_w16.argtypes = [P, P, I64, I64, I64, P, I64, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -176,6 +179,40 @@ def quantize_act_plain(x: np.ndarray, k: int | None = None, threads: int | None 
 def prepare_weights_plain(w: np.ndarray, threads: int | None = None) -> np.ndarray:
     """R9 (unrotated ablation): plain Q4_0 of the unrotated weights."""
     return q4_0_quantize(w, threads)
+
+
+def rotate_act16(x: np.ndarray, k: int | None = None, threads: int | None = None) -> np.ndarray:
+    """R10: x fp32 or fp16 [m, ldx] -> rotated activations as fp16 [m, k]."""
+    assert x.dtype in (np.float32, np.float16)
+    x = np.ascontiguousarray(x)
+    m, ldx = x.shape
+    k = ldx if k is None else k
+    assert k % QK == 0 and k <= ldx
+    out = np.empty((m, k), np.uint16)
+    _load().oracle_rotate_act16(_ptr(x), 0 if x.dtype == np.float32 else 1, m, k, ldx, _ptr(out),
+                                threads or default_threads())
+    return out.view(np.float16)
+
+
+def dequantize_w16(q4: np.ndarray, k: int) -> np.ndarray:
+    """R10: Q4_0 bytes [n, k/32, 18] -> dequantised weights as fp16 [n, k]."""
+    q4 = np.ascontiguousarray(q4, np.uint8)
+    n = q4.shape[0]
+    out = np.empty((n, k), np.uint16)
+    _load().oracle_dequantize_w16(_ptr(q4), n, k, _ptr(out))
+    return out.view(np.float16)
+
+
+def gemm_w16(w16: np.ndarray, x16: np.ndarray, threads: int | None = None) -> np.ndarray:
+    """R10: fp32 [m, n] = fp64 sums of the fp16 operands' products, rounded once."""
+    w16 = np.ascontiguousarray(w16, np.float16)
+    x16 = np.ascontiguousarray(x16, np.float16)
+    n, k = w16.shape
+    m = x16.shape[0]
+    assert x16.shape[1] == k
+    y = np.empty((m, n), np.float32)
+    _load().oracle_gemm_w16(_ptr(w16), _ptr(x16), m, n, k, _ptr(y), n, threads or default_threads())
+    return y
 
 
 def block_sums(q4: np.ndarray, codes: np.ndarray, k: int) -> np.ndarray:

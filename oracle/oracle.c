@@ -58,6 +58,14 @@
  *       no rotation and no normalisation: v = x, d = amax/7, id = 1/d,
  *       q = clamp(round_half_away(v*id), -7, 7), s = d, zero blocks as in
  *       R5; the output is R6 with these codes and scales.
+ *   R10 Rotated W4A16, the page's route where the rotated file runs with the
+ *       activations rotated but not rounded to 4 bits (section
+ *       "Hadamard-rotated Q4_0: W4A4 prompt processing"; no rule printed):
+ *       activations x16_t = fp16( fl(v_t * c32) ) with v the R4 butterflies
+ *       of the block (fp16 round to nearest even); weights dequantised as
+ *       w16_t = fp16( fl(dw * (q_t - 8)) ) with dw = fp32(fp16 d) (the fp32
+ *       product is exact; one rounding to fp16); output y[m][n] = sum over k
+ *       of (double)w16 * (double)x16 in fp64, rounded once to fp32.
  *
  * Byte layouts:
  *   Q4_0 block (18 bytes): fp16 d (little endian), then 16 bytes; byte j holds
@@ -444,6 +452,78 @@ void oracle_quantize_act_plain(const void *x, int dtype, int64_t m, int64_t k, i
 {
     act_ctx c = {x, dtype, k, ldx, codes, scales};
     parallel_rows(m, nthreads, act_plain_rows, &c);
+}
+
+/* R10 activations: x fp32/fp16 [m][ldx] -> rotated fp16 bits [m][k]. */
+typedef struct {
+    const void *x;
+    int dtype;
+    int64_t k, ldx;
+    uint16_t *xr;
+} rot16_ctx;
+
+static void rot16_rows(void *p, int64_t r0, int64_t r1)
+{
+    rot16_ctx *c = (rot16_ctx *)p;
+    const int64_t k = c->k, nb = k / QK;
+    const float cc = oracle_c32();
+    for (int64_t r = r0; r < r1; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            float v[QK];
+            load_block(c->x, c->dtype, c->ldx, r, b, v);
+            oracle_fwht32_f32(v);
+            for (int t = 0; t < QK; t++)
+                c->xr[r * k + b * QK + t] = oracle_float_to_half(v[t] * cc);
+        }
+    }
+}
+
+void oracle_rotate_act16(const void *x, int dtype, int64_t m, int64_t k, int64_t ldx, uint16_t *xr,
+                         int nthreads)
+{
+    rot16_ctx c = {x, dtype, k, ldx, xr};
+    parallel_rows(m, nthreads, rot16_rows, &c);
+}
+
+/* R10 weights: Q4_0 [n][k/32][18] -> dequantised fp16 bits [n][k]. */
+void oracle_dequantize_w16(const uint8_t *q4, int64_t n, int64_t k, uint16_t *w16)
+{
+    const int64_t nb = k / QK;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t b = 0; b < nb; b++) {
+            const uint8_t *blk = q4 + (r * nb + b) * 18;
+            const float d = q4_scale(blk);
+            for (int t = 0; t < QK; t++)
+                w16[r * k + b * QK + t] = oracle_float_to_half(d * (float)(q4_code(blk, t) - 8));
+        }
+}
+
+/* R10 output: y[m][n] = fp32( sum_k (double)w16 * (double)x16 ), fp64 sums. */
+typedef struct {
+    const uint16_t *w16, *x16;
+    int64_t n, k;
+    float *y;
+    int64_t ldy;
+} gemm16_ctx;
+
+static void gemm16_rows(void *p, int64_t r0, int64_t r1)
+{
+    gemm16_ctx *c = (gemm16_ctx *)p;
+    for (int64_t r = r0; r < r1; r++)
+        for (int64_t j = 0; j < c->n; j++) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < c->k; t++)
+                acc += (double)oracle_half_to_float(c->w16[j * c->k + t]) *
+                       (double)oracle_half_to_float(c->x16[r * c->k + t]);
+            c->y[r * c->ldy + j] = (float)acc;
+        }
+}
+
+void oracle_gemm_w16(const uint16_t *w16, const uint16_t *x16, int64_t m, int64_t n, int64_t k, float *y,
+                     int64_t ldy, int nthreads)
+{
+    gemm16_ctx c = {w16, x16, n, k, y, ldy};
+    parallel_rows(m, nthreads, gemm16_rows, &c);
 }
 
 static void act8_rows(void *p, int64_t r0, int64_t r1)

@@ -615,3 +615,70 @@ def test_ablation_without_rotation_costs_more():
     err_rot = np.abs(y_rot - ref).mean()
     err_plain = np.abs(y_plain - ref).mean()
     assert err_plain > 1.3 * err_rot
+
+
+# --------------------------------------------------------------------------
+# Rotated W4A16 (reading R10): rotated fp16 activations, fp16-dequantised Q4_0
+# --------------------------------------------------------------------------
+
+def test_act16_is_the_rounded_fwht():
+    """x16 = fp16(fl(FWHT(x) * c32)): the pinned butterflies, then numpy's own
+    fp16 rounding (nearest even) of the fp32 product."""
+    rng = np.random.default_rng(51)
+    for dtype in (np.float32, np.float16):
+        x = synth.activations(5, 160, rng, 2).astype(dtype)
+        got = oracle.rotate_act16(x)
+        c32 = np.float32(oracle.c32())
+        want = np.stack([(oracle.fwht32_f32(blk.astype(np.float32)) * c32).astype(np.float16)
+                         for blk in x.reshape(-1, 32)]).reshape(5, 160)
+        assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+def test_act16_closed_forms():
+    """Constant block a: (32 a c32, 0, ..., 0); one-hot a e_j: a c32 H[:, j],
+    each rounded to fp16."""
+    c32 = np.float32(oracle.c32())
+    for a in (0.5, -3.0, 1e-3):
+        got = oracle.rotate_act16(np.full((1, 32), a, np.float32))[0]
+        assert got[0] == np.float16(np.float32(np.float32(32 * np.float32(a)) * c32)) and not got[1:].any()
+    for j in (0, 9, 31):
+        x = np.zeros((1, 32), np.float32)
+        x[0, j] = -7.5
+        got = oracle.rotate_act16(x)[0].astype(np.float64)
+        assert np.array_equal(got, float(np.float16(np.float32(np.float32(7.5) * c32))) * -H_SCIPY[:, j])
+
+
+def test_w16_dequantisation_from_the_bytes():
+    """w16 = fp16(fl(d * (q - 8))) decoded straight from the Q4_0 bytes with
+    numpy: d from the little-endian fp16, codes from the nibbles."""
+    rng = np.random.default_rng(53)
+    w = synth.weights(7, 96, rng)
+    q4 = oracle.prepare_weights(w)
+    got = oracle.dequantize_w16(q4, 96)
+    d = q4[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float32)          # [n, nb]
+    lo, hi = q4[..., 2:] & 0xF, q4[..., 2:] >> 4                                  # codes j, j + 16
+    q = np.concatenate([lo, hi], axis=-1).astype(np.float32) - 8.0               # [n, nb, 32]
+    want = (d[..., None] * q).astype(np.float16).reshape(7, 96)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+def test_gemm_w16_is_the_fp64_product_of_the_operands():
+    rng = np.random.default_rng(55)
+    w16 = oracle.dequantize_w16(oracle.prepare_weights(synth.weights(24, 128, rng)), 128)
+    x16 = oracle.rotate_act16(synth.activations(9, 128, rng, 2))
+    y = oracle.gemm_w16(w16, x16).astype(np.float64)
+    ref = x16.astype(np.float64) @ w16.astype(np.float64).T
+    # fp64 sums in another order differ far below half an fp32 ulp of the result
+    assert np.array_equal(y.astype(np.float32), ref.astype(np.float32)) or \
+        (np.abs(y - ref) <= np.abs(ref) * 2.0 ** -23).all()
+
+
+def test_w4a16_error_below_w4a4():
+    """Keeping the rotated activations at 16 bits lands closer to the exact
+    product than rounding them to 4 bits (same rotated Q4_0 weights)."""
+    d = synth.tiny()
+    ref = d.x.astype(np.float64) @ d.w.astype(np.float64).T
+    q4 = oracle.prepare_weights(d.w)
+    y16 = oracle.gemm_w16(oracle.dequantize_w16(q4, d.k), oracle.rotate_act16(d.x))
+    y4 = oracle.gemm(q4, *oracle.rotate_quantize_act(d.x), d.k)
+    assert np.abs(y16 - ref).mean() < 0.9 * np.abs(y4 - ref).mean()
