@@ -18,7 +18,8 @@ Prints ONE JSON line (stdout).  Besides the contract's fields it carries:
   cpu_baseline  the CPU oracle (test infrastructure) timed on a bounded sample
                 of the same workload on the host cores;
   extras        the 16-token verify set (GB/s vs 8 TB/s), the MoE layer
-                (MUL_MAT_ID) and the dense layer set over a 1,838-token prompt.
+                (MUL_MAT_ID), W4A8-H32, rotated W4A16, the unrotated ablation
+                and the dense layer set over a 1,838-token prompt.
 """
 from __future__ import annotations
 
@@ -37,10 +38,11 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
 PEAK_FP6_TOPS = 10100.0      # MI355X dense FP6 / FP4 MFMA, TFLOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+PEAK_FP16_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 MFMA, TFLOP/s
 COLD_BYTES = 1 << 30         # weight copies rotated per step exceed this
 PROFILE_JSON = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "hadamard_rotated_w4a4_amd", "csrc", f)
-                  for f in ("common.h", "k_route.h", "k_dense.h", "k_smallm.h", "k_grouped.h", "k_rotq.h", "k_prep.h", "w4a4.hip")]
+                  for f in ("common.h", "k_route.h", "k_dense.h", "k_smallm.h", "k_grouped.h", "k_rotq.h", "k_prep.h", "k_w16.h", "w4a4.hip")]
 
 
 def log(msg):
@@ -290,6 +292,49 @@ def run_w4a8(torch, ops, synth):
             "timing": "events over back-to-back calls (M=512); HIP graph replay (m=16)"}
 
 
+def run_w4a16(torch, ops, synth):
+    """Rotated W4A16 (section "Hadamard-rotated Q4_0: W4A4 prompt processing":
+    the rotated file with 16-bit rotated activations): the FFN-up step at
+    M=512, fp16 operands on the fp16 matrix cores, and its error against the
+    exact product beside W4A4's on sampled rows."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    d = synth.ffn_up()
+    w = torch.from_numpy(d.w).to(dev)
+    q4 = ops.quantize_q4_0_h32(w)
+    w16 = ops.dequantize_w16(q4, d.n, d.k)
+    packed = ops.repack_q4_0_h32(q4, d.n, d.k)
+    del w
+    nbytes = w16.numel() * w16.element_size()
+    copies = [w16] + [w16.clone() for _ in range(max(1, -(-COLD_BYTES // nbytes) - 1))]
+    x = torch.from_numpy(d.x).to(dev)
+    a16 = ops.rotate_act16(x)
+    y = torch.empty((d.m, d.n), dtype=torch.float32, device=dev)
+
+    def step(i):
+        ops.rotate_act16(x, out=a16)
+        ops.gemm_w16(copies[i % len(copies)], a16, d.m, d.n, d.k, y=y)
+    for i in range(3):
+        step(i)
+    step_us = events_ms(torch, step, 10) * 1e3
+    gemm_us = events_ms(torch, lambda i: ops.gemm_w16(copies[i % len(copies)], a16, d.m, d.n, d.k, y=y), 10) * 1e3
+    rot_us = events_ms(torch, lambda i: ops.rotate_act16(x, out=a16), 20) * 1e3
+    flops = 2.0 * d.m * d.n * d.k
+    rows = np.arange(0, d.m, d.m // 16)
+    ops.gemm_w16(w16, a16, d.m, d.n, d.k, y=y)
+    y4 = ops.gemm(packed, *ops.rotate_quantize_act(x), d.n, d.k)
+    torch.cuda.synchronize()
+    exact = d.x[rows].astype(np.float64) @ d.w.astype(np.float64).T
+    err = {name: float(np.abs(t.cpu().numpy()[rows].astype(np.float64) - exact).mean())
+           for name, t in (("w4a16", y), ("w4a4", y4))}
+    return {"workload": d.name, "step_us": round(step_us, 2), "gemm_us": round(gemm_us, 2),
+            "rotate_act16_us": round(rot_us, 2), "tokens/s": round(d.m / (step_us * 1e-6), 1),
+            "TFLOP/s": round(flops / (gemm_us * 1e-6) / 1e12, 1),
+            "frac_of_fp16_peak": round(flops / (gemm_us * 1e-6) / 1e12 / PEAK_FP16_TFLOPS, 4),
+            "mean_abs_err": {k_: round(v, 6) for k_, v in err.items()}, "rows_sampled": len(rows),
+            "timing": "events over back-to-back calls"}
+
+
 def run_ablation(torch, ops, synth):
     """Unrotated W4A4 ablation (section "MoE: W4A4 on the experts": without
     the rotation W4A4 costs about twice the accuracy): the FFN-up workload
@@ -457,6 +502,8 @@ def main():
         log("[bench] extra: W4A8-H32 (int8 activations)")
         extras["w4a8"] = run_w4a8(torch, ops, synth)
         log(f"[bench] w4a8: {extras['w4a8']['ffn_up_m512']}")
+        extras["w4a16"] = run_w4a16(torch, ops, synth)
+        log(f"[bench] w4a16: {extras['w4a16']['gemm_us']} us, {extras['w4a16']['TFLOP/s']} TFLOP/s")
         extras["ablation_unrotated"] = run_ablation(torch, ops, synth)
         log(f"[bench] ablation: error ratio {extras['ablation_unrotated']['err_ratio_unrotated_over_rotated']}")
         log("[bench] extra: dense layer set over a 1,838-token prompt")

@@ -53,6 +53,11 @@ def lib() -> ctypes.CDLL:
             "w4a4_gemm_a8_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_gemm_a8": ([P, P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_id": ([P, I64, P, P, I64, P, I64, I64, P, I64, I64, P, SZ, P], ST),
+            "w4a4_w16_weight_bytes": ([I64, I64], SZ),
+            "w4a4_w16_act_bytes": ([I64, I64], SZ),
+            "w4a4_dequantize_w16": ([P, I64, I64, P, SZ, P], ST),
+            "w4a4_rotate_act16": ([P, ST, I64, I64, I64, P, SZ, P], ST),
+            "w4a4_gemm_w16": ([P, P, P, I64, I64, I64, I64, P], ST),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -311,3 +316,52 @@ def prepare_weights_plain(w: torch.Tensor) -> torch.Tensor:
     """fp32 [n, k] -> plain (unrotated) Q4_0 -> packed buffer (the ablation's weights)."""
     n, k = w.shape
     return repack_q4_0_h32(quantize_q4_0(w), n, k)
+
+
+# --------------------------------------------------------------------------
+# Rotated W4A16: the rotated Q4_0 weights against rotated fp16 activations
+# --------------------------------------------------------------------------
+
+def w16_row_stride(k: int) -> int:
+    """Elements per row of both padded fp16 operands (the block count padded to 8)."""
+    return (k // 32 + 7) // 8 * 8 * 32
+
+
+def dequantize_w16(q4: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Q4_0 bytes -> fp16 [ceil(n/32)*32, w16_row_stride(k)], zero-padded."""
+    _require_cuda(q4, out)
+    need = int(lib().w4a4_w16_weight_bytes(n, k))
+    if out is None:
+        out = torch.empty(((n + 31) // 32 * 32, w16_row_stride(k)), dtype=torch.float16, device=q4.device)
+    _check(lib().w4a4_dequantize_w16(_ptr(q4), n, k, _ptr(out), out.numel() * out.element_size(),
+                                     _stream(q4.device)), "w4a4_dequantize_w16")
+    assert out.numel() * out.element_size() >= need
+    return out
+
+
+def rotate_act16(x: torch.Tensor, k: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """x fp16/fp32 [m, >=k] -> rotated fp16 [ceil(m/32)*32, w16_row_stride(k)], zero-padded."""
+    _require_cuda(x, out)
+    assert x.dim() == 2 and x.stride(1) == 1
+    dt = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16}.get(x.dtype)
+    if dt is None:
+        raise W4A4Error(f"unsupported activation dtype {x.dtype}")
+    m = x.shape[0]
+    k = x.shape[1] if k is None else k
+    if out is None:
+        out = torch.empty(((m + 31) // 32 * 32, w16_row_stride(k)), dtype=torch.float16, device=x.device)
+    _check(lib().w4a4_rotate_act16(_ptr(x), dt, m, k, x.stride(0), _ptr(out), out.numel() * out.element_size(),
+                                   _stream(x.device)), "w4a4_rotate_act16")
+    return out
+
+
+def gemm_w16(w16: torch.Tensor, a16: torch.Tensor, m: int, n: int, k: int,
+             y: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A16 product of the two padded fp16 operands: fp32 [m, n] (row stride y.stride(0))."""
+    _require_cuda(w16, a16, y)
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=a16.device)
+    assert y.stride(1) == 1
+    _check(lib().w4a4_gemm_w16(_ptr(w16), _ptr(a16), _ptr(y), m, n, k, y.stride(0), _stream(a16.device)),
+           "w4a4_gemm_w16")
+    return y

@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libw4a4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = [os.path.join(CSRC, "w4a4.hip")]
-HEADERS = [os.path.join(CSRC, h) for h in ("common.h", "k_prep.h", "k_rotq.h", "k_route.h", "k_dense.h", "k_smallm.h", "k_grouped.h")] + [
+HEADERS = [os.path.join(CSRC, h) for h in ("common.h", "k_prep.h", "k_rotq.h", "k_route.h", "k_dense.h", "k_smallm.h", "k_grouped.h", "k_w16.h")] + [
     os.path.join(ROOT, "include", "w4a4.h")]
 
 FLAGS = [

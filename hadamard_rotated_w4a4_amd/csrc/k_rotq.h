@@ -81,6 +81,39 @@ __device__ __forceinline__ float quad_f32(float v) {
     return __uint_as_float(quad_u32<CTRL>(__float_as_uint(v)));
 }
 
+// The five butterfly stages of one block held by a quad of lanes (lane L:
+// elements 8L .. 8L + 7): stages 1, 2, 4 in the lane, 8 and 16 with lane
+// L ^ 1, L ^ 2.  Stage h turns each pair (i, i + h) with i & h == 0 into
+// (v_i + v_{i+h}, v_i - v_{i+h}).
+__device__ __forceinline__ void fwht32_quad(float v[8], int L) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            if (i & h) continue;
+            const float a0 = v[i], a1 = v[i + h];
+            v[i] = __fadd_rn(a0, a1);
+            v[i + h] = __fsub_rn(a0, a1);
+        }
+    }
+    {
+        const bool upper = L & 1;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float p = quad_f32<QP_XOR1>(v[i]);
+            v[i] = upper ? __fsub_rn(p, v[i]) : __fadd_rn(v[i], p);  // (lower - upper) / (lower + upper)
+        }
+    }
+    {
+        const bool upper = L & 2;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float p = quad_f32<QP_XOR2>(v[i]);
+            v[i] = upper ? __fsub_rn(p, v[i]) : __fadd_rn(v[i], p);
+        }
+    }
+}
+
 // One workgroup = 32 rows (row tile blockIdx.y) x 2 neighbouring blocks
 // (2 blockIdx.x and 2 blockIdx.x + 1), four lanes per (row, block): wave w
 // takes block w / 2 and rows 16 (w % 2) .. + 15, lane 4 i + L row i, elements
@@ -116,36 +149,7 @@ __global__ __launch_bounds__(128 * RQ_BLOCKS) void rotate_quantize_kernel(const 
         for (int t = 0; t < 8; t++) v[t] = 0.0f;
     }
 
-    if constexpr (ROTATE) {
-        // stage h: each pair (i, i + h) with i & h == 0 becomes (v_i + v_{i+h}, v_i - v_{i+h})
-#pragma unroll
-        for (int h = 1; h < 8; h <<= 1) {
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                if (i & h) continue;
-                const float a0 = v[i], a1 = v[i + h];
-                v[i] = __fadd_rn(a0, a1);
-                v[i + h] = __fsub_rn(a0, a1);
-            }
-        }
-        // stages 8 and 16: the partner element sits in lane L ^ 1, L ^ 2
-        {
-            const bool upper = L & 1;
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const float p = quad_f32<QP_XOR1>(v[i]);
-                v[i] = upper ? __fsub_rn(p, v[i]) : __fadd_rn(v[i], p);  // (lower - upper) / (lower + upper)
-            }
-        }
-        {
-            const bool upper = L & 2;
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const float p = quad_f32<QP_XOR2>(v[i]);
-                v[i] = upper ? __fsub_rn(p, v[i]) : __fadd_rn(v[i], p);
-            }
-        }
-    }
+    if constexpr (ROTATE) fwht32_quad(v, L);
 
     float amax = 0.0f;
 #pragma unroll

@@ -17,6 +17,7 @@
 #include "k_rotq.h"
 #include "k_route.h"
 #include "k_smallm.h"
+#include "k_w16.h"
 
 using namespace w4a4;
 
@@ -418,6 +419,79 @@ w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, 
     a.k = k;
     launch_mx(a, s);
     return hip_status("gemm_mx_kernel");
+}
+
+size_t w4a4_w16_weight_bytes(int64_t n, int64_t k) {
+    if (n < 0 || k < 0 || k % QK) return 0;
+    return (size_t)(padded_n(n) * w16_row_stride(k) * 2);
+}
+
+size_t w4a4_w16_act_bytes(int64_t m, int64_t k) {
+    if (m < 0 || k < 0 || k % QK) return 0;
+    return (size_t)((m + 31) / 32 * 32 * w16_row_stride(k) * 2);
+}
+
+w4a4_status w4a4_dequantize_w16(const void *q4_0, int64_t n, int64_t k, void *w16, size_t w16_bytes,
+                                void *stream) {
+    if (n < 0 || k < 0) return W4A4_ERR_INVALID_VALUE;
+    if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
+    if (n == 0 || k == 0) return W4A4_OK;
+    if (!q4_0 || !w16) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(w16, 16)) return W4A4_ERR_MISALIGNED;
+    if (w16_bytes < w4a4_w16_weight_bytes(n, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
+    const int64_t threads = padded_n(n) * mx_blocks(k);
+    dequantize_w16_kernel<<<blocks_for(threads, 256), 256, 0, as_stream(stream)>>>(
+        static_cast<const uint8_t *>(q4_0), n, k, static_cast<_Float16 *>(w16));
+    return hip_status("dequantize_w16_kernel");
+}
+
+w4a4_status w4a4_rotate_act16(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx, void *a16,
+                              size_t a16_bytes, void *stream) {
+    if (dt != W4A4_DTYPE_F32 && dt != W4A4_DTYPE_F16) return W4A4_ERR_UNSUPPORTED_DTYPE;
+    if (m < 0 || k < 0 || ldx < k || m > kMaxRows) return W4A4_ERR_INVALID_VALUE;
+    if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
+    if (m == 0 || k == 0) return W4A4_OK;
+    if (!x || !a16) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(x, dt == W4A4_DTYPE_F32 ? 4 : 2) || !aligned(a16, 16)) return W4A4_ERR_MISALIGNED;
+    if (a16_bytes < w4a4_w16_act_bytes(m, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
+    const size_t esz = dt == W4A4_DTYPE_F32 ? 4 : 2;
+    const int vec = aligned(x, 16) && (ldx * esz) % 16 == 0 ? 2 : aligned(x, 4 * esz) && (ldx % 4) == 0 ? 1 : 0;
+    const dim3 grid((unsigned)(mx_blocks(k) / 2), (unsigned)((m + 31) / 32));
+    hipStream_t s = as_stream(stream);
+    _Float16 *out = static_cast<_Float16 *>(a16);
+    if (dt == W4A4_DTYPE_F32)
+        rotate_act16_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(x), m, k, ldx, vec, out);
+    else
+        rotate_act16_kernel<__half><<<grid, 256, 0, s>>>(static_cast<const __half *>(x), m, k, ldx, vec, out);
+    return hip_status("rotate_act16_kernel");
+}
+
+w4a4_status w4a4_gemm_w16(const void *w16, const void *a16, float *y, int64_t m, int64_t n, int64_t k,
+                          int64_t ldy, void *stream) {
+    if (m < 0 || n < 0 || k < 0 || m > kMaxRows || ldy < n) return W4A4_ERR_INVALID_VALUE;
+    if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
+    if (m == 0 || n == 0) return W4A4_OK;
+    if (!y) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(y, 4)) return W4A4_ERR_MISALIGNED;
+    hipStream_t s = as_stream(stream);
+    if (k == 0) {  // empty sum
+        zero_rows_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(y, m, n, ldy);
+        return hip_status("zero_rows_kernel");
+    }
+    if (!w16 || !a16) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(w16, 16) || !aligned(a16, 16)) return W4A4_ERR_MISALIGNED;
+    const int64_t tiles = (m + 127) / 128 * ((n + 127) / 128);
+    if (tiles >= (int64_t{1} << 24)) return W4A4_ERR_INVALID_VALUE;  // grid of < 2^32 threads
+    W16Args a{};
+    a.a16 = static_cast<const _Float16 *>(a16);
+    a.w16 = static_cast<const _Float16 *>(w16);
+    a.y = y;
+    a.ldy = ldy;
+    a.m = m;
+    a.n = n;
+    a.k = k;
+    gemm_w16_kernel<<<(unsigned)tiles, 256, 0, s>>>(a);
+    return hip_status("gemm_w16_kernel");
 }
 
 namespace {

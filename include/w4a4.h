@@ -217,6 +217,58 @@ w4a4_status w4a4_quantize_q4_0(const float *w, int64_t n, int64_t k, int64_t ldw
 w4a4_status w4a4_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx, uint8_t *codes,
                               float *scales, void *stream);
 
+/*
+ * Rotated W4A16 (section "Hadamard-rotated Q4_0: W4A4 prompt processing":
+ * the rotated Q4_0 files also run with the activations rotated and kept at
+ * 16 bits, with no 4-bit activation step).  Both operands are fp16 matrices
+ * in a padded row-major layout shared by the three calls below:
+ *   row stride kp = nbp * 32 elements, nbp = ceil(k / 32 / 8) * 8 (the
+ *   block count padded to a multiple of 8); rows padded to a multiple of 32;
+ *   every element past k in a row, and every padding row, is +0.
+ * The padding lets the GEMM load whole 32-row, 8-block tiles without bounds
+ * checks; it contributes exact zeros to every sum.
+ *
+ * w4a4_w16_weight_bytes(n, k): bytes of the dequantised weights,
+ *   ceil(n / 32) * 32 * kp * 2.  w4a4_w16_act_bytes(m, k): bytes of the
+ *   rotated activations, ceil(m / 32) * 32 * kp * 2.  Both 0 for invalid
+ *   sizes; host only, pure.
+ *
+ * w4a4_dequantize_w16: Q4_0 [n][k/32] blocks (as w4a4_quantize_q4_0_h32
+ *   writes them) -> w16, element t of block b of row r =
+ *   fp16(fl(d * (q_t - 8))) (d the block's fp16 scale as fp32; the product
+ *   is exact, one rounding to nearest even).  w16: device, 16-byte aligned,
+ *   at least w4a4_w16_weight_bytes(n, k) bytes (else
+ *   W4A4_ERR_WORKSPACE_TOO_SMALL), fully written including the padding.
+ *   Done once per weight matrix.
+ *
+ * w4a4_rotate_act16: x as w4a4_rotate_quantize_act (fp32 or fp16 [m][ldx],
+ *   element-aligned) -> a16, element t of block b of row r =
+ *   fp16(fl(v_t * c32)) with v the block's unnormalised 32-point
+ *   Walsh-Hadamard butterflies in fp32 (the same sums the W4A4 quantiser
+ *   forms) and c32 = fp32(1/sqrt(32)).  a16: device, 16-byte aligned, at
+ *   least w4a4_w16_act_bytes(m, k) bytes, fully written including padding.
+ *
+ * w4a4_gemm_w16: y[i][j] = sum over t < k of a16[i][t] * w16[j][t], fp32
+ *   sums of the exact fp16 products (the summation order is the matrix
+ *   cores', not fixed).  a16, w16 as the two calls above write them, for
+ *   the same k; y: fp32 [m][ldy], ldy >= n, 4-byte aligned; only the m x n
+ *   block is written.  k == 0 writes zeros.
+ *
+ * Errors (all three): negative sizes, ldx < k or ldy < n ->
+ * W4A4_ERR_INVALID_VALUE; k % 32 -> W4A4_ERR_K_NOT_MULTIPLE_OF_32; null
+ * pointers with work to do, m > 8388480, or 2^24 or more 128 x 128 output tiles ->
+ * W4A4_ERR_INVALID_VALUE; misalignment ->
+ * W4A4_ERR_MISALIGNED.  Empty sizes return W4A4_OK having done nothing.
+ */
+size_t w4a4_w16_weight_bytes(int64_t n, int64_t k);
+size_t w4a4_w16_act_bytes(int64_t m, int64_t k);
+w4a4_status w4a4_dequantize_w16(const void *q4_0, int64_t n, int64_t k, void *w16, size_t w16_bytes,
+                                void *stream);
+w4a4_status w4a4_rotate_act16(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx, void *a16,
+                              size_t a16_bytes, void *stream);
+w4a4_status w4a4_gemm_w16(const void *w16, const void *a16, float *y, int64_t m, int64_t n, int64_t k,
+                          int64_t ldy, void *stream);
+
 /* Workspace bytes w4a4_gemm_id needs (0 for invalid sizes).  Host only, pure. */
 size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t top_k);
 

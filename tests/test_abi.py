@@ -171,6 +171,36 @@ def test_ablation_validation(L):
     assert w(None, 0, 64, 64, None, None) == OK
 
 
+def test_w16_validation(L):
+    assert L.w4a4_w16_weight_bytes(17408, 5120) == 17408 * 5120 * 2          # 160 blocks: no K padding
+    assert L.w4a4_w16_weight_bytes(33, 64) == 64 * 256 * 2                   # rows to 64, blocks to 8
+    assert L.w4a4_w16_act_bytes(1, 5120) == 32 * 5120 * 2
+    assert L.w4a4_w16_act_bytes(4, 40) == 0 and L.w4a4_w16_weight_bytes(-1, 64) == 0
+    d = L.w4a4_dequantize_w16
+    need = L.w4a4_w16_weight_bytes(4, 64)
+    assert d(P(A), 4, 40, P(A), need, None) == KMUL
+    assert d(P(A), 4, 64, P(A + 8), need, None) == MISALIGNED
+    assert d(P(A), 4, 64, P(A), need - 1, None) == WS
+    assert d(None, 4, 64, P(A), need, None) == INVALID
+    assert d(None, 0, 64, None, 0, None) == OK
+    r = L.w4a4_rotate_act16
+    need = L.w4a4_w16_act_bytes(4, 64)
+    assert r(P(A), 2, 4, 64, 64, P(A), need, None) == DTYPE
+    assert r(P(A), 1, 4, 48, 64, P(A), need, None) == KMUL
+    assert r(P(A), 1, 4, 64, 32, P(A), need, None) == INVALID  # ldx < k
+    assert r(P(ODD), 1, 4, 64, 64, P(A), need, None) == MISALIGNED
+    assert r(P(A), 1, 4, 64, 64, P(A + 8), need, None) == MISALIGNED
+    assert r(P(A), 1, 4, 64, 64, P(A), need - 2, None) == WS
+    assert r(None, 1, 0, 64, 64, None, 0, None) == OK
+    g = L.w4a4_gemm_w16
+    assert g(P(A), P(A), P(A), 4, 8, 48, 8, None) == KMUL
+    assert g(P(A), P(A), P(A), 4, 8, 64, 4, None) == INVALID  # ldy < n
+    assert g(P(A + 8), P(A), P(A), 4, 8, 64, 8, None) == MISALIGNED
+    assert g(None, P(A), P(A), 4, 8, 64, 8, None) == INVALID
+    assert g(P(A), P(A), P(A), 1 << 22, 1 << 22, 64, 1 << 22, None) == INVALID  # 2^30 tiles
+    assert g(None, None, None, 0, 8, 64, 8, None) == OK
+
+
 def test_prep_validation(L):
     q = L.w4a4_quantize_q4_0_h32
     assert q(P(A), 4, 40, 40, P(A), None) == KMUL
