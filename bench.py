@@ -319,6 +319,15 @@ def run_w4a16(torch, ops, synth):
     step_us = events_ms(torch, step, 10) * 1e3
     gemm_us = events_ms(torch, lambda i: ops.gemm_w16(copies[i % len(copies)], a16, d.m, d.n, d.k, y=y), 10) * 1e3
     rot_us = events_ms(torch, lambda i: ops.rotate_act16(x, out=a16), 20) * 1e3
+    # context only: the platform's library fp16 GEMM (fp16 out) on the same
+    # operands, weights pre-transposed to K x N, two copies alternated
+    wt = [ops.w16_to_rows(c, d.n, d.k).t().contiguous() for c in copies[:2]]
+    a_rows = ops.w16_to_rows(a16, d.m, d.k)
+    lib_out = torch.empty((d.m, d.n), dtype=torch.float16, device=dev)
+    for i in range(3):
+        torch.mm(a_rows, wt[i % 2], out=lib_out)
+    lib_us = events_ms(torch, lambda i: torch.mm(a_rows, wt[i % 2], out=lib_out), 10) * 1e3
+    del wt, a_rows
     flops = 2.0 * d.m * d.n * d.k
     rows = np.arange(0, d.m, d.m // 16)
     ops.gemm_w16(w16, a16, d.m, d.n, d.k, y=y)
@@ -331,6 +340,7 @@ def run_w4a16(torch, ops, synth):
             "rotate_act16_us": round(rot_us, 2), "tokens/s": round(d.m / (step_us * 1e-6), 1),
             "TFLOP/s": round(flops / (gemm_us * 1e-6) / 1e12, 1),
             "frac_of_fp16_peak": round(flops / (gemm_us * 1e-6) / 1e12 / PEAK_FP16_TFLOPS, 4),
+            "library_fp16_gemm_us": round(lib_us, 2),
             "mean_abs_err": {k_: round(v, 6) for k_, v in err.items()}, "rows_sampled": len(rows),
             "timing": "events over back-to-back calls"}
 

@@ -322,25 +322,31 @@ def prepare_weights_plain(w: torch.Tensor) -> torch.Tensor:
 # Rotated W4A16: the rotated Q4_0 weights against rotated fp16 activations
 # --------------------------------------------------------------------------
 
-def w16_row_stride(k: int) -> int:
-    """Elements per row of both padded fp16 operands (the block count padded to 8)."""
-    return (k // 32 + 7) // 8 * 8 * 32
+def w16_blocks(k: int) -> int:
+    """Blocks per row of a tiled fp16 operand (k / 32 padded to a multiple of 8)."""
+    return (k // 32 + 7) // 8 * 8
+
+
+def w16_to_rows(buf: torch.Tensor, rows: int, k: int) -> torch.Tensor:
+    """A tiled fp16 operand as a row-major [rows, k] view copy (layout only)."""
+    nbp, tiles = w16_blocks(k), (rows + 31) // 32
+    t = buf.reshape(tiles, nbp, 2, 2, 32, 8).permute(0, 4, 1, 2, 3, 5)
+    return t.reshape(tiles * 32, nbp * 32)[:rows, :k].contiguous()
 
 
 def dequantize_w16(q4: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Q4_0 bytes -> fp16 [ceil(n/32)*32, w16_row_stride(k)], zero-padded."""
+    """Q4_0 bytes -> tiled fp16 weights (flat, w4a4_w16_weight_bytes(n, k) bytes)."""
     _require_cuda(q4, out)
     need = int(lib().w4a4_w16_weight_bytes(n, k))
     if out is None:
-        out = torch.empty(((n + 31) // 32 * 32, w16_row_stride(k)), dtype=torch.float16, device=q4.device)
+        out = torch.empty(need // 2, dtype=torch.float16, device=q4.device)
     _check(lib().w4a4_dequantize_w16(_ptr(q4), n, k, _ptr(out), out.numel() * out.element_size(),
                                      _stream(q4.device)), "w4a4_dequantize_w16")
-    assert out.numel() * out.element_size() >= need
     return out
 
 
 def rotate_act16(x: torch.Tensor, k: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
-    """x fp16/fp32 [m, >=k] -> rotated fp16 [ceil(m/32)*32, w16_row_stride(k)], zero-padded."""
+    """x fp16/fp32 [m, >=k] -> tiled rotated fp16 activations (flat, w4a4_w16_act_bytes(m, k) bytes)."""
     _require_cuda(x, out)
     assert x.dim() == 2 and x.stride(1) == 1
     dt = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16}.get(x.dtype)
@@ -349,7 +355,7 @@ def rotate_act16(x: torch.Tensor, k: int | None = None, out: torch.Tensor | None
     m = x.shape[0]
     k = x.shape[1] if k is None else k
     if out is None:
-        out = torch.empty(((m + 31) // 32 * 32, w16_row_stride(k)), dtype=torch.float16, device=x.device)
+        out = torch.empty(int(lib().w4a4_w16_act_bytes(m, k)) // 2, dtype=torch.float16, device=x.device)
     _check(lib().w4a4_rotate_act16(_ptr(x), dt, m, k, x.stride(0), _ptr(out), out.numel() * out.element_size(),
                                    _stream(x.device)), "w4a4_rotate_act16")
     return out
@@ -357,7 +363,7 @@ def rotate_act16(x: torch.Tensor, k: int | None = None, out: torch.Tensor | None
 
 def gemm_w16(w16: torch.Tensor, a16: torch.Tensor, m: int, n: int, k: int,
              y: torch.Tensor | None = None) -> torch.Tensor:
-    """W4A16 product of the two padded fp16 operands: fp32 [m, n] (row stride y.stride(0))."""
+    """W4A16 product of the two tiled fp16 operands: fp32 [m, n] (row stride y.stride(0))."""
     _require_cuda(w16, a16, y)
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=a16.device)

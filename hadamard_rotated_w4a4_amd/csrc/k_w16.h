@@ -10,10 +10,15 @@
 // for W4A4 and rounded to fp16 once, the Q4_0 weights dequantised to
 // fp16(d * (q - 8)) once (the block scale folded into the weight, so no
 // per-block epilogue remains), and v_mfma_f32_32x32x16_f16 accumulating in
-// its own registers.  Both operands are row-major fp16 matrices padded with
-// zeros to whole 32-row tiles and to the padded block count (a multiple of
-// MX_BLOCK_PAD blocks): the global-to-LDS loads gather each MFMA fragment
-// straight from the rows and never read past a buffer.
+// its own registers.  Both operands are stored pre-tiled in the MFMA's
+// fragment order, so each global-to-LDS load copies 1 KB of contiguous
+// memory (a row-major operand would touch 32 cache lines for 64 bytes each
+// per load):
+//   [32-row tile][padded block][K half h][lane l][8 elements]
+// element (r, t) sits in tile r / 32, block t / 32, half (t % 32) / 16, lane
+// (r % 32) + 32 ((t % 16) / 8), slot t % 8; 2 KB per (tile, block).  Rows are
+// padded to whole tiles and blocks to a multiple of MX_BLOCK_PAD, with zeros,
+// so the GEMM loads whole stages without bounds checks.
 #pragma once
 
 #include "common.h"
@@ -24,8 +29,17 @@ namespace w4a4 {
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-// Row stride (elements) of both padded fp16 operands.
-__host__ __device__ inline int64_t w16_row_stride(int64_t k) { return mx_blocks(k) * QK; }
+constexpr int W16_TILE_BLOCK = 2048;  // bytes per (32-row tile, block) of a tiled operand
+
+// Bytes of a tiled operand of `rows` rows.
+__host__ __device__ inline int64_t w16_operand_bytes(int64_t rows, int64_t k) {
+    return (rows + 31) / 32 * mx_blocks(k) * W16_TILE_BLOCK;
+}
+
+// Element index of piece p (elements 8 p .. 8 p + 7 of block b) of row r.
+__device__ __forceinline__ int64_t w16_piece(int64_t r, int64_t b, int p, int64_t nbp) {
+    return ((((r >> 5) * nbp + b) * 2 + (p >> 1)) * 64 + (r & 31) + 32 * (p & 1)) * 8;
+}
 
 // ---------------------------------------------------------------------------
 // Operands
@@ -61,9 +75,9 @@ __global__ __launch_bounds__(256) void dequantize_w16_kernel(const uint8_t *__re
 #pragma unroll
         for (int j = 0; j < 16; j++) h[j] = 0;
     }
-    uint4 *dst = reinterpret_cast<uint4 *>(w16 + row * w16_row_stride(k) + b * QK);
 #pragma unroll
-    for (int j = 0; j < 4; j++) dst[j] = make_uint4(h[4 * j], h[4 * j + 1], h[4 * j + 2], h[4 * j + 3]);
+    for (int p = 0; p < 4; p++)
+        *reinterpret_cast<uint4 *>(w16 + w16_piece(row, b, p, nbp)) = make_uint4(h[4 * p], h[4 * p + 1], h[4 * p + 2], h[4 * p + 3]);
 }
 
 // Activations: as rotate_quantize_kernel's mapping (four lanes per (row,
@@ -100,7 +114,7 @@ __global__ __launch_bounds__(256) void rotate_act16_kernel(const T *__restrict__
     for (int j = 0; j < 4; j++)
         h[j] = (uint32_t)__half_as_ushort(__float2half_rn(p[2 * j])) |
                (uint32_t)__half_as_ushort(__float2half_rn(p[2 * j + 1])) << 16;
-    *reinterpret_cast<uint4 *>(a16 + row * w16_row_stride(k) + b * QK + 8 * L) = make_uint4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<uint4 *>(a16 + w16_piece(row, b, L, mx_blocks(k))) = make_uint4(h[0], h[1], h[2], h[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -109,30 +123,31 @@ __global__ __launch_bounds__(256) void rotate_act16_kernel(const T *__restrict__
 // Workgroup: 4 waves (2 x 2), each a 64 x 64 tile of 2 x 2 MFMA tiles: a
 // 128 x 128 output tile.  K in stages of one 32-element block through a
 // ring of W16_NS LDS stage buffers filled by global-to-LDS loads.  In a
-// stage, the fragment of (32-row tile t, K half h) is 1 KB at (2 t + h) KB:
-// lane l holds row l % 32, elements 16 h + 8 (l / 32) .. + 7 of the block.
+// stage, the fragment of (32-row tile t, K half h) is 1 KB at (2 t + h) KB,
+// a copy of the operand's 1 KB (lane l: row l % 32, elements
+// 16 h + 8 (l / 32) .. + 7 of the block).
 constexpr int W16_NS = 4;
 constexpr int W16_RT = 4, W16_CT = 4;                               // 32-row / 32-column tiles per workgroup
 constexpr int W16_STAGE = (W16_RT + W16_CT) * 2 * 1024;            // 16 KB
 constexpr int W16_DMA_PER_WAVE = (W16_RT + W16_CT) * 2 / 4;        // 4
 
 struct W16Args {
-    const _Float16 *a16;   // [rtiles * 32][w16_row_stride(k)]
-    const _Float16 *w16;   // [padded_n(n)][w16_row_stride(k)]
+    const _Float16 *a16;   // tiled, ceil(m / 32) row tiles
+    const _Float16 *w16;   // tiled, padded_n(n) / 32 row tiles
     float *y;
     int64_t ldy, m, n, k;
 };
 
-__global__ __launch_bounds__(256) void gemm_w16_kernel(W16Args a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[W16_NS * W16_STAGE];
+// One whole 128 x 128 tile (workgroup index id).
+__device__ __forceinline__ void w16_tile(const W16Args &a, int64_t id, uint8_t *smem) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t kp = w16_row_stride(a.k), nbp = mx_blocks(a.k);
+    const int64_t nbp = mx_blocks(a.k);
     const int64_t rtiles = (a.m + 31) / 32, ctiles = padded_n(a.n) / TILE_N;
 
     int64_t bx, by;
-    mx_tile_of(blockIdx.x, (a.n + 127) / 128, (a.m + 127) / 128, bx, by);
+    mx_tile_of(id, (a.n + 127) / 128, (a.m + 127) / 128, bx, by);
     const int64_t rt0 = by * W16_RT, ct0 = bx * W16_CT;
 
     // this wave's loads: tile t = wave * 2 + (d / 2), half h = d % 2 (row
@@ -144,19 +159,19 @@ __global__ __launch_bounds__(256) void gemm_w16_kernel(W16Args a) {
 #pragma unroll
     for (int d = 0; d < W16_DMA_PER_WAVE; d++) {
         const int t = wave * 2 + (d >> 1), h = d & 1;
-        const _Float16 *base = t < W16_RT ? a.a16 + min(rt0 + t, rtiles - 1) * 32 * kp
-                                          : a.w16 + min(ct0 + t - W16_RT, ctiles - 1) * 32 * kp;
-        src[d] = uniform_ptr(reinterpret_cast<const uint8_t *>(base + 16 * h));
+        const uint8_t *base = t < W16_RT ? reinterpret_cast<const uint8_t *>(a.a16) + min(rt0 + t, rtiles - 1) * nbp * W16_TILE_BLOCK
+                                         : reinterpret_cast<const uint8_t *>(a.w16) + min(ct0 + t - W16_RT, ctiles - 1) * nbp * W16_TILE_BLOCK;
+        src[d] = uniform_ptr(base + h * 1024);
         dst[d] = (uint32_t)((2 * t + h) * 1024);
     }
-    const uint32_t voff = (uint32_t)((lane & 31) * kp * 2 + 16 * (lane >> 5));
+    const uint32_t voff = (uint32_t)(lane * 16);
     const int nstages = (int)nbp;
     auto issue = [&](int stage, int slot) {
         // past the last stage the ring reloads the last one (never computed)
         const int64_t b = min(stage, nstages - 1);
         const uint32_t lds = __builtin_amdgcn_readfirstlane(smem_base + slot * W16_STAGE);
 #pragma unroll
-        for (int d = 0; d < W16_DMA_PER_WAVE; d++) dma16s(src[d] + b * QK * 2, voff, lds + dst[d]);
+        for (int d = 0; d < W16_DMA_PER_WAVE; d++) dma16s(src[d] + b * W16_TILE_BLOCK, voff, lds + dst[d]);
     };
 
     v16f acc[2][2];
@@ -194,14 +209,21 @@ __global__ __launch_bounds__(256) void gemm_w16_kernel(W16Args a) {
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(W16_DMA_PER_WAVE * (W16_NS - 3)) : "memory");
             __syncthreads();
             issue(s + W16_NS - 1, (s + W16_NS - 1) % W16_NS);
+            // all of stage s + 1's fragment reads are issued before stage s's
+            // MFMAs, so their latency hides behind them (the scheduler would
+            // otherwise sink each read to just before its first use)
             load_frags(smem + ((s + 1) % W16_NS) * W16_STAGE, u ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+            // K half outermost: four independent accumulators between the
+            // two MFMAs that share one
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int h = 0; h < 2; h++)
 #pragma unroll
-                for (int j = 0; j < 2; j++)
+                for (int i = 0; i < 2; i++)
 #pragma unroll
-                    for (int h = 0; h < 2; h++)
+                    for (int j = 0; j < 2; j++)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[u][i][h], bf[u][j][h], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still be writing LDS at exit
@@ -221,6 +243,93 @@ __global__ __launch_bounds__(256) void gemm_w16_kernel(W16Args a) {
             }
         }
     }
+}
+
+// Leftover tiles (as in the W4A4 GEMM): when the whole tiles leave a
+// partial last round, each leftover tile is split into 16 pieces of 32 x 32,
+// one workgroup each, its 4 waves over a quarter of K each.  A wave streams
+// its own fragments (A and B, both halves of one block per stage) through
+// its own LDS ring, waits only for its own loads, and the quarters meet in
+// LDS in ascending K order.
+constexpr int W16_PIECES = W16_RT * W16_CT;
+constexpr int W16_PNS = 4;                      // stages per wave ring
+constexpr int W16_PSTAGE = 4 * 1024;            // A h0, A h1, B h0, B h1
+
+__device__ __forceinline__ void w16_piece(const W16Args &a, int64_t first_tile, int64_t id, uint8_t *smem) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t nbp = mx_blocks(a.k);
+    const int64_t rtiles = (a.m + 31) / 32, ctiles = padded_n(a.n) / TILE_N;
+
+    int64_t bx, by;
+    mx_tile_of(first_tile + id / W16_PIECES, (a.n + 127) / 128, (a.m + 127) / 128, bx, by);
+    const int sub = (int)(id % W16_PIECES);
+    const int64_t rt = by * W16_RT + sub / W16_CT, ct = bx * W16_CT + sub % W16_CT;
+    // pieces past the matrix edge compute on clamped tiles and store nothing
+    const uint8_t *abase = uniform_ptr(reinterpret_cast<const uint8_t *>(a.a16) + min(rt, rtiles - 1) * nbp * W16_TILE_BLOCK);
+    const uint8_t *bbase = uniform_ptr(reinterpret_cast<const uint8_t *>(a.w16) + min(ct, ctiles - 1) * nbp * W16_TILE_BLOCK);
+
+    // this wave's quarter of the blocks (nbp is a multiple of 8: never empty)
+    const int64_t b0 = nbp / 4 * wave;
+    const int nst = (int)(nbp / 4);
+    uint8_t *ring = smem + wave * W16_PNS * W16_PSTAGE;
+    const uint32_t ring_lds =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)ring);
+    const uint32_t voff = lane * 16;
+    auto issue = [&](int stage, int slot) {
+        // past the last stage the ring reloads the last one (never computed)
+        const int64_t off = (b0 + min(stage, nst - 1)) * W16_TILE_BLOCK;
+        const uint32_t lds = ring_lds + slot * W16_PSTAGE;
+        dma16s(abase + off, voff, lds);
+        dma16s(abase + off + 1024, voff, lds + 1024);
+        dma16s(bbase + off, voff, lds + 2048);
+        dma16s(bbase + off + 1024, voff, lds + 3072);
+    };
+
+    v16f acc;
+#pragma unroll
+    for (int v = 0; v < 16; v++) acc[v] = 0.0f;
+#pragma unroll
+    for (int x = 0; x < W16_PNS - 1; x++) issue(x, x);
+    for (int s = 0; s < nst; s++) {
+        // stage s has landed: only the W16_PNS - 2 stages after it may be in flight
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * (W16_PNS - 2)) : "memory");
+        const uint8_t *st = ring + (s % W16_PNS) * W16_PSTAGE + 16 * lane;
+        const v8h a0 = lds_read<v8h>(st), a1 = lds_read<v8h>(st + 1024);
+        const v8h b0f = lds_read<v8h>(st + 2048), b1f = lds_read<v8h>(st + 3072);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0f, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1f, acc, 0, 0, 0);
+        // the reads above have fed their MFMAs before the slot they came from
+        // can be refilled (three stages later)
+        __builtin_amdgcn_sched_barrier(0);
+        issue(s + W16_PNS - 1, (s + W16_PNS - 1) % W16_PNS);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still be writing the ring
+
+    // the quarters meet in LDS (the rings are free now) in ascending K order
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int v = 0; v < 16; v++) red[(wave * 16 + v) * 64 + lane] = acc[v];
+    __syncthreads();
+    for (int i = tid; i < 16 * 64; i += 256) {
+        const int v = i / 64, l = i % 64;
+        const float sum = ((red[(0 * 16 + v) * 64 + l] + red[(1 * 16 + v) * 64 + l]) + red[(2 * 16 + v) * 64 + l]) +
+                          red[(3 * 16 + v) * 64 + l];
+        const int64_t r = rt * 32 + mfma32_row(v, l), col = ct * 32 + (l & 31);
+        if (rt < rtiles && r < a.m && col < a.n) a.y[r * a.ldy + col] = sum;
+    }
+}
+
+static_assert(4 * W16_PNS * W16_PSTAGE <= W16_NS * W16_STAGE, "the piece rings fit the tile's LDS");
+
+// One launch: workgroups below main_wgs take whole tiles (XCD-aware order),
+// the rest the pieces of the leftover tiles, which fill the CUs that the last
+// whole tiles leave idle (workgroups are dispatched in index order).
+__global__ __launch_bounds__(256) void gemm_w16_kernel(W16Args a, int64_t main_wgs, int64_t first_piece_tile) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[W16_NS * W16_STAGE];
+    if ((int64_t)blockIdx.x < main_wgs) w16_tile(a, blockIdx.x, smem);
+    else w16_piece(a, first_piece_tile, blockIdx.x - main_wgs, smem);
 }
 
 }  // namespace w4a4

@@ -423,12 +423,12 @@ w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, 
 
 size_t w4a4_w16_weight_bytes(int64_t n, int64_t k) {
     if (n < 0 || k < 0 || k % QK) return 0;
-    return (size_t)(padded_n(n) * w16_row_stride(k) * 2);
+    return (size_t)w16_operand_bytes(n, k);
 }
 
 size_t w4a4_w16_act_bytes(int64_t m, int64_t k) {
     if (m < 0 || k < 0 || k % QK) return 0;
-    return (size_t)((m + 31) / 32 * 32 * w16_row_stride(k) * 2);
+    return (size_t)w16_operand_bytes(m, k);
 }
 
 w4a4_status w4a4_dequantize_w16(const void *q4_0, int64_t n, int64_t k, void *w16, size_t w16_bytes,
@@ -481,7 +481,7 @@ w4a4_status w4a4_gemm_w16(const void *w16, const void *a16, float *y, int64_t m,
     if (!w16 || !a16) return W4A4_ERR_INVALID_VALUE;
     if (!aligned(w16, 16) || !aligned(a16, 16)) return W4A4_ERR_MISALIGNED;
     const int64_t tiles = (m + 127) / 128 * ((n + 127) / 128);
-    if (tiles >= (int64_t{1} << 24)) return W4A4_ERR_INVALID_VALUE;  // grid of < 2^32 threads
+    if (tiles >= (int64_t{1} << 20)) return W4A4_ERR_INVALID_VALUE;  // grid of < 2^32 threads, pieces included
     W16Args a{};
     a.a16 = static_cast<const _Float16 *>(a16);
     a.w16 = static_cast<const _Float16 *>(w16);
@@ -490,7 +490,20 @@ w4a4_status w4a4_gemm_w16(const void *w16, const void *a16, float *y, int64_t m,
     a.m = m;
     a.n = n;
     a.k = k;
-    gemm_w16_kernel<<<(unsigned)tiles, 256, 0, s>>>(a);
+    // whole rounds of resident workgroups take whole tiles; a partial last
+    // round is split into pieces when one round of pieces (~1.6x the work
+    // per output) is shorter than a round of whole tiles
+    static const int occ = [] {
+        int o = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, gemm_w16_kernel, 256, 0) != hipSuccess || o < 1) o = 1;
+        return o;
+    }();
+    const int64_t slots = (int64_t)device_cus() * occ;
+    const int64_t whole = tiles / slots * slots, left = tiles - whole;
+    const double prounds = (double)((left * W16_PIECES + slots - 1) / slots) * 1.6 / W16_PIECES;
+    const bool pieces = left > 0 && prounds < 1.0;
+    const int64_t main_wgs = pieces ? whole : tiles, piece_wgs = pieces ? left * W16_PIECES : 0;
+    gemm_w16_kernel<<<(unsigned)(main_wgs + piece_wgs), 256, 0, s>>>(a, main_wgs, whole);
     return hip_status("gemm_w16_kernel");
 }
 

@@ -221,16 +221,17 @@ w4a4_status w4a4_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k
  * Rotated W4A16 (section "Hadamard-rotated Q4_0: W4A4 prompt processing":
  * the rotated Q4_0 files also run with the activations rotated and kept at
  * 16 bits, with no 4-bit activation step).  Both operands are fp16 matrices
- * in a padded row-major layout shared by the three calls below:
- *   row stride kp = nbp * 32 elements, nbp = ceil(k / 32 / 8) * 8 (the
- *   block count padded to a multiple of 8); rows padded to a multiple of 32;
- *   every element past k in a row, and every padding row, is +0.
- * The padding lets the GEMM load whole 32-row, 8-block tiles without bounds
- * checks; it contributes exact zeros to every sum.
+ * in one tiled layout, the matrix cores' fragment order, shared by the three
+ * calls below.  With nbp = ceil(k / 32 / 8) * 8 (the block count padded to a
+ * multiple of 8), the layout is [ceil(rows / 32)][nbp][2][64][8] fp16:
+ * element (r, t) sits at tile r / 32, block t / 32, half (t % 32) / 16, lane
+ * (r % 32) + 32 * ((t % 16) / 8), slot t % 8.  Rows past the matrix and
+ * blocks past k / 32 hold +0.  The padding lets the GEMM load whole 32-row,
+ * 8-block tiles without bounds checks; it adds exact zeros to every sum.
  *
  * w4a4_w16_weight_bytes(n, k): bytes of the dequantised weights,
- *   ceil(n / 32) * 32 * kp * 2.  w4a4_w16_act_bytes(m, k): bytes of the
- *   rotated activations, ceil(m / 32) * 32 * kp * 2.  Both 0 for invalid
+ *   ceil(n / 32) * nbp * 2048.  w4a4_w16_act_bytes(m, k): bytes of the
+ *   rotated activations, ceil(m / 32) * nbp * 2048.  Both 0 for invalid
  *   sizes; host only, pure.
  *
  * w4a4_dequantize_w16: Q4_0 [n][k/32] blocks (as w4a4_quantize_q4_0_h32
@@ -256,7 +257,7 @@ w4a4_status w4a4_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k
  *
  * Errors (all three): negative sizes, ldx < k or ldy < n ->
  * W4A4_ERR_INVALID_VALUE; k % 32 -> W4A4_ERR_K_NOT_MULTIPLE_OF_32; null
- * pointers with work to do, m > 8388480, or 2^24 or more 128 x 128 output tiles ->
+ * pointers with work to do, m > 8388480, or 2^20 or more 128 x 128 output tiles ->
  * W4A4_ERR_INVALID_VALUE; misalignment ->
  * W4A4_ERR_MISALIGNED.  Empty sizes return W4A4_OK having done nothing.
  */

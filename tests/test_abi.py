@@ -197,7 +197,7 @@ def test_w16_validation(L):
     assert g(P(A), P(A), P(A), 4, 8, 64, 4, None) == INVALID  # ldy < n
     assert g(P(A + 8), P(A), P(A), 4, 8, 64, 8, None) == MISALIGNED
     assert g(None, P(A), P(A), 4, 8, 64, 8, None) == INVALID
-    assert g(P(A), P(A), P(A), 1 << 22, 1 << 22, 64, 1 << 22, None) == INVALID  # 2^30 tiles
+    assert g(P(A), P(A), P(A), 1 << 17, 1 << 17, 64, 1 << 17, None) == INVALID  # 2^20 tiles
     assert g(None, None, None, 0, 8, 64, 8, None) == OK
 
 

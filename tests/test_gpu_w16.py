@@ -1,6 +1,6 @@
 """GPU parity of rotated W4A16 (reading R10) against the CPU oracle: the
-rotated fp16 activations and the fp16-dequantised weights bit-exact (with
-their zero padding), the fp16 matrix-core GEMM on them within max|err| <=
+rotated fp16 activations and the fp16-dequantised weights bit-exact in the
+documented tiled layout (with its zero padding), the fp16 matrix-core GEMM on them within max|err| <=
 2e-3 * max|ref| per row, and its place between W4A4 and the exact product."""
 import numpy as np
 import pytest
@@ -34,8 +34,16 @@ def say(msg):
     print(f"[gpu w16] {msg}", flush=True)
 
 
-def kp(k):
-    return (k // 32 + 7) // 8 * 8 * 32
+def nbp(k):
+    return (k // 32 + 7) // 8 * 8
+
+
+def untile(buf, rows, k):
+    """The documented tiled layout, [tile][block][half][lane group][row][8],
+    back to a padded row-major [ceil(rows/32)*32, nbp*32] array."""
+    tiles = (rows + 31) // 32
+    a = np.asarray(buf).reshape(tiles, nbp(k), 2, 2, 32, 8).transpose(0, 4, 1, 2, 3, 5)
+    return a.reshape(tiles * 32, nbp(k) * 32)
 
 
 def bits(a):
@@ -56,8 +64,7 @@ def test_rotate_act16_bit_exact_and_padded(ops, m, k, dtype, pad):
     rng = np.random.default_rng(7 * m + k + pad)
     x = synth.activations(m, k + pad, rng, max(1, k // 100)).astype(dtype)
     say(f"rotate_act16 m={m} k={k} {np.dtype(dtype).name} ldx={k + pad}")
-    a16 = host(ops.rotate_act16(dev(x), k=k))
-    assert a16.shape == ((m + 31) // 32 * 32, kp(k))
+    a16 = untile(host(ops.rotate_act16(dev(x), k=k)), m, k)
     assert np.array_equal(bits(a16[:m, :k]), bits(oracle.rotate_act16(x, k=k)))
     assert not bits(a16[:, k:]).any() and not bits(a16[m:]).any()
 
@@ -67,7 +74,7 @@ def test_rotate_act16_special_blocks(ops):
     x[1, :32] = 1e-44            # subnormal input
     x[2, 32:64] = -3.0           # constant block: one non-zero output
     x[3, 70] = 4.0e5             # beyond fp16 after the rotation: +-inf on both sides
-    a16 = host(ops.rotate_act16(dev(x)))
+    a16 = untile(host(ops.rotate_act16(dev(x))), 4, 128)
     assert np.array_equal(bits(a16[:4, :128]), bits(oracle.rotate_act16(x)))
 
 
@@ -76,8 +83,7 @@ def test_dequantize_w16_bit_exact_and_padded(ops, n, k):
     rng = np.random.default_rng(n + 3 * k)
     q4 = oracle.prepare_weights(synth.weights(n, k, rng))
     say(f"dequantize_w16 n={n} k={k}")
-    w16 = host(ops.dequantize_w16(dev(q4), n, k))
-    assert w16.shape == ((n + 31) // 32 * 32, kp(k))
+    w16 = untile(host(ops.dequantize_w16(dev(q4), n, k)), n, k)
     assert np.array_equal(bits(w16[:n, :k]), bits(oracle.dequantize_w16(q4, k)))
     assert not bits(w16[:, k:]).any() and not bits(w16[n:]).any()
 
@@ -100,11 +106,24 @@ def test_gemm_w16_matches_oracle(ops, m, n, k):
     assert_rows_close(y, ref, "gemm_w16")
 
 
+@pytest.mark.parametrize("m,n,k", [(128, 65600, 256), (200, 33000, 320)])
+def test_gemm_w16_leftover_pieces(ops, m, n, k):
+    """Slightly more than one round of 128 x 128 tiles on a 256-CU part (513
+    and 516 tiles for 512 resident workgroups): the leftover tiles run as
+    32 x 32 pieces, the last of them ragged in both directions."""
+    w, x = _problem(m, n, k, m + n)
+    say(f"gemm_w16 leftover pieces m={m} n={n} k={k}")
+    q4 = oracle.prepare_weights(w)
+    y = host(ops.gemm_w16(ops.dequantize_w16(dev(q4), n, k), ops.rotate_act16(dev(x)), m, n, k))
+    ref = oracle.gemm_w16(oracle.dequantize_w16(q4, k), oracle.rotate_act16(x))
+    assert_rows_close(y, ref, "gemm_w16 pieces")
+
+
 def test_gemm_w16_weights_from_gpu_quantiser(ops):
     """The whole chain on the GPU: fp32 weights -> rotated Q4_0 -> fp16."""
     w, x = _problem(40, 96, 640, 5)
     q4 = ops.quantize_q4_0_h32(dev(w))
-    w16 = host(ops.dequantize_w16(q4, 96, 640))
+    w16 = untile(host(ops.dequantize_w16(q4, 96, 640)), 96, 640)
     assert np.array_equal(bits(w16[:96, :640]), bits(oracle.dequantize_w16(oracle.prepare_weights(w), 640)))
 
 
