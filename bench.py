@@ -197,6 +197,43 @@ def run_verify16(torch, ops, synth):
     out["hbm_frac"] = round(tot_bytes / (tot_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
     out["step_us"] = round(step_us, 2)
     out["tokens/s"] = round(16 / (step_us * 1e-6), 1)
+    del sets, packed
+
+    # The same set with the projections that read one input packed side by
+    # side (q|k|v: n = 8192, gate|up: n = 34816): the same weight bytes and
+    # arithmetic in 4 GEMMs instead of 7 (fewer launches and K-split sums).
+    ws = synth.layer_weights(workload=4)
+    groups = (("qkv", ("q", "k", "v"), "attn_in"), ("o", ("o",), "attn_out"),
+              ("gate_up", ("gate", "up"), "ffn_in"), ("down", ("down",), "ffn_act"))
+    fused = {g: ops.prepare_weights(torch.from_numpy(np.concatenate([ws[p] for p in parts])).to(dev))
+             for g, parts, _ in groups}
+    shape = {g: (ws[parts[0]].shape[1], sum(ws[p].shape[0] for p in parts)) for g, parts, _ in groups}
+    del ws
+    fsets = [fused] + [{k_: v.clone() for k_, v in fused.items()} for _ in range(nsets - 1)]
+    fys = {g: torch.empty((16, shape[g][1]), dtype=torch.float32, device=dev) for g, _, _ in groups}
+    fws = {g: torch.empty(max(1, ops.gemm_workspace_bytes(16, shape[g][1], shape[g][0])), dtype=torch.uint8, device=dev)
+           for g, _, _ in groups}
+    f_us = 0.0
+    for g, _, inp in groups:
+        k, n = shape[g]
+        c, sc = q[inp]
+
+        def one(g=g, k=k, n=n, c=c, sc=sc):
+            for i in range(2 * nsets):
+                ops.gemm(fsets[i % nsets][g], c, sc, n, k, y=fys[g], workspace=fws[g])
+        f_us += graph_time_us(torch, one, inner=2 * nsets)
+
+    def fstep():
+        for i in range(nsets):
+            qq = {inp: ops.rotate_quantize_act(xin) for inp, xin in inputs.items()}
+            for g, _, inp in groups:
+                k, n = shape[g]
+                ops.gemm(fsets[i][g], *qq[inp], n, k, y=fys[g], workspace=fws[g])
+    fstep_us = graph_time_us(torch, fstep, inner=nsets)
+    out["same_input_fused"] = {"gemms": len(groups), "gemm_us_total": round(f_us, 2),
+                               "gemm_GB/s": round(tot_bytes / (f_us * 1e-6) / 1e9, 1),
+                               "hbm_frac": round(tot_bytes / (f_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                               "step_us": round(fstep_us, 2), "tokens/s": round(16 / (fstep_us * 1e-6), 1)}
     return out
 
 
