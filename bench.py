@@ -276,6 +276,21 @@ def run_moe(torch, ops, synth):
     tot_ops = 2 * (2.0 * rows * dff * dm) + 2.0 * rows * dm * dff
     tot_bytes = 2 * b_gate + b_down
     gemm_us = g + u + dd
+    del pg, pu
+
+    # gate|up of each expert packed as one 2 * d_ff-row matrix: one routed
+    # GEMM for both (the same weight bytes and arithmetic)
+    pgu = torch.cat([ops.prepare_weights(torch.from_numpy(np.concatenate([mo.w_gate[e], mo.w_up[e]])).to(dev))
+                     for e in range(E)])
+    ygu = torch.empty((T, top_k, 2 * dff), dtype=torch.float32, device=dev)
+    gu = graph_time_us(torch, lambda: ops.gemm_id(pgu, E, cx, sx, 1, ids, 2 * dff, dm, y=ygu, workspace=ws))
+
+    def fstep():
+        ops.rotate_quantize_act(x, codes=cx, scales=sx)
+        ops.rotate_quantize_act(h, codes=ch, scales=sh)
+        ops.gemm_id(pgu, E, cx, sx, 1, ids, 2 * dff, dm, y=ygu, workspace=ws)
+        ops.gemm_id(pd, E, ch, sh, top_k, ids, dm, dff, y=yd, workspace=ws)
+    fstep_us = graph_time_us(torch, fstep)
     return {"experts": E, "tokens": T, "top_k": top_k, "count_min": int(counts.min()),
             "count_median": float(np.median(counts)), "count_max": int(counts.max()),
             "timing": "HIP graph replay (weights resident in the last-level cache across replays)",
@@ -285,7 +300,10 @@ def run_moe(torch, ops, synth):
             "gemm_TOP/s": round(tot_ops / (gemm_us * 1e-6) / 1e12, 1),
             "mfma_frac": round(tot_ops / (gemm_us * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4),
             "gemm_GB/s": round(tot_bytes / (gemm_us * 1e-6) / 1e9, 1),
-            "hbm_frac": round(tot_bytes / (gemm_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            "hbm_frac": round(tot_bytes / (gemm_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "gate_up_fused": {"gate_up_us": round(gu, 2), "step_us": round(fstep_us, 2),
+                              "tokens/s": round(T / (fstep_us * 1e-6), 1),
+                              "gemm_GB/s": round(tot_bytes / ((gu + dd) * 1e-6) / 1e9, 1)}}
 
 
 def run_w4a8(torch, ops, synth):
@@ -436,13 +454,38 @@ def run_layer_prompt(torch, ops, synth):
             for name, k, n in synth.DENSE_PROJECTIONS:
                 ops.gemm_prepared(packed[name], acts[synth.DENSE_INPUT_OF[name]], mrows, n, k, y=yb[name])
     us = graph_time_us(torch, layer, reps=5)
+    del packed, ys
+
+    # q|k|v and gate|up packed side by side: 4 GEMMs per micro-batch
+    ws = synth.layer_weights(workload=3)
+    groups = (("qkv", ("q", "k", "v"), "attn_in"), ("o", ("o",), "attn_out"),
+              ("gate_up", ("gate", "up"), "ffn_in"), ("down", ("down",), "ffn_act"))
+    shape = {g: (ws[parts[0]].shape[1], sum(ws[p].shape[0] for p in parts)) for g, parts, _ in groups}
+    fused = {g: ops.prepare_weights(torch.from_numpy(np.concatenate([ws[p] for p in parts])).to(dev))
+             for g, parts, _ in groups}
+    del ws
+    fys = [{g: torch.empty((mb["attn_in"].shape[0], shape[g][1]), dtype=torch.float32, device=dev)
+            for g, _, _ in groups} for mb in mbs]
+
+    def flayer():
+        for mb, yb in zip(mbs, fys):
+            mrows = mb["attn_in"].shape[0]
+            for inp, xin in mb.items():
+                ops.rotate_quantize_prepare(xin, acts[inp])
+            for g, _, inp in groups:
+                k, n = shape[g]
+                ops.gemm_prepared(fused[g], acts[inp], mrows, n, k, y=yb[g])
+    fus = graph_time_us(torch, flayer, reps=5)
     tokens = sum(synth.PROMPT_MICROBATCHES)
     ops_tot = sum(2.0 * tokens * n * k for _, k, n in synth.DENSE_PROJECTIONS)
     return {"tokens": tokens, "microbatches": list(synth.PROMPT_MICROBATCHES), "layer_ms": round(us * 1e-3, 4),
             "timing": "HIP graph replay of the four micro-batches",
             "tokens/s": round(tokens / (us * 1e-6), 1),
             "TOP/s": round(ops_tot / (us * 1e-6) / 1e12, 1),
-            "mfma_frac": round(ops_tot / (us * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4)}
+            "mfma_frac": round(ops_tot / (us * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4),
+            "same_input_fused": {"gemms_per_microbatch": len(groups), "layer_ms": round(fus * 1e-3, 4),
+                                 "tokens/s": round(tokens / (fus * 1e-6), 1),
+                                 "TOP/s": round(ops_tot / (fus * 1e-6) / 1e12, 1)}}
 
 
 # --------------------------------------------------------------------------
