@@ -359,6 +359,39 @@ def test_last_microbatch_302_rows(ops):
     assert_rows_close(y[rows], oracle.gemm(oracle.prepare_weights(w), rc[rows], rs[rows], k))
 
 
+def test_down_projection_m512_k17408_sampled_rows(ops):
+    """The longest K of the layer (17408 = 544 blocks) at M = 512 on the
+    matrix-core path, rows sampled across all four row tiles."""
+    k, n = 17408, 5120
+    w = synth.weights(n, k, synth.rng_for(0, 3, 6))
+    x = synth.layer_inputs(512, microbatch=0)["ffn_act"]
+    say("m=512 down 17408->5120, sampled rows")
+    packed = ops.prepare_weights(dev(w))
+    c, s = ops.rotate_quantize_act(dev(x))
+    y = host(ops.gemm(packed, c, s, n, k))
+    rows = np.array([0, 127, 128, 300, 383, 511])
+    rc, rs = oracle.rotate_quantize_act(x)
+    assert_rows_close(y[rows], oracle.gemm(oracle.prepare_weights(w), rc[rows], rs[rows], k), "down m512")
+
+
+def test_gate_up_packed_side_by_side_sampled_rows(ops):
+    """Gate and up packed as one 34816-column matrix (the layout the
+    benchmark's fused figures use): more than two rounds of 128 x 128 tiles,
+    the rest as pieces; each half equals the oracle on its own weights."""
+    k, n = 5120, 17408
+    wg = synth.weights(n, k, synth.rng_for(0, 3, 4))
+    wu = synth.weights(n, k, synth.rng_for(0, 3, 5))
+    x = synth.layer_inputs(512, microbatch=1)["ffn_in"]
+    say("m=512 gate|up 5120->34816, sampled rows")
+    packed = ops.prepare_weights(dev(np.concatenate([wg, wu])))
+    c, s = ops.rotate_quantize_act(dev(x))
+    y = host(ops.gemm(packed, c, s, 2 * n, k))
+    rows = np.array([0, 200, 511])
+    rc, rs = oracle.rotate_quantize_act(x)
+    assert_rows_close(y[rows, :n], oracle.gemm(oracle.prepare_weights(wg), rc[rows], rs[rows], k), "gate half")
+    assert_rows_close(y[rows, n:], oracle.gemm(oracle.prepare_weights(wu), rc[rows], rs[rows], k), "up half")
+
+
 # --------------------------------------------------------------------------
 # MUL_MAT_ID
 # --------------------------------------------------------------------------
