@@ -572,12 +572,16 @@ def main():
         f"gemm {r['gemm_ms'] * 1e3:.1f} us, {r['gemm_tops']:.1f} TOP/s")
     value = r["m"] / (r["wall_ms"] * 1e-3)
     traffic = counters_for("gemm_mx_kernel")
+    util = None
+    if traffic is not None:  # the same hash guard as the byte counters
+        util = json.load(open(PROFILE_JSON)).get("mfma_utilisation", {}).get("gemm_mx_kernel")
     roofline = {"bound": "mfma", "achieved": round(r["gemm_tops"], 2), "peak": PEAK_FP6_TOPS,
                 "unit": "TOP/s", "frac": round(r["gemm_tops"] / PEAK_FP6_TOPS, 4), "traffic": traffic,
                 "kernel": "gemm_mx_kernel (whole tiles, then K pieces of the leftover tiles, one launch: "
                           "FP6 32x32x64 MFMA block dots, bf16 MFMA scale products, fp32 epilogue)",
                 "ops_per_launch": r["gemm_ops"], "algorithmic_bytes_per_launch": r["gemm_bytes"],
                 "mean_launch_us": round(r["gemm_ms"] * 1e3, 3),
+                "mfma_busy_pct": None if util is None else util["mfma_busy_pct"],
                 "frac_of_int8_peak": round(r["gemm_tops"] / PEAK_INT8_TOPS, 4),
                 "note": "a 32-code block fills half the K of one FP6 MFMA, so exact per-block dots "
                         "can reach at most half the FP6 peak, the int8 peak"}
