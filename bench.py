@@ -443,6 +443,10 @@ def run_layer_prompt(torch, ops, synth):
            for name, _, n in synth.DENSE_PROJECTIONS} for mb in mbs]
     acts = {name: torch.empty(max(1, ops.act_operand_bytes(512, k)), dtype=torch.uint8, device=dev)
             for name, k in (("attn_in", 5120), ("attn_out", 6144), ("ffn_in", 5120), ("ffn_act", 17408))}
+    # one split-K workspace for every product (they run one after another on one stream)
+    ws_bytes = max(ops.gemm_prepared_workspace_bytes(mr, n, k) for mr in synth.PROMPT_MICROBATCHES
+                   for _, k, n in synth.DENSE_PROJECTIONS + (("qkv", 5120, 8192), ("gate_up", 5120, 34816)))
+    wsp = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
 
     def layer():
         # each distinct input is quantised and prepared once (Q/K/V share one,
@@ -452,7 +456,7 @@ def run_layer_prompt(torch, ops, synth):
             for inp, xin in mb.items():
                 ops.rotate_quantize_prepare(xin, acts[inp])
             for name, k, n in synth.DENSE_PROJECTIONS:
-                ops.gemm_prepared(packed[name], acts[synth.DENSE_INPUT_OF[name]], mrows, n, k, y=yb[name])
+                ops.gemm_prepared(packed[name], acts[synth.DENSE_INPUT_OF[name]], mrows, n, k, y=yb[name], workspace=wsp)
     us = graph_time_us(torch, layer, reps=5)
     del packed, ys
 
@@ -474,7 +478,7 @@ def run_layer_prompt(torch, ops, synth):
                 ops.rotate_quantize_prepare(xin, acts[inp])
             for g, _, inp in groups:
                 k, n = shape[g]
-                ops.gemm_prepared(fused[g], acts[inp], mrows, n, k, y=yb[g])
+                ops.gemm_prepared(fused[g], acts[inp], mrows, n, k, y=yb[g], workspace=wsp)
     fus = graph_time_us(torch, flayer, reps=5)
     tokens = sum(synth.PROMPT_MICROBATCHES)
     ops_tot = sum(2.0 * tokens * n * k for _, k, n in synth.DENSE_PROJECTIONS)

@@ -44,7 +44,8 @@ def lib() -> ctypes.CDLL:
             "w4a4_gemm_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_act_operand_bytes": ([I64, I64], SZ),
             "w4a4_gemm_prepare_act": ([P, P, I64, I64, P, SZ, P], ST),
-            "w4a4_gemm_prepared": ([P, P, P, I64, I64, I64, I64, P], ST),
+            "w4a4_gemm_prepared": ([P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
+            "w4a4_gemm_prepared_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_gemm": ([P, P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_id_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_rotate_quantize_act8": ([P, ST, I64, I64, I64, P, P, P], ST),
@@ -206,15 +207,24 @@ def prepare_act(codes: torch.Tensor, scales: torch.Tensor, k: int,
     return out
 
 
+def gemm_prepared_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(lib().w4a4_gemm_prepared_workspace_bytes(m, n, k))
+
+
 def gemm_prepared(packed: torch.Tensor, act: torch.Tensor, m: int, n: int, k: int,
-                  y: torch.Tensor | None = None) -> torch.Tensor:
-    """W4A4 product on a prepared activation: fp32 [m, n] (row stride y.stride(0))."""
-    _require_cuda(packed, act, y)
+                  y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A4 product on a prepared activation: fp32 [m, n] (row stride y.stride(0)).
+    The split-K workspace is allocated here when one is needed and not given."""
+    _require_cuda(packed, act, y, workspace)
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=act.device)
     assert y.stride(1) == 1
-    _check(lib().w4a4_gemm_prepared(_ptr(packed), _ptr(act), _ptr(y), m, n, k, y.stride(0),
-                                    _stream(act.device)), "w4a4_gemm_prepared")
+    need = gemm_prepared_workspace_bytes(m, n, k)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=act.device)
+    _check(lib().w4a4_gemm_prepared(_ptr(packed), _ptr(act), _ptr(y), m, n, k, y.stride(0), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(), _stream(act.device)),
+           "w4a4_gemm_prepared")
     return y
 
 

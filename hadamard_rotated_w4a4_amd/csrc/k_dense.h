@@ -131,6 +131,8 @@ struct MxArgs {
     const uint8_t *wrec;    // weight records [tiles_n][nbp][1 KB]
     float *y;
     int64_t ldy, m, n, k;
+    int64_t splits = 1;     // K splits of every tile (1: whole K, stored to y)
+    float *partial = nullptr;  // splits > 1: [splits][m][n] partial sums
 };
 
 template <int BKB_, int NS_, int TM_, int TN_>
@@ -197,6 +199,9 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
     const int64_t nbp = mx_blocks(a.k);
     const int64_t rtiles = (a.m + 31) / 32, ctiles = padded_n(a.n) / TILE_N;
 
+    // split K: workgroups id * splits + z take K part z of one tile
+    const int64_t z = a.splits > 1 ? id % a.splits : 0;
+    if (a.splits > 1) id /= a.splits;
     int64_t bx, by;
     mx_tile_of(id, (a.n + C::BN - 1) / C::BN, (a.m + C::BM - 1) / C::BM, bx, by);
     const int64_t rt0 = by * RT, ct0 = bx * C::CT;
@@ -217,12 +222,15 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
         dst[d] = (uint32_t)((t * BKB + bb) * MX_REC);
     }
     const uint32_t voff = lane * 16;
-    const int nstages = (int)(nbp / BKB);
+    // this workgroup's stages: whole pairs of stages, part z of splits
+    const int64_t pairs = nbp / BKB / 2;
+    const int s_lo = (int)(z * pairs / a.splits) * 2;
+    const int nstages = (int)((z + 1) * pairs / a.splits) * 2 - s_lo;
     // Load d of stage `stage` into ring slot `slot`.  Past the last stage
     // the ring keeps reloading the last one (its slot is never computed): the
     // count of loads in flight stays fixed.
     auto issue_one = [&](int stage, int slot, int d) {
-        const int64_t kb0 = (int64_t)min(stage, nstages - 1) * BKB;
+        const int64_t kb0 = (int64_t)(s_lo + min(stage, nstages - 1)) * BKB;
         const uint32_t lds = __builtin_amdgcn_readfirstlane(smem_base + slot * C::STAGE_BYTES);
         dma16s(src[d] + kb0 * MX_REC, voff, lds + dst[d]);
     };
@@ -350,7 +358,9 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int64_t r = rbase + mfma32_row(v, lane);
-                if (r < a.m) a.y[r * a.ldy + col] = acc[i][j][v];
+                if (r >= a.m) continue;
+                if (a.splits > 1) a.partial[(z * a.m + r) * a.n + col] = acc[i][j][v];
+                else a.y[r * a.ldy + col] = acc[i][j][v];
             }
         }
     }

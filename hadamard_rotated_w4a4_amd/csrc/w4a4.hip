@@ -101,7 +101,46 @@ void launch_mx_cfg(const MxArgs &a, const MxPlan &p, hipStream_t s) {
     gemm_mx_kernel<C><<<(unsigned)(p.main_wgs + p.piece_wgs), C::NT, 0, s>>>(a, p.main_wgs, p.first_piece_tile);
 }
 
-void launch_mx(const MxArgs &a, hipStream_t s) {
+// Split K.  A product with fewer 128 x 128 tiles than one round of resident
+// workgroups would otherwise run entirely as 32 x 32 pieces (no operand reuse
+// across waves, ~1.6x the cost per output).  With a long K, S whole-tile
+// workgroups per tile, each over 1/S of the stage pairs, fill the round
+// instead; their partial sums are added in ascending split order by a second
+// kernel.  Pure function of the sizes, modelled on a 256-CU part with two
+// resident workgroups per CU (so the workspace size is one too): S =
+// min(round / tiles, pairs of stages / 16), taken when its modelled time is
+// under 3/4 of the pieces'.  Returns 1 for no split.
+constexpr int64_t kSplitRefSlots = 512;
+int64_t mx_k_splits(int64_t m, int64_t n, int64_t k) {
+    if (m <= SMALL_M_MAX || k <= 0) return 1;
+    const int64_t tiles = (m + 127) / 128 * ((n + 127) / 128);
+    if (tiles >= kSplitRefSlots) return 1;
+    const int64_t pairs = mx_blocks(k) / 4;
+    const int64_t S = std::min(kSplitRefSlots / tiles, pairs / 16);
+    if (S < 2) return 1;
+    const double t_split = (double)((tiles * S + kSplitRefSlots - 1) / kSplitRefSlots) / S;
+    const double t_pieces = (double)((tiles * 16 + kSplitRefSlots - 1) / kSplitRefSlots) * 1.6 / 16;
+    return t_split < 0.75 * t_pieces ? S : 1;
+}
+
+size_t split_partial_bytes(int64_t m, int64_t n, int64_t k) {
+    const int64_t S = mx_k_splits(m, n, k);
+    return S > 1 ? (size_t)((S * m * n * 4 + 255) / 256 * 256) : 0;
+}
+
+// partial: S x m x n fp32 when mx_k_splits(m, n, k) = S > 1 (checked by the caller)
+void launch_mx(const MxArgs &a0, float *partial, hipStream_t s) {
+    const int64_t S = mx_k_splits(a0.m, a0.n, a0.k);
+    if (S > 1) {
+        MxArgs a = a0;
+        a.splits = S;
+        a.partial = partial;
+        const int64_t wgs = (a.m + 127) / 128 * ((a.n + 127) / 128) * S;
+        gemm_mx_kernel<Mx128x128><<<(unsigned)wgs, Mx128x128::NT, 0, s>>>(a, wgs, 0);
+        small_m_reduce_kernel<<<blocks_for(a.m * a.n, 256), 256, 0, s>>>(partial, S, a.m, a.n, a.y, a.ldy);
+        return;
+    }
+    const MxArgs &a = a0;
     const MxPlan p0 = mx_plan<Mx128x128>(a.m, a.n), p1 = mx_plan<Mx128x64>(a.m, a.n), p2 = mx_plan<Mx64x128>(a.m, a.n);
     if (p0 <= p1 && p0 <= p2) launch_mx_cfg<Mx128x128>(a, p0, s);
     else if (p1 <= p2) launch_mx_cfg<Mx128x64>(a, p1, s);
@@ -259,7 +298,13 @@ size_t w4a4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
         const int64_t splits = small_m_splits(n, k);
         return splits > 1 ? (size_t)((splits * m * n * 4 + 255) / 256 * 256) : 0;
     }
-    return w4a4_act_operand_bytes(m, k);
+    return (w4a4_act_operand_bytes(m, k) + 255) / 256 * 256 + split_partial_bytes(m, n, k);
+}
+
+size_t w4a4_gemm_prepared_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+    if (m < 0 || n < 0 || k < 0 || k % QK) return 0;
+    if (m == 0 || n == 0 || k == 0) return 0;
+    return split_partial_bytes(m, n, k);
 }
 
 w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *scales, float *y,
@@ -303,9 +348,15 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
         small_m_reduce_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(a.partial, splits, m, n, y, ldy);
         return hip_status("small_m_reduce_kernel");
     }
+    // workspace: the activation operand, then the split-K partial sums
+    if (!workspace) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(workspace, 256)) return W4A4_ERR_MISALIGNED;
+    if (workspace_bytes < w4a4_gemm_workspace_bytes(m, n, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
     const w4a4_status pst = w4a4_gemm_prepare_act(codes, scales, m, k, workspace, workspace_bytes, stream);
     if (pst != W4A4_OK) return pst;
-    return w4a4_gemm_prepared(packed_w, workspace, y, m, n, k, ldy, stream);
+    const size_t act_bytes = (w4a4_act_operand_bytes(m, k) + 255) / 256 * 256;
+    return w4a4_gemm_prepared(packed_w, workspace, y, m, n, k, ldy, static_cast<uint8_t *>(workspace) + act_bytes,
+                              workspace_bytes - act_bytes, stream);
 }
 
 size_t w4a4_gemm_a8_workspace_bytes(int64_t m, int64_t n, int64_t k) {
@@ -396,7 +447,7 @@ w4a4_status w4a4_gemm_prepare_act(const uint8_t *codes, const float *scales, int
 }
 
 w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, int64_t m, int64_t n,
-                               int64_t k, int64_t ldy, void *stream) {
+                               int64_t k, int64_t ldy, void *workspace, size_t workspace_bytes, void *stream) {
     if (m < 0 || n < 0 || k < 0 || m > kMaxRows || ldy < n) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
     if (m == 0 || n == 0) return W4A4_OK;
@@ -409,6 +460,12 @@ w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, 
     }
     if (!packed_w || !act) return W4A4_ERR_INVALID_VALUE;
     if (!aligned(packed_w, 16) || !aligned(act, 256)) return W4A4_ERR_MISALIGNED;
+    const size_t need = w4a4_gemm_prepared_workspace_bytes(m, n, k);
+    if (need) {
+        if (!workspace) return W4A4_ERR_INVALID_VALUE;
+        if (!aligned(workspace, 256)) return W4A4_ERR_MISALIGNED;
+        if (workspace_bytes < need) return W4A4_ERR_WORKSPACE_TOO_SMALL;
+    }
     MxArgs a{};
     a.act = static_cast<const uint8_t *>(act);
     a.wrec = static_cast<const uint8_t *>(packed_w);  // the matrix-core section
@@ -417,7 +474,7 @@ w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, 
     a.m = m;
     a.n = n;
     a.k = k;
-    launch_mx(a, s);
+    launch_mx(a, static_cast<float *>(workspace), s);
     return hip_status("gemm_mx_kernel");
 }
 

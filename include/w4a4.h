@@ -144,8 +144,10 @@ w4a4_status w4a4_rotate_quantize_prepare(const void *x, w4a4_dtype dt, int64_t m
  * with few 32-column tiles or long K split K over workgroups; the workspace
  * then holds their partial sums, added in ascending split order by a second
  * kernel).  Larger m first re-lays the activation codes and
- * scales into the matrix-core operand format in the workspace, then runs the
- * tiled matrix-core kernel.
+ * scales into the matrix-core operand format at the start of the workspace
+ * (w4a4_act_operand_bytes rounded up to 256), then runs the tiled
+ * matrix-core kernel with the rest of the workspace as its own
+ * (w4a4_gemm_prepared).
  */
 w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *scales, float *y,
                       int64_t m, int64_t n, int64_t k, int64_t ldy, void *workspace,
@@ -163,12 +165,24 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
  *         layout.
  *
  * w4a4_gemm_prepared: the product of packed_w with a prepared activation, as
- * w4a4_gemm (any m >= 1; y [m][ldy] fp32).
+ * w4a4_gemm (any m >= 1; y [m][ldy] fp32).  A product with fewer 128 x 128
+ * output tiles than one round of resident workgroups and a long K splits K
+ * over whole tiles: then workspace holds w4a4_gemm_prepared_workspace_bytes
+ * (m, n, k) bytes of partial sums (256-byte aligned; contents on entry
+ * ignored; calls sharing it must not overlap), added in ascending split
+ * order by a second kernel.  workspace may be NULL when that size is 0
+ * (for instance any m <= 16, or more tiles than one round).
+ *
+ * w4a4_gemm_prepared_workspace_bytes: 0 when no split (or invalid sizes),
+ * else splits * m * n * 4 rounded up to 256.  Host only, pure: the split
+ * count is a function of the sizes alone.
  */
 w4a4_status w4a4_gemm_prepare_act(const uint8_t *codes, const float *scales, int64_t m, int64_t k,
                                   void *act, size_t act_bytes, void *stream);
+size_t w4a4_gemm_prepared_workspace_bytes(int64_t m, int64_t n, int64_t k);
 w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, int64_t m, int64_t n,
-                               int64_t k, int64_t ldy, void *stream);
+                               int64_t k, int64_t ldy, void *workspace, size_t workspace_bytes,
+                               void *stream);
 
 /*
  * W4A8-H32: the exact int8 path for a rotated file (section "Hadamard-rotated

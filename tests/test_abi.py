@@ -122,14 +122,27 @@ def test_prepared_gemm_validation(L):
     assert prep(P(A), P(A), 64, 64, P(A), pb - 1, None) == WS
     assert prep(None, None, 0, 64, None, 0, None) == OK
     run = L.w4a4_gemm_prepared
-    assert run(P(A), P(A), P(A), 64, 64, 33, 64, None) == KMUL
-    assert run(P(A), P(A), P(A), 64, 64, 64, 63, None) == INVALID  # ldy < n
-    assert run(None, P(A), P(A), 64, 64, 64, 64, None) == INVALID
-    assert run(P(A), None, P(A), 64, 64, 64, 64, None) == INVALID
-    assert run(P(A), P(A), None, 64, 64, 64, 64, None) == INVALID
-    assert run(P(A), P(A + 16), P(A), 64, 64, 64, 64, None) == MISALIGNED
-    assert run(P(A + 8), P(A), P(A), 64, 64, 64, 64, None) == MISALIGNED
-    assert run(None, None, None, 0, 64, 64, 64, None) == OK
+    assert run(P(A), P(A), P(A), 64, 64, 33, 64, None, 0, None) == KMUL
+    assert run(P(A), P(A), P(A), 64, 64, 64, 63, None, 0, None) == INVALID  # ldy < n
+    assert run(None, P(A), P(A), 64, 64, 64, 64, None, 0, None) == INVALID
+    assert run(P(A), None, P(A), 64, 64, 64, 64, None, 0, None) == INVALID
+    assert run(P(A), P(A), None, 64, 64, 64, 64, None, 0, None) == INVALID
+    assert run(P(A), P(A + 16), P(A), 64, 64, 64, 64, None, 0, None) == MISALIGNED
+    assert run(P(A + 8), P(A), P(A), 64, 64, 64, 64, None, 0, None) == MISALIGNED
+    assert run(None, None, None, 0, 64, 64, 64, None, 0, None) == OK
+    # split K: the FFN-down shape (160 tiles of 128 x 128, 544 blocks) needs
+    # 3 x m x n fp32 of partial sums; the FFN-up shape (544 tiles) none
+    need = L.w4a4_gemm_prepared_workspace_bytes(512, 5120, 17408)
+    assert need == 3 * 512 * 5120 * 4
+    assert L.w4a4_gemm_prepared_workspace_bytes(512, 17408, 5120) == 0
+    assert L.w4a4_gemm_prepared_workspace_bytes(16, 5120, 17408) == 0   # m <= 16: no matrix-core path
+    assert L.w4a4_gemm_prepared_workspace_bytes(512, 1024, 5120) == 0   # K too short to split
+    assert run(P(A), P(A), P(A), 512, 5120, 17408, 5120, None, 0, None) == INVALID
+    assert run(P(A), P(A), P(A), 512, 5120, 17408, 5120, P(A + 16), need, None) == MISALIGNED
+    assert run(P(A), P(A), P(A), 512, 5120, 17408, 5120, P(A), need - 1, None) == WS
+    # w4a4_gemm's workspace: the operand (256-rounded), then the partial sums
+    assert L.w4a4_gemm_workspace_bytes(512, 5120, 17408) == L.w4a4_act_operand_bytes(512, 17408) + need
+    assert L.w4a4_gemm_workspace_bytes(512, 17408, 5120) == L.w4a4_act_operand_bytes(512, 5120)
 
 
 def test_rotate_quantize_prepare_validation(L):

@@ -74,6 +74,24 @@ def test_dense_step_replays(ops):
     replay_matches_eager(step, x, inputs, [codes, scales, y])
 
 
+def test_dense_split_k_step_replays(ops):
+    m, n, k = 512, 5120, 6144                   # few tiles, long K: split K and the reduction
+    say(f"graph: rotate-quantise-prepare + split-K gemm_prepared m={m} n={n} k={k}")
+    assert ops.gemm_prepared_workspace_bytes(m, n, k) > 0
+    rng = np.random.default_rng(9)
+    packed = ops.prepare_weights(torch.from_numpy(synth.weights(n, k, rng)).cuda())
+    inputs = _inputs(m, k, 10, count=2)
+    x = torch.empty_like(inputs[0])
+    act = torch.empty(ops.act_operand_bytes(m, k), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(ops.gemm_prepared_workspace_bytes(m, n, k), dtype=torch.uint8, device="cuda")
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+
+    def step():
+        ops.rotate_quantize_prepare(x, act)
+        ops.gemm_prepared(packed, act, m, n, k, y=y, workspace=ws)
+    replay_matches_eager(step, x, inputs, [y])
+
+
 def test_small_m_split_k_step_replays(ops):
     m, n, k = 16, 1024, 5120                     # K split over many workgroups, then the reduction
     say(f"graph: rotate-quantise + small-M gemm (split K) m={m} n={n} k={k}")

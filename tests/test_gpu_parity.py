@@ -374,6 +374,41 @@ def test_down_projection_m512_k17408_sampled_rows(ops):
     assert_rows_close(y[rows], oracle.gemm(oracle.prepare_weights(w), rc[rows], rs[rows], k), "down m512")
 
 
+@pytest.mark.parametrize("m,k,name", [(512, 6144, "o"), (512, 17408, "down"), (302, 17408, "down302")])
+def test_split_k_whole_tiles_sampled_rows(ops, m, k, name):
+    """Products with few 128 x 128 tiles and a long K (the layer's o and down
+    projections, N = 5120) split K over whole tiles; the partial sums are
+    added in ascending split order, so repeated calls agree bit for bit."""
+    n = 5120
+    assert ops.gemm_prepared_workspace_bytes(m, n, k) > 0
+    rng = np.random.default_rng(m + k)
+    w = synth.weights(n, k, rng)
+    x = synth.activations(m, k, rng, k // 100)
+    say(f"split K {name} m={m} n={n} k={k}, sampled rows")
+    packed = ops.prepare_weights(dev(w))
+    c, s = ops.rotate_quantize_act(dev(x))
+    ws = torch.empty(ops.gemm_workspace_bytes(m, n, k), dtype=torch.uint8, device="cuda")
+    y = host(ops.gemm(packed, c, s, n, k, workspace=ws))
+    assert np.array_equal(y, host(ops.gemm(packed, c, s, n, k, workspace=ws)))
+    rows = np.array([0, 127, 128, m // 2, m - 1])
+    rc, rs = oracle.rotate_quantize_act(x[rows])
+    assert_rows_close(y[rows], oracle.gemm(oracle.prepare_weights(w), rc, rs, k), name)
+
+
+def test_split_k_integer_unit_scales(ops):
+    """Split K with unit scales: every partial sum is an exact integer, so
+    the product equals the oracle's integer sums exactly."""
+    m, n, k = 512, 5120, 17408
+    w, x = _problem(m, n, k, 99)
+    q4 = with_unit_scales(oracle.prepare_weights(w))
+    rc, _ = oracle.rotate_quantize_act(x)
+    ones = np.ones((m, k // 32), np.float32)
+    say(f"split K integer unit scales m={m} n={n} k={k}")
+    y = host(ops.gemm(ops.repack_q4_0_h32(dev(q4), n, k), dev(rc), dev(ones), n, k))
+    rows = np.array([0, 200, 511])
+    assert np.array_equal(y[rows], oracle.gemm(q4, rc[rows], ones[rows], k))
+
+
 def test_gate_up_packed_side_by_side_sampled_rows(ops):
     """Gate and up packed as one 34816-column matrix (the layout the
     benchmark's fused figures use): more than two rounds of 128 x 128 tiles,
