@@ -395,6 +395,25 @@ def test_split_k_whole_tiles_sampled_rows(ops, m, k, name):
     assert_rows_close(y[rows], oracle.gemm(oracle.prepare_weights(w), rc, rs, k), name)
 
 
+def test_split_k_many_splits_small_m(ops):
+    """m = 100, n = 1000 (8 tiles), K = 32768: 16 splits of 16 stage pairs;
+    sampled rows against the oracle, and exact integer sums with unit scales."""
+    m, n, k = 100, 1000, 32768
+    assert ops.gemm_prepared_workspace_bytes(m, n, k) == 16 * m * n * 4
+    w, x = _problem(m, n, k, 5)
+    say(f"split K x16 m={m} n={n} k={k}")
+    q4 = oracle.prepare_weights(w)
+    c, s = ops.rotate_quantize_act(dev(x))
+    y = host(ops.gemm(ops.repack_q4_0_h32(dev(q4), n, k), c, s, n, k))
+    rows = np.array([0, 31, 32, 99])
+    rc, rs = oracle.rotate_quantize_act(x[rows])
+    assert_rows_close(y[rows], oracle.gemm(q4, rc, rs, k), "split x16")
+    qu = with_unit_scales(q4)
+    ones = np.ones((m, k // 32), np.float32)
+    yu = host(ops.gemm(ops.repack_q4_0_h32(dev(qu), n, k), c, dev(ones), n, k))
+    assert np.array_equal(yu[rows], oracle.gemm(qu, host(c)[rows], ones[rows], k))
+
+
 def test_split_k_integer_unit_scales(ops):
     """Split K with unit scales: every partial sum is an exact integer, so
     the product equals the oracle's integer sums exactly."""
