@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
             "w4a4_gemm_a8_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_gemm_a8": ([P, P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_id": ([P, I64, P, P, I64, P, I64, I64, P, I64, I64, P, SZ, P], ST),
+            "w4a4_gemm_id_route": ([P, I64, I64, I64, P, SZ, P], ST),
+            "w4a4_gemm_id_routed": ([P, I64, P, P, I64, I64, I64, P, I64, I64, P, SZ, P], ST),
             "w4a4_w16_weight_bytes": ([I64, I64], SZ),
             "w4a4_w16_act_bytes": ([I64, I64], SZ),
             "w4a4_dequantize_w16": ([P, I64, I64, P, SZ, P], ST),
@@ -243,6 +245,32 @@ def gemm_id(packed: torch.Tensor, n_expert: int, codes: torch.Tensor, scales: to
     _check(lib().w4a4_gemm_id(_ptr(packed), n_expert, _ptr(codes), _ptr(scales), act_rows_per_token,
                               _ptr(ids.contiguous()), n_tokens, top_k, _ptr(y), n, k, _ptr(workspace),
                               workspace.numel(), _stream(ids.device)), "w4a4_gemm_id")
+    return y
+
+
+def gemm_id_route(ids: torch.Tensor, n_expert: int, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """MUL_MAT_ID routing of ids [n_tokens, top_k] into a workspace (returned)."""
+    _require_cuda(ids, workspace)
+    assert ids.dtype == torch.int32 and ids.dim() == 2 and ids.is_contiguous()
+    n_tokens, top_k = ids.shape
+    if workspace is None:
+        workspace = torch.empty(max(1, gemm_id_workspace_bytes(n_expert, n_tokens, top_k)), dtype=torch.uint8,
+                                device=ids.device)
+    _check(lib().w4a4_gemm_id_route(_ptr(ids), n_expert, n_tokens, top_k, _ptr(workspace), workspace.numel(),
+                                    _stream(ids.device)), "w4a4_gemm_id_route")
+    return workspace
+
+
+def gemm_id_routed(packed: torch.Tensor, n_expert: int, codes: torch.Tensor, scales: torch.Tensor,
+                   act_rows_per_token: int, n_tokens: int, top_k: int, n: int, k: int, workspace: torch.Tensor,
+                   y: torch.Tensor | None = None) -> torch.Tensor:
+    """MUL_MAT_ID on a routing from gemm_id_route: fp32 [n_tokens, top_k, n]."""
+    _require_cuda(packed, codes, scales, workspace, y)
+    if y is None:
+        y = torch.empty((n_tokens, top_k, n), dtype=torch.float32, device=codes.device)
+    _check(lib().w4a4_gemm_id_routed(_ptr(packed), n_expert, _ptr(codes), _ptr(scales), act_rows_per_token,
+                                     n_tokens, top_k, _ptr(y), n, k, _ptr(workspace), workspace.numel(),
+                                     _stream(codes.device)), "w4a4_gemm_id_routed")
     return y
 
 

@@ -49,6 +49,7 @@ struct GsArgs {
     int64_t dense_rows;      // >= 0: a plain product of this many rows, no routing
     Routing g;
     int top_k, per_slot;     // activation row of routed row i: i (per slot) or i / top_k
+    int64_t n_rows;          // routed rows (tokens x slots); those past offsets[E] have invalid ids
     int64_t col_chunks;      // ceil(tiles / GS_WAVES)
 };
 
@@ -64,8 +65,16 @@ __global__ __launch_bounds__(64 * GS_WAVES) void gemm_grouped_stream_kernel(GsAr
     const int64_t k = a.k, nb = k / QK, nq = sq_quads(k);
     const int64_t tiles = padded_n(a.n) / TILE_N;
 
-    // item: contiguous share per XCD (ids x, x + 8, ... run on XCD x)
     const bool dense = a.dense_rows >= 0;
+    // workgroup 0 first zeroes the output rows of invalid ids (the routing put
+    // them after the valid rows), whatever item it takes after
+    if (!dense && blockIdx.x == 0) {
+        const int64_t first = a.g.offsets[a.g.n_expert], bad = a.n_rows - first;
+        for (int64_t i = tid; i < bad * a.n; i += 64 * GS_WAVES)
+            a.y[(int64_t)a.g.perm[first + i / a.n] * a.ldy + i % a.n] = 0.0f;
+    }
+
+    // item: contiguous share per XCD (ids x, x + 8, ... run on XCD x)
     const int64_t rtiles = dense ? (a.dense_rows + GS_ROWS - 1) / GS_ROWS : a.g.tile_prefix[a.g.n_expert];
     const int64_t items = rtiles * a.col_chunks, per_xcd = (items + 7) / 8;
     const int64_t j = blockIdx.x / 8, item = (blockIdx.x % 8) * per_xcd + j;

@@ -31,7 +31,10 @@ __device__ __forceinline__ int expert_of_tile(const Routing &g, int64_t t) {
 
 // -------------------------------------------------------------------------
 // MUL_MAT_ID routing: one workgroup groups the (token, slot) rows by expert
-// and counts each expert's row tiles; rows with an invalid id are zeroed.
+// and counts each expert's row tiles; rows with an invalid id go to the end
+// of the permutation (perm[offsets[E] ..]), where the GEMM zeroes their
+// output rows.  The routing depends on the ids alone, so one routing serves
+// every product of a layer that reads the same ids.
 // -------------------------------------------------------------------------
 constexpr int ROUTE_THREADS = 1024;
 constexpr int ROUTE_MAX_EXPERTS = 8192;
@@ -45,10 +48,10 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t *__r
                                                               int n_expert, int tile_rows,
                                                               int32_t *__restrict__ offsets,
                                                               int32_t *__restrict__ tile_prefix,
-                                                              int32_t *__restrict__ perm, float *__restrict__ y,
-                                                              int64_t n) {
+                                                              int32_t *__restrict__ perm) {
     __shared__ int cnt[ROUTE_MAX_EXPERTS];
     __shared__ int wrow[ROUTE_THREADS / 64], wtile[ROUTE_THREADS / 64];
+    __shared__ int bad_cursor;  // next slot for a row with an invalid id
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int e = tid; e < n_expert; e += ROUTE_THREADS) cnt[e] = 0;
     __syncthreads();
@@ -94,14 +97,11 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t *__r
     if (tid == ROUTE_THREADS - 1) {
         offsets[n_expert] = run;
         tile_prefix[n_expert] = trun;
+        bad_cursor = run;  // the valid rows end here
     }
     __syncthreads();
     auto place = [&](int i, int e) {
-        if (e >= 0 && e < n_expert) {
-            perm[atomicAdd(&cnt[e], 1)] = i;
-        } else {
-            for (int64_t j = 0; j < n; j++) y[(int64_t)i * n + j] = 0.0f;
-        }
+        perm[atomicAdd(e >= 0 && e < n_expert ? &cnt[e] : &bad_cursor, 1)] = i;
     };
 #pragma unroll
     for (int q = 0; q < ROUTE_KEEP; q++) {

@@ -577,10 +577,29 @@ size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t 
     return 2 * up256((n_expert + 1) * 4) + up256(n_tokens * top_k * 4);
 }
 
-w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *codes, const float *scales,
-                         int64_t act_rows_per_token, const int32_t *ids, int64_t n_tokens, int64_t top_k,
-                         float *y, int64_t n, int64_t k, void *workspace, size_t workspace_bytes,
-                         void *stream) {
+w4a4_status w4a4_gemm_id_route(const int32_t *ids, int64_t n_expert, int64_t n_tokens, int64_t top_k,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    if (n_tokens < 0 || top_k < 0 || n_expert < 0) return W4A4_ERR_INVALID_VALUE;
+    if (n_tokens == 0 || top_k == 0) return W4A4_OK;
+    if (n_expert < 1 || n_expert > ROUTE_MAX_EXPERTS) return W4A4_ERR_INVALID_VALUE;
+    const int64_t n_rows = n_tokens * top_k;
+    if (n_rows > INT32_MAX) return W4A4_ERR_INVALID_VALUE;
+    if (!ids || !workspace) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(ids, 4) || !aligned(workspace, 256)) return W4A4_ERR_MISALIGNED;
+    if (workspace_bytes < w4a4_gemm_id_workspace_bytes(n_expert, n_tokens, top_k))
+        return W4A4_ERR_WORKSPACE_TOO_SMALL;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    route_kernel<<<1, ROUTE_THREADS, 0, as_stream(stream)>>>(
+        ids, (int)n_rows, (int)n_expert, GS_ROWS, reinterpret_cast<int32_t *>(ws),
+        reinterpret_cast<int32_t *>(ws + up256((n_expert + 1) * 4)),
+        reinterpret_cast<int32_t *>(ws + 2 * up256((n_expert + 1) * 4)));
+    return hip_status("route_kernel");
+}
+
+w4a4_status w4a4_gemm_id_routed(const void *packed_w, int64_t n_expert, const uint8_t *codes,
+                                const float *scales, int64_t act_rows_per_token, int64_t n_tokens, int64_t top_k,
+                                float *y, int64_t n, int64_t k, const void *workspace, size_t workspace_bytes,
+                                void *stream) {
     if (n_tokens < 0 || top_k < 0 || n_expert < 0 || n < 0 || k < 0) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
     if (n_tokens == 0 || top_k == 0 || n == 0) return W4A4_OK;
@@ -590,14 +609,14 @@ w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *
     const int64_t row_tiles = grouped_row_tiles(n_expert, n_rows, GS_ROWS);
     const int64_t col_chunks = (padded_n(n) / TILE_N + GS_WAVES - 1) / GS_WAVES;
     if (n_rows > INT32_MAX || row_tiles * col_chunks + 8 > INT32_MAX) return W4A4_ERR_INVALID_VALUE;
-    if (!ids || !workspace) return W4A4_ERR_INVALID_VALUE;
+    if (!workspace) return W4A4_ERR_INVALID_VALUE;
     if (k > 0) {
         const w4a4_status st = check_gemm_common(packed_w, codes, scales, y, n, k);
         if (st != W4A4_OK) return st;
     } else if (!y) {
         return W4A4_ERR_INVALID_VALUE;
     }
-    if (!aligned(ids, 4) || !aligned(workspace, 256) || !aligned(y, 4)) return W4A4_ERR_MISALIGNED;
+    if (!aligned(workspace, 256) || !aligned(y, 4)) return W4A4_ERR_MISALIGNED;
     if (workspace_bytes < w4a4_gemm_id_workspace_bytes(n_expert, n_tokens, top_k))
         return W4A4_ERR_WORKSPACE_TOO_SMALL;
 
@@ -606,16 +625,7 @@ w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *
         zero_rows_kernel<<<blocks_for(n_rows * n, 256), 256, 0, s>>>(y, n_rows, n, n);
         return hip_status("zero_rows_kernel");
     }
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    int32_t *offsets = reinterpret_cast<int32_t *>(ws);
-    int32_t *tile_prefix = reinterpret_cast<int32_t *>(ws + up256((n_expert + 1) * 4));
-    int32_t *perm = reinterpret_cast<int32_t *>(ws + 2 * up256((n_expert + 1) * 4));
-
-    route_kernel<<<1, ROUTE_THREADS, 0, s>>>(ids, (int)n_rows, (int)n_expert, GS_ROWS, offsets, tile_prefix, perm,
-                                             y, n);
-    w4a4_status st = hip_status("route_kernel");
-    if (st != W4A4_OK) return st;
-
+    const uint8_t *ws = static_cast<const uint8_t *>(workspace);
     GsArgs a{};
     a.codes = codes;
     a.scales = scales;
@@ -626,13 +636,49 @@ w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *
     a.n = n;
     a.k = k;
     a.dense_rows = -1;
-    a.g = Routing{perm, offsets, tile_prefix, (int)n_expert};
+    a.g = Routing{reinterpret_cast<const int32_t *>(ws + 2 * up256((n_expert + 1) * 4)),
+                  reinterpret_cast<const int32_t *>(ws), reinterpret_cast<const int32_t *>(ws + up256((n_expert + 1) * 4)),
+                  (int)n_expert};
     a.top_k = (int)top_k;
     a.per_slot = act_rows_per_token != 1 ? 1 : 0;
+    a.n_rows = n_rows;
     a.col_chunks = col_chunks;
     // a bound on the items (row tiles x column chunks), rounded up to whole XCD rows
     gemm_grouped_stream_kernel<false><<<(unsigned)((row_tiles * col_chunks + 7) / 8 * 8), 64 * GS_WAVES, 0, s>>>(a);
     return hip_status("gemm_grouped_stream_kernel");
+}
+
+w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *codes, const float *scales,
+                         int64_t act_rows_per_token, const int32_t *ids, int64_t n_tokens, int64_t top_k,
+                         float *y, int64_t n, int64_t k, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    if (n_tokens < 0 || top_k < 0 || n_expert < 0 || n < 0 || k < 0) return W4A4_ERR_INVALID_VALUE;
+    if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
+    if (n_tokens == 0 || top_k == 0 || n == 0) return W4A4_OK;
+    if (!ids) return W4A4_ERR_INVALID_VALUE;
+    // validate everything before the first launch
+    if (n_expert < 1 || n_expert > ROUTE_MAX_EXPERTS) return W4A4_ERR_INVALID_VALUE;
+    if (act_rows_per_token != 1 && act_rows_per_token != top_k) return W4A4_ERR_INVALID_VALUE;
+    const int64_t n_rows = n_tokens * top_k;
+    const int64_t row_tiles = grouped_row_tiles(n_expert, n_rows, GS_ROWS);
+    const int64_t col_chunks = (padded_n(n) / TILE_N + GS_WAVES - 1) / GS_WAVES;
+    if (n_rows > INT32_MAX || row_tiles * col_chunks + 8 > INT32_MAX) return W4A4_ERR_INVALID_VALUE;
+    if (!workspace) return W4A4_ERR_INVALID_VALUE;
+    if (k > 0) {
+        const w4a4_status st = check_gemm_common(packed_w, codes, scales, y, n, k);
+        if (st != W4A4_OK) return st;
+    } else if (!y) {
+        return W4A4_ERR_INVALID_VALUE;
+    }
+    if (!aligned(ids, 4) || !aligned(workspace, 256) || !aligned(y, 4)) return W4A4_ERR_MISALIGNED;
+    if (workspace_bytes < w4a4_gemm_id_workspace_bytes(n_expert, n_tokens, top_k))
+        return W4A4_ERR_WORKSPACE_TOO_SMALL;
+    if (k > 0) {
+        const w4a4_status rst = w4a4_gemm_id_route(ids, n_expert, n_tokens, top_k, workspace, workspace_bytes, stream);
+        if (rst != W4A4_OK) return rst;
+    }
+    return w4a4_gemm_id_routed(packed_w, n_expert, codes, scales, act_rows_per_token, n_tokens, top_k, y, n, k,
+                               workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -302,9 +302,9 @@ size_t w4a4_gemm_id_workspace_bytes(int64_t n_expert, int64_t n_tokens, int64_t 
  *             offsets, tile counts, row permutation); contents on entry are
  *             ignored.  Calls that share a workspace must not overlap.
  * One launch groups the (token, slot) rows by expert (tiles of 32 rows per
- * expert); a second streams each expert's 4-bit weight records once per row
- * tile against the tile's activation rows (read through the permutation)
- * and scatters the rows to y.  Each output element depends only on its own
+ * expert; w4a4_gemm_id_route); a second streams each expert's 4-bit weight
+ * records once per row tile against the tile's activation rows (read through
+ * the permutation) and scatters the rows to y (w4a4_gemm_id_routed).  Each output element depends only on its own
  * row and column: the result does not depend on how rows are grouped.
  * Supports n_expert <= 8192.
  */
@@ -312,6 +312,29 @@ w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *
                          const float *scales, int64_t act_rows_per_token, const int32_t *ids,
                          int64_t n_tokens, int64_t top_k, float *y, int64_t n, int64_t k,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * w4a4_gemm_id in two steps, so that one routing serves every product of a
+ * layer that reads the same ids (gate, up and down of an MoE block):
+ *
+ * w4a4_gemm_id_route: groups the (token, slot) rows of ids by expert into
+ *   workspace (w4a4_gemm_id_workspace_bytes(n_expert, n_tokens, top_k)
+ *   bytes, 256-byte aligned): expert offsets, row tiles per expert, and the
+ *   row permutation, with the rows of invalid ids after the valid ones.  It
+ *   depends on ids, n_expert, n_tokens and top_k only.
+ *
+ * w4a4_gemm_id_routed: the product of w4a4_gemm_id, reading the routing that
+ *   w4a4_gemm_id_route wrote into workspace for the same n_expert, n_tokens
+ *   and top_k (enqueued before it; the workspace is only read, so several
+ *   routed products may share one routing).  Rows of invalid ids are zeroed
+ *   as in w4a4_gemm_id.  Other arguments and errors as w4a4_gemm_id.
+ */
+w4a4_status w4a4_gemm_id_route(const int32_t *ids, int64_t n_expert, int64_t n_tokens, int64_t top_k,
+                               void *workspace, size_t workspace_bytes, void *stream);
+w4a4_status w4a4_gemm_id_routed(const void *packed_w, int64_t n_expert, const uint8_t *codes,
+                                const float *scales, int64_t act_rows_per_token, int64_t n_tokens, int64_t top_k,
+                                float *y, int64_t n, int64_t k, const void *workspace, size_t workspace_bytes,
+                                void *stream);
 
 #ifdef __cplusplus
 }

@@ -248,3 +248,19 @@ def test_gemm_id_validation(L):
     assert call(ws=P(A + 16)) == MISALIGNED
     assert call(ids=P(A + 2)) == MISALIGNED
     assert call(T=0, packed=None, codes=None, scales=None, ids=None, y=None, ws=None) == OK
+    r = L.w4a4_gemm_id_route
+    assert r(None, 4, 8, 2, P(A), ws, None) == INVALID
+    assert r(P(A), 0, 8, 2, P(A), ws, None) == INVALID
+    assert r(P(A), 4, 8, 2, None, ws, None) == INVALID
+    assert r(P(A + 2), 4, 8, 2, P(A), ws, None) == MISALIGNED
+    assert r(P(A), 4, 8, 2, P(A + 16), ws, None) == MISALIGNED
+    assert r(P(A), 4, 8, 2, P(A), ws - 1, None) == WS
+    assert r(None, 4, 0, 2, None, 0, None) == OK
+    g = L.w4a4_gemm_id_routed
+    gargs = (P(A), 4, P(A), P(A), 1, 8, 2, P(A), 64, 64)
+    assert g(*gargs[:-1], 40, P(A), ws, None) == KMUL
+    assert g(*gargs, None, ws, None) == INVALID
+    assert g(*gargs, P(A + 16), ws, None) == MISALIGNED
+    assert g(*gargs, P(A), ws - 1, None) == WS
+    assert g(P(A), 4, P(A), P(A), 3, 8, 2, P(A), 64, 64, P(A), ws, None) == INVALID  # rows per token
+    assert g(None, 4, None, None, 1, 0, 2, None, 64, 64, None, 0, None) == OK

@@ -476,6 +476,43 @@ def test_gemm_id_small_end_to_end(ops, rows_per_token):
     assert_rows_close(y.reshape(-1, n), ref.reshape(-1, n), "gemm_id")
 
 
+def test_gemm_id_route_once_for_several_products(ops):
+    """One routing (w4a4_gemm_id_route) serves a gate-like product (one
+    activation row per token) and a down-like one (one per slot); each equals
+    w4a4_gemm_id bit for bit, invalid ids' rows included."""
+    E, T, top_k, n, k = 6, 11, 3, 70, 96
+    we, ids, rng = _moe_small(21)
+    x1 = synth.activations(T, k, rng, 2)
+    x3 = synth.activations(T * top_k, k, rng, 2)
+    say("gemm_id route once, two products")
+    packed = torch.cat([ops.prepare_weights(dev(w)) for w in we])
+    c1, s1 = ops.rotate_quantize_act(dev(x1))
+    c3, s3 = ops.rotate_quantize_act(dev(x3))
+    idsd = dev(ids)
+    ws = ops.gemm_id_route(idsd, E)
+    y1 = torch.full((T, top_k, n), float("nan"), device="cuda")
+    y3 = torch.full((T, top_k, n), float("nan"), device="cuda")
+    ops.gemm_id_routed(packed, E, c1, s1, 1, T, top_k, n, k, ws, y=y1)
+    ops.gemm_id_routed(packed, E, c3, s3, top_k, T, top_k, n, k, ws, y=y3)
+    assert np.array_equal(host(y1), host(ops.gemm_id(packed, E, c1, s1, 1, idsd, n, k)))
+    assert np.array_equal(host(y3), host(ops.gemm_id(packed, E, c3, s3, top_k, idsd, n, k)))
+    assert not host(y1)[2, 1].any() and not host(y3)[5, 0].any()
+
+
+def test_gemm_id_all_ids_invalid(ops):
+    """No valid id at all: no work item, every output row zero."""
+    E, T, top_k, n, k = 6, 5, 2, 70, 96
+    we, _, rng = _moe_small(22)
+    ids = np.full((T, top_k), E + 3, np.int32)
+    ids[1, 0] = -1
+    x = synth.activations(T, k, rng, 2)
+    packed = torch.cat([ops.prepare_weights(dev(w)) for w in we])
+    c, s = ops.rotate_quantize_act(dev(x))
+    y = torch.full((T, top_k, n), float("nan"), device="cuda")
+    ops.gemm_id(packed, E, c, s, 1, dev(ids), n, k, y=y)
+    assert not host(y).any()
+
+
 def test_gemm_id_integer_unit_scales(ops):
     E, T, top_k, n, k = 6, 11, 3, 70, 96
     we, ids, rng = _moe_small(9)
