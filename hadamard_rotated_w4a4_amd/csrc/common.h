@@ -25,15 +25,19 @@ constexpr int TILE_N = 32;           // columns per packed weight tile (one MFMA
 // operand of FP6 E2M3 fields, code t at bits 6t..6t+5; its six dwords lie in
 // three planes so that 32 lanes read each plane conflict-free:
 //   bytes [0, 768)     dwords 2p, 2p + 1 of column c at 256 p + 8 c (p < 3);
-//   bytes [768, 1024)  4 B at 768 + 4 (32 g + c) (g = 0, 1): the bf16 part d_g
-//                      of 64 * d = d_0 + d_1 (exact; d the column's fp16 Q4_0
-//                      scale) in both halves, so that lane 32 g + c of the
-//                      scale-product MFMA reads its operand as one dword.
+//   bytes [768, 896)   4 B at 768 + 4 c: the bf16 pair (d_0, d_1) with
+//                      64 * d = d_0 + d_1 exactly (d the column's fp16 Q4_0
+//                      scale; d_0 its leading 8 bits, d_1 the remaining 3);
+//   bytes [896, 1024)  zero.
 // A 32x32x64 MFMA lane l takes its operand from the record of block b + l/32
 // (lanes 32..63 the next block), so one operand register set carries two
-// blocks; per-lane MX scales select one of them per MFMA.
+// blocks; per-lane MX scales select one of them per MFMA.  The scale-product
+// MFMA (32x32x4, two blocks per instruction) reads lane l's (d_0, d_1) from
+// the same record as the codes.
 // The activation operand built by the GEMM's pre-pass has the same record
-// shape per (32-row tile, block), with a bf16 triple per row at 768.
+// shape per (32-row tile, block); at 768 + 8 r it holds the bf16 quadruple
+// (s_1, s_1, s_2, s_2) of row r's scale, s_1 its leading 8 bits and s_2 the
+// next 8 (s_1 + s_2 is s to within 2^-16 relative).
 __host__ __device__ inline int64_t padded_n(int64_t n) { return (n + TILE_N - 1) / TILE_N * TILE_N; }
 constexpr int MX_REC = 1024;            // bytes per (tile, block) record
 constexpr int MX_CODE_BYTES = 768;      // fp6 codes of 32 rows / columns
@@ -94,11 +98,35 @@ __host__ __device__ inline void put_mx_row(uint8_t *rec, int r, const uint32_t w
     for (int p = 0; p < 3; p++) reinterpret_cast<uint2 *>(rec + 256 * p)[r] = make_uint2(w[2 * p], w[2 * p + 1]);
 }
 
-// 32x32x8 bf16 MFMA: 4 bf16 per lane, lane groups l/32 hold K 0..3 and 4..7.
-__device__ __forceinline__ v16f mfma_bf16_32x32x8(uint2 a, uint2 b) {
-    v16f zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(v4s, a), __builtin_bit_cast(v4s, b),
-                                                   zero, 0, 0, 0);
+// Scale products of two blocks at once: the 32x32x4 bf16 MFMA in its
+// two-block form.  Lane l supplies 4 bf16 K values of row (A) or column (B)
+// l % 32 of block l / 32; the result holds block 0's 32x32 tile in elements
+// 0..15 and block 1's in 16..31, each in the usual 32x32 output layout.
+typedef float v32f __attribute__((ext_vector_type(32)));
+__device__ __forceinline__ v32f mfma_bf16_32x32x4_2blk(uint2 a, uint2 b) {
+    v32f zero = {};
+    return __builtin_amdgcn_mfma_f32_32x32x4bf16_1k(__builtin_bit_cast(v4s, a), __builtin_bit_cast(v4s, b), zero, 0,
+                                                   0, 0);
+}
+
+// Scale operands of the two-block scale-product MFMA (K slots k = 0..3 of a
+// lane pair up as A_k * B_k).
+// Activation row: (s_1, s_1, s_2, s_2), s_1 the leading 8 bits of s
+// (truncation), s_2 the leading 8 bits of the exact remainder s - s_1.
+__device__ __forceinline__ uint2 act_scale_operand(float s) {
+    const uint32_t h1 = __float_as_uint(s) & 0xFFFF0000u;
+    const float r1 = __fsub_rn(s, __uint_as_float(h1));
+    const uint32_t h2 = __float_as_uint(r1) & 0xFFFF0000u;
+    return make_uint2(h1 | (h1 >> 16), h2 | (h2 >> 16));
+}
+// Weight column: (d_0, d_1) with d_0 + d_1 = x exactly for x = 64 * d (d an
+// fp16 value: 11 significant bits, the leading 8 in d_0, the rest in d_1);
+// the MFMA reads it twice, as (d_0, d_1, d_0, d_1).
+__device__ __forceinline__ uint32_t weight_scale_operand(float x) {
+    const uint32_t h1 = __float_as_uint(x) & 0xFFFF0000u;
+    const float r1 = __fsub_rn(x, __uint_as_float(h1));  // exact: at most 3 significant bits remain
+    const uint32_t h2 = __float_as_uint(r1) & 0xFFFF0000u;
+    return (h1 >> 16) | h2;
 }
 
 // A K8 word (8 signed nibbles, see the streaming section) as 8 int8 MFMA

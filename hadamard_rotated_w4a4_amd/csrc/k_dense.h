@@ -19,13 +19,14 @@
 //
 // Per 32x32 tile and block the exact epilogue is one fp32 multiply-add per
 // output, y += (s[m] * d_w[n]) * S.  The scale product P = s (x) d_w is an
-// outer product formed by a bf16 MFMA over exact splits of the scales
-// (s = s1 + s2 + s3 on the K slots of each lane group, 64 d_w = d_0 + d_1
-// with lane group g holding d_g in all its slots; all six partial products
-// are exact in fp32).  So a tile and block cost two MFMAs and 16 vector multiply-adds per
-// lane; on gfx950 vector and matrix instructions of one SIMD overlap only
-// partly, and this kernel keeps every other vector instruction out of the
-// loop: operands arrive in the MFMA's register layout (weights repacked
+// outer product, formed on the matrix cores too: the 32x32x4 bf16 MFMA in its
+// two-block form gives P for both blocks of a stage in one instruction
+// (lane K slots (s_1, s_1, s_2, s_2) against (d_0, d_1, d_0, d_1), with
+// 64 d_w = d_0 + d_1 exact and s_1 + s_2 equal to s within 2^-16 relative;
+// the four partial products are exact in fp32).  So a tile and a stage of two
+// blocks cost two FP6 MFMAs, one scale-product MFMA and 32 vector
+// multiply-adds per lane, and every other vector instruction is kept out of
+// the loop: operands arrive in the MFMAs' register layouts (weights repacked
 // offline, activations by a pre-pass), by direct global-to-LDS loads.
 //
 // Workgroup: 4 waves (2 x 2), each owning TM x TN tiles of 32x32 (a 128 x 128
@@ -72,8 +73,8 @@ __device__ __forceinline__ v16f mfma_block(v8i a, v8i b, int sel) {
 // Activation pre-pass: int4 codes [m][k/2] + fp32 scales [m][k/32] -> operand
 // records [ceil(m/32)][nbp][1 KB] (same shape as the weight records):
 //   [0, 768)    fp6 E2M3 codes of row r, laid out as for the weights;
-//   [768, 1024) per row the bf16 split {s1, s2, s3, 0} of the scale, read by
-//               both lane groups of the scale-product MFMA.
+//   [768, 1024) per row the bf16 quadruple (s1, s1, s2, s2) of the scale,
+//               the scale-product MFMA's A operand.
 // One thread per (row, padded block); padding rows and blocks are zero.
 // ---------------------------------------------------------------------------
 // Row r (of 32) of record `rec`: block b of activation row `src` (codes and
@@ -97,14 +98,7 @@ __device__ __forceinline__ void write_act_record(const uint8_t *__restrict__ cod
             f[j + 16] = fp6_e2m3_of(((int)(byte << 24)) >> 28);  // code j + 16: high nibble
         }
         pack_fp6x32(f, w);
-        // exact bf16 split s = s1 + s2 + s3 (truncations; each remainder is exact)
-        const float s = scales[row * nb + b];
-        const uint32_t h1 = __float_as_uint(s) & 0xFFFF0000u;
-        const float r1 = __fsub_rn(s, __uint_as_float(h1));
-        const uint32_t h2 = __float_as_uint(r1) & 0xFFFF0000u;
-        const float r2 = __fsub_rn(r1, __uint_as_float(h2));
-        const uint32_t h3 = __float_as_uint(r2) & 0xFFFF0000u;
-        sop = make_uint2((h1 >> 16) | h2, h3 >> 16);
+        sop = act_scale_operand(scales[row * nb + b]);
     }
     put_mx_row(rec, r, w);
     reinterpret_cast<uint2 *>(rec + MX_CODE_BYTES)[r] = sop;
@@ -250,99 +244,108 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
     // ---- one software pipeline over all blocks ----
     // A stage is two blocks; one operand register set per row / column tile
     // carries both (lanes 0..31 block 0, lanes 32..63 block 1).  Step t of a
-    // stage = (block t / PER, tile t % PER); the two MFMAs of step t + 1 are
-    // issued around the halves of step t's multiply-adds.  At step BAR of
-    // stage s the wait + barrier publish stage s + 1 and the slot of stage
-    // s - 1 (read during stage s - 2) is refilled; stage s + 1's operands are
-    // then read into the other register set one tile per step, in the order
-    // of first use, so that no burst of LDS reads stalls the wave and every
-    // read has several steps to land.  The pipeline never drains at a stage
-    // boundary.
+    // stage is tile (t / TN, t % TN): its 32 multiply-adds consume the three
+    // MFMAs (the scale products of both blocks and the two block dots) issued
+    // during the step before, while the three MFMAs of tile t + 1 are issued
+    // among them, so every MFMA has a whole step to finish.  The tiles' operand
+    // registers are single: right after the MFMAs of a step have taken an
+    // operand for the last time in this stage, the operand of the next stage
+    // is read into its registers (at the latest one step before its first
+    // use).  At step BAR of stage s the wait + barrier publish stage s + 1 and
+    // the slot of stage s - 1 (read during stage s - 1) is refilled.  The
+    // pipeline never drains at a stage boundary.
     static_assert(BKB == 2, "one operand register set carries a stage's two blocks");
     static_assert(NS >= 3, "one stage in flight besides the two in use");
-    constexpr int STEPS = BKB * TM * TN, PER = TM * TN;
-    constexpr int BAR = STEPS - (TM + TN) < 2 ? STEPS - (TM + TN) : 2;  // step of the barrier
-    static_assert(BAR >= 0, "a stage's steps cover its operand reads");
-    static_assert(BAR + C::DMA_PER_WAVE <= STEPS, "a stage's steps cover its loads");
-    v8i af[2][TM], bf[2][TN];
-    uint2 ap[2][BKB][TM];
-    uint32_t bw[2][BKB][TN];
-    const int sel[BKB] = {g ? 0 : 127, g ? 127 : 0};  // E8M0 lane masks of blocks 0 and 1
+    constexpr int STEPS = TM * TN;
+    static_assert(STEPS % 2 == 0, "the result buffers alternate by step parity");
+    constexpr int PARTS = TM + TN;  // parts 0 .. TM - 1: row tiles, then the column tiles
+    constexpr int BAR = 0;          // step of the barrier
+    constexpr int SPAN = STEPS - BAR;  // steps that carry a stage's loads
+    v8i af[TM], bf[TN];
+    uint2 ap[TM];     // (s1, s1, s2, s2) of row c of block g
+    uint32_t bw[TN];  // (d0, d1) of column c of block g
+    const int sel0 = g ? 0 : 127, sel1 = g ? 127 : 0;  // E8M0 lane masks of blocks 0 and 1
     const uint32_t id_sel = opaque_identity_selector();
-    // Operand reads of one row tile (i) or column tile (j) of a stage.
-    auto load_a = [&](const uint8_t *st, int buf, int i) {
-        const uint8_t *rec = st + (wm * TM + i) * BKB * MX_REC, *p = rec + g * MX_REC + 8 * c;
-        af[buf][i] = fp6_operand(lds_read<u32x2>(p), lds_read<u32x2>(p + 256), lds_read<u32x2>(p + 512));
-#pragma unroll
-        for (int bb = 0; bb < BKB; bb++) {
-            const u32x2 sp = lds_read<u32x2>(rec + bb * MX_REC + MX_CODE_BYTES + 8 * c);
-            ap[buf][bb][i] = make_uint2(sp.x, sp.y);
-        }
+    // Operand reads of one row tile (i) or column tile (j) of a stage; lane
+    // group g reads block g's record.
+    auto load_a = [&](const uint8_t *st, int i) {
+        const uint8_t *rec = st + ((wm * TM + i) * BKB + g) * MX_REC, *p = rec + 8 * c;
+        af[i] = fp6_operand(lds_read<u32x2>(p), lds_read<u32x2>(p + 256), lds_read<u32x2>(p + 512));
+        const u32x2 sp = lds_read<u32x2>(rec + MX_CODE_BYTES + 8 * c);
+        ap[i] = make_uint2(sp.x, sp.y);
     };
-    auto load_b = [&](const uint8_t *st, int buf, int j) {
-        const uint8_t *rec = st + (RT + wn * TN + j) * BKB * MX_REC, *p = rec + g * MX_REC + 8 * c;
-        bf[buf][j] = fp6_operand(lds_read<u32x2>(p), lds_read<u32x2>(p + 256), lds_read<u32x2>(p + 512));
-#pragma unroll
-        for (int bb = 0; bb < BKB; bb++) bw[buf][bb][j] = lds_read<uint32_t>(rec + bb * MX_REC + MX_CODE_BYTES + 4 * lane);
+    auto load_b = [&](const uint8_t *st, int j) {
+        const uint8_t *rec = st + ((RT + wn * TN + j) * BKB + g) * MX_REC, *p = rec + 8 * c;
+        bf[j] = fp6_operand(lds_read<u32x2>(p), lds_read<u32x2>(p + 256), lds_read<u32x2>(p + 512));
+        bw[j] = lds_read<uint32_t>(rec + MX_CODE_BYTES + 4 * c);
     };
-    // Part p of a stage's operands, in the order the stage's steps first use
-    // them (steps run j fastest): A 0, B 0, the other B tiles, the other A tiles.
-    constexpr int PARTS = TM + TN;
-    auto load_part = [&](const uint8_t *st, int buf, int p) {
-        if (p == 0) load_a(st, buf, 0);
-        else if (p <= TN) load_b(st, buf, p - 1);
-        else load_a(st, buf, p - TN);
+    auto load_part = [&](const uint8_t *st, int p) {
+        if (p < TM) load_a(st, p);
+        else load_b(st, p - TM);
     };
-    auto mfma_s = [&](int buf, int bb, int i, int j) { return mfma_block(af[buf][i], bf[buf][j], sel[bb]); };
-    auto mfma_p = [&](int buf, int bb, int i, int j) {
-        // lane group g: K slots {s1, s2, s3, 0} against {d_g, d_g, d_g, d_g}
-        return mfma_bf16_32x32x8(ap[buf][bb][i], dup_at_use(bw[buf][bb][j], id_sel));
+    // The step during which a stage issues its last MFMA on part p (the MFMAs
+    // of tile t are issued at step t - 1; tile 0's at the previous stage's
+    // last step, here -1): the part is reread for the next stage right after.
+    auto last_issue = [](int p) {
+        int last = -1;
+        for (int t = 0; t < STEPS; t++)
+            if ((p < TM && t / TN == p) || (p >= TM && t % TN == p - TM)) last = t - 1;
+        return last < 0 ? 0 : last;
     };
+    auto mfma_p = [&](int i, int j) { return mfma_bf16_32x32x4_2blk(ap[i], dup_at_use(bw[j], id_sel)); };
 
 #pragma unroll
     for (int x = 0; x < NS - 1; x++) issue(x, x);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 2)) : "memory");
     __syncthreads();
-    v16f S[2], P[2];
+    v16f S0[2], S1[2];
+    v32f P[2];
 #pragma unroll
-    for (int p = 0; p < PARTS; p++) load_part(smem, 0, p);
-    S[0] = mfma_s(0, 0, 0, 0);
-    P[0] = mfma_p(0, 0, 0, 0);
+    for (int p = 0; p < PARTS; p++) load_part(smem, p);
+    P[0] = mfma_p(0, 0);
+    S0[0] = mfma_block(af[0], bf[0], sel0);
+    S1[0] = mfma_block(af[0], bf[0], sel1);
 
-    // stages in pairs, so that the operand register set of each is fixed at
-    // compile time (the stage count is a multiple of MX_BLOCK_PAD / BKB)
-    static_assert((MX_BLOCK_PAD / BKB) % 2 == 0, "even stage count");
-    for (int s0 = 0; s0 < nstages; s0 += 2) {
+    for (int s = 0; s < nstages; s++) {
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-            const int s = s0 + u;
-#pragma unroll
-            for (int t = 0; t < STEPS; t++) {
-                const int i = (t / TN) % TM, j = t % TN;
-                if (t == BAR) {
-                    // stage s + 1 has landed for this wave; after the barrier
-                    // for every wave, and stage s - 1's slot is free.  (After
-                    // the last stage the reads below see a reloaded stage; the
-                    // MFMAs they feed are never consumed.)
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 3)) : "memory");
-                    __syncthreads();
-                }
-                // refill stage s - 1's slot, one load per step (a burst of them
-                // stalls the issue while every wave of the CU does the same)
-                if (t >= BAR && t - BAR < C::DMA_PER_WAVE) issue_one(s + NS - 1, (s + NS - 1) % NS, t - BAR);
-                if (t >= BAR && t - BAR < PARTS) load_part(smem + ((s + 1) % NS) * C::STAGE_BYTES, u ^ 1, t - BAR);
-                const int t1 = (t + 1) % STEPS, buf1 = t1 == 0 ? u ^ 1 : u;
-                const int b1 = t1 / PER, i1 = (t1 / TN) % TM, j1 = t1 % TN;
-                S[(t + 1) & 1] = mfma_s(buf1, b1, i1, j1);
-#pragma unroll
-                for (int v = 0; v < 8; v++) acc[i][j][v] = fmaf(S[t & 1][v], P[t & 1][v], acc[i][j][v]);
-                __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);  // scalar and global-to-LDS ops may move; LDS reads stay in their step
-                P[(t + 1) & 1] = mfma_p(buf1, b1, i1, j1);
-#pragma unroll
-                for (int v = 8; v < 16; v++) acc[i][j][v] = fmaf(S[t & 1][v], P[t & 1][v], acc[i][j][v]);
-                asm volatile("" : "+v"(acc[i][j]));  // materialised here, not sunk past the loop's end
-                __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);  // scalar and global-to-LDS ops may move; LDS reads stay in their step
+        for (int t = 0; t < STEPS; t++) {
+            const int i = t / TN, j = t % TN, b = t & 1, b1 = b ^ 1;
+            if (t == BAR) {
+                // stage s + 1 has landed for this wave; after the barrier for
+                // every wave, and stage s - 1's slot is free.  (After the last
+                // stage the reads below see a reloaded stage; the MFMAs they
+                // feed are never consumed.)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 3)) : "memory");
+                __syncthreads();
             }
+            if (t >= BAR) {  // refill stage s - 1's slot, spread over the steps
+                const int q = t - BAR;
+#pragma unroll
+                for (int d = q * C::DMA_PER_WAVE / SPAN; d < (q + 1) * C::DMA_PER_WAVE / SPAN; d++)
+                    issue_one(s + NS - 1, (s + NS - 1) % NS, d);
+            }
+            // the MFMAs of tile t + 1 (of stage s + 1 after the last step) ...
+            const int t1 = (t + 1) % STEPS, i1 = t1 / TN, j1 = t1 % TN;
+            P[b1] = mfma_p(i1, j1);
+#pragma unroll
+            for (int v = 0; v < 11; v++) acc[i][j][v] = fmaf(S0[b][v], P[b][v], acc[i][j][v]);
+            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);  // scalar and global-to-LDS ops may move
+            S0[b1] = mfma_block(af[i1], bf[j1], sel0);
+#pragma unroll
+            for (int v = 11; v < 16; v++) acc[i][j][v] = fmaf(S0[b][v], P[b][v], acc[i][j][v]);
+#pragma unroll
+            for (int v = 0; v < 6; v++) acc[i][j][v] = fmaf(S1[b][v], P[b][16 + v], acc[i][j][v]);
+            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);
+            S1[b1] = mfma_block(af[i1], bf[j1], sel1);
+            // ... then the operands they were the last to take, for stage s + 1
+#pragma unroll
+            for (int p = 0; p < PARTS; p++)
+                if (last_issue(p) == t) load_part(smem + ((s + 1) % NS) * C::STAGE_BYTES, p);
+            // ... while the multiply-adds of tile t finish
+#pragma unroll
+            for (int v = 6; v < 16; v++) acc[i][j][v] = fmaf(S1[b][v], P[b][16 + v], acc[i][j][v]);
+            asm volatile("" : "+v"(acc[i][j]));  // materialised here, not sunk past the loop's end
+            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still be writing LDS at exit
@@ -418,58 +421,58 @@ __device__ __forceinline__ void mx_piece(const MxArgs &a, int64_t first_tile, in
             dma16s(brec + (kb0 + bb) * MX_REC, voff, lds + (BKB + bb) * MX_REC);
         }
     };
-    const int sel[BKB] = {g ? 0 : 127, g ? 127 : 0};  // E8M0 lane masks of blocks 0 and 1
+    const int sel0 = g ? 0 : 127, sel1 = g ? 127 : 0;  // E8M0 lane masks of blocks 0 and 1
     const uint32_t id_sel = opaque_identity_selector();
     static_assert(BKB == 2, "one operand register set carries a stage's two blocks");
 
     v16f acc;
 #pragma unroll
     for (int v = 0; v < 16; v++) acc[v] = 0.0f;
-    // The operands of a stage (both blocks) are read at once; the two MFMAs
-    // of the next block are issued before the multiply-adds of the current
-    // one (one tile per wave leaves nothing else to cover their latency).
+    // One operand set per stage (both blocks; lane group g reads block g's
+    // records).  The three MFMAs of stage s + 1 are issued around the 32
+    // multiply-adds of stage s, each once the multiply-adds have read the
+    // result it replaces (one tile per wave leaves nothing else to cover
+    // their latency).
     v8i af, bf;
-    uint2 ap[BKB];
-    uint32_t bw[BKB];
+    uint2 ap;
+    uint32_t bw;
     auto load = [&](const uint8_t *st) {
-        const uint8_t *pa = st + g * MX_REC + 8 * c, *pb = st + (BKB + g) * MX_REC + 8 * c;
-        af = fp6_operand(lds_read<u32x2>(pa), lds_read<u32x2>(pa + 256), lds_read<u32x2>(pa + 512));
-        bf = fp6_operand(lds_read<u32x2>(pb), lds_read<u32x2>(pb + 256), lds_read<u32x2>(pb + 512));
-#pragma unroll
-        for (int bb = 0; bb < BKB; bb++) {
-            const u32x2 sp = lds_read<u32x2>(st + bb * MX_REC + MX_CODE_BYTES + 8 * c);
-            ap[bb] = make_uint2(sp.x, sp.y);
-            bw[bb] = lds_read<uint32_t>(st + (BKB + bb) * MX_REC + MX_CODE_BYTES + 4 * lane);
-        }
-    };
-    auto mfmas = [&](int bb, v16f &S, v16f &P) {
-        S = mfma_block(af, bf, sel[bb]);
-        P = mfma_bf16_32x32x8(ap[bb], dup_at_use(bw[bb], id_sel));
+        const uint8_t *pa = st + g * MX_REC, *pb = st + (BKB + g) * MX_REC;
+        af = fp6_operand(lds_read<u32x2>(pa + 8 * c), lds_read<u32x2>(pa + 256 + 8 * c),
+                         lds_read<u32x2>(pa + 512 + 8 * c));
+        bf = fp6_operand(lds_read<u32x2>(pb + 8 * c), lds_read<u32x2>(pb + 256 + 8 * c),
+                         lds_read<u32x2>(pb + 512 + 8 * c));
+        const u32x2 sp = lds_read<u32x2>(pa + MX_CODE_BYTES + 8 * c);
+        ap = make_uint2(sp.x, sp.y);
+        bw = lds_read<uint32_t>(pb + MX_CODE_BYTES + 4 * c);
     };
     if (nst > 0) {
 #pragma unroll
         for (int x = 0; x < NS - 1; x++) issue(x, x);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * BKB * (NS - 2)) : "memory");  // stage 0 has landed
-        v16f S[2], P[2];
+        v16f S0, S1;
+        v32f P;
         load(ring);
-        mfmas(0, S[0], P[0]);
+        P = mfma_bf16_32x32x4_2blk(ap, dup_at_use(bw, id_sel));
+        S0 = mfma_block(af, bf, sel0);
+        S1 = mfma_block(af, bf, sel1);
         for (int s = 0; s < nst; s++) {
-            // block 1 of stage s
-            mfmas(1, S[1], P[1]);
-#pragma unroll
-            for (int v = 0; v < 16; v++) acc[v] = fmaf(S[0][v], P[0][v], acc[v]);
-            asm volatile("" : "+v"(acc));
-            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
-            // next stage: refill the slot computed last, wait for stage s + 1
-            // and read its operands (after the last stage this reads a
-            // reloaded stage; unused)
+            // refill the slot computed last, wait for stage s + 1 and read its
+            // operands (after the last stage this reads a reloaded stage;
+            // unused)
             issue(s + NS - 1, (s + NS - 1) % NS);
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * BKB * (NS - 2)) : "memory");
             load(ring + ((s + 1) % NS) * BKB * 2 * MX_REC);
-            mfmas(0, S[0], P[0]);
 #pragma unroll
-            for (int v = 0; v < 16; v++) acc[v] = fmaf(S[1][v], P[1][v], acc[v]);
+            for (int v = 0; v < 16; v++) acc[v] = fmaf(S0[v], P[v], acc[v]);
+            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
+            S0 = mfma_block(af, bf, sel0);
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[v] = fmaf(S1[v], P[16 + v], acc[v]);
             asm volatile("" : "+v"(acc));
+            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
+            P = mfma_bf16_32x32x4_2blk(ap, dup_at_use(bw, id_sel));
+            S1 = mfma_block(af, bf, sel1);
             __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still be writing the ring

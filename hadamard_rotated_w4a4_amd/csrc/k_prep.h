@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void repack_mx_kernel(const uint8_t *__restric
     const int64_t tile = tb / nbp, b = tb % nbp;
     const int64_t col = tile * TILE_N + c;
     uint32_t w[6] = {0, 0, 0, 0, 0, 0};
-    uint32_t sw0 = 0, sw1 = 0;
+    uint32_t sw = 0;
     if (col < n && b < nb) {
         const uint8_t *blk = q4 + (col * nb + b) * 18;
         uint32_t f[32];
@@ -90,17 +90,12 @@ __global__ __launch_bounds__(256) void repack_mx_kernel(const uint8_t *__restric
         }
         pack_fp6x32(f, w);
         // 64 * d: the MFMA reads codes as q / 8
-        const float d = __half2float(__ushort_as_half((uint16_t)(blk[0] | (blk[1] << 8)))) * 64.0f;
-        const uint32_t h1 = __float_as_uint(d) & 0xFFFF0000u;
-        const float r1 = __fsub_rn(d, __uint_as_float(h1));  // exact: at most 3 significant bits remain
-        const uint32_t h2 = __float_as_uint(r1) & 0xFFFF0000u;
-        sw0 = h1 | (h1 >> 16);
-        sw1 = h2 | (h2 >> 16);
+        sw = weight_scale_operand(__half2float(__ushort_as_half((uint16_t)(blk[0] | (blk[1] << 8)))) * 64.0f);
     }
     uint8_t *rec = packed + tb * MX_REC;
     put_mx_row(rec, c, w);
-    reinterpret_cast<uint32_t *>(rec + MX_CODE_BYTES)[c] = sw0;
-    reinterpret_cast<uint32_t *>(rec + MX_CODE_BYTES)[32 + c] = sw1;
+    reinterpret_cast<uint32_t *>(rec + MX_CODE_BYTES)[c] = sw;
+    reinterpret_cast<uint32_t *>(rec + MX_CODE_BYTES)[32 + c] = 0;  // unused tail of the record
 }
 
 // Streaming records (see common.h), one thread per (tile, padded block,

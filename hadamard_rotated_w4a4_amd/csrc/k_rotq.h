@@ -208,13 +208,7 @@ __global__ __launch_bounds__(128 * RQ_BLOCKS) void rotate_quantize_kernel(const 
             const uint64_t plane = L == 0 ? (mine | next << 48) : L == 1 ? (mine >> 16 | next << 32) : (mine >> 32 | next << 16);
             reinterpret_cast<uint2 *>(rec + 256 * L)[r] = make_uint2((uint32_t)plane, (uint32_t)(plane >> 32));
         } else {
-            // exact bf16 split s = s1 + s2 + s3 (truncations; each remainder is exact)
-            const uint32_t h1 = __float_as_uint(s) & 0xFFFF0000u;
-            const float r1 = __fsub_rn(s, __uint_as_float(h1));
-            const uint32_t h2 = __float_as_uint(r1) & 0xFFFF0000u;
-            const float r2 = __fsub_rn(r1, __uint_as_float(h2));
-            const uint32_t h3 = __float_as_uint(r2) & 0xFFFF0000u;
-            reinterpret_cast<uint2 *>(rec + MX_CODE_BYTES)[r] = make_uint2((h1 >> 16) | h2, h3 >> 16);
+            reinterpret_cast<uint2 *>(rec + MX_CODE_BYTES)[r] = act_scale_operand(s);
         }
     }
 }
