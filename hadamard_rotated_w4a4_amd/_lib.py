@@ -92,6 +92,58 @@ def _require_cuda(*ts):
 
 
 # --------------------------------------------------------------------------
+# argument checks: the kernels trust the sizes they are given, so every
+# buffer is checked against the library's own size rules before a call
+# --------------------------------------------------------------------------
+
+def _span_bytes(t: torch.Tensor) -> int:
+    """Bytes from t's first element to the end of its last one."""
+    if t.numel() == 0:
+        return 0
+    return (sum((size - 1) * stride for size, stride in zip(t.shape, t.stride())) + 1) * t.element_size()
+
+
+def _need(t, name: str, dtype=None, nbytes: int = 0, dense: bool = True):
+    """t exists, has the dtype, is contiguous (when the kernel reads it as a
+    flat buffer) and spans at least nbytes."""
+    if t is None:
+        raise W4A4Error(f"{name} is required")
+    if dtype is not None and t.dtype != dtype:
+        raise W4A4Error(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if dense and not t.is_contiguous():
+        raise W4A4Error(f"{name} must be contiguous")
+    if _span_bytes(t) < nbytes:
+        raise W4A4Error(f"{name}: {_span_bytes(t)} bytes, at least {nbytes} needed")
+
+
+def _need_rows(t, name: str, dtype, rows: int, cols: int):
+    """t is a 2-D matrix of at least rows x cols with unit column stride and
+    a row stride of at least cols (the kernels take the row stride)."""
+    if t is None:
+        raise W4A4Error(f"{name} is required")
+    if dtype is not None and t.dtype != dtype:
+        raise W4A4Error(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.dim() != 2 or t.shape[0] < rows or t.shape[1] < cols:
+        raise W4A4Error(f"{name}: shape {tuple(t.shape)}, expected at least ({rows}, {cols})")
+    if rows > 1 and cols > 0 and (t.stride(1) != 1 or t.stride(0) < cols):
+        raise W4A4Error(f"{name}: strides {t.stride()}, expected unit column stride and row stride >= {cols}")
+
+
+def _act_dtype(x) -> int:
+    dt = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16}.get(x.dtype)
+    if dt is None:
+        raise W4A4Error(f"unsupported activation dtype {x.dtype}")
+    return dt
+
+
+def _k_of(x, k):
+    k = x.shape[1] if k is None else k
+    if k < 0 or k % 32:
+        raise W4A4Error(f"k = {k} is not a multiple of 32")
+    return k
+
+
+# --------------------------------------------------------------------------
 # sizes
 # --------------------------------------------------------------------------
 
@@ -121,9 +173,13 @@ def gemm_id_workspace_bytes(n_expert: int, n_tokens: int, top_k: int) -> int:
 
 def quantize_q4_0_h32(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """fp32 [n, k] (row stride w.stride(0)) -> rotated Q4_0 bytes uint8 [n, k/32, 18]."""
-    _require_cuda(w, out)
-    assert w.dtype == torch.float32 and w.dim() == 2 and w.stride(1) == 1
+    if w is None or w.dim() != 2:
+        raise W4A4Error("w must be a 2-D fp32 matrix")
     n, k = w.shape
+    _need_rows(w, "w", torch.float32, n, k)
+    if out is not None:
+        _need(out, "out", torch.uint8, q4_0_bytes(n, k))
+    _require_cuda(w, out)
     if out is None:
         out = torch.empty((n, k // 32, 18), dtype=torch.uint8, device=w.device)
     _check(lib().w4a4_quantize_q4_0_h32(_ptr(w), n, k, w.stride(0), _ptr(out), _stream(w.device)),
@@ -133,6 +189,9 @@ def quantize_q4_0_h32(w: torch.Tensor, out: torch.Tensor | None = None) -> torch
 
 def repack_q4_0_h32(q4: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None) -> torch.Tensor:
     """Rotated Q4_0 bytes -> packed weight buffer (uint8, private layout)."""
+    _need(q4, "q4", torch.uint8, q4_0_bytes(n, k))
+    if out is not None:
+        _need(out, "out", torch.uint8, packed_weight_bytes(n, k))
     _require_cuda(q4, out)
     if out is None:
         out = torch.empty(packed_weight_bytes(n, k), dtype=torch.uint8, device=q4.device)
@@ -141,20 +200,26 @@ def repack_q4_0_h32(q4: torch.Tensor, n: int, k: int, out: torch.Tensor | None =
     return out
 
 
+def _quantiser_outputs(x, k, codes, scales, code_bytes_per_row, code_dtype):
+    m = x.shape[0]
+    _need_rows(x, "x", None, m, k)
+    if codes is not None:
+        _need(codes, "codes", code_dtype, m * code_bytes_per_row)
+    if scales is not None:
+        _need(scales, "scales", torch.float32, m * (k // 32) * 4)
+    _require_cuda(x, codes, scales)
+    if codes is None:
+        codes = torch.empty((m, code_bytes_per_row), dtype=code_dtype, device=x.device)
+    if scales is None:
+        scales = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    return m, codes, scales
+
+
 def rotate_quantize_act(x: torch.Tensor, k: int | None = None, codes: torch.Tensor | None = None,
                         scales: torch.Tensor | None = None):
     """x fp16/fp32 [m, >=k] (row stride x.stride(0)) -> (codes uint8 [m, k/2], scales fp32 [m, k/32])."""
-    _require_cuda(x, codes, scales)
-    assert x.dim() == 2 and x.stride(1) == 1
-    dt = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16}.get(x.dtype)
-    if dt is None:
-        raise W4A4Error(f"unsupported activation dtype {x.dtype}")
-    m = x.shape[0]
-    k = x.shape[1] if k is None else k
-    if codes is None:
-        codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    dt, k = _act_dtype(x), _k_of(x, k)
+    m, codes, scales = _quantiser_outputs(x, k, codes, scales, k // 2, torch.uint8)
     _check(lib().w4a4_rotate_quantize_act(_ptr(x), dt, m, k, x.stride(0), _ptr(codes), _ptr(scales),
                                           _stream(x.device)), "w4a4_rotate_quantize_act")
     return codes, scales
@@ -163,34 +228,46 @@ def rotate_quantize_act(x: torch.Tensor, k: int | None = None, codes: torch.Tens
 def rotate_quantize_prepare(x: torch.Tensor, act: torch.Tensor, k: int | None = None,
                             codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
     """rotate_quantize_act that also writes the matrix-core operand into `act`."""
-    _require_cuda(x, act, codes, scales)
-    assert x.dim() == 2 and x.stride(1) == 1
-    dt = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16}.get(x.dtype)
-    if dt is None:
-        raise W4A4Error(f"unsupported activation dtype {x.dtype}")
-    m = x.shape[0]
-    k = x.shape[1] if k is None else k
-    if codes is None:
-        codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    dt, k = _act_dtype(x), _k_of(x, k)
+    _need(act, "act", torch.uint8, act_operand_bytes(x.shape[0], k))
+    m, codes, scales = _quantiser_outputs(x, k, codes, scales, k // 2, torch.uint8)
+    _require_cuda(act)
     _check(lib().w4a4_rotate_quantize_prepare(_ptr(x), dt, m, k, x.stride(0), _ptr(codes), _ptr(scales), _ptr(act),
                                               act.numel(), _stream(x.device)), "w4a4_rotate_quantize_prepare")
     return codes, scales
+
+
+def _check_out(y, ws, m, n, need):
+    if y is not None:
+        _need_rows(y, "y", torch.float32, m, n)
+    if ws is not None:
+        _need(ws, "workspace", torch.uint8, need)
+
+
+def _output(y, m, n, device):
+    return torch.empty((m, n), dtype=torch.float32, device=device) if y is None else y
+
+
+def _workspace(ws, need, device):
+    if ws is not None:
+        _need(ws, "workspace", torch.uint8, need)
+        return ws
+    return torch.empty(need, dtype=torch.uint8, device=device) if need else None
 
 
 def gemm(packed: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: int, k: int,
          y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """W4A4 product: fp32 [m, n] (row stride y.stride(0)).  The workspace is
     allocated here unless given (uint8, at least gemm_workspace_bytes)."""
-    _require_cuda(packed, codes, scales, y, workspace)
     m = codes.shape[0]
-    if y is None:
-        y = torch.empty((m, n), dtype=torch.float32, device=codes.device)
-    assert y.stride(1) == 1
+    _need(packed, "packed", torch.uint8, packed_weight_bytes(n, k))
+    _need(codes, "codes", torch.uint8, m * (k // 2))
+    _need(scales, "scales", torch.float32, m * (k // 32) * 4)
     need = gemm_workspace_bytes(m, n, k)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=codes.device)
+    _check_out(y, workspace, m, n, need)
+    _require_cuda(packed, codes, scales, y, workspace)
+    y = _output(y, m, n, codes.device)
+    workspace = _workspace(workspace, need, codes.device)
     _check(lib().w4a4_gemm(_ptr(packed), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, y.stride(0),
                            _ptr(workspace), 0 if workspace is None else workspace.numel(),
                            _stream(codes.device)), "w4a4_gemm")
@@ -200,8 +277,12 @@ def gemm(packed: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: int
 def prepare_act(codes: torch.Tensor, scales: torch.Tensor, k: int,
                 out: torch.Tensor | None = None) -> torch.Tensor:
     """Activation codes + scales -> prepared matrix-core operand (uint8, private layout)."""
-    _require_cuda(codes, scales, out)
     m = codes.shape[0]
+    _need(codes, "codes", torch.uint8, m * (k // 2))
+    _need(scales, "scales", torch.float32, m * (k // 32) * 4)
+    if out is not None:
+        _need(out, "out", torch.uint8, act_operand_bytes(m, k))
+    _require_cuda(codes, scales, out)
     if out is None:
         out = torch.empty(max(1, act_operand_bytes(m, k)), dtype=torch.uint8, device=codes.device)
     _check(lib().w4a4_gemm_prepare_act(_ptr(codes), _ptr(scales), m, k, _ptr(out), out.numel(),
@@ -217,16 +298,31 @@ def gemm_prepared(packed: torch.Tensor, act: torch.Tensor, m: int, n: int, k: in
                   y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """W4A4 product on a prepared activation: fp32 [m, n] (row stride y.stride(0)).
     The split-K workspace is allocated here when one is needed and not given."""
-    _require_cuda(packed, act, y, workspace)
-    if y is None:
-        y = torch.empty((m, n), dtype=torch.float32, device=act.device)
-    assert y.stride(1) == 1
+    _need(packed, "packed", torch.uint8, packed_weight_bytes(n, k))
+    _need(act, "act", torch.uint8, act_operand_bytes(m, k))
     need = gemm_prepared_workspace_bytes(m, n, k)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=act.device)
+    _check_out(y, workspace, m, n, need)
+    _require_cuda(packed, act, y, workspace)
+    y = _output(y, m, n, act.device)
+    workspace = _workspace(workspace, need, act.device)
     _check(lib().w4a4_gemm_prepared(_ptr(packed), _ptr(act), _ptr(y), m, n, k, y.stride(0), _ptr(workspace),
                                     0 if workspace is None else workspace.numel(), _stream(act.device)),
            "w4a4_gemm_prepared")
+    return y
+
+
+def _gemm_id_args(packed, n_expert, codes, scales, act_rows_per_token, n_tokens, top_k, n, k, y, code_bytes):
+    if act_rows_per_token not in (1, top_k):
+        raise W4A4Error(f"act_rows_per_token = {act_rows_per_token}, expected 1 or top_k = {top_k}")
+    rows = n_tokens * act_rows_per_token
+    _need(packed, "packed", torch.uint8, n_expert * packed_weight_bytes(n, k))
+    _need(codes, "codes", None, rows * code_bytes)
+    _need(scales, "scales", torch.float32, rows * (k // 32) * 4)
+    if y is not None:
+        _need(y, "y", torch.float32, n_tokens * top_k * n * 4)
+    _require_cuda(packed, codes, scales, y)
+    if y is None:
+        y = torch.empty((n_tokens, top_k, n), dtype=torch.float32, device=codes.device)
     return y
 
 
@@ -234,28 +330,30 @@ def gemm_id(packed: torch.Tensor, n_expert: int, codes: torch.Tensor, scales: to
             act_rows_per_token: int, ids: torch.Tensor, n: int, k: int, y: torch.Tensor | None = None,
             workspace: torch.Tensor | None = None) -> torch.Tensor:
     """MUL_MAT_ID: fp32 [n_tokens, top_k, n]."""
-    _require_cuda(packed, codes, scales, ids, y, workspace)
-    assert ids.dtype == torch.int32 and ids.dim() == 2
+    if ids is None or ids.dim() != 2:
+        raise W4A4Error("ids must be an int32 [n_tokens, top_k] matrix")
+    _need(ids, "ids", torch.int32)
     n_tokens, top_k = ids.shape
-    if y is None:
-        y = torch.empty((n_tokens, top_k, n), dtype=torch.float32, device=ids.device)
+    _need(codes, "codes", torch.uint8)
+    y = _gemm_id_args(packed, n_expert, codes, scales, act_rows_per_token, n_tokens, top_k, n, k, y, k // 2)
     need = gemm_id_workspace_bytes(n_expert, n_tokens, top_k)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ids.device)
+    workspace = _workspace(workspace, need, ids.device) if need else _workspace(workspace, 1, ids.device)
+    _require_cuda(ids, workspace)
     _check(lib().w4a4_gemm_id(_ptr(packed), n_expert, _ptr(codes), _ptr(scales), act_rows_per_token,
-                              _ptr(ids.contiguous()), n_tokens, top_k, _ptr(y), n, k, _ptr(workspace),
+                              _ptr(ids), n_tokens, top_k, _ptr(y), n, k, _ptr(workspace),
                               workspace.numel(), _stream(ids.device)), "w4a4_gemm_id")
     return y
 
 
 def gemm_id_route(ids: torch.Tensor, n_expert: int, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """MUL_MAT_ID routing of ids [n_tokens, top_k] into a workspace (returned)."""
-    _require_cuda(ids, workspace)
-    assert ids.dtype == torch.int32 and ids.dim() == 2 and ids.is_contiguous()
+    if ids is None or ids.dim() != 2:
+        raise W4A4Error("ids must be an int32 [n_tokens, top_k] matrix")
+    _need(ids, "ids", torch.int32)
     n_tokens, top_k = ids.shape
-    if workspace is None:
-        workspace = torch.empty(max(1, gemm_id_workspace_bytes(n_expert, n_tokens, top_k)), dtype=torch.uint8,
-                                device=ids.device)
+    need = max(1, gemm_id_workspace_bytes(n_expert, n_tokens, top_k))
+    workspace = _workspace(workspace, need, ids.device)
+    _require_cuda(ids, workspace)
     _check(lib().w4a4_gemm_id_route(_ptr(ids), n_expert, n_tokens, top_k, _ptr(workspace), workspace.numel(),
                                     _stream(ids.device)), "w4a4_gemm_id_route")
     return workspace
@@ -265,9 +363,10 @@ def gemm_id_routed(packed: torch.Tensor, n_expert: int, codes: torch.Tensor, sca
                    act_rows_per_token: int, n_tokens: int, top_k: int, n: int, k: int, workspace: torch.Tensor,
                    y: torch.Tensor | None = None) -> torch.Tensor:
     """MUL_MAT_ID on a routing from gemm_id_route: fp32 [n_tokens, top_k, n]."""
-    _require_cuda(packed, codes, scales, workspace, y)
-    if y is None:
-        y = torch.empty((n_tokens, top_k, n), dtype=torch.float32, device=codes.device)
+    _need(codes, "codes", torch.uint8)
+    _need(workspace, "workspace", torch.uint8, gemm_id_workspace_bytes(n_expert, n_tokens, top_k))
+    y = _gemm_id_args(packed, n_expert, codes, scales, act_rows_per_token, n_tokens, top_k, n, k, y, k // 2)
+    _require_cuda(workspace)
     _check(lib().w4a4_gemm_id_routed(_ptr(packed), n_expert, _ptr(codes), _ptr(scales), act_rows_per_token,
                                      n_tokens, top_k, _ptr(y), n, k, _ptr(workspace), workspace.numel(),
                                      _stream(codes.device)), "w4a4_gemm_id_routed")
@@ -277,17 +376,8 @@ def gemm_id_routed(packed: torch.Tensor, n_expert: int, codes: torch.Tensor, sca
 def rotate_quantize_act8(x: torch.Tensor, k: int | None = None, codes: torch.Tensor | None = None,
                          scales: torch.Tensor | None = None):
     """W4A8-H32 activations: x fp16/fp32 [m, >=k] -> (codes int8 [m, k], scales fp32 [m, k/32])."""
-    _require_cuda(x, codes, scales)
-    assert x.dim() == 2 and x.stride(1) == 1
-    dt = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16}.get(x.dtype)
-    if dt is None:
-        raise W4A4Error(f"unsupported activation dtype {x.dtype}")
-    m = x.shape[0]
-    k = x.shape[1] if k is None else k
-    if codes is None:
-        codes = torch.empty((m, k), dtype=torch.int8, device=x.device)
-    if scales is None:
-        scales = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    dt, k = _act_dtype(x), _k_of(x, k)
+    m, codes, scales = _quantiser_outputs(x, k, codes, scales, k, torch.int8)
     _check(lib().w4a4_rotate_quantize_act8(_ptr(x), dt, m, k, x.stride(0), _ptr(codes), _ptr(scales),
                                            _stream(x.device)), "w4a4_rotate_quantize_act8")
     return codes, scales
@@ -296,14 +386,15 @@ def rotate_quantize_act8(x: torch.Tensor, k: int | None = None, codes: torch.Ten
 def gemm_a8(packed: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: int, k: int,
             y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """W4A8-H32 product: fp32 [m, n] (row stride y.stride(0))."""
-    _require_cuda(packed, codes, scales, y, workspace)
     m = codes.shape[0]
-    if y is None:
-        y = torch.empty((m, n), dtype=torch.float32, device=codes.device)
-    assert y.stride(1) == 1
+    _need(packed, "packed", torch.uint8, packed_weight_bytes(n, k))
+    _need(codes, "codes", torch.int8, m * k)
+    _need(scales, "scales", torch.float32, m * (k // 32) * 4)
     need = int(lib().w4a4_gemm_a8_workspace_bytes(m, n, k))
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=codes.device)
+    _check_out(y, workspace, m, n, need)
+    _require_cuda(packed, codes, scales, y, workspace)
+    y = _output(y, m, n, codes.device)
+    workspace = _workspace(workspace, need, codes.device)
     _check(lib().w4a4_gemm_a8(_ptr(packed), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, y.stride(0),
                               _ptr(workspace), 0 if workspace is None else workspace.numel(),
                               _stream(codes.device)), "w4a4_gemm_a8")
@@ -322,9 +413,13 @@ def prepare_weights(w: torch.Tensor) -> torch.Tensor:
 
 def quantize_q4_0(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """fp32 [n, k] (row stride w.stride(0)) -> plain (unrotated) Q4_0 bytes uint8 [n, k/32, 18]."""
-    _require_cuda(w, out)
-    assert w.dtype == torch.float32 and w.dim() == 2 and w.stride(1) == 1
+    if w is None or w.dim() != 2:
+        raise W4A4Error("w must be a 2-D fp32 matrix")
     n, k = w.shape
+    _need_rows(w, "w", torch.float32, n, k)
+    if out is not None:
+        _need(out, "out", torch.uint8, q4_0_bytes(n, k))
+    _require_cuda(w, out)
     if out is None:
         out = torch.empty((n, k // 32, 18), dtype=torch.uint8, device=w.device)
     _check(lib().w4a4_quantize_q4_0(_ptr(w), n, k, w.stride(0), _ptr(out), _stream(w.device)), "w4a4_quantize_q4_0")
@@ -334,17 +429,8 @@ def quantize_q4_0(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Ten
 def quantize_act(x: torch.Tensor, k: int | None = None, codes: torch.Tensor | None = None,
                  scales: torch.Tensor | None = None):
     """x fp16/fp32 [m, >=k] -> unrotated int4 (codes uint8 [m, k/2], scales fp32 [m, k/32])."""
-    _require_cuda(x, codes, scales)
-    assert x.dim() == 2 and x.stride(1) == 1
-    dt = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16}.get(x.dtype)
-    if dt is None:
-        raise W4A4Error(f"unsupported activation dtype {x.dtype}")
-    m = x.shape[0]
-    k = x.shape[1] if k is None else k
-    if codes is None:
-        codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    dt, k = _act_dtype(x), _k_of(x, k)
+    m, codes, scales = _quantiser_outputs(x, k, codes, scales, k // 2, torch.uint8)
     _check(lib().w4a4_quantize_act(_ptr(x), dt, m, k, x.stride(0), _ptr(codes), _ptr(scales), _stream(x.device)),
            "w4a4_quantize_act")
     return codes, scales
@@ -374,8 +460,11 @@ def w16_to_rows(buf: torch.Tensor, rows: int, k: int) -> torch.Tensor:
 
 def dequantize_w16(q4: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None) -> torch.Tensor:
     """Q4_0 bytes -> tiled fp16 weights (flat, w4a4_w16_weight_bytes(n, k) bytes)."""
-    _require_cuda(q4, out)
     need = int(lib().w4a4_w16_weight_bytes(n, k))
+    _need(q4, "q4", torch.uint8, q4_0_bytes(n, k))
+    if out is not None:
+        _need(out, "out", torch.float16, need)
+    _require_cuda(q4, out)
     if out is None:
         out = torch.empty(need // 2, dtype=torch.float16, device=q4.device)
     _check(lib().w4a4_dequantize_w16(_ptr(q4), n, k, _ptr(out), out.numel() * out.element_size(),
@@ -385,15 +474,15 @@ def dequantize_w16(q4: torch.Tensor, n: int, k: int, out: torch.Tensor | None = 
 
 def rotate_act16(x: torch.Tensor, k: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
     """x fp16/fp32 [m, >=k] -> tiled rotated fp16 activations (flat, w4a4_w16_act_bytes(m, k) bytes)."""
-    _require_cuda(x, out)
-    assert x.dim() == 2 and x.stride(1) == 1
-    dt = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16}.get(x.dtype)
-    if dt is None:
-        raise W4A4Error(f"unsupported activation dtype {x.dtype}")
+    dt, k = _act_dtype(x), _k_of(x, k)
     m = x.shape[0]
-    k = x.shape[1] if k is None else k
+    _need_rows(x, "x", None, m, k)
+    need = int(lib().w4a4_w16_act_bytes(m, k))
+    if out is not None:
+        _need(out, "out", torch.float16, need)
+    _require_cuda(x, out)
     if out is None:
-        out = torch.empty(int(lib().w4a4_w16_act_bytes(m, k)) // 2, dtype=torch.float16, device=x.device)
+        out = torch.empty(need // 2, dtype=torch.float16, device=x.device)
     _check(lib().w4a4_rotate_act16(_ptr(x), dt, m, k, x.stride(0), _ptr(out), out.numel() * out.element_size(),
                                    _stream(x.device)), "w4a4_rotate_act16")
     return out
@@ -402,10 +491,11 @@ def rotate_act16(x: torch.Tensor, k: int | None = None, out: torch.Tensor | None
 def gemm_w16(w16: torch.Tensor, a16: torch.Tensor, m: int, n: int, k: int,
              y: torch.Tensor | None = None) -> torch.Tensor:
     """W4A16 product of the two tiled fp16 operands: fp32 [m, n] (row stride y.stride(0))."""
+    _need(w16, "w16", torch.float16, int(lib().w4a4_w16_weight_bytes(n, k)))
+    _need(a16, "a16", torch.float16, int(lib().w4a4_w16_act_bytes(m, k)))
+    _check_out(y, None, m, n, 0)
     _require_cuda(w16, a16, y)
-    if y is None:
-        y = torch.empty((m, n), dtype=torch.float32, device=a16.device)
-    assert y.stride(1) == 1
+    y = _output(y, m, n, a16.device)
     _check(lib().w4a4_gemm_w16(_ptr(w16), _ptr(a16), _ptr(y), m, n, k, y.stride(0), _stream(a16.device)),
            "w4a4_gemm_w16")
     return y

@@ -1,11 +1,13 @@
 // Activation rotation + int4 quantisation, one pass over the activations.
 //
 // 1bit-MONSTER engine docs, "The lean option: ROCmFP4, ROCmI4 and Hadamard
-// Q4_0", section "Hadamard-rotated Q4_0: W4A4 prompt processing": only the
-// activations are rounded to 4 bits, and a 32-point Walsh-Hadamard rotation
-// spreads a block's few large values before rounding so they no longer force a
-// coarse scale on the rest.  The same per-block rotation was applied to the
-// weights offline, so the product is unchanged in exact arithmetic.
+// Q4_0", section "Hadamard-rotated Q4_0: W4A4 prompt processing".  The
+// weights are 4-bit already; at run time it is the activations that get
+// rounded to 4 bits.  Each 32-element block first goes through the 32-point
+// Walsh-Hadamard transform that was applied to the weights offline: every
+// output mixes all 32 inputs, so one large input no longer decides the
+// block's scale on its own, and since the transform is orthogonal, dot
+// products of rotated rows equal those of the original rows.
 //
 // Mapping: four lanes per (row, 32-element block), lane L holding elements
 // 8L .. 8L + 7: butterfly stages 1, 2 and 4 run inside the lane, stages 8 and

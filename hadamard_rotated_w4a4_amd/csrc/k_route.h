@@ -113,8 +113,9 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t *__r
 
 // Fill rows of y with zeros (used when k == 0: an empty sum).
 __global__ void zero_rows_kernel(float *y, int64_t m, int64_t n, int64_t ldy) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < m * n) y[(i / n) * ldy + i % n] = 0.0f;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < m * n; i += stride)
+        y[(i / n) * ldy + i % n] = 0.0f;
 }
 
 }  // namespace w4a4

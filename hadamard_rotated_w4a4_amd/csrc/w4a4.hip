@@ -35,6 +35,10 @@ w4a4_status hip_status(const char *what) {
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 inline unsigned blocks_for(int64_t work, int per) { return (unsigned)((work + per - 1) / per); }
+// y[0..m)[0..n) = 0 (row stride ldy): a grid-stride kernel on at most 2^16 workgroups
+inline void launch_zero_rows(float *y, int64_t m, int64_t n, int64_t ldy, hipStream_t s) {
+    zero_rows_kernel<<<(unsigned)std::min<int64_t>((m * n + 255) / 256, 1 << 16), 256, 0, s>>>(y, m, n, ldy);
+}
 
 // Dense m > 16: stages of 2 blocks, a ring of 4 stages; workgroup tiles of
 // 128 x 128, 128 x 64 or 64 x 128, chosen per problem (see launch_mx).
@@ -147,9 +151,21 @@ void launch_mx(const MxArgs &a0, float *partial, hipStream_t s) {
     else launch_mx_cfg<Mx64x128>(a, p2, s);
 }
 
-// Row bounds that keep every grid.y within the hardware's 65535.
+// Size bounds, so that every launch fits the hardware's grid limits and the
+// kernels' 32-bit offsets: rows (m, or routed rows) within 65535 row tiles of
+// 32 (the quantisers' grid.y); K and N well past any model's.  A 1-D launch
+// must stay below 2^32 threads in all.
 constexpr int64_t kMaxGridY = 65535;
-constexpr int64_t kMaxRows = kMaxGridY * 128;  // also bounds the 1-D dense grid (< 2^31 workgroups)
+constexpr int64_t kMaxRows = kMaxGridY * 32;
+constexpr int64_t kMaxK = int64_t{1} << 24;
+constexpr int64_t kMaxN = int64_t{1} << 26;
+constexpr int64_t kMaxThreads = (int64_t{1} << 32) - 1;
+inline bool grid_fits(int64_t threads) { return threads <= kMaxThreads; }
+// m rows, n columns, k: inside the bounds above (sizes already known >= 0)
+inline bool within_bounds(int64_t m, int64_t n, int64_t k) { return m <= kMaxRows && n <= kMaxN && k <= kMaxK; }
+// 128 x 128 output tiles of a dense product: each is at most one 256-thread
+// workgroup, plus at most 16 pieces per leftover tile of one round
+constexpr int64_t kMaxDenseTiles = int64_t{1} << 20;
 
 w4a4_status check_gemm_common(const void *packed_w, const uint8_t *codes, const float *scales,
                               const float *y, int64_t n, int64_t k) {
@@ -192,10 +208,11 @@ size_t w4a4_packed_weight_bytes(int64_t n, int64_t k) {
 
 namespace {
 w4a4_status quantize_q4_0(bool rotate, const float *w, int64_t n, int64_t k, int64_t ldw, void *q4_0, void *stream) {
-    if (n < 0 || k < 0 || ldw < k) return W4A4_ERR_INVALID_VALUE;
+    if (n < 0 || k < 0 || ldw < k || !within_bounds(0, n, k)) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
     if (n == 0 || k == 0) return W4A4_OK;
     if (!w || !q4_0) return W4A4_ERR_INVALID_VALUE;
+    if (!grid_fits(n * (k / QK))) return W4A4_ERR_INVALID_VALUE;
     if (!aligned(w, 4)) return W4A4_ERR_MISALIGNED;
     const int64_t blocks = n * (k / QK);
     uint8_t *q = static_cast<uint8_t *>(q4_0);
@@ -215,12 +232,14 @@ w4a4_status w4a4_quantize_q4_0(const float *w, int64_t n, int64_t k, int64_t ldw
 }
 
 w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int64_t k, void *stream) {
-    if (n < 0 || k < 0) return W4A4_ERR_INVALID_VALUE;
+    if (n < 0 || k < 0 || !within_bounds(0, n, k)) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
     if (n == 0 || k == 0) return W4A4_OK;
     if (!q4_0 || !packed) return W4A4_ERR_INVALID_VALUE;
     if (!aligned(packed, 16)) return W4A4_ERR_MISALIGNED;
     const int64_t mx_threads = padded_n(n) / TILE_N * mx_blocks(k) * 32;
+    if (!grid_fits(mx_threads) || !grid_fits(padded_n(n) / TILE_N * sq_quads(k) * SQ_BLOCKS * 32))
+        return W4A4_ERR_INVALID_VALUE;
     repack_mx_kernel<<<blocks_for(mx_threads, 256), 256, 0, as_stream(stream)>>>(
         static_cast<const uint8_t *>(q4_0), n, k, static_cast<uint8_t *>(packed));
     const w4a4_status st2 = hip_status("repack_mx_kernel");
@@ -238,7 +257,7 @@ w4a4_status rotate_quantize(bool a8, const void *x, w4a4_dtype dt, int64_t m, in
                             uint8_t *codes, float *scales, void *act, size_t act_bytes, void *stream,
                             bool rotate = true) {
     if (dt != W4A4_DTYPE_F32 && dt != W4A4_DTYPE_F16) return W4A4_ERR_UNSUPPORTED_DTYPE;
-    if (m < 0 || k < 0 || ldx < k || m > kMaxRows) return W4A4_ERR_INVALID_VALUE;
+    if (m < 0 || k < 0 || ldx < k || !within_bounds(m, 0, k)) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
     if (m == 0 || k == 0) return W4A4_OK;
     if (!x || !codes || !scales) return W4A4_ERR_INVALID_VALUE;
@@ -310,16 +329,17 @@ size_t w4a4_gemm_prepared_workspace_bytes(int64_t m, int64_t n, int64_t k) {
 w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *scales, float *y,
                       int64_t m, int64_t n, int64_t k, int64_t ldy, void *workspace, size_t workspace_bytes,
                       void *stream) {
-    if (m < 0 || m > kMaxRows || ldy < n) return W4A4_ERR_INVALID_VALUE;
+    if (m < 0 || ldy < n) return W4A4_ERR_INVALID_VALUE;
     if (m == 0 || n == 0) {
         if (n < 0 || k < 0) return W4A4_ERR_INVALID_VALUE;
         return k % QK ? W4A4_ERR_K_NOT_MULTIPLE_OF_32 : W4A4_OK;
     }
+    if (n < 0 || k < 0 || !within_bounds(m, n, k)) return W4A4_ERR_INVALID_VALUE;
     const w4a4_status st = check_gemm_common(packed_w, codes, scales, y, n, k);
     if (st != W4A4_OK) return st;
     hipStream_t s = as_stream(stream);
     if (k == 0) {  // empty sum
-        zero_rows_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(y, m, n, ldy);
+        launch_zero_rows(y, m, n, ldy, s);
         return hip_status("zero_rows_kernel");
     }
     if (m <= SMALL_M_MAX) {
@@ -369,17 +389,18 @@ size_t w4a4_gemm_a8_workspace_bytes(int64_t m, int64_t n, int64_t k) {
 w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float *scales, float *y, int64_t m,
                          int64_t n, int64_t k, int64_t ldy, void *workspace, size_t workspace_bytes,
                          void *stream) {
-    if (m < 0 || m > kMaxRows || ldy < n) return W4A4_ERR_INVALID_VALUE;
+    if (m < 0 || ldy < n) return W4A4_ERR_INVALID_VALUE;
     if (m == 0 || n == 0) {
         if (n < 0 || k < 0) return W4A4_ERR_INVALID_VALUE;
         return k % QK ? W4A4_ERR_K_NOT_MULTIPLE_OF_32 : W4A4_OK;
     }
+    if (n < 0 || k < 0 || !within_bounds(m, n, k)) return W4A4_ERR_INVALID_VALUE;
     const uint8_t *c8 = reinterpret_cast<const uint8_t *>(codes);
     const w4a4_status st = check_gemm_common(packed_w, c8, scales, y, n, k);
     if (st != W4A4_OK) return st;
     hipStream_t s = as_stream(stream);
     if (k == 0) {  // empty sum
-        zero_rows_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(y, m, n, ldy);
+        launch_zero_rows(y, m, n, ldy, s);
         return hip_status("zero_rows_kernel");
     }
     if (m <= SMALL_M_MAX) {
@@ -410,7 +431,7 @@ w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float 
     // m > 16: the streaming kernel, all rows as one group
     const int64_t col_chunks = (padded_n(n) / TILE_N + GS_WAVES - 1) / GS_WAVES;
     const int64_t items = (m + GS_ROWS - 1) / GS_ROWS * col_chunks;
-    if (items + 8 > INT32_MAX) return W4A4_ERR_INVALID_VALUE;
+    if (!grid_fits((items + 8) * 64 * GS_WAVES)) return W4A4_ERR_INVALID_VALUE;
     GsArgs a{};
     a.codes = c8;
     a.scales = scales;
@@ -434,10 +455,11 @@ size_t w4a4_act_operand_bytes(int64_t m, int64_t k) {
 
 w4a4_status w4a4_gemm_prepare_act(const uint8_t *codes, const float *scales, int64_t m, int64_t k,
                                   void *act, size_t act_bytes, void *stream) {
-    if (m < 0 || k < 0 || m > kMaxRows) return W4A4_ERR_INVALID_VALUE;
+    if (m < 0 || k < 0 || !within_bounds(m, 0, k)) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
     if (m == 0 || k == 0) return W4A4_OK;
     if (!codes || !scales || !act) return W4A4_ERR_INVALID_VALUE;
+    if (!grid_fits((m + 31) / 32 * 32 * mx_blocks(k))) return W4A4_ERR_INVALID_VALUE;
     if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(act, 256)) return W4A4_ERR_MISALIGNED;
     if (act_bytes < w4a4_act_operand_bytes(m, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
     const int64_t threads = (m + 31) / 32 * 32 * mx_blocks(k);
@@ -448,14 +470,15 @@ w4a4_status w4a4_gemm_prepare_act(const uint8_t *codes, const float *scales, int
 
 w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, int64_t m, int64_t n,
                                int64_t k, int64_t ldy, void *workspace, size_t workspace_bytes, void *stream) {
-    if (m < 0 || n < 0 || k < 0 || m > kMaxRows || ldy < n) return W4A4_ERR_INVALID_VALUE;
+    if (m < 0 || n < 0 || k < 0 || ldy < n || !within_bounds(m, n, k)) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
     if (m == 0 || n == 0) return W4A4_OK;
     if (!y) return W4A4_ERR_INVALID_VALUE;
     if (!aligned(y, 4)) return W4A4_ERR_MISALIGNED;
+    if ((m + 127) / 128 * ((n + 127) / 128) >= kMaxDenseTiles) return W4A4_ERR_INVALID_VALUE;
     hipStream_t s = as_stream(stream);
     if (k == 0) {  // empty sum
-        zero_rows_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(y, m, n, ldy);
+        launch_zero_rows(y, m, n, ldy, s);
         return hip_status("zero_rows_kernel");
     }
     if (!packed_w || !act) return W4A4_ERR_INVALID_VALUE;
@@ -490,10 +513,11 @@ size_t w4a4_w16_act_bytes(int64_t m, int64_t k) {
 
 w4a4_status w4a4_dequantize_w16(const void *q4_0, int64_t n, int64_t k, void *w16, size_t w16_bytes,
                                 void *stream) {
-    if (n < 0 || k < 0) return W4A4_ERR_INVALID_VALUE;
+    if (n < 0 || k < 0 || !within_bounds(0, n, k)) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
     if (n == 0 || k == 0) return W4A4_OK;
     if (!q4_0 || !w16) return W4A4_ERR_INVALID_VALUE;
+    if (!grid_fits(padded_n(n) * mx_blocks(k))) return W4A4_ERR_INVALID_VALUE;
     if (!aligned(w16, 16)) return W4A4_ERR_MISALIGNED;
     if (w16_bytes < w4a4_w16_weight_bytes(n, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
     const int64_t threads = padded_n(n) * mx_blocks(k);
@@ -505,7 +529,7 @@ w4a4_status w4a4_dequantize_w16(const void *q4_0, int64_t n, int64_t k, void *w1
 w4a4_status w4a4_rotate_act16(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx, void *a16,
                               size_t a16_bytes, void *stream) {
     if (dt != W4A4_DTYPE_F32 && dt != W4A4_DTYPE_F16) return W4A4_ERR_UNSUPPORTED_DTYPE;
-    if (m < 0 || k < 0 || ldx < k || m > kMaxRows) return W4A4_ERR_INVALID_VALUE;
+    if (m < 0 || k < 0 || ldx < k || !within_bounds(m, 0, k)) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
     if (m == 0 || k == 0) return W4A4_OK;
     if (!x || !a16) return W4A4_ERR_INVALID_VALUE;
@@ -525,14 +549,14 @@ w4a4_status w4a4_rotate_act16(const void *x, w4a4_dtype dt, int64_t m, int64_t k
 
 w4a4_status w4a4_gemm_w16(const void *w16, const void *a16, float *y, int64_t m, int64_t n, int64_t k,
                           int64_t ldy, void *stream) {
-    if (m < 0 || n < 0 || k < 0 || m > kMaxRows || ldy < n) return W4A4_ERR_INVALID_VALUE;
+    if (m < 0 || n < 0 || k < 0 || ldy < n || !within_bounds(m, n, k)) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
     if (m == 0 || n == 0) return W4A4_OK;
     if (!y) return W4A4_ERR_INVALID_VALUE;
     if (!aligned(y, 4)) return W4A4_ERR_MISALIGNED;
     hipStream_t s = as_stream(stream);
     if (k == 0) {  // empty sum
-        zero_rows_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(y, m, n, ldy);
+        launch_zero_rows(y, m, n, ldy, s);
         return hip_status("zero_rows_kernel");
     }
     if (!w16 || !a16) return W4A4_ERR_INVALID_VALUE;
@@ -583,7 +607,7 @@ w4a4_status w4a4_gemm_id_route(const int32_t *ids, int64_t n_expert, int64_t n_t
     if (n_tokens == 0 || top_k == 0) return W4A4_OK;
     if (n_expert < 1 || n_expert > ROUTE_MAX_EXPERTS) return W4A4_ERR_INVALID_VALUE;
     const int64_t n_rows = n_tokens * top_k;
-    if (n_rows > INT32_MAX) return W4A4_ERR_INVALID_VALUE;
+    if (n_rows > kMaxRows) return W4A4_ERR_INVALID_VALUE;
     if (!ids || !workspace) return W4A4_ERR_INVALID_VALUE;
     if (!aligned(ids, 4) || !aligned(workspace, 256)) return W4A4_ERR_MISALIGNED;
     if (workspace_bytes < w4a4_gemm_id_workspace_bytes(n_expert, n_tokens, top_k))
@@ -608,7 +632,8 @@ w4a4_status w4a4_gemm_id_routed(const void *packed_w, int64_t n_expert, const ui
     const int64_t n_rows = n_tokens * top_k;
     const int64_t row_tiles = grouped_row_tiles(n_expert, n_rows, GS_ROWS);
     const int64_t col_chunks = (padded_n(n) / TILE_N + GS_WAVES - 1) / GS_WAVES;
-    if (n_rows > INT32_MAX || row_tiles * col_chunks + 8 > INT32_MAX) return W4A4_ERR_INVALID_VALUE;
+    if (!within_bounds(n_rows, n, k) || !grid_fits((row_tiles * col_chunks + 8) * 64 * GS_WAVES))
+        return W4A4_ERR_INVALID_VALUE;
     if (!workspace) return W4A4_ERR_INVALID_VALUE;
     if (k > 0) {
         const w4a4_status st = check_gemm_common(packed_w, codes, scales, y, n, k);
@@ -622,7 +647,7 @@ w4a4_status w4a4_gemm_id_routed(const void *packed_w, int64_t n_expert, const ui
 
     hipStream_t s = as_stream(stream);
     if (k == 0) {  // empty sums: every row is zero
-        zero_rows_kernel<<<blocks_for(n_rows * n, 256), 256, 0, s>>>(y, n_rows, n, n);
+        launch_zero_rows(y, n_rows, n, n, s);
         return hip_status("zero_rows_kernel");
     }
     const uint8_t *ws = static_cast<const uint8_t *>(workspace);
@@ -662,7 +687,8 @@ w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *
     const int64_t n_rows = n_tokens * top_k;
     const int64_t row_tiles = grouped_row_tiles(n_expert, n_rows, GS_ROWS);
     const int64_t col_chunks = (padded_n(n) / TILE_N + GS_WAVES - 1) / GS_WAVES;
-    if (n_rows > INT32_MAX || row_tiles * col_chunks + 8 > INT32_MAX) return W4A4_ERR_INVALID_VALUE;
+    if (!within_bounds(n_rows, n, k) || !grid_fits((row_tiles * col_chunks + 8) * 64 * GS_WAVES))
+        return W4A4_ERR_INVALID_VALUE;
     if (!workspace) return W4A4_ERR_INVALID_VALUE;
     if (k > 0) {
         const w4a4_status st = check_gemm_common(packed_w, codes, scales, y, n, k);

@@ -25,7 +25,14 @@
  *   - A failed launch returns W4A4_ERR_HIP (detail: w4a4_last_hip_error()).
  *     Faults during execution surface at the caller's next synchronisation.
  *   - No C++ exception crosses this interface.
- *   - K must be a multiple of 32 (one Q4_0 block).  Any m, n >= 1 works.
+ *   - K must be a multiple of 32 (one Q4_0 block).  Any m, n >= 1 works up
+ *     to these bounds (larger sizes return W4A4_ERR_INVALID_VALUE before any
+ *     launch): m, and the routed rows n_tokens * top_k, at most 65535 * 32 =
+ *     2097120 (row tiles of 32 within the 65535 grid rows of the row-tiled
+ *     kernels); n at most 2^26; k at most 2^24; and sizes whose one-dimensional
+ *     launch would reach 2^32 threads (for a dense product m > 16: 2^20 or
+ *     more output tiles of 128 x 128; for weight preparation: n * k / 32 of
+ *     2^32 or more) are refused.
  */
 #ifndef W4A4_H
 #define W4A4_H
@@ -43,7 +50,7 @@ typedef enum {
     W4A4_ERR_K_NOT_MULTIPLE_OF_32 = 2, /* k % 32 != 0 */
     W4A4_ERR_MISALIGNED = 3,           /* a pointer below its required alignment */
     W4A4_ERR_UNSUPPORTED_DTYPE = 4,    /* activation dtype not in w4a4_dtype */
-    W4A4_ERR_WORKSPACE_TOO_SMALL = 5,  /* workspace_bytes below w4a4_gemm_id_workspace_bytes() */
+    W4A4_ERR_WORKSPACE_TOO_SMALL = 5,  /* a buffer's byte count below what its size query names */
     W4A4_ERR_HIP = 6                   /* a HIP runtime call failed */
 } w4a4_status;
 
@@ -82,22 +89,27 @@ size_t w4a4_packed_weight_bytes(int64_t n, int64_t k);
  *   q4_0    [n][k/32] x 18 B, as above (any alignment).  The `_h32` in the
  *           name is the caller's assertion that the weights were rotated:
  *           unrotated weights give silently wrong products.
- *   packed  out, w4a4_packed_weight_bytes(n, k) bytes, 256-byte aligned.  Its
- *           layout is private to this library.  It holds the weights three
- *           times, losslessly, once per consumer: 4-bit codes stored as
- *           q ^ 8 (read as a signed nibble that is exactly q - 8, the page's
- *           identity) with the fp16 scales, in the tile order of the grouped
- *           expert kernel; the matrix-core operand of the m > 16 kernels
- *           (each q - 8 as an FP6 E2M3 code, the scale as an exact bf16
- *           pair), 8 bits per weight; and the same 4-bit codes and fp16
- *           scales in 2304-byte records of 32 columns x 4 blocks, streamed
- *           by the m <= 16 kernel.
+ *   packed  out, w4a4_packed_weight_bytes(n, k) bytes, 16-byte aligned.  Its
+ *           layout is private to this library.  It holds the weights twice,
+ *           losslessly, once per kind of reader: the matrix-core operand of
+ *           the m > 16 kernel (each q - 8 as an FP6 E2M3 code, 64 times the
+ *           scale as an exact pair of bf16 parts; 1 KB per 32 columns and
+ *           block), then the 4-bit codes stored as q ^ 8 (read as a signed
+ *           nibble that is exactly q - 8, the page's identity) with the fp16
+ *           scales, in 2304-byte records of 32 columns x 4 blocks, streamed
+ *           by the m <= 16 kernel and by the MUL_MAT_ID kernel.
+ * Errors: negative sizes or sizes past the bounds -> W4A4_ERR_INVALID_VALUE;
+ * k % 32 -> W4A4_ERR_K_NOT_MULTIPLE_OF_32; null pointers with work to do ->
+ * W4A4_ERR_INVALID_VALUE; packed below 16-byte alignment -> W4A4_ERR_MISALIGNED.
  */
 w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int64_t k,
                                  void *stream);
 
 /*
- * Rotate and quantise activations, one 32-element block at a time:
+ * Rotate and quantise activations, one 32-element block at a time (section
+ * "Hadamard-rotated Q4_0: W4A4 prompt processing": each activation row gets
+ * the weights' per-block rotation at run time and is then rounded to 4 bits;
+ * the page prints no rounding rule, this is the reading taken):
  * unnormalised fast Walsh-Hadamard butterflies in fp32 (stages 1, 2, 4, 8,
  * 16), amax = max |v|, d = amax / 7, codes = clamp(round-half-away(v *
  * (1/d)), -7, 7), stored scale s = d * fp32(1/sqrt(32)).  A block with d below
@@ -108,6 +120,10 @@ w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int6
  *           code of element 32b + j in its low nibble and of element
  *           32b + j + 16 in its high nibble, two's complement.
  *   scales  out, [m][k/32] fp32, 4-byte aligned.
+ * Errors: dt not a w4a4_dtype -> W4A4_ERR_UNSUPPORTED_DTYPE; negative sizes,
+ * ldx < k or sizes past the bounds -> W4A4_ERR_INVALID_VALUE; k % 32 ->
+ * W4A4_ERR_K_NOT_MULTIPLE_OF_32; null pointers with work to do ->
+ * W4A4_ERR_INVALID_VALUE; misalignment -> W4A4_ERR_MISALIGNED.
  */
 w4a4_status w4a4_rotate_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k,
                                      int64_t ldx, uint8_t *codes, float *scales, void *stream);
@@ -131,9 +147,13 @@ w4a4_status w4a4_rotate_quantize_prepare(const void *x, w4a4_dtype dt, int64_t m
                                          size_t act_bytes, void *stream);
 
 /*
- * Dense W4A4 product: y[i][j] = sum_b d_w[j][b] * s[i][b] * S[i][j][b], where
- * S = sum_t (q_w - 8) * q_a is the exact integer dot of block b, accumulated
- * in fp32 (block order ascending within a thread).
+ * Dense W4A4 product (section "Hadamard-rotated Q4_0: W4A4 prompt
+ * processing": the 4-bit weight and activation codes are multiplied in
+ * integer arithmetic and each block's dot is scaled into fp32):
+ * y[i][j] = sum_b d_w[j][b] * s[i][b] * S[i][j][b], where S = sum_t (q_w - 8)
+ * * q_a is the exact integer dot of block b, accumulated in fp32 (block order
+ * ascending within a thread; the scale product d_w * s is formed to within
+ * 2^-16 relative for m > 16, exactly for m <= 16).
  *   packed_w  from w4a4_repack_q4_0_h32(n, k), 16-byte aligned.
  *   codes, scales  from w4a4_rotate_quantize_act (m rows).
  *   y         out, [m][ldy] fp32, ldy >= n, 4-byte aligned.
@@ -160,7 +180,8 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
  *
  * w4a4_gemm_prepare_act: re-lays activation codes and scales from
  * w4a4_rotate_quantize_act into the matrix-core operand format (every code
- * as an FP6 E2M3 value, exactly q / 8; every scale as an exact bf16 triple).
+ * as an FP6 E2M3 value, exactly q / 8; every scale as two bf16 parts whose
+ * sum is the scale to within 2^-16 relative).
  *   act   out, w4a4_act_operand_bytes(m, k) bytes, 256-byte aligned; private
  *         layout.
  *
@@ -271,8 +292,8 @@ w4a4_status w4a4_quantize_act(const void *x, w4a4_dtype dt, int64_t m, int64_t k
  *
  * Errors (all three): negative sizes, ldx < k or ldy < n ->
  * W4A4_ERR_INVALID_VALUE; k % 32 -> W4A4_ERR_K_NOT_MULTIPLE_OF_32; null
- * pointers with work to do, m > 8388480, or 2^20 or more 128 x 128 output tiles ->
- * W4A4_ERR_INVALID_VALUE; misalignment ->
+ * pointers with work to do, or sizes past the bounds (2^20 or more 128 x 128
+ * output tiles for w4a4_gemm_w16) -> W4A4_ERR_INVALID_VALUE; misalignment ->
  * W4A4_ERR_MISALIGNED.  Empty sizes return W4A4_OK having done nothing.
  */
 size_t w4a4_w16_weight_bytes(int64_t n, int64_t k);

@@ -16,8 +16,9 @@
  *   - the weights are rotated once by a 32-point Walsh-Hadamard transform per
  *     32-element block along K, and the activations are rotated by the same
  *     transform at run time, so x.w = (Hx).(Hw) in exact arithmetic;
- *   - only the activations are rounded to 4 bits; the product of the 4-bit
- *     weight and activation codes is formed in integer arithmetic.
+ *   - at run time it is the activations that get rounded to 4 bits (the
+ *     weights are 4-bit already); the 4-bit weight codes and 4-bit
+ *     activation codes are multiplied as integers.
  * Section "MoE: W4A4 on the experts" of the same page: the expert matmuls
  * (MUL_MAT_ID) take the same path.
  *

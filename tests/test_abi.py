@@ -264,3 +264,34 @@ def test_gemm_id_validation(L):
     assert g(*gargs, P(A), ws - 1, None) == WS
     assert g(P(A), 4, P(A), P(A), 3, 8, 2, P(A), 64, 64, P(A), ws, None) == INVALID  # rows per token
     assert g(None, 4, None, None, 1, 0, 2, None, 64, 64, None, 0, None) == OK
+
+
+MAX_ROWS = 65535 * 32  # row tiles of 32 within the 65535 grid.y of the row-tiled kernels
+
+
+def test_size_bounds_are_refused_before_any_launch(L):
+    """Sizes whose launches would not fit the hardware's grid limits (or the
+    kernels' 32-bit offsets) are refused on the host; only refused sizes are
+    passed here, so nothing is ever launched on the fake pointers."""
+    rq = L.w4a4_rotate_quantize_act
+    assert rq(P(A), 1, MAX_ROWS + 1, 64, 64, P(A), P(A), None) == INVALID
+    assert rq(P(A), 1, 4, (1 << 24) + 32, (1 << 24) + 32, P(A), P(A), None) == INVALID
+    assert L.w4a4_rotate_quantize_act8(P(A), 1, MAX_ROWS + 1, 64, 64, P(A), P(A), None) == INVALID
+    assert L.w4a4_rotate_act16(P(A), 1, MAX_ROWS + 1, 64, 64, P(A), 1 << 40, None) == INVALID
+    assert L.w4a4_gemm_prepare_act(P(A), P(A), MAX_ROWS + 1, 64, P(A), 1 << 40, None) == INVALID
+    g = L.w4a4_gemm
+    assert g(P(A), P(A), P(A), P(A), MAX_ROWS + 1, 64, 64, 64, P(A), 1 << 40, None) == INVALID
+    assert g(P(A), P(A), P(A), P(A), 8, (1 << 26) + 32, 64, (1 << 26) + 32, P(A), 1 << 40, None) == INVALID
+    assert g(P(A), P(A), P(A), P(A), 8, 64, (1 << 24) + 32, 64, P(A), 1 << 40, None) == INVALID
+    # 2^20 output tiles of 128 x 128 (1024 x 1024): the dense grid would pass 2^32 threads with pieces
+    gp = L.w4a4_gemm_prepared
+    assert gp(P(A), P(A), P(A), 1024 * 128, 1024 * 128, 64, 1024 * 128, P(A), 1 << 40, None) == INVALID
+    assert gp(P(A), P(A), P(A), MAX_ROWS + 1, 64, 64, 64, P(A), 1 << 40, None) == INVALID
+    # weight preparation: n * k / 32 threads past 2^32
+    assert L.w4a4_repack_q4_0_h32(P(A), P(A), 1 << 26, 1 << 24, None) == INVALID
+    assert L.w4a4_quantize_q4_0_h32(P(A), 1 << 26, 1 << 24, 1 << 24, P(A), None) == INVALID
+    assert L.w4a4_dequantize_w16(P(A), 1 << 26, 1 << 24, P(A), 1 << 60, None) == INVALID
+    # routed rows: n_tokens * top_k past the row bound
+    gid = L.w4a4_gemm_id
+    assert gid(P(A), 8, P(A), P(A), 1, P(A), MAX_ROWS // 4 + 1, 4, P(A), 64, 64, P(A), 1 << 40, None) == INVALID
+    assert L.w4a4_gemm_id_route(P(A), 8, MAX_ROWS // 4 + 1, 4, P(A), 1 << 40, None) == INVALID
