@@ -260,7 +260,7 @@ def gemm(packed: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: int
     """W4A4 product: fp32 [m, n] (row stride y.stride(0)).  The workspace is
     allocated here unless given (uint8, at least gemm_workspace_bytes)."""
     m = codes.shape[0]
-    _need(packed, "packed", torch.uint8, packed_weight_bytes(n, k))
+    _need(packed, "packed", torch.uint8, packed_weight_bytes(n, k) if m and n else 0)
     _need(codes, "codes", torch.uint8, m * (k // 2))
     _need(scales, "scales", torch.float32, m * (k // 32) * 4)
     need = gemm_workspace_bytes(m, n, k)
@@ -298,7 +298,7 @@ def gemm_prepared(packed: torch.Tensor, act: torch.Tensor, m: int, n: int, k: in
                   y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """W4A4 product on a prepared activation: fp32 [m, n] (row stride y.stride(0)).
     The split-K workspace is allocated here when one is needed and not given."""
-    _need(packed, "packed", torch.uint8, packed_weight_bytes(n, k))
+    _need(packed, "packed", torch.uint8, packed_weight_bytes(n, k) if m and n else 0)
     _need(act, "act", torch.uint8, act_operand_bytes(m, k))
     need = gemm_prepared_workspace_bytes(m, n, k)
     _check_out(y, workspace, m, n, need)
@@ -387,7 +387,7 @@ def gemm_a8(packed: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: 
             y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """W4A8-H32 product: fp32 [m, n] (row stride y.stride(0))."""
     m = codes.shape[0]
-    _need(packed, "packed", torch.uint8, packed_weight_bytes(n, k))
+    _need(packed, "packed", torch.uint8, packed_weight_bytes(n, k) if m and n else 0)
     _need(codes, "codes", torch.int8, m * k)
     _need(scales, "scales", torch.float32, m * (k // 32) * 4)
     need = int(lib().w4a4_gemm_a8_workspace_bytes(m, n, k))
