@@ -47,6 +47,8 @@ def lib() -> ctypes.CDLL:
             "w4a4_gemm_prepared": ([P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_prepared_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_gemm": ([P, P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
+            "w4a4_gemm_noalloc_scratch_bytes": ([], SZ),
+            "w4a4_gemm_noalloc": ([P, P, P, P, I64, I64, I64, I64, P], ST),
             "w4a4_gemm_id_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_rotate_quantize_act8": ([P, ST, I64, I64, I64, P, P, P], ST),
             "w4a4_quantize_q4_0": ([P, I64, I64, I64, P, P], ST),
@@ -271,6 +273,22 @@ def gemm(packed: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: int
     _check(lib().w4a4_gemm(_ptr(packed), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, y.stride(0),
                            _ptr(workspace), 0 if workspace is None else workspace.numel(),
                            _stream(codes.device)), "w4a4_gemm")
+    return y
+
+
+def gemm_noalloc(packed: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: int, k: int,
+                 y: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A4 product with the library's own fixed scratch (no workspace
+    allocated anywhere; y is allocated here only when not given)."""
+    m = codes.shape[0]
+    _need(packed, "packed", torch.uint8, packed_weight_bytes(n, k) if m and n else 0)
+    _need(codes, "codes", torch.uint8, m * (k // 2))
+    _need(scales, "scales", torch.float32, m * (k // 32) * 4)
+    _check_out(y, None, m, n, 0)
+    _require_cuda(packed, codes, scales, y)
+    y = _output(y, m, n, codes.device)
+    _check(lib().w4a4_gemm_noalloc(_ptr(packed), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, y.stride(0),
+                                   _stream(codes.device)), "w4a4_gemm_noalloc")
     return y
 
 

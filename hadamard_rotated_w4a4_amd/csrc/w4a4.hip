@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 #include "k_dense.h"
@@ -377,6 +378,63 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
     const size_t act_bytes = (w4a4_act_operand_bytes(m, k) + 255) / 256 * 256;
     return w4a4_gemm_prepared(packed_w, workspace, y, m, n, k, ldy, static_cast<uint8_t *>(workspace) + act_bytes,
                               workspace_bytes - act_bytes, stream);
+}
+
+}  // extern "C"
+
+// Scratch of w4a4_gemm_noalloc: a device array of fixed size, one instance per
+// GPU (each holds its copy while the library is loaded).  Host code never
+// passes this name to a kernel or a copy: it stands for the array only in
+// device code, and its device address is looked up per device below.
+namespace {
+constexpr size_t kNoAllocScratchBytes = size_t{64} << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// The current device's copy of `scratch`: its address is looked up once per
+// device, on that device's first call, with that device current.
+w4a4_status current_scratch(void **out) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        std::snprintf(g_last_hip_error, sizeof g_last_hip_error, "hipGetDevice: %s",
+                      e != hipSuccess ? hipGetErrorString(e) : "device index out of range");
+        return W4A4_ERR_HIP;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) {
+        std::snprintf(g_last_hip_error, sizeof g_last_hip_error, "hipGetSymbolAddress(scratch): %s",
+                      hipGetErrorString(g_scratch_err[dev]));
+        return W4A4_ERR_HIP;
+    }
+    *out = g_scratch_ptr[dev];
+    return W4A4_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t w4a4_gemm_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+w4a4_status w4a4_gemm_noalloc(const void *packed_w, const uint8_t *codes, const float *scales, float *y,
+                              int64_t m, int64_t n, int64_t k, int64_t ldy, void *stream) {
+    // invalid sizes need no workspace: w4a4_gemm then reports them
+    const size_t need = w4a4_gemm_workspace_bytes(m, n, k);
+    if (need > kNoAllocScratchBytes) return W4A4_ERR_WORKSPACE_TOO_SMALL;
+    void *ws = nullptr;
+    if (need) {
+        const w4a4_status st = current_scratch(&ws);
+        if (st != W4A4_OK) return st;
+    }
+    return w4a4_gemm(packed_w, codes, scales, y, m, n, k, ldy, ws, need, stream);
 }
 
 size_t w4a4_gemm_a8_workspace_bytes(int64_t m, int64_t n, int64_t k) {

@@ -174,6 +174,28 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
                       size_t workspace_bytes, void *stream);
 
 /*
+ * w4a4_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same product and the same kernels, with the workspace taken from a
+ * fixed-size array that the library holds on each GPU it runs on (allocated
+ * when the library's code object is loaded, kept until the process ends;
+ * nothing is allocated or freed per call).
+ *   Arguments, results and errors as w4a4_gemm, without the workspace.
+ *   Sizes whose w4a4_gemm_workspace_bytes(m, n, k) exceeds
+ *   w4a4_gemm_noalloc_scratch_bytes() (64 MiB) return
+ *   W4A4_ERR_WORKSPACE_TOO_SMALL before any launch.
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents (no kernel needs it cleared: every byte read is written
+ *   first in the same call).  Calls that overlap on one GPU (several streams
+ *   or threads) race on it: serialise them.  The array's device address is
+ *   looked up on the first call on each device, with that device current;
+ *   a failed lookup returns W4A4_ERR_HIP.
+ */
+size_t w4a4_gemm_noalloc_scratch_bytes(void);
+w4a4_status w4a4_gemm_noalloc(const void *packed_w, const uint8_t *codes, const float *scales, float *y,
+                              int64_t m, int64_t n, int64_t k, int64_t ldy, void *stream);
+
+/*
  * The two steps of w4a4_gemm for m > 16, callable on their own (one prepared
  * activation can feed several products that read the same rows, e.g. the
  * query, key and value projections).

@@ -295,3 +295,16 @@ def test_size_bounds_are_refused_before_any_launch(L):
     gid = L.w4a4_gemm_id
     assert gid(P(A), 8, P(A), P(A), 1, P(A), MAX_ROWS // 4 + 1, 4, P(A), 64, 64, P(A), 1 << 40, None) == INVALID
     assert L.w4a4_gemm_id_route(P(A), 8, MAX_ROWS // 4 + 1, 4, P(A), 1 << 40, None) == INVALID
+
+
+def test_noalloc_refuses_sizes_past_its_scratch(L):
+    """The allocation-free GEMM refuses, before any device call, a product
+    whose workspace would not fit its fixed scratch."""
+    cap = L.w4a4_gemm_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    m, n, k = 16384, 32, 5120
+    assert L.w4a4_gemm_workspace_bytes(m, n, k) > cap
+    assert L.w4a4_gemm_noalloc(P(A), P(A), P(A), P(A), m, n, k, n, None) == WS
+    # invalid sizes are reported as w4a4_gemm reports them
+    assert L.w4a4_gemm_noalloc(P(A), P(A), P(A), P(A), 64, 64, 33, 64, None) == KMUL
+    assert L.w4a4_gemm_noalloc(None, None, None, None, 0, 64, 64, 64, None) == OK
