@@ -12,6 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libw4a4.so")
+CEILINGS_LIB = os.path.join(PKG, "libw4a4_ceilings.so")  # measured ceilings for the benchmark
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = [os.path.join(CSRC, "w4a4.hip")]
@@ -37,9 +38,16 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libw4a4.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *SOURCES]
+    """Compile the HIP sources into libw4a4.so and the ceiling probes into
+    libw4a4_ceilings.so (always recompiles)."""
+    _compile(LIB, SOURCES, verbose)
+    _compile(CEILINGS_LIB, [os.path.join(CSRC, "ceilings.hip")], verbose)
+    return LIB
+
+
+def _compile(lib: str, sources: list, verbose: bool) -> None:
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,8 +58,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":
