@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
             "w4a4_gemm_prepared_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_gemm": ([P, P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_noalloc_scratch_bytes": ([], SZ),
+            "w4a4_rotate_quantize_gemm_workspace_bytes": ([I64, I64, I64], SZ),
+            "w4a4_rotate_quantize_gemm": ([P, ST, I64, I64, I64, P, I64, P, I64, P, P, P, SZ, P], ST),
             "w4a4_gemm_noalloc": ([P, P, P, P, I64, I64, I64, I64, P], ST),
             "w4a4_gemm_id_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_rotate_quantize_act8": ([P, ST, I64, I64, I64, P, P, P], ST),
@@ -290,6 +292,39 @@ def gemm_noalloc(packed: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor
     _check(lib().w4a4_gemm_noalloc(_ptr(packed), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, y.stride(0),
                                    _stream(codes.device)), "w4a4_gemm_noalloc")
     return y
+
+
+def rotate_quantize_gemm_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(lib().w4a4_rotate_quantize_gemm_workspace_bytes(m, n, k))
+
+
+def fused_workspace(m: int, n: int, k: int, device) -> torch.Tensor:
+    """A zero-filled workspace for rotate_quantize_gemm (zero before its first
+    use; the calls keep it ready for the next)."""
+    return torch.zeros(max(256, rotate_quantize_gemm_workspace_bytes(m, n, k)), dtype=torch.uint8, device=device)
+
+
+def rotate_quantize_gemm(x: torch.Tensor, packed: torch.Tensor, n: int, k: int | None = None,
+                         y: torch.Tensor | None = None, codes: torch.Tensor | None = None,
+                         scales: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Rotate-quantise x fp16/fp32 [m, >=k] and multiply with the packed
+    weights in one call (one launch for m <= 16): returns (y fp32 [m, n],
+    codes, scales).  The workspace must come from fused_workspace (or be
+    zeroed likewise); a new one is made when none is given."""
+    dt, k = _act_dtype(x), _k_of(x, k)
+    m = x.shape[0]
+    _need(packed, "packed", torch.uint8, packed_weight_bytes(n, k) if m and n else 0)
+    need = rotate_quantize_gemm_workspace_bytes(m, n, k)
+    _check_out(y, workspace, m, n, need)
+    m, codes, scales = _quantiser_outputs(x, k, codes, scales, k // 2, torch.uint8)
+    _require_cuda(packed, y, workspace)
+    y = _output(y, m, n, x.device)
+    if workspace is None:
+        workspace = fused_workspace(m, n, k, x.device)
+    _check(lib().w4a4_rotate_quantize_gemm(_ptr(x), dt, m, k, x.stride(0), _ptr(packed), n, _ptr(y), y.stride(0),
+                                           _ptr(codes), _ptr(scales), _ptr(workspace), workspace.numel(),
+                                           _stream(x.device)), "w4a4_rotate_quantize_gemm")
+    return y, codes, scales
 
 
 def prepare_act(codes: torch.Tensor, scales: torch.Tensor, k: int,

@@ -116,6 +116,56 @@ __device__ __forceinline__ void fwht32_quad(float v[8], int L) {
     }
 }
 
+// One (row, block) of the quantiser, held by a quad of lanes (lane L of the
+// quad: elements 8L .. 8L + 7 at src): the butterflies (unless ROTATE is
+// false), the absmax, the scale s and this lane's 8 codes.  live: the row
+// and block exist (uniform per quad; a dead quad quantises zeros).  Every
+// lane of the quad must take part (the butterflies and the absmax exchange
+// values through quad permutes).
+template <typename T, int QMAX, bool ROTATE>
+__device__ __forceinline__ void quantise_quad(const T *src, int mode, bool live, int L, int q[8], float &s) {
+    float v[8];
+    if (live) {
+        load8(src, mode, v);
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; t++) v[t] = 0.0f;
+    }
+    if constexpr (ROTATE) fwht32_quad(v, L);
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; t++) amax = fmaxf(amax, fabsf(v[t]));
+    amax = fmaxf(amax, quad_f32<QP_XOR1>(amax));
+    amax = fmaxf(amax, quad_f32<QP_XOR2>(amax));
+
+    const float d = __fdiv_rn(amax, (float)QMAX);
+    const bool nonzero = d >= 1.17549435e-38f;  // FLT_MIN: zero and subnormal scales give a zero block
+    const float id = nonzero ? __fdiv_rn(1.0f, d) : 0.0f;
+    s = !nonzero ? 0.0f : ROTATE ? __fmul_rn(d, kInvSqrt32f) : d;
+#pragma unroll
+    for (int t = 0; t < 8; t++)
+        q[t] = nonzero ? (int)fminf((float)QMAX, fmaxf(-(float)QMAX, round_half_away(__fmul_rn(v[t], id)))) : 0;
+}
+
+// The public int4 codes of a block (byte j = code j | code j + 16 << 4) from
+// its quad: lane L < 2 writes bytes 8L .. 8L + 7 (its codes and those of lane
+// L + 2), lane 0 the scale.  Every lane of the quad must take part.
+__device__ __forceinline__ void store_codes4(const int q[8], float s, int L, bool live, uint8_t *blk_codes,
+                                             float *blk_scale) {
+    uint32_t nib0 = 0, nib1 = 0;  // this lane's 8 codes, one nibble each, in byte positions
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        nib0 |= (uint32_t)(q[i] & 0xF) << (8 * i);
+        nib1 |= (uint32_t)(q[4 + i] & 0xF) << (8 * i);
+    }
+    const uint32_t hi0 = quad_u32<QP_XOR2>(nib0), hi1 = quad_u32<QP_XOR2>(nib1);
+    if (live && L < 2) {
+        *reinterpret_cast<uint2 *>(blk_codes + 8 * L) = make_uint2(nib0 | hi0 << 4, nib1 | hi1 << 4);
+        if (L == 0) *blk_scale = s;
+    }
+}
+
 // One workgroup = 32 rows (row tile blockIdx.y) x 2 neighbouring blocks
 // (2 blockIdx.x and 2 blockIdx.x + 1), four lanes per (row, block): wave w
 // takes block w / 2 and rows 16 (w % 2) .. + 15, lane 4 i + L row i, elements
@@ -143,30 +193,9 @@ __global__ __launch_bounds__(128 * RQ_BLOCKS) void rotate_quantize_kernel(const 
     const int64_t b = (int64_t)blockIdx.x * RQ_BLOCKS + (wave >> 1), row = (int64_t)blockIdx.y * 32 + r;
     const bool live = row < m && b < nb;  // uniform per quad
 
-    float v[8];
-    if (live) {
-        load8(x + row * ldx + b * QK + 8 * L, mode, v);
-    } else {
-#pragma unroll
-        for (int t = 0; t < 8; t++) v[t] = 0.0f;
-    }
-
-    if constexpr (ROTATE) fwht32_quad(v, L);
-
-    float amax = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 8; t++) amax = fmaxf(amax, fabsf(v[t]));
-    amax = fmaxf(amax, quad_f32<QP_XOR1>(amax));
-    amax = fmaxf(amax, quad_f32<QP_XOR2>(amax));
-
-    const float d = __fdiv_rn(amax, (float)QMAX);
-    const bool nonzero = d >= 1.17549435e-38f;  // FLT_MIN: zero and subnormal scales give a zero block
-    const float id = nonzero ? __fdiv_rn(1.0f, d) : 0.0f;
-    const float s = !nonzero ? 0.0f : ROTATE ? __fmul_rn(d, kInvSqrt32f) : d;
     int q[8];
-#pragma unroll
-    for (int t = 0; t < 8; t++)
-        q[t] = nonzero ? (int)fminf((float)QMAX, fmaxf(-(float)QMAX, round_half_away(__fmul_rn(v[t], id)))) : 0;
+    float s;
+    quantise_quad<T, QMAX, ROTATE>(x + row * ldx + b * QK + 8 * L, mode, live, L, q, s);
 
     if constexpr (QMAX == 127) {  // int8 codes: lane L writes elements 8L .. 8L + 7
         if (live) {
@@ -182,19 +211,7 @@ __global__ __launch_bounds__(128 * RQ_BLOCKS) void rotate_quantize_kernel(const 
         return;
     }
 
-    // public codes: byte j = code j | code j + 16 << 4; lane L < 2 writes bytes
-    // 8L .. 8L + 7 from its codes and those of lane L + 2
-    uint32_t nib0 = 0, nib1 = 0;  // this lane's 8 codes, one nibble each, in byte positions
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        nib0 |= (uint32_t)(q[i] & 0xF) << (8 * i);
-        nib1 |= (uint32_t)(q[4 + i] & 0xF) << (8 * i);
-    }
-    const uint32_t hi0 = quad_u32<QP_XOR2>(nib0), hi1 = quad_u32<QP_XOR2>(nib1);
-    if (live && codes && L < 2) {
-        *reinterpret_cast<uint2 *>(codes + row * (k / 2) + b * 16 + 8 * L) = make_uint2(nib0 | hi0 << 4, nib1 | hi1 << 4);
-        if (L == 0) scales[row * nb + b] = s;
-    }
+    if (codes) store_codes4(q, s, L, live, codes + row * (k / 2) + b * 16, scales + row * nb + b);
 
     if (act && b < mx_blocks(k)) {
         // operand record of (row tile, block): row r's 32 codes as one 192-bit

@@ -28,6 +28,7 @@
 #pragma once
 
 #include "common.h"
+#include "k_rotq.h"
 
 namespace w4a4 {
 
@@ -44,6 +45,18 @@ struct SmallArgs {
     float *partial;         // ... or [splits][m][n] partial sums
     int64_t ldy, m, n, k;
     int64_t range;          // records per split
+    // fused rotate-quantise only (gemm_small_m_fused_kernel): the
+    // activations, their row stride and load mode (as the quantiser takes
+    // them), where the producers write the codes and scales (= codes,
+    // scales above), and the workspace's synchronisation words
+    const void *x = nullptr;
+    int64_t ldx = 0;
+    int mode = 0;
+    uint8_t *codes_out = nullptr;
+    float *scales_out = nullptr;
+    uint32_t *sync = nullptr;   // [0] epoch, [1] workgroups finished, [2] waits that timed out
+    uint32_t *flags = nullptr;  // one per quad of blocks: the epoch that published it
+    int64_t producers = 0;      // workgroups 0 .. producers - 1 quantise
 };
 
 // Launch plan of an m <= 16 product: the K splits.  Narrow projections split
@@ -71,13 +84,42 @@ __host__ __device__ inline int64_t small_m_splits(int64_t n, int64_t k, bool a8 
 // A8: int8 activation codes (the exact int8 path on a rotated file): staged
 // as 8-byte K-group entries and fed to the MFMA as they are; the weights still
 // enter as 16 x nibble, so d is scaled by 2^-4.
-template <int WAVES, int DEPTH, bool A8 = false>
-__global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+// Spin limit of a consumer's wait for its activations (each round is one
+// device-scope load and a short sleep): the wait always ends, and a wait that
+// runs out (which in-order dispatch of the producers rules out) is counted in
+// the workspace so that a caller can see it.
+constexpr int FUSE_SPIN_LIMIT = 1 << 20;
+
+// Wait until the quads q0 .. q0 + nr - 1 of the activations carry `target`,
+// then acquire (the activation loads after it see the producers' stores).
+__device__ __forceinline__ void wait_for_quads(const SmallArgs &a, int64_t q0, int nr, uint32_t target) {
+    const int lane = threadIdx.x & 63;
+    for (int base = 0; base < nr; base += 64) {
+        const int i = base + lane;
+        int spins = 0;
+        while (true) {
+            const bool ready =
+                i >= nr || __hip_atomic_load(a.flags + q0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == target;
+            if (__all(ready)) break;
+            if (++spins >= FUSE_SPIN_LIMIT) {
+                if (lane == 0) atomicAdd(a.sync + 2, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// The streaming GEMM of one workgroup: column tile `tile`, K split z.  With
+// FUSED, the first records' weight loads are issued, then the wave waits
+// for the activation quads of its split (published with `target`).
+template <int WAVES, int DEPTH, bool A8, bool FUSED>
+__device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, int64_t z, uint8_t *smem,
+                                             uint32_t target) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
     const int64_t k = a.k, nb = k / QK, nq = sq_quads(k);
-    const int64_t tile = blockIdx.x, z = blockIdx.y;
     const int m = (int)a.m;
     const int64_t q_lo = z * a.range;
     const int nr = (int)min(nq - q_lo, a.range);  // records of this split (>= 1)
@@ -112,16 +154,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
     // reload the split's last record, a cache hit), so the number of loads in
     // flight is the same on every path into the main loop and its waits stay
     // exact.
-    auto load = [&](int i, Rec &R) {
+    auto load_w = [&](int i, Rec &R) {
         const int li = min(wave + WAVES * i, nr - 1);
         const int off = __builtin_amdgcn_readfirstlane(li * SQ_REC);
-        const int blk = (int)(q_lo + li) * SQ_BLOCKS + ab;  // block of this lane's activations
         R.c0 = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lo16, off, 0);
         __builtin_amdgcn_sched_barrier(0);  // one issue order everywhere
         R.c1 = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lo16 + 1024, off, 0);
         __builtin_amdgcn_sched_barrier(0);
         R.d = __builtin_amdgcn_raw_buffer_load_b128(wbuf, d16, off, 0);
         __builtin_amdgcn_sched_barrier(0);
+    };
+    auto load_a = [&](int i, Rec &R) {
+        const int li = min(wave + WAVES * i, nr - 1);
+        const int blk = (int)(q_lo + li) * SQ_BLOCKS + ab;  // block of this lane's activations
 #pragma unroll
         for (int h = 0; h < (A8 ? 2 : 1); h++) {
             const v4u u = __builtin_amdgcn_raw_buffer_load_b128(cbuf, (ar * (int)nb + blk) * ROW_BYTES + 16 * h, 0, 0);
@@ -130,6 +175,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
         }
         R.as = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, (ar * (int)nb + blk) * 4, 0, 0));
         __builtin_amdgcn_sched_barrier(0);
+    };
+    auto load = [&](int i, Rec &R) {
+        load_w(i, R);
+        load_a(i, R);
     };
 
     // This wave's LDS slot for one record's activations, in the MFMA's lane
@@ -195,8 +244,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
     // is static; the scheduling barriers keep the loads ahead of the compute
     // (the scheduler would otherwise sink them to their first use).
     Rec ring[DEPTH];
+    if constexpr (FUSED) {
+        // the weights do not depend on the producers: start their stream,
+        // then wait for this split's activations
 #pragma unroll
-    for (int j = 0; j < DEPTH - 1; j++) load(j, ring[j]);
+        for (int j = 0; j < DEPTH - 1; j++) load_w(j, ring[j]);
+        wait_for_quads(a, q_lo, nr, target);
+#pragma unroll
+        for (int j = 0; j < DEPTH - 1; j++) load_a(j, ring[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < DEPTH - 1; j++) load(j, ring[j]);
+    }
     for (int i = 0; i < cnt; i += DEPTH) {
 #pragma unroll
         for (int j = 0; j < DEPTH; j++) {
@@ -224,6 +283,68 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
         if (r < m && col < a.n) {
             if (a.partial) a.partial[(z * a.m + r) * a.n + col] = sum;
             else a.y[(int64_t)r * a.ldy + col] = sum;
+        }
+    }
+}
+
+// Grid (tiles, splits).
+template <int WAVES, int DEPTH, bool A8 = false>
+__global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    small_m_tile<WAVES, DEPTH, A8, false>(a, blockIdx.x, blockIdx.y, smem, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Rotate-quantise fused into the m <= 16 product, one launch: workgroups
+// 0 .. producers - 1 quantise the activations (FUSE_QUADS quads of 4 blocks
+// each, every row; the quantiser's own per-block code, so the codes are the
+// standalone quantiser's bit for bit) into the public codes and scales and
+// publish each quad by storing the call's epoch + 1 into its flag (release);
+// the other workgroups are the streaming GEMM's (tile, split), in the
+// unfused grid's order.  Workgroups are dispatched in index order, so every
+// producer is running or done before a consumer can wait for it; the wait
+// is bounded all the same.  Each call's epoch comes from the workspace: all
+// workgroups read it at their start, and the last one to finish (by a
+// device-scope count) advances it and clears the count, so the workspace is
+// ready for the next call without a separate clearing launch.
+// ---------------------------------------------------------------------------
+constexpr int FUSE_QUADS = 2;  // 2 quads x 4 blocks x 16 rows x a quad of lanes = 512 threads
+
+template <typename T>
+__device__ __forceinline__ void fused_producer(const SmallArgs &a, int64_t pid, uint32_t target) {
+    const int tid = threadIdx.x, L = tid & 3, g = tid >> 2;  // quad g: row g % 16, block g / 16
+    const int row = g & 15;
+    const int64_t nb = a.k / QK, nq = sq_quads(a.k);
+    const int64_t b = pid * FUSE_QUADS * SQ_BLOCKS + (g >> 4);
+    const bool live = row < a.m && b < nb;  // uniform per quad
+    int q[8];
+    float s;
+    quantise_quad<T, 7, true>(static_cast<const T *>(a.x) + row * a.ldx + b * QK + 8 * L, a.mode, live, L, q, s);
+    store_codes4(q, s, L, live, a.codes_out + row * (a.k / 2) + b * 16, a.scales_out + row * nb + b);
+    __threadfence();  // this thread's codes and scale are visible device-wide ...
+    __syncthreads();  // ... for every thread of the workgroup, before the flags
+    if (tid < FUSE_QUADS) {
+        const int64_t quad = pid * FUSE_QUADS + tid;
+        if (quad < nq) __hip_atomic_store(a.flags + quad, target, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <int WAVES, int DEPTH, typename T>
+__global__ __launch_bounds__(64 * WAVES) void gemm_small_m_fused_kernel(SmallArgs a, int64_t tiles, uint32_t total) {
+    static_assert(64 * WAVES == FUSE_QUADS * SQ_BLOCKS * SMALL_M_MAX * 4, "one producer thread per lane of a quad");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const uint32_t epoch = __hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t target = epoch + 1;
+    const int64_t id = blockIdx.x;
+    if (id < a.producers) fused_producer<T>(a, id, target);  // uniform per workgroup
+    else small_m_tile<WAVES, DEPTH, false, true>(a, (id - a.producers) % tiles, (id - a.producers) / tiles, smem, target);
+    // the last workgroup to finish advances the epoch for the next call
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        if (atomicAdd(a.sync + 1, 1u) + 1 == total) {
+            __hip_atomic_store(a.sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.sync, target, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

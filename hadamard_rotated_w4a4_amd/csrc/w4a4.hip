@@ -36,6 +36,7 @@ w4a4_status hip_status(const char *what) {
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 inline unsigned blocks_for(int64_t work, int per) { return (unsigned)((work + per - 1) / per); }
+inline size_t up256_bytes(int64_t b) { return (size_t)((b + 255) / 256 * 256); }
 // y[0..m)[0..n) = 0 (row stride ldy): a grid-stride kernel on at most 2^16 workgroups
 inline void launch_zero_rows(float *y, int64_t m, int64_t n, int64_t ldy, hipStream_t s) {
     zero_rows_kernel<<<(unsigned)std::min<int64_t>((m * n + 255) / 256, 1 << 16), 256, 0, s>>>(y, m, n, ldy);
@@ -435,6 +436,91 @@ w4a4_status w4a4_gemm_noalloc(const void *packed_w, const uint8_t *codes, const 
         if (st != W4A4_OK) return st;
     }
     return w4a4_gemm(packed_w, codes, scales, y, m, n, k, ldy, ws, need, stream);
+}
+
+// Fused rotate-quantise + product.  Workspace: m <= 16: 256 bytes of
+// synchronisation words and one flag per quad of blocks (zero before the
+// first use; every call leaves them ready for the next), then the K splits'
+// partial sums; m > 16: the matrix-core operand, then the split-K partial
+// sums (w4a4_gemm's workspace).
+namespace {
+size_t fused_sync_bytes(int64_t k) { return 256 + up256_bytes(sq_quads(k) * 4); }
+}  // namespace
+
+size_t w4a4_rotate_quantize_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+    if (m < 0 || n < 0 || k < 0 || k % QK) return 0;
+    if (m == 0 || n == 0 || k == 0) return 0;
+    if (m > SMALL_M_MAX) return w4a4_gemm_workspace_bytes(m, n, k);
+    const int64_t splits = small_m_splits(n, k);
+    return fused_sync_bytes(k) + (splits > 1 ? (size_t)((splits * m * n * 4 + 255) / 256 * 256) : 0);
+}
+
+w4a4_status w4a4_rotate_quantize_gemm(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                                      const void *packed_w, int64_t n, float *y, int64_t ldy, uint8_t *codes,
+                                      float *scales, void *workspace, size_t workspace_bytes, void *stream) {
+    if (dt != W4A4_DTYPE_F32 && dt != W4A4_DTYPE_F16) return W4A4_ERR_UNSUPPORTED_DTYPE;
+    if (m < 0 || n < 0 || k < 0 || ldx < k || ldy < n || !within_bounds(m, n, k)) return W4A4_ERR_INVALID_VALUE;
+    if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
+    if (m == 0 || n == 0) return W4A4_OK;
+    if (!y) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(y, 4)) return W4A4_ERR_MISALIGNED;
+    hipStream_t s = as_stream(stream);
+    if (k == 0) {  // empty sums (no codes to write)
+        launch_zero_rows(y, m, n, ldy, s);
+        return hip_status("zero_rows_kernel");
+    }
+    if (!x || !packed_w || !codes || !scales) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(x, dt == W4A4_DTYPE_F32 ? 4 : 2) || !aligned(packed_w, 16) || !aligned(codes, 16) ||
+        !aligned(scales, 4))
+        return W4A4_ERR_MISALIGNED;
+    const size_t need = w4a4_rotate_quantize_gemm_workspace_bytes(m, n, k);
+    if (!workspace) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(workspace, 256)) return W4A4_ERR_MISALIGNED;
+    if (workspace_bytes < need) return W4A4_ERR_WORKSPACE_TOO_SMALL;
+    if (m > SMALL_M_MAX) {
+        // the quantiser writes the matrix-core operand as well; then the tiled product
+        const size_t act_bytes = (w4a4_act_operand_bytes(m, k) + 255) / 256 * 256;
+        const w4a4_status st = w4a4_rotate_quantize_prepare(x, dt, m, k, ldx, codes, scales, workspace,
+                                                            act_bytes, stream);
+        if (st != W4A4_OK) return st;
+        return w4a4_gemm_prepared(packed_w, workspace, y, m, n, k, ldy, static_cast<uint8_t *>(workspace) + act_bytes,
+                                  workspace_bytes - act_bytes, stream);
+    }
+    const SmallPlan plan = small_m_plan(n, k);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const size_t esz = dt == W4A4_DTYPE_F32 ? 4 : 2;
+    SmallArgs a{};
+    a.codes = codes;
+    a.scales = scales;
+    a.sq = static_cast<const uint8_t *>(packed_w) + sq_section_offset(n, k);
+    a.y = y;
+    a.partial = plan.splits > 1 ? reinterpret_cast<float *>(ws + fused_sync_bytes(k)) : nullptr;
+    a.ldy = ldy;
+    a.m = m;
+    a.n = n;
+    a.k = k;
+    a.range = plan.range;
+    a.x = x;
+    a.ldx = ldx;
+    a.mode = aligned(x, 16) && (ldx * esz) % 16 == 0 ? 2 : aligned(x, 4 * esz) && (ldx % 4) == 0 ? 1 : 0;
+    a.codes_out = codes;
+    a.scales_out = scales;
+    a.sync = reinterpret_cast<uint32_t *>(ws);
+    a.flags = reinterpret_cast<uint32_t *>(ws + 256);
+    a.producers = (sq_quads(k) + FUSE_QUADS - 1) / FUSE_QUADS;
+    const int64_t consumers = plan.tiles * plan.splits;
+    const int64_t total = a.producers + consumers;
+    if (!grid_fits(total * 64 * SM_WAVES)) return W4A4_ERR_INVALID_VALUE;
+    if (dt == W4A4_DTYPE_F32)
+        gemm_small_m_fused_kernel<SM_WAVES, SM_DEPTH, float>
+            <<<(unsigned)total, 64 * SM_WAVES, small_m_lds_bytes(plan), s>>>(a, plan.tiles, (uint32_t)total);
+    else
+        gemm_small_m_fused_kernel<SM_WAVES, SM_DEPTH, __half>
+            <<<(unsigned)total, 64 * SM_WAVES, small_m_lds_bytes(plan), s>>>(a, plan.tiles, (uint32_t)total);
+    const w4a4_status st = hip_status("gemm_small_m_fused_kernel");
+    if (st != W4A4_OK || plan.splits == 1) return st;
+    small_m_reduce_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(a.partial, plan.splits, m, n, y, ldy);
+    return hip_status("small_m_reduce_kernel");
 }
 
 size_t w4a4_gemm_a8_workspace_bytes(int64_t m, int64_t n, int64_t k) {

@@ -174,6 +174,40 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
                       size_t workspace_bytes, void *stream);
 
 /*
+ * Rotate-quantise fused with the product (section "Hadamard-rotated Q4_0: W4A4
+ * prompt processing": the activations are rotated and rounded to 4 bits just
+ * before the integer product; here both happen in one launch for m <= 16).
+ * Computes what w4a4_rotate_quantize_act followed by w4a4_gemm computes, with
+ * the same codes, scales and outputs:
+ *   x, dt, m, k, ldx   the activations, as w4a4_rotate_quantize_act.
+ *   packed_w, n        as w4a4_gemm; y [m][ldy] fp32 out, ldy >= n.
+ *   codes, scales      out, as w4a4_rotate_quantize_act writes them (other
+ *                      products that read the same rows can reuse them).
+ *   workspace          w4a4_rotate_quantize_gemm_workspace_bytes(m, n, k)
+ *                      bytes, 256-byte aligned.  For m <= 16 its first
+ *                      256 + 4 * ceil(k / 128) bytes (rounded up to 256) hold
+ *                      synchronisation words and must be zero before the
+ *                      workspace's first use; every call leaves them ready
+ *                      for the next, so one workspace serves any sequence of
+ *                      calls (and HIP graph replays) on one stream.  Calls that
+ *                      share a workspace must not overlap.
+ * m <= 16: one launch: its first workgroups rotate and quantise the rows
+ * (each block once) and publish them block group by block group; the
+ * weight-streaming workgroups of the product wait for the groups of their K
+ * range (a bounded wait; the fourth workspace word counts waits that ran
+ * out, which in-order dispatch of the workgroups rules out).  A K split then
+ * adds a second launch that sums the splits.  m > 16: the quantiser (writing
+ * the matrix-core operand too) and the tiled product, two launches: the tiled
+ * product reads each row tile once per 128 output columns, so quantising in
+ * its prologue would repeat the work that many times.
+ * Errors: as w4a4_rotate_quantize_act and w4a4_gemm.
+ */
+size_t w4a4_rotate_quantize_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+w4a4_status w4a4_rotate_quantize_gemm(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                                      const void *packed_w, int64_t n, float *y, int64_t ldy, uint8_t *codes,
+                                      float *scales, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * w4a4_gemm for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same product and the same kernels, with the workspace taken from a

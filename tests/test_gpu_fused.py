@@ -1,0 +1,168 @@
+"""Rotate-quantise fused with the m <= 16 product (one launch): the codes and
+scales it writes are the oracle's bit for bit, its outputs equal those of
+rotate_quantize_act followed by gemm bit for bit (the same block dots and
+epilogue in the same order), and within the tolerance of the oracle.  The
+workspace's synchronisation words carry across calls, shapes and HIP-graph
+replays; no wait ever runs out.
+The method: 1bit-MONSTER engine docs, page "The lean option: ROCmFP4, ROCmI4
+and Hadamard Q4_0", section "Hadamard-rotated Q4_0: W4A4 prompt processing".
+"""
+import numpy as np
+import pytest
+
+import oracle
+from hadamard_rotated_w4a4_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from hadamard_rotated_w4a4_amd import _lib
+    _lib.lib()
+    return _lib
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def assert_rows_close(y, ref, what=""):
+    err = np.abs(y.astype(np.float64) - ref.astype(np.float64)).max(axis=-1)
+    bound = TOL * np.abs(ref.astype(np.float64)).max(axis=-1)
+    assert np.all(err <= bound), f"{what}: worst err {err.max():.3e}"
+
+
+def sync_words(ws):
+    return host(ws[:12]).view(np.uint32)  # epoch, workgroups finished, timed-out waits
+
+
+def check_fused(ops, w, x, n, k, ws=None, what=""):
+    packed = ops.prepare_weights(dev(w))
+    xd = dev(x)
+    y, c, s = ops.rotate_quantize_gemm(xd, packed, n, k, workspace=ws)
+    rc, rs = oracle.rotate_quantize_act(np.ascontiguousarray(x[:, :k]))
+    assert np.array_equal(host(c), rc), f"{what}: codes"
+    assert np.array_equal(host(s), rs), f"{what}: scales"
+    c2, s2 = ops.rotate_quantize_act(xd, k)
+    y2 = ops.gemm(packed, c2, s2, n, k)
+    yh = host(y)
+    assert np.array_equal(yh, host(y2)), f"{what}: differs from the two-launch path"
+    assert_rows_close(yh, oracle.gemm(oracle.prepare_weights(w), rc, rs, k), what)
+    return yh
+
+
+@pytest.mark.parametrize("name,k,n", synth.DENSE_PROJECTIONS)
+def test_fused_verify_projection(ops, name, k, n):
+    w = synth.weights(n, k, synth.rng_for(0, 4, k + n))
+    x = synth.activations(16, k, synth.rng_for(0, 4, 7 * k + n), synth.outlier_count(k))
+    say(f"fused m=16 {name} {k}->{n}")
+    ws = ops.fused_workspace(16, n, k, "cuda")
+    check_fused(ops, w, x, n, k, ws, name)
+    assert list(sync_words(ws)) == [1, 0, 0]
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (3, 70, 96), (8, 1024, 160), (15, 96, 17408), (16, 33, 288)])
+def test_fused_ragged(ops, m, n, k):
+    rng = np.random.default_rng(m * 7 + n + k)
+    w = synth.weights(n, k, rng)
+    x = synth.activations(m, k, rng, max(1, k // 100))
+    say(f"fused ragged m={m} n={n} k={k}")
+    check_fused(ops, w, x, n, k, what=f"m={m} n={n} k={k}")
+
+
+def test_fused_fp32_strided_input(ops):
+    rng = np.random.default_rng(5)
+    m, n, k = 9, 200, 640
+    w = synth.weights(n, k, rng)
+    x = synth.activations(m, k + 48, rng, 6, dtype=np.float32)  # row stride 688 > k
+    say("fused fp32, row stride > k")
+    packed = ops.prepare_weights(dev(w))
+    y, c, s = ops.rotate_quantize_gemm(dev(x), packed, n, k)
+    rc, rs = oracle.rotate_quantize_act(np.ascontiguousarray(x[:, :k]))
+    assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs)
+    assert_rows_close(host(y), oracle.gemm(oracle.prepare_weights(w), rc, rs, k))
+
+
+def test_fused_shared_workspace_across_shapes(ops):
+    """One workspace (sized for the largest shape) serves interleaved calls
+    of different shapes, split and unsplit; the epoch counts the calls and
+    no wait runs out."""
+    shapes = [(16, 5120, 17408), (16, 1024, 5120), (7, 17408, 5120), (16, 6144, 5120)]
+    need = max(ops.rotate_quantize_gemm_workspace_bytes(m, n, k) for m, n, k in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    probs = []
+    for i, (m, n, k) in enumerate(shapes):
+        rng = np.random.default_rng(400 + i)
+        w = synth.weights(n, k, rng)
+        x = synth.activations(m, k, rng, k // 100)
+        say(f"shared fused workspace m={m} n={n} k={k}")
+        probs.append((ops.prepare_weights(dev(w)), dev(x), n, k, check_fused(ops, w, x, n, k, ws)))
+    calls = len(shapes)
+    for rep in range(3):
+        for packed, xd, n, k, ref in probs:
+            y, _, _ = ops.rotate_quantize_gemm(xd, packed, n, k, workspace=ws)
+            calls += 1
+            assert np.array_equal(host(y), ref)
+    assert list(sync_words(ws)) == [calls, 0, 0]
+
+
+def test_fused_graph_replays(ops):
+    """Three fused products captured in one HIP graph (a split one among
+    them), replayed with eager work and synchronisations between the
+    replays: every replay equals the eager result."""
+    shapes = [(16, 1024, 5120), (16, 5120, 17408), (4, 300, 2048)]
+    need = max(ops.rotate_quantize_gemm_workspace_bytes(m, n, k) for m, n, k in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    probs = []
+    for i, (m, n, k) in enumerate(shapes):
+        rng = np.random.default_rng(500 + i)
+        packed = ops.prepare_weights(dev(synth.weights(n, k, rng)))
+        xd = dev(synth.activations(m, k, rng, k // 100))
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        c = torch.empty((m, k // 2), dtype=torch.uint8, device="cuda")
+        s = torch.empty((m, k // 32), dtype=torch.float32, device="cuda")
+        probs.append((packed, xd, n, k, y, c, s))
+
+    def run():
+        for packed, xd, n, k, y, c, s in probs:
+            ops.rotate_quantize_gemm(xd, packed, n, k, y=y, codes=c, scales=s, workspace=ws)
+    run()
+    eager = [host(p[4]).copy() for p in probs]
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        run()
+    for rep in range(3):
+        for p in probs:
+            p[4].fill_(-1.0)
+        say(f"fused graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for p, ref in zip(probs, eager):
+            assert np.array_equal(host(p[4]), ref)
+        run()  # eager work between replays
+    words = sync_words(ws)
+    assert words[1] == 0 and words[2] == 0
+
+
+def test_fused_entry_point_above_16_rows(ops):
+    rng = np.random.default_rng(9)
+    m, n, k = 100, 1000, 2048
+    w = synth.weights(n, k, rng)
+    x = synth.activations(m, k, rng, 20)
+    say("fused entry point, m=100 (two launches)")
+    check_fused(ops, w, x, n, k, what="m=100")
