@@ -216,6 +216,35 @@ def run_verify16(torch, ops, synth):
                 c, sc = qq[synth.DENSE_INPUT_OF[name]]
                 ops.gemm(sets[i][name], c, sc, n, k, y=ys[name])
     step_us = graph_time_us(torch, step, inner=nsets)
+
+    # rotate-quantise fused into the product (one launch per distinct input:
+    # its first projection quantises, the others reuse the codes it wrote)
+    firsts = {}
+    for name, k, n in synth.DENSE_PROJECTIONS:
+        firsts.setdefault(synth.DENSE_INPUT_OF[name], name)
+    qbuf = {inp: (torch.empty((16, xin.shape[1] // 2), dtype=torch.uint8, device=dev),
+                  torch.empty((16, xin.shape[1] // 32), dtype=torch.float32, device=dev))
+            for inp, xin in inputs.items()}
+    fq_ws = torch.zeros(max(ops.rotate_quantize_gemm_workspace_bytes(16, n, k) for _, k, n in synth.DENSE_PROJECTIONS),
+                        dtype=torch.uint8, device=dev)  # zero before its first use
+    gws = torch.empty(max(ops.gemm_workspace_bytes(16, n, k) for _, k, n in synth.DENSE_PROJECTIONS),
+                      dtype=torch.uint8, device=dev)
+
+    def fused_step():
+        for i in range(nsets):
+            for name, k, n in synth.DENSE_PROJECTIONS:
+                inp = synth.DENSE_INPUT_OF[name]
+                c, sc = qbuf[inp]
+                if firsts[inp] == name:
+                    ops.rotate_quantize_gemm(inputs[inp], sets[i][name], n, k, y=ys[name], codes=c, scales=sc,
+                                             workspace=fq_ws)
+                else:
+                    ops.gemm(sets[i][name], c, sc, n, k, y=ys[name], workspace=gws)
+    fused_step_us = graph_time_us(torch, fused_step, inner=nsets)
+    out["rotate_quantize_fused"] = {"step_us": round(fused_step_us, 2),
+                                    "tokens/s": round(16 / (fused_step_us * 1e-6), 1),
+                                    "launches": "4 fused rotate-quantise + product, 3 products on the codes "
+                                                "(+ the K-split sums)"}
     out["gemm_us_total"] = round(tot_us, 2)
     out["gemm_GB/s"] = round(tot_bytes / (tot_us * 1e-6) / 1e9, 1)
     out["hbm_frac"] = round(tot_bytes / (tot_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
@@ -254,7 +283,19 @@ def run_verify16(torch, ops, synth):
                 k, n = shape[g]
                 ops.gemm(fsets[i][g], *qq[inp], n, k, y=fys[g], workspace=fws[g])
     fstep_us = graph_time_us(torch, fstep, inner=nsets)
+    fws2 = torch.zeros(max(ops.rotate_quantize_gemm_workspace_bytes(16, n, k) for k, n in shape.values()),
+                       dtype=torch.uint8, device=dev)
+
+    def fqstep():  # the four packed products, each with its rotate-quantise fused in
+        for i in range(nsets):
+            for g, _, inp in groups:
+                k, n = shape[g]
+                ops.rotate_quantize_gemm(inputs[inp], fsets[i][g], n, k, y=fys[g], codes=qbuf[inp][0],
+                                         scales=qbuf[inp][1], workspace=fws2)
+    fqstep_us = graph_time_us(torch, fqstep, inner=nsets)
     out["same_input_fused"] = {"gemms": len(groups), "gemm_us_total": round(f_us, 2),
+                               "rotate_quantize_fused_step_us": round(fqstep_us, 2),
+                               "rotate_quantize_fused_tokens/s": round(16 / (fqstep_us * 1e-6), 1),
                                "gemm_GB/s": round(tot_bytes / (f_us * 1e-6) / 1e9, 1),
                                "hbm_frac": round(tot_bytes / (f_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                                "step_us": round(fstep_us, 2), "tokens/s": round(16 / (fstep_us * 1e-6), 1)}

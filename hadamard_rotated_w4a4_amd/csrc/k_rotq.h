@@ -151,6 +151,9 @@ __device__ __forceinline__ void quantise_quad(const T *src, int mode, bool live,
 // The public int4 codes of a block (byte j = code j | code j + 16 << 4) from
 // its quad: lane L < 2 writes bytes 8L .. 8L + 7 (its codes and those of lane
 // L + 2), lane 0 the scale.  Every lane of the quad must take part.
+// COHERENT: device-scope stores (written through to where every compute unit
+// of the device reads them), for readers in the same launch.
+template <bool COHERENT = false>
 __device__ __forceinline__ void store_codes4(const int q[8], float s, int L, bool live, uint8_t *blk_codes,
                                              float *blk_scale) {
     uint32_t nib0 = 0, nib1 = 0;  // this lane's 8 codes, one nibble each, in byte positions
@@ -161,8 +164,17 @@ __device__ __forceinline__ void store_codes4(const int q[8], float s, int L, boo
     }
     const uint32_t hi0 = quad_u32<QP_XOR2>(nib0), hi1 = quad_u32<QP_XOR2>(nib1);
     if (live && L < 2) {
-        *reinterpret_cast<uint2 *>(blk_codes + 8 * L) = make_uint2(nib0 | hi0 << 4, nib1 | hi1 << 4);
-        if (L == 0) *blk_scale = s;
+        const uint32_t lo = nib0 | hi0 << 4, hi = nib1 | hi1 << 4;
+        if constexpr (COHERENT) {
+            __hip_atomic_store(reinterpret_cast<uint64_t *>(blk_codes + 8 * L), (uint64_t)hi << 32 | lo,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (L == 0)
+                __hip_atomic_store(reinterpret_cast<uint32_t *>(blk_scale), __float_as_uint(s), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            *reinterpret_cast<uint2 *>(blk_codes + 8 * L) = make_uint2(lo, hi);
+            if (L == 0) *blk_scale = s;
+        }
     }
 }
 

@@ -81,19 +81,21 @@ __host__ __device__ inline int64_t small_m_splits(int64_t n, int64_t k, bool a8 
     return small_m_plan(n, k, a8).splits;
 }
 
-// A8: int8 activation codes (the exact int8 path on a rotated file): staged
-// as 8-byte K-group entries and fed to the MFMA as they are; the weights still
-// enter as 16 x nibble, so d is scaled by 2^-4.
 // Spin limit of a consumer's wait for its activations (each round is one
 // device-scope load and a short sleep): the wait always ends, and a wait that
 // runs out (which in-order dispatch of the producers rules out) is counted in
 // the workspace so that a caller can see it.
 constexpr int FUSE_SPIN_LIMIT = 1 << 20;
 
-// Wait until the quads q0 .. q0 + nr - 1 of the activations carry `target`,
-// then acquire (the activation loads after it see the producers' stores).
-__device__ __forceinline__ void wait_for_quads(const SmallArgs &a, int64_t q0, int nr, uint32_t target) {
-    const int lane = threadIdx.x & 63;
+// Wave 0 of the workgroup waits until the quads q0 .. q0 + nr - 1 of the
+// activations carry `target`; the barrier then holds every wave's
+// activation loads back until it has.  The producers store the codes and
+// scales with device-scope (write-through) stores and complete them before
+// their flags, and the consumers load them with device-scope loads, so no
+// cache-wide write-back or invalidation is needed on either side.  Every
+// wave of the workgroup must call wait_for_quads.
+__device__ __forceinline__ void wait_for_quads_wave(const SmallArgs &a, int64_t q0, int nr, uint32_t target,
+                                                    int lane) {
     for (int base = 0; base < nr; base += 64) {
         const int i = base + lane;
         int spins = 0;
@@ -105,14 +107,21 @@ __device__ __forceinline__ void wait_for_quads(const SmallArgs &a, int64_t q0, i
                 if (lane == 0) atomicAdd(a.sync + 2, 1u);
                 break;
             }
-            __builtin_amdgcn_s_sleep(2);
+            __builtin_amdgcn_s_sleep(20);  // ~0.6 us between polls: hundreds of waves poll the same lines
         }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
+__device__ __forceinline__ void wait_for_quads(const SmallArgs &a, int64_t q0, int nr, uint32_t target) {
+    if (threadIdx.x < 64) wait_for_quads_wave(a, q0, nr, target, threadIdx.x & 63);
+    __syncthreads();
+}
+
+// A8: int8 activation codes (the exact int8 path on a rotated file): staged
+// as 8-byte K-group entries and fed to the MFMA as they are; the weights still
+// enter as 16 x nibble, so d is scaled by 2^-4.
 // The streaming GEMM of one workgroup: column tile `tile`, K split z.  With
-// FUSED, the first records' weight loads are issued, then the wave waits
+// FUSED, the first records' weight loads are issued, then the workgroup waits
 // for the activation quads of its split (published with `target`).
 template <int WAVES, int DEPTH, bool A8, bool FUSED>
 __device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, int64_t z, uint8_t *smem,
@@ -164,16 +173,19 @@ __device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, i
         R.d = __builtin_amdgcn_raw_buffer_load_b128(wbuf, d16, off, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
+    // fused: the activations were written in this launch, read them with
+    // device-scope (sc1) loads
+    constexpr int ACT_CPOL = FUSED ? 16 : 0;
     auto load_a = [&](int i, Rec &R) {
         const int li = min(wave + WAVES * i, nr - 1);
         const int blk = (int)(q_lo + li) * SQ_BLOCKS + ab;  // block of this lane's activations
 #pragma unroll
         for (int h = 0; h < (A8 ? 2 : 1); h++) {
-            const v4u u = __builtin_amdgcn_raw_buffer_load_b128(cbuf, (ar * (int)nb + blk) * ROW_BYTES + 16 * h, 0, 0);
+            const v4u u = __builtin_amdgcn_raw_buffer_load_b128(cbuf, (ar * (int)nb + blk) * ROW_BYTES + 16 * h, 0, ACT_CPOL);
             R.ac[h] = make_uint4(u[0], u[1], u[2], u[3]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        R.as = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, (ar * (int)nb + blk) * 4, 0, 0));
+        R.as = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, (ar * (int)nb + blk) * 4, 0, ACT_CPOL));
         __builtin_amdgcn_sched_barrier(0);
     };
     auto load = [&](int i, Rec &R) {
@@ -320,12 +332,14 @@ __device__ __forceinline__ void fused_producer(const SmallArgs &a, int64_t pid, 
     int q[8];
     float s;
     quantise_quad<T, 7, true>(static_cast<const T *>(a.x) + row * a.ldx + b * QK + 8 * L, a.mode, live, L, q, s);
-    store_codes4(q, s, L, live, a.codes_out + row * (a.k / 2) + b * 16, a.scales_out + row * nb + b);
-    __threadfence();  // this thread's codes and scale are visible device-wide ...
-    __syncthreads();  // ... for every thread of the workgroup, before the flags
+    store_codes4<true>(q, s, L, live, a.codes_out + row * (a.k / 2) + b * 16, a.scales_out + row * nb + b);
+    // every thread's device-scope stores have completed before the barrier,
+    // so the flags, stored after it, follow them
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     if (tid < FUSE_QUADS) {
         const int64_t quad = pid * FUSE_QUADS + tid;
-        if (quad < nq) __hip_atomic_store(a.flags + quad, target, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        if (quad < nq) __hip_atomic_store(a.flags + quad, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -338,14 +352,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_fused_kernel(SmallArg
     const int64_t id = blockIdx.x;
     if (id < a.producers) fused_producer<T>(a, id, target);  // uniform per workgroup
     else small_m_tile<WAVES, DEPTH, false, true>(a, (id - a.producers) % tiles, (id - a.producers) / tiles, smem, target);
-    // the last workgroup to finish advances the epoch for the next call
+    // the last workgroup to finish advances the epoch for the next call (the
+    // next call reads it after this launch has ended: no fence is needed)
     __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        if (atomicAdd(a.sync + 1, 1u) + 1 == total) {
-            __hip_atomic_store(a.sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.sync, target, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
+    if (threadIdx.x == 0 && atomicAdd(a.sync + 1, 1u) + 1 == total) {
+        __hip_atomic_store(a.sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.sync, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
