@@ -43,20 +43,22 @@ constexpr int MX_REC = 1024;            // bytes per (tile, block) record
 constexpr int MX_CODE_BYTES = 768;      // fp6 codes of 32 rows / columns
 constexpr int MX_BLOCK_PAD = 8;         // records per tile are padded to a multiple of this
 __host__ __device__ inline int64_t mx_blocks(int64_t k) { return (k / QK + MX_BLOCK_PAD - 1) / MX_BLOCK_PAD * MX_BLOCK_PAD; }
-// Streaming section (the m <= 16 kernel), directly after the matrix-core
-// section (a multiple of 1 KB): [Np/32][nq][2304 B] with nq = ceil(nb / 4), one record
-// per (32-column tile, 4 consecutive blocks).  Per column and block the 32
-// signed codes (q ^ 8) form four "K8 words", one per K-group g of 8 codes:
-// byte i of word g holds code 8 g + i in its low nibble and code 8 g + 4 + i
-// in its high nibble.  Lane l = 16 g + c (c < 16) of a 16x16x32 int8 MFMA
-// wants word g of columns c and 16 + c:
-//   bytes [0, 1024)     lane l's 16 B at 16 l: blocks 0 and 1 of the record,
-//                       each as (word of column c, word of column 16 + c);
+// Streaming section (the m <= 16 and grouped kernels), directly after the
+// matrix-core section (a multiple of 1 KB): [Np/32][nq][2304 B] with
+// nq = ceil(nb / 4), one record per (32-column tile, 4 consecutive blocks).
+// Per column and block the 32 signed codes (q ^ 8) form four "K8 words", one
+// per K-group w of 8 codes: byte i of word w holds code 8 w + i in its low
+// nibble and code 8 w + 4 + i in its high nibble.  Lane l = 32 g + c of a
+// 32x32x32 int8 MFMA takes codes 16 g .. 16 g + 15 (words 2 g and 2 g + 1)
+// of column c:
+//   bytes [0, 1024)     lane l's 16 B at 16 l: for blocks 0 and 1 of the
+//                       record, words 2 g and 2 g + 1 of column c;
 //   bytes [1024, 2048)  the same for blocks 2 and 3;
-//   bytes [2048, 2304)  16 B at 2048 + 16 c: for blocks 0..3 the fp16 pair
-//                       (d of column c, d of column 16 + c).
+//   bytes [2048, 2304)  4 B at 2048 + 4 l: the fp16 d of column c for block g
+//                       (low half) and block 2 + g (high half), the lane's
+//                       operands of the two two-block scale-product MFMAs.
 // Blocks past nb and padding columns hold zero codes and zero scales.  A wave
-// reads a record with three 16-byte loads per lane, the first two contiguous.
+// reads a record with two 16-byte loads and one 4-byte load per lane.
 constexpr int SQ_BLOCKS = 4;            // blocks per streaming record
 constexpr int SQ_REC = 2304;            // bytes per (tile, 4 blocks) record
 constexpr int SQ_SCALE_OFF = 2048;
@@ -136,8 +138,18 @@ __device__ __forceinline__ long widen_k8(uint32_t w) {  // 8 signed nibbles -> 8
     return (long)((uint64_t)hi << 32 | lo);
 }
 
-__device__ __forceinline__ v4i mfma_i8_16x16x32(long a, long b) {
-    return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, v4i{0, 0, 0, 0}, 0, 0, 0);
+typedef int v16i __attribute__((ext_vector_type(16)));
+// The integer dot of one block for a 32x32 tile: lane l gives 16 int8 codes
+// of row / column l % 32 (K half l / 32, the same K order on both sides);
+// the result is in the usual 32x32 output layout.
+__device__ __forceinline__ v16i mfma_i8_32x32x32(v4i a, v4i b) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, v16i{}, 0, 0, 0);
+}
+// Two K8 words as the 16 int8 operand bytes of one lane (each 16 x the
+// nibble), in K order.
+__device__ __forceinline__ v4i widen_k8x2(uint32_t w0, uint32_t w1) {
+    const long a = widen_k8(w0), b = widen_k8(w1);
+    return v4i{(int)(uint32_t)a, (int)(uint32_t)((uint64_t)a >> 32), (int)(uint32_t)b, (int)(uint32_t)((uint64_t)b >> 32)};
 }
 
 // Materialise a value in a register so that the compiler cannot fuse the

@@ -5,24 +5,26 @@
 // W4A4 path as the dense ones -- int4 x int4 block dots, per-block scaling.
 //
 // The experts of a micro-batch get few rows each (tens, a few hundred for the
-// popular ones), so the product is bound by streaming the weights, as for
-// m <= 16.  Work item = (expert tile of GS_ROWS routed rows, chunk of
-// GS_WAVES column tiles): the workgroup stages its rows' activations in LDS
-// straight from the activation rows (the routing's row permutation picks
-// them; no gathered copy is written), then each wave streams one 32-column
-// tile's 2304-byte records (the m <= 16 layout, 0.5625 B per weight) through
-// a 2-deep register ring.  Per block and wave: 4 int8 16x16x32 MFMAs (two
-// 16-row halves x columns c and 16 + c), then per output the scale product
-// and a fused multiply-add (codes enter as 16 x nibble, so d is scaled by
-// 2^-8).  Long K is staged in chunks (gs_kchunk blocks).  Each
-// workgroup scatters its rows to y.  Each XCD takes a contiguous share of
-// the expert-ordered items, so an expert's row tiles share one L2 and read
-// its weights from HBM about once.
+// popular ones), so the product streams the weights, as for m <= 16.  Work
+// item = (expert tile of GS_ROWS routed rows, chunk of GS_WAVES column
+// tiles): the workgroup stages its rows' activations in LDS straight from the
+// activation rows (the routing's row permutation picks them; no gathered
+// copy is written), already in the int8 MFMA's lane order and with each
+// scale split into its scale-product operand; then each wave streams one
+// 32-column tile's 2304-byte records (0.5625 B per weight) through a 2-deep
+// register ring.  Per block and wave: one 32x32x32 int8 MFMA (all 32 rows x
+// the tile's 32 columns); per two blocks one 32x32x4 bf16 MFMA forms both
+// blocks' scale products s (x) d (the split operands the dense kernel uses);
+// per output a convert and one fused multiply-add remain.  Codes enter as
+// 16 x nibble, so d is scaled by 2^-8.  Long K is staged in chunks of
+// GS_KCHUNK blocks, each chunk's loads issued while the previous chunk
+// streams.  Each workgroup scatters its rows to y.  Each XCD takes a
+// contiguous share of the expert-ordered items, so an expert's row tiles
+// share one L2 and read its weights from HBM about once.
 //
 // The same kernel runs a plain (dense) product as one "expert" holding every
 // row (no routing), and takes int8 activation codes (A8: the exact int8 path
-// on a rotated file, staged as 8-byte K-group entries and fed to the MFMA as
-// they are; d is then scaled by 2^-4).
+// on a rotated file, staged as they are; d is then scaled by 2^-4).
 #pragma once
 
 #include "common.h"
@@ -30,14 +32,11 @@
 
 namespace w4a4 {
 
-constexpr int GS_ROWS = 32;     // routed rows per item (two 16-row MFMA halves)
+constexpr int GS_ROWS = 32;     // routed rows per item (one 32x32 MFMA tile)
 constexpr int GS_WAVES = 8;     // waves per workgroup, one column tile each
-// blocks of activations staged per pass (a multiple of 4): 40 KB of K8
-// words and scales, or 36 KB of int8 codes and scales
-template <bool A8>
-constexpr int gs_kchunk() { return A8 ? 32 : 64; }
-template <bool A8>
-constexpr int gs_stage_bytes() { return gs_kchunk<A8>() * (4 * GS_ROWS * (A8 ? 8 : 4) + GS_ROWS * 4); }
+constexpr int GS_KCHUNK = 32;   // blocks of activations staged per pass (a multiple of 4)
+// per staged block: 32 rows x 32 int8 codes (1 KB), 32 scale operands (256 B)
+constexpr int GS_STAGE_BYTES = GS_KCHUNK * (GS_ROWS * QK + GS_ROWS * 8);
 
 struct GsArgs {
     const uint8_t *codes;    // activation codes [rows][k/2] (A8: [rows][k])
@@ -54,10 +53,9 @@ struct GsArgs {
 };
 
 template <bool A8>
-__global__ __launch_bounds__(64 * GS_WAVES) void gemm_grouped_stream_kernel(GsArgs a) {
-    constexpr int KCHUNK = gs_kchunk<A8>();
+__global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(GsArgs a) {  // 4 waves per SIMD: two workgroups per CU
     constexpr int ROW_BYTES = A8 ? QK : QK / 2;  // activation code bytes per (row, block)
-    __shared__ __attribute__((aligned(16))) uint8_t smem[gs_stage_bytes<A8>()];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[GS_STAGE_BYTES];
     __shared__ int64_t src_row[GS_ROWS];
     __shared__ int32_t out_row[GS_ROWS];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -100,132 +98,130 @@ __global__ __launch_bounds__(64 * GS_WAVES) void gemm_grouped_stream_kernel(GsAr
     const int64_t tile = cc * GS_WAVES + wave;
     const int64_t ltile = min(tile, tiles - 1);
     const uint8_t *sq = a.packed + e * a.expert_bytes + sq_section_offset(a.n, k) + ltile * nq * SQ_REC;
-    const int lo16 = lane * 16, d16 = SQ_SCALE_OFF + (lane & 15) * 16;
+    const int lo16 = lane * 16, d4 = SQ_SCALE_OFF + lane * 4;
+    const int g = lane >> 5, r32 = lane & 31;  // K half and row / column of this lane
 
-    float acc[2][2][4];  // [row half][column half][4 rows]
-#pragma unroll
-    for (int h = 0; h < 2; h++)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; c2++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) acc[h][c2][i] = 0.0f;
+    v16f acc = {};
+    uint4 *codes16 = reinterpret_cast<uint4 *>(smem);                                  // [block][g][row]
+    uint2 *sop = reinterpret_cast<uint2 *>(smem + GS_KCHUNK * GS_ROWS * QK);            // [block][row]
 
-    uint32_t *act = reinterpret_cast<uint32_t *>(smem);                            // [block][g][row]
-    uint2 *act8 = reinterpret_cast<uint2 *>(smem);                                 // A8: [block][g][row]
-    float *asc = reinterpret_cast<float *>(smem + KCHUNK * 4 * GS_ROWS * (A8 ? 8 : 4));  // [block][row]
-
-    for (int64_t c0 = 0; c0 < nb; c0 += KCHUNK) {
-        const int kc = (int)min((int64_t)KCHUNK, nb - c0);  // blocks of this chunk
-        const int nr = (kc + SQ_BLOCKS - 1) / SQ_BLOCKS;         // its records (the last may be padded)
-        __syncthreads();  // the row table is written; the previous chunk's reads are done
-        // stage: one (row, block) per thread and step; rows past the expert's
-        // count and blocks past nb are zero
-        for (int i = tid; i < nr * SQ_BLOCKS * GS_ROWS; i += 64 * GS_WAVES) {
-            const int bl = i / GS_ROWS, r = i % GS_ROWS;
+    // Activations of a chunk: thread t stages entries (row, block) t and
+    // t + 64 GS_WAVES of the chunk's GS_KCHUNK x GS_ROWS; their loads are
+    // issued one chunk ahead, into registers, so that they overlap the
+    // previous chunk's stream.  Rows past the expert's count and blocks past
+    // nb are zero.
+    constexpr int NT = 64 * GS_WAVES, PER = GS_KCHUNK * GS_ROWS / NT;
+    struct Stage {
+        uint4 u[PER], u1[A8 ? PER : 1];
+        float s[PER];
+    } st;
+    auto stage_load = [&](int64_t c0) {
+#pragma unroll
+        for (int p = 0; p < PER; p++) {
+            const int i = tid + p * NT, bl = i / GS_ROWS, r = i % GS_ROWS;
             const int64_t b = c0 + bl, src = src_row[r];
-            uint4 u = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
-            float s = 0.0f;
+            st.u[p] = make_uint4(0, 0, 0, 0);
+            if constexpr (A8) st.u1[p] = make_uint4(0, 0, 0, 0);
+            st.s[p] = 0.0f;
             if (src >= 0 && b < nb) {
-                const uint4 *p = reinterpret_cast<const uint4 *>(a.codes + src * (k / 32 * ROW_BYTES) + b * ROW_BYTES);
-                u = p[0];
-                if constexpr (A8) u1 = p[1];
-                s = a.scales[src * nb + b];
+                const uint4 *q = reinterpret_cast<const uint4 *>(a.codes + src * (k / 32 * ROW_BYTES) + b * ROW_BYTES);
+                st.u[p] = q[0];
+                if constexpr (A8) st.u1[p] = q[1];
+                st.s[p] = a.scales[src * nb + b];
             }
-            if constexpr (A8) {
-                act8[(bl * 4 + 0) * GS_ROWS + r] = make_uint2(u.x, u.y);  // codes 0..7
-                act8[(bl * 4 + 1) * GS_ROWS + r] = make_uint2(u.z, u.w);
-                act8[(bl * 4 + 2) * GS_ROWS + r] = make_uint2(u1.x, u1.y);
-                act8[(bl * 4 + 3) * GS_ROWS + r] = make_uint2(u1.z, u1.w);
-            } else {
-                const uint4 w = k8_words(u);
-                act[(bl * 4 + 0) * GS_ROWS + r] = w.x;
-                act[(bl * 4 + 1) * GS_ROWS + r] = w.y;
-                act[(bl * 4 + 2) * GS_ROWS + r] = w.z;
-                act[(bl * 4 + 3) * GS_ROWS + r] = w.w;
-            }
-            asc[bl * GS_ROWS + r] = s;
         }
-        __syncthreads();
-
-        // this wave's records of the chunk, in order, through a 2-deep ring
-        const __amdgpu_buffer_rsrc_t wbuf = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t *>(sq + (c0 / SQ_BLOCKS) * SQ_REC), 0, nr * SQ_REC, 0x00020000);
-        struct Rec {
-            v4u c0, c1, d;
-        };
-        auto load = [&](int i, Rec &R) {  // slots past the chunk reload its last record (a cache hit)
-            const int off = __builtin_amdgcn_readfirstlane(min(i, nr - 1) * SQ_REC);
-            R.c0 = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lo16, off, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            R.c1 = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lo16 + 1024, off, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            R.d = __builtin_amdgcn_raw_buffer_load_b128(wbuf, d16, off, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        constexpr float UNSCALE = A8 ? 1.0f / 16.0f : 1.0f / 256.0f;  // the operands' 16 x factors
-        auto block = [&](int bl, uint32_t w0, uint32_t w1, uint32_t dpair) {
-            const long b0 = widen_k8(w0), b1 = widen_k8(w1);
-            const float d0 = __half2float(__ushort_as_half((uint16_t)(dpair & 0xFFFF))) * UNSCALE;
-            const float d1 = __half2float(__ushort_as_half((uint16_t)(dpair >> 16))) * UNSCALE;
+    };
+    // ... and written to LDS as the MFMA's two K halves of 16 int8 codes and
+    // the scale operand
+    auto stage_store = [&]() {
 #pragma unroll
-            for (int h = 0; h < 2; h++) {
-                // row h * 16 + lane % 16, K-group lane / 16
-                const int ai = (bl * 4 + (lane >> 4)) * GS_ROWS + h * 16 + (lane & 15);
-                long av;
-                if constexpr (A8) {
-                    const uint2 u = act8[ai];
-                    av = (long)((uint64_t)u.y << 32 | u.x);
-                } else {
-                    av = widen_k8(act[ai]);
-                }
-                const v4i S0 = mfma_i8_16x16x32(av, b0);
-                const v4i S1 = mfma_i8_16x16x32(av, b1);
-                const float4 s4 = *reinterpret_cast<const float4 *>(asc + bl * GS_ROWS + h * 16 + 4 * (lane >> 4));
-                const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    acc[h][0][i] = fmaf((float)S0[i], __fmul_rn(sv[i], d0), acc[h][0][i]);
-                    acc[h][1][i] = fmaf((float)S1[i], __fmul_rn(sv[i], d1), acc[h][1][i]);
-                }
+        for (int p = 0; p < PER; p++) {
+            const int i = tid + p * NT, bl = i / GS_ROWS, r = i % GS_ROWS;
+            if constexpr (A8) {
+                codes16[(bl * 2 + 0) * GS_ROWS + r] = st.u[p];   // codes 0..15
+                codes16[(bl * 2 + 1) * GS_ROWS + r] = st.u1[p];  // codes 16..31
+            } else {
+                const uint4 w = k8_words(st.u[p]);
+                const v4i h0 = widen_k8x2(w.x, w.y), h1 = widen_k8x2(w.z, w.w);
+                codes16[(bl * 2 + 0) * GS_ROWS + r] = make_uint4(h0[0], h0[1], h0[2], h0[3]);
+                codes16[(bl * 2 + 1) * GS_ROWS + r] = make_uint4(h1[0], h1[1], h1[2], h1[3]);
             }
-        };
-        auto compute = [&](int i, const Rec &R) {
-            const int bl = i * SQ_BLOCKS;
-            block(bl + 0, R.c0[0], R.c0[1], R.d[0]);
-            block(bl + 1, R.c0[2], R.c0[3], R.d[1]);
-            block(bl + 2, R.c1[0], R.c1[1], R.d[2]);
-            block(bl + 3, R.c1[2], R.c1[3], R.d[3]);
-        };
-        Rec r0, r1;
-        load(0, r0);
-        for (int i = 0; i < nr; i += 2) {
-            load(i + 1, r1);
+            sop[bl * GS_ROWS + r] = act_scale_operand(st.s[p]);
+        }
+    };
+
+    // This wave's records, in order, through a 2-deep ring that runs across
+    // the chunks (the weights do not wait for the staging).
+    const __amdgpu_buffer_rsrc_t wbuf =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(sq), 0, (int)(nq * SQ_REC), 0x00020000);
+    struct Rec {
+        v4u c0, c1;
+        uint32_t d;
+    };
+    auto load = [&](int64_t i, Rec &R) {  // slots past the tile reload its last record (a cache hit)
+        const int off = __builtin_amdgcn_readfirstlane((int)min(i, nq - 1) * SQ_REC);
+        R.c0 = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lo16, off, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        R.c1 = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lo16 + 1024, off, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        R.d = __builtin_amdgcn_raw_buffer_load_b32(wbuf, d4, off, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    constexpr float UNSCALE = A8 ? 1.0f / 16.0f : 1.0f / 256.0f;  // the operands' 16 x factors
+    // blocks bl and bl + 1 of the chunk: (w0, w1) this lane's words of each,
+    // dh its d of block bl + g
+    auto pair = [&](int bl, uint32_t w00, uint32_t w01, uint32_t w10, uint32_t w11, uint16_t dh) {
+        const uint32_t wop = weight_scale_operand(__half2float(__ushort_as_half(dh)) * UNSCALE);
+        const v32f P = mfma_bf16_32x32x4_2blk(sop[(bl + g) * GS_ROWS + r32], make_uint2(wop, wop));
+        const uint4 a0 = codes16[(bl * 2 + g) * GS_ROWS + r32];
+        const v16i S0 = mfma_i8_32x32x32(v4i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w}, widen_k8x2(w00, w01));
+        const uint4 a1 = codes16[((bl + 1) * 2 + g) * GS_ROWS + r32];
+        const v16i S1 = mfma_i8_32x32x32(v4i{(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w}, widen_k8x2(w10, w11));
+#pragma unroll
+        for (int v = 0; v < 16; v++) acc[v] = fmaf((float)S0[v], P[v], acc[v]);
+#pragma unroll
+        for (int v = 0; v < 16; v++) acc[v] = fmaf((float)S1[v], P[16 + v], acc[v]);
+    };
+    auto compute = [&](int rec, const Rec &R) {  // rec: record index within the chunk
+        const int bl = rec * SQ_BLOCKS;
+        pair(bl + 0, R.c0[0], R.c0[1], R.c0[2], R.c0[3], (uint16_t)(R.d & 0xFFFF));
+        pair(bl + 2, R.c1[0], R.c1[1], R.c1[2], R.c1[3], (uint16_t)(R.d >> 16));
+    };
+
+    constexpr int RPC = GS_KCHUNK / SQ_BLOCKS;  // records per chunk (even)
+    Rec q0, q1;
+    load(0, q0);
+    __syncthreads();  // the row table is written
+    stage_load(0);
+    for (int64_t r0 = 0; r0 < nq; r0 += RPC) {
+        __syncthreads();  // the previous chunk's LDS reads are done
+        stage_store();
+        __syncthreads();
+        if (r0 + RPC < nq) stage_load((r0 + RPC) * SQ_BLOCKS);
+        // records r0 .. r1 - 1; an even count leaves record r1 in q0
+        const int cnt_r = (int)min((int64_t)RPC, nq - r0);
+        for (int i = 0; i < cnt_r; i += 2) {
+            load(r0 + i + 1, q1);
             __builtin_amdgcn_sched_barrier(0);
-            compute(i, r0);
+            compute(i, q0);
             __builtin_amdgcn_sched_barrier(0);
-            if (i + 1 >= nr) break;
-            load(i + 2, r0);
+            if (i + 1 >= cnt_r) break;
+            load(r0 + i + 2, q0);
             __builtin_amdgcn_sched_barrier(0);
-            compute(i + 1, r1);
+            compute(i + 1, q1);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 
     // scatter: output row of local row r is out_row[r]
     if (tile >= tiles) return;
+    const int64_t col = tile * TILE_N + r32;
+    if (col >= a.n) return;
 #pragma unroll
-    for (int h = 0; h < 2; h++)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; c2++) {
-            const int64_t col = tile * TILE_N + c2 * 16 + (lane & 15);
-            if (col >= a.n) continue;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int r = h * 16 + 4 * (lane >> 4) + i;
-                const int32_t orow = out_row[r];
-                if (orow >= 0) a.y[(int64_t)orow * a.ldy + col] = acc[h][c2][i];
-            }
-        }
+    for (int v = 0; v < 16; v++) {
+        const int32_t orow = out_row[mfma32_row(v, lane)];
+        if (orow >= 0) a.y[(int64_t)orow * a.ldy + col] = acc[v];
+    }
 }
 
 }  // namespace w4a4

@@ -122,11 +122,15 @@ __global__ __launch_bounds__(256) void repack_sq_kernel(const uint8_t *__restric
         dbits = (uint16_t)(blk[0] | (blk[1] << 8));
     }
     uint8_t *rec = packed + sq_section_offset(n, k) + (tile * nq + b / SQ_BLOCKS) * SQ_REC;
-    const int j = (int)(b % SQ_BLOCKS), c16 = c & 15, half = c >> 4;
+    const int j = (int)(b % SQ_BLOCKS);
+    // word w goes to lane 32 (w / 2) + c, at 8 (j % 2) + 4 (w % 2) of its 16 B
+    // in the half (j / 2) of the record
     const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-    for (int g = 0; g < 4; g++)
-        reinterpret_cast<uint32_t *>(rec + (j >> 1) * 1024 + (16 * g + c16) * 16 + (j & 1) * 8)[half] = words[g];
-    reinterpret_cast<uint16_t *>(rec + SQ_SCALE_OFF + c16 * 16 + j * 4)[half] = dbits;
+    for (int wd = 0; wd < 4; wd++)
+        *reinterpret_cast<uint32_t *>(rec + (j >> 1) * 1024 + (32 * (wd >> 1) + c) * 16 + (j & 1) * 8 + (wd & 1) * 4) =
+            words[wd];
+    // d goes to lane 32 (j % 2) + c, low half for blocks 0 and 1, high for 2 and 3
+    reinterpret_cast<uint16_t *>(rec + SQ_SCALE_OFF + (32 * (j & 1) + c) * 4)[j >> 1] = dbits;
 }
 
 }  // namespace w4a4

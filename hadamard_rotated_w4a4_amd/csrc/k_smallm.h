@@ -15,13 +15,15 @@
 // lane).  A record's activations are needed by its wave alone: the wave
 // moves them through its own LDS slot into the MFMA's lane order just before
 // computing the record, so no workgroup-wide staging phase or barrier
-// precedes the stream.  Per block and wave: two 16x16x32 int8 MFMAs (columns
-// c and 16 + c of the tile, all 16 rows), then per output a convert, the
-// scale product s * d and a fused multiply-add.  Codes enter the MFMA as
-// 16 x (signed nibble), so the integer sum is 256 S, and d is scaled by 2^-8
-// (exact) to match.  The waves' sums meet in LDS; the workgroup stores its
-// 16 x 32 outputs, or its partial sums when K is split (a second kernel adds
-// the splits in ascending order).
+// precedes the stream.  Per block and wave: one 32x32x32 int8 MFMA (the 16
+// rows, and 16 rows of don't-care lanes whose outputs are dropped, x the
+// tile's 32 columns); per two blocks one 32x32x4 bf16 MFMA forms the scale
+// products s (x) d of both (the split operands the dense kernel uses); per
+// output a convert and one fused multiply-add remain.  Codes enter the MFMA
+// as 16 x (signed nibble), so the integer sum is 256 S, and d is scaled by
+// 2^-8 (exact) to match.  The waves' sums meet in LDS; the workgroup stores
+// its 16 x 32 outputs, or its partial sums when K is split (a second kernel
+// adds the splits in ascending order).
 //
 // Measured on MI355X (7 dense projections of a 27B-class layer, 16 rows):
 // 8 waves per workgroup and a 2-record ring beat 4 waves or deeper rings.
@@ -118,7 +120,7 @@ __device__ __forceinline__ void wait_for_quads(const SmallArgs &a, int64_t q0, i
 }
 
 // A8: int8 activation codes (the exact int8 path on a rotated file): staged
-// as 8-byte K-group entries and fed to the MFMA as they are; the weights still
+// as they are (16 codes per K half) and fed to the MFMA; the weights still
 // enter as 16 x nibble, so d is scaled by 2^-4.
 // The streaming GEMM of one workgroup: column tile `tile`, K split z.  With
 // FUSED, the first records' weight loads are issued, then the workgroup waits
@@ -146,7 +148,8 @@ __device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, i
         const_cast<uint8_t *>(a.codes), 0, (int)(m * nb * ROW_BYTES), CFG);
     const __amdgpu_buffer_rsrc_t sbuf = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(a.scales), 0, (int)(m * nb * 4), CFG);
-    const int lo16 = lane * 16, d16 = SQ_SCALE_OFF + (lane & 15) * 16;
+    const int lo16 = lane * 16, d4 = SQ_SCALE_OFF + lane * 4;
+    const int g = lane >> 5, r16 = lane & 15;  // K half and row (mod 16) of this lane in the MFMAs
     // A record's activations are loaded by its own wave, lane (row r = l % 16,
     // block l / 16 of the record) taking that row's code bytes of the block
     // and its scale; the range check zeroes rows past m and the bytes past the
@@ -155,7 +158,8 @@ __device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, i
     // lane offset because the range check does not cover the scalar offset.
     const int ar = lane & 15, ab = lane >> 4;
     struct Rec {
-        v4u c0, c1, d;
+        v4u c0, c1;
+        uint32_t d;
         uint4 ac[A8 ? 2 : 1];
         float as;
     };
@@ -170,7 +174,7 @@ __device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, i
         __builtin_amdgcn_sched_barrier(0);  // one issue order everywhere
         R.c1 = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lo16 + 1024, off, 0);
         __builtin_amdgcn_sched_barrier(0);
-        R.d = __builtin_amdgcn_raw_buffer_load_b128(wbuf, d16, off, 0);
+        R.d = __builtin_amdgcn_raw_buffer_load_b32(wbuf, d4, off, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     // fused: the activations were written in this launch, read them with
@@ -194,61 +198,49 @@ __device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, i
     };
 
     // This wave's LDS slot for one record's activations, in the MFMA's lane
-    // order: A4 K8 words [block][g][row] (4 B), A8 8 codes [block][g][row]
-    // (8 B), then the scales [block][row].
-    constexpr int SLOT = SQ_BLOCKS * 64 * (A8 ? 8 : 4) + SQ_BLOCKS * 16 * 4;
+    // order: [block][K half][row] 16 int8 codes (16 B), then the scale
+    // operands [block][row] (8 B).
+    constexpr int SLOT = SQ_BLOCKS * 2 * 16 * 16 + SQ_BLOCKS * 16 * 8;
     uint8_t *slot = smem + wave * SLOT;
-    uint32_t *act = reinterpret_cast<uint32_t *>(slot);
-    uint2 *act8 = reinterpret_cast<uint2 *>(slot);
-    float *asc = reinterpret_cast<float *>(slot + SQ_BLOCKS * 64 * (A8 ? 8 : 4));
+    uint4 *codes16 = reinterpret_cast<uint4 *>(slot);
+    uint2 *sop = reinterpret_cast<uint2 *>(slot + SQ_BLOCKS * 2 * 16 * 16);
     auto put = [&](const Rec &R) {
         if constexpr (A8) {
-            act8[ab * 64 + 0 * 16 + ar] = make_uint2(R.ac[0].x, R.ac[0].y);  // codes 0..7
-            act8[ab * 64 + 1 * 16 + ar] = make_uint2(R.ac[0].z, R.ac[0].w);  // codes 8..15
-            act8[ab * 64 + 2 * 16 + ar] = make_uint2(R.ac[1].x, R.ac[1].y);
-            act8[ab * 64 + 3 * 16 + ar] = make_uint2(R.ac[1].z, R.ac[1].w);
+            codes16[(ab * 2 + 0) * 16 + ar] = R.ac[0];  // codes 0..15
+            codes16[(ab * 2 + 1) * 16 + ar] = R.ac[1];  // codes 16..31
         } else {
             const uint4 w = k8_words(R.ac[0]);
-            act[ab * 64 + 0 * 16 + ar] = w.x;
-            act[ab * 64 + 1 * 16 + ar] = w.y;
-            act[ab * 64 + 2 * 16 + ar] = w.z;
-            act[ab * 64 + 3 * 16 + ar] = w.w;
+            const v4i h0 = widen_k8x2(w.x, w.y), h1 = widen_k8x2(w.z, w.w);
+            codes16[(ab * 2 + 0) * 16 + ar] = make_uint4(h0[0], h0[1], h0[2], h0[3]);
+            codes16[(ab * 2 + 1) * 16 + ar] = make_uint4(h1[0], h1[1], h1[2], h1[3]);
         }
-        asc[ab * 16 + ar] = R.as;
+        sop[ab * 16 + ar] = act_scale_operand(R.as);
     };
 
+    // outputs of rows 0..15: elements 0..7 of the 32x32 layout
     float acc[8];
 #pragma unroll
     for (int v = 0; v < 8; v++) acc[v] = 0.0f;
-    // One block: two MFMAs (columns c and 16 + c of the tile, all 16 rows),
-    // then per output the scale product and a fused multiply-add.
     constexpr float UNSCALE = A8 ? 1.0f / 16.0f : 1.0f / 256.0f;  // the operands' 16 x factors
-    auto block = [&](int bl, uint32_t w0, uint32_t w1, uint32_t dpair) {
-        long av;  // row lane % 16, K-group lane / 16
-        if constexpr (A8) {
-            const uint2 u = act8[bl * 64 + lane];
-            av = (long)((uint64_t)u.y << 32 | u.x);
-        } else {
-            av = widen_k8(act[bl * 64 + lane]);
-        }
-        const v4i S0 = mfma_i8_16x16x32(av, widen_k8(w0));
-        const v4i S1 = mfma_i8_16x16x32(av, widen_k8(w1));
-        const float4 s4 = *reinterpret_cast<const float4 *>(asc + bl * 16 + 4 * (lane >> 4));
-        const float d0 = __half2float(__ushort_as_half((uint16_t)(dpair & 0xFFFF))) * UNSCALE;
-        const float d1 = __half2float(__ushort_as_half((uint16_t)(dpair >> 16))) * UNSCALE;
-        const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+    // blocks bl and bl + 1 of the record: (w0, w1) this lane's words of
+    // each, dh its d of block bl + g.  Lanes of rows 16..31 read row r % 16
+    // (their outputs are not used).
+    auto pair = [&](int bl, uint32_t w00, uint32_t w01, uint32_t w10, uint32_t w11, uint16_t dh) {
+        const uint32_t wop = weight_scale_operand(__half2float(__ushort_as_half(dh)) * UNSCALE);
+        const v32f P = mfma_bf16_32x32x4_2blk(sop[(bl + g) * 16 + r16], make_uint2(wop, wop));
+        const uint4 a0 = codes16[(bl * 2 + g) * 16 + r16];
+        const v16i S0 = mfma_i8_32x32x32(v4i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w}, widen_k8x2(w00, w01));
+        const uint4 a1 = codes16[((bl + 1) * 2 + g) * 16 + r16];
+        const v16i S1 = mfma_i8_32x32x32(v4i{(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w}, widen_k8x2(w10, w11));
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            acc[i] = fmaf((float)S0[i], __fmul_rn(sv[i], d0), acc[i]);
-            acc[4 + i] = fmaf((float)S1[i], __fmul_rn(sv[i], d1), acc[4 + i]);
-        }
+        for (int v = 0; v < 8; v++) acc[v] = fmaf((float)S0[v], P[v], acc[v]);
+#pragma unroll
+        for (int v = 0; v < 8; v++) acc[v] = fmaf((float)S1[v], P[16 + v], acc[v]);
     };
     auto compute = [&](const Rec &R) {
         put(R);  // the same wave reads the slot next: LDS operations of a wave stay in order
-        block(0, R.c0[0], R.c0[1], R.d[0]);
-        block(1, R.c0[2], R.c0[3], R.d[1]);
-        block(2, R.c1[0], R.c1[1], R.d[2]);
-        block(3, R.c1[2], R.c1[3], R.d[3]);
+        pair(0, R.c0[0], R.c0[1], R.c0[2], R.c0[3], (uint16_t)(R.d & 0xFFFF));
+        pair(2, R.c1[0], R.c1[1], R.c1[2], R.c1[3], (uint16_t)(R.d >> 16));
     };
 
     // Ring of DEPTH records: record i + DEPTH - 1 is loaded before record i
@@ -290,8 +282,8 @@ __device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, i
         float sum = red[i];
 #pragma unroll
         for (int w = 1; w < WAVES; w++) sum += red[w * 512 + i];
-        const int r = 4 * (l >> 4) + (v & 3);
-        const int64_t col = tile * TILE_N + (v >> 2) * 16 + (l & 15);
+        const int r = mfma32_row(v, l);  // v < 8: rows 0..15
+        const int64_t col = tile * TILE_N + (l & 31);
         if (r < m && col < a.n) {
             if (a.partial) a.partial[(z * a.m + r) * a.n + col] = sum;
             else a.y[(int64_t)r * a.ldy + col] = sum;
@@ -365,7 +357,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_m_fused_kernel(SmallArg
 // reduction if that is larger.
 __host__ inline size_t small_m_lds_bytes(const SmallPlan &p, bool a8 = false) {
     (void)p;
-    const size_t slots = (size_t)SM_WAVES * SQ_BLOCKS * (64 * (a8 ? 8 : 4) + 16 * 4),
+    (void)a8;
+    const size_t slots = (size_t)SM_WAVES * SQ_BLOCKS * (2 * 16 * 16 + 16 * 8),
                  red = (size_t)SM_WAVES * 8 * 64 * 4;
     return slots > red ? slots : red;
 }
