@@ -72,21 +72,25 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
             a.y[(int64_t)a.g.perm[first + i / a.n] * a.ldy + i % a.n] = 0.0f;
     }
 
-    // item: contiguous share per XCD (ids x, x + 8, ... run on XCD x)
+    // item: contiguous share per XCD (ids x, x + 8, ... run on XCD x).  The
+    // items of one expert (row tiles x column chunks) are consecutive and
+    // column-chunk-major, so a chunk's weights are read from HBM once and
+    // then from the XCD's L2 by the expert's other row tiles.
     const int64_t rtiles = dense ? (a.dense_rows + GS_ROWS - 1) / GS_ROWS : a.g.tile_prefix[a.g.n_expert];
     const int64_t items = rtiles * a.col_chunks, per_xcd = (items + 7) / 8;
     const int64_t j = blockIdx.x / 8, item = (blockIdx.x % 8) * per_xcd + j;
     if (j >= per_xcd || item >= items) return;  // uniform
-    const int64_t rt = item / a.col_chunks, cc = item % a.col_chunks;
-    const int e = dense ? 0 : expert_of_tile(a.g, rt);
+    const int e = dense ? 0 : expert_of_tile(a.g, item / a.col_chunks);
+    const int64_t t0 = dense ? 0 : a.g.tile_prefix[e], ne = dense ? rtiles : a.g.tile_prefix[e + 1] - t0;
+    const int64_t local = item - t0 * a.col_chunks, cc = local / ne, rt_e = local % ne;
     const int64_t cnt = dense ? a.dense_rows : a.g.offsets[e + 1] - a.g.offsets[e];
-    const int64_t row_lo = (dense ? rt : rt - a.g.tile_prefix[e]) * GS_ROWS;
+    const int64_t row_lo = rt_e * GS_ROWS;
     if (tid < GS_ROWS) {
-        const int64_t local = row_lo + tid;
+        const int64_t lr = row_lo + tid;  // row within the expert
         int64_t src = -1;
         int32_t orow = -1;
-        if (local < cnt) {
-            orow = dense ? (int32_t)local : a.g.perm[a.g.offsets[e] + local];
+        if (lr < cnt) {
+            orow = dense ? (int32_t)lr : a.g.perm[a.g.offsets[e] + lr];
             src = dense || a.per_slot ? orow : orow / a.top_k;
         }
         src_row[tid] = src;
