@@ -725,20 +725,31 @@ def measure_ceilings(torch):
 
 
 def gpu_clock_mhz():
-    """The current shader clock as the platform tool reports it (None if it
-    cannot be read): recorded before and after the run."""
-    import subprocess
-    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+    """The shader clock the driver reports for the GPU (sysfs: the hwmon
+    frequency, else the starred pp_dpm_sclk level), in MHz; None if it cannot
+    be read.  A file read, not a tool: a process that has initialised the GPU
+    must not start other programs.  Recorded before and after the run (an idle
+    part reports its low idle level)."""
+    import glob
+    import re
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
         try:
-            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
-        except (OSError, subprocess.TimeoutExpired):
+            if open(os.path.join(dev, "vendor")).read().strip() != "0x1002":
+                continue
+        except OSError:
             continue
-        if r.returncode != 0:
-            continue
-        import re
-        m = re.search(r'"?(?:sclk|gfx_0|GFX_0)[^0-9]{0,80}?(\d{3,4})', r.stdout, flags=re.I)
-        if m:
-            return int(m.group(1))
+        for f in glob.glob(os.path.join(dev, "hwmon", "hwmon*", "freq1_input")):
+            try:
+                return int(open(f).read().strip()) // 1000000
+            except (OSError, ValueError):
+                pass
+        try:
+            for line in open(os.path.join(dev, "pp_dpm_sclk")):
+                m = re.search(r"(\d+)\s*Mhz\s*\*", line, flags=re.I)
+                if m:
+                    return int(m.group(1))
+        except OSError:
+            pass
     return None
 
 

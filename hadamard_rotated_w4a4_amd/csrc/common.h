@@ -111,6 +111,14 @@ __device__ __forceinline__ v32f mfma_bf16_32x32x4_2blk(uint2 a, uint2 b) {
                                                    0, 0);
 }
 
+// Scale products of one block: the 32x32x8 bf16 MFMA, whose K slots 0..3
+// come from lanes 0..31 and 4..7 from lanes 32..63; the caller zeroes one
+// lane group's A operand so that only the other group's block contributes.
+__device__ __forceinline__ v16f mfma_bf16_32x32x8(uint2 a, uint2 b) {
+    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(v4s, a), __builtin_bit_cast(v4s, b), v16f{}, 0,
+                                                   0, 0);
+}
+
 // Scale operands of the two-block scale-product MFMA (K slots k = 0..3 of a
 // lane pair up as A_k * B_k).
 // Activation row: (s_1, s_1, s_2, s_2), s_1 the leading 8 bits of s

@@ -225,17 +225,23 @@ __device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, i
     // blocks bl and bl + 1 of the record: (w0, w1) this lane's words of
     // each, dh its d of block bl + g.  Lanes of rows 16..31 read row r % 16
     // (their outputs are not used).
+    // Per block the scale products come from a single-block 32x32x8 MFMA
+    // (half the result registers of the two-block form, which keeps the
+    // kernel at three workgroups per CU): lane group g holds block bl + g's
+    // operands, and the other group's A operand is zeroed.
     auto pair = [&](int bl, uint32_t w00, uint32_t w01, uint32_t w10, uint32_t w11, uint16_t dh) {
         const uint32_t wop = weight_scale_operand(__half2float(__ushort_as_half(dh)) * UNSCALE);
-        const v32f P = mfma_bf16_32x32x4_2blk(sop[(bl + g) * 16 + r16], make_uint2(wop, wop));
+        const uint2 sa = sop[(bl + g) * 16 + r16], zero = make_uint2(0, 0);
+        const v16f P0 = mfma_bf16_32x32x8(g ? zero : sa, make_uint2(wop, wop));
         const uint4 a0 = codes16[(bl * 2 + g) * 16 + r16];
         const v16i S0 = mfma_i8_32x32x32(v4i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w}, widen_k8x2(w00, w01));
+#pragma unroll
+        for (int v = 0; v < 8; v++) acc[v] = fmaf((float)S0[v], P0[v], acc[v]);
+        const v16f P1 = mfma_bf16_32x32x8(g ? sa : zero, make_uint2(wop, wop));
         const uint4 a1 = codes16[((bl + 1) * 2 + g) * 16 + r16];
         const v16i S1 = mfma_i8_32x32x32(v4i{(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w}, widen_k8x2(w10, w11));
 #pragma unroll
-        for (int v = 0; v < 8; v++) acc[v] = fmaf((float)S0[v], P[v], acc[v]);
-#pragma unroll
-        for (int v = 0; v < 8; v++) acc[v] = fmaf((float)S1[v], P[16 + v], acc[v]);
+        for (int v = 0; v < 8; v++) acc[v] = fmaf((float)S1[v], P1[v], acc[v]);
     };
     auto compute = [&](const Rec &R) {
         put(R);  // the same wave reads the slot next: LDS operations of a wave stay in order
@@ -291,9 +297,11 @@ __device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, i
     }
 }
 
-// Grid (tiles, splits).
+// Grid (tiles, splits).  At most 80 registers (int4 activations): six waves
+// per SIMD keep three workgroups resident per CU, so the 544 workgroups of a
+// 17408-column projection run in one round.
 template <int WAVES, int DEPTH, bool A8 = false>
-__global__ __launch_bounds__(64 * WAVES) void gemm_small_m_kernel(SmallArgs a) {
+__global__ __launch_bounds__(64 * WAVES, A8 ? 1 : 6) void gemm_small_m_kernel(SmallArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     small_m_tile<WAVES, DEPTH, A8, false>(a, blockIdx.x, blockIdx.y, smem, 0);
 }
@@ -336,7 +344,9 @@ __device__ __forceinline__ void fused_producer(const SmallArgs &a, int64_t pid, 
 }
 
 template <int WAVES, int DEPTH, typename T>
-__global__ __launch_bounds__(64 * WAVES) void gemm_small_m_fused_kernel(SmallArgs a, int64_t tiles, uint32_t total) {
+__global__ __launch_bounds__(64 * WAVES, 6) void gemm_small_m_fused_kernel(SmallArgs a, int64_t tiles, uint32_t total) {
+    // (three workgroups per CU, as the unfused kernel: the waiting consumers
+    // and the producers are resident together)
     static_assert(64 * WAVES == FUSE_QUADS * SQ_BLOCKS * SMALL_M_MAX * 4, "one producer thread per lane of a quad");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const uint32_t epoch = __hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
