@@ -573,6 +573,49 @@ def test_gemm_id_long_k_ragged_tiles(ops, rows_per_token):
     assert_rows_close(y.reshape(-1, n), ref.reshape(-1, n), "gemm_id long k")
 
 
+def _heavy_ids(T, E):
+    """Slot 0: expert 0 for tokens 0..199 (200 rows), expert 2 after; slot 1:
+    expert 1 for tokens 0..129 (129 rows after one invalid id), expert 4 for
+    127 tokens, expert 3 after.  No token repeats an expert."""
+    ids = np.zeros((T, 2), np.int32)
+    ids[200:, 0] = 2
+    ids[:130, 1] = 1
+    ids[130:257, 1] = 4
+    ids[257:, 1] = 3
+    ids[5, 1] = E  # invalid
+    return ids
+
+
+@pytest.mark.parametrize("rows_per_token", [1, 2])
+def test_gemm_id_popular_experts_ragged(ops, rows_per_token):
+    """Experts with hundreds of rows (200 and 129: whole 32-row tiles plus a
+    ragged one, over one column chunk and two staging passes of K) beside
+    experts with fewer, one invalid id among a popular expert's tokens:
+    against the oracle, and exact integer sums with unit scales."""
+    E, T, top_k, n, k = 5, 300, 2, 200, 1344
+    rng = np.random.default_rng(1344 + rows_per_token)
+    we = [synth.weights(n, k, rng) for _ in range(E)]
+    ids = _heavy_ids(T, E)
+    counts = np.bincount(ids[ids < E], minlength=E)
+    assert counts[0] == 200 and counts[1] == 129 and counts[4] == 127
+    x = synth.activations(T * rows_per_token, k, rng, synth.outlier_count(k))
+    say(f"gemm_id popular experts rows_per_token={rows_per_token}: counts {counts}")
+    packed = torch.cat([ops.prepare_weights(dev(w)) for w in we])
+    c, s = ops.rotate_quantize_act(dev(x))
+    idsd = dev(ids)
+    y = host(ops.gemm_id(packed, E, c, s, rows_per_token, idsd, n, k))
+    q4e = np.stack([oracle.prepare_weights(w) for w in we])
+    rc, rs = oracle.rotate_quantize_act(x)
+    ref = oracle.gemm_id(q4e, rc, rs, rows_per_token, ids, n, k)
+    assert not y[5, 1].any()
+    assert_rows_close(y.reshape(-1, n), ref.reshape(-1, n), "popular experts")
+    q1 = np.stack([with_unit_scales(q) for q in q4e])
+    p1 = torch.cat([ops.repack_q4_0_h32(dev(q), n, k) for q in q1])
+    ones = np.ones_like(rs)
+    yi = host(ops.gemm_id(p1, E, dev(rc), dev(ones), rows_per_token, idsd, n, k))
+    assert np.array_equal(yi, oracle.gemm_id(q1, rc, ones, rows_per_token, ids, n, k))
+
+
 @pytest.mark.parametrize("which", ["gate", "down"])
 def test_gemm_id_moe_full_size_sampled(ops, which):
     mo = synth.moe()
