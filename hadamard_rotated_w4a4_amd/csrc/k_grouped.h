@@ -38,6 +38,16 @@ constexpr int GS_KCHUNK = 32;   // blocks of activations staged per pass (a mult
 // per staged block: 32 rows x 32 int8 codes (1 KB), 32 scale operands (256 B)
 constexpr int GS_STAGE_BYTES = GS_KCHUNK * (GS_ROWS * QK + GS_ROWS * 8);
 
+// Column tiles per wave and item: two when K fits one staging pass (the
+// staged activations then serve twice as many columns), else one.
+__host__ inline int grouped_tiles_per_wave(int64_t n, int64_t k) {
+    return k / QK <= GS_KCHUNK && padded_n(n) / TILE_N > GS_WAVES ? 2 : 1;
+}
+__host__ inline int64_t grouped_col_chunks(int64_t n, int64_t k) {
+    const int64_t per = (int64_t)GS_WAVES * grouped_tiles_per_wave(n, k);
+    return (padded_n(n) / TILE_N + per - 1) / per;
+}
+
 struct GsArgs {
     const uint8_t *codes;    // activation codes [rows][k/2] (A8: [rows][k])
     const float *scales;     // activation scales [rows][k/32]
@@ -49,7 +59,8 @@ struct GsArgs {
     Routing g;
     int top_k, per_slot;     // activation row of routed row i: i (per slot) or i / top_k
     int64_t n_rows;          // routed rows (tokens x slots); those past offsets[E] have invalid ids
-    int64_t col_chunks;      // ceil(tiles / GS_WAVES)
+    int64_t col_chunks;      // ceil(tiles / (GS_WAVES * tiles_per_wave))
+    int tiles_per_wave = 1;  // > 1 only when K fits one staging pass
 };
 
 template <bool A8>
@@ -97,15 +108,9 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
         out_row[tid] = orow;
     }
 
-    // this wave's column tile (a last chunk's extra waves stream the last
-    // tile again and store nothing)
-    const int64_t tile = cc * GS_WAVES + wave;
-    const int64_t ltile = min(tile, tiles - 1);
-    const uint8_t *sq = a.packed + e * a.expert_bytes + sq_section_offset(a.n, k) + ltile * nq * SQ_REC;
     const int lo16 = lane * 16, d4 = SQ_SCALE_OFF + lane * 4;
     const int g = lane >> 5, r32 = lane & 31;  // K half and row / column of this lane
-
-    v16f acc = {};
+    v16f acc;
     uint4 *codes16 = reinterpret_cast<uint4 *>(smem);                                  // [block][g][row]
     uint2 *sop = reinterpret_cast<uint2 *>(smem + GS_KCHUNK * GS_ROWS * QK);            // [block][row]
 
@@ -156,12 +161,11 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
 
     // This wave's records, in order, through a 2-deep ring that runs across
     // the chunks (the weights do not wait for the staging).
-    const __amdgpu_buffer_rsrc_t wbuf =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(sq), 0, (int)(nq * SQ_REC), 0x00020000);
     struct Rec {
         v4u c0, c1;
         uint32_t d;
     };
+    __amdgpu_buffer_rsrc_t wbuf;
     auto load = [&](int64_t i, Rec &R) {  // slots past the tile reload its last record (a cache hit)
         const int off = __builtin_amdgcn_readfirstlane((int)min(i, nq - 1) * SQ_REC);
         R.c0 = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lo16, off, 0);
@@ -193,17 +197,18 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
     };
 
     constexpr int RPC = GS_KCHUNK / SQ_BLOCKS;  // records per chunk (even)
-    Rec q0, q1;
-    load(0, q0);
-    __syncthreads();  // the row table is written
-    stage_load(0);
-    for (int64_t r0 = 0; r0 < nq; r0 += RPC) {
-        __syncthreads();  // the previous chunk's LDS reads are done
-        stage_store();
-        __syncthreads();
-        if (r0 + RPC < nq) stage_load((r0 + RPC) * SQ_BLOCKS);
-        // records r0 .. r1 - 1; an even count leaves record r1 in q0
-        const int cnt_r = (int)min((int64_t)RPC, nq - r0);
+    // The wave's tt-th column tile: of the item's tiles_per_wave rounds of
+    // GS_WAVES (a last chunk's extra waves stream the last tile again and
+    // store nothing).
+    auto tile_of = [&](int tt) { return (cc * a.tiles_per_wave + tt) * GS_WAVES + wave; };
+    auto set_tile = [&](int64_t tile) {
+        const uint8_t *sq = a.packed + e * a.expert_bytes + sq_section_offset(a.n, k) + min(tile, tiles - 1) * nq * SQ_REC;
+        wbuf = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(sq), 0, (int)(nq * SQ_REC), 0x00020000);
+        acc = v16f{};
+    };
+    // records r0 .. r0 + cnt_r - 1 of the tile, record r0 already in q0; an
+    // even count leaves record r0 + cnt_r in q0
+    auto stream = [&](int64_t r0, int cnt_r, Rec &q0, Rec &q1) {
         for (int i = 0; i < cnt_r; i += 2) {
             load(r0 + i + 1, q1);
             __builtin_amdgcn_sched_barrier(0);
@@ -215,16 +220,50 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
             compute(i + 1, q1);
             __builtin_amdgcn_sched_barrier(0);
         }
-    }
-
+    };
     // scatter: output row of local row r is out_row[r]
-    if (tile >= tiles) return;
-    const int64_t col = tile * TILE_N + r32;
-    if (col >= a.n) return;
+    auto scatter = [&](int64_t tile) {
+        const int64_t col = tile * TILE_N + r32;
+        if (tile >= tiles || col >= a.n) return;
 #pragma unroll
-    for (int v = 0; v < 16; v++) {
-        const int32_t orow = out_row[mfma32_row(v, lane)];
-        if (orow >= 0) a.y[(int64_t)orow * a.ldy + col] = acc[v];
+        for (int v = 0; v < 16; v++) {
+            const int32_t orow = out_row[mfma32_row(v, lane)];
+            if (orow >= 0) a.y[(int64_t)orow * a.ldy + col] = acc[v];
+        }
+    };
+
+    Rec q0, q1;
+    if (nq <= RPC) {
+        // K fits one pass: stage once, then stream each of the wave's tiles
+        set_tile(tile_of(0));
+        load(0, q0);
+        __syncthreads();  // the row table is written
+        stage_load(0);
+        stage_store();
+        __syncthreads();
+        for (int tt = 0; tt < a.tiles_per_wave; tt++) {
+            if (tt > 0) {
+                set_tile(tile_of(tt));
+                load(0, q0);
+            }
+            stream(0, (int)nq, q0, q1);
+            scatter(tile_of(tt));
+        }
+    } else {
+        // passes of GS_KCHUNK blocks, the next pass's loads issued during
+        // this one's stream; the weight ring runs across the passes
+        set_tile(tile_of(0));
+        load(0, q0);
+        __syncthreads();  // the row table is written
+        stage_load(0);
+        for (int64_t r0 = 0; r0 < nq; r0 += RPC) {
+            __syncthreads();  // the previous chunk's LDS reads are done
+            stage_store();
+            __syncthreads();
+            if (r0 + RPC < nq) stage_load((r0 + RPC) * SQ_BLOCKS);
+            stream(r0, (int)min((int64_t)RPC, nq - r0), q0, q1);
+        }
+        scatter(tile_of(0));
     }
 }
 

@@ -573,7 +573,7 @@ w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float 
         return hip_status("small_m_reduce_kernel");
     }
     // m > 16: the streaming kernel, all rows as one group
-    const int64_t col_chunks = (padded_n(n) / TILE_N + GS_WAVES - 1) / GS_WAVES;
+    const int64_t col_chunks = grouped_col_chunks(n, k);
     const int64_t items = (m + GS_ROWS - 1) / GS_ROWS * col_chunks;
     if (!grid_fits((items + 8) * 64 * GS_WAVES)) return W4A4_ERR_INVALID_VALUE;
     GsArgs a{};
@@ -588,6 +588,7 @@ w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float 
     a.top_k = 1;
     a.per_slot = 1;
     a.col_chunks = col_chunks;
+    a.tiles_per_wave = grouped_tiles_per_wave(n, k);
     gemm_grouped_stream_kernel<true><<<(unsigned)((items + 7) / 8 * 8), 64 * GS_WAVES, 0, s>>>(a);
     return hip_status("gemm_grouped_stream_kernel<a8>");
 }
@@ -775,7 +776,7 @@ w4a4_status w4a4_gemm_id_routed(const void *packed_w, int64_t n_expert, const ui
     if (act_rows_per_token != 1 && act_rows_per_token != top_k) return W4A4_ERR_INVALID_VALUE;
     const int64_t n_rows = n_tokens * top_k;
     const int64_t row_tiles = grouped_row_tiles(n_expert, n_rows, GS_ROWS);
-    const int64_t col_chunks = (padded_n(n) / TILE_N + GS_WAVES - 1) / GS_WAVES;
+    const int64_t col_chunks = grouped_col_chunks(n, k);
     if (!within_bounds(n_rows, n, k) || !grid_fits((row_tiles * col_chunks + 8) * 64 * GS_WAVES))
         return W4A4_ERR_INVALID_VALUE;
     if (!workspace) return W4A4_ERR_INVALID_VALUE;
@@ -812,6 +813,7 @@ w4a4_status w4a4_gemm_id_routed(const void *packed_w, int64_t n_expert, const ui
     a.per_slot = act_rows_per_token != 1 ? 1 : 0;
     a.n_rows = n_rows;
     a.col_chunks = col_chunks;
+    a.tiles_per_wave = grouped_tiles_per_wave(n, k);
     // a bound on the items (row tiles x column chunks), rounded up to whole XCD rows
     gemm_grouped_stream_kernel<false><<<(unsigned)((row_tiles * col_chunks + 7) / 8 * 8), 64 * GS_WAVES, 0, s>>>(a);
     return hip_status("gemm_grouped_stream_kernel");
@@ -830,7 +832,7 @@ w4a4_status w4a4_gemm_id(const void *packed_w, int64_t n_expert, const uint8_t *
     if (act_rows_per_token != 1 && act_rows_per_token != top_k) return W4A4_ERR_INVALID_VALUE;
     const int64_t n_rows = n_tokens * top_k;
     const int64_t row_tiles = grouped_row_tiles(n_expert, n_rows, GS_ROWS);
-    const int64_t col_chunks = (padded_n(n) / TILE_N + GS_WAVES - 1) / GS_WAVES;
+    const int64_t col_chunks = grouped_col_chunks(n, k);
     if (!within_bounds(n_rows, n, k) || !grid_fits((row_tiles * col_chunks + 8) * 64 * GS_WAVES))
         return W4A4_ERR_INVALID_VALUE;
     if (!workspace) return W4A4_ERR_INVALID_VALUE;
