@@ -22,8 +22,10 @@
 // output a convert and one fused multiply-add remain.  Codes enter the MFMA
 // as 16 x (signed nibble), so the integer sum is 256 S, and d is scaled by
 // 2^-8 (exact) to match.  The waves' sums meet in LDS; the workgroup stores
-// its 16 x 32 outputs, or its partial sums when K is split (a second kernel
-// adds the splits in ascending order).
+// its 16 x 32 outputs, or its partial sums when K is split: then the last
+// workgroup of the tile to finish (by a per-tile arrival count) adds the
+// splits in ascending order, so no second launch is needed and the sum does
+// not depend on which split finished last.
 //
 // Measured on MI355X (7 dense projections of a 27B-class layer, 16 rows):
 // 8 waves per workgroup and a 2-record ring beat 4 waves or deeper rings.
@@ -38,6 +40,7 @@ constexpr int SMALL_M_MAX = 16;
 constexpr int SM_WAVES = 8;             // waves per workgroup
 constexpr int SM_DEPTH = 2;             // streaming records in flight per wave
 constexpr int SM_ITEM_TARGET = 512;     // workgroups wanted (two per CU on a 256-CU part)
+static_assert(SM_ITEM_TARGET < (1 << 16), "a tile's K splits are counted in 16 bits");
 
 struct SmallArgs {
     const uint8_t *codes;   // activation codes [m][k/2] (int8 activations: [m][k])
@@ -45,6 +48,11 @@ struct SmallArgs {
     const uint8_t *sq;      // streaming section of the packed weights
     float *y;               // [m][ldy] (splits == 1) ...
     float *partial;         // ... or [splits][m][n] partial sums
+    // K split: per column tile, a count of the workgroups arrived, tagged
+    // with this call's ticket (small_m_arrive); the last of the tile's
+    // splits resets it to zero.
+    unsigned long long *arrivals = nullptr;
+    unsigned long long ticket = 0;  // 48 bits, non-zero, drawn per call
     int64_t ldy, m, n, k;
     int64_t range;          // records per split
     // fused rotate-quantise only (gemm_small_m_fused_kernel): the
@@ -70,10 +78,12 @@ struct SmallPlan {
 __host__ __device__ inline SmallPlan small_m_plan(int64_t n, int64_t k, bool a8 = false) {
     (void)a8;
     const int64_t tiles = padded_n(n) / TILE_N, nq = sq_quads(k);
-    // K up to 5120 aims at half as many workgroups (measured on the 16-row
-    // verify set: q, k and v each ~1 us faster with fewer K splits, while
-    // the long-K down projection is faster with the full target)
-    const int64_t target = k <= 5120 ? SM_ITEM_TARGET / 2 : SM_ITEM_TARGET;
+    // K up to 5120 aims at a quarter as many workgroups (measured on the
+    // 16-row verify set with the splits added in-kernel: q unsplit and k, v
+    // in 4 splits beat 2 and 8 splits by 0.3 to 2 us each; 2 or 1 split for
+    // k and v lose 0.3 us; the long-K o and down projections are fastest
+    // with the full target, against a half or twice it)
+    const int64_t target = k <= 5120 ? SM_ITEM_TARGET / 4 : SM_ITEM_TARGET;
     const int64_t want = (target + tiles - 1) / tiles;
     const int64_t splits = want < nq ? want : nq;
     const int64_t range = (nq + splits - 1) / splits;
@@ -117,6 +127,43 @@ __device__ __forceinline__ void wait_for_quads_wave(const SmallArgs &a, int64_t 
 __device__ __forceinline__ void wait_for_quads(const SmallArgs &a, int64_t q0, int nr, uint32_t target) {
     if (threadIdx.x < 64) wait_for_quads_wave(a, q0, nr, target, threadIdx.x & 63);
     __syncthreads();
+}
+
+// Bytes of the cross-wave reduction in LDS ([wave][8][64] floats); the
+// word after it tells the workgroup whether it arrived last.
+constexpr int SM_RED_BYTES = SM_WAVES * 8 * 64 * 4;
+
+// Counts one arrival of a K split at its column tile's word and returns 1 to
+// the last of `splits` (< 2^16) arrivals, which also resets the word to zero.
+// Every arrival adds ticket << 16 | 1, so after c arrivals on a word that
+// started at zero it holds (c * ticket mod 2^48) << 16 | c: one fetch-and-add
+// per arrival, with no retry however many splits arrive at once, and a value
+// that stale contents match only by chance (hi == lo * ticket for a 48-bit
+// ticket drawn per call).  An arrival that finds another form (the
+// workspace's previous contents) counts itself with compare-and-swaps into a
+// word of this call's form; each swap that fails does so because another
+// arrival's update succeeded, so the loop ends.
+__device__ __forceinline__ int small_m_arrive(unsigned long long *word, unsigned long long ticket, int64_t splits) {
+    const unsigned long long inc = ticket << 16 | 1ull, lo = 0xffffull;
+    auto ours = [&](unsigned long long w) {  // a count of this call's arrivals
+        const unsigned long long c = w & lo;
+        return c < (unsigned long long)splits && (w >> 16) == ((c * ticket) & 0xffffffffffffull);
+    };
+    const unsigned long long old = __hip_atomic_fetch_add(word, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long pos;
+    if (ours(old)) {
+        pos = (old & lo) + 1;
+    } else {
+        unsigned long long w = old + inc, next;
+        do {
+            next = ours(w) ? w + inc : inc;
+        } while (!__hip_atomic_compare_exchange_strong(word, &w, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT));
+        pos = next & lo;
+    }
+    if ((int64_t)pos < splits) return 0;
+    __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return 1;
 }
 
 // A8: int8 activation codes (the exact int8 path on a rotated file): staged
@@ -283,6 +330,7 @@ __device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, i
 #pragma unroll
     for (int v = 0; v < 8; v++) red[(wave * 8 + v) * 64 + lane] = acc[v];
     __syncthreads();
+    uint32_t *part = reinterpret_cast<uint32_t *>(a.partial);
     for (int i = tid; i < 512; i += 64 * WAVES) {
         const int v = i >> 6, l = i & 63;
         float sum = red[i];
@@ -291,9 +339,45 @@ __device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, i
         const int r = mfma32_row(v, l);  // v < 8: rows 0..15
         const int64_t col = tile * TILE_N + (l & 31);
         if (r < m && col < a.n) {
-            if (a.partial) a.partial[(z * a.m + r) * a.n + col] = sum;
+            // partial sums are stored device-scope (write-through), so the
+            // tile's last workgroup reads them from any XCD
+            if (part)
+                __hip_atomic_store(part + (z * a.m + r) * a.n + col, __float_as_uint(sum), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             else a.y[(int64_t)r * a.ldy + col] = sum;
         }
+    }
+    if (!part) return;  // uniform
+
+    // K split: every thread's partial stores have completed before the
+    // barrier, so the arrival counted after it follows them
+    const int64_t splits = (sq_quads(k) + a.range - 1) / a.range;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    static_assert(WAVES * 8 * 64 * 4 <= SM_RED_BYTES, "the last-arrival word follows the reduction");
+    int *last = reinterpret_cast<int *>(smem + SM_RED_BYTES);
+    if (tid == 0) *last = small_m_arrive(a.arrivals + tile, a.ticket, splits);
+    __syncthreads();
+    if (!*last) return;  // uniform
+    const int64_t mn = a.m * a.n;
+    for (int i = tid; i < 512; i += 64 * WAVES) {
+        const int v = i >> 6, l = i & 63;
+        const int r = mfma32_row(v, l);
+        const int64_t col = tile * TILE_N + (l & 31);
+        if (r >= m || col >= a.n) continue;
+        const uint32_t *p = part + (int64_t)r * a.n + col;
+        float sum = 0.0f;
+        for (int64_t z0 = 0; z0 < splits; z0 += 8) {  // eight loads in flight, then the adds in order
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                x[j] = __uint_as_float(
+                    __hip_atomic_load(p + min(z0 + j, splits - 1) * mn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                if (z0 + j < splits) sum = z0 + j == 0 ? x[j] : sum + x[j];
+        }
+        a.y[(int64_t)r * a.ldy + col] = sum;
     }
 }
 
@@ -364,17 +448,24 @@ __global__ __launch_bounds__(64 * WAVES, 6) void gemm_small_m_fused_kernel(Small
 }
 
 // LDS bytes of one workgroup: the waves' activation slots, or the cross-wave
-// reduction if that is larger.
+// reduction and the last-arrival word if that is larger.
 __host__ inline size_t small_m_lds_bytes(const SmallPlan &p, bool a8 = false) {
     (void)p;
     (void)a8;
-    const size_t slots = (size_t)SM_WAVES * SQ_BLOCKS * (2 * 16 * 16 + 16 * 8),
-                 red = (size_t)SM_WAVES * 8 * 64 * 4;
+    const size_t slots = (size_t)SM_WAVES * SQ_BLOCKS * (2 * 16 * 16 + 16 * 8), red = (size_t)SM_RED_BYTES + 16;
     return slots > red ? slots : red;
 }
 
-// y = sum over the K splits of the partial sums, in ascending split order.
-// The loads of eight splits are issued together (clamped past the last
+// Workspace of an m <= 16 product that splits K: the tiles' arrival words,
+// then the splits' partial sums (both in whole 256-byte units); 0 without a
+// split.
+__host__ inline size_t small_m_arrival_bytes(const SmallPlan &p) { return (size_t)((p.tiles * 8 + 255) / 256 * 256); }
+__host__ inline size_t small_m_workspace_bytes(const SmallPlan &p, int64_t m, int64_t n) {
+    return p.splits > 1 ? small_m_arrival_bytes(p) + (size_t)((p.splits * m * n * 4 + 255) / 256 * 256) : 0;
+}
+
+// y = sum over the K splits of the partial sums, in ascending split order
+// (the dense kernel's split K).  The loads of eight splits are issued together (clamped past the last
 // split, which then adds nothing), so the latency is paid once per eight.
 __global__ __launch_bounds__(256) void small_m_reduce_kernel(const float *__restrict__ partial, int64_t splits,
                                                              int64_t m, int64_t n, float *__restrict__ y,

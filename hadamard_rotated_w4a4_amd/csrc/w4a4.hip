@@ -6,6 +6,7 @@
 #include "w4a4.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -37,6 +38,24 @@ inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 inline unsigned blocks_for(int64_t work, int per) { return (unsigned)((work + per - 1) / per); }
 inline size_t up256_bytes(int64_t b) { return (size_t)((b + 255) / 256 * 256); }
+// An odd 48-bit ticket per m <= 16 launch that splits K, for its tiles'
+// arrival words: the top 48 bits of the call count times an odd 64-bit
+// constant (a Weyl sequence), made odd, so that a word of the ticket's form
+// (see small_m_arrive) looks like no small integer or float pair that a
+// workspace may hold.  A captured launch keeps its ticket on every replay,
+// which is sound because each launch leaves the words at zero.
+std::atomic<uint64_t> g_calls{0};
+unsigned long long next_ticket() {
+    return (((g_calls.fetch_add(1, std::memory_order_relaxed) + 1) * 0x9E3779B97F4A7C15ull) >> 16) | 1ull;
+}
+// m <= 16 with a K split: the arrival words at the workspace's start, the
+// partial sums after them
+inline void set_small_m_split(SmallArgs &a, const SmallPlan &p, void *workspace) {
+    if (p.splits <= 1) return;
+    a.arrivals = static_cast<unsigned long long *>(workspace);
+    a.partial = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + small_m_arrival_bytes(p));
+    a.ticket = next_ticket();
+}
 // y[0..m)[0..n) = 0 (row stride ldy): a grid-stride kernel on at most 2^16 workgroups
 inline void launch_zero_rows(float *y, int64_t m, int64_t n, int64_t ldy, hipStream_t s) {
     zero_rows_kernel<<<(unsigned)std::min<int64_t>((m * n + 255) / 256, 1 << 16), 256, 0, s>>>(y, m, n, ldy);
@@ -315,10 +334,7 @@ w4a4_status w4a4_rotate_quantize_prepare(const void *x, w4a4_dtype dt, int64_t m
 size_t w4a4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
     if (m < 0 || n < 0 || k < 0 || k % QK) return 0;
     if (n == 0 || k == 0 || m == 0) return 0;
-    if (m <= SMALL_M_MAX) {  // partial sums of the K splits
-        const int64_t splits = small_m_splits(n, k);
-        return splits > 1 ? (size_t)((splits * m * n * 4 + 255) / 256 * 256) : 0;
-    }
+    if (m <= SMALL_M_MAX) return small_m_workspace_bytes(small_m_plan(n, k), m, n);  // the K splits' sums
     return (w4a4_act_operand_bytes(m, k) + 255) / 256 * 256 + split_partial_bytes(m, n, k);
 }
 
@@ -356,19 +372,16 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
         a.scales = scales;
         a.sq = static_cast<const uint8_t *>(packed_w) + sq_section_offset(n, k);
         a.y = y;
-        a.partial = splits > 1 ? static_cast<float *>(workspace) : nullptr;
         a.ldy = ldy;
         a.m = m;
         a.n = n;
         a.k = k;
         const SmallPlan plan = small_m_plan(n, k);
         a.range = plan.range;
+        set_small_m_split(a, plan, workspace);
         gemm_small_m_kernel<SM_WAVES, SM_DEPTH><<<dim3((unsigned)plan.tiles, (unsigned)plan.splits), 64 * SM_WAVES,
                                                    small_m_lds_bytes(plan), s>>>(a);
-        const w4a4_status st2 = hip_status("gemm_small_m_kernel");
-        if (st2 != W4A4_OK || splits == 1) return st2;
-        small_m_reduce_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(a.partial, splits, m, n, y, ldy);
-        return hip_status("small_m_reduce_kernel");
+        return hip_status("gemm_small_m_kernel");
     }
     // workspace: the activation operand, then the split-K partial sums
     if (!workspace) return W4A4_ERR_INVALID_VALUE;
@@ -441,7 +454,7 @@ w4a4_status w4a4_gemm_noalloc(const void *packed_w, const uint8_t *codes, const 
 // Fused rotate-quantise + product.  Workspace: m <= 16: 256 bytes of
 // synchronisation words and one flag per quad of blocks (zero before the
 // first use; every call leaves them ready for the next), then the K splits'
-// partial sums; m > 16: the matrix-core operand, then the split-K partial
+// arrival words and partial sums (as w4a4_gemm's); m > 16: the matrix-core operand, then the split-K partial
 // sums (w4a4_gemm's workspace).
 namespace {
 size_t fused_sync_bytes(int64_t k) { return 256 + up256_bytes(sq_quads(k) * 4); }
@@ -451,8 +464,7 @@ size_t w4a4_rotate_quantize_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k
     if (m < 0 || n < 0 || k < 0 || k % QK) return 0;
     if (m == 0 || n == 0 || k == 0) return 0;
     if (m > SMALL_M_MAX) return w4a4_gemm_workspace_bytes(m, n, k);
-    const int64_t splits = small_m_splits(n, k);
-    return fused_sync_bytes(k) + (splits > 1 ? (size_t)((splits * m * n * 4 + 255) / 256 * 256) : 0);
+    return fused_sync_bytes(k) + small_m_workspace_bytes(small_m_plan(n, k), m, n);
 }
 
 w4a4_status w4a4_rotate_quantize_gemm(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
@@ -494,7 +506,7 @@ w4a4_status w4a4_rotate_quantize_gemm(const void *x, w4a4_dtype dt, int64_t m, i
     a.scales = scales;
     a.sq = static_cast<const uint8_t *>(packed_w) + sq_section_offset(n, k);
     a.y = y;
-    a.partial = plan.splits > 1 ? reinterpret_cast<float *>(ws + fused_sync_bytes(k)) : nullptr;
+    set_small_m_split(a, plan, ws + fused_sync_bytes(k));
     a.ldy = ldy;
     a.m = m;
     a.n = n;
@@ -517,17 +529,13 @@ w4a4_status w4a4_rotate_quantize_gemm(const void *x, w4a4_dtype dt, int64_t m, i
     else
         gemm_small_m_fused_kernel<SM_WAVES, SM_DEPTH, __half>
             <<<(unsigned)total, 64 * SM_WAVES, small_m_lds_bytes(plan), s>>>(a, plan.tiles, (uint32_t)total);
-    const w4a4_status st = hip_status("gemm_small_m_fused_kernel");
-    if (st != W4A4_OK || plan.splits == 1) return st;
-    small_m_reduce_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(a.partial, plan.splits, m, n, y, ldy);
-    return hip_status("small_m_reduce_kernel");
+    return hip_status("gemm_small_m_fused_kernel");
 }
 
 size_t w4a4_gemm_a8_workspace_bytes(int64_t m, int64_t n, int64_t k) {
     if (m < 0 || n < 0 || k < 0 || k % QK) return 0;
     if (n == 0 || k == 0 || m == 0 || m > SMALL_M_MAX) return 0;
-    const int64_t splits = small_m_splits(n, k, true);  // partial sums of the K splits
-    return splits > 1 ? (size_t)((splits * m * n * 4 + 255) / 256 * 256) : 0;
+    return small_m_workspace_bytes(small_m_plan(n, k, true), m, n);  // the K splits' sums
 }
 
 w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float *scales, float *y, int64_t m,
@@ -559,18 +567,15 @@ w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float 
         a.scales = scales;
         a.sq = static_cast<const uint8_t *>(packed_w) + sq_section_offset(n, k);
         a.y = y;
-        a.partial = plan.splits > 1 ? static_cast<float *>(workspace) : nullptr;
         a.ldy = ldy;
         a.m = m;
         a.n = n;
         a.k = k;
         a.range = plan.range;
+        set_small_m_split(a, plan, workspace);
         gemm_small_m_kernel<SM_WAVES, SM_DEPTH, true>
             <<<dim3((unsigned)plan.tiles, (unsigned)plan.splits), 64 * SM_WAVES, small_m_lds_bytes(plan, true), s>>>(a);
-        const w4a4_status st2 = hip_status("gemm_small_m_kernel<a8>");
-        if (st2 != W4A4_OK || plan.splits == 1) return st2;
-        small_m_reduce_kernel<<<blocks_for(m * n, 256), 256, 0, s>>>(a.partial, plan.splits, m, n, y, ldy);
-        return hip_status("small_m_reduce_kernel");
+        return hip_status("gemm_small_m_kernel<a8>");
     }
     // m > 16: the streaming kernel, all rows as one group
     const int64_t col_chunks = grouped_col_chunks(n, k);

@@ -158,12 +158,20 @@ w4a4_status w4a4_rotate_quantize_prepare(const void *x, w4a4_dtype dt, int64_t m
  *   codes, scales  from w4a4_rotate_quantize_act (m rows).
  *   y         out, [m][ldy] fp32, ldy >= n, 4-byte aligned.
  *   workspace device scratch of w4a4_gemm_workspace_bytes(m, n, k) bytes,
- *             256-byte aligned (may be NULL when that is 0); contents on entry
- *             are ignored.  Calls that share a workspace must not overlap.
- * m <= 16 takes a weight-streaming kernel on the 4-bit records (products
- * with few 32-column tiles or long K split K over workgroups; the workspace
- * then holds their partial sums, added in ascending split order by a second
- * kernel).  Larger m first re-lays the activation codes and
+ *             256-byte aligned (may be NULL when that is 0); it needs no
+ *             clearing: whatever it holds on entry is overwritten or, for
+ *             the arrival words below, recognised as stale by its ticket.
+ *             Calls that share a workspace must not overlap.
+ * m <= 16 takes a weight-streaming kernel on the 4-bit records, one launch.
+ * Products with few 32-column tiles or long K split K over workgroups; the
+ * workspace then holds one 8-byte arrival word per 32-column tile (rounded
+ * up to 256 bytes), then the splits' partial sums.  An arrival word counts
+ * the tile's workgroups in a form tagged with a 48-bit ticket that the
+ * library draws per call, so stale contents pass for a count of this call
+ * only by a 2^-48 chance; the last workgroup of a tile to arrive adds the
+ * tile's splits in ascending split order and leaves the word at zero, so
+ * later calls and replays of a captured launch start from a clean word.
+ * Larger m first re-lays the activation codes and
  * scales into the matrix-core operand format at the start of the workspace
  * (w4a4_act_operand_bytes rounded up to 256), then runs the tiled
  * matrix-core kernel with the rest of the workspace as its own
@@ -195,8 +203,8 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
  * (each block once) and publish them block group by block group; the
  * weight-streaming workgroups of the product wait for the groups of their K
  * range (a bounded wait; the fourth workspace word counts waits that ran
- * out, which in-order dispatch of the workgroups rules out).  A K split then
- * adds a second launch that sums the splits.  m > 16: the quantiser (writing
+ * out, which in-order dispatch of the workgroups rules out).  A K split adds
+ * its splits in the same launch, as w4a4_gemm does.  m > 16: the quantiser (writing
  * the matrix-core operand too) and the tiled product, two launches: the tiled
  * product reads each row tile once per 128 output columns, so quantising in
  * its prologue would repeat the work that many times.
@@ -220,7 +228,8 @@ w4a4_status w4a4_rotate_quantize_gemm(const void *x, w4a4_dtype dt, int64_t m, i
  *   W4A4_ERR_WORKSPACE_TOO_SMALL before any launch.
  *   Every call on one GPU shares that GPU's array, which keeps the last
  *   call's contents (no kernel needs it cleared: every byte read is written
- *   first in the same call).  Calls that overlap on one GPU (several streams
+ *   first in the same call, except the arrival words of an m <= 16 K split,
+ *   which each call leaves at zero and which carry a per-call ticket).  Calls that overlap on one GPU (several streams
  *   or threads) race on it: serialise them.  The array's device address is
  *   looked up on the first call on each device, with that device current;
  *   a failed lookup returns W4A4_ERR_HIP.
@@ -276,7 +285,8 @@ w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, 
  * w4a4_gemm_a8: y = sum_b d_w * s * S with S the exact integer dot of the
  * Q4_0 codes (q - 8) with the int8 codes.  Arguments as w4a4_gemm, with the
  * workspace of w4a4_gemm_a8_workspace_bytes (non-zero only for m <= 16 when
- * K is split; may be NULL when 0).  m <= 16 streams the weights as w4a4_gemm
+ * K is split: arrival words and partial sums as in w4a4_gemm; may be NULL
+ * when 0).  m <= 16 streams the weights as w4a4_gemm
  * does; larger m runs the streaming kernel over 32-row groups.
  */
 w4a4_status w4a4_rotate_quantize_act8(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,

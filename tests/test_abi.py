@@ -81,6 +81,12 @@ def test_gemm_validation(L):
     need = L.w4a4_gemm_workspace_bytes(64, 64, 64)
     assert need == 2 * 8 * 1024  # 32-row tiles x blocks padded to 8 x 1 KB records
     assert L.w4a4_gemm_workspace_bytes(16, 64, 64) == 0
+    # m <= 16 with K split (n = 1024: 32 column tiles, K = 5120: 4 splits):
+    # one 8-byte arrival word per tile (256 bytes), then the partial sums
+    assert L.w4a4_gemm_workspace_bytes(16, 1024, 5120) == 256 + 4 * 16 * 1024 * 4
+    assert L.w4a4_gemm_workspace_bytes(3, 1024, 5120) == 256 + 4 * 3 * 1024 * 4
+    # n = 5120 (160 tiles), K = 17408 (136 records): 4 splits; 1280 bytes of words
+    assert L.w4a4_gemm_workspace_bytes(16, 5120, 17408) == 1280 + 4 * 16 * 5120 * 4
     assert L.w4a4_gemm_workspace_bytes(17, 64, 33) == 0
     assert g(P(A), P(A), P(A), P(A), 64, 64, 64, 64, None, need, None) == INVALID
     assert g(P(A), P(A), P(A), P(A), 64, 64, 64, 64, P(A + 16), need, None) == MISALIGNED

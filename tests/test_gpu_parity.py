@@ -346,6 +346,30 @@ def test_small_m_split_k_shared_workspace(ops):
             assert np.array_equal(y, fresh)
 
 
+def test_small_m_split_k_random_workspace(ops):
+    """The tiles' arrival words of a K split start from whatever the workspace
+    holds: random bytes there give the same outputs as a fresh workspace, bit
+    for bit, on this call and on the next ones (each call leaves the words at
+    zero and tags them with its own ticket)."""
+    import torch
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    for i, (m, n, k) in enumerate([(16, 1024, 5120), (5, 5120, 17408)]):
+        need = ops.gemm_workspace_bytes(m, n, k)
+        assert need > 0
+        w, x = _problem(m, n, k, 400 + i)
+        packed = ops.prepare_weights(dev(w))
+        c, s = ops.rotate_quantize_act(dev(x))
+        fresh = host(ops.gemm(packed, c, s, n, k))
+        ws = torch.randint(0, 256, (need,), dtype=torch.uint8, generator=gen).to("cuda:0")
+        for rep in range(3):
+            say(f"random workspace m={m} n={n} k={k} rep {rep}")
+            y = host(ops.gemm(packed, c, s, n, k, workspace=ws))
+            assert np.array_equal(y, fresh)
+        # the arrival words are back at zero after every call
+        words = ws[: (n + 31) // 32 * 8].cpu().numpy()
+        assert not words.any()
+
+
 def test_last_microbatch_302_rows(ops):
     k, n = 6144, 5120  # the output projection
     w = synth.weights(n, k, synth.rng_for(0, 3, 3))
