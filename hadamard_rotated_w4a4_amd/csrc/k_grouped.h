@@ -17,8 +17,8 @@
 // blocks' scale products s (x) d (the split operands the dense kernel uses);
 // per output a convert and one fused multiply-add remain.  Codes enter as
 // 16 x nibble, so d is scaled by 2^-8.  Long K is staged in chunks of
-// GS_KCHUNK blocks, each chunk's loads issued while the previous chunk
-// streams.  Each workgroup scatters its rows to y.  Each XCD takes a
+// GS_KCHUNK blocks (half that for int8 activations), each chunk's loads
+// issued while the previous chunk streams.  Each workgroup scatters its rows to y.  Each XCD takes a
 // contiguous share of the expert-ordered items, so an expert's row tiles
 // share one L2 and read its weights from HBM about once.
 //
@@ -36,15 +36,18 @@ constexpr int GS_ROWS = 32;     // routed rows per item (one 32x32 MFMA tile)
 constexpr int GS_WAVES = 8;     // waves per workgroup, one column tile each
 constexpr int GS_KCHUNK = 32;   // blocks of activations staged per pass (a multiple of 4)
 // per staged block: 32 rows x 32 int8 codes (1 KB), 32 scale operands (256 B)
-constexpr int GS_STAGE_BYTES = GS_KCHUNK * (GS_ROWS * QK + GS_ROWS * 8);
+// Blocks per pass: int8 activations (A8) stage half as many, so that the
+// next pass's loads, held in registers, fit beside the weight ring without
+// spilling.
+constexpr int gs_kchunk(bool a8) { return a8 ? GS_KCHUNK / 2 : GS_KCHUNK; }
 
 // Column tiles per wave and item: two when K fits one staging pass (the
 // staged activations then serve twice as many columns), else one.
-__host__ inline int grouped_tiles_per_wave(int64_t n, int64_t k) {
-    return k / QK <= GS_KCHUNK && padded_n(n) / TILE_N > GS_WAVES ? 2 : 1;
+__host__ inline int grouped_tiles_per_wave(int64_t n, int64_t k, bool a8 = false) {
+    return k / QK <= gs_kchunk(a8) && padded_n(n) / TILE_N > GS_WAVES ? 2 : 1;
 }
-__host__ inline int64_t grouped_col_chunks(int64_t n, int64_t k) {
-    const int64_t per = (int64_t)GS_WAVES * grouped_tiles_per_wave(n, k);
+__host__ inline int64_t grouped_col_chunks(int64_t n, int64_t k, bool a8 = false) {
+    const int64_t per = (int64_t)GS_WAVES * grouped_tiles_per_wave(n, k, a8);
     return (padded_n(n) / TILE_N + per - 1) / per;
 }
 
@@ -66,7 +69,8 @@ struct GsArgs {
 template <bool A8>
 __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(GsArgs a) {  // 4 waves per SIMD: two workgroups per CU
     constexpr int ROW_BYTES = A8 ? QK : QK / 2;  // activation code bytes per (row, block)
-    __shared__ __attribute__((aligned(16))) uint8_t smem[GS_STAGE_BYTES];
+    constexpr int KCHUNK = gs_kchunk(A8);
+    __shared__ __attribute__((aligned(16))) uint8_t smem[KCHUNK * (GS_ROWS * QK + GS_ROWS * 8)];
     __shared__ int64_t src_row[GS_ROWS];
     __shared__ int32_t out_row[GS_ROWS];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -112,14 +116,14 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
     const int g = lane >> 5, r32 = lane & 31;  // K half and row / column of this lane
     v16f acc;
     uint4 *codes16 = reinterpret_cast<uint4 *>(smem);                                  // [block][g][row]
-    uint2 *sop = reinterpret_cast<uint2 *>(smem + GS_KCHUNK * GS_ROWS * QK);            // [block][row]
+    uint2 *sop = reinterpret_cast<uint2 *>(smem + KCHUNK * GS_ROWS * QK);               // [block][row]
 
     // Activations of a chunk: thread t stages entries (row, block) t and
-    // t + 64 GS_WAVES of the chunk's GS_KCHUNK x GS_ROWS; their loads are
+    // t + 64 GS_WAVES of the chunk's KCHUNK x GS_ROWS; their loads are
     // issued one chunk ahead, into registers, so that they overlap the
     // previous chunk's stream.  Rows past the expert's count and blocks past
     // nb are zero.
-    constexpr int NT = 64 * GS_WAVES, PER = GS_KCHUNK * GS_ROWS / NT;
+    constexpr int NT = 64 * GS_WAVES, PER = KCHUNK * GS_ROWS / NT;
     struct Stage {
         uint4 u[PER], u1[A8 ? PER : 1];
         float s[PER];
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
         pair(bl + 2, R.c1[0], R.c1[1], R.c1[2], R.c1[3], (uint16_t)(R.d >> 16));
     };
 
-    constexpr int RPC = GS_KCHUNK / SQ_BLOCKS;  // records per chunk (even)
+    constexpr int RPC = KCHUNK / SQ_BLOCKS;  // records per chunk (even)
     // The wave's tt-th column tile: of the item's tiles_per_wave rounds of
     // GS_WAVES (a last chunk's extra waves stream the last tile again and
     // store nothing).
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
             scatter(tile_of(tt));
         }
     } else {
-        // passes of GS_KCHUNK blocks, the next pass's loads issued during
+        // passes of KCHUNK blocks, the next pass's loads issued during
         // this one's stream; the weight ring runs across the passes
         set_tile(tile_of(0));
         load(0, q0);

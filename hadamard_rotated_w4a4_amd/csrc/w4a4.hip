@@ -578,7 +578,7 @@ w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float 
         return hip_status("gemm_small_m_kernel<a8>");
     }
     // m > 16: the streaming kernel, all rows as one group
-    const int64_t col_chunks = grouped_col_chunks(n, k);
+    const int64_t col_chunks = grouped_col_chunks(n, k, true);
     const int64_t items = (m + GS_ROWS - 1) / GS_ROWS * col_chunks;
     if (!grid_fits((items + 8) * 64 * GS_WAVES)) return W4A4_ERR_INVALID_VALUE;
     GsArgs a{};
@@ -593,7 +593,7 @@ w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float 
     a.top_k = 1;
     a.per_slot = 1;
     a.col_chunks = col_chunks;
-    a.tiles_per_wave = grouped_tiles_per_wave(n, k);
+    a.tiles_per_wave = grouped_tiles_per_wave(n, k, true);
     gemm_grouped_stream_kernel<true><<<(unsigned)((items + 7) / 8 * 8), 64 * GS_WAVES, 0, s>>>(a);
     return hip_status("gemm_grouped_stream_kernel<a8>");
 }
