@@ -419,6 +419,27 @@ def test_split_k_whole_tiles_sampled_rows(ops, m, k, name):
     assert_rows_close(y[rows], oracle.gemm(oracle.prepare_weights(w), rc, rs, k), name)
 
 
+def test_split_k_whole_tiles_random_workspace(ops):
+    """Split K over whole tiles (the o projection, M = 512: 40 tiles) on a
+    workspace of random bytes: every call equals one on a fresh workspace bit
+    for bit."""
+    import torch
+    m, n, k = 512, 5120, 6144
+    need = ops.gemm_workspace_bytes(m, n, k)
+    assert ops.gemm_prepared_workspace_bytes(m, n, k) > 0
+    rng = np.random.default_rng(21)
+    w = synth.weights(n, k, rng)
+    x = synth.activations(m, k, rng, k // 100)
+    packed = ops.prepare_weights(dev(w))
+    c, s = ops.rotate_quantize_act(dev(x))
+    fresh = host(ops.gemm(packed, c, s, n, k))
+    gen = torch.Generator(device="cpu").manual_seed(12)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, generator=gen).to("cuda:0")
+    for rep in range(3):
+        say(f"split K random workspace m={m} n={n} k={k} rep {rep}")
+        assert np.array_equal(host(ops.gemm(packed, c, s, n, k, workspace=ws)), fresh)
+
+
 def test_split_k_many_splits_small_m(ops):
     """m = 100, n = 1000 (8 tiles), K = 32768: 16 splits of 16 stage pairs;
     sampled rows against the oracle, and exact integer sums with unit scales."""
