@@ -787,7 +787,7 @@ def main():
                     help="first run 5 plain device copies of this many MiB (scales rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the GEMM would shard over N with no exchange).", file=sys.stderr)
         sys.exit(2)
 
