@@ -68,6 +68,11 @@ __device__ __forceinline__ uint32_t opaque_identity_selector() {
 __device__ __forceinline__ v16f mfma_block(v8i a, v8i b, int sel) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, v16f{}, 2, 2, 0, sel, 0, sel);
 }
+// A8: S / 64 of a block from its two planes (a: h in lane group 0, l in lane
+// group 1; b: the block's weights in both): the h lanes' block scale is 2^4.
+__device__ __forceinline__ v16f mfma_block8(v8i a, v8i b, int g) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, v16f{}, 2, 2, 0, g ? 127 : 131, 0, 127);
+}
 
 // ---------------------------------------------------------------------------
 // Activation pre-pass: int4 codes [m][k/2] + fp32 scales [m][k/32] -> operand
@@ -117,6 +122,45 @@ __global__ __launch_bounds__(256) void act_operand_kernel(const uint8_t *__restr
                      (int)(row % 32));
 }
 
+// A8 pre-pass: int8 codes [m][k] + fp32 scales [m][k/32] -> two planes of
+// operand records per row tile, [ceil(m/32)][2][nbp][1 KB]: plane 0 holds the
+// h codes of every code a = 16 h + l (h = (a + 8) >> 4, l = a - 16 h) with
+// the scale operand at [768, 1024), plane 1 the l codes with a zero scale
+// operand.  One thread per (row, padded block); padding rows and blocks are
+// zero.
+__global__ __launch_bounds__(256) void act8_operand_kernel(const int8_t *__restrict__ codes,
+                                                           const float *__restrict__ scales, int64_t m,
+                                                           int64_t k, uint8_t *__restrict__ ws) {
+    const int64_t nb = k / QK, nbp = mx_blocks(k);
+    const int64_t rows = (m + 31) / 32 * 32;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= rows * nbp) return;
+    const int64_t b = gid / rows, row = gid % rows;  // consecutive threads: consecutive rows of one block
+    uint32_t wh[6] = {0, 0, 0, 0, 0, 0}, wl[6] = {0, 0, 0, 0, 0, 0};
+    uint2 sop = make_uint2(0, 0);
+    if (row < m && b < nb) {
+        const uint4 *q = reinterpret_cast<const uint4 *>(codes + row * k + b * QK);
+        const uint4 q0 = q[0], q1 = q[1];
+        const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        uint32_t fh[32], fl[32];
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            const int a = (int)(int8_t)(qw[j >> 2] >> (8 * (j & 3)));
+            const int h = (a + 8) >> 4;  // floor: h in [-8, 8], a - 16 h in [-8, 7]
+            fh[j] = fp6_e2m3_of(h);
+            fl[j] = fp6_e2m3_of(a - 16 * h);
+        }
+        pack_fp6x32(fh, wh);
+        pack_fp6x32(fl, wl);
+        sop = act_scale_operand(scales[row * nb + b]);
+    }
+    uint8_t *rh = ws + (((row / 32) * 2 + 0) * nbp + b) * MX_REC, *rl = ws + (((row / 32) * 2 + 1) * nbp + b) * MX_REC;
+    put_mx_row(rh, (int)(row % 32), wh);
+    reinterpret_cast<uint2 *>(rh + MX_CODE_BYTES)[row % 32] = sop;
+    put_mx_row(rl, (int)(row % 32), wl);
+    reinterpret_cast<uint2 *>(rl + MX_CODE_BYTES)[row % 32] = make_uint2(0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // The GEMM.
 // ---------------------------------------------------------------------------
@@ -129,14 +173,28 @@ struct MxArgs {
     float *partial = nullptr;  // splits > 1: [splits][m][n] partial sums
 };
 
-template <int BKB_, int NS_, int TM_, int TN_>
+// A8: int8 activation codes (the exact int8 path on a rotated file).  Every
+// code a is 16 h + l with h = (a + 8) >> 4 in [-8, 8] and l in [-8, 7], both
+// exact in E2M3; a row tile's records come in two planes (act8_operand_kernel),
+// and one operand register set holds the h plane of a block in lanes 0..31
+// and its l plane in lanes 32..63, against the block's weights in both lane
+// groups.  One FP6 MFMA with the E8M0 scale 2^4 (byte 131) on the h lanes
+// then gives 16 S_h + S_l = S, the integer dot of the int8 codes (over 64),
+// exactly (|S| <= 127 * 8 * 32): a block costs one block-dot MFMA, as in
+// W4A4, with no lanes masked.  Stages are one block (BKB = 1) and the scale
+// products single-block 32x32x8 bf16 MFMAs (the l plane's scale operand is
+// zero, so the second lane group adds nothing).
+template <int BKB_, int NS_, int TM_, int TN_, bool A8_ = false>
 struct MxCfg {
     static constexpr int BKB = BKB_, NS = NS_;
     static constexpr int TM = TM_, TN = TN_, WM = 2, WN = 2, NT = 256;
     static constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     static constexpr int RT = BM / 32, CT = BN / 32;
-    static constexpr int STAGE_BYTES = (RT + CT) * BKB * MX_REC;
-    static constexpr int DMA_PER_STAGE = (RT + CT) * BKB;  // 1 KB each
+    static constexpr bool A8 = A8_;
+    static constexpr int AP = A8 ? 2 : 1;  // activation record planes per row tile
+    static_assert(A8 ? BKB == 1 : BKB == 2, "W4A4: two blocks per operand set; A8: the two planes of one");
+    static constexpr int STAGE_BYTES = (RT * AP + CT) * BKB * MX_REC;
+    static constexpr int DMA_PER_STAGE = (RT * AP + CT) * BKB;  // 1 KB each
     static constexpr int DMA_PER_WAVE = DMA_PER_STAGE / 4;
     static_assert(DMA_PER_STAGE % 4 == 0, "loads split evenly over the 4 waves");
     static_assert(MX_BLOCK_PAD % BKB == 0, "stages tile the padded block range");
@@ -202,16 +260,18 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
 
     // ---- this wave's loads: DMA_PER_WAVE records of 1 KB per stage ----
     // load i = wave * DMA_PER_WAVE + d covers tile i / BKB (row tiles first,
-    // then column tiles), block i % BKB of the stage.  Tiles past the matrix
-    // edge are clamped to the last one (their outputs are never stored).
+    // each with its AP planes, then column tiles), block i % BKB of the stage.
+    // Tiles past the matrix edge are clamped to the last one (their outputs
+    // are never stored).
+    constexpr int AP = C::AP;
     const uint8_t *src[C::DMA_PER_WAVE];
     uint32_t dst[C::DMA_PER_WAVE];
     const uint32_t smem_base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)smem;
 #pragma unroll
     for (int d = 0; d < C::DMA_PER_WAVE; d++) {
         const int i = wave * C::DMA_PER_WAVE + d, t = i / BKB, bb = i % BKB;
-        const uint8_t *base = t < RT ? a.act + min(rt0 + t, rtiles - 1) * nbp * MX_REC
-                                     : a.wrec + min(ct0 + t - RT, ctiles - 1) * nbp * MX_REC;
+        const uint8_t *base = t < RT * AP ? a.act + (min(rt0 + t / AP, rtiles - 1) * AP + t % AP) * nbp * MX_REC
+                                          : a.wrec + min(ct0 + t - RT * AP, ctiles - 1) * nbp * MX_REC;
         src[d] = uniform_ptr(base + bb * MX_REC);
         dst[d] = (uint32_t)((t * BKB + bb) * MX_REC);
     }
@@ -254,7 +314,6 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
     // use).  At step BAR of stage s the wait + barrier publish stage s + 1 and
     // the slot of stage s - 1 (read during stage s - 1) is refilled.  The
     // pipeline never drains at a stage boundary.
-    static_assert(BKB == 2, "one operand register set carries a stage's two blocks");
     static_assert(NS >= 3, "one stage in flight besides the two in use");
     constexpr int STEPS = TM * TN;
     static_assert(STEPS % 2 == 0, "the result buffers alternate by step parity");
@@ -267,15 +326,16 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
     const int sel0 = g ? 0 : 127, sel1 = g ? 127 : 0;  // E8M0 lane masks of blocks 0 and 1
     const uint32_t id_sel = opaque_identity_selector();
     // Operand reads of one row tile (i) or column tile (j) of a stage; lane
-    // group g reads block g's record.
+    // group g reads block g's record (A8: plane g's of the stage's block, and
+    // both groups the block's weight record).
     auto load_a = [&](const uint8_t *st, int i) {
-        const uint8_t *rec = st + ((wm * TM + i) * BKB + g) * MX_REC, *p = rec + 8 * c;
+        const uint8_t *rec = st + ((wm * TM + i) * AP * BKB + g) * MX_REC, *p = rec + 8 * c;
         af[i] = fp6_operand(lds_read<u32x2>(p), lds_read<u32x2>(p + 256), lds_read<u32x2>(p + 512));
         const u32x2 sp = lds_read<u32x2>(rec + MX_CODE_BYTES + 8 * c);
         ap[i] = make_uint2(sp.x, sp.y);
     };
     auto load_b = [&](const uint8_t *st, int j) {
-        const uint8_t *rec = st + ((RT + wn * TN + j) * BKB + g) * MX_REC, *p = rec + 8 * c;
+        const uint8_t *rec = st + ((RT * AP + wn * TN + j) * BKB + (C::A8 ? 0 : g)) * MX_REC, *p = rec + 8 * c;
         bf[j] = fp6_operand(lds_read<u32x2>(p), lds_read<u32x2>(p + 256), lds_read<u32x2>(p + 512));
         bw[j] = lds_read<uint32_t>(rec + MX_CODE_BYTES + 4 * c);
     };
@@ -298,54 +358,96 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
     for (int x = 0; x < NS - 1; x++) issue(x, x);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 2)) : "memory");
     __syncthreads();
-    v16f S0[2], S1[2];
-    v32f P[2];
+    if constexpr (C::A8) {
+        // A8: one block per stage, one FP6 MFMA and one single-block scale
+        // product per tile, the same pipeline otherwise (the scale operand
+        // of lane group 1 is the l plane record's zeros)
+        v16f S[2], P[2];
+        auto mfma_p8 = [&](int i, int j) { return mfma_bf16_32x32x8(ap[i], dup_at_use(bw[j], id_sel)); };
 #pragma unroll
-    for (int p = 0; p < PARTS; p++) load_part(smem, p);
-    P[0] = mfma_p(0, 0);
-    S0[0] = mfma_block(af[0], bf[0], sel0);
-    S1[0] = mfma_block(af[0], bf[0], sel1);
+        for (int p = 0; p < PARTS; p++) load_part(smem, p);
+        P[0] = mfma_p8(0, 0);
+        S[0] = mfma_block8(af[0], bf[0], g);
 
-    for (int s = 0; s < nstages; s++) {
+        for (int s = 0; s < nstages; s++) {
 #pragma unroll
-        for (int t = 0; t < STEPS; t++) {
-            const int i = t / TN, j = t % TN, b = t & 1, b1 = b ^ 1;
-            if (t == BAR) {
-                // stage s + 1 has landed for this wave; after the barrier for
-                // every wave, and stage s - 1's slot is free.  (After the last
-                // stage the reads below see a reloaded stage; the MFMAs they
-                // feed are never consumed.)
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 3)) : "memory");
-                __syncthreads();
+            for (int t = 0; t < STEPS; t++) {
+                const int i = t / TN, j = t % TN, b = t & 1, b1 = b ^ 1;
+                if (t == BAR) {
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 3)) : "memory");
+                    __syncthreads();
+                }
+                if (t >= BAR) {
+                    const int q = t - BAR;
+#pragma unroll
+                    for (int d = q * C::DMA_PER_WAVE / SPAN; d < (q + 1) * C::DMA_PER_WAVE / SPAN; d++)
+                        issue_one(s + NS - 1, (s + NS - 1) % NS, d);
+                }
+                const int t1 = (t + 1) % STEPS, i1 = t1 / TN, j1 = t1 % TN;
+                P[b1] = mfma_p8(i1, j1);
+#pragma unroll
+                for (int v = 0; v < 8; v++) acc[i][j][v] = fmaf(S[b][v], P[b][v], acc[i][j][v]);
+                __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);
+                S[b1] = mfma_block8(af[i1], bf[j1], g);
+#pragma unroll
+                for (int p = 0; p < PARTS; p++)
+                    if (last_issue(p) == t) load_part(smem + ((s + 1) % NS) * C::STAGE_BYTES, p);
+#pragma unroll
+                for (int v = 8; v < 16; v++) acc[i][j][v] = fmaf(S[b][v], P[b][v], acc[i][j][v]);
+                asm volatile("" : "+v"(acc[i][j]));
+                __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);
             }
-            if (t >= BAR) {  // refill stage s - 1's slot, spread over the steps
-                const int q = t - BAR;
+        }
+    } else {
+        v16f S0[2], S1[2];
+        v32f P[2];
 #pragma unroll
-                for (int d = q * C::DMA_PER_WAVE / SPAN; d < (q + 1) * C::DMA_PER_WAVE / SPAN; d++)
-                    issue_one(s + NS - 1, (s + NS - 1) % NS, d);
+        for (int p = 0; p < PARTS; p++) load_part(smem, p);
+        P[0] = mfma_p(0, 0);
+        S0[0] = mfma_block(af[0], bf[0], sel0);
+        S1[0] = mfma_block(af[0], bf[0], sel1);
+
+        for (int s = 0; s < nstages; s++) {
+#pragma unroll
+            for (int t = 0; t < STEPS; t++) {
+                const int i = t / TN, j = t % TN, b = t & 1, b1 = b ^ 1;
+                if (t == BAR) {
+                    // stage s + 1 has landed for this wave; after the barrier for
+                    // every wave, and stage s - 1's slot is free.  (After the last
+                    // stage the reads below see a reloaded stage; the MFMAs they
+                    // feed are never consumed.)
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 3)) : "memory");
+                    __syncthreads();
+                }
+                if (t >= BAR) {  // refill stage s - 1's slot, spread over the steps
+                    const int q = t - BAR;
+#pragma unroll
+                    for (int d = q * C::DMA_PER_WAVE / SPAN; d < (q + 1) * C::DMA_PER_WAVE / SPAN; d++)
+                        issue_one(s + NS - 1, (s + NS - 1) % NS, d);
+                }
+                // the MFMAs of tile t + 1 (of stage s + 1 after the last step) ...
+                const int t1 = (t + 1) % STEPS, i1 = t1 / TN, j1 = t1 % TN;
+                P[b1] = mfma_p(i1, j1);
+#pragma unroll
+                for (int v = 0; v < 11; v++) acc[i][j][v] = fmaf(S0[b][v], P[b][v], acc[i][j][v]);
+                __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);  // scalar and global-to-LDS ops may move
+                S0[b1] = mfma_block(af[i1], bf[j1], sel0);
+#pragma unroll
+                for (int v = 11; v < 16; v++) acc[i][j][v] = fmaf(S0[b][v], P[b][v], acc[i][j][v]);
+#pragma unroll
+                for (int v = 0; v < 6; v++) acc[i][j][v] = fmaf(S1[b][v], P[b][16 + v], acc[i][j][v]);
+                __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);
+                S1[b1] = mfma_block(af[i1], bf[j1], sel1);
+                // ... then the operands they were the last to take, for stage s + 1
+#pragma unroll
+                for (int p = 0; p < PARTS; p++)
+                    if (last_issue(p) == t) load_part(smem + ((s + 1) % NS) * C::STAGE_BYTES, p);
+                // ... while the multiply-adds of tile t finish
+#pragma unroll
+                for (int v = 6; v < 16; v++) acc[i][j][v] = fmaf(S1[b][v], P[b][16 + v], acc[i][j][v]);
+                asm volatile("" : "+v"(acc[i][j]));  // materialised here, not sunk past the loop's end
+                __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);
             }
-            // the MFMAs of tile t + 1 (of stage s + 1 after the last step) ...
-            const int t1 = (t + 1) % STEPS, i1 = t1 / TN, j1 = t1 % TN;
-            P[b1] = mfma_p(i1, j1);
-#pragma unroll
-            for (int v = 0; v < 11; v++) acc[i][j][v] = fmaf(S0[b][v], P[b][v], acc[i][j][v]);
-            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);  // scalar and global-to-LDS ops may move
-            S0[b1] = mfma_block(af[i1], bf[j1], sel0);
-#pragma unroll
-            for (int v = 11; v < 16; v++) acc[i][j][v] = fmaf(S0[b][v], P[b][v], acc[i][j][v]);
-#pragma unroll
-            for (int v = 0; v < 6; v++) acc[i][j][v] = fmaf(S1[b][v], P[b][16 + v], acc[i][j][v]);
-            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);
-            S1[b1] = mfma_block(af[i1], bf[j1], sel1);
-            // ... then the operands they were the last to take, for stage s + 1
-#pragma unroll
-            for (int p = 0; p < PARTS; p++)
-                if (last_issue(p) == t) load_part(smem + ((s + 1) % NS) * C::STAGE_BYTES, p);
-            // ... while the multiply-adds of tile t finish
-#pragma unroll
-            for (int v = 6; v < 16; v++) acc[i][j][v] = fmaf(S1[b][v], P[b][16 + v], acc[i][j][v]);
-            asm volatile("" : "+v"(acc[i][j]));  // materialised here, not sunk past the loop's end
-            __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still be writing LDS at exit
@@ -377,12 +479,14 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
 // streams its own operand records through its own LDS ring (no barrier until
 // the reduction), two MFMAs and 16 multiply-adds per block as above.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_>
+template <int BM_, int BN_, bool A8_ = false>
 struct MxPieceCfg {
     static constexpr int BM = BM_, BN = BN_;                 // tile shape of the main kernel
     static constexpr int PIECES = (BM / 32) * (BN / 32);     // 32x32 pieces per leftover tile
-    static constexpr int BKB = 2, NS = 4, NT = 256;          // per wave: NS stages of BKB blocks
-    static constexpr int WAVE_RING = NS * BKB * 2 * MX_REC;  // per stage: A records of its blocks, then B's
+    static constexpr bool A8 = A8_;
+    static constexpr int AP = A8 ? 2 : 1;                    // activation planes (see MxCfg)
+    static constexpr int BKB = A8 ? 1 : 2, NS = 4, NT = 256; // per wave: NS stages of BKB blocks
+    static constexpr int WAVE_RING = NS * BKB * (AP + 1) * MX_REC;  // per stage: A records (each plane), then B's
 };
 
 template <class C>
@@ -400,7 +504,8 @@ __device__ __forceinline__ void mx_piece(const MxArgs &a, int64_t first_tile, in
     const int sub = (int)(id % C::PIECES);
     const int64_t rt = by * (C::BM / 32) + sub / (C::BN / 32), ct = bx * (C::BN / 32) + sub % (C::BN / 32);
     // pieces past the matrix edge compute on clamped tiles and store nothing
-    const uint8_t *arec = uniform_ptr(a.act + min(rt, rtiles - 1) * nbp * MX_REC);
+    constexpr int AP = C::AP;
+    const uint8_t *arec = uniform_ptr(a.act + min(rt, rtiles - 1) * AP * nbp * MX_REC);  // (A8: the l plane follows)
     const uint8_t *brec = uniform_ptr(a.wrec + min(ct, ctiles - 1) * nbp * MX_REC);
 
     // this wave's quarter of the blocks, in whole stages
@@ -414,16 +519,17 @@ __device__ __forceinline__ void mx_piece(const MxArgs &a, int64_t first_tile, in
     auto issue = [&](int stage, int slot) {
         // past the last stage the ring reloads the last one (never computed)
         const int64_t kb0 = (s_begin + min(stage, max(nst - 1, 0))) * BKB;
-        const uint32_t lds = ring_lds + slot * BKB * 2 * MX_REC;
+        const uint32_t lds = ring_lds + slot * BKB * (AP + 1) * MX_REC;
 #pragma unroll
         for (int bb = 0; bb < BKB; bb++) {
-            dma16s(arec + (kb0 + bb) * MX_REC, voff, lds + bb * MX_REC);
-            dma16s(brec + (kb0 + bb) * MX_REC, voff, lds + (BKB + bb) * MX_REC);
+#pragma unroll
+            for (int pl = 0; pl < AP; pl++)
+                dma16s(arec + (pl * nbp + kb0 + bb) * MX_REC, voff, lds + (pl * BKB + bb) * MX_REC);
+            dma16s(brec + (kb0 + bb) * MX_REC, voff, lds + (AP * BKB + bb) * MX_REC);
         }
     };
     const int sel0 = g ? 0 : 127, sel1 = g ? 127 : 0;  // E8M0 lane masks of blocks 0 and 1
     const uint32_t id_sel = opaque_identity_selector();
-    static_assert(BKB == 2, "one operand register set carries a stage's two blocks");
 
     v16f acc;
 #pragma unroll
@@ -436,8 +542,8 @@ __device__ __forceinline__ void mx_piece(const MxArgs &a, int64_t first_tile, in
     v8i af, bf;
     uint2 ap;
     uint32_t bw;
-    auto load = [&](const uint8_t *st) {
-        const uint8_t *pa = st + g * MX_REC, *pb = st + (BKB + g) * MX_REC;
+    auto load = [&](const uint8_t *st) {  // (A8: lane group g reads plane g, both the weights)
+        const uint8_t *pa = st + g * MX_REC, *pb = st + (AP * BKB + (C::A8 ? 0 : g)) * MX_REC;
         af = fp6_operand(lds_read<u32x2>(pa + 8 * c), lds_read<u32x2>(pa + 256 + 8 * c),
                          lds_read<u32x2>(pa + 512 + 8 * c));
         bf = fp6_operand(lds_read<u32x2>(pb + 8 * c), lds_read<u32x2>(pb + 256 + 8 * c),
@@ -446,7 +552,31 @@ __device__ __forceinline__ void mx_piece(const MxArgs &a, int64_t first_tile, in
         ap = make_uint2(sp.x, sp.y);
         bw = lds_read<uint32_t>(pb + MX_CODE_BYTES + 4 * c);
     };
-    if (nst > 0) {
+    if constexpr (C::A8) {
+        if (nst > 0) {
+            // A8: one block per stage, one FP6 MFMA and one single-block scale
+            // product per stage
+            constexpr int LOADS = (AP + 1) * BKB;  // per stage
+#pragma unroll
+            for (int x = 0; x < NS - 1; x++) issue(x, x);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS * (NS - 2)) : "memory");  // stage 0 has landed
+            load(ring);
+            v16f P = mfma_bf16_32x32x8(ap, dup_at_use(bw, id_sel)), S = mfma_block8(af, bf, g);
+            for (int s = 0; s < nst; s++) {
+                issue(s + NS - 1, (s + NS - 1) % NS);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS * (NS - 2)) : "memory");
+                load(ring + ((s + 1) % NS) * BKB * (AP + 1) * MX_REC);
+#pragma unroll
+                for (int v = 0; v < 16; v++) acc[v] = fmaf(S[v], P[v], acc[v]);
+                asm volatile("" : "+v"(acc));
+                __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
+                P = mfma_bf16_32x32x8(ap, dup_at_use(bw, id_sel));
+                S = mfma_block8(af, bf, g);
+                __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still be writing the ring
+        }
+    } else if (nst > 0) {
 #pragma unroll
         for (int x = 0; x < NS - 1; x++) issue(x, x);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * BKB * (NS - 2)) : "memory");  // stage 0 has landed
@@ -462,7 +592,7 @@ __device__ __forceinline__ void mx_piece(const MxArgs &a, int64_t first_tile, in
             // unused)
             issue(s + NS - 1, (s + NS - 1) % NS);
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * BKB * (NS - 2)) : "memory");
-            load(ring + ((s + 1) % NS) * BKB * 2 * MX_REC);
+            load(ring + ((s + 1) % NS) * BKB * (AP + 1) * MX_REC);
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[v] = fmaf(S0[v], P[v], acc[v]);
             __builtin_amdgcn_sched_barrier(0x0004 | 0x0010 | 0x0080);
@@ -499,7 +629,7 @@ __device__ __forceinline__ void mx_piece(const MxArgs &a, int64_t first_tile, in
 // the last whole tiles leave idle, without a second launch and its gap.
 template <class C>
 __global__ __launch_bounds__(C::NT) void gemm_mx_kernel(MxArgs a, int64_t main_wgs, int64_t first_piece_tile) {
-    using P = MxPieceCfg<C::BM, C::BN>;
+    using P = MxPieceCfg<C::BM, C::BN, C::A8>;
     static_assert(P::NT == C::NT, "one workgroup size for both kinds");
     constexpr int MAIN_LDS = C::NS * C::STAGE_BYTES, PIECE_LDS = 4 * P::WAVE_RING;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[MAIN_LDS > PIECE_LDS ? MAIN_LDS : PIECE_LDS];

@@ -17,14 +17,10 @@
 // blocks' scale products s (x) d (the split operands the dense kernel uses);
 // per output a convert and one fused multiply-add remain.  Codes enter as
 // 16 x nibble, so d is scaled by 2^-8.  Long K is staged in chunks of
-// GS_KCHUNK blocks (half that for int8 activations), each chunk's loads
-// issued while the previous chunk streams.  Each workgroup scatters its rows to y.  Each XCD takes a
+// GS_KCHUNK blocks, each chunk's loads issued while the previous chunk
+// streams.  Each workgroup scatters its rows to y.  Each XCD takes a
 // contiguous share of the expert-ordered items, so an expert's row tiles
 // share one L2 and read its weights from HBM about once.
-//
-// The same kernel runs a plain (dense) product as one "expert" holding every
-// row (no routing), and takes int8 activation codes (A8: the exact int8 path
-// on a rotated file, staged as they are; d is then scaled by 2^-4).
 #pragma once
 
 #include "common.h"
@@ -36,29 +32,25 @@ constexpr int GS_ROWS = 32;     // routed rows per item (one 32x32 MFMA tile)
 constexpr int GS_WAVES = 8;     // waves per workgroup, one column tile each
 constexpr int GS_KCHUNK = 32;   // blocks of activations staged per pass (a multiple of 4)
 // per staged block: 32 rows x 32 int8 codes (1 KB), 32 scale operands (256 B)
-// Blocks per pass: int8 activations (A8) stage half as many, so that the
-// next pass's loads, held in registers, fit beside the weight ring without
-// spilling.
-constexpr int gs_kchunk(bool a8) { return a8 ? GS_KCHUNK / 2 : GS_KCHUNK; }
+constexpr int GS_STAGE_BYTES = GS_KCHUNK * (GS_ROWS * QK + GS_ROWS * 8);
 
 // Column tiles per wave and item: two when K fits one staging pass (the
 // staged activations then serve twice as many columns), else one.
-__host__ inline int grouped_tiles_per_wave(int64_t n, int64_t k, bool a8 = false) {
-    return k / QK <= gs_kchunk(a8) && padded_n(n) / TILE_N > GS_WAVES ? 2 : 1;
+__host__ inline int grouped_tiles_per_wave(int64_t n, int64_t k) {
+    return k / QK <= GS_KCHUNK && padded_n(n) / TILE_N > GS_WAVES ? 2 : 1;
 }
-__host__ inline int64_t grouped_col_chunks(int64_t n, int64_t k, bool a8 = false) {
-    const int64_t per = (int64_t)GS_WAVES * grouped_tiles_per_wave(n, k, a8);
+__host__ inline int64_t grouped_col_chunks(int64_t n, int64_t k) {
+    const int64_t per = (int64_t)GS_WAVES * grouped_tiles_per_wave(n, k);
     return (padded_n(n) / TILE_N + per - 1) / per;
 }
 
 struct GsArgs {
-    const uint8_t *codes;    // activation codes [rows][k/2] (A8: [rows][k])
+    const uint8_t *codes;    // activation codes [rows][k/2]
     const float *scales;     // activation scales [rows][k/32]
     const uint8_t *packed;   // packed weights of expert 0; expert e at + e * expert_bytes
     int64_t expert_bytes;
-    float *y;                // [n_tokens * top_k][n] (dense: [rows][ldy])
+    float *y;                // [n_tokens * top_k][n]
     int64_t ldy, n, k;
-    int64_t dense_rows;      // >= 0: a plain product of this many rows, no routing
     Routing g;
     int top_k, per_slot;     // activation row of routed row i: i (per slot) or i / top_k
     int64_t n_rows;          // routed rows (tokens x slots); those past offsets[E] have invalid ids
@@ -66,11 +58,9 @@ struct GsArgs {
     int tiles_per_wave = 1;  // > 1 only when K fits one staging pass
 };
 
-template <bool A8>
 __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(GsArgs a) {  // 4 waves per SIMD: two workgroups per CU
-    constexpr int ROW_BYTES = A8 ? QK : QK / 2;  // activation code bytes per (row, block)
-    constexpr int KCHUNK = gs_kchunk(A8);
-    __shared__ __attribute__((aligned(16))) uint8_t smem[KCHUNK * (GS_ROWS * QK + GS_ROWS * 8)];
+    constexpr int ROW_BYTES = QK / 2;  // activation code bytes per (row, block)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[GS_STAGE_BYTES];
     __shared__ int64_t src_row[GS_ROWS];
     __shared__ int32_t out_row[GS_ROWS];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -78,10 +68,9 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
     const int64_t k = a.k, nb = k / QK, nq = sq_quads(k);
     const int64_t tiles = padded_n(a.n) / TILE_N;
 
-    const bool dense = a.dense_rows >= 0;
     // workgroup 0 first zeroes the output rows of invalid ids (the routing put
     // them after the valid rows), whatever item it takes after
-    if (!dense && blockIdx.x == 0) {
+    if (blockIdx.x == 0) {
         const int64_t first = a.g.offsets[a.g.n_expert], bad = a.n_rows - first;
         for (int64_t i = tid; i < bad * a.n; i += 64 * GS_WAVES)
             a.y[(int64_t)a.g.perm[first + i / a.n] * a.ldy + i % a.n] = 0.0f;
@@ -91,22 +80,22 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
     // items of one expert (row tiles x column chunks) are consecutive and
     // column-chunk-major, so a chunk's weights are read from HBM once and
     // then from the XCD's L2 by the expert's other row tiles.
-    const int64_t rtiles = dense ? (a.dense_rows + GS_ROWS - 1) / GS_ROWS : a.g.tile_prefix[a.g.n_expert];
+    const int64_t rtiles = a.g.tile_prefix[a.g.n_expert];
     const int64_t items = rtiles * a.col_chunks, per_xcd = (items + 7) / 8;
     const int64_t j = blockIdx.x / 8, item = (blockIdx.x % 8) * per_xcd + j;
     if (j >= per_xcd || item >= items) return;  // uniform
-    const int e = dense ? 0 : expert_of_tile(a.g, item / a.col_chunks);
-    const int64_t t0 = dense ? 0 : a.g.tile_prefix[e], ne = dense ? rtiles : a.g.tile_prefix[e + 1] - t0;
+    const int e = expert_of_tile(a.g, item / a.col_chunks);
+    const int64_t t0 = a.g.tile_prefix[e], ne = a.g.tile_prefix[e + 1] - t0;
     const int64_t local = item - t0 * a.col_chunks, cc = local / ne, rt_e = local % ne;
-    const int64_t cnt = dense ? a.dense_rows : a.g.offsets[e + 1] - a.g.offsets[e];
+    const int64_t cnt = a.g.offsets[e + 1] - a.g.offsets[e];
     const int64_t row_lo = rt_e * GS_ROWS;
     if (tid < GS_ROWS) {
         const int64_t lr = row_lo + tid;  // row within the expert
         int64_t src = -1;
         int32_t orow = -1;
         if (lr < cnt) {
-            orow = dense ? (int32_t)lr : a.g.perm[a.g.offsets[e] + lr];
-            src = dense || a.per_slot ? orow : orow / a.top_k;
+            orow = a.g.perm[a.g.offsets[e] + lr];
+            src = a.per_slot ? orow : orow / a.top_k;
         }
         src_row[tid] = src;
         out_row[tid] = orow;
@@ -116,16 +105,16 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
     const int g = lane >> 5, r32 = lane & 31;  // K half and row / column of this lane
     v16f acc;
     uint4 *codes16 = reinterpret_cast<uint4 *>(smem);                                  // [block][g][row]
-    uint2 *sop = reinterpret_cast<uint2 *>(smem + KCHUNK * GS_ROWS * QK);               // [block][row]
+    uint2 *sop = reinterpret_cast<uint2 *>(smem + GS_KCHUNK * GS_ROWS * QK);            // [block][row]
 
     // Activations of a chunk: thread t stages entries (row, block) t and
-    // t + 64 GS_WAVES of the chunk's KCHUNK x GS_ROWS; their loads are
+    // t + 64 GS_WAVES of the chunk's GS_KCHUNK x GS_ROWS; their loads are
     // issued one chunk ahead, into registers, so that they overlap the
     // previous chunk's stream.  Rows past the expert's count and blocks past
     // nb are zero.
-    constexpr int NT = 64 * GS_WAVES, PER = KCHUNK * GS_ROWS / NT;
+    constexpr int NT = 64 * GS_WAVES, PER = GS_KCHUNK * GS_ROWS / NT;
     struct Stage {
-        uint4 u[PER], u1[A8 ? PER : 1];
+        uint4 u[PER];
         float s[PER];
     } st;
     auto stage_load = [&](int64_t c0) {
@@ -134,12 +123,10 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
             const int i = tid + p * NT, bl = i / GS_ROWS, r = i % GS_ROWS;
             const int64_t b = c0 + bl, src = src_row[r];
             st.u[p] = make_uint4(0, 0, 0, 0);
-            if constexpr (A8) st.u1[p] = make_uint4(0, 0, 0, 0);
             st.s[p] = 0.0f;
             if (src >= 0 && b < nb) {
                 const uint4 *q = reinterpret_cast<const uint4 *>(a.codes + src * (k / 32 * ROW_BYTES) + b * ROW_BYTES);
                 st.u[p] = q[0];
-                if constexpr (A8) st.u1[p] = q[1];
                 st.s[p] = a.scales[src * nb + b];
             }
         }
@@ -150,15 +137,10 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
 #pragma unroll
         for (int p = 0; p < PER; p++) {
             const int i = tid + p * NT, bl = i / GS_ROWS, r = i % GS_ROWS;
-            if constexpr (A8) {
-                codes16[(bl * 2 + 0) * GS_ROWS + r] = st.u[p];   // codes 0..15
-                codes16[(bl * 2 + 1) * GS_ROWS + r] = st.u1[p];  // codes 16..31
-            } else {
-                const uint4 w = k8_words(st.u[p]);
-                const v4i h0 = widen_k8x2(w.x, w.y), h1 = widen_k8x2(w.z, w.w);
-                codes16[(bl * 2 + 0) * GS_ROWS + r] = make_uint4(h0[0], h0[1], h0[2], h0[3]);
-                codes16[(bl * 2 + 1) * GS_ROWS + r] = make_uint4(h1[0], h1[1], h1[2], h1[3]);
-            }
+            const uint4 w = k8_words(st.u[p]);
+            const v4i h0 = widen_k8x2(w.x, w.y), h1 = widen_k8x2(w.z, w.w);
+            codes16[(bl * 2 + 0) * GS_ROWS + r] = make_uint4(h0[0], h0[1], h0[2], h0[3]);
+            codes16[(bl * 2 + 1) * GS_ROWS + r] = make_uint4(h1[0], h1[1], h1[2], h1[3]);
             sop[bl * GS_ROWS + r] = act_scale_operand(st.s[p]);
         }
     };
@@ -179,7 +161,7 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
         R.d = __builtin_amdgcn_raw_buffer_load_b32(wbuf, d4, off, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    constexpr float UNSCALE = A8 ? 1.0f / 16.0f : 1.0f / 256.0f;  // the operands' 16 x factors
+    constexpr float UNSCALE = 1.0f / 256.0f;  // the operands' 16 x factors
     // blocks bl and bl + 1 of the chunk: (w0, w1) this lane's words of each,
     // dh its d of block bl + g
     auto pair = [&](int bl, uint32_t w00, uint32_t w01, uint32_t w10, uint32_t w11, uint16_t dh) {
@@ -200,7 +182,7 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
         pair(bl + 2, R.c1[0], R.c1[1], R.c1[2], R.c1[3], (uint16_t)(R.d >> 16));
     };
 
-    constexpr int RPC = KCHUNK / SQ_BLOCKS;  // records per chunk (even)
+    constexpr int RPC = GS_KCHUNK / SQ_BLOCKS;  // records per chunk (even)
     // The wave's tt-th column tile: of the item's tiles_per_wave rounds of
     // GS_WAVES (a last chunk's extra waves stream the last tile again and
     // store nothing).
@@ -254,7 +236,7 @@ __global__ __launch_bounds__(64 * GS_WAVES, 4) void gemm_grouped_stream_kernel(G
             scatter(tile_of(tt));
         }
     } else {
-        // passes of KCHUNK blocks, the next pass's loads issued during
+        // passes of GS_KCHUNK blocks, the next pass's loads issued during
         // this one's stream; the weight ring runs across the passes
         set_tile(tile_of(0));
         load(0, q0);

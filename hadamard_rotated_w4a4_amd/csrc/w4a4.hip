@@ -66,6 +66,11 @@ inline void launch_zero_rows(float *y, int64_t m, int64_t n, int64_t ldy, hipStr
 using Mx128x128 = MxCfg<2, 4, 2, 2>;
 using Mx128x64 = MxCfg<2, 4, 2, 1>;
 using Mx64x128 = MxCfg<2, 4, 1, 2>;
+// int8 activations (two FP6 planes in one operand set, one block per
+// stage): 128 x 128 and 64 x 128 tiles (a 128 x 64 stage would not split
+// into equal loads over the four waves)
+using Mx128x128A8 = MxCfg<1, 4, 2, 2, true>;
+using Mx64x128A8 = MxCfg<1, 4, 1, 2, true>;
 
 // Compute units of the current device (cached per device).
 int device_cus() {
@@ -96,8 +101,9 @@ int mx_occupancy() {  // resident workgroups per CU (registers and LDS decide)
 // when that is cheaper, are split into pieces (a piece is 1/PIECES of a tile
 // at about 1.6x the cost per output: no operand reuse across waves).  The
 // modelled time counts rounds x padded work per tile (the smaller tiles reuse
-// operands less: ~15% slower per output on MI355X); ties go to the shape that
-// pads less.
+// operands less: ~15% slower per output on MI355X, ~35% with int8 activations,
+// whose stages are one block and twice the activation records); ties go to the
+// shape that pads less.
 struct MxPlan {
     int64_t main_wgs, piece_wgs, first_piece_tile;
     double time, padded;
@@ -105,7 +111,7 @@ struct MxPlan {
 };
 template <class C>
 MxPlan mx_plan(int64_t m, int64_t n) {
-    using P = MxPieceCfg<C::BM, C::BN>;
+    using P = MxPieceCfg<C::BM, C::BN, C::A8>;
     const int64_t tm = (m + C::BM - 1) / C::BM, tn = (n + C::BN - 1) / C::BN, tiles = tm * tn;
     const int64_t slots = (int64_t)device_cus() * mx_occupancy<C>();
     const int64_t whole = tiles / slots * slots, left = tiles - whole;
@@ -116,7 +122,7 @@ MxPlan mx_plan(int64_t m, int64_t n) {
     p.main_wgs = pieces ? whole : tiles;
     p.piece_wgs = pieces ? left * P::PIECES : 0;
     p.first_piece_tile = whole;
-    p.time = rounds * C::BM * C::BN * (C::TM * C::TN == 4 ? 1.0 : 1.15);
+    p.time = rounds * C::BM * C::BN * (C::TM * C::TN == 4 ? 1.0 : C::A8 ? 1.35 : 1.15);
     p.padded = (double)(tm * C::BM) * (tn * C::BN);
     return p;
 }
@@ -170,6 +176,14 @@ void launch_mx(const MxArgs &a0, float *partial, hipStream_t s) {
     if (p0 <= p1 && p0 <= p2) launch_mx_cfg<Mx128x128>(a, p0, s);
     else if (p1 <= p2) launch_mx_cfg<Mx128x64>(a, p1, s);
     else launch_mx_cfg<Mx64x128>(a, p2, s);
+}
+
+// int8 activations at m > 16 (act: the two-plane records of act8_operand_kernel):
+// whole tiles and pieces as for W4A4, no K split.
+void launch_mx_a8(const MxArgs &a, hipStream_t s) {
+    const MxPlan p0 = mx_plan<Mx128x128A8>(a.m, a.n), p2 = mx_plan<Mx64x128A8>(a.m, a.n);
+    if (p0 <= p2) launch_mx_cfg<Mx128x128A8>(a, p0, s);
+    else launch_mx_cfg<Mx64x128A8>(a, p2, s);
 }
 
 // Size bounds, so that every launch fits the hardware's grid limits and the
@@ -534,7 +548,8 @@ w4a4_status w4a4_rotate_quantize_gemm(const void *x, w4a4_dtype dt, int64_t m, i
 
 size_t w4a4_gemm_a8_workspace_bytes(int64_t m, int64_t n, int64_t k) {
     if (m < 0 || n < 0 || k < 0 || k % QK) return 0;
-    if (n == 0 || k == 0 || m == 0 || m > SMALL_M_MAX) return 0;
+    if (n == 0 || k == 0 || m == 0) return 0;
+    if (m > SMALL_M_MAX) return up256_bytes(2 * (int64_t)w4a4_act_operand_bytes(m, k));  // the two-plane records
     return small_m_workspace_bytes(small_m_plan(n, k, true), m, n);  // the K splits' sums
 }
 
@@ -577,25 +592,27 @@ w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float 
             <<<dim3((unsigned)plan.tiles, (unsigned)plan.splits), 64 * SM_WAVES, small_m_lds_bytes(plan, true), s>>>(a);
         return hip_status("gemm_small_m_kernel<a8>");
     }
-    // m > 16: the streaming kernel, all rows as one group
-    const int64_t col_chunks = grouped_col_chunks(n, k, true);
-    const int64_t items = (m + GS_ROWS - 1) / GS_ROWS * col_chunks;
-    if (!grid_fits((items + 8) * 64 * GS_WAVES)) return W4A4_ERR_INVALID_VALUE;
-    GsArgs a{};
-    a.codes = c8;
-    a.scales = scales;
-    a.packed = static_cast<const uint8_t *>(packed_w);
+    // m > 16: the codes as two FP6 planes, then the matrix-core kernel
+    if (!workspace) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(workspace, 256)) return W4A4_ERR_MISALIGNED;
+    if (workspace_bytes < w4a4_gemm_a8_workspace_bytes(m, n, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
+    if ((m + 127) / 128 * ((n + 127) / 128) >= kMaxDenseTiles) return W4A4_ERR_INVALID_VALUE;
+    const int64_t rows = (m + 31) / 32 * 32, threads = rows * mx_blocks(k);
+    if (!grid_fits(threads)) return W4A4_ERR_INVALID_VALUE;
+    act8_operand_kernel<<<blocks_for(threads, 256), 256, 0, s>>>(codes, scales, m, k,
+                                                                 static_cast<uint8_t *>(workspace));
+    const w4a4_status st2 = hip_status("act8_operand_kernel");
+    if (st2 != W4A4_OK) return st2;
+    MxArgs a{};
+    a.act = static_cast<const uint8_t *>(workspace);
+    a.wrec = static_cast<const uint8_t *>(packed_w);  // the matrix-core section
     a.y = y;
     a.ldy = ldy;
+    a.m = m;
     a.n = n;
     a.k = k;
-    a.dense_rows = m;
-    a.top_k = 1;
-    a.per_slot = 1;
-    a.col_chunks = col_chunks;
-    a.tiles_per_wave = grouped_tiles_per_wave(n, k, true);
-    gemm_grouped_stream_kernel<true><<<(unsigned)((items + 7) / 8 * 8), 64 * GS_WAVES, 0, s>>>(a);
-    return hip_status("gemm_grouped_stream_kernel<a8>");
+    launch_mx_a8(a, s);
+    return hip_status("gemm_mx_kernel<a8>");
 }
 
 size_t w4a4_act_operand_bytes(int64_t m, int64_t k) {
@@ -810,7 +827,6 @@ w4a4_status w4a4_gemm_id_routed(const void *packed_w, int64_t n_expert, const ui
     a.ldy = n;
     a.n = n;
     a.k = k;
-    a.dense_rows = -1;
     a.g = Routing{reinterpret_cast<const int32_t *>(ws + 2 * up256((n_expert + 1) * 4)),
                   reinterpret_cast<const int32_t *>(ws), reinterpret_cast<const int32_t *>(ws + up256((n_expert + 1) * 4)),
                   (int)n_expert};
@@ -820,7 +836,7 @@ w4a4_status w4a4_gemm_id_routed(const void *packed_w, int64_t n_expert, const ui
     a.col_chunks = col_chunks;
     a.tiles_per_wave = grouped_tiles_per_wave(n, k);
     // a bound on the items (row tiles x column chunks), rounded up to whole XCD rows
-    gemm_grouped_stream_kernel<false><<<(unsigned)((row_tiles * col_chunks + 7) / 8 * 8), 64 * GS_WAVES, 0, s>>>(a);
+    gemm_grouped_stream_kernel<<<(unsigned)((row_tiles * col_chunks + 7) / 8 * 8), 64 * GS_WAVES, 0, s>>>(a);
     return hip_status("gemm_grouped_stream_kernel");
 }
 

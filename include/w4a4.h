@@ -284,10 +284,15 @@ w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, 
  *
  * w4a4_gemm_a8: y = sum_b d_w * s * S with S the exact integer dot of the
  * Q4_0 codes (q - 8) with the int8 codes.  Arguments as w4a4_gemm, with the
- * workspace of w4a4_gemm_a8_workspace_bytes (non-zero only for m <= 16 when
- * K is split: arrival words and partial sums as in w4a4_gemm; may be NULL
- * when 0).  m <= 16 streams the weights as w4a4_gemm
- * does; larger m runs the streaming kernel over 32-row groups.
+ * workspace of w4a4_gemm_a8_workspace_bytes (256-byte aligned, needs no
+ * clearing; may be NULL when 0): for m <= 16 non-zero only when K is split
+ * (arrival words and partial sums as in w4a4_gemm); for m > 16 the codes
+ * re-laid as two planes of FP6 matrix-core records (every code a = 16 h + l,
+ * h = (a + 8) >> 4 and l both exact in FP6), 2 * w4a4_act_operand_bytes(m, k)
+ * rounded up to 256.  m <= 16 streams the weights as w4a4_gemm does; larger
+ * m runs the FP6 matrix-core kernel with two block dots per block (the h
+ * plane's scaled by 2^4 through the instruction's block scale, the l plane's
+ * accumulated on it), so S is exact.
  */
 w4a4_status w4a4_rotate_quantize_act8(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
                                       int8_t *codes, float *scales, void *stream);

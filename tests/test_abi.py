@@ -105,10 +105,12 @@ def test_a8_validation(L):
     assert g(P(A), P(A + 8), P(A), P(A), 8, 64, 64, 64, None, 0, None) == MISALIGNED
     assert g(P(A), P(A), P(A), P(A), 8, 64, 64, 32, None, 0, None) == INVALID  # ldy < n
     assert g(None, None, None, None, 0, 64, 64, 64, None, 0, None) == OK
-    # m <= 16 with K split needs the partial-sum workspace; m > 16 needs none
+    # m <= 16 with K split needs the partial-sum workspace; m > 16 the codes'
+    # two FP6 planes (row tiles x 2 planes x 160 blocks x 1 KB)
     need = L.w4a4_gemm_a8_workspace_bytes(16, 1024, 5120)
     assert need > 0 and need % 256 == 0
-    assert L.w4a4_gemm_a8_workspace_bytes(64, 1024, 5120) == 0
+    assert L.w4a4_gemm_a8_workspace_bytes(64, 1024, 5120) == 2 * L.w4a4_act_operand_bytes(64, 5120) == 2 * 2 * 160 * 1024
+    assert L.w4a4_gemm_a8_workspace_bytes(65, 1024, 5120) == 2 * 3 * 160 * 1024
     assert L.w4a4_gemm_a8_workspace_bytes(16, 64, 33) == 0
     assert g(P(A), P(A), P(A), P(A), 16, 1024, 5120, 1024, None, 0, None) == INVALID
     assert g(P(A), P(A), P(A), P(A), 16, 1024, 5120, 1024, P(A), need - 1, None) == WS
