@@ -57,6 +57,9 @@ def lib() -> ctypes.CDLL:
             "w4a4_quantize_act": ([P, ST, I64, I64, I64, P, P, P], ST),
             "w4a4_gemm_a8_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_gemm_a8": ([P, P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
+            "w4a4_act8_operand_bytes": ([I64, I64], SZ),
+            "w4a4_rotate_quantize_prepare8": ([P, ST, I64, I64, I64, P, P, P, SZ, P], ST),
+            "w4a4_gemm_a8_prepared": ([P, P, P, I64, I64, I64, I64, P], ST),
             "w4a4_gemm_id": ([P, I64, P, P, I64, P, I64, I64, P, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_id_route": ([P, I64, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_id_routed": ([P, I64, P, P, I64, I64, I64, P, I64, I64, P, SZ, P], ST),
@@ -451,6 +454,36 @@ def gemm_a8(packed: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: 
     _check(lib().w4a4_gemm_a8(_ptr(packed), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, y.stride(0),
                               _ptr(workspace), 0 if workspace is None else workspace.numel(),
                               _stream(codes.device)), "w4a4_gemm_a8")
+    return y
+
+
+def act8_operand_bytes(m: int, k: int) -> int:
+    return int(lib().w4a4_act8_operand_bytes(m, k))
+
+
+def rotate_quantize_prepare8(x: torch.Tensor, act: torch.Tensor, k: int | None = None,
+                             codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """rotate_quantize_act8 that also writes the int8 matrix-core operand into `act`."""
+    dt, k = _act_dtype(x), _k_of(x, k)
+    _need(act, "act", torch.uint8, act8_operand_bytes(x.shape[0], k))
+    m, codes, scales = _quantiser_outputs(x, k, codes, scales, k, torch.int8)
+    _require_cuda(act)
+    _check(lib().w4a4_rotate_quantize_prepare8(_ptr(x), dt, m, k, x.stride(0), _ptr(codes), _ptr(scales),
+                                               _ptr(act), act.numel(), _stream(x.device)),
+           "w4a4_rotate_quantize_prepare8")
+    return codes, scales
+
+
+def gemm_a8_prepared(packed: torch.Tensor, act: torch.Tensor, m: int, n: int, k: int,
+                     y: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A8-H32 product on a prepared int8 operand: fp32 [m, n] (row stride y.stride(0))."""
+    _need(packed, "packed", torch.uint8, packed_weight_bytes(n, k) if m and n else 0)
+    _need(act, "act", torch.uint8, act8_operand_bytes(m, k))
+    _check_out(y, None, m, n, 0)
+    _require_cuda(packed, act, y)
+    y = _output(y, m, n, act.device)
+    _check(lib().w4a4_gemm_a8_prepared(_ptr(packed), _ptr(act), _ptr(y), m, n, k, y.stride(0),
+                                       _stream(act.device)), "w4a4_gemm_a8_prepared")
     return y
 
 

@@ -178,6 +178,25 @@ __device__ __forceinline__ void store_codes4(const int q[8], float s, int L, boo
     }
 }
 
+// Row r of a block's operand record (see common.h) from the quad that holds
+// the row: its 32 codes as one 192-bit string of fp6 fields, lane L's 8 codes
+// (fields f) at bit 48 L; lanes 0, 1, 2 write 64-bit parts 0, 1, 2 of the
+// string, lane 3 the scale operand `sop`.  Every lane of the quad must take
+// part (the parts cross lanes through a quad permute).
+__device__ __forceinline__ void put_quad_row(const uint32_t f[8], int L, uint8_t *rec, int r, uint2 sop) {
+    uint64_t mine = 0;
+#pragma unroll
+    for (int t = 0; t < 8; t++) mine |= (uint64_t)f[t] << (6 * t);
+    const uint64_t next = (uint64_t)quad_u32<QP_NEXT>((uint32_t)mine) |
+                          (uint64_t)quad_u32<QP_NEXT>((uint32_t)(mine >> 32)) << 32;
+    if (L < 3) {
+        const uint64_t part = L == 0 ? (mine | next << 48) : L == 1 ? (mine >> 16 | next << 32) : (mine >> 32 | next << 16);
+        reinterpret_cast<uint2 *>(rec + 256 * L)[r] = make_uint2((uint32_t)part, (uint32_t)(part >> 32));
+    } else {
+        reinterpret_cast<uint2 *>(rec + MX_CODE_BYTES)[r] = sop;
+    }
+}
+
 // One workgroup = 32 rows (row tile blockIdx.y) x 2 neighbouring blocks
 // (2 blockIdx.x and 2 blockIdx.x + 1), four lanes per (row, block): wave w
 // takes block w / 2 and rows 16 (w % 2) .. + 15, lane 4 i + L row i, elements
@@ -187,7 +206,11 @@ __device__ __forceinline__ void store_codes4(const int q[8], float s, int L, boo
 //
 // QMAX = 7: int4 codes (W4A4).  QMAX = 127: int8 codes for the exact int8
 // path on a rotated file (W4A8), one signed byte per element in `codes`
-// ([m][k]), same rotation, d = amax / 127; no operand record.
+// ([m][k]), same rotation, d = amax / 127; with `act` set, the operand
+// records of the int8 matrix-core product, two planes per row tile
+// ([row tile][plane][padded block][1 KB]): every code a = 16 h + l with
+// h = (a + 8) >> 4, plane 0 the h codes and the scale operand, plane 1 the l
+// codes and a zero scale operand.
 // ROTATE = false: the unrotated W4A4 ablation (section "MoE: W4A4 on the
 // experts"): no butterflies, and the stored scale is d itself (there is no
 // normalisation to fold in).
@@ -220,27 +243,28 @@ __global__ __launch_bounds__(128 * RQ_BLOCKS) void rotate_quantize_kernel(const 
             *reinterpret_cast<uint2 *>(codes + row * k + b * QK + 8 * L) = make_uint2(w0, w1);
             if (L == 0) scales[row * nb + b] = s;
         }
+        if (act && b < mx_blocks(k)) {
+            uint32_t fh[8], fl[8];
+#pragma unroll
+            for (int t = 0; t < 8; t++) {
+                const int h = (q[t] + 8) >> 4;  // floor: h in [-8, 8], q - 16 h in [-8, 7]
+                fh[t] = fp6_e2m3_of(h);
+                fl[t] = fp6_e2m3_of(q[t] - 16 * h);
+            }
+            uint8_t *rec = act + ((int64_t)blockIdx.y * 2 * mx_blocks(k) + b) * MX_REC;
+            put_quad_row(fh, L, rec, r, act_scale_operand(s));
+            put_quad_row(fl, L, rec + mx_blocks(k) * MX_REC, r, make_uint2(0, 0));
+        }
         return;
     }
 
     if (codes) store_codes4(q, s, L, live, codes + row * (k / 2) + b * 16, scales + row * nb + b);
 
-    if (act && b < mx_blocks(k)) {
-        // operand record of (row tile, block): row r's 32 codes as one 192-bit
-        // string of fp6 fields; this lane's 8 codes are 48 bits at bit 48 L,
-        // lanes 0, 1, 2 write planes 0, 1, 2 (bits 64 p .. 64 p + 63)
-        uint64_t mine = 0;
+    if (act && b < mx_blocks(k)) {  // the operand record of (row tile, block)
+        uint32_t f[8];
 #pragma unroll
-        for (int t = 0; t < 8; t++) mine |= (uint64_t)fp6_e2m3_of(q[t]) << (6 * t);
-        const uint64_t next = (uint64_t)quad_u32<QP_NEXT>((uint32_t)mine) |
-                              (uint64_t)quad_u32<QP_NEXT>((uint32_t)(mine >> 32)) << 32;
-        uint8_t *rec = act + ((int64_t)blockIdx.y * mx_blocks(k) + b) * MX_REC;
-        if (L < 3) {
-            const uint64_t plane = L == 0 ? (mine | next << 48) : L == 1 ? (mine >> 16 | next << 32) : (mine >> 32 | next << 16);
-            reinterpret_cast<uint2 *>(rec + 256 * L)[r] = make_uint2((uint32_t)plane, (uint32_t)(plane >> 32));
-        } else {
-            reinterpret_cast<uint2 *>(rec + MX_CODE_BYTES)[r] = act_scale_operand(s);
-        }
+        for (int t = 0; t < 8; t++) f[t] = fp6_e2m3_of(q[t]);
+        put_quad_row(f, L, act + ((int64_t)blockIdx.y * mx_blocks(k) + b) * MX_REC, r, act_scale_operand(s));
     }
 }
 

@@ -299,8 +299,10 @@ w4a4_status rotate_quantize(bool a8, const void *x, w4a4_dtype dt, int64_t m, in
     if (!aligned(x, dt == W4A4_DTYPE_F32 ? 4 : 2) || !aligned(codes, 16) || !aligned(scales, 4))
         return W4A4_ERR_MISALIGNED;
     if (act) {
+        if (!rotate) return W4A4_ERR_INVALID_VALUE;
         if (!aligned(act, 256)) return W4A4_ERR_MISALIGNED;
-        if (act_bytes < w4a4_act_operand_bytes(m, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
+        if (act_bytes < (a8 ? w4a4_act8_operand_bytes(m, k) : w4a4_act_operand_bytes(m, k)))
+            return W4A4_ERR_WORKSPACE_TOO_SMALL;
     }
     const size_t esz = dt == W4A4_DTYPE_F32 ? 4 : 2;
     // vector loads of a block: 16-byte (every block start 16-byte aligned),
@@ -343,6 +345,14 @@ w4a4_status w4a4_rotate_quantize_prepare(const void *x, w4a4_dtype dt, int64_t m
                                          void *stream) {
     if (!act && m > 0 && k > 0) return W4A4_ERR_INVALID_VALUE;
     return rotate_quantize(false, x, dt, m, k, ldx, codes, scales, act, act_bytes, stream);
+}
+
+w4a4_status w4a4_rotate_quantize_prepare8(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                                          int8_t *codes, float *scales, void *act, size_t act_bytes,
+                                          void *stream) {
+    if (!act && m > 0 && k > 0) return W4A4_ERR_INVALID_VALUE;
+    return rotate_quantize(true, x, dt, m, k, ldx, reinterpret_cast<uint8_t *>(codes), scales, act, act_bytes,
+                           stream);
 }
 
 size_t w4a4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
@@ -603,8 +613,31 @@ w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float 
                                                                  static_cast<uint8_t *>(workspace));
     const w4a4_status st2 = hip_status("act8_operand_kernel");
     if (st2 != W4A4_OK) return st2;
+    return w4a4_gemm_a8_prepared(packed_w, workspace, y, m, n, k, ldy, stream);
+}
+
+size_t w4a4_act8_operand_bytes(int64_t m, int64_t k) {
+    if (m < 0 || k < 0 || k % QK) return 0;
+    return 2 * w4a4_act_operand_bytes(m, k);
+}
+
+w4a4_status w4a4_gemm_a8_prepared(const void *packed_w, const void *act, float *y, int64_t m, int64_t n,
+                                  int64_t k, int64_t ldy, void *stream) {
+    if (m < 0 || n < 0 || k < 0 || ldy < n || !within_bounds(m, n, k)) return W4A4_ERR_INVALID_VALUE;
+    if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
+    if (m == 0 || n == 0) return W4A4_OK;
+    if (!y) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(y, 4)) return W4A4_ERR_MISALIGNED;
+    if ((m + 127) / 128 * ((n + 127) / 128) >= kMaxDenseTiles) return W4A4_ERR_INVALID_VALUE;
+    hipStream_t s = as_stream(stream);
+    if (k == 0) {  // empty sum
+        launch_zero_rows(y, m, n, ldy, s);
+        return hip_status("zero_rows_kernel");
+    }
+    if (!packed_w || !act) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(packed_w, 16) || !aligned(act, 256)) return W4A4_ERR_MISALIGNED;
     MxArgs a{};
-    a.act = static_cast<const uint8_t *>(workspace);
+    a.act = static_cast<const uint8_t *>(act);
     a.wrec = static_cast<const uint8_t *>(packed_w);  // the matrix-core section
     a.y = y;
     a.ldy = ldy;

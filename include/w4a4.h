@@ -302,6 +302,29 @@ w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float 
                          size_t workspace_bytes, void *stream);
 
 /*
+ * The W4A8 product in two steps, as w4a4_rotate_quantize_prepare and
+ * w4a4_gemm_prepared are for W4A4 (same section of the pages):
+ *
+ * w4a4_act8_operand_bytes: bytes of the int8 matrix-core operand of m rows of
+ *   width k, 2 * w4a4_act_operand_bytes(m, k) (0 for invalid sizes).  Host
+ *   only, pure.
+ * w4a4_rotate_quantize_prepare8: w4a4_rotate_quantize_act8, and in the same
+ *   pass the operand of the rows (the two FP6 planes that w4a4_gemm_a8 lays
+ *   out in its workspace for m > 16):
+ *   act   out, w4a4_act8_operand_bytes(m, k) bytes, 256-byte aligned; private
+ *         layout.  Other arguments and errors as w4a4_rotate_quantize_act8.
+ * w4a4_gemm_a8_prepared: the product of packed_w with such an operand, as
+ *   w4a4_gemm_a8 (any m >= 1; y [m][ldy] fp32; no workspace: the int8 path
+ *   does not split K).  Errors as w4a4_gemm_prepared.
+ */
+size_t w4a4_act8_operand_bytes(int64_t m, int64_t k);
+w4a4_status w4a4_rotate_quantize_prepare8(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                                          int8_t *codes, float *scales, void *act, size_t act_bytes,
+                                          void *stream);
+w4a4_status w4a4_gemm_a8_prepared(const void *packed_w, const void *act, float *y, int64_t m, int64_t n,
+                                  int64_t k, int64_t ldy, void *stream);
+
+/*
  * Unrotated W4A4, the ablation of section "MoE: W4A4 on the experts" (the
  * same W4A4 without the rotation costs about twice the accuracy).  Both
  * sides skip the rotation; the GEMM entry points are the same, fed with

@@ -116,6 +116,30 @@ def test_a8_validation(L):
     assert g(P(A), P(A), P(A), P(A), 16, 1024, 5120, 1024, P(A), need - 1, None) == WS
 
 
+def test_a8_prepared_validation(L):
+    # two planes of the W4A4 operand's shape: (row tiles) x 2 x 160 blocks x 1 KB
+    assert L.w4a4_act8_operand_bytes(64, 5120) == 2 * L.w4a4_act_operand_bytes(64, 5120) == 2 * 2 * 160 * 1024
+    assert L.w4a4_act8_operand_bytes(1, 64) == 2 * 8 * 1024
+    assert L.w4a4_act8_operand_bytes(8, 33) == 0
+    pb = L.w4a4_act8_operand_bytes(4, 64)
+    q = L.w4a4_rotate_quantize_prepare8
+    assert q(P(A), 0, 4, 40, 64, P(A), P(A), P(A), pb, None) == KMUL
+    assert q(P(A), 5, 4, 64, 64, P(A), P(A), P(A), pb, None) == DTYPE
+    assert q(P(A), 0, 4, 64, 64, P(A), P(A), None, pb, None) == INVALID
+    assert q(P(A), 0, 4, 64, 64, P(A), P(A), P(A + 16), pb, None) == MISALIGNED
+    assert q(P(A), 0, 4, 64, 64, P(A), P(A), P(A), pb - 1, None) == WS
+    # the W4A4 operand's size is too small for the two planes
+    assert q(P(A), 0, 4, 64, 64, P(A), P(A), P(A), L.w4a4_act_operand_bytes(4, 64), None) == WS
+    assert q(None, 0, 0, 64, 64, None, None, None, 0, None) == OK
+    g = L.w4a4_gemm_a8_prepared
+    assert g(P(A), P(A), P(A), 8, 64, 40, 64, None) == KMUL
+    assert g(P(A), P(A), P(A), 8, 64, 64, 32, None) == INVALID  # ldy < n
+    assert g(P(A), None, P(A), 8, 64, 64, 64, None) == INVALID
+    assert g(P(A), P(A + 16), P(A), 8, 64, 64, 64, None) == MISALIGNED
+    assert g(P(A), P(A), P(A + 2), 8, 64, 64, 64, None) == MISALIGNED
+    assert g(None, None, None, 0, 64, 64, 64, None) == OK
+
+
 def test_prepared_gemm_validation(L):
     pb = L.w4a4_act_operand_bytes(64, 64)
     assert pb == 2 * 8 * 1024

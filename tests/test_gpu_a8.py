@@ -131,3 +131,56 @@ def test_gemm_a8_output_stride_and_degenerate(ops):
     y0 = torch.full((3, 8), 5.0, device="cuda")
     ops.gemm_a8(packed, c[:3], s[:3], 8, 0, y=y0)  # k = 0: an empty sum
     assert not host(y0).any()
+
+
+@pytest.mark.parametrize("m,k,dtype", [(5, 320, np.float32), (17, 96, np.float32), (130, 2208, np.float16),
+                                       (512, 5120, np.float16)])
+def test_rotate_quantize_prepare8_operand(ops, m, k, dtype):
+    """The fused quantiser's codes and scales equal the oracle's bit for bit,
+    and the operand it writes equals byte for byte the one gemm_a8's pre-pass
+    builds in its workspace from those codes (over stale buffer contents)."""
+    rng = np.random.default_rng(3 * m + k)
+    x = synth.activations(m, k, rng, max(1, k // 100)).astype(dtype)
+    say(f"rotate_quantize_prepare8 m={m} k={k} {np.dtype(dtype).name}")
+    act = torch.full((ops.act8_operand_bytes(m, k),), 0xA5, dtype=torch.uint8, device="cuda")
+    c, s = ops.rotate_quantize_prepare8(dev(x), act)
+    rc, rs = oracle.rotate_quantize_act8(x)
+    assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs)
+    if m > 16:
+        n = 64
+        packed = ops.prepare_weights(dev(synth.weights(n, k, rng)))
+        ws = torch.full((int(ops.lib().w4a4_gemm_a8_workspace_bytes(m, n, k)),), 0x5A, dtype=torch.uint8,
+                        device="cuda")
+        ops.gemm_a8(packed, c, s, n, k, workspace=ws)
+        torch.cuda.synchronize()
+        assert ws.numel() >= act.numel() and torch.equal(ws[:act.numel()], act)
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_gemm_a8_prepared(ops, m, n, k):
+    """Above 16 rows gemm_a8 is the pre-pass plus this product, so the two
+    agree bit for bit; at any m the result meets the oracle's bar."""
+    w, x = _problem(m, n, k, 13 * m + n)
+    say(f"gemm_a8_prepared m={m} n={n} k={k}")
+    packed = ops.prepare_weights(dev(w))
+    act = torch.empty(ops.act8_operand_bytes(m, k), dtype=torch.uint8, device="cuda")
+    c, s = ops.rotate_quantize_prepare8(dev(x), act)
+    y = host(ops.gemm_a8_prepared(packed, act, m, n, k))
+    if m > 16:
+        assert np.array_equal(y, host(ops.gemm_a8(packed, c, s, n, k)))
+    ref = oracle.gemm_a8(oracle.prepare_weights(w), *oracle.rotate_quantize_act8(x), k)
+    assert_rows_close(y, ref, "gemm_a8_prepared")
+
+
+def test_gemm_a8_prepared_ffn_up_matches_gemm_a8(ops):
+    d = synth.ffn_up()
+    say("gemm_a8_prepared ffn_up 512x5120x17408 vs gemm_a8")
+    packed = ops.prepare_weights(dev(d.w))
+    xd = dev(d.x)
+    act = torch.empty(ops.act8_operand_bytes(d.m, d.k), dtype=torch.uint8, device="cuda")
+    c, s = ops.rotate_quantize_prepare8(xd, act)
+    y = ops.gemm_a8_prepared(packed, act, d.m, d.n, d.k)
+    assert torch.equal(y, ops.gemm_a8(packed, c, s, d.n, d.k))
+    ybig = torch.full((d.m, d.n + 8), 3.0, device="cuda")
+    ops.gemm_a8_prepared(packed, act, d.m, d.n, d.k, y=ybig[:, :d.n])
+    assert torch.equal(ybig[:, :d.n], y) and bool((ybig[:, d.n:] == 3.0).all())
