@@ -309,6 +309,7 @@ def test_size_bounds_are_refused_before_any_launch(L):
     assert rq(P(A), 1, MAX_ROWS + 1, 64, 64, P(A), P(A), None) == INVALID
     assert rq(P(A), 1, 4, (1 << 24) + 32, (1 << 24) + 32, P(A), P(A), None) == INVALID
     assert L.w4a4_rotate_quantize_act8(P(A), 1, MAX_ROWS + 1, 64, 64, P(A), P(A), None) == INVALID
+    assert L.w4a4_rotate_quantize_prepare8(P(A), 1, MAX_ROWS + 1, 64, 64, P(A), P(A), P(A), 1 << 40, None) == INVALID
     assert L.w4a4_rotate_act16(P(A), 1, MAX_ROWS + 1, 64, 64, P(A), 1 << 40, None) == INVALID
     assert L.w4a4_gemm_prepare_act(P(A), P(A), MAX_ROWS + 1, 64, P(A), 1 << 40, None) == INVALID
     g = L.w4a4_gemm
@@ -319,6 +320,11 @@ def test_size_bounds_are_refused_before_any_launch(L):
     gp = L.w4a4_gemm_prepared
     assert gp(P(A), P(A), P(A), 1024 * 128, 1024 * 128, 64, 1024 * 128, P(A), 1 << 40, None) == INVALID
     assert gp(P(A), P(A), P(A), MAX_ROWS + 1, 64, 64, 64, P(A), 1 << 40, None) == INVALID
+    g8 = L.w4a4_gemm_a8_prepared
+    assert g8(P(A), P(A), P(A), 1024 * 128, 1024 * 128, 64, 1024 * 128, None) == INVALID
+    assert g8(P(A), P(A), P(A), MAX_ROWS + 1, 64, 64, 64, None) == INVALID
+    assert L.w4a4_gemm_a8(P(A), P(A), P(A), P(A), 1024 * 128, 1024 * 128, 64, 1024 * 128, P(A), 1 << 40,
+                          None) == INVALID
     # weight preparation: n * k / 32 threads past 2^32
     assert L.w4a4_repack_q4_0_h32(P(A), P(A), 1 << 26, 1 << 24, None) == INVALID
     assert L.w4a4_quantize_q4_0_h32(P(A), 1 << 26, 1 << 24, 1 << 24, P(A), None) == INVALID
