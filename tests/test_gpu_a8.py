@@ -133,18 +133,20 @@ def test_gemm_a8_output_stride_and_degenerate(ops):
     assert not host(y0).any()
 
 
-@pytest.mark.parametrize("m,k,dtype", [(5, 320, np.float32), (17, 96, np.float32), (130, 2208, np.float16),
-                                       (512, 5120, np.float16)])
-def test_rotate_quantize_prepare8_operand(ops, m, k, dtype):
-    """The fused quantiser's codes and scales equal the oracle's bit for bit,
-    and the operand it writes equals byte for byte the one gemm_a8's pre-pass
-    builds in its workspace from those codes (over stale buffer contents)."""
+@pytest.mark.parametrize("m,k,dtype,pad", [(5, 320, np.float32, 0), (17, 96, np.float32, 0),
+                                           (130, 2208, np.float16, 0), (512, 5120, np.float16, 0),
+                                           (33, 96, np.float16, 8), (40, 288, np.float32, 32)])
+def test_rotate_quantize_prepare8_operand(ops, m, k, dtype, pad):
+    """The fused quantiser's codes and scales equal the oracle's bit for bit
+    (also from rows with a stride past k), and the operand it writes equals
+    byte for byte the one gemm_a8's pre-pass builds in its workspace from
+    those codes (over stale buffer contents)."""
     rng = np.random.default_rng(3 * m + k)
-    x = synth.activations(m, k, rng, max(1, k // 100)).astype(dtype)
-    say(f"rotate_quantize_prepare8 m={m} k={k} {np.dtype(dtype).name}")
+    x = synth.activations(m, k + pad, rng, max(1, k // 100)).astype(dtype)
+    say(f"rotate_quantize_prepare8 m={m} k={k} {np.dtype(dtype).name} ldx={k + pad}")
     act = torch.full((ops.act8_operand_bytes(m, k),), 0xA5, dtype=torch.uint8, device="cuda")
-    c, s = ops.rotate_quantize_prepare8(dev(x), act)
-    rc, rs = oracle.rotate_quantize_act8(x)
+    c, s = ops.rotate_quantize_prepare8(dev(x), act, k=k)
+    rc, rs = oracle.rotate_quantize_act8(x, k=k)
     assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs)
     if m > 16:
         n = 64
