@@ -28,7 +28,10 @@
 // not depend on which split finished last.
 //
 // Measured on MI355X (7 dense projections of a 27B-class layer, 16 rows):
-// 8 waves per workgroup and a 2-record ring beat 4 waves or deeper rings.
+// 8 waves per workgroup and a 2-record ring beat 4 waves or deeper rings;
+// long K (past 5120) runs 16 waves per workgroup over the whole of K (the o
+// and down projections 9.2 and 16.1 us, against 10.3 and 16.7 us with 8
+// waves in 4 K splits).
 #pragma once
 
 #include "common.h"
@@ -37,7 +40,8 @@
 namespace w4a4 {
 
 constexpr int SMALL_M_MAX = 16;
-constexpr int SM_WAVES = 8;             // waves per workgroup
+constexpr int SM_WAVES = 8;             // waves per workgroup (SM_WAVES_LONG_K past 5120)
+constexpr int SM_WAVES_LONG_K = 16;
 constexpr int SM_DEPTH = 2;             // streaming records in flight per wave
 constexpr int SM_ITEM_TARGET = 512;     // workgroups wanted (two per CU on a 256-CU part)
 static_assert(SM_ITEM_TARGET < (1 << 16), "a tile's K splits are counted in 16 bits");
@@ -69,28 +73,31 @@ struct SmallArgs {
     int64_t producers = 0;      // workgroups 0 .. producers - 1 quantise
 };
 
-// Launch plan of an m <= 16 product: the K splits.  Narrow projections split
-// K so that about SM_ITEM_TARGET workgroups run.  Pure function of the sizes
-// (the workspace size depends on it).
+// Launch plan of an m <= 16 product: waves per workgroup and the K splits.
+// Narrow projections split K so that about a target number of workgroups
+// run.  Pure function of the sizes and the kernel (the workspace size
+// depends on it).
 struct SmallPlan {
     int64_t tiles, splits, range;
+    int waves;
 };
+// a8: int8 activations (8 waves per workgroup at every K).
 __host__ __device__ inline SmallPlan small_m_plan(int64_t n, int64_t k, bool a8 = false) {
-    (void)a8;
     const int64_t tiles = padded_n(n) / TILE_N, nq = sq_quads(k);
-    // K up to 5120 aims at a quarter as many workgroups (measured on the
-    // 16-row verify set with the splits added in-kernel: q unsplit and k, v
-    // in 4 splits beat 2 and 8 splits by 0.3 to 2 us each; 2 or 1 split for
-    // k and v lose 0.3 us; the long-K o and down projections are fastest
-    // with the full target, against a half or twice it)
-    const int64_t target = k <= 5120 ? SM_ITEM_TARGET / 4 : SM_ITEM_TARGET;
+    // Measured on the 16-row verify set with the splits added in-kernel.  K
+    // up to 5120 aims at a quarter as many workgroups (q unsplit and k, v in
+    // 4 splits beat 2 and 8 splits by 0.3 to 2 us each).  Past 5120, 16
+    // waves per workgroup at the same quarter (the o and down projections
+    // then run whole K: 9.2 and 16.1 us, against 10.3 and 16.7 us for 8
+    // waves at the full target, their best with 8; 16 waves for K up to 5120
+    // lose 0.6 to 0.8 us on q, k and v).  The 8-wave kernels past 5120 keep
+    // the full target.
+    const bool long_k = !a8 && k > 5120;
+    const int64_t target = k <= 5120 || long_k ? SM_ITEM_TARGET / 4 : SM_ITEM_TARGET;
     const int64_t want = (target + tiles - 1) / tiles;
     const int64_t splits = want < nq ? want : nq;
     const int64_t range = (nq + splits - 1) / splits;
-    return SmallPlan{tiles, (nq + range - 1) / range, range};
-}
-__host__ __device__ inline int64_t small_m_splits(int64_t n, int64_t k, bool a8 = false) {
-    return small_m_plan(n, k, a8).splits;
+    return SmallPlan{tiles, (nq + range - 1) / range, range, long_k ? SM_WAVES_LONG_K : SM_WAVES};
 }
 
 // Spin limit of a consumer's wait for its activations (each round is one
@@ -131,7 +138,7 @@ __device__ __forceinline__ void wait_for_quads(const SmallArgs &a, int64_t q0, i
 
 // Bytes of the cross-wave reduction in LDS ([wave][8][64] floats); the
 // word after it tells the workgroup whether it arrived last.
-constexpr int SM_RED_BYTES = SM_WAVES * 8 * 64 * 4;
+__host__ __device__ constexpr int sm_red_bytes(int waves) { return waves * 8 * 64 * 4; }
 
 // Counts one arrival of a K split at its column tile's word and returns 1 to
 // the last of `splits` (< 2^16) arrivals, which also resets the word to zero.
@@ -354,8 +361,7 @@ __device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, i
     const int64_t splits = (sq_quads(k) + a.range - 1) / a.range;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    static_assert(WAVES * 8 * 64 * 4 <= SM_RED_BYTES, "the last-arrival word follows the reduction");
-    int *last = reinterpret_cast<int *>(smem + SM_RED_BYTES);
+    int *last = reinterpret_cast<int *>(smem + sm_red_bytes(WAVES));  // after the reduction
     if (tid == 0) *last = small_m_arrive(a.arrivals + tile, a.ticket, splits);
     __syncthreads();
     if (!*last) return;  // uniform
@@ -381,18 +387,20 @@ __device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, i
     }
 }
 
-// Grid (tiles, splits).  At most 80 registers (int4 activations): six waves
-// per SIMD keep three workgroups resident per CU, so the 544 workgroups of a
-// 17408-column projection run in one round.
+// Grid (tiles, splits).  8 waves: at most 80 registers (int4 activations),
+// six waves per SIMD keep three workgroups resident per CU, so the 544
+// workgroups of a 17408-column projection run in one round.  16 waves (long
+// K, at most a few hundred workgroups): four waves per SIMD, one workgroup
+// per CU.
 template <int WAVES, int DEPTH, bool A8 = false>
-__global__ __launch_bounds__(64 * WAVES, A8 ? 1 : 6) void gemm_small_m_kernel(SmallArgs a) {
+__global__ __launch_bounds__(64 * WAVES, A8 ? 1 : WAVES > 8 ? 4 : 6) void gemm_small_m_kernel(SmallArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     small_m_tile<WAVES, DEPTH, A8, false>(a, blockIdx.x, blockIdx.y, smem, 0);
 }
 
 // ---------------------------------------------------------------------------
 // Rotate-quantise fused into the m <= 16 product, one launch: workgroups
-// 0 .. producers - 1 quantise the activations (FUSE_QUADS quads of 4 blocks
+// 0 .. producers - 1 quantise the activations (fuse_quads(WAVES) quads of 4 blocks
 // each, every row; the quantiser's own per-block code, so the codes are the
 // standalone quantiser's bit for bit) into the public codes and scales and
 // publish each quad by storing the call's epoch + 1 into its flag (release);
@@ -404,14 +412,16 @@ __global__ __launch_bounds__(64 * WAVES, A8 ? 1 : 6) void gemm_small_m_kernel(Sm
 // device-scope count) advances it and clears the count, so the workspace is
 // ready for the next call without a separate clearing launch.
 // ---------------------------------------------------------------------------
-constexpr int FUSE_QUADS = 2;  // 2 quads x 4 blocks x 16 rows x a quad of lanes = 512 threads
+// quads per producer workgroup: one thread per lane of a (block, row) quad,
+// 4 blocks x 16 rows x 4 lanes = 256 threads per quad of blocks
+__host__ __device__ constexpr int fuse_quads(int waves) { return waves * 64 / (SQ_BLOCKS * SMALL_M_MAX * 4); }
 
-template <typename T>
+template <int QUADS, typename T>
 __device__ __forceinline__ void fused_producer(const SmallArgs &a, int64_t pid, uint32_t target) {
     const int tid = threadIdx.x, L = tid & 3, g = tid >> 2;  // quad g: row g % 16, block g / 16
     const int row = g & 15;
     const int64_t nb = a.k / QK, nq = sq_quads(a.k);
-    const int64_t b = pid * FUSE_QUADS * SQ_BLOCKS + (g >> 4);
+    const int64_t b = pid * QUADS * SQ_BLOCKS + (g >> 4);
     const bool live = row < a.m && b < nb;  // uniform per quad
     int q[8];
     float s;
@@ -421,22 +431,23 @@ __device__ __forceinline__ void fused_producer(const SmallArgs &a, int64_t pid, 
     // so the flags, stored after it, follow them
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid < FUSE_QUADS) {
-        const int64_t quad = pid * FUSE_QUADS + tid;
+    if (tid < QUADS) {
+        const int64_t quad = pid * QUADS + tid;
         if (quad < nq) __hip_atomic_store(a.flags + quad, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 template <int WAVES, int DEPTH, typename T>
-__global__ __launch_bounds__(64 * WAVES, 6) void gemm_small_m_fused_kernel(SmallArgs a, int64_t tiles, uint32_t total) {
-    // (three workgroups per CU, as the unfused kernel: the waiting consumers
-    // and the producers are resident together)
-    static_assert(64 * WAVES == FUSE_QUADS * SQ_BLOCKS * SMALL_M_MAX * 4, "one producer thread per lane of a quad");
+__global__ __launch_bounds__(64 * WAVES, WAVES > 8 ? 4 : 6) void gemm_small_m_fused_kernel(SmallArgs a, int64_t tiles,
+                                                                                           uint32_t total) {
+    // (the unfused kernel's occupancy: the waiting consumers and the
+    // producers are resident together)
+    static_assert(64 * WAVES == fuse_quads(WAVES) * SQ_BLOCKS * SMALL_M_MAX * 4, "one producer thread per lane of a quad");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const uint32_t epoch = __hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t target = epoch + 1;
     const int64_t id = blockIdx.x;
-    if (id < a.producers) fused_producer<T>(a, id, target);  // uniform per workgroup
+    if (id < a.producers) fused_producer<fuse_quads(WAVES), T>(a, id, target);  // uniform per workgroup
     else small_m_tile<WAVES, DEPTH, false, true>(a, (id - a.producers) % tiles, (id - a.producers) / tiles, smem, target);
     // the last workgroup to finish advances the epoch for the next call (the
     // next call reads it after this launch has ended: no fence is needed)
@@ -449,10 +460,8 @@ __global__ __launch_bounds__(64 * WAVES, 6) void gemm_small_m_fused_kernel(Small
 
 // LDS bytes of one workgroup: the waves' activation slots, or the cross-wave
 // reduction and the last-arrival word if that is larger.
-__host__ inline size_t small_m_lds_bytes(const SmallPlan &p, bool a8 = false) {
-    (void)p;
-    (void)a8;
-    const size_t slots = (size_t)SM_WAVES * SQ_BLOCKS * (2 * 16 * 16 + 16 * 8), red = (size_t)SM_RED_BYTES + 16;
+__host__ inline size_t small_m_lds_bytes(const SmallPlan &p) {
+    const size_t slots = (size_t)p.waves * SQ_BLOCKS * (2 * 16 * 16 + 16 * 8), red = (size_t)sm_red_bytes(p.waves) + 16;
     return slots > red ? slots : red;
 }
 

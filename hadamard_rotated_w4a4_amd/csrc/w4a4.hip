@@ -385,8 +385,8 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
         return hip_status("zero_rows_kernel");
     }
     if (m <= SMALL_M_MAX) {
-        const int64_t splits = small_m_splits(n, k);
-        if (splits > 1) {
+        const SmallPlan plan = small_m_plan(n, k);
+        if (plan.splits > 1) {
             if (!workspace) return W4A4_ERR_INVALID_VALUE;
             if (!aligned(workspace, 256)) return W4A4_ERR_MISALIGNED;
             if (workspace_bytes < w4a4_gemm_workspace_bytes(m, n, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
@@ -400,11 +400,13 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
         a.m = m;
         a.n = n;
         a.k = k;
-        const SmallPlan plan = small_m_plan(n, k);
         a.range = plan.range;
         set_small_m_split(a, plan, workspace);
-        gemm_small_m_kernel<SM_WAVES, SM_DEPTH><<<dim3((unsigned)plan.tiles, (unsigned)plan.splits), 64 * SM_WAVES,
-                                                   small_m_lds_bytes(plan), s>>>(a);
+        const dim3 grid((unsigned)plan.tiles, (unsigned)plan.splits);
+        if (plan.waves == SM_WAVES_LONG_K)
+            gemm_small_m_kernel<SM_WAVES_LONG_K, SM_DEPTH><<<grid, 64 * SM_WAVES_LONG_K, small_m_lds_bytes(plan), s>>>(a);
+        else
+            gemm_small_m_kernel<SM_WAVES, SM_DEPTH><<<grid, 64 * SM_WAVES, small_m_lds_bytes(plan), s>>>(a);
         return hip_status("gemm_small_m_kernel");
     }
     // workspace: the activation operand, then the split-K partial sums
@@ -522,7 +524,7 @@ w4a4_status w4a4_rotate_quantize_gemm(const void *x, w4a4_dtype dt, int64_t m, i
         return w4a4_gemm_prepared(packed_w, workspace, y, m, n, k, ldy, static_cast<uint8_t *>(workspace) + act_bytes,
                                   workspace_bytes - act_bytes, stream);
     }
-    const SmallPlan plan = small_m_plan(n, k);
+    const SmallPlan plan = small_m_plan(n, k);  // the two-launch path's plan: the same sums in the same order
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     const size_t esz = dt == W4A4_DTYPE_F32 ? 4 : 2;
     SmallArgs a{};
@@ -543,16 +545,21 @@ w4a4_status w4a4_rotate_quantize_gemm(const void *x, w4a4_dtype dt, int64_t m, i
     a.scales_out = scales;
     a.sync = reinterpret_cast<uint32_t *>(ws);
     a.flags = reinterpret_cast<uint32_t *>(ws + 256);
-    a.producers = (sq_quads(k) + FUSE_QUADS - 1) / FUSE_QUADS;
+    const int quads = fuse_quads(plan.waves);
+    a.producers = (sq_quads(k) + quads - 1) / quads;
     const int64_t consumers = plan.tiles * plan.splits;
     const int64_t total = a.producers + consumers;
-    if (!grid_fits(total * 64 * SM_WAVES)) return W4A4_ERR_INVALID_VALUE;
-    if (dt == W4A4_DTYPE_F32)
-        gemm_small_m_fused_kernel<SM_WAVES, SM_DEPTH, float>
-            <<<(unsigned)total, 64 * SM_WAVES, small_m_lds_bytes(plan), s>>>(a, plan.tiles, (uint32_t)total);
+    if (!grid_fits(total * 64 * plan.waves)) return W4A4_ERR_INVALID_VALUE;
+    const unsigned threads = 64 * plan.waves;
+    const size_t lds = small_m_lds_bytes(plan);
+    if (plan.waves == SM_WAVES_LONG_K && dt == W4A4_DTYPE_F32)
+        gemm_small_m_fused_kernel<SM_WAVES_LONG_K, SM_DEPTH, float><<<(unsigned)total, threads, lds, s>>>(a, plan.tiles, (uint32_t)total);
+    else if (plan.waves == SM_WAVES_LONG_K)
+        gemm_small_m_fused_kernel<SM_WAVES_LONG_K, SM_DEPTH, __half><<<(unsigned)total, threads, lds, s>>>(a, plan.tiles, (uint32_t)total);
+    else if (dt == W4A4_DTYPE_F32)
+        gemm_small_m_fused_kernel<SM_WAVES, SM_DEPTH, float><<<(unsigned)total, threads, lds, s>>>(a, plan.tiles, (uint32_t)total);
     else
-        gemm_small_m_fused_kernel<SM_WAVES, SM_DEPTH, __half>
-            <<<(unsigned)total, 64 * SM_WAVES, small_m_lds_bytes(plan), s>>>(a, plan.tiles, (uint32_t)total);
+        gemm_small_m_fused_kernel<SM_WAVES, SM_DEPTH, __half><<<(unsigned)total, threads, lds, s>>>(a, plan.tiles, (uint32_t)total);
     return hip_status("gemm_small_m_fused_kernel");
 }
 
@@ -599,7 +606,7 @@ w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float 
         a.range = plan.range;
         set_small_m_split(a, plan, workspace);
         gemm_small_m_kernel<SM_WAVES, SM_DEPTH, true>
-            <<<dim3((unsigned)plan.tiles, (unsigned)plan.splits), 64 * SM_WAVES, small_m_lds_bytes(plan, true), s>>>(a);
+            <<<dim3((unsigned)plan.tiles, (unsigned)plan.splits), 64 * SM_WAVES, small_m_lds_bytes(plan), s>>>(a);
         return hip_status("gemm_small_m_kernel<a8>");
     }
     // m > 16: the codes as two FP6 planes, then the matrix-core kernel
