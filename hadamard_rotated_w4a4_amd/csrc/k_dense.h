@@ -181,9 +181,10 @@ struct MxArgs {
 // groups.  One FP6 MFMA with the E8M0 scale 2^4 (byte 131) on the h lanes
 // then gives 16 S_h + S_l = S, the integer dot of the int8 codes (over 64),
 // exactly (|S| <= 127 * 8 * 32): a block costs one block-dot MFMA, as in
-// W4A4, with no lanes masked.  Stages are one block (BKB = 1) and the scale
-// products single-block 32x32x8 bf16 MFMAs (the l plane's scale operand is
-// zero, so the second lane group adds nothing).
+// W4A4, with no lanes masked.  A stage holds BKB blocks (1 or 2), each with
+// its own operand registers, and the scale products are single-block
+// 32x32x8 bf16 MFMAs (the l plane's scale operand is zero, so the second
+// lane group adds nothing).
 template <int BKB_, int NS_, int TM_, int TN_, bool A8_ = false>
 struct MxCfg {
     static constexpr int BKB = BKB_, NS = NS_;
@@ -192,7 +193,8 @@ struct MxCfg {
     static constexpr int RT = BM / 32, CT = BN / 32;
     static constexpr bool A8 = A8_;
     static constexpr int AP = A8 ? 2 : 1;  // activation record planes per row tile
-    static_assert(A8 ? BKB == 1 : BKB == 2, "W4A4: two blocks per operand set; A8: the two planes of one");
+    static_assert(A8 ? (BKB == 1 || BKB == 2) : BKB == 2,
+                  "W4A4: two blocks per operand set; A8: the two planes of one block per operand set");
     static constexpr int STAGE_BYTES = (RT * AP + CT) * BKB * MX_REC;
     static constexpr int DMA_PER_STAGE = (RT * AP + CT) * BKB;  // 1 KB each
     static constexpr int DMA_PER_WAVE = DMA_PER_STAGE / 4;
@@ -326,8 +328,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
     const int sel0 = g ? 0 : 127, sel1 = g ? 127 : 0;  // E8M0 lane masks of blocks 0 and 1
     const uint32_t id_sel = opaque_identity_selector();
     // Operand reads of one row tile (i) or column tile (j) of a stage; lane
-    // group g reads block g's record (A8: plane g's of the stage's block, and
-    // both groups the block's weight record).
+    // group g reads block g's record.
     auto load_a = [&](const uint8_t *st, int i) {
         const uint8_t *rec = st + ((wm * TM + i) * AP * BKB + g) * MX_REC, *p = rec + 8 * c;
         af[i] = fp6_operand(lds_read<u32x2>(p), lds_read<u32x2>(p + 256), lds_read<u32x2>(p + 512));
@@ -335,7 +336,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
         ap[i] = make_uint2(sp.x, sp.y);
     };
     auto load_b = [&](const uint8_t *st, int j) {
-        const uint8_t *rec = st + ((RT * AP + wn * TN + j) * BKB + (C::A8 ? 0 : g)) * MX_REC, *p = rec + 8 * c;
+        const uint8_t *rec = st + ((RT * AP + wn * TN + j) * BKB + g) * MX_REC, *p = rec + 8 * c;
         bf[j] = fp6_operand(lds_read<u32x2>(p), lds_read<u32x2>(p + 256), lds_read<u32x2>(p + 512));
         bw[j] = lds_read<uint32_t>(rec + MX_CODE_BYTES + 4 * c);
     };
@@ -359,39 +360,76 @@ __device__ __forceinline__ void mx_tile(const MxArgs &a, int64_t id, uint8_t *sm
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 2)) : "memory");
     __syncthreads();
     if constexpr (C::A8) {
-        // A8: one block per stage, one FP6 MFMA and one single-block scale
-        // product per tile, the same pipeline otherwise (the scale operand
-        // of lane group 1 is the l plane record's zeros)
+        // A8: per block and tile one FP6 MFMA (both planes) and one
+        // single-block scale product.  Step t of a stage is block t / TT,
+        // tile t % TT; every (tile, block) part of a stage has its own
+        // operand registers, reread for the next stage right after the step
+        // that issues its last MFMAs, as in the W4A4 pipeline.
+        constexpr int TT = TM * TN, ST8 = TT * BKB, PARTS8 = (TM + TN) * BKB;
+        static_assert(ST8 % 2 == 0, "the result buffers alternate by step parity");
+        v8i af8[TM][BKB], bf8[TN][BKB];
+        uint2 ap8[TM][BKB];     // (s1, s1, s2, s2) of row c (the h plane; zeros in the l plane)
+        uint32_t bw8[TN][BKB];  // (d0, d1) of column c
+        auto load_a8 = [&](const uint8_t *st, int i, int bb) {
+            const uint8_t *rec = st + (((wm * TM + i) * AP + g) * BKB + bb) * MX_REC, *p = rec + 8 * c;
+            af8[i][bb] = fp6_operand(lds_read<u32x2>(p), lds_read<u32x2>(p + 256), lds_read<u32x2>(p + 512));
+            const u32x2 sp = lds_read<u32x2>(rec + MX_CODE_BYTES + 8 * c);
+            ap8[i][bb] = make_uint2(sp.x, sp.y);
+        };
+        auto load_b8 = [&](const uint8_t *st, int j, int bb) {
+            const uint8_t *rec = st + ((RT * AP + wn * TN + j) * BKB + bb) * MX_REC, *p = rec + 8 * c;
+            bf8[j][bb] = fp6_operand(lds_read<u32x2>(p), lds_read<u32x2>(p + 256), lds_read<u32x2>(p + 512));
+            bw8[j][bb] = lds_read<uint32_t>(rec + MX_CODE_BYTES + 4 * c);
+        };
+        // part p: block p / (TM + TN); row tiles first, then column tiles
+        auto load_part8 = [&](const uint8_t *st, int p) {
+            const int bb = p / (TM + TN), q = p % (TM + TN);
+            if (q < TM) load_a8(st, q, bb);
+            else load_b8(st, q - TM, bb);
+        };
+        auto last_issue8 = [](int p) {
+            const int bb = p / (TM + TN), q = p % (TM + TN);
+            int last = -1;
+            for (int t = 0; t < ST8; t++) {
+                const int tt = t % TT;
+                if (t / TT == bb && ((q < TM && tt / TN == q) || (q >= TM && tt % TN == q - TM))) last = t - 1;
+            }
+            return last < 0 ? 0 : last;
+        };
+        auto mfma_p8 = [&](int t) {
+            const int bb = t / TT, tt = t % TT;
+            return mfma_bf16_32x32x8(ap8[tt / TN][bb], dup_at_use(bw8[tt % TN][bb], id_sel));
+        };
+        auto mfma_s8 = [&](int t) {
+            const int bb = t / TT, tt = t % TT;
+            return mfma_block8(af8[tt / TN][bb], bf8[tt % TN][bb], g);
+        };
         v16f S[2], P[2];
-        auto mfma_p8 = [&](int i, int j) { return mfma_bf16_32x32x8(ap[i], dup_at_use(bw[j], id_sel)); };
 #pragma unroll
-        for (int p = 0; p < PARTS; p++) load_part(smem, p);
-        P[0] = mfma_p8(0, 0);
-        S[0] = mfma_block8(af[0], bf[0], g);
+        for (int p = 0; p < PARTS8; p++) load_part8(smem, p);
+        P[0] = mfma_p8(0);
+        S[0] = mfma_s8(0);
 
         for (int s = 0; s < nstages; s++) {
 #pragma unroll
-            for (int t = 0; t < STEPS; t++) {
-                const int i = t / TN, j = t % TN, b = t & 1, b1 = b ^ 1;
-                if (t == BAR) {
+            for (int t = 0; t < ST8; t++) {
+                const int tt = t % TT, i = tt / TN, j = tt % TN, b = t & 1, b1 = b ^ 1;
+                if (t == 0) {  // stage s + 1 has landed and stage s - 1's slot is free
                     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::DMA_PER_WAVE * (NS - 3)) : "memory");
                     __syncthreads();
                 }
-                if (t >= BAR) {
-                    const int q = t - BAR;
 #pragma unroll
-                    for (int d = q * C::DMA_PER_WAVE / SPAN; d < (q + 1) * C::DMA_PER_WAVE / SPAN; d++)
-                        issue_one(s + NS - 1, (s + NS - 1) % NS, d);
-                }
-                const int t1 = (t + 1) % STEPS, i1 = t1 / TN, j1 = t1 % TN;
-                P[b1] = mfma_p8(i1, j1);
+                for (int d = t * C::DMA_PER_WAVE / ST8; d < (t + 1) * C::DMA_PER_WAVE / ST8; d++)
+                    issue_one(s + NS - 1, (s + NS - 1) % NS, d);
+                const int t1 = (t + 1) % ST8;
+                P[b1] = mfma_p8(t1);
 #pragma unroll
                 for (int v = 0; v < 8; v++) acc[i][j][v] = fmaf(S[b][v], P[b][v], acc[i][j][v]);
                 __builtin_amdgcn_sched_barrier(0x0004 | 0x0010);
-                S[b1] = mfma_block8(af[i1], bf[j1], g);
+                S[b1] = mfma_s8(t1);
 #pragma unroll
-                for (int p = 0; p < PARTS; p++)
-                    if (last_issue(p) == t) load_part(smem + ((s + 1) % NS) * C::STAGE_BYTES, p);
+                for (int p = 0; p < PARTS8; p++)
+                    if (last_issue8(p) == t) load_part8(smem + ((s + 1) % NS) * C::STAGE_BYTES, p);
 #pragma unroll
                 for (int v = 8; v < 16; v++) acc[i][j][v] = fmaf(S[b][v], P[b][v], acc[i][j][v]);
                 asm volatile("" : "+v"(acc[i][j]));

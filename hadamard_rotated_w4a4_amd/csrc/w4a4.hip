@@ -68,7 +68,9 @@ using Mx128x64 = MxCfg<2, 4, 2, 1>;
 using Mx64x128 = MxCfg<2, 4, 1, 2>;
 // int8 activations (two FP6 planes in one operand set, one block per
 // stage): 128 x 128 and 64 x 128 tiles (a 128 x 64 stage would not split
-// into equal loads over the four waves)
+// into equal loads over the four waves).  Two-block stages in a 3-stage
+// ring (72 KB, still two workgroups per CU) measured slower: 127 against
+// 116-117 us at FFN up.
 using Mx128x128A8 = MxCfg<1, 4, 2, 2, true>;
 using Mx64x128A8 = MxCfg<1, 4, 1, 2, true>;
 
