@@ -49,6 +49,7 @@ PEAK_FP6_TOPS = 10100.0      # MI355X dense FP6 / FP4 MFMA, TFLOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_FP16_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 MFMA, TFLOP/s
 COLD_BYTES = 1 << 30         # weight copies rotated per step exceed this
+LLC_BYTES = 256 << 20        # MI355X last-level (Infinity) cache
 PROFILE_JSON = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "hadamard_rotated_w4a4_amd", "csrc", f)
                   for f in ("common.h", "k_route.h", "k_dense.h", "k_smallm.h", "k_grouped.h", "k_rotq.h", "k_prep.h", "k_w16.h", "w4a4.hip")]
@@ -165,6 +166,32 @@ def events_ms(torch, fn, reps):
     return a.elapsed_time(b) / reps
 
 
+GRAPH_CALLS = 64  # at least this many launches per timing graph of a short kernel
+
+
+STEP_GRAPH_STEPS = 16  # at least this many whole steps per timing graph of a step
+
+
+def graph_steps(copies):
+    """Steps per timing graph of a multi-kernel step over `copies` weight
+    sets: whole rotations, at least STEP_GRAPH_STEPS."""
+    return max(1, -(-STEP_GRAPH_STEPS // copies)) * copies
+
+
+def cold_copies(read_bytes):
+    """Copies to rotate over so that the bytes a call reads, over one
+    rotation, are twice the last-level cache: each call then finds its
+    weights evicted."""
+    return max(2, -(-2 * LLC_BYTES // max(1, int(read_bytes))))
+
+
+def graph_calls(copies):
+    """Launches per timing graph over `copies` rotating buffers: whole
+    rotations, at least GRAPH_CALLS, so that the replay's own cost (its
+    submission and the event pair around it) is spread over many launches."""
+    return max(2, -(-GRAPH_CALLS // copies)) * copies
+
+
 def graph_time_us(torch, fn, reps=20, inner=1):
     """Capture `fn` (which enqueues `inner` identical units of work) in a HIP
     graph, replay it `reps` times with an event pair around each replay, and
@@ -192,9 +219,9 @@ _READ_FLOOR = {}
 
 def read_floor_us(torch, nbytes, copies):
     """The time of a plain read of `nbytes` in the regime the small-M
-    products are timed in (a HIP graph of 2 x `copies` back-to-back launches
-    over `copies` buffers, as each product rotates over that many weight
-    copies), with the committed read-stream probe (libw4a4_ceilings.so), at
+    products are timed in (a HIP graph of graph_calls(copies) back-to-back
+    launches over `copies` buffers, as each product rotates over that many
+    weight copies), with the committed read-stream probe (libw4a4_ceilings.so), at
     the best of four grid sizes: the size-matched ceiling of a weight stream
     of that many bytes, launch and ramp included.  None without the probe
     library."""
@@ -215,12 +242,12 @@ def read_floor_us(torch, nbytes, copies):
     for blocks in (512, 1024, 2048, 4096):
         def one(blocks=blocks):
             st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-            for i in range(2 * nbuf):
+            for i in range(graph_calls(nbuf)):
                 rc = L.w4a4c_read_stream(ctypes.c_void_p(bufs[i % nbuf].data_ptr()), nbytes,
                                          ctypes.c_void_p(sink.data_ptr()), blocks, st)
                 if rc:
                     raise RuntimeError(f"read stream launch failed ({rc})")
-        us = graph_time_us(torch, one, inner=2 * nbuf)
+        us = graph_time_us(torch, one, inner=graph_calls(nbuf))
         best = us if best is None else min(best, us)
     del bufs
     _READ_FLOOR[(nbytes, copies)] = best
@@ -241,22 +268,27 @@ def run_verify16(torch, ops, synth):
     q = {inp: ops.rotate_quantize_act(xin) for inp, xin in inputs.items()}
     ys = {name: torch.empty((16, n), dtype=torch.float32, device=dev) for name, _, n in synth.DENSE_PROJECTIONS}
     out = {"rows": 16, "weight_sets": nsets,
-           "timing": "HIP graph replay, weights rotated over the sets (one projection's copies alone can fit "
-                     "the 256 MB last-level cache; the step, all seven per set, is cold); read_floor_us: a plain "
-                     "read of the projection's weight bytes in the same rotation"}
+           "timing": "HIP graph replay; each projection alone over copies of its weights whose streamed bytes "
+                     "per rotation are twice the 256 MB last-level cache, the steps over the layer's weight sets "
+                     "(cold either way); read_floor_us: a plain read of the projection's weight bytes in the same "
+                     "rotation"}
     tot_us, tot_bytes = 0.0, 0
+    ncopies = {}
     for name, k, n in synth.DENSE_PROJECTIONS:
         c, sc = q[synth.DENSE_INPUT_OF[name]]
+        nc = ncopies[name] = cold_copies(n * k * 18 // 32)  # the 4-bit records this product streams
+        copies = [packed[name]] + [packed[name].clone() for _ in range(nc - 1)]
 
-        def one(name=name, k=k, n=n, c=c, sc=sc):
-            for i in range(2 * nsets):
-                ops.gemm(sets[i % nsets][name], c, sc, n, k, y=ys[name])
-        us = graph_time_us(torch, one, inner=2 * nsets)
+        def one(k=k, n=n, c=c, sc=sc, copies=copies, nc=nc, y=ys[name]):
+            for i in range(graph_calls(nc)):
+                ops.gemm(copies[i % nc], c, sc, n, k, y=y)
+        us = graph_time_us(torch, one, inner=graph_calls(nc))
+        del copies
         b = gemm_bytes(16, n, k)
         tot_us += us
         tot_bytes += b
         out[name] = {"k": k, "n": n, "us": round(us, 2), "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
-    floors = {name: read_floor_us(torch, n * k * 18 // 32, nsets) for name, k, n in synth.DENSE_PROJECTIONS}
+    floors = {name: read_floor_us(torch, n * k * 18 // 32, ncopies[name]) for name, k, n in synth.DENSE_PROJECTIONS}
     if all(f is not None for f in floors.values()):
         for name, _, _ in synth.DENSE_PROJECTIONS:
             out[name]["read_floor_us"] = round(floors[name], 2)
@@ -265,12 +297,12 @@ def run_verify16(torch, ops, synth):
         out["frac_of_read_floor"] = round(sum(floors.values()) / tot_us, 3)
 
     def step():
-        for i in range(nsets):
+        for i in range(graph_steps(nsets)):
             qq = {inp: ops.rotate_quantize_act(xin) for inp, xin in inputs.items()}
             for name, k, n in synth.DENSE_PROJECTIONS:
                 c, sc = qq[synth.DENSE_INPUT_OF[name]]
-                ops.gemm(sets[i][name], c, sc, n, k, y=ys[name])
-    step_us = graph_time_us(torch, step, inner=nsets)
+                ops.gemm(sets[i % nsets][name], c, sc, n, k, y=ys[name])
+    step_us = graph_time_us(torch, step, inner=graph_steps(nsets))
 
     # rotate-quantise fused into the product (one launch per distinct input:
     # its first projection quantises, the others reuse the codes it wrote)
@@ -286,16 +318,16 @@ def run_verify16(torch, ops, synth):
                       dtype=torch.uint8, device=dev)
 
     def fused_step():
-        for i in range(nsets):
+        for i in range(graph_steps(nsets)):
             for name, k, n in synth.DENSE_PROJECTIONS:
                 inp = synth.DENSE_INPUT_OF[name]
                 c, sc = qbuf[inp]
                 if firsts[inp] == name:
-                    ops.rotate_quantize_gemm(inputs[inp], sets[i][name], n, k, y=ys[name], codes=c, scales=sc,
+                    ops.rotate_quantize_gemm(inputs[inp], sets[i % nsets][name], n, k, y=ys[name], codes=c, scales=sc,
                                              workspace=fq_ws)
                 else:
-                    ops.gemm(sets[i][name], c, sc, n, k, y=ys[name], workspace=gws)
-    fused_step_us = graph_time_us(torch, fused_step, inner=nsets)
+                    ops.gemm(sets[i % nsets][name], c, sc, n, k, y=ys[name], workspace=gws)
+    fused_step_us = graph_time_us(torch, fused_step, inner=graph_steps(nsets))
     out["rotate_quantize_fused"] = {"step_us": round(fused_step_us, 2),
                                     "tokens/s": round(16 / (fused_step_us * 1e-6), 1),
                                     "launches": "4 fused rotate-quantise + product, 3 products on the codes "
@@ -325,29 +357,32 @@ def run_verify16(torch, ops, synth):
     for g, _, inp in groups:
         k, n = shape[g]
         c, sc = q[inp]
+        nc = cold_copies(n * k * 18 // 32)
+        copies = [fused[g]] + [fused[g].clone() for _ in range(nc - 1)]
 
-        def one(g=g, k=k, n=n, c=c, sc=sc):
-            for i in range(2 * nsets):
-                ops.gemm(fsets[i % nsets][g], c, sc, n, k, y=fys[g], workspace=fws[g])
-        f_us += graph_time_us(torch, one, inner=2 * nsets)
+        def one(g=g, k=k, n=n, c=c, sc=sc, copies=copies, nc=nc):
+            for i in range(graph_calls(nc)):
+                ops.gemm(copies[i % nc], c, sc, n, k, y=fys[g], workspace=fws[g])
+        f_us += graph_time_us(torch, one, inner=graph_calls(nc))
+        del copies
 
     def fstep():
-        for i in range(nsets):
+        for i in range(graph_steps(nsets)):
             qq = {inp: ops.rotate_quantize_act(xin) for inp, xin in inputs.items()}
             for g, _, inp in groups:
                 k, n = shape[g]
-                ops.gemm(fsets[i][g], *qq[inp], n, k, y=fys[g], workspace=fws[g])
-    fstep_us = graph_time_us(torch, fstep, inner=nsets)
+                ops.gemm(fsets[i % nsets][g], *qq[inp], n, k, y=fys[g], workspace=fws[g])
+    fstep_us = graph_time_us(torch, fstep, inner=graph_steps(nsets))
     fws2 = torch.zeros(max(ops.rotate_quantize_gemm_workspace_bytes(16, n, k) for k, n in shape.values()),
                        dtype=torch.uint8, device=dev)
 
     def fqstep():  # the four packed products, each with its rotate-quantise fused in
-        for i in range(nsets):
+        for i in range(graph_steps(nsets)):
             for g, _, inp in groups:
                 k, n = shape[g]
-                ops.rotate_quantize_gemm(inputs[inp], fsets[i][g], n, k, y=fys[g], codes=qbuf[inp][0],
+                ops.rotate_quantize_gemm(inputs[inp], fsets[i % nsets][g], n, k, y=fys[g], codes=qbuf[inp][0],
                                          scales=qbuf[inp][1], workspace=fws2)
-    fqstep_us = graph_time_us(torch, fqstep, inner=nsets)
+    fqstep_us = graph_time_us(torch, fqstep, inner=graph_steps(nsets))
     out["same_input_fused"] = {"gemms": len(groups), "gemm_us_total": round(f_us, 2),
                                "rotate_quantize_fused_step_us": round(fqstep_us, 2),
                                "rotate_quantize_fused_tokens/s": round(16 / (fqstep_us * 1e-6), 1),
@@ -359,9 +394,10 @@ def run_verify16(torch, ops, synth):
 
 def run_moe(torch, ops, synth):
     """MoE layer: gate, up (one activation row per token) and down (one per
-    slot).  Timed cold: the three expert weight matrices are cloned into sets
-    totalling more than 1 GB and consecutive calls take consecutive sets, so
-    the 256 MB last-level cache cannot hold the experts a call reads."""
+    slot).  Timed cold: the three expert weight matrices are cloned into
+    sets, consecutive calls take consecutive sets, and there are enough sets
+    that the expert records one product streams, over a rotation, are twice
+    the 256 MB last-level cache."""
     dev = torch.device("cuda:0")
     mo = synth.moe()
     E, T, top_k = mo.w_gate.shape[0], mo.ids.shape[0], mo.ids.shape[1]
@@ -371,12 +407,13 @@ def run_moe(torch, ops, synth):
         return torch.cat([ops.prepare_weights(torch.from_numpy(w[e]).to(dev)) for e in range(E)])
     base = {"g": experts(mo.w_gate), "u": experts(mo.w_up), "d": experts(mo.w_down)}
     set_bytes = sum(t.numel() for t in base.values())
-    nsets = max(2, -(-COLD_BYTES // set_bytes))
+    counts = np.bincount(mo.ids.reshape(-1), minlength=E)
+    streamed = int((counts > 0).sum()) * q4_bytes(dff, dm)  # one matrix's used experts, 4-bit records
+    nsets = max(-(-COLD_BYTES // set_bytes), cold_copies(streamed))
     sets = [base] + [{k_: v.clone() for k_, v in base.items()} for _ in range(nsets - 1)]
     ids = torch.from_numpy(mo.ids).to(dev)
     x = torch.from_numpy(mo.x).to(dev)
     h = torch.from_numpy(mo.h).to(dev)
-    counts = np.bincount(mo.ids.reshape(-1), minlength=E)
     ws = torch.empty(ops.gemm_id_workspace_bytes(E, T, top_k), dtype=torch.uint8, device=dev)
     yg = torch.empty((T, top_k, dff), dtype=torch.float32, device=dev)
     yu = torch.empty_like(yg)
@@ -384,8 +421,13 @@ def run_moe(torch, ops, synth):
     cx, sx = ops.rotate_quantize_act(x)
     ch, sh = ops.rotate_quantize_act(h)
 
-    def rotating(call):  # 2 * nsets calls, consecutive sets
-        return graph_time_us(torch, lambda: [call(sets[i % nsets]) for i in range(2 * nsets)], inner=2 * nsets)
+    def rotating(call):  # graph_calls(nsets) calls, consecutive sets
+        return graph_time_us(torch, lambda: [call(sets[i % nsets]) for i in range(graph_calls(nsets))],
+                             inner=graph_calls(nsets))
+
+    def steps(fn):  # graph_steps(nsets) steps, consecutive sets
+        return graph_time_us(torch, lambda: [fn(sets[i % nsets]) for i in range(graph_steps(nsets))],
+                             inner=graph_steps(nsets))
     g = rotating(lambda st: ops.gemm_id(st["g"], E, cx, sx, 1, ids, dff, dm, y=yg, workspace=ws))
     u = rotating(lambda st: ops.gemm_id(st["u"], E, cx, sx, 1, ids, dff, dm, y=yu, workspace=ws))
     dd = rotating(lambda st: ops.gemm_id(st["d"], E, ch, sh, top_k, ids, dm, dff, y=yd, workspace=ws))
@@ -400,7 +442,7 @@ def run_moe(torch, ops, synth):
         ops.gemm_id(st["g"], E, cx, sx, 1, ids, dff, dm, y=yg, workspace=ws)
         ops.gemm_id(st["u"], E, cx, sx, 1, ids, dff, dm, y=yu, workspace=ws)
         ops.gemm_id(st["d"], E, ch, sh, top_k, ids, dm, dff, y=yd, workspace=ws)
-    step_us = graph_time_us(torch, lambda: [step(st) for st in sets], inner=nsets)
+    step_us = steps(step)
 
     # the same step routed once for the three products
     def rstep(st):
@@ -410,7 +452,7 @@ def run_moe(torch, ops, synth):
         ops.gemm_id_routed(st["g"], E, cx, sx, 1, T, top_k, dff, dm, ws, y=yg)
         ops.gemm_id_routed(st["u"], E, cx, sx, 1, T, top_k, dff, dm, ws, y=yu)
         ops.gemm_id_routed(st["d"], E, ch, sh, top_k, T, top_k, dm, dff, ws, y=yd)
-    rstep_us = graph_time_us(torch, lambda: [rstep(st) for st in sets], inner=nsets)
+    rstep_us = steps(rstep)
     rows = T * top_k
     used = int((counts > 0).sum())
     b_gate = used * q4_bytes(dff, dm) + T * dm // 2 + T * dm // 8 + rows * dff * 4
@@ -433,7 +475,7 @@ def run_moe(torch, ops, synth):
         ops.gemm_id_route(ids, E, workspace=ws)
         ops.gemm_id_routed(st["gu"], E, cx, sx, 1, T, top_k, 2 * dff, dm, ws, y=ygu)
         ops.gemm_id_routed(st["d"], E, ch, sh, top_k, T, top_k, dm, dff, ws, y=yd)
-    fstep_us = graph_time_us(torch, lambda: [fstep(st) for st in sets], inner=nsets)
+    fstep_us = steps(fstep)
     del sets, base
     return {"experts": E, "tokens": T, "top_k": top_k, "count_min": int(counts.min()),
             "count_median": float(np.median(counts)), "count_max": int(counts.max()),
@@ -487,9 +529,9 @@ def run_w4a8(torch, ops, synth):
     nsets = len(copies)
 
     def one():
-        for i in range(2 * nsets):
+        for i in range(graph_calls(nsets)):
             ops.gemm_a8(copies[i % nsets], c16, s16, d.n, d.k, y=y16, workspace=ws)
-    us16 = graph_time_us(torch, one, inner=2 * nsets)
+    us16 = graph_time_us(torch, one, inner=graph_calls(nsets))
     b16 = gemm_bytes(16, d.n, d.k) + 16 * d.k // 2  # int8 codes: twice the int4 bytes
     return {"ffn_up_m512": {"step_us": round(step_us, 2), "gemm_us": round(gemm_us, 2),
                             "gemm_a8_call_us": round(call_us, 2),

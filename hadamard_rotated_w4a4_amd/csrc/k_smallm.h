@@ -29,9 +29,9 @@
 //
 // Measured on MI355X (7 dense projections of a 27B-class layer, 16 rows):
 // 8 waves per workgroup and a 2-record ring beat 4 waves or deeper rings;
-// long K (past 5120) runs 16 waves per workgroup over the whole of K (the o
-// and down projections 9.2 and 16.1 us, against 10.3 and 16.7 us with 8
-// waves in 4 K splits).
+// K from 5120 to 8192 runs 16 waves per workgroup over the whole of K (the o
+// projection, K = 6144: 9.1 us against 9.8 us with 8 waves in 4 K splits,
+// weights cold).
 #pragma once
 
 #include "common.h"
@@ -40,7 +40,7 @@
 namespace w4a4 {
 
 constexpr int SMALL_M_MAX = 16;
-constexpr int SM_WAVES = 8;             // waves per workgroup (SM_WAVES_LONG_K past 5120)
+constexpr int SM_WAVES = 8;             // waves per workgroup (SM_WAVES_LONG_K for K in (5120, 8192])
 constexpr int SM_WAVES_LONG_K = 16;
 constexpr int SM_DEPTH = 2;             // streaming records in flight per wave
 constexpr int SM_ITEM_TARGET = 512;     // workgroups wanted (two per CU on a 256-CU part)
@@ -86,13 +86,14 @@ __host__ __device__ inline SmallPlan small_m_plan(int64_t n, int64_t k, bool a8 
     const int64_t tiles = padded_n(n) / TILE_N, nq = sq_quads(k);
     // Measured on the 16-row verify set with the splits added in-kernel.  K
     // up to 5120 aims at a quarter as many workgroups (q unsplit and k, v in
-    // 4 splits beat 2 and 8 splits by 0.3 to 2 us each).  Past 5120, 16
-    // waves per workgroup at the same quarter (the o and down projections
-    // then run whole K: 9.2 and 16.1 us, against 10.3 and 16.7 us for 8
-    // waves at the full target, their best with 8; 16 waves for K up to 5120
-    // lose 0.6 to 0.8 us on q, k and v).  The 8-wave kernels past 5120 keep
-    // the full target.
-    const bool long_k = !a8 && k > 5120;
+    // 4 splits beat 2 and 8 splits by 0.3 to 2 us each).  K up to 8192 (at
+    // most 64 records per tile) takes 16 waves per workgroup at the same
+    // quarter, so the o projection runs whole K: 9.1 us against 9.8 us for 8
+    // waves in 4 splits, weights cold.  Longer K keeps 8 waves at the full
+    // target (down, K = 17408: 17.9 us in 4 splits against 19.9 us whole K
+    // with 16 waves, where each wave streams 8 or 9 records in turn); 16
+    // waves for K up to 5120 lose 0.6 to 0.8 us on q, k and v.
+    const bool long_k = !a8 && k > 5120 && nq <= 64;
     const int64_t target = k <= 5120 || long_k ? SM_ITEM_TARGET / 4 : SM_ITEM_TARGET;
     const int64_t want = (target + tiles - 1) / tiles;
     const int64_t splits = want < nq ? want : nq;

@@ -85,12 +85,14 @@ def test_gemm_validation(L):
     # one 8-byte arrival word per tile (256 bytes), then the partial sums
     assert L.w4a4_gemm_workspace_bytes(16, 1024, 5120) == 256 + 4 * 16 * 1024 * 4
     assert L.w4a4_gemm_workspace_bytes(3, 1024, 5120) == 256 + 4 * 3 * 1024 * 4
-    # K past 5120 runs 16 waves per workgroup at a quarter of the target:
-    # n = 5120 (160 tiles) whole K, n = 1024 (32 tiles) in 4 splits
-    assert L.w4a4_gemm_workspace_bytes(16, 5120, 17408) == 0
-    assert L.w4a4_gemm_workspace_bytes(16, 1024, 17408) == 256 + 4 * 16 * 1024 * 4
+    # n = 5120 (160 tiles), K = 17408 (136 records): 4 splits; 1280 bytes of words
+    assert L.w4a4_gemm_workspace_bytes(16, 5120, 17408) == 1280 + 4 * 16 * 5120 * 4
+    # K in (5120, 8192] runs 16 waves per workgroup at a quarter of the
+    # target: n = 5120 whole K, n = 1024 (32 tiles) in 4 splits
+    assert L.w4a4_gemm_workspace_bytes(16, 5120, 6144) == 0
+    assert L.w4a4_gemm_workspace_bytes(16, 1024, 6144) == 256 + 4 * 16 * 1024 * 4
     # the fused launch takes the same plan: its own sync words and flags only
-    assert L.w4a4_rotate_quantize_gemm_workspace_bytes(16, 5120, 17408) == 256 + 768
+    assert L.w4a4_rotate_quantize_gemm_workspace_bytes(16, 5120, 6144) == 256 + 256
     assert L.w4a4_gemm_workspace_bytes(17, 64, 33) == 0
     assert g(P(A), P(A), P(A), P(A), 64, 64, 64, 64, None, need, None) == INVALID
     assert g(P(A), P(A), P(A), P(A), 64, 64, 64, 64, P(A + 16), need, None) == MISALIGNED

@@ -168,7 +168,7 @@ def test_rotate_quantize_prepare_operand(ops, m, k, dtype):
 
 SHAPES = [(64, 256, 256), (1, 32, 32), (5, 33, 96), (16, 100, 288), (17, 64, 64),
           (33, 257, 160), (130, 96, 320), (300, 200, 128), (16, 1024, 5120),
-          (7, 1024, 6176)]  # long K at m <= 16: 16 waves, 4 K splits, a ragged last record
+          (7, 1024, 6176)]  # K past 5120 at m <= 16: 16 waves, 4 K splits, a ragged last record
 
 
 def _problem(m, n, k, seed):
@@ -354,7 +354,7 @@ def test_small_m_split_k_random_workspace(ops):
     zero and tags them with its own ticket)."""
     import torch
     gen = torch.Generator(device="cpu").manual_seed(11)
-    for i, (m, n, k) in enumerate([(16, 1024, 5120), (5, 1024, 17408)]):  # 8 and 16 waves per workgroup
+    for i, (m, n, k) in enumerate([(16, 1024, 5120), (5, 5120, 17408), (6, 1024, 6144)]):  # 8, 8, 16 waves
         need = ops.gemm_workspace_bytes(m, n, k)
         assert need > 0
         w, x = _problem(m, n, k, 400 + i)
