@@ -167,6 +167,12 @@ def events_ms(torch, fn, reps):
 
 
 GRAPH_CALLS = 64  # at least this many launches per timing graph of a short kernel
+GRAPH_REPS = 20   # timed replays per graph
+# --light (for counter passes under a profiler, where every dispatch is slow
+# and times mean nothing): few copies, launches and replays; the kernels and
+# their launch shapes are the same
+LIGHT = False
+LIGHT_COPIES = 4
 
 
 STEP_GRAPH_STEPS = 16  # at least this many whole steps per timing graph of a step
@@ -175,24 +181,25 @@ STEP_GRAPH_STEPS = 16  # at least this many whole steps per timing graph of a st
 def graph_steps(copies):
     """Steps per timing graph of a multi-kernel step over `copies` weight
     sets: whole rotations, at least STEP_GRAPH_STEPS."""
-    return max(1, -(-STEP_GRAPH_STEPS // copies)) * copies
+    return copies if LIGHT else max(1, -(-STEP_GRAPH_STEPS // copies)) * copies
 
 
 def cold_copies(read_bytes):
     """Copies to rotate over so that the bytes a call reads, over one
     rotation, are twice the last-level cache: each call then finds its
     weights evicted."""
-    return max(2, -(-2 * LLC_BYTES // max(1, int(read_bytes))))
+    n = max(2, -(-2 * LLC_BYTES // max(1, int(read_bytes))))
+    return min(n, LIGHT_COPIES) if LIGHT else n
 
 
 def graph_calls(copies):
     """Launches per timing graph over `copies` rotating buffers: whole
     rotations, at least GRAPH_CALLS, so that the replay's own cost (its
     submission and the event pair around it) is spread over many launches."""
-    return max(2, -(-GRAPH_CALLS // copies)) * copies
+    return copies if LIGHT else max(2, -(-GRAPH_CALLS // copies)) * copies
 
 
-def graph_time_us(torch, fn, reps=20, inner=1):
+def graph_time_us(torch, fn, reps=None, inner=1):
     """Capture `fn` (which enqueues `inner` identical units of work) in a HIP
     graph, replay it `reps` times with an event pair around each replay, and
     return the median time of one unit in microseconds.  Graph replay removes
@@ -205,6 +212,7 @@ def graph_time_us(torch, fn, reps=20, inner=1):
     for _ in range(2):
         g.replay()
     torch.cuda.synchronize()
+    reps = reps or GRAPH_REPS
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in ev:
         a.record()
@@ -239,7 +247,7 @@ def read_floor_us(torch, nbytes, copies):
     bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
     sink = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
     best = None
-    for blocks in (512, 1024, 2048, 4096):
+    for blocks in ((1024,) if LIGHT else (512, 1024, 2048, 4096)):
         def one(blocks=blocks):
             st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
             for i in range(graph_calls(nbuf)):
@@ -288,7 +296,11 @@ def run_verify16(torch, ops, synth):
         tot_us += us
         tot_bytes += b
         out[name] = {"k": k, "n": n, "us": round(us, 2), "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
-    floors = {name: read_floor_us(torch, n * k * 18 // 32, ncopies[name]) for name, k, n in synth.DENSE_PROJECTIONS}
+        log(f"[bench] verify_m16 {name}: {us:.2f} us over {nc} copies")
+    floors = {}
+    for name, k, n in synth.DENSE_PROJECTIONS:
+        floors[name] = read_floor_us(torch, n * k * 18 // 32, ncopies[name])
+        log(f"[bench] verify_m16 {name}: read floor {floors[name]}")
     if all(f is not None for f in floors.values()):
         for name, _, _ in synth.DENSE_PROJECTIONS:
             out[name]["read_floor_us"] = round(floors[name], 2)
@@ -888,7 +900,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first run 5 plain device copies of this many MiB (scales rocprofv3 byte counters)")
+    ap.add_argument("--light", action="store_true",
+                    help="extras with few weight copies, launches and replays (counter passes under a profiler)")
     args = ap.parse_args()
+    global LIGHT, GRAPH_REPS
+    if args.light:
+        LIGHT, GRAPH_REPS = True, 3
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the GEMM would shard over N with no exchange).", file=sys.stderr)
