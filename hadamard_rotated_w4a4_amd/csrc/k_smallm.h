@@ -17,9 +17,9 @@
 // computing the record, so no workgroup-wide staging phase or barrier
 // precedes the stream.  Per block and wave: one 32x32x32 int8 MFMA (the 16
 // rows, and 16 rows of don't-care lanes whose outputs are dropped, x the
-// tile's 32 columns); per two blocks one 32x32x4 bf16 MFMA forms the scale
-// products s (x) d of both (the split operands the dense kernel uses); per
-// output a convert and one fused multiply-add remain.  Codes enter the MFMA
+// tile's 32 columns) and one single-block 32x32x8 bf16 MFMA for the scale
+// products s (x) d (the split operands the dense kernel uses); per output a
+// convert and one fused multiply-add remain.  Codes enter the MFMA
 // as 16 x (signed nibble), so the integer sum is 256 S, and d is scaled by
 // 2^-8 (exact) to match.  The waves' sums meet in LDS; the workgroup stores
 // its 16 x 32 outputs, or its partial sums when K is split: then the last
