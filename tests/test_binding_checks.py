@@ -99,3 +99,20 @@ def test_gemm_id_checks():
     raises("codes: .* bytes", ops.gemm_id, packed, E, codes, scales, top_k, ids, N, K)  # per-slot rows need T*top_k
     raises("y: .* bytes", ops.gemm_id, packed, E, codes, scales, 1, ids, N, K, y=f32(T, top_k, N - 1))
     raises("workspace: .* bytes", ops.gemm_id_routed, packed, E, codes, scales, 1, T, top_k, N, K, u8(4))
+
+
+def test_a8_prepared_path_checks():
+    x = torch.zeros((M, K), dtype=torch.float16)
+    act8 = u8(ops.act8_operand_bytes(M, K))
+    assert ops.act8_operand_bytes(M, K) == 2 * ops.act_operand_bytes(M, K)
+    raises(GPU_ONLY, ops.rotate_quantize_prepare8, x, act8)
+    # the W4A4 operand's size is too small for the two planes of int8 codes
+    raises("act: .* bytes", ops.rotate_quantize_prepare8, x, u8(ops.act_operand_bytes(M, K)))
+    raises("act: dtype", ops.rotate_quantize_prepare8, x, torch.zeros(act8.numel(), dtype=torch.int8))
+    raises("codes: dtype", ops.rotate_quantize_prepare8, x, act8, codes=u8(M * K))
+    raises("codes: .* bytes", ops.rotate_quantize_prepare8, x, act8, codes=torch.zeros(M * K - 1, dtype=torch.int8))
+    packed = u8(ops.packed_weight_bytes(N, K))
+    raises(GPU_ONLY, ops.gemm_a8_prepared, packed, act8, M, N, K)
+    raises("act: .* bytes", ops.gemm_a8_prepared, packed, act8[:-1], M, N, K)
+    raises("packed: .* bytes", ops.gemm_a8_prepared, packed[:-1], act8, M, N, K)
+    raises("y: shape", ops.gemm_a8_prepared, packed, act8, M, N, K, y=f32(M, N - 1))
