@@ -74,7 +74,8 @@ def test_fused_verify_projection(ops, name, k, n):
     assert list(sync_words(ws)) == [1, 0, 0]
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (3, 70, 96), (8, 1024, 160), (15, 96, 17408), (16, 33, 288)])
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (3, 70, 96), (8, 1024, 160), (15, 96, 17408), (16, 33, 288),
+                                   (7, 300, 6144)])  # the last: 16-wave workgroups, 4 producer quads each
 def test_fused_ragged(ops, m, n, k):
     rng = np.random.default_rng(m * 7 + n + k)
     w = synth.weights(n, k, rng)
