@@ -273,30 +273,46 @@ def run_verify16(torch, ops, synth):
     nsets = max(2, -(-COLD_BYTES // layer_bytes))
     sets = [packed] + [{k_: v.clone() for k_, v in packed.items()} for _ in range(nsets - 1)]
     inputs = {name: torch.from_numpy(a).to(dev) for name, a in xs.items()}
-    q = {inp: ops.rotate_quantize_act(xin) for inp, xin in inputs.items()}
+    # each input quantised once with its record-ordered operand (the m <= 16
+    # prepared path); the codes and scales feed the from-codes path
+    acts = {inp: torch.empty(ops.small_act_operand_bytes(16, xin.shape[1]), dtype=torch.uint8, device=dev)
+            for inp, xin in inputs.items()}
+    q = {inp: ops.rotate_quantize_prepare_small(xin, acts[inp]) for inp, xin in inputs.items()}
     ys = {name: torch.empty((16, n), dtype=torch.float32, device=dev) for name, _, n in synth.DENSE_PROJECTIONS}
+    gws = torch.empty(max(ops.gemm_workspace_bytes(16, n, k) for _, k, n in synth.DENSE_PROJECTIONS),
+                      dtype=torch.uint8, device=dev)
     out = {"rows": 16, "weight_sets": nsets,
+           "path": "rotate_quantize_prepare_small once per input (codes, scales and the record-ordered operand), "
+                   "then gemm_prepared_small per projection; *_from_codes: gemm on the public codes and scales",
            "timing": "HIP graph replay; each projection alone over copies of its weights whose streamed bytes "
                      "per rotation are twice the 256 MB last-level cache, the steps over the layer's weight sets "
                      "(cold either way); read_floor_us: a plain read of the projection's weight bytes in the same "
                      "rotation"}
-    tot_us, tot_bytes = 0.0, 0
+    tot_us, tot_bytes, codes_us = 0.0, 0, 0.0
     ncopies = {}
     for name, k, n in synth.DENSE_PROJECTIONS:
-        c, sc = q[synth.DENSE_INPUT_OF[name]]
+        inp = synth.DENSE_INPUT_OF[name]
+        c, sc = q[inp]
         nc = ncopies[name] = cold_copies(n * k * 18 // 32)  # the 4-bit records this product streams
         copies = [packed[name]] + [packed[name].clone() for _ in range(nc - 1)]
 
-        def one(k=k, n=n, c=c, sc=sc, copies=copies, nc=nc, y=ys[name]):
+        def one(k=k, n=n, act=acts[inp], copies=copies, nc=nc, y=ys[name]):
             for i in range(graph_calls(nc)):
-                ops.gemm(copies[i % nc], c, sc, n, k, y=y)
+                ops.gemm_prepared_small(copies[i % nc], act, 16, n, k, y=y, workspace=gws)
+
+        def one_codes(k=k, n=n, c=c, sc=sc, copies=copies, nc=nc, y=ys[name]):
+            for i in range(graph_calls(nc)):
+                ops.gemm(copies[i % nc], c, sc, n, k, y=y, workspace=gws)
         us = graph_time_us(torch, one, inner=graph_calls(nc))
+        us_c = graph_time_us(torch, one_codes, inner=graph_calls(nc))
         del copies
         b = gemm_bytes(16, n, k)
         tot_us += us
+        codes_us += us_c
         tot_bytes += b
-        out[name] = {"k": k, "n": n, "us": round(us, 2), "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
-        log(f"[bench] verify_m16 {name}: {us:.2f} us over {nc} copies")
+        out[name] = {"k": k, "n": n, "us": round(us, 2), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                     "us_from_codes": round(us_c, 2)}
+        log(f"[bench] verify_m16 {name}: {us:.2f} us ({us_c:.2f} from codes) over {nc} copies")
     floors = {}
     for name, k, n in synth.DENSE_PROJECTIONS:
         floors[name] = read_floor_us(torch, n * k * 18 // 32, ncopies[name])
@@ -310,11 +326,20 @@ def run_verify16(torch, ops, synth):
 
     def step():
         for i in range(graph_steps(nsets)):
+            for inp, xin in inputs.items():
+                ops.rotate_quantize_prepare_small(xin, acts[inp], codes=q[inp][0], scales=q[inp][1])
+            for name, k, n in synth.DENSE_PROJECTIONS:
+                ops.gemm_prepared_small(sets[i % nsets][name], acts[synth.DENSE_INPUT_OF[name]], 16, n, k,
+                                        y=ys[name], workspace=gws)
+    step_us = graph_time_us(torch, step, inner=graph_steps(nsets))
+
+    def step_codes():
+        for i in range(graph_steps(nsets)):
             qq = {inp: ops.rotate_quantize_act(xin) for inp, xin in inputs.items()}
             for name, k, n in synth.DENSE_PROJECTIONS:
                 c, sc = qq[synth.DENSE_INPUT_OF[name]]
-                ops.gemm(sets[i % nsets][name], c, sc, n, k, y=ys[name])
-    step_us = graph_time_us(torch, step, inner=graph_steps(nsets))
+                ops.gemm(sets[i % nsets][name], c, sc, n, k, y=ys[name], workspace=gws)
+    step_codes_us = graph_time_us(torch, step_codes, inner=graph_steps(nsets))
 
     # rotate-quantise fused into the product (one launch per distinct input:
     # its first projection quantises, the others reuse the codes it wrote)
@@ -326,8 +351,6 @@ def run_verify16(torch, ops, synth):
             for inp, xin in inputs.items()}
     fq_ws = torch.zeros(max(ops.rotate_quantize_gemm_workspace_bytes(16, n, k) for _, k, n in synth.DENSE_PROJECTIONS),
                         dtype=torch.uint8, device=dev)  # zero before its first use
-    gws = torch.empty(max(ops.gemm_workspace_bytes(16, n, k) for _, k, n in synth.DENSE_PROJECTIONS),
-                      dtype=torch.uint8, device=dev)
 
     def fused_step():
         for i in range(graph_steps(nsets)):
@@ -349,6 +372,8 @@ def run_verify16(torch, ops, synth):
     out["hbm_frac"] = round(tot_bytes / (tot_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
     out["step_us"] = round(step_us, 2)
     out["tokens/s"] = round(16 / (step_us * 1e-6), 1)
+    out["gemm_us_total_from_codes"] = round(codes_us, 2)
+    out["step_us_from_codes"] = round(step_codes_us, 2)
     del sets, packed
 
     # The same set with the projections that read one input packed side by
@@ -368,22 +393,22 @@ def run_verify16(torch, ops, synth):
     f_us = 0.0
     for g, _, inp in groups:
         k, n = shape[g]
-        c, sc = q[inp]
         nc = cold_copies(n * k * 18 // 32)
         copies = [fused[g]] + [fused[g].clone() for _ in range(nc - 1)]
 
-        def one(g=g, k=k, n=n, c=c, sc=sc, copies=copies, nc=nc):
+        def one(g=g, k=k, n=n, act=acts[inp], copies=copies, nc=nc):
             for i in range(graph_calls(nc)):
-                ops.gemm(copies[i % nc], c, sc, n, k, y=fys[g], workspace=fws[g])
+                ops.gemm_prepared_small(copies[i % nc], act, 16, n, k, y=fys[g], workspace=fws[g])
         f_us += graph_time_us(torch, one, inner=graph_calls(nc))
         del copies
 
     def fstep():
         for i in range(graph_steps(nsets)):
-            qq = {inp: ops.rotate_quantize_act(xin) for inp, xin in inputs.items()}
+            for inp, xin in inputs.items():
+                ops.rotate_quantize_prepare_small(xin, acts[inp], codes=q[inp][0], scales=q[inp][1])
             for g, _, inp in groups:
                 k, n = shape[g]
-                ops.gemm(fsets[i % nsets][g], *qq[inp], n, k, y=fys[g], workspace=fws[g])
+                ops.gemm_prepared_small(fsets[i % nsets][g], acts[inp], 16, n, k, y=fys[g], workspace=fws[g])
     fstep_us = graph_time_us(torch, fstep, inner=graph_steps(nsets))
     fws2 = torch.zeros(max(ops.rotate_quantize_gemm_workspace_bytes(16, n, k) for k, n in shape.values()),
                        dtype=torch.uint8, device=dev)

@@ -45,6 +45,9 @@ def lib() -> ctypes.CDLL:
             "w4a4_act_operand_bytes": ([I64, I64], SZ),
             "w4a4_gemm_prepare_act": ([P, P, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_prepared": ([P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
+            "w4a4_small_act_operand_bytes": ([I64, I64], SZ),
+            "w4a4_rotate_quantize_prepare_small": ([P, ST, I64, I64, I64, P, P, P, SZ, P], ST),
+            "w4a4_gemm_prepared_small": ([P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_prepared_workspace_bytes": ([I64, I64, I64], SZ),
             "w4a4_gemm": ([P, P, P, P, I64, I64, I64, I64, P, SZ, P], ST),
             "w4a4_gemm_noalloc_scratch_bytes": ([], SZ),
@@ -364,6 +367,46 @@ def gemm_prepared(packed: torch.Tensor, act: torch.Tensor, m: int, n: int, k: in
     _check(lib().w4a4_gemm_prepared(_ptr(packed), _ptr(act), _ptr(y), m, n, k, y.stride(0), _ptr(workspace),
                                     0 if workspace is None else workspace.numel(), _stream(act.device)),
            "w4a4_gemm_prepared")
+    return y
+
+
+def small_act_operand_bytes(m: int, k: int) -> int:
+    return int(lib().w4a4_small_act_operand_bytes(m, k))
+
+
+def rotate_quantize_prepare_small(x: torch.Tensor, act: torch.Tensor, k: int | None = None,
+                                  codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """rotate_quantize_act for m <= 16 rows that also writes the record-ordered
+    operand of the m <= 16 product into `act`."""
+    dt, k = _act_dtype(x), _k_of(x, k)
+    if x.shape[0] > 16:
+        raise W4A4Error(f"rotate_quantize_prepare_small: {x.shape[0]} rows (at most 16)")
+    _need(act, "act", torch.uint8, small_act_operand_bytes(x.shape[0], k))
+    m, codes, scales = _quantiser_outputs(x, k, codes, scales, k // 2, torch.uint8)
+    _require_cuda(act)
+    _check(lib().w4a4_rotate_quantize_prepare_small(_ptr(x), dt, m, k, x.stride(0), _ptr(codes), _ptr(scales),
+                                                    _ptr(act), act.numel(), _stream(x.device)),
+           "w4a4_rotate_quantize_prepare_small")
+    return codes, scales
+
+
+def gemm_prepared_small(packed: torch.Tensor, act: torch.Tensor, m: int, n: int, k: int,
+                        y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The m <= 16 product on a record-ordered operand: fp32 [m, n] (row
+    stride y.stride(0)); the same result as gemm on the same codes and scales.
+    The workspace (K splits) is allocated here when needed and not given."""
+    if m > 16:
+        raise W4A4Error(f"gemm_prepared_small: {m} rows (at most 16)")
+    _need(packed, "packed", torch.uint8, packed_weight_bytes(n, k) if m and n else 0)
+    _need(act, "act", torch.uint8, small_act_operand_bytes(m, k))
+    need = gemm_workspace_bytes(m, n, k)
+    _check_out(y, workspace, m, n, need)
+    _require_cuda(packed, act, y, workspace)
+    y = _output(y, m, n, act.device)
+    workspace = _workspace(workspace, need, act.device)
+    _check(lib().w4a4_gemm_prepared_small(_ptr(packed), _ptr(act), _ptr(y), m, n, k, y.stride(0),
+                                          _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                          _stream(act.device)), "w4a4_gemm_prepared_small")
     return y
 
 

@@ -214,13 +214,17 @@ __device__ __forceinline__ void put_quad_row(const uint32_t f[8], int L, uint8_t
 // ROTATE = false: the unrotated W4A4 ablation (section "MoE: W4A4 on the
 // experts"): no butterflies, and the stored scale is d itself (there is no
 // normalisation to fold in).
+// With `sma` set (W4A4, m <= 16): also the record-ordered operand of the
+// m <= 16 product (common.h); the blocks then run over whole quads, and rows
+// m .. 15 and blocks past nb get zero codes and scales.
 constexpr int RQ_BLOCKS = 2;  // blocks per workgroup
 template <typename T, int QMAX = 7, bool ROTATE = true>
 __global__ __launch_bounds__(128 * RQ_BLOCKS) void rotate_quantize_kernel(const T *__restrict__ x, int64_t m,
                                                                           int64_t k, int64_t ldx, int mode,
                                                                           uint8_t *__restrict__ codes,
                                                                           float *__restrict__ scales,
-                                                                          uint8_t *__restrict__ act) {
+                                                                          uint8_t *__restrict__ act,
+                                                                          uint8_t *__restrict__ sma = nullptr) {
     static_assert(QMAX == 7 || QMAX == 127, "int4 or int8 codes");
     const int64_t nb = k / QK;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, L = lane & 3;
@@ -259,6 +263,14 @@ __global__ __launch_bounds__(128 * RQ_BLOCKS) void rotate_quantize_kernel(const 
     }
 
     if (codes) store_codes4(q, s, L, live, codes + row * (k / 2) + b * 16, scales + row * nb + b);
+
+    if (sma && row < SMA_ROWS && b < sq_quads(k) * SQ_BLOCKS) {  // uniform per quad
+        const int64_t qd = b / SQ_BLOCKS;
+        const int j = (int)(b % SQ_BLOCKS);
+        store_codes4(q, s, L, true, sma + qd * SMA_CODE_BYTES + row * 64 + j * 16,
+                     reinterpret_cast<float *>(sma + sq_quads(k) * SMA_CODE_BYTES + qd * SMA_SCALE_BYTES +
+                                               row * 16 + j * 4));
+    }
 
     if (act && b < mx_blocks(k)) {  // the operand record of (row tile, block)
         uint32_t f[8];

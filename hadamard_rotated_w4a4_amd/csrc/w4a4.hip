@@ -290,9 +290,11 @@ w4a4_status w4a4_repack_q4_0_h32(const void *q4_0, void *packed, int64_t n, int6
 namespace {
 // a8: int8 codes ([m][k] bytes) instead of int4 ([m][k/2]); rotate = false:
 // no rotation (the unrotated ablation; int4 only)
+// sma: the record-ordered operand of an m <= 16 product (W4A4, rotated;
+// instead of `act`)
 w4a4_status rotate_quantize(bool a8, const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
                             uint8_t *codes, float *scales, void *act, size_t act_bytes, void *stream,
-                            bool rotate = true) {
+                            bool rotate = true, void *sma = nullptr) {
     if (dt != W4A4_DTYPE_F32 && dt != W4A4_DTYPE_F16) return W4A4_ERR_UNSUPPORTED_DTYPE;
     if (m < 0 || k < 0 || ldx < k || !within_bounds(m, 0, k)) return W4A4_ERR_INVALID_VALUE;
     if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
@@ -306,11 +308,16 @@ w4a4_status rotate_quantize(bool a8, const void *x, w4a4_dtype dt, int64_t m, in
         if (act_bytes < (a8 ? w4a4_act8_operand_bytes(m, k) : w4a4_act_operand_bytes(m, k)))
             return W4A4_ERR_WORKSPACE_TOO_SMALL;
     }
+    if (sma) {
+        if (a8 || !rotate || act || m > SMALL_M_MAX) return W4A4_ERR_INVALID_VALUE;
+        if (!aligned(sma, 256)) return W4A4_ERR_MISALIGNED;
+        if (act_bytes < w4a4_small_act_operand_bytes(m, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
+    }
     const size_t esz = dt == W4A4_DTYPE_F32 ? 4 : 2;
     // vector loads of a block: 16-byte (every block start 16-byte aligned),
     // 4-element (every 4-element group aligned), or none
     const int vec = aligned(x, 16) && (ldx * esz) % 16 == 0 ? 2 : aligned(x, 4 * esz) && (ldx % 4) == 0 ? 1 : 0;
-    const int64_t blocks = act ? mx_blocks(k) : k / QK;
+    const int64_t blocks = act ? mx_blocks(k) : sma ? sq_quads(k) * SQ_BLOCKS : k / QK;
     const dim3 grid((unsigned)((blocks + RQ_BLOCKS - 1) / RQ_BLOCKS), (unsigned)((m + 31) / 32));
     hipStream_t s = as_stream(stream);
     uint8_t *a = static_cast<uint8_t *>(act);
@@ -320,9 +327,9 @@ w4a4_status rotate_quantize(bool a8, const void *x, w4a4_dtype dt, int64_t m, in
     if (!rotate && dt == W4A4_DTYPE_F32) rotate_quantize_kernel<float, 7, false><<<grid, nt, 0, s>>>(xf, m, k, ldx, vec, codes, scales, a);
     else if (!rotate) rotate_quantize_kernel<__half, 7, false><<<grid, nt, 0, s>>>(xh, m, k, ldx, vec, codes, scales, a);
     else if (dt == W4A4_DTYPE_F32 && a8) rotate_quantize_kernel<float, 127><<<grid, nt, 0, s>>>(xf, m, k, ldx, vec, codes, scales, a);
-    else if (dt == W4A4_DTYPE_F32) rotate_quantize_kernel<float, 7><<<grid, nt, 0, s>>>(xf, m, k, ldx, vec, codes, scales, a);
+    else if (dt == W4A4_DTYPE_F32) rotate_quantize_kernel<float, 7><<<grid, nt, 0, s>>>(xf, m, k, ldx, vec, codes, scales, a, static_cast<uint8_t *>(sma));
     else if (a8) rotate_quantize_kernel<__half, 127><<<grid, nt, 0, s>>>(xh, m, k, ldx, vec, codes, scales, a);
-    else rotate_quantize_kernel<__half, 7><<<grid, nt, 0, s>>>(xh, m, k, ldx, vec, codes, scales, a);
+    else rotate_quantize_kernel<__half, 7><<<grid, nt, 0, s>>>(xh, m, k, ldx, vec, codes, scales, a, static_cast<uint8_t *>(sma));
     return hip_status("rotate_quantize_kernel");
 }
 }  // namespace
@@ -349,6 +356,19 @@ w4a4_status w4a4_rotate_quantize_prepare(const void *x, w4a4_dtype dt, int64_t m
     return rotate_quantize(false, x, dt, m, k, ldx, codes, scales, act, act_bytes, stream);
 }
 
+size_t w4a4_small_act_operand_bytes(int64_t m, int64_t k) {
+    if (m < 0 || m > SMALL_M_MAX || k < 0 || k % QK) return 0;
+    return (size_t)small_act_bytes(k);
+}
+
+w4a4_status w4a4_rotate_quantize_prepare_small(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                                               uint8_t *codes, float *scales, void *act, size_t act_bytes,
+                                               void *stream) {
+    if (m > SMALL_M_MAX) return W4A4_ERR_INVALID_VALUE;
+    if (!act && m > 0 && k > 0) return W4A4_ERR_INVALID_VALUE;
+    return rotate_quantize(false, x, dt, m, k, ldx, codes, scales, nullptr, act_bytes, stream, true, act);
+}
+
 w4a4_status w4a4_rotate_quantize_prepare8(const void *x, w4a4_dtype dt, int64_t m, int64_t k, int64_t ldx,
                                           int8_t *codes, float *scales, void *act, size_t act_bytes,
                                           void *stream) {
@@ -370,6 +390,67 @@ size_t w4a4_gemm_prepared_workspace_bytes(int64_t m, int64_t n, int64_t k) {
     return split_partial_bytes(m, n, k);
 }
 
+}  // extern "C"
+
+namespace {
+// The m <= 16 product (sizes and buffers checked by the caller), from the
+// public codes and scales or (act_rec) from the record-ordered operand.
+w4a4_status launch_small_m(const void *packed_w, const uint8_t *codes, const float *scales, const void *act_rec,
+                           float *y, int64_t m, int64_t n, int64_t k, int64_t ldy, void *workspace,
+                           size_t workspace_bytes, hipStream_t s) {
+    const SmallPlan plan = small_m_plan(n, k);
+    if (plan.splits > 1) {
+        if (!workspace) return W4A4_ERR_INVALID_VALUE;
+        if (!aligned(workspace, 256)) return W4A4_ERR_MISALIGNED;
+        if (workspace_bytes < w4a4_gemm_workspace_bytes(m, n, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
+    }
+    SmallArgs a{};
+    a.codes = codes;
+    a.scales = scales;
+    a.act_rec = static_cast<const uint8_t *>(act_rec);
+    a.sq = static_cast<const uint8_t *>(packed_w) + sq_section_offset(n, k);
+    a.y = y;
+    a.ldy = ldy;
+    a.m = m;
+    a.n = n;
+    a.k = k;
+    a.range = plan.range;
+    set_small_m_split(a, plan, workspace);
+    const dim3 grid((unsigned)plan.tiles, (unsigned)plan.splits);
+    const bool rec = act_rec != nullptr;
+    if (plan.waves == SM_WAVES_LONG_K && rec)
+        gemm_small_m_kernel<SM_WAVES_LONG_K, SM_DEPTH, false, true><<<grid, 64 * SM_WAVES_LONG_K, small_m_lds_bytes(plan), s>>>(a);
+    else if (plan.waves == SM_WAVES_LONG_K)
+        gemm_small_m_kernel<SM_WAVES_LONG_K, SM_DEPTH><<<grid, 64 * SM_WAVES_LONG_K, small_m_lds_bytes(plan), s>>>(a);
+    else if (rec)
+        gemm_small_m_kernel<SM_WAVES, SM_DEPTH, false, true><<<grid, 64 * SM_WAVES, small_m_lds_bytes(plan), s>>>(a);
+    else
+        gemm_small_m_kernel<SM_WAVES, SM_DEPTH><<<grid, 64 * SM_WAVES, small_m_lds_bytes(plan), s>>>(a);
+    return hip_status("gemm_small_m_kernel");
+}
+}  // namespace
+
+extern "C" {
+
+w4a4_status w4a4_gemm_prepared_small(const void *packed_w, const void *act, float *y, int64_t m, int64_t n,
+                                     int64_t k, int64_t ldy, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+    if (m < 0 || m > SMALL_M_MAX || n < 0 || k < 0 || ldy < n || !within_bounds(m, n, k))
+        return W4A4_ERR_INVALID_VALUE;
+    if (k % QK) return W4A4_ERR_K_NOT_MULTIPLE_OF_32;
+    if (m == 0 || n == 0) return W4A4_OK;
+    if (!y) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(y, 4)) return W4A4_ERR_MISALIGNED;
+    hipStream_t s = as_stream(stream);
+    if (k == 0) {  // empty sum
+        launch_zero_rows(y, m, n, ldy, s);
+        return hip_status("zero_rows_kernel");
+    }
+    if (!packed_w || !act) return W4A4_ERR_INVALID_VALUE;
+    if (!aligned(packed_w, 16) || !aligned(act, 256)) return W4A4_ERR_MISALIGNED;
+    return launch_small_m(packed_w, nullptr, nullptr, act, y, m, n, k, ldy, workspace, workspace_bytes, s);
+}
+
 w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *scales, float *y,
                       int64_t m, int64_t n, int64_t k, int64_t ldy, void *workspace, size_t workspace_bytes,
                       void *stream) {
@@ -386,31 +467,8 @@ w4a4_status w4a4_gemm(const void *packed_w, const uint8_t *codes, const float *s
         launch_zero_rows(y, m, n, ldy, s);
         return hip_status("zero_rows_kernel");
     }
-    if (m <= SMALL_M_MAX) {
-        const SmallPlan plan = small_m_plan(n, k);
-        if (plan.splits > 1) {
-            if (!workspace) return W4A4_ERR_INVALID_VALUE;
-            if (!aligned(workspace, 256)) return W4A4_ERR_MISALIGNED;
-            if (workspace_bytes < w4a4_gemm_workspace_bytes(m, n, k)) return W4A4_ERR_WORKSPACE_TOO_SMALL;
-        }
-        SmallArgs a{};
-        a.codes = codes;
-        a.scales = scales;
-        a.sq = static_cast<const uint8_t *>(packed_w) + sq_section_offset(n, k);
-        a.y = y;
-        a.ldy = ldy;
-        a.m = m;
-        a.n = n;
-        a.k = k;
-        a.range = plan.range;
-        set_small_m_split(a, plan, workspace);
-        const dim3 grid((unsigned)plan.tiles, (unsigned)plan.splits);
-        if (plan.waves == SM_WAVES_LONG_K)
-            gemm_small_m_kernel<SM_WAVES_LONG_K, SM_DEPTH><<<grid, 64 * SM_WAVES_LONG_K, small_m_lds_bytes(plan), s>>>(a);
-        else
-            gemm_small_m_kernel<SM_WAVES, SM_DEPTH><<<grid, 64 * SM_WAVES, small_m_lds_bytes(plan), s>>>(a);
-        return hip_status("gemm_small_m_kernel");
-    }
+    if (m <= SMALL_M_MAX) return launch_small_m(packed_w, codes, scales, nullptr, y, m, n, k, ldy, workspace,
+                                                workspace_bytes, s);
     // workspace: the activation operand, then the split-K partial sums
     if (!workspace) return W4A4_ERR_INVALID_VALUE;
     if (!aligned(workspace, 256)) return W4A4_ERR_MISALIGNED;

@@ -271,6 +271,40 @@ w4a4_status w4a4_gemm_prepared(const void *packed_w, const void *act, float *y, 
                                void *stream);
 
 /*
+ * The same two steps for m <= 16 (a speculative-verify-sized batch), where
+ * the product streams the weights once and each wave reads the activations
+ * of every 4-block group of K it computes: the quantiser also writes the
+ * codes and scales in the order the waves load them, so those loads are
+ * contiguous (section "Hadamard-rotated Q4_0: W4A4 prompt processing": the
+ * rotated activations rounded to 4 bits per block, with one scale each).
+ *
+ * w4a4_small_act_operand_bytes: bytes of that operand for m <= 16 rows and
+ * width k: 1280 per group of 4 blocks, g = ceil(k / 128) groups (0 for
+ * m > 16 or invalid sizes).  Host only, pure.
+ *
+ * w4a4_rotate_quantize_prepare_small: w4a4_rotate_quantize_act for m <= 16
+ * (m > 16: W4A4_ERR_INVALID_VALUE) that also writes
+ *   act   out, w4a4_small_act_operand_bytes(m, k) bytes, 256-byte aligned:
+ *         for group q of 4 blocks, row r's 16 code bytes of block 4 q + j
+ *         at 1024 q + 64 r + 16 j, and its fp32 scale at 1024 g + 256 q +
+ *         16 r + 4 j; rows m .. 15 and blocks past k / 32 are zero.
+ * codes and scales are written as by w4a4_rotate_quantize_act, bit for bit.
+ *
+ * w4a4_gemm_prepared_small: the m <= 16 product of packed_w with such an
+ * operand (m > 16: W4A4_ERR_INVALID_VALUE); y, workspace and its size query
+ * (w4a4_gemm_workspace_bytes) as for w4a4_gemm with m <= 16, and the result
+ * is w4a4_gemm's on the same codes and scales, bit for bit (the same block
+ * dots, scale products and summation order).
+ */
+size_t w4a4_small_act_operand_bytes(int64_t m, int64_t k);
+w4a4_status w4a4_rotate_quantize_prepare_small(const void *x, w4a4_dtype dt, int64_t m, int64_t k,
+                                               int64_t ldx, uint8_t *codes, float *scales, void *act,
+                                               size_t act_bytes, void *stream);
+w4a4_status w4a4_gemm_prepared_small(const void *packed_w, const void *act, float *y, int64_t m,
+                                     int64_t n, int64_t k, int64_t ldy, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
  * W4A8-H32: the exact int8 path for a rotated file (section "Hadamard-rotated
  * Q4_0: W4A4 prompt processing" names it as the alternative to W4A4 for the
  * same file).  The activations get the same rotation and are rounded to 8

@@ -352,3 +352,35 @@ def test_noalloc_refuses_sizes_past_its_scratch(L):
     # invalid sizes are reported as w4a4_gemm reports them
     assert L.w4a4_gemm_noalloc(P(A), P(A), P(A), P(A), 64, 64, 33, 64, None) == KMUL
     assert L.w4a4_gemm_noalloc(None, None, None, None, 0, 64, 64, 64, None) == OK
+
+
+def test_small_prepared_sizes_and_validation(L):
+    # one 1280-byte record (16 rows x 4 blocks of codes, then their scales)
+    # per group of 4 blocks; none for m > 16
+    assert L.w4a4_small_act_operand_bytes(16, 5120) == 40 * 1280
+    assert L.w4a4_small_act_operand_bytes(1, 160) == 2 * 1280   # 5 blocks: 2 groups
+    assert L.w4a4_small_act_operand_bytes(17, 5120) == 0
+    assert L.w4a4_small_act_operand_bytes(16, 33) == 0
+    assert L.w4a4_small_act_operand_bytes(-1, 64) == 0
+    q = L.w4a4_rotate_quantize_prepare_small
+    ab = L.w4a4_small_act_operand_bytes(8, 5120)
+    assert q(P(A), 1, 17, 5120, 5120, P(A), P(A), P(A), 1 << 30, None) == INVALID   # more than 16 rows
+    assert q(P(A), 1, 8, 5120, 5120, P(A), P(A), None, ab, None) == INVALID       # act required
+    assert q(P(A), 1, 8, 5120, 5120, P(A), P(A), P(A + 16), ab, None) == MISALIGNED
+    assert q(P(A), 1, 8, 5120, 5120, P(A), P(A), P(A), ab - 1, None) == WS
+    assert q(P(A), 7, 8, 5120, 5120, P(A), P(A), P(A), ab, None) == DTYPE
+    assert q(P(A), 1, 8, 48, 64, P(A), P(A), P(A), ab, None) == KMUL
+    assert q(None, 1, 0, 64, 64, None, None, None, 0, None) == OK
+    g = L.w4a4_gemm_prepared_small
+    need = L.w4a4_gemm_workspace_bytes(16, 1024, 5120)   # K splits of a narrow product
+    assert need > 0
+    assert g(P(A), P(A), P(A), 17, 1024, 5120, 1024, P(A), need, None) == INVALID   # more than 16 rows
+    assert g(P(A), P(A), P(A), 16, 1024, 5120, 1000, P(A), need, None) == INVALID   # ldy < n
+    assert g(P(A), P(A), P(A), 16, 1024, 48, 1024, P(A), need, None) == KMUL
+    assert g(P(A), None, P(A), 16, 1024, 5120, 1024, P(A), need, None) == INVALID
+    assert g(P(A), P(A + 16), P(A), 16, 1024, 5120, 1024, P(A), need, None) == MISALIGNED
+    assert g(P(ODD), P(A), P(A), 16, 1024, 5120, 1024, P(A), need, None) == MISALIGNED
+    assert g(P(A), P(A), P(A), 16, 1024, 5120, 1024, None, need, None) == INVALID    # split sums need it
+    assert g(P(A), P(A), P(A), 16, 1024, 5120, 1024, P(A), need - 1, None) == WS
+    assert g(P(A), P(A), P(A), 16, 1024, 5120, 1024, P(A + 16), need, None) == MISALIGNED
+    assert g(None, None, None, 0, 1024, 5120, 1024, None, 0, None) == OK

@@ -116,3 +116,19 @@ def test_a8_prepared_path_checks():
     raises("act: .* bytes", ops.gemm_a8_prepared, packed, act8[:-1], M, N, K)
     raises("packed: .* bytes", ops.gemm_a8_prepared, packed[:-1], act8, M, N, K)
     raises("y: shape", ops.gemm_a8_prepared, packed, act8, M, N, K, y=f32(M, N - 1))
+
+
+def test_small_prepared_calls_refuse_short_or_mistyped_buffers():
+    m, n, k = 16, 70, 160
+    act = u8(ops.small_act_operand_bytes(m, k))
+    x = torch.zeros((m, k), dtype=torch.float16)
+    raises(GPU_ONLY, ops.rotate_quantize_prepare_small, x, act)
+    raises("act: .* bytes", ops.rotate_quantize_prepare_small, x, u8(act.numel() - 1))
+    raises("at most 16", ops.rotate_quantize_prepare_small, torch.zeros((17, k), dtype=torch.float16), act)
+    packed = u8(ops.packed_weight_bytes(n, k))
+    raises(GPU_ONLY, ops.gemm_prepared_small, packed, act, m, n, k)
+    raises("act: .* bytes", ops.gemm_prepared_small, packed, u8(act.numel() - 1), m, n, k)
+    raises("act: dtype", ops.gemm_prepared_small, packed, act.to(torch.int8), m, n, k)
+    raises("packed: .* bytes", ops.gemm_prepared_small, packed, act, m, n + 32, k)
+    raises("y: shape", ops.gemm_prepared_small, packed, act, m, n, k, y=f32(m, n - 1))
+    raises("at most 16", ops.gemm_prepared_small, packed, act, 17, n, k)
