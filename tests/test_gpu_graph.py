@@ -111,6 +111,31 @@ def test_small_m_split_k_step_replays(ops):
     replay_matches_eager(step, x, inputs, [codes, scales, y])
 
 
+def test_small_m_prepared_step_replays(ops):
+    """The m <= 16 prepared path: the quantiser writes codes, scales and the
+    record-ordered operand, then two products read the operand (one whole-K,
+    one with K splits summed in the same launch)."""
+    m, k = 13, 5120
+    shapes = ((17408, "whole K"), (1024, "K split"))
+    say(f"graph: rotate_quantize_prepare_small + gemm_prepared_small m={m} k={k}")
+    rng = np.random.default_rng(5)
+    packed = [ops.prepare_weights(torch.from_numpy(synth.weights(n, k, rng)).cuda()) for n, _ in shapes]
+    inputs = _inputs(m, k, 6)
+    x = torch.empty_like(inputs[0])
+    codes = torch.empty((m, k // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((m, k // 32), dtype=torch.float32, device="cuda")
+    act = torch.empty(ops.small_act_operand_bytes(m, k), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(1, max(ops.gemm_workspace_bytes(m, n, k) for n, _ in shapes)), dtype=torch.uint8,
+                     device="cuda")
+    ys = [torch.empty((m, n), dtype=torch.float32, device="cuda") for n, _ in shapes]
+
+    def step():
+        ops.rotate_quantize_prepare_small(x, act, codes=codes, scales=scales)
+        for (n, _), p, y in zip(shapes, packed, ys):
+            ops.gemm_prepared_small(p, act, m, n, k, y=y, workspace=ws)
+    replay_matches_eager(step, x, inputs, [codes, scales, act] + ys)
+
+
 def test_mul_mat_id_step_replays(ops):
     e, t, top_k, n, k = 16, 64, 4, 256, 512
     say(f"graph: rotate-quantise + gemm_id E={e} T={t} top_k={top_k} n={n} k={k}")
