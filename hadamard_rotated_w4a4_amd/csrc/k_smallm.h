@@ -59,7 +59,8 @@ struct SmallArgs {
     unsigned long long *arrivals = nullptr;
     unsigned long long ticket = 0;  // 48 bits, non-zero, drawn per call
     int64_t ldy, m, n, k;
-    int64_t range;          // records per split
+    int64_t range;          // records per split (tiles past `whole`)
+    int64_t whole = 0;      // tiles 0 .. whole - 1 run whole K (no partial sums)
     // fused rotate-quantise only (gemm_small_m_fused_kernel): the
     // activations, their row stride and load mode (as the quantiser takes
     // them), where the producers write the codes and scales (= codes,
@@ -78,10 +79,16 @@ struct SmallArgs {
 // Narrow projections split K so that about a target number of workgroups
 // run.  Pure function of the sizes and the kernel (the workspace size
 // depends on it).
+// Tiles 0 .. whole - 1 run whole K in one workgroup each; the other tiles
+// split K in `splits` ranges of `range` records.
 struct SmallPlan {
     int64_t tiles, splits, range;
     int waves;
+    int64_t whole;
 };
+// CUs the plan balances over (MI355X): the leftover tiles of whole rounds of
+// this many are split so that every CU gets the same number of records.
+constexpr int64_t SM_REF_CUS = 256;
 // a8: int8 activations (8 waves per workgroup at every K).
 __host__ __device__ inline SmallPlan small_m_plan(int64_t n, int64_t k, bool a8 = false) {
     const int64_t tiles = padded_n(n) / TILE_N, nq = sq_quads(k);
@@ -95,12 +102,27 @@ __host__ __device__ inline SmallPlan small_m_plan(int64_t n, int64_t k, bool a8 
     // with 16 waves, where each wave streams 8 or 9 records in turn); 16
     // waves for K up to 5120 lose 0.6 to 0.8 us on q, k and v.
     const bool long_k = !a8 && k > 5120 && nq <= 64;
+    const int waves = long_k ? SM_WAVES_LONG_K : SM_WAVES;
     const int64_t target = k <= 5120 || long_k ? SM_ITEM_TARGET / 4 : SM_ITEM_TARGET;
     const int64_t want = (target + tiles - 1) / tiles;
     const int64_t splits = want < nq ? want : nq;
     const int64_t range = (nq + splits - 1) / splits;
-    return SmallPlan{tiles, (nq + range - 1) / range, range, long_k ? SM_WAVES_LONG_K : SM_WAVES};
+    if ((nq + range - 1) / range > 1) return SmallPlan{tiles, (nq + range - 1) / range, range, waves, 0};
+    // Unsplit: more tiles than CUs leave the L = tiles mod SM_REF_CUS tiles
+    // of the last round to a few CUs (a 544-tile projection: 32 CUs hold a
+    // third workgroup; 512 tiles run 1.17x faster per byte).  Those L tiles
+    // split K in SM_REF_CUS / L parts instead, one piece per CU, and their
+    // parts are added in the same launch as other K splits are.
+    const int64_t left = tiles % SM_REF_CUS;
+    if (tiles > SM_REF_CUS && left > 0 && SM_REF_CUS / left >= 2 && nq >= 2) {
+        const int64_t parts = SM_REF_CUS / left < nq ? SM_REF_CUS / left : nq;
+        const int64_t r = (nq + parts - 1) / parts;
+        return SmallPlan{tiles, (nq + r - 1) / r, r, waves, tiles - left};
+    }
+    return SmallPlan{tiles, 1, nq, waves, tiles};
 }
+// Workgroups of a plan: the whole tiles, then the split tiles' ranges.
+__host__ __device__ inline int64_t small_m_items(const SmallPlan &p) { return p.whole + (p.tiles - p.whole) * p.splits; }
 
 // Spin limit of a consumer's wait for its activations (each round is one
 // device-scope load and a short sleep): the wait always ends, and a wait that
@@ -408,10 +430,30 @@ __device__ __forceinline__ void small_m_tile(const SmallArgs &a, int64_t tile, i
 // workgroups of a 17408-column projection run in one round.  16 waves (long
 // K, at most a few hundred workgroups): four waves per SIMD, one workgroup
 // per CU.
+// Item c of a plan (small_m_items): whole tiles first, then the split
+// tiles' ranges, range-major (range 0 of every split tile, then range 1, ...).
+// Returns the tile and range and the arguments for that item.
+__device__ __forceinline__ SmallArgs small_m_item(const SmallArgs &a, int64_t c, int64_t &tile, int64_t &z) {
+    SmallArgs b = a;
+    if (c < a.whole) {
+        tile = c;
+        z = 0;
+        b.range = sq_quads(a.k);
+        b.partial = nullptr;
+    } else {
+        const int64_t split_tiles = padded_n(a.n) / TILE_N - a.whole, p = c - a.whole;
+        tile = a.whole + p % split_tiles;
+        z = p / split_tiles;
+    }
+    return b;
+}
+
 template <int WAVES, int DEPTH, bool A8 = false, bool REC = false>
 __global__ __launch_bounds__(64 * WAVES, A8 ? 1 : WAVES > 8 ? 4 : 6) void gemm_small_m_kernel(SmallArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    small_m_tile<WAVES, DEPTH, A8, false, REC>(a, blockIdx.x, blockIdx.y, smem, 0);
+    int64_t tile, z;
+    const SmallArgs b = small_m_item(a, blockIdx.x, tile, z);
+    small_m_tile<WAVES, DEPTH, A8, false, REC>(b, tile, z, smem, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -454,8 +496,7 @@ __device__ __forceinline__ void fused_producer(const SmallArgs &a, int64_t pid, 
 }
 
 template <int WAVES, int DEPTH, typename T>
-__global__ __launch_bounds__(64 * WAVES, WAVES > 8 ? 4 : 6) void gemm_small_m_fused_kernel(SmallArgs a, int64_t tiles,
-                                                                                           uint32_t total) {
+__global__ __launch_bounds__(64 * WAVES, WAVES > 8 ? 4 : 6) void gemm_small_m_fused_kernel(SmallArgs a, uint32_t total) {
     // (the unfused kernel's occupancy: the waiting consumers and the
     // producers are resident together)
     static_assert(64 * WAVES == fuse_quads(WAVES) * SQ_BLOCKS * SMALL_M_MAX * 4, "one producer thread per lane of a quad");
@@ -463,8 +504,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES > 8 ? 4 : 6) void gemm_small_m_fu
     const uint32_t epoch = __hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t target = epoch + 1;
     const int64_t id = blockIdx.x;
-    if (id < a.producers) fused_producer<fuse_quads(WAVES), T>(a, id, target);  // uniform per workgroup
-    else small_m_tile<WAVES, DEPTH, false, true>(a, (id - a.producers) % tiles, (id - a.producers) / tiles, smem, target);
+    if (id < a.producers) {
+        fused_producer<fuse_quads(WAVES), T>(a, id, target);  // uniform per workgroup
+    } else {
+        int64_t tile, z;
+        const SmallArgs b = small_m_item(a, id - a.producers, tile, z);
+        small_m_tile<WAVES, DEPTH, false, true>(b, tile, z, smem, target);
+    }
     // the last workgroup to finish advances the epoch for the next call (the
     // next call reads it after this launch has ended: no fence is needed)
     __syncthreads();

@@ -51,6 +51,7 @@ unsigned long long next_ticket() {
 // m <= 16 with a K split: the arrival words at the workspace's start, the
 // partial sums after them
 inline void set_small_m_split(SmallArgs &a, const SmallPlan &p, void *workspace) {
+    a.whole = p.whole;
     if (p.splits <= 1) return;
     a.arrivals = static_cast<unsigned long long *>(workspace);
     a.partial = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + small_m_arrival_bytes(p));
@@ -416,7 +417,7 @@ w4a4_status launch_small_m(const void *packed_w, const uint8_t *codes, const flo
     a.k = k;
     a.range = plan.range;
     set_small_m_split(a, plan, workspace);
-    const dim3 grid((unsigned)plan.tiles, (unsigned)plan.splits);
+    const unsigned grid = (unsigned)small_m_items(plan);
     const bool rec = act_rec != nullptr;
     if (plan.waves == SM_WAVES_LONG_K && rec)
         gemm_small_m_kernel<SM_WAVES_LONG_K, SM_DEPTH, false, true><<<grid, 64 * SM_WAVES_LONG_K, small_m_lds_bytes(plan), s>>>(a);
@@ -607,19 +608,19 @@ w4a4_status w4a4_rotate_quantize_gemm(const void *x, w4a4_dtype dt, int64_t m, i
     a.flags = reinterpret_cast<uint32_t *>(ws + 256);
     const int quads = fuse_quads(plan.waves);
     a.producers = (sq_quads(k) + quads - 1) / quads;
-    const int64_t consumers = plan.tiles * plan.splits;
+    const int64_t consumers = small_m_items(plan);
     const int64_t total = a.producers + consumers;
     if (!grid_fits(total * 64 * plan.waves)) return W4A4_ERR_INVALID_VALUE;
     const unsigned threads = 64 * plan.waves;
     const size_t lds = small_m_lds_bytes(plan);
     if (plan.waves == SM_WAVES_LONG_K && dt == W4A4_DTYPE_F32)
-        gemm_small_m_fused_kernel<SM_WAVES_LONG_K, SM_DEPTH, float><<<(unsigned)total, threads, lds, s>>>(a, plan.tiles, (uint32_t)total);
+        gemm_small_m_fused_kernel<SM_WAVES_LONG_K, SM_DEPTH, float><<<(unsigned)total, threads, lds, s>>>(a, (uint32_t)total);
     else if (plan.waves == SM_WAVES_LONG_K)
-        gemm_small_m_fused_kernel<SM_WAVES_LONG_K, SM_DEPTH, __half><<<(unsigned)total, threads, lds, s>>>(a, plan.tiles, (uint32_t)total);
+        gemm_small_m_fused_kernel<SM_WAVES_LONG_K, SM_DEPTH, __half><<<(unsigned)total, threads, lds, s>>>(a, (uint32_t)total);
     else if (dt == W4A4_DTYPE_F32)
-        gemm_small_m_fused_kernel<SM_WAVES, SM_DEPTH, float><<<(unsigned)total, threads, lds, s>>>(a, plan.tiles, (uint32_t)total);
+        gemm_small_m_fused_kernel<SM_WAVES, SM_DEPTH, float><<<(unsigned)total, threads, lds, s>>>(a, (uint32_t)total);
     else
-        gemm_small_m_fused_kernel<SM_WAVES, SM_DEPTH, __half><<<(unsigned)total, threads, lds, s>>>(a, plan.tiles, (uint32_t)total);
+        gemm_small_m_fused_kernel<SM_WAVES, SM_DEPTH, __half><<<(unsigned)total, threads, lds, s>>>(a, (uint32_t)total);
     return hip_status("gemm_small_m_fused_kernel");
 }
 
@@ -666,7 +667,7 @@ w4a4_status w4a4_gemm_a8(const void *packed_w, const int8_t *codes, const float 
         a.range = plan.range;
         set_small_m_split(a, plan, workspace);
         gemm_small_m_kernel<SM_WAVES, SM_DEPTH, true>
-            <<<dim3((unsigned)plan.tiles, (unsigned)plan.splits), 64 * SM_WAVES, small_m_lds_bytes(plan), s>>>(a);
+            <<<(unsigned)small_m_items(plan), 64 * SM_WAVES, small_m_lds_bytes(plan), s>>>(a);
         return hip_status("gemm_small_m_kernel<a8>");
     }
     // m > 16: the codes as two FP6 planes, then the matrix-core kernel
